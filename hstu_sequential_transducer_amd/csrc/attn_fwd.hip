@@ -1,0 +1,323 @@
+// attn_fwd.hip -- forward of HSTU pointwise aggregated attention on gfx950.
+//
+// Computes, for each sequence b, head h and query i (review of "Actions Speak
+// Louder than Words", section 3, Eq. 2, with phi2 read as SiLU(s)/N_max):
+//   O[i] = (1/N) * sum_{j <= i} SiLU(q_i.k_j + rab_p[h][clip(j-i)] + rab_t[h][bucket(t_i - t_j)]) v_j
+//
+// bf16 kernel (d = 128): a workgroup of 4 waves owns 128 query rows of one
+// (sequence, head); wave w owns rows 32w..32w+31 and keeps their Q in
+// registers.  Keys stream through LDS in tiles of 64 (double buffered, one
+// barrier per tile).  Per 32-key block a wave computes S^T = K Q^T with
+// 32x32x16 bf16 MFMA (so each lane holds one query and 16 keys), adds both
+// biases in registers (rab_p from a per-tile window in LDS indexed by
+// key - query, rab_t from a 32-entry LDS table indexed by count-leading-zeros
+// of |dt| + 1), applies SiLU and the causal mask, packs P to bf16 and
+// accumulates O^T += V^T P^T with V^T read by the transposing LDS load.  P
+// never leaves registers.  Blocks above the diagonal are skipped; blocks on
+// it are masked.  1/N is applied once at the end.
+#include "kernels.h"
+
+namespace {
+
+constexpr int D = 128;
+constexpr int BM = FWD_BM; // 128 query rows
+constexpr int BN = 64;     // keys per LDS tile
+constexpr int NT = 256;
+constexpr int RS = 136;    // LDS row stride (bf16 elements) of K and V tiles
+constexpr int WIN = 192;   // rab_p window entries per tile (BM + BN - 1 used)
+
+struct Stage {
+    bf16 k[BN * RS];
+    bf16 v[BN * RS];
+    float win[WIN];
+    uint32_t kt[BN];
+};
+struct Smem {
+    Stage st[2];
+    float rabt_rev[32]; // rab_t[31 - c], indexed by clz(|dt| + 1)
+    float rabt[128];    // full table for sequences whose time span needs 64 bits
+};
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4v lds_short4v;
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Inside each group of 16 lanes,
+// lane i receives element i%4 of the 4-element chunks addressed by lanes
+// i/4, i/4+4, i/4+8, i/4+12 (in that order).
+DEV u32x2 lds_read_tr(const bf16 *p)
+{
+    short4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(p));
+    return __builtin_bit_cast(u32x2, r);
+}
+
+} // namespace
+
+__global__ void __launch_bounds__(NT) attn_fwd_bf16_kernel(AttnFwdArgs a)
+{
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    Smem &sm = *reinterpret_cast<Smem *>(smem_raw);
+    const int item = blockIdx.x;
+    if (item >= *a.n_items) return;
+    const int2 it = a.items[item];
+    const int b = it.x, qt = it.y >> 8, h = it.y & 255;
+    const int o_b = a.offsets[b];
+    const int L = a.offsets[b + 1] - o_b;
+    const int q0 = qt * BM;
+    const int kend = min(q0 + BM, L); // keys [0, kend) are needed
+    const int nkt = (kend + BN - 1) / BN;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, lq = l & 31;
+    const bool has_t = a.ts != nullptr && a.rab_t != nullptr;
+    const bool wide = has_t && a.wide[b] != 0;
+    const bool has_p = a.rab_p != nullptr;
+    const bf16 *Q = (const bf16 *)a.q, *K = (const bf16 *)a.k, *V = (const bf16 *)a.v;
+
+    if (tid < 128) sm.rabt[tid] = has_t ? a.rab_t[h * a.rt_hs + tid] : 0.f;
+    if (tid < 32) sm.rabt_rev[tid] = has_t ? a.rab_t[h * a.rt_hs + 31 - tid] : 0.f;
+
+    // This lane's query (sequence-local index) and its Q fragment: lane holds
+    // Q[row][16s + 8g .. +8] for s = 0..7 (B operand of S^T = K Q^T).
+    const int qrow = q0 + w * 32 + lq;
+    const bool qvalid = qrow < L;
+    bf16x8 qreg[8];
+    {
+        const bf16 *qp = Q + (int64_t)(o_b + (qvalid ? qrow : 0)) * a.ldq + h * D + g * 8;
+#pragma unroll
+        for (int s = 0; s < 8; s++) {
+            u32x4 x = qvalid ? *(const u32x4 *)(qp + s * 16) : u32x4{0, 0, 0, 0};
+            qreg[s] = as_bf16x8(x);
+        }
+    }
+    const uint32_t tq = (has_t && !wide && qvalid) ? a.rel[o_b + qrow] : 0u;
+    const int64_t tq64 = (wide && qvalid) ? a.ts[o_b + qrow] : 0;
+
+    floatx16 oacc[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) oacc[i][r] = 0.f;
+
+    // Loader mapping: thread -> (key quad lc, 8-wide d group le).
+    const int lc = tid >> 4, le = tid & 15;
+    u32x4 kreg[4], vreg[4];
+    float wreg = 0.f;
+    uint32_t treg = 0;
+    auto gload = [&](int kt) {
+        const int kb0 = kt * BN;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int key = kb0 + lc * 4 + i;
+            const bool ok = key < kend;
+            const int64_t row = (int64_t)(o_b + (ok ? key : 0));
+            kreg[i] = ok ? *(const u32x4 *)(K + row * a.ldk + h * D + le * 8) : u32x4{0, 0, 0, 0};
+            vreg[i] = ok ? *(const u32x4 *)(V + row * a.ldv + h * D + le * 8) : u32x4{0, 0, 0, 0};
+        }
+        if (tid < WIN) {
+            int dl = kb0 - q0 - (BM - 1) + tid; // key - query of window slot tid
+            dl = dl < -a.N ? -a.N : (dl > a.N ? a.N : dl);
+            wreg = has_p ? a.rab_p[h * a.rp_hs + dl + a.N] : 0.f;
+        }
+        if (tid < BN) {
+            const int key = kb0 + tid;
+            treg = (has_t && !wide && key < kend) ? a.rel[o_b + key] : 0u;
+        }
+    };
+    auto sstore = [&](int buf) {
+        Stage &S = sm.st[buf];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            *(u32x4 *)&S.k[(lc * 4 + i) * RS + le * 8] = kreg[i];
+            *(u32x4 *)&S.v[(lc * 4 + i) * RS + le * 8] = vreg[i];
+        }
+        if (tid < WIN) S.win[tid] = wreg;
+        if (tid < BN) S.kt[tid] = treg;
+    };
+
+    gload(0);
+    sstore(0);
+    __syncthreads();
+
+    const int qstart = q0 + w * 32; // first query of this wave
+    // transposing-read lane constants for the V operand
+    const int tj = l & 15, ts_ = tj >> 2;
+    const int cpart = ((l >> 4) & 1) * 16 + 4 * (tj & 3);
+
+    for (int kt = 0; kt < nkt; kt++) {
+        if (kt + 1 < nkt) gload(kt + 1);
+        const Stage &S = sm.st[kt & 1];
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++) {
+            const int kstart = kt * BN + kb * 32;
+            if (kstart > qstart + 31 || qstart >= L) continue; // wave-uniform
+            const bool diag = kstart + 31 > qstart;
+            floatx16 sacc;
+#pragma unroll
+            for (int r = 0; r < 16; r++) sacc[r] = 0.f;
+#pragma unroll
+            for (int s = 0; s < 8; s++) {
+                const bf16x8 ka = *(const bf16x8 *)&S.k[(kb * 32 + lq) * RS + s * 16 + g * 8];
+                sacc = mfma32(ka, qreg[s], sacc);
+            }
+            // register r <-> key kstart + 8(r/4) + 4g + r%4, query qstart + lq
+            const int xb = kb * 32 + 4 * g - w * 32 - lq + (BM - 1);
+            uint32_t pk[8];
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                float p2[2];
+#pragma unroll
+                for (int u = 0; u < 2; u++) {
+                    const int rr = r + u;
+                    const int koff = 8 * (rr >> 2) + (rr & 3);
+                    float x = sacc[rr];
+                    if (has_p) x += S.win[xb + koff];
+                    if (has_t) {
+                        if (!wide) {
+                            const uint32_t tk = S.kt[kb * 32 + 4 * g + koff];
+                            const uint32_t dd = (tq > tk ? tq - tk : tk - tq) + 1u; // |tq - tk| + 1
+                            x += sm.rabt_rev[__builtin_clz(dd)];
+                        } else {
+                            int key = kstart + 4 * g + koff;
+                            key = key < L ? key : L - 1;
+                            x += sm.rabt[time_bucket64(tq64 - a.ts[o_b + key])];
+                        }
+                    }
+                    float p = silu_f(x);
+                    if (diag && (kstart + 4 * g + koff > qstart + lq)) p = 0.f;
+                    p2[u] = p;
+                }
+                pk[r >> 1] = pack2_bf16(p2[0], p2[1]);
+            }
+#pragma unroll
+            for (int m = 0; m < 2; m++) {
+                const bf16x8 pb = as_bf16x8(u32x4{pk[4 * m], pk[4 * m + 1], pk[4 * m + 2], pk[4 * m + 3]});
+                // keys for element e of this lane's operand: 16m + 8(e/4) + 4g + e%4
+                const int key1 = kb * 32 + 16 * m + 4 * g + ts_;
+#pragma unroll
+                for (int db = 0; db < 4; db++) {
+                    const u32x2 r1 = lds_read_tr(&S.v[key1 * RS + db * 32 + cpart]);
+                    const u32x2 r2 = lds_read_tr(&S.v[(key1 + 8) * RS + db * 32 + cpart]);
+                    const bf16x8 va = as_bf16x8(u32x4{r1[0], r1[1], r2[0], r2[1]});
+                    oacc[db] = mfma32(va, pb, oacc[db]);
+                }
+            }
+        }
+        if (kt + 1 < nkt) sstore((kt + 1) & 1);
+        __syncthreads();
+    }
+
+    if (!qvalid) return;
+    // O^T accumulator: lane holds query qrow, d = 32 db + 8(r/4) + 4g + r%4.
+    const int64_t row = (int64_t)(o_b + qrow);
+#pragma unroll
+    for (int db = 0; db < 4; db++) {
+#pragma unroll
+        for (int gr = 0; gr < 4; gr++) {
+            const int d0 = db * 32 + 8 * gr + 4 * g;
+            floatx4 o4 = {oacc[db][4 * gr] * a.inv_n, oacc[db][4 * gr + 1] * a.inv_n, oacc[db][4 * gr + 2] * a.inv_n,
+                          oacc[db][4 * gr + 3] * a.inv_n};
+            if (a.o32) *(floatx4 *)(a.o32 + row * a.ld_o32 + h * D + d0) = o4;
+            if (a.o16) {
+                u32x2 pk2 = {pack2_bf16(o4[0], o4[1]), pack2_bf16(o4[2], o4[3])};
+                *(u32x2 *)((bf16 *)a.o16 + row * a.ld_o16 + h * D + d0) = pk2;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel (any d in {16, 32, 64, 128}): one thread per query row, keys
+// streamed through LDS in tiles of 32, plain fp32 FMA.  For the small fp32
+// layers; the bf16 path above is the MFMA one.
+template <int DD>
+__global__ void __launch_bounds__(F32_BM) attn_fwd_f32_kernel(AttnFwdArgs a)
+{
+    constexpr int KT = 32;
+    __shared__ float ks[KT][DD];
+    __shared__ float vs[KT][DD];
+    __shared__ int64_t kts[KT];
+    const int item = blockIdx.x;
+    if (item >= *a.n_items) return;
+    const int2 it = a.items[item];
+    const int b = it.x, qt = it.y >> 8, h = it.y & 255;
+    const int o_b = a.offsets[b];
+    const int L = a.offsets[b + 1] - o_b;
+    const int q0 = qt * F32_BM;
+    const int i = q0 + threadIdx.x;
+    const bool valid = i < L;
+    const bool has_t = a.ts != nullptr && a.rab_t != nullptr;
+    const float *Q = (const float *)a.q, *Kp = (const float *)a.k, *Vp = (const float *)a.v;
+    float q[DD], acc[DD];
+#pragma unroll
+    for (int c = 0; c < DD; c++) {
+        q[c] = valid ? Q[(int64_t)(o_b + i) * a.ldq + h * DD + c] : 0.f;
+        acc[c] = 0.f;
+    }
+    const int64_t ti = (valid && has_t) ? a.ts[o_b + i] : 0;
+    const int kend = min(q0 + F32_BM, L);
+    for (int k0 = 0; k0 < kend; k0 += KT) {
+        __syncthreads();
+        for (int e = threadIdx.x; e < KT * DD; e += F32_BM) {
+            const int kk = e / DD, c = e % DD, key = k0 + kk;
+            const bool ok = key < kend;
+            ks[kk][c] = ok ? Kp[(int64_t)(o_b + key) * a.ldk + h * DD + c] : 0.f;
+            vs[kk][c] = ok ? Vp[(int64_t)(o_b + key) * a.ldv + h * DD + c] : 0.f;
+        }
+        if (threadIdx.x < KT) {
+            const int key = k0 + threadIdx.x;
+            kts[threadIdx.x] = (has_t && key < kend) ? a.ts[o_b + key] : 0;
+        }
+        __syncthreads();
+        if (!valid) continue;
+        for (int kk = 0; kk < KT; kk++) {
+            const int j = k0 + kk;
+            if (j > i) break;
+            float s = 0.f;
+#pragma unroll
+            for (int c = 0; c < DD; c++) s = fmaf(q[c], ks[kk][c], s);
+            if (a.rab_p) {
+                int dl = j - i;
+                dl = dl < -a.N ? -a.N : (dl > a.N ? a.N : dl);
+                s += a.rab_p[h * a.rp_hs + dl + a.N];
+            }
+            if (has_t) s += a.rab_t[h * a.rt_hs + time_bucket64(ti - kts[kk])];
+            const float p = s / (1.0f + expf(-s));
+#pragma unroll
+            for (int c = 0; c < DD; c++) acc[c] = fmaf(p, vs[kk][c], acc[c]);
+        }
+    }
+    if (!valid) return;
+    const int64_t row = o_b + i;
+#pragma unroll
+    for (int c = 0; c < DD; c++) {
+        const float o = acc[c] * a.inv_n;
+        if (a.o32) a.o32[row * a.ld_o32 + h * DD + c] = o;
+        if (a.o16) ((float *)a.o16)[row * a.ld_o16 + h * DD + c] = o;
+    }
+}
+
+hipError_t launch_attn_fwd_bf16(const AttnFwdArgs &a, int max_items, hipStream_t st)
+{
+    static bool init = false;
+    const size_t smem = sizeof(Smem);
+    if (!init) {
+        hipError_t e = hipFuncSetAttribute((const void *)attn_fwd_bf16_kernel,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        if (e != hipSuccess) return e;
+        init = true;
+    }
+    if (max_items <= 0) return hipSuccess;
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3(max_items), dim3(NT), smem, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd_f32(const AttnFwdArgs &a, int max_items, hipStream_t st)
+{
+    if (max_items <= 0) return hipSuccess;
+    switch (a.d) {
+    case 16: hipLaunchKernelGGL(attn_fwd_f32_kernel<16>, dim3(max_items), dim3(F32_BM), 0, st, a); break;
+    case 32: hipLaunchKernelGGL(attn_fwd_f32_kernel<32>, dim3(max_items), dim3(F32_BM), 0, st, a); break;
+    case 64: hipLaunchKernelGGL(attn_fwd_f32_kernel<64>, dim3(max_items), dim3(F32_BM), 0, st, a); break;
+    case 128: hipLaunchKernelGGL(attn_fwd_f32_kernel<128>, dim3(max_items), dim3(F32_BM), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}

@@ -1,0 +1,134 @@
+// kernels.h -- launch interfaces between the host ABI layer (api.cpp) and the
+// gfx950 kernels.  Internal to libhstu; not part of the public C ABI.
+#pragma once
+#include "common.h"
+
+constexpr int SCHED_BINS = 4096; // longest sequence: (SCHED_BINS - 1) tiles
+
+// ---- launcher (sched.hip)
+void launch_sched(const int32_t *offsets, const int64_t *ts, int B, int T, int tile, int H, int *status, int *n_items,
+                  int2 *items, int max_items, uint32_t *rel, int32_t *wide, hipStream_t st);
+
+// ---- attention forward (attn_fwd.hip)
+struct AttnFwdArgs {
+    const void *q, *k, *v;
+    int64_t ldq, ldk, ldv;      // token strides (elements)
+    const int32_t *offsets;
+    const int64_t *ts;          // NULL: no time bias
+    const uint32_t *rel;        // sequence-relative 32-bit times
+    const int32_t *wide;        // per sequence: 1 = 64-bit time path
+    const float *rab_p;         // NULL: no position bias
+    int64_t rp_hs;
+    const float *rab_t;         // NULL: no time bias
+    int64_t rt_hs;
+    int H, N, d;
+    float inv_n;
+    const int2 *items;
+    const int *n_items;
+    float *o32;                 // fp32 output [T][H*d] (ld_o32) or NULL
+    int64_t ld_o32;
+    void *o16;                  // storage-dtype output or NULL
+    int64_t ld_o16;
+};
+constexpr int FWD_BM = 128; // query rows per workgroup (bf16 MFMA kernel)
+constexpr int F32_BM = 64;  // query rows per workgroup (fp32 kernel)
+hipError_t launch_attn_fwd_bf16(const AttnFwdArgs &a, int max_items, hipStream_t st);
+hipError_t launch_attn_fwd_f32(const AttnFwdArgs &a, int max_items, hipStream_t st);
+
+// ---- LayerNorm(O) (.) U epilogue and its backward (epilogue.hip)
+// G = (O - mean) * rstd * U over F features per row; out dtype per flag.
+hipError_t launch_ln_gate_fwd(const float *O, int64_t ldo, int nparts, int64_t part_stride, const void *U, int64_t ldu,
+                              bool bf16io, void *G, int64_t ldg, float *stats, float *o_copy, int64_t ld_oc, int T,
+                              int F, float eps, const int *status, hipStream_t st);
+hipError_t launch_ln_gate_bwd(const void *dG, int64_t ldg, const void *U, int64_t ldu, const float *O, int64_t ldo,
+                              const float *stats, bool bf16io, void *dU, int64_t lddu, bf16 *dO, float scale, int T,
+                              int F, const int *status, hipStream_t st);
+
+// ---- attention backward (attn_bwd.hip)
+struct AttnBwdArgs {
+    const bf16 *q, *k, *v;
+    int64_t ldq, ldk, ldv;
+    const bf16 *dO;             // dO / N_max, [T][H*d] bf16 (ld = H*d)
+    const int32_t *offsets;
+    const int64_t *ts;
+    const uint32_t *rel;
+    const int32_t *wide;
+    const float *rab_p;
+    int64_t rp_hs;
+    const float *rab_t;
+    int64_t rt_hs;
+    int H, N;
+    const int2 *items;
+    const int *n_items;
+    float *dq_acc;              // fp32 [T][H*d] accumulator, zeroed
+    bf16 *dk, *dv;
+    int64_t lddk, lddv;
+    float *drab_p;              // fp32 [H][2N+1] accumulator (zeroed) or NULL
+    float *drab_t;              // fp32 [H][128] accumulator (zeroed) or NULL
+};
+constexpr int BWD_BN = 128; // keys per workgroup
+hipError_t launch_attn_bwd_bf16(const AttnBwdArgs &a, int max_items, hipStream_t st);
+
+// ---- small helpers (misc.hip)
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st);
+hipError_t launch_cast_f32_to_bf16(const float *src, int64_t lds, bf16 *dst, int64_t ldd, int rows, int cols,
+                                   const int *status, hipStream_t st);
+hipError_t launch_copy_f32(const float *src, float *dst, size_t n, hipStream_t st);
+
+// ---- GEMM with fused epilogues (gemm.hip)
+// C[M][N] = epi(A[M][K] . W[N][K]^T + bias) (+ R), A/W/C storage dtype or fp32.
+enum GemmEpi { EPI_NONE = 0, EPI_SILU = 1, EPI_RELU = 2 };
+struct GemmArgs {
+    const void *A;
+    int64_t lda;
+    const void *W;              // [N][K] ([out][in])
+    const float *bias;          // [N] or NULL
+    const void *R;              // residual [M][N] or NULL (added after the activation)
+    int64_t ldr;
+    bool r_f32;                 // residual is fp32 (else storage dtype)
+    void *C;
+    int64_t ldc;
+    bool c_f32;                 // output fp32 (else storage dtype)
+    int M, N, K;
+    int epi;
+    // optional second output: columns [split_lo, split_hi) also copied to C2
+    // (used to write this layer's K and V into the M-FALCON cache)
+    void *C2a;
+    int64_t ldc2a;
+    int c2a_lo;
+    void *C2b;
+    int64_t ldc2b;
+    int c2b_lo;
+    int c2_width;
+};
+hipError_t launch_gemm_bf16(const GemmArgs &g, hipStream_t st);
+hipError_t launch_gemm_f32(const GemmArgs &g, hipStream_t st);
+
+// ---- M-FALCON (mfalcon.hip)
+struct MfalconArgs {
+    const void *q;              // candidate Q [M][H*d] view (ld)
+    const void *k;              // candidate K
+    const void *v;              // candidate V
+    int64_t ldz;
+    const void *kc, *vc;        // cached history K, V [T_hist][H][d]
+    int64_t ldkc, ldvc;
+    const int32_t *hoff;        // [U+1]
+    const int32_t *coff;        // [U+1]
+    const int64_t *hts;         // [T_hist] or NULL
+    const int64_t *cts;         // [U] or NULL
+    const float *rab_p;
+    int64_t rp_hs;
+    const float *rab_t;
+    int64_t rt_hs;
+    int H, N, U, M;
+    float inv_n;
+    int ctile;                  // candidates per workgroup tile
+    int kchunk;                 // history keys per split
+    int nsplit;                 // key splits
+    const int4 *items;          // (user, cand tile start, head, split)
+    const int *n_items;
+    float *part;                // [nsplit][M][H*d] fp32 partial sums
+};
+hipError_t launch_mfalcon_sched(const int32_t *hoff, const int32_t *coff, int U, int M, int H, int ctile, int kchunk,
+                                int nsplit, int4 *items, int *n_items, int *status, int max_items, hipStream_t st);
+hipError_t launch_mfalcon_attn(const MfalconArgs &a, int max_items, bool bf16io, hipStream_t st);

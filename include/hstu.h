@@ -1,0 +1,195 @@
+/*
+ * hstu.h -- C ABI of libhstu.so: HSTU pointwise aggregated attention on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Source of the method: the paper review page "Actions Speak Louder than
+ * Words: Trillion-Parameter Sequential Transducers for Generative
+ * Recommendations" (arXiv 2402.17152), written [GR review] below.  Its
+ * section 3 (core formulas) gives the HSTU layer:
+ *   Eq. 1  U, V, Q, K = Split(phi1(f1(X))),  f_i(X) = W_i X + b_i
+ *   Eq. 2  A(X)V(X)   = phi2(Q K^T + rab^{p,t}) V(X)
+ *   Eq. 3  Y(X)       = f2(Norm(A(X)V(X)) (.) U(X))
+ * and residual connections between layers; its M-FALCON subsection scores m
+ * candidates in ceil(m/b_m) microbatches against cached history work.
+ *
+ * Readings used wherever the page leaves a step open (each is exact, not an
+ * approximation):
+ *   phi2(s)  = SiLU(s) / N_max, causal mask j <= i (diagonal included);
+ *              masked pairs contribute exactly nothing; no 1/sqrt(d) scale.
+ *   rab^p    = rab_p[h][clip(j - i, -N_max, N_max) + N_max]   (j key, i query)
+ *   rab^t    = rab_t[h][min(127, floor(log2(|t_i - t_j| + 1)))] (int64 seconds)
+ *   Norm     = LayerNorm over all H*d_v features of a token, no affine,
+ *              biased variance, eps = hstu_dims.ln_eps.
+ *   Split    = column blocks U | V | Q | K of f1's output, head-major inside.
+ *   f_i      = x W^T + b with W stored [out][in];  layer: y = x + f2(.).
+ *
+ * Conventions for every entry point
+ *   - Device pointers are HIP device memory; the caller owns every buffer.
+ *     No entry point allocates or frees device memory: scratch space is the
+ *     caller's workspace `ws` of at least hstu_workspace_size() bytes,
+ *     256-byte aligned.
+ *   - Jagged batches have no padding: sequence b owns tokens
+ *     [offsets[b], offsets[b+1]) of every [T][...] array.
+ *   - Matrices are row-major with a token stride `ld` in elements, so Q/K/V/U
+ *     may be views into one f1 output buffer [T][4*H*d] (ld = 4*H*d).
+ *     Per-head tensors are [T][H][d] inside a row: head h at column h*d.
+ *   - Everything is enqueued on `stream` (a hipStream_t, NULL = default
+ *     stream); nothing synchronises the host and nothing is copied device to
+ *     host.  Outputs are overwritten, never accumulated into.
+ *   - On a non-OK status nothing has been enqueued and hstu_last_error()
+ *     describes the problem.  Launch failures return HSTU_ERR_DEVICE.
+ *     Device-side data checks (offsets[0] == 0, non-decreasing offsets,
+ *     offsets[B] == T) write a status word into the workspace; with the
+ *     environment variable HSTU_DEBUG=1 each call synchronises the stream and
+ *     reports a failed check as HSTU_ERR_ARG.  A batch that fails the check
+ *     computes nothing (outputs are left unwritten).
+ *   - Entry points are thread-safe for distinct workspaces; calls that share
+ *     a workspace must be ordered on one stream.
+ */
+#ifndef HSTU_H
+#define HSTU_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HSTU_ABI_VERSION 1
+
+typedef enum {
+    HSTU_OK = 0,
+    HSTU_ERR_ARG = 1,         /* invalid argument (null pointer, bad size, bad layout) */
+    HSTU_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. a head size) */
+    HSTU_ERR_WORKSPACE = 3,   /* workspace missing, misaligned or too small */
+    HSTU_ERR_DEVICE = 4       /* HIP runtime error while launching */
+} hstu_status;
+
+typedef enum { HSTU_F32 = 0, HSTU_BF16 = 1 } hstu_dtype;
+typedef enum { HSTU_ACT_SILU = 0, HSTU_ACT_RELU = 1 } hstu_act; /* phi1 of Eq. 1 */
+
+typedef enum {
+    HSTU_OP_ATTN_FWD = 0,
+    HSTU_OP_ATTN_BWD = 1,
+    HSTU_OP_LAYER_FWD = 2,
+    HSTU_OP_MFALCON = 3
+} hstu_op;
+
+/* A jagged batch.  batch, total and n_max are host values; offsets and ts
+ * are device pointers.  n_max is the N_max of phi2 and of rab^p (a constant
+ * of the model, not the realised maximum length). */
+typedef struct {
+    int32_t batch;          /* B >= 1 */
+    int32_t total;          /* T = offsets[B] (host copy), >= 0 */
+    int32_t n_max;          /* N_max >= 1 */
+    const int32_t *offsets; /* device [B+1], offsets[0] = 0, non-decreasing */
+    const int64_t *ts;      /* device [T] int64 seconds, or NULL: no rab^t term */
+} hstu_jagged;
+
+/* Head geometry and storage dtype of activations (Q, K, V, U, outputs). */
+typedef struct {
+    hstu_dtype dtype; /* HSTU_BF16: MFMA path (d_qk = d_v = 128); HSTU_F32: any d <= 128 */
+    int32_t heads;    /* H >= 1 */
+    int32_t d_qk;
+    int32_t d_v;      /* d_qk must equal d_v */
+    float ln_eps;     /* eps of Norm, > 0 */
+} hstu_dims;
+
+/* rab tables, fp32, device.  A NULL table omits that term.  hstride is the
+ * distance between heads in elements; 0 shares one table across heads. */
+typedef struct {
+    const float *rab_p;    /* [H][2*N_max+1] */
+    int64_t rab_p_hstride; /* usually 2*N_max+1 */
+    const float *rab_t;    /* [H][128] */
+    int64_t rab_t_hstride; /* usually 128 */
+} hstu_bias;
+
+typedef struct { const void *ptr; int64_t ld; } hstu_cmat; /* read-only row-major view */
+typedef struct { void *ptr; int64_t ld; } hstu_mat;        /* writable row-major view */
+
+/* One HSTU layer's parameters (device).  Storage dtype = hstu_dims.dtype.
+ *   w1 [4*H*d][D]: output rows U | V | Q | K, head-major inside each block
+ *   b1 [4*H*d] or NULL, w2 [D][H*d], b2 [D] or NULL (biases always fp32). */
+typedef struct {
+    const void *w1;
+    const float *b1;
+    const void *w2;
+    const float *b2;
+    hstu_bias rab;
+    hstu_act phi1;
+} hstu_layer;
+
+/* Bytes of workspace an entry point needs for these sizes.  d_model and
+ * total_cand are used by HSTU_OP_LAYER_FWD / HSTU_OP_MFALCON only (pass 0
+ * otherwise); for HSTU_OP_MFALCON `j` describes the histories (batch = users).
+ * Returns 0 and sets hstu_last_error() on invalid sizes. */
+size_t hstu_workspace_size(hstu_op op, const hstu_jagged *j, const hstu_dims *dims, int32_t d_model,
+                           int32_t total_cand);
+
+/*
+ * Forward of Eq. 2 ([GR review] §3, spatial aggregation), optionally with
+ * Eq. 3's Norm(AV) (.) U gate.
+ *   q, k [T][H][d_qk], v [T][H][d_v] (storage dtype).
+ *   u == NULL pointer: out = O = phi2(QK^T + rab) V, [T][H*d_v], storage dtype.
+ *   u given ([T][H*d_v]): out = G = LayerNorm(O) (.) U, storage dtype.
+ *   o_save (optional, fp32 [T][H*d_v], ld = H*d_v): O in fp32, for the
+ *   backward; ln_stats (optional, fp32 [T][2]): per token (mean, rstd).
+ */
+hstu_status hstu_attn_fwd(const hstu_jagged *j, const hstu_dims *dims, const hstu_bias *bias, hstu_cmat q,
+                          hstu_cmat k, hstu_cmat v, hstu_cmat u, hstu_mat out, float *o_save, float *ln_stats,
+                          void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Backward of hstu_attn_fwd (chain rule through Eq. 3's Norm (.) U and
+ * Eq. 2).  bf16 only.
+ *   dout: upstream gradient at G when u is given (then o_save and ln_stats
+ *   from the forward are required), else at O.
+ *   Outputs (storage dtype): dq, dk [T][H][d], dv [T][H][d], du [T][H*d]
+ *   (when u is given); fp32 drab_p [H][2*N_max+1] and drab_t [H][128] (each
+ *   may be NULL to skip; contiguous, hstride as in `bias`, which must not be
+ *   0 when the gradient is requested).
+ */
+hstu_status hstu_attn_bwd(const hstu_jagged *j, const hstu_dims *dims, const hstu_bias *bias, hstu_cmat q,
+                          hstu_cmat k, hstu_cmat v, hstu_cmat u, const float *o_save, const float *ln_stats,
+                          hstu_cmat dout, hstu_mat dq, hstu_mat dk, hstu_mat dv, hstu_mat du, float *drab_p,
+                          float *drab_t, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * One HSTU layer forward ([GR review] §3 Eq. 1-3 and the residual between
+ * layers): y = x + f2(LayerNorm(O) (.) U) with U, V, Q, K = Split(phi1(f1(x))).
+ *   x [T][D] (storage dtype), y [T][D] (storage dtype; may not alias x).
+ *   k_cache / v_cache (optional, ptr NULL to skip): this layer's K and V,
+ *   [T][H][d] storage dtype -- the cacheable history work M-FALCON reuses.
+ */
+hstu_status hstu_layer_fwd(const hstu_jagged *j, const hstu_dims *dims, int32_t d_model, const hstu_layer *layer,
+                           hstu_cmat x, hstu_mat y, hstu_mat k_cache, hstu_mat v_cache, void *ws, size_t ws_bytes,
+                           void *stream);
+
+/*
+ * M-FALCON candidate scoring ([GR review] §3, M-FALCON).  User u has a history
+ * of n_u tokens (hist->offsets) whose per-layer K, V were cached by
+ * hstu_layer_fwd, and candidates [cand_offsets[u], cand_offsets[u+1]) of
+ * x_cand.  Every candidate sits at position n_u with time cand_ts[u] and
+ * attends to the whole history and to itself, never to other candidates.
+ * Candidates are processed in microbatches of b_m (>= 1); the result does not
+ * depend on b_m.  Output: the candidates' final hidden states, fp32 [M][D].
+ *   layers, k_cache, v_cache: host arrays of n_layers entries (device data).
+ *   cand_offsets: device [U+1]; cand_ts: device [U] (NULL iff hist->ts NULL).
+ */
+hstu_status mfalcon_score(const hstu_jagged *hist, const hstu_dims *dims, int32_t d_model, int32_t n_layers,
+                          const hstu_layer *layers, const hstu_cmat *k_cache, const hstu_cmat *v_cache,
+                          const int32_t *cand_offsets, int32_t total_cand, const int64_t *cand_ts, hstu_cmat x_cand,
+                          int32_t b_m, float *y_cand, void *ws, size_t ws_bytes, void *stream);
+
+/* Message of the last non-OK status on this thread ("" if none). */
+const char *hstu_last_error(void);
+
+/* HSTU_ABI_VERSION of the loaded library. */
+int32_t hstu_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSTU_H */

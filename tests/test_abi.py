@@ -1,0 +1,79 @@
+"""The C ABI library loads and exports every symbol include/hstu.h declares,
+and host-side argument validation rejects bad calls before any device work
+(no GPU needed: every call below returns before touching HIP)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import hstu_sequential_transducer_amd as hs
+from hstu_sequential_transducer_amd import binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hstu.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
+    skip = {"if", "sizeof", "defined"}
+    return sorted({n for n in names if n not in skip and (n.startswith("hstu_") or n.startswith("mfalcon_"))})
+
+
+def test_library_exports_every_declared_symbol():
+    lib = hs.load_library()
+    decl = declared_functions()
+    assert set(decl) == set(bd.EXPORTED), decl
+    for name in decl:
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_matches_header():
+    m = re.search(r"#define HSTU_ABI_VERSION (\d+)", open(HEADER).read())
+    assert hs.abi_version() == int(m.group(1))
+
+
+def _dims(dtype=bd.HSTU_BF16, H=4, d=128, eps=1e-5):
+    return bd.Dims(dtype, H, d, d, eps)
+
+
+def _jag(B=2, T=10, n=8, off=1, ts=None):
+    return bd.Jagged(B, T, n, off, ts)
+
+
+def _call_fwd(jag, dims, ws=None, ws_bytes=0, q=8, ldq=512, out=8):
+    lib = hs.load_library()
+    bias = bd.Bias(None, 0, None, 0)
+    m = lambda p, ld: bd.CMat(p, ld)
+    return lib.hstu_attn_fwd(ctypes.byref(jag) if jag is not None else None, ctypes.byref(dims), ctypes.byref(bias),
+                             m(q, ldq), m(8, 512), m(8, 512), m(None, 0), bd.Mat(out, 512), None, None, ws, ws_bytes,
+                             None)
+
+
+def test_validation_errors_are_reported():
+    assert _call_fwd(None, _dims()) == bd.HSTU_ERR_ARG
+    assert "NULL" in hs.last_error()
+    assert _call_fwd(_jag(B=0), _dims()) == bd.HSTU_ERR_ARG
+    assert _call_fwd(_jag(n=0), _dims()) == bd.HSTU_ERR_ARG
+    assert _call_fwd(_jag(), _dims(d=64)) == bd.HSTU_ERR_UNSUPPORTED
+    assert _call_fwd(_jag(), _dims(dtype=bd.HSTU_F32, d=24)) == bd.HSTU_ERR_UNSUPPORTED
+    assert _call_fwd(_jag(), _dims(eps=0.0)) == bd.HSTU_ERR_ARG
+    assert _call_fwd(_jag(), _dims(), q=None) == bd.HSTU_ERR_ARG
+    assert _call_fwd(_jag(), _dims(), ldq=100) == bd.HSTU_ERR_ARG
+    assert "ld" in hs.last_error()
+    assert _call_fwd(_jag(), _dims(), ws=None) == bd.HSTU_ERR_WORKSPACE
+    assert _call_fwd(_jag(), _dims(), ws=256 * 3 + 4, ws_bytes=1 << 30) == bd.HSTU_ERR_WORKSPACE
+    assert _call_fwd(_jag(), _dims(), ws=256 * 4, ws_bytes=16) == bd.HSTU_ERR_WORKSPACE
+    assert "too small" in hs.last_error()
+
+
+def test_workspace_size_grows_with_tokens():
+    lib = hs.load_library()
+    d = _dims()
+    small = lib.hstu_workspace_size(bd.OP_ATTN_FWD, ctypes.byref(_jag(T=100)), ctypes.byref(d), 0, 0)
+    big = lib.hstu_workspace_size(bd.OP_ATTN_FWD, ctypes.byref(_jag(T=100000)), ctypes.byref(d), 0, 0)
+    assert 0 < small < big
+    assert big % 256 == 0
+    assert lib.hstu_workspace_size(bd.OP_ATTN_FWD, ctypes.byref(_jag(B=0)), ctypes.byref(d), 0, 0) == 0
