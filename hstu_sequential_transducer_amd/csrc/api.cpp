@@ -79,7 +79,7 @@ AttnWs attn_ws(const hstu_jagged *j, const hstu_dims *dm, int tile)
     w.wide = c.take((size_t)B * 4);
     w.obuf = c.take((size_t)T * H * dm->d_v * 4);
     w.dq = c.take((size_t)T * H * dm->d_qk * 4);
-    w.dO = c.take((size_t)T * H * dm->d_v * 2);
+    w.dO = c.take((size_t)T * H * dm->d_v * 2 * 2); // hi and lo bf16 planes
     w.total = c.cur;
     return w;
 }
@@ -267,9 +267,89 @@ hstu_status hstu_attn_bwd(const hstu_jagged *j, const hstu_dims *dm, const hstu_
                           hstu_mat dq, hstu_mat dk, hstu_mat dv, hstu_mat du, float *drab_p, float *drab_t, void *ws,
                           size_t ws_bytes, void *stream)
 {
-    (void)j; (void)dm; (void)bias; (void)q; (void)k; (void)v; (void)u; (void)o_save; (void)ln_stats; (void)dout;
-    (void)dq; (void)dk; (void)dv; (void)du; (void)drab_p; (void)drab_t; (void)ws; (void)ws_bytes; (void)stream;
-    return fail(HSTU_ERR_UNSUPPORTED, "hstu_attn_bwd: not built yet");
+    TRY(check_jagged(j));
+    TRY(check_dims(dm));
+    TRY(check_bias(bias, j));
+    if (dm->dtype != HSTU_BF16) return fail(HSTU_ERR_UNSUPPORTED, "hstu_attn_bwd supports bf16 storage only");
+    const int H = dm->heads, d = dm->d_qk, F = H * dm->d_v;
+    TRY(check_view(q.ptr, q.ld, (int64_t)H * d, "q"));
+    TRY(check_view(k.ptr, k.ld, (int64_t)H * d, "k"));
+    TRY(check_view(v.ptr, v.ld, (int64_t)F, "v"));
+    TRY(check_view(dout.ptr, dout.ld, (int64_t)F, "dout"));
+    TRY(check_view(dq.ptr, dq.ld, (int64_t)H * d, "dq"));
+    TRY(check_view(dk.ptr, dk.ld, (int64_t)H * d, "dk"));
+    TRY(check_view(dv.ptr, dv.ld, (int64_t)F, "dv"));
+    if (u.ptr) {
+        TRY(check_view(u.ptr, u.ld, (int64_t)F, "u"));
+        TRY(check_view(du.ptr, du.ld, (int64_t)F, "du"));
+        if (!o_save || !ln_stats) return fail(HSTU_ERR_ARG, "with u, o_save and ln_stats from the forward are required");
+    }
+    const bool has_p = bias && bias->rab_p;
+    const bool has_t = bias && bias->rab_t && j->ts;
+    if (drab_p && has_p && bias->rab_p_hstride == 0)
+        return fail(HSTU_ERR_ARG, "drab_p needs a per-head rab_p (hstride != 0)");
+    if (drab_t && has_t && bias->rab_t_hstride == 0)
+        return fail(HSTU_ERR_ARG, "drab_t needs a per-head rab_t (hstride != 0)");
+    const AttnWs w = attn_ws(j, dm, BWD_BN);
+    TRY(check_ws(ws, ws_bytes, w.total));
+    hipStream_t st = (hipStream_t)stream;
+    char *wb = (char *)ws;
+    int *status = (int *)(wb + w.header), *n_items = status + 1;
+    int2 *items = (int2 *)(wb + w.items);
+    uint32_t *rel = (uint32_t *)(wb + w.rel);
+    int32_t *wide = (int32_t *)(wb + w.wide);
+    float *dq_acc = (float *)(wb + w.dq);
+    bf16 *dO = (bf16 *)(wb + w.dO);
+    const int T = j->total, B = j->batch, N = j->n_max;
+    const int max_items = max_items_for(B, T, BWD_BN, H);
+    const int64_t p_hs = has_p ? bias->rab_p_hstride : 2 * (int64_t)N + 1;
+    const int64_t t_hs = (bias && bias->rab_t) ? bias->rab_t_hstride : 128;
+    launch_sched(j->offsets, j->ts, B, T, BWD_BN, H, status, n_items, items, max_items, rel, wide, st);
+    TRY(launched(hipGetLastError(), "schedule kernel"));
+    TRY(launched(launch_fill_zero(dq_acc, (size_t)T * H * d * 4, st), "zero fill"));
+    if (drab_p) TRY(launched(launch_fill_zero(drab_p, (size_t)H * p_hs * 4, st), "zero fill"));
+    if (drab_t) TRY(launched(launch_fill_zero(drab_t, (size_t)H * t_hs * 4, st), "zero fill"));
+    const float inv_n = 1.0f / (float)N;
+    if (u.ptr) {
+        TRY(launched(launch_ln_gate_bwd(dout.ptr, dout.ld, u.ptr, u.ld, o_save, F, ln_stats, true, du.ptr, du.ld, dO,
+                                        inv_n, T, F, status, st),
+                     "LayerNorm gate backward kernel"));
+    } else {
+        TRY(launched(launch_scale_bf16((const bf16 *)dout.ptr, dout.ld, dO, F, T, F, inv_n, st), "scale kernel"));
+    }
+    AttnBwdArgs a{};
+    a.q = (const bf16 *)q.ptr;
+    a.k = (const bf16 *)k.ptr;
+    a.v = (const bf16 *)v.ptr;
+    a.ldq = q.ld;
+    a.ldk = k.ld;
+    a.ldv = v.ld;
+    a.dO = dO;
+    a.T = T;
+    a.offsets = j->offsets;
+    a.ts = has_t ? j->ts : nullptr;
+    a.rel = rel;
+    a.wide = wide;
+    a.rab_p = has_p ? bias->rab_p : nullptr;
+    a.rp_hs = p_hs;
+    a.rab_t = has_t ? bias->rab_t : nullptr;
+    a.rt_hs = t_hs;
+    a.H = H;
+    a.N = N;
+    a.items = items;
+    a.n_items = n_items;
+    a.dq_acc = dq_acc;
+    a.dk = (bf16 *)dk.ptr;
+    a.dv = (bf16 *)dv.ptr;
+    a.lddk = dk.ld;
+    a.lddv = dv.ld;
+    a.drab_p = drab_p;
+    a.drab_t = has_t ? drab_t : nullptr;
+    TRY(launched(launch_attn_bwd_bf16(a, max_items, st), "attention backward kernel"));
+    TRY(launched(launch_cast_f32_to_bf16(dq_acc, (int64_t)H * d, (bf16 *)dq.ptr, dq.ld, T, H * d, status, st),
+                 "cast kernel"));
+    TRY(debug_check(ws, st));
+    return ok();
 }
 
 hstu_status hstu_layer_fwd(const hstu_jagged *j, const hstu_dims *dm, int32_t d_model, const hstu_layer *layer,

@@ -1,0 +1,364 @@
+// attn_bwd.hip -- backward of HSTU pointwise aggregated attention on gfx950.
+//
+// Chain rule through Eq. 2 of the review of "Actions Speak Louder than Words"
+// (section 3), phi2 read as SiLU(s)/N_max; with dO' = dO / N_max:
+//   p_ij  = SiLU(x_ij),  x_ij = q_i.k_j + rab_p[clip(j-i)] + rab_t[bucket]
+//   dV_j += sum_i p_ij dO'_i          dP_ij = dO'_i . v_j
+//   dS_ij = dP_ij * s(x)(1 + x(1 - s(x)))   (s = sigmoid; 0 where j > i)
+//   dK_j += sum_i dS_ij q_i           dQ_i += sum_j dS_ij k_j
+//   drab_p[clip(j-i)] += dS_ij        drab_t[bucket] += dS_ij
+// x is recomputed from Q, K and the tables (pointwise attention keeps no
+// softmax statistics, so nothing else is needed).
+//
+// A workgroup of 4 waves owns 128 keys of one (sequence, head); wave w owns
+// keys 32w..32w+31 with their K and V rows in registers and their dK^T, dV^T
+// accumulators in registers.  Query blocks of 32 stream through LDS (double
+// buffered).  Per block a wave computes S and dP with 32x32x16 bf16 MFMA
+// (lane = key, registers = queries), the element-wise step, dV^T += dO'^T P
+// and dK^T += Q^T dS (transposing LDS reads for dO'^T and Q^T), and writes dS
+// to LDS; then wave w computes dQ for d-block w over all 128 keys and adds it
+// to an fp32 accumulator with global atomics.  drab_p is summed in an LDS
+// ring indexed by j - i and flushed with one atomic per entry once no later
+// block can touch it; drab_t goes through per-wave LDS tables.
+#include "kernels.h"
+
+namespace {
+
+constexpr int D = 128;
+constexpr int BN = BWD_BN; // 128 keys per workgroup
+constexpr int BQ = 32;     // queries per block
+constexpr int NT = 256;
+constexpr int RS = 136;    // LDS row stride (bf16) of Q, dO and K tiles
+constexpr int SS = 40;     // LDS row stride (bf16) of the dS tile [key][query]
+constexpr int WIN = 160;   // rab_p window per block (BQ + BN - 1 used)
+constexpr int RING = 256;  // drab_p ring (power of two >= WIN + BQ)
+constexpr int TB = 64;     // time buckets that int64 differences can reach
+constexpr int TCOPY = 4;   // copies of each wave's drab_t table
+
+struct Stage {
+    bf16 q[BQ * RS];
+    bf16 dO[BQ * RS];
+    bf16 dOl[BQ * RS]; // low part of dO' (dO' = dO + dOl to ~16 bits)
+    float win[WIN];
+    uint32_t qt[BQ];
+    int64_t qt64[BQ];
+};
+struct Smem {
+    bf16 k[BN * RS];
+    Stage st[2];
+    bf16 ds[BN * SS];
+    float ring[RING];
+    float dtab[4][TCOPY][TB];
+    float rabt_rev[32];
+    float rabt[128];
+};
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4v lds_short4v;
+
+DEV u32x2 lds_read_tr(const bf16 *p)
+{
+    short4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(p));
+    return __builtin_bit_cast(u32x2, r);
+}
+
+} // namespace
+
+__global__ void __launch_bounds__(NT) attn_bwd_bf16_kernel(AttnBwdArgs a)
+{
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    Smem &sm = *reinterpret_cast<Smem *>(smem_raw);
+    const int item = blockIdx.x;
+    if (item >= *a.n_items) return;
+    const int2 it = a.items[item];
+    const int b = it.x, tsched = it.y >> 8, h = it.y & 255;
+    const int o_b = a.offsets[b];
+    const int L = a.offsets[b + 1] - o_b;
+    const int nkt = (L + BN - 1) / BN;
+    const int kt = nkt - 1 - tsched; // most expensive key tile (kt = 0) first
+    const int k0 = kt * BN;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, lq = l & 31;
+    const bool has_t = a.ts != nullptr && a.rab_t != nullptr;
+    const bool wide = has_t && a.wide[b] != 0;
+    const bool has_p = a.rab_p != nullptr;
+    const bf16 *Q = a.q, *K = a.k, *V = a.v, *dO = a.dO;
+    const int64_t ld_do = (int64_t)a.H * D;
+
+    // ---- prologue: tables, K tile in LDS, own K/V rows in registers
+    if (tid < 128) sm.rabt[tid] = has_t ? a.rab_t[h * a.rt_hs + tid] : 0.f;
+    if (tid < 32) sm.rabt_rev[tid] = has_t ? a.rab_t[h * a.rt_hs + 31 - tid] : 0.f;
+    for (int i = tid; i < RING; i += NT) sm.ring[i] = 0.f;
+    for (int i = tid; i < 4 * TCOPY * TB; i += NT) (&sm.dtab[0][0][0])[i] = 0.f;
+    {
+        const int lc = tid >> 4, le = tid & 15; // 16 keys x 16 d-groups per pass
+#pragma unroll
+        for (int pass = 0; pass < BN / 16; pass++) {
+            const int key = k0 + pass * 16 + lc;
+            const bool ok = key < L;
+            u32x4 x = ok ? *(const u32x4 *)(K + (int64_t)(o_b + key) * a.ldk + h * D + le * 8) : u32x4{0, 0, 0, 0};
+            *(u32x4 *)&sm.k[(pass * 16 + lc) * RS + le * 8] = x;
+        }
+    }
+    const int mykey = k0 + 32 * w + lq;
+    const bool kvalid = mykey < L;
+    bf16x8 kreg[8], vreg[8];
+    {
+        const bf16 *kp = K + (int64_t)(o_b + (kvalid ? mykey : 0)) * a.ldk + h * D + g * 8;
+        const bf16 *vp = V + (int64_t)(o_b + (kvalid ? mykey : 0)) * a.ldv + h * D + g * 8;
+#pragma unroll
+        for (int s = 0; s < 8; s++) {
+            kreg[s] = as_bf16x8(kvalid ? *(const u32x4 *)(kp + s * 16) : u32x4{0, 0, 0, 0});
+            vreg[s] = as_bf16x8(kvalid ? *(const u32x4 *)(vp + s * 16) : u32x4{0, 0, 0, 0});
+        }
+    }
+    const uint32_t tk = (has_t && !wide && kvalid) ? a.rel[o_b + mykey] : 0u;
+    const int64_t tk64 = (wide && kvalid) ? a.ts[o_b + mykey] : 0;
+
+    floatx16 dv_acc[4], dk_acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            dv_acc[i][r] = 0.f;
+            dk_acc[i][r] = 0.f;
+        }
+
+    // ---- query-block stage loader: thread -> (query lcq, 16 d-groups)
+    const int lcq = tid >> 3, leq = tid & 7; // 32 queries x 8 threads x 16 elements
+    u32x4 qreg2[2], dreg2[2], lreg2[2];
+    const bf16 *dOlo = dO + (int64_t)a.T * ld_do;
+    float wreg = 0.f;
+    uint32_t treg = 0;
+    int64_t treg64 = 0;
+    auto gload = [&](int q0) {
+        const int qi = q0 + lcq;
+        const bool ok = qi < L;
+        const int64_t row = (int64_t)(o_b + (ok ? qi : 0));
+#pragma unroll
+        for (int c = 0; c < 2; c++) {
+            qreg2[c] = ok ? *(const u32x4 *)(Q + row * a.ldq + h * D + leq * 16 + c * 8) : u32x4{0, 0, 0, 0};
+            dreg2[c] = ok ? *(const u32x4 *)(dO + row * ld_do + h * D + leq * 16 + c * 8) : u32x4{0, 0, 0, 0};
+            lreg2[c] = ok ? *(const u32x4 *)(dOlo + row * ld_do + h * D + leq * 16 + c * 8) : u32x4{0, 0, 0, 0};
+        }
+        if (tid < WIN) {
+            int dl = k0 - q0 - (BQ - 1) + tid; // key - query of window slot tid
+            dl = dl < -a.N ? -a.N : (dl > a.N ? a.N : dl);
+            wreg = has_p ? a.rab_p[h * a.rp_hs + dl + a.N] : 0.f;
+        }
+        if (tid < BQ) {
+            const int q = q0 + tid;
+            treg = (has_t && !wide && q < L) ? a.rel[o_b + q] : 0u;
+            treg64 = (wide && q < L) ? a.ts[o_b + q] : 0;
+        }
+    };
+    auto sstore = [&](int buf) {
+        Stage &S = sm.st[buf];
+#pragma unroll
+        for (int c = 0; c < 2; c++) {
+            *(u32x4 *)&S.q[lcq * RS + leq * 16 + c * 8] = qreg2[c];
+            *(u32x4 *)&S.dO[lcq * RS + leq * 16 + c * 8] = dreg2[c];
+            *(u32x4 *)&S.dOl[lcq * RS + leq * 16 + c * 8] = lreg2[c];
+        }
+        if (tid < WIN) S.win[tid] = wreg;
+        if (tid < BQ) {
+            S.qt[tid] = treg;
+            S.qt64[tid] = treg64;
+        }
+    };
+
+    const int nqb = (L - k0 + BQ - 1) / BQ; // query blocks [k0, L)
+    if (nqb > 0) {
+        gload(k0);
+        sstore(0);
+    }
+    __syncthreads();
+
+    const int tj = l & 15, ts_ = tj >> 2;
+    const int cpart = ((l >> 4) & 1) * 16 + 4 * (tj & 3);
+    const int p_hs = a.rp_hs > 0 ? (int)a.rp_hs : 2 * a.N + 1;
+    const int t_hs = a.rt_hs > 0 ? (int)a.rt_hs : 128;
+
+    for (int n = 0; n < nqb; n++) {
+        const int q0 = k0 + n * BQ;
+        if (n + 1 < nqb) gload(q0 + BQ);
+        const Stage &S = sm.st[n & 1];
+        const int kw0 = k0 + 32 * w; // this wave's first key
+        const bool skip = kw0 > q0 + BQ - 1 || kw0 >= L;
+        const bool diag = kw0 + 31 > q0;
+        if (!skip) {
+            floatx16 sacc, pacc;
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                sacc[r] = 0.f;
+                pacc[r] = 0.f;
+            }
+#pragma unroll
+            for (int s = 0; s < 8; s++) {
+                const bf16x8 qa = *(const bf16x8 *)&S.q[lq * RS + s * 16 + g * 8];
+                const bf16x8 da = *(const bf16x8 *)&S.dO[lq * RS + s * 16 + g * 8];
+                const bf16x8 dl = *(const bf16x8 *)&S.dOl[lq * RS + s * 16 + g * 8];
+                sacc = mfma32(qa, kreg[s], sacc);
+                pacc = mfma32(da, vreg[s], pacc);
+                pacc = mfma32(dl, vreg[s], pacc);
+            }
+            // register r <-> query q0 + ql(r), ql = 8(r/4) + 4g + r%4; key = mykey
+            uint32_t ppk[8], dpk[8];
+            const int wb = 32 * w + lq + (BQ - 1); // window index = wb - ql
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                float pp[2], dd[2];
+#pragma unroll
+                for (int u = 0; u < 2; u++) {
+                    const int rr = r + u;
+                    const int ql = 8 * (rr >> 2) + 4 * g + (rr & 3);
+                    float x = sacc[rr];
+                    if (has_p) x += S.win[wb - ql];
+                    int bucket = 0;
+                    if (has_t) {
+                        if (!wide) {
+                            const uint32_t tq = S.qt[ql];
+                            const uint32_t dd1 = (tq > tk ? tq - tk : tk - tq) + 1u;
+                            const int cz = __builtin_clz(dd1);
+                            x += sm.rabt_rev[cz];
+                            bucket = 31 - cz;
+                        } else {
+                            bucket = time_bucket64(S.qt64[ql] - tk64);
+                            x += sm.rabt[bucket];
+                        }
+                    }
+                    const float e = __builtin_amdgcn_exp2f(x * -1.4426950408889634f);
+                    const float sg = __builtin_amdgcn_rcpf(1.0f + e);
+                    float p = x * sg;
+                    float ds = pacc[rr] * sg * (1.0f + x * (1.0f - sg));
+                    if (diag && mykey > q0 + ql) {
+                        p = 0.f;
+                        ds = 0.f;
+                    }
+                    pp[u] = p;
+                    dd[u] = ds;
+                    if (ds != 0.f) {
+                        if (a.drab_p) atomicAdd(&sm.ring[(mykey - (q0 + ql)) & (RING - 1)], ds);
+                        if (a.drab_t && has_t) atomicAdd(&sm.dtab[w][lq & (TCOPY - 1)][bucket], ds);
+                    }
+                }
+                ppk[r >> 1] = pack2_bf16(pp[0], pp[1]);
+                dpk[r >> 1] = pack2_bf16(dd[0], dd[1]);
+            }
+            // dV^T += dO'^T P and dK^T += Q^T dS  (contraction over the 32 queries)
+#pragma unroll
+            for (int m = 0; m < 2; m++) {
+                const bf16x8 pb = as_bf16x8(u32x4{ppk[4 * m], ppk[4 * m + 1], ppk[4 * m + 2], ppk[4 * m + 3]});
+                const bf16x8 sb = as_bf16x8(u32x4{dpk[4 * m], dpk[4 * m + 1], dpk[4 * m + 2], dpk[4 * m + 3]});
+                const int qr1 = 16 * m + 4 * g + ts_; // query row of the transposing read
+#pragma unroll
+                for (int db = 0; db < 4; db++) {
+                    const u32x2 d1 = lds_read_tr(&S.dO[qr1 * RS + db * 32 + cpart]);
+                    const u32x2 d2 = lds_read_tr(&S.dO[(qr1 + 8) * RS + db * 32 + cpart]);
+                    dv_acc[db] = mfma32(as_bf16x8(u32x4{d1[0], d1[1], d2[0], d2[1]}), pb, dv_acc[db]);
+                    const u32x2 q1 = lds_read_tr(&S.q[qr1 * RS + db * 32 + cpart]);
+                    const u32x2 q2 = lds_read_tr(&S.q[(qr1 + 8) * RS + db * 32 + cpart]);
+                    dk_acc[db] = mfma32(as_bf16x8(u32x4{q1[0], q1[1], q2[0], q2[1]}), sb, dk_acc[db]);
+                }
+            }
+            // dS -> LDS as [key][query]: lane writes 4 queries (r%4) per r/4 group
+            const int krow = 32 * w + lq;
+#pragma unroll
+            for (int gr = 0; gr < 4; gr++) {
+                const u32x2 v2 = {dpk[2 * gr], dpk[2 * gr + 1]};
+                *(u32x2 *)&sm.ds[krow * SS + 8 * gr + 4 * g] = v2;
+            }
+        } else {
+            const int krow = 32 * w + lq;
+#pragma unroll
+            for (int gr = 0; gr < 4; gr++) *(u32x2 *)&sm.ds[krow * SS + 8 * gr + 4 * g] = u32x2{0u, 0u};
+        }
+        __syncthreads();
+        // dQ[32 queries][d-block w] = sum over the 128 keys of dS[q][key] K[key][d]
+        {
+            floatx16 qacc;
+#pragma unroll
+            for (int r = 0; r < 16; r++) qacc[r] = 0.f;
+#pragma unroll
+            for (int t = 0; t < BN / 16; t++) {
+                // A: dS[q = lq][keys 16t + 8g..], from ds[key][q]; B: K[keys][d = 32w + lq]
+                const int kr1 = 16 * t + 8 * g + ts_; // keys 16t + 8g + e, e = 0..7 (natural order)
+                const u32x2 s1 = lds_read_tr(&sm.ds[kr1 * SS + cpart]);
+                const u32x2 s2 = lds_read_tr(&sm.ds[(kr1 + 4) * SS + cpart]);
+                const u32x2 k1 = lds_read_tr(&sm.k[kr1 * RS + 32 * w + cpart]);
+                const u32x2 k2 = lds_read_tr(&sm.k[(kr1 + 4) * RS + 32 * w + cpart]);
+                qacc = mfma32(as_bf16x8(u32x4{s1[0], s1[1], s2[0], s2[1]}),
+                              as_bf16x8(u32x4{k1[0], k1[1], k2[0], k2[1]}), qacc);
+            }
+            // C layout: lane holds d = 32w + lq, queries 8(r/4) + 4g + r%4
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int qi = q0 + 8 * (r >> 2) + 4 * g + (r & 3);
+                if (qi < L) atomicAdd(&a.dq_acc[(int64_t)(o_b + qi) * ld_do + h * D + 32 * w + lq], qacc[r]);
+            }
+        }
+        // flush drab_p ring entries no later block can reach: key - query in
+        // (k0 + BN - 1 - (q0 + BQ), k0 + BN - 1 - q0]
+        if (a.drab_p && tid < BQ) {
+            const int dl = k0 + BN - 1 - q0 - tid;
+            const int slot = dl & (RING - 1);
+            const float v = sm.ring[slot];
+            if (v != 0.f) {
+                int c = dl < -a.N ? -a.N : (dl > a.N ? a.N : dl);
+                atomicAdd(&a.drab_p[h * p_hs + c + a.N], v);
+            }
+            sm.ring[slot] = 0.f;
+        }
+        if (n + 1 < nqb) sstore((n + 1) & 1);
+        __syncthreads();
+    }
+    // flush what is left in the ring and the time tables
+    if (a.drab_p && nqb > 0) {
+        const int qlast = k0 + (nqb - 1) * BQ;
+        // remaining key - query values: [k0 - qlast - (BQ - 1), k0 + BN - 1 - qlast - BQ]
+        const int lo = k0 - qlast - (BQ - 1), hi = k0 + BN - 1 - qlast - BQ;
+        for (int dl = lo + tid; dl <= hi; dl += NT) {
+            const float v = sm.ring[dl & (RING - 1)];
+            if (v != 0.f) {
+                int c = dl < -a.N ? -a.N : (dl > a.N ? a.N : dl);
+                atomicAdd(&a.drab_p[h * p_hs + c + a.N], v);
+            }
+        }
+    }
+    if (a.drab_t && has_t && tid < TB) {
+        float s = 0.f;
+        for (int ww = 0; ww < 4; ww++)
+            for (int c = 0; c < TCOPY; c++) s += sm.dtab[ww][c][tid];
+        if (s != 0.f) atomicAdd(&a.drab_t[h * t_hs + tid], s);
+    }
+    // dK^T, dV^T: lane holds key mykey, d = 32 db + 8(r/4) + 4g + r%4
+    if (kvalid) {
+        const int64_t row = o_b + mykey;
+#pragma unroll
+        for (int db = 0; db < 4; db++)
+#pragma unroll
+            for (int gr = 0; gr < 4; gr++) {
+                const int d0 = db * 32 + 8 * gr + 4 * g;
+                const u32x2 kk = {pack2_bf16(dk_acc[db][4 * gr], dk_acc[db][4 * gr + 1]),
+                                  pack2_bf16(dk_acc[db][4 * gr + 2], dk_acc[db][4 * gr + 3])};
+                const u32x2 vv = {pack2_bf16(dv_acc[db][4 * gr], dv_acc[db][4 * gr + 1]),
+                                  pack2_bf16(dv_acc[db][4 * gr + 2], dv_acc[db][4 * gr + 3])};
+                *(u32x2 *)(a.dk + row * a.lddk + h * D + d0) = kk;
+                *(u32x2 *)(a.dv + row * a.lddv + h * D + d0) = vv;
+            }
+    }
+}
+
+hipError_t launch_attn_bwd_bf16(const AttnBwdArgs &a, int max_items, hipStream_t st)
+{
+    static bool init = false;
+    const size_t smem = sizeof(Smem);
+    if (!init) {
+        hipError_t e = hipFuncSetAttribute((const void *)attn_bwd_bf16_kernel,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        if (e != hipSuccess) return e;
+        init = true;
+    }
+    if (max_items <= 0) return hipSuccess;
+    hipLaunchKernelGGL(attn_bwd_bf16_kernel, dim3(max_items), dim3(NT), smem, st, a);
+    return hipGetLastError();
+}

@@ -73,7 +73,9 @@ __global__ void __launch_bounds__(256) ln_gate_fwd_kernel(const float *__restric
 // Backward of G = xhat (.) U, xhat = (O - mean) * rstd:
 //   dU = xhat (.) dG ;  dxhat = dG (.) U ;
 //   dO = rstd * (dxhat - mean(dxhat) - xhat * mean(dxhat (.) xhat)),
-// written as bf16 dO * scale (scale = 1/N_max folds phi2's normaliser).
+// written as dO * scale (scale = 1/N_max folds phi2's normaliser) in two bf16
+// planes, hi = bf16(x) and lo = bf16(x - hi), so that products with dO keep
+// ~16 significant bits: plane hi at dO[0 .. T*F), plane lo at dO[T*F .. 2*T*F).
 template <int VPL, bool BF>
 __global__ void __launch_bounds__(256) ln_gate_bwd_kernel(const void *__restrict__ dG, int64_t ldg, const void *__restrict__ U,
                                                           int64_t ldu, const float *__restrict__ O, int64_t ldo,
@@ -106,7 +108,10 @@ __global__ void __launch_bounds__(256) ln_gate_bwd_kernel(const void *__restrict
     for (int i = 0; i < VPL; i++) {
         const int c = lane * VPL + i;
         if (c >= F) continue;
-        dO[(int64_t)row * F + c] = to_bf16(rstd * (dxh[i] - m1 - xh[i] * m2) * scale);
+        const float g = rstd * (dxh[i] - m1 - xh[i] * m2) * scale;
+        const bf16 hi = to_bf16(g);
+        dO[(int64_t)row * F + c] = hi;
+        dO[(int64_t)T * F + (int64_t)row * F + c] = to_bf16(g - from_bf16(hi));
     }
 }
 

@@ -48,7 +48,8 @@ hipError_t launch_ln_gate_bwd(const void *dG, int64_t ldg, const void *U, int64_
 struct AttnBwdArgs {
     const bf16 *q, *k, *v;
     int64_t ldq, ldk, ldv;
-    const bf16 *dO;             // dO / N_max, [T][H*d] bf16 (ld = H*d)
+    const bf16 *dO;             // dO / N_max as bf16 hi plane [T][H*d], then lo plane [T][H*d]
+    int T;
     const int32_t *offsets;
     const int64_t *ts;
     const uint32_t *rel;
@@ -74,6 +75,8 @@ hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st);
 hipError_t launch_cast_f32_to_bf16(const float *src, int64_t lds, bf16 *dst, int64_t ldd, int rows, int cols,
                                    const int *status, hipStream_t st);
 hipError_t launch_copy_f32(const float *src, float *dst, size_t n, hipStream_t st);
+hipError_t launch_scale_bf16(const bf16 *src, int64_t lds, bf16 *dst, int64_t ldd, int rows, int cols, float scale,
+                             hipStream_t st);
 
 // ---- GEMM with fused epilogues (gemm.hip)
 // C[M][N] = epi(A[M][K] . W[N][K]^T + bias) (+ R), A/W/C storage dtype or fp32.

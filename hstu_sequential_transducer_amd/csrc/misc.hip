@@ -58,3 +58,30 @@ hipError_t launch_copy_f32(const float *src, float *dst, size_t n, hipStream_t s
     hipLaunchKernelGGL(copy_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, st, src, dst, n);
     return hipGetLastError();
 }
+
+__global__ void __launch_bounds__(256) scale_bf16_kernel(const bf16 *__restrict__ src, int64_t lds, bf16 *__restrict__ dst,
+                                                         int64_t ldd, int rows, int cols, float scale)
+{
+    const int64_t n = (int64_t)rows * cols;
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (; i < n; i += stride) {
+        const int64_t r = i / cols, c = i % cols;
+        const float x = from_bf16(src[r * lds + c]) * scale;
+        const bf16 hi = to_bf16(x);
+        dst[r * ldd + c] = hi;
+        dst[n + r * ldd + c] = to_bf16(x - from_bf16(hi)); // lo plane (ldd == cols)
+    }
+}
+
+hipError_t launch_scale_bf16(const bf16 *src, int64_t lds, bf16 *dst, int64_t ldd, int rows, int cols, float scale,
+                             hipStream_t st)
+{
+    const int64_t n = (int64_t)rows * cols;
+    if (n <= 0) return hipSuccess;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(scale_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, st, src, lds, dst, ldd, rows, cols,
+                       scale);
+    return hipGetLastError();
+}

@@ -150,6 +150,23 @@ def attn_bwd(offsets, ts, q, k, v, rab_p, rab_t, n_max: int, U, eps: float, dout
     return res
 
 
+def attn_bwd_dq_rows(offsets, ts, q, k, v, rab_p, rab_t, n_max: int, U, eps: float, dout, rows):
+    """dq of the listed token rows only (same chain as attn_bwd).  Returns
+    [len(rows)][H][dqk]."""
+    lib = _load()
+    off = _i32(offsets)
+    B = len(off) - 1
+    q, k, v = _d(q), _d(k), _d(v)
+    T, H, dqk = q.shape
+    rows_a = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.zeros((len(rows_a), H, dqk))
+    lib.oracle_attn_bwd_dq_rows(ctypes.c_int(B), _p(off), _p(_i64(ts)), ctypes.c_int(H), ctypes.c_int(dqk),
+                                ctypes.c_int(v.shape[2]), ctypes.c_int64(n_max), _p(_d(rab_p)), _p(_d(rab_t)), _p(q),
+                                _p(k), _p(v), _p(_d(U)), ctypes.c_double(eps), _p(_d(dout)),
+                                ctypes.c_int64(len(rows_a)), _p(rows_a), _p(out))
+    return out
+
+
 def layer_fwd(offsets, ts, x, layer, heads: int, d: int, n_max: int, phi1: int = 0, eps: float = 1e-5,
               return_kv: bool = False):
     """One HSTU layer (Eq. 1-3 + residual).  ``layer`` has w1 [4Hd][D], b1,

@@ -261,6 +261,68 @@ void oracle_attn_bwd(int B, const int32_t *off, const int64_t *ts, int H, int dq
     free(dO);
 }
 
+/*
+ * dq for a subset of token rows only (same chain as oracle_attn_bwd, restricted
+ * to what those rows need): for each listed row r = o_b + i, recompute O_r
+ * (all heads), the epilogue's dO_r (when U is given), then
+ *   dq[r] = sum_{j <= i} dP_ij SiLU'(s_ij) k_j,  dP_ij = dO_r . v_j / N.
+ * dq_rows: [n_rows][H][dqk].
+ */
+void oracle_attn_bwd_dq_rows(int B, const int32_t *off, const int64_t *ts, int H, int dqk, int dv, int64_t N,
+                             const double *rab_p, const double *rab_t, const double *q, const double *k,
+                             const double *v, const double *U, double eps, const double *dout, int64_t n_rows,
+                             const int64_t *rows, double *dq_rows)
+{
+    int F = H * dv;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t ri = 0; ri < n_rows; ri++) {
+        int64_t r = rows[ri];
+        int b = seq_of(B, off, r);
+        int64_t o_b = off[b], i = r - o_b;
+        double *O = (double *)malloc(sizeof(double) * F);
+        double *dO = (double *)malloc(sizeof(double) * F);
+        oracle_attn_fwd(B, off, ts, H, dqk, dv, N, rab_p, rab_t, q, k, v, O, 1, &r);
+        if (U) {
+            double mu = 0.0, var = 0.0;
+            for (int c = 0; c < F; c++) mu += O[c];
+            mu /= F;
+            for (int c = 0; c < F; c++) var += (O[c] - mu) * (O[c] - mu);
+            var /= F;
+            double rstd = 1.0 / sqrt(var + eps), m1 = 0.0, m2 = 0.0;
+            for (int c = 0; c < F; c++) {
+                double xh = (O[c] - mu) * rstd, dxh = dout[r * F + c] * U[r * F + c];
+                m1 += dxh;
+                m2 += dxh * xh;
+            }
+            m1 /= F;
+            m2 /= F;
+            for (int c = 0; c < F; c++) {
+                double xh = (O[c] - mu) * rstd, dxh = dout[r * F + c] * U[r * F + c];
+                dO[c] = rstd * (dxh - m1 - xh * m2);
+            }
+        } else {
+            for (int c = 0; c < F; c++) dO[c] = dout[r * F + c];
+        }
+        for (int h = 0; h < H; h++) {
+            double *dqr = dq_rows + (ri * H + h) * dqk;
+            for (int c = 0; c < dqk; c++) dqr[c] = 0.0;
+            for (int64_t j = 0; j <= i; j++) {
+                int64_t rk = o_b + j;
+                const double *qi = q + (r * H + h) * dqk, *kj = k + (rk * H + h) * dqk;
+                double s = pair_logit(qi, kj, dqk, i, j, N, h, rab_p, rab_t, ts ? ts[r] : 0, ts ? ts[rk] : 0,
+                                      ts != NULL);
+                double dp = 0.0;
+                for (int c = 0; c < dv; c++) dp += dO[h * dv + c] * v[(rk * H + h) * dv + c];
+                dp /= (double)N;
+                double ds = dp * silu_grad(s);
+                for (int c = 0; c < dqk; c++) dqr[c] += ds * kj[c];
+            }
+        }
+        free(O);
+        free(dO);
+    }
+}
+
 /* Activation phi1: 0 = SiLU, 1 = ReLU. */
 static double act(int phi1, double z) { return phi1 == 1 ? (z > 0.0 ? z : 0.0) : silu(z); }
 

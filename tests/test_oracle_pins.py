@@ -325,6 +325,20 @@ def test_bwd_finite_differences(with_u):
         assert err < 1e-6, (name, err)
 
 
+@pytest.mark.parametrize("with_u", [True, False])
+def test_bwd_dq_rows_equal_full_backward(with_u):
+    rng = np.random.default_rng(22)
+    c = rand_case(rng, B=3, Lmax=20, H=2, d=4, monotone_ts=True)
+    T = int(c["off"][-1])
+    U = rng.standard_normal((T, c["H"] * c["d"])) if with_u else None
+    dG = rng.standard_normal((T, c["H"] * c["d"]))
+    g = oracle.attn_bwd(c["off"], c["ts"], c["q"], c["k"], c["v"], c["rab_p"], c["rab_t"], c["N"], U, 1e-5, dG)
+    rows = rng.choice(T, size=min(7, T), replace=False)
+    sub = oracle.attn_bwd_dq_rows(c["off"], c["ts"], c["q"], c["k"], c["v"], c["rab_p"], c["rab_t"], c["N"], U, 1e-5,
+                                  dG, rows)
+    assert np.allclose(sub, g["dq"][rows], rtol=1e-12, atol=1e-12)
+
+
 def test_bwd_identities():
     """Every ds_ij lands once in each table: sum(drab_p[h]) = sum(drab_t[h]);
     and sum_i dq_i . q_i = sum_j dk_j . k_j per head (both = sum ds_ij q_i.k_j)."""
