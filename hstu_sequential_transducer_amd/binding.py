@@ -22,7 +22,7 @@ HSTU_ACT_SILU, HSTU_ACT_RELU = 0, 1
 OP_ATTN_FWD, OP_ATTN_BWD, OP_LAYER_FWD, OP_MFALCON = range(4)
 
 EXPORTED = ["hstu_attn_fwd", "hstu_attn_bwd", "hstu_layer_fwd", "mfalcon_score", "hstu_workspace_size",
-            "hstu_last_error", "hstu_abi_version"]
+            "hstu_profile_enable", "hstu_profile_collect", "hstu_last_error", "hstu_abi_version"]
 
 
 class HstuError(RuntimeError):
@@ -59,6 +59,10 @@ class Layer(ctypes.Structure):
                 ("rab", Bias), ("phi1", ctypes.c_int)]
 
 
+class KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int32), ("total_ms", ctypes.c_double)]
+
+
 _lib = None
 
 
@@ -89,8 +93,23 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mfalcon_score.argtypes = [P(Jagged), P(Dims), ctypes.c_int32, ctypes.c_int32, P(Layer), P(CMat), P(CMat),
                                   ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, CMat, ctypes.c_int32,
                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.hstu_profile_enable.restype = None
+    lib.hstu_profile_enable.argtypes = [ctypes.c_int32]
+    lib.hstu_profile_collect.restype = ctypes.c_int32
+    lib.hstu_profile_collect.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int32]
     _lib = lib
     return lib
+
+
+def profile_enable(on: bool = True):
+    load_library().hstu_profile_enable(1 if on else 0)
+
+
+def profile_collect():
+    """{kernel name: (launches, total ms)} since the previous collect."""
+    arr = (KernelTime * 64)()
+    n = load_library().hstu_profile_collect(arr, 64)
+    return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms) for i in range(n)}
 
 
 def abi_version() -> int:

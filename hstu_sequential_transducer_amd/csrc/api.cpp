@@ -4,6 +4,7 @@
 // copies device data to the host.
 #include "../../include/hstu.h"
 #include "kernels.h"
+#include "profile.h"
 
 #include <cstdarg>
 #include <cstdio>
@@ -215,7 +216,10 @@ hstu_status hstu_attn_fwd(const hstu_jagged *j, const hstu_dims *dm, const hstu_
     int32_t *wide = (int32_t *)(wb + w.wide);
     const int T = j->total, B = j->batch;
     const int max_items = max_items_for(B, T, tile, H);
-    launch_sched(j->offsets, j->ts, B, T, tile, H, status, n_items, items, max_items, rel, wide, st);
+    {
+        ProfScope ps("sched_kernel", st);
+        launch_sched(j->offsets, j->ts, B, T, tile, H, status, n_items, items, max_items, rel, wide, st);
+    }
     TRY(launched(hipGetLastError(), "schedule kernel"));
 
     AttnFwdArgs a{};
@@ -251,11 +255,18 @@ hstu_status hstu_attn_fwd(const hstu_jagged *j, const hstu_dims *dm, const hstu_
         a.o16 = out.ptr;
         a.ld_o16 = out.ld;
     }
-    hipError_t e = dm->dtype == HSTU_BF16 ? launch_attn_fwd_bf16(a, max_items, st) : launch_attn_fwd_f32(a, max_items, st);
+    hipError_t e;
+    {
+        ProfScope ps(dm->dtype == HSTU_BF16 ? "attn_fwd_bf16_kernel" : "attn_fwd_f32_kernel", st);
+        e = dm->dtype == HSTU_BF16 ? launch_attn_fwd_bf16(a, max_items, st) : launch_attn_fwd_f32(a, max_items, st);
+    }
     TRY(launched(e, "attention forward kernel"));
     if (u.ptr) {
-        e = launch_ln_gate_fwd(obuf, F, 1, 0, u.ptr, u.ld, dm->dtype == HSTU_BF16, out.ptr, out.ld, ln_stats, nullptr, 0,
-                               T, F, dm->ln_eps, status, st);
+        {
+            ProfScope ps("ln_gate_fwd_kernel", st);
+            e = launch_ln_gate_fwd(obuf, F, 1, 0, u.ptr, u.ld, dm->dtype == HSTU_BF16, out.ptr, out.ld, ln_stats, nullptr,
+                                   0, T, F, dm->ln_eps, status, st);
+        }
         TRY(launched(e, "LayerNorm gate kernel"));
     }
     TRY(debug_check(ws, st));
@@ -304,17 +315,25 @@ hstu_status hstu_attn_bwd(const hstu_jagged *j, const hstu_dims *dm, const hstu_
     const int max_items = max_items_for(B, T, BWD_BN, H);
     const int64_t p_hs = has_p ? bias->rab_p_hstride : 2 * (int64_t)N + 1;
     const int64_t t_hs = (bias && bias->rab_t) ? bias->rab_t_hstride : 128;
-    launch_sched(j->offsets, j->ts, B, T, BWD_BN, H, status, n_items, items, max_items, rel, wide, st);
+    {
+        ProfScope ps("sched_kernel", st);
+        launch_sched(j->offsets, j->ts, B, T, BWD_BN, H, status, n_items, items, max_items, rel, wide, st);
+    }
     TRY(launched(hipGetLastError(), "schedule kernel"));
-    TRY(launched(launch_fill_zero(dq_acc, (size_t)T * H * d * 4, st), "zero fill"));
-    if (drab_p) TRY(launched(launch_fill_zero(drab_p, (size_t)H * p_hs * 4, st), "zero fill"));
-    if (drab_t) TRY(launched(launch_fill_zero(drab_t, (size_t)H * t_hs * 4, st), "zero fill"));
+    {
+        ProfScope ps("fill_zero_kernel", st);
+        TRY(launched(launch_fill_zero(dq_acc, (size_t)T * H * d * 4, st), "zero fill"));
+        if (drab_p) TRY(launched(launch_fill_zero(drab_p, (size_t)H * p_hs * 4, st), "zero fill"));
+        if (drab_t) TRY(launched(launch_fill_zero(drab_t, (size_t)H * t_hs * 4, st), "zero fill"));
+    }
     const float inv_n = 1.0f / (float)N;
     if (u.ptr) {
+        ProfScope ps("ln_gate_bwd_kernel", st);
         TRY(launched(launch_ln_gate_bwd(dout.ptr, dout.ld, u.ptr, u.ld, o_save, F, ln_stats, true, du.ptr, du.ld, dO,
                                         inv_n, T, F, status, st),
                      "LayerNorm gate backward kernel"));
     } else {
+        ProfScope ps("scale_bf16_kernel", st);
         TRY(launched(launch_scale_bf16((const bf16 *)dout.ptr, dout.ld, dO, F, T, F, inv_n, st), "scale kernel"));
     }
     AttnBwdArgs a{};
@@ -345,9 +364,15 @@ hstu_status hstu_attn_bwd(const hstu_jagged *j, const hstu_dims *dm, const hstu_
     a.lddv = dv.ld;
     a.drab_p = drab_p;
     a.drab_t = has_t ? drab_t : nullptr;
-    TRY(launched(launch_attn_bwd_bf16(a, max_items, st), "attention backward kernel"));
-    TRY(launched(launch_cast_f32_to_bf16(dq_acc, (int64_t)H * d, (bf16 *)dq.ptr, dq.ld, T, H * d, status, st),
-                 "cast kernel"));
+    {
+        ProfScope ps("attn_bwd_bf16_kernel", st);
+        TRY(launched(launch_attn_bwd_bf16(a, max_items, st), "attention backward kernel"));
+    }
+    {
+        ProfScope ps("cast_kernel", st);
+        TRY(launched(launch_cast_f32_to_bf16(dq_acc, (int64_t)H * d, (bf16 *)dq.ptr, dq.ld, T, H * d, status, st),
+                     "cast kernel"));
+    }
     TRY(debug_check(ws, st));
     return ok();
 }

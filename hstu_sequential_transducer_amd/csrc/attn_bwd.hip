@@ -17,9 +17,14 @@
 // (lane = key, registers = queries), the element-wise step, dV^T += dO'^T P
 // and dK^T += Q^T dS (transposing LDS reads for dO'^T and Q^T), and writes dS
 // to LDS; then wave w computes dQ for d-block w over all 128 keys and adds it
-// to an fp32 accumulator with global atomics.  drab_p is summed in an LDS
-// ring indexed by j - i and flushed with one atomic per entry once no later
-// block can touch it; drab_t goes through per-wave LDS tables.
+// to an fp32 accumulator with global atomics.  drab_p: each wave also writes
+// its fp32 dS into an LDS tile skewed by j - i ([query][key - query]), one
+// thread per diagonal sums it into an LDS ring indexed by j - i, and an entry
+// is flushed with one global atomic once no later block can touch it.
+// drab_t: when every pair of a 32x32 block falls in one time bucket (checked
+// per block from the min/max times of its queries and keys) the bucket's bias
+// is a scalar and the block's dS is summed by a wave reduction; otherwise
+// per-element adds go to per-wave LDS tables.
 #include "kernels.h"
 
 namespace {
@@ -32,6 +37,7 @@ constexpr int RS = 136;    // LDS row stride (bf16) of Q, dO and K tiles
 constexpr int SS = 40;     // LDS row stride (bf16) of the dS tile [key][query]
 constexpr int WIN = 160;   // rab_p window per block (BQ + BN - 1 used)
 constexpr int RING = 256;  // drab_p ring (power of two >= WIN + BQ)
+constexpr int DK = 160;    // columns of the skewed dS tile: key - query + BQ - 1
 constexpr int TB = 64;     // time buckets that int64 differences can reach
 constexpr int TCOPY = 4;   // copies of each wave's drab_t table
 
@@ -42,11 +48,13 @@ struct Stage {
     float win[WIN];
     uint32_t qt[BQ];
     int64_t qt64[BQ];
+    uint32_t qtmin, qtmax; // over the block's valid queries
 };
 struct Smem {
     bf16 k[BN * RS];
     Stage st[2];
     bf16 ds[BN * SS];
+    float dsk[BQ * DK]; // fp32 dS skewed: [query][key - query + BQ - 1]
     float ring[RING];
     float dtab[4][TCOPY][TB];
     float rabt_rev[32];
@@ -113,6 +121,12 @@ __global__ void __launch_bounds__(NT) attn_bwd_bf16_kernel(AttnBwdArgs a)
     }
     const uint32_t tk = (has_t && !wide && kvalid) ? a.rel[o_b + mykey] : 0u;
     const int64_t tk64 = (wide && kvalid) ? a.ts[o_b + mykey] : 0;
+    // time range of this wave's valid keys (for the uniform-bucket test)
+    uint32_t tkmin = kvalid ? tk : 0xFFFFFFFFu, tkmax = kvalid ? tk : 0u;
+    for (int o = 32; o >= 1; o >>= 1) {
+        tkmin = min(tkmin, (uint32_t)__shfl_xor((int)tkmin, o, 64));
+        tkmax = max(tkmax, (uint32_t)__shfl_xor((int)tkmax, o, 64));
+    }
 
     floatx16 dv_acc[4], dk_acc[4];
 #pragma unroll
@@ -128,7 +142,7 @@ __global__ void __launch_bounds__(NT) attn_bwd_bf16_kernel(AttnBwdArgs a)
     u32x4 qreg2[2], dreg2[2], lreg2[2];
     const bf16 *dOlo = dO + (int64_t)a.T * ld_do;
     float wreg = 0.f;
-    uint32_t treg = 0;
+    uint32_t treg = 0, tmn = 0xFFFFFFFFu, tmx = 0u;
     int64_t treg64 = 0;
     auto gload = [&](int q0) {
         const int qi = q0 + lcq;
@@ -145,10 +159,17 @@ __global__ void __launch_bounds__(NT) attn_bwd_bf16_kernel(AttnBwdArgs a)
             dl = dl < -a.N ? -a.N : (dl > a.N ? a.N : dl);
             wreg = has_p ? a.rab_p[h * a.rp_hs + dl + a.N] : 0.f;
         }
-        if (tid < BQ) {
+        if (tid < 64) { // wave 0: query times and their range
             const int q = q0 + tid;
-            treg = (has_t && !wide && q < L) ? a.rel[o_b + q] : 0u;
-            treg64 = (wide && q < L) ? a.ts[o_b + q] : 0;
+            const bool okq = tid < BQ && q < L;
+            treg = (has_t && !wide && okq) ? a.rel[o_b + q] : 0u;
+            treg64 = (wide && okq) ? a.ts[o_b + q] : 0;
+            tmn = okq ? treg : 0xFFFFFFFFu;
+            tmx = okq ? treg : 0u;
+            for (int o = 32; o >= 1; o >>= 1) {
+                tmn = min(tmn, (uint32_t)__shfl_xor((int)tmn, o, 64));
+                tmx = max(tmx, (uint32_t)__shfl_xor((int)tmx, o, 64));
+            }
         }
     };
     auto sstore = [&](int buf) {
@@ -163,6 +184,10 @@ __global__ void __launch_bounds__(NT) attn_bwd_bf16_kernel(AttnBwdArgs a)
         if (tid < BQ) {
             S.qt[tid] = treg;
             S.qt64[tid] = treg64;
+        }
+        if (tid == 0) {
+            S.qtmin = tmn;
+            S.qtmax = tmx;
         }
     };
 
@@ -202,20 +227,37 @@ __global__ void __launch_bounds__(NT) attn_bwd_bf16_kernel(AttnBwdArgs a)
                 pacc = mfma32(dl, vreg[s], pacc);
             }
             // register r <-> query q0 + ql(r), ql = 8(r/4) + 4g + r%4; key = mykey
+            // Uniform time bucket over the block: |t_q - t_k| spans [lo, hi].
+            bool uni = false;
+            int ubk = 0;
+            if (has_t && !wide && S.qtmin <= S.qtmax && tkmin <= tkmax) {
+                const int64_t a1 = (int64_t)S.qtmin - (int64_t)tkmax, a2 = (int64_t)S.qtmax - (int64_t)tkmin;
+                const int64_t lo = a1 > 0 ? a1 : (a2 < 0 ? -a2 : 0);
+                const int64_t hi = (a1 < 0 ? -a1 : a1) > (a2 < 0 ? -a2 : a2) ? (a1 < 0 ? -a1 : a1) : (a2 < 0 ? -a2 : a2);
+                const int blo = floor_log2_u32((uint32_t)lo + 1u), bhi = floor_log2_u32((uint32_t)hi + 1u);
+                uni = blo == bhi;
+                ubk = blo;
+            }
+            const float ubias = uni ? sm.rabt[ubk] : 0.f;
+            float tsum = 0.f;
             uint32_t ppk[8], dpk[8];
             const int wb = 32 * w + lq + (BQ - 1); // window index = wb - ql
+            float *dskl = &sm.dsk[4 * g * DK + 32 * w + lq + (BQ - 1) - 4 * g];
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
                 float pp[2], dd[2];
 #pragma unroll
                 for (int u = 0; u < 2; u++) {
                     const int rr = r + u;
-                    const int ql = 8 * (rr >> 2) + 4 * g + (rr & 3);
+                    const int cr = 8 * (rr >> 2) + (rr & 3); // ql - 4g
+                    const int ql = cr + 4 * g;
                     float x = sacc[rr];
                     if (has_p) x += S.win[wb - ql];
                     int bucket = 0;
                     if (has_t) {
-                        if (!wide) {
+                        if (uni) {
+                            x += ubias;
+                        } else if (!wide) {
                             const uint32_t tq = S.qt[ql];
                             const uint32_t dd1 = (tq > tk ? tq - tk : tk - tq) + 1u;
                             const int cz = __builtin_clz(dd1);
@@ -236,13 +278,19 @@ __global__ void __launch_bounds__(NT) attn_bwd_bf16_kernel(AttnBwdArgs a)
                     }
                     pp[u] = p;
                     dd[u] = ds;
-                    if (ds != 0.f) {
-                        if (a.drab_p) atomicAdd(&sm.ring[(mykey - (q0 + ql)) & (RING - 1)], ds);
-                        if (a.drab_t && has_t) atomicAdd(&sm.dtab[w][lq & (TCOPY - 1)][bucket], ds);
+                    // skewed tile: row ql, column key_local - ql + BQ - 1
+                    dskl[cr * (DK - 1)] = ds;
+                    if (a.drab_t && has_t) {
+                        if (uni) tsum += ds;
+                        else if (ds != 0.f) atomicAdd(&sm.dtab[w][lq & (TCOPY - 1)][bucket], ds);
                     }
                 }
                 ppk[r >> 1] = pack2_bf16(pp[0], pp[1]);
                 dpk[r >> 1] = pack2_bf16(dd[0], dd[1]);
+            }
+            if (a.drab_t && uni) {
+                tsum = wave_sum(tsum);
+                if (l == 0) sm.dtab[w][0][ubk] += tsum;
             }
             // dV^T += dO'^T P and dK^T += Q^T dS  (contraction over the 32 queries)
 #pragma unroll
@@ -271,6 +319,9 @@ __global__ void __launch_bounds__(NT) attn_bwd_bf16_kernel(AttnBwdArgs a)
             const int krow = 32 * w + lq;
 #pragma unroll
             for (int gr = 0; gr < 4; gr++) *(u32x2 *)&sm.ds[krow * SS + 8 * gr + 4 * g] = u32x2{0u, 0u};
+            float *dskl = &sm.dsk[4 * g * DK + 32 * w + lq + (BQ - 1) - 4 * g];
+#pragma unroll
+            for (int rr = 0; rr < 16; rr++) dskl[(8 * (rr >> 2) + (rr & 3)) * (DK - 1)] = 0.f;
         }
         __syncthreads();
         // dQ[32 queries][d-block w] = sum over the 128 keys of dS[q][key] K[key][d]
@@ -296,17 +347,28 @@ __global__ void __launch_bounds__(NT) attn_bwd_bf16_kernel(AttnBwdArgs a)
                 if (qi < L) atomicAdd(&a.dq_acc[(int64_t)(o_b + qi) * ld_do + h * D + 32 * w + lq], qacc[r]);
             }
         }
-        // flush drab_p ring entries no later block can reach: key - query in
-        // (k0 + BN - 1 - (q0 + BQ), k0 + BN - 1 - q0]
-        if (a.drab_p && tid < BQ) {
-            const int dl = k0 + BN - 1 - q0 - tid;
+        // drab_p: thread c sums diagonal c of the skewed tile (key - query =
+        // k0 - q0 + c - (BQ - 1)) over the rows that hold a key of this tile,
+        // adds it into the ring, and flushes the entry once no later block can
+        // reach it (key - query > k0 + BN - 1 - (q0 + BQ)  <=>  c > BN - 2).
+        if (a.drab_p && tid < DK - 1) {
+            const int c = tid;
+            const int rlo = c < BQ - 1 ? BQ - 1 - c : 0;
+            const int rhi = c > BN - 1 ? BN + BQ - 2 - c : BQ - 1;
+            float sum = 0.f;
+            for (int rq = rlo; rq <= rhi; rq++) sum += sm.dsk[rq * DK + c];
+            const int dl = k0 - q0 + c - (BQ - 1);
             const int slot = dl & (RING - 1);
-            const float v = sm.ring[slot];
-            if (v != 0.f) {
-                int c = dl < -a.N ? -a.N : (dl > a.N ? a.N : dl);
-                atomicAdd(&a.drab_p[h * p_hs + c + a.N], v);
+            const float tot = sm.ring[slot] + sum;
+            if (c > BN - 2) {
+                if (tot != 0.f) {
+                    const int cl = dl < -a.N ? -a.N : (dl > a.N ? a.N : dl);
+                    atomicAdd(&a.drab_p[h * p_hs + cl + a.N], tot);
+                }
+                sm.ring[slot] = 0.f;
+            } else {
+                sm.ring[slot] = tot;
             }
-            sm.ring[slot] = 0.f;
         }
         if (n + 1 < nqb) sstore((n + 1) & 1);
         __syncthreads();

@@ -9,12 +9,22 @@
 // registers.  Keys stream through LDS in tiles of 64 (double buffered, one
 // barrier per tile).  Per 32-key block a wave computes S^T = K Q^T with
 // 32x32x16 bf16 MFMA (so each lane holds one query and 16 keys), adds both
-// biases in registers (rab_p from a per-tile window in LDS indexed by
-// key - query, rab_t from a 32-entry LDS table indexed by count-leading-zeros
-// of |dt| + 1), applies SiLU and the causal mask, packs P to bf16 and
+// biases in registers, applies SiLU and the causal mask, packs P to bf16 and
 // accumulates O^T += V^T P^T with V^T read by the transposing LDS load.  P
 // never leaves registers.  Blocks above the diagonal are skipped; blocks on
-// it are masked.  1/N is applied once at the end.
+// it are masked.
+//
+// The element-wise step works in the base-2 domain: x' = -log2(e) (s + bias)
+// (one FMA, the tables are staged pre-scaled), P' = x' / (1 + 2^x') =
+// -log2(e) SiLU(s + bias), and the constant -ln(2)/N is applied to O once at
+// the end.  rab_p comes from a per-tile window in LDS indexed by key - query.
+// rab_t: when all pairs of a 32x32 block share one time bucket (decided per
+// block from the min/max times of its 32 queries and 32 keys) the bias is a
+// scalar; otherwise it is read from a 32-entry LDS table indexed by
+// count-leading-zeros of |dt| + 1 (exact for sequences whose time span fits
+// 32 bits; wider sequences take an exact 64-bit path).  Every variant is a
+// separate compile-time instantiation, so the element-wise code has no
+// branches.
 #include "kernels.h"
 
 namespace {
@@ -25,17 +35,20 @@ constexpr int BN = 64;     // keys per LDS tile
 constexpr int NT = 256;
 constexpr int RS = 136;    // LDS row stride (bf16 elements) of K and V tiles
 constexpr int WIN = 192;   // rab_p window entries per tile (BM + BN - 1 used)
+constexpr float NLOG2E = -1.4426950408889634f;
+constexpr float NLN2 = -0.69314718055994531f;
 
 struct Stage {
     bf16 k[BN * RS];
     bf16 v[BN * RS];
-    float win[WIN];
-    uint32_t kt[BN];
+    float win[WIN];        // -log2(e) * rab_p[clip(key - query)]
+    uint32_t kt[BN];       // sequence-relative key times
+    uint32_t kmin[2], kmax[2]; // per 32-key half, over valid keys
 };
 struct Smem {
     Stage st[2];
-    float rabt_rev[32]; // rab_t[31 - c], indexed by clz(|dt| + 1)
-    float rabt[128];    // full table for sequences whose time span needs 64 bits
+    float rabt_rev[32]; // -log2(e) * rab_t[31 - c], indexed by clz(|dt| + 1)
+    float rabt[128];    // -log2(e) * rab_t
 };
 
 typedef short short4v __attribute__((ext_vector_type(4)));
@@ -50,32 +63,53 @@ DEV u32x2 lds_read_tr(const bf16 *p)
     return __builtin_bit_cast(u32x2, r);
 }
 
-} // namespace
-
-__global__ void __launch_bounds__(NT) attn_fwd_bf16_kernel(AttnFwdArgs a)
+// TM: 0 = no time bias, 1 = 32-bit relative times, 2 = 64-bit times.
+// Register r of the S^T accumulator <-> key kbase + koff(r), koff = 8(r/4) + r%4
+// (kbase = block start + 4g), query = this lane's.
+template <bool HP, int TM, bool DIAG, bool UNI>
+DEV void pointwise(const floatx16 &sacc, uint32_t (&pk)[8], const float *win_lane, const uint32_t *kt_lane,
+                   const float *rabt_rev, const float *rabt, uint32_t tq, int64_t tq64, const int64_t *tsk, int kbase,
+                   int klast, float ubias, int dmask)
 {
-    extern __shared__ __align__(16) unsigned char smem_raw[];
-    Smem &sm = *reinterpret_cast<Smem *>(smem_raw);
-    const int item = blockIdx.x;
-    if (item >= *a.n_items) return;
-    const int2 it = a.items[item];
-    const int b = it.x, qt = it.y >> 8, h = it.y & 255;
-    const int o_b = a.offsets[b];
-    const int L = a.offsets[b + 1] - o_b;
-    const int q0 = qt * BM;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+        float p2[2];
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+            const int rr = r + u, koff = 8 * (rr >> 2) + (rr & 3);
+            float bsum = 0.f;
+            if constexpr (HP) bsum = win_lane[koff];
+            if constexpr (TM == 1) {
+                if constexpr (UNI) {
+                    bsum += ubias;
+                } else {
+                    const uint32_t tk = kt_lane[koff];
+                    const uint32_t dd = (tq > tk ? tq - tk : tk - tq) + 1u; // |dt| + 1
+                    bsum += rabt_rev[__builtin_clz(dd)];
+                }
+            } else if constexpr (TM == 2) {
+                const int key = min(kbase + koff, klast);
+                bsum += rabt[time_bucket64(tq64 - tsk[key])];
+            }
+            const float x = __builtin_fmaf(sacc[rr], NLOG2E, bsum);
+            float p = x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x));
+            if constexpr (DIAG) p = koff > dmask ? 0.f : p;
+            p2[u] = p;
+        }
+        pk[r >> 1] = pack2_bf16(p2[0], p2[1]);
+    }
+}
+
+template <bool HP, int TM>
+DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h)
+{
     const int kend = min(q0 + BM, L); // keys [0, kend) are needed
     const int nkt = (kend + BN - 1) / BN;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, lq = l & 31;
-    const bool has_t = a.ts != nullptr && a.rab_t != nullptr;
-    const bool wide = has_t && a.wide[b] != 0;
-    const bool has_p = a.rab_p != nullptr;
     const bf16 *Q = (const bf16 *)a.q, *K = (const bf16 *)a.k, *V = (const bf16 *)a.v;
 
-    if (tid < 128) sm.rabt[tid] = has_t ? a.rab_t[h * a.rt_hs + tid] : 0.f;
-    if (tid < 32) sm.rabt_rev[tid] = has_t ? a.rab_t[h * a.rt_hs + 31 - tid] : 0.f;
-
-    // This lane's query (sequence-local index) and its Q fragment: lane holds
-    // Q[row][16s + 8g .. +8] for s = 0..7 (B operand of S^T = K Q^T).
+    // This lane's query and its Q fragment: Q[row][16s + 8g .. +8], s = 0..7
+    // (B operand of S^T = K Q^T).
     const int qrow = q0 + w * 32 + lq;
     const bool qvalid = qrow < L;
     bf16x8 qreg[8];
@@ -87,8 +121,15 @@ __global__ void __launch_bounds__(NT) attn_fwd_bf16_kernel(AttnFwdArgs a)
             qreg[s] = as_bf16x8(x);
         }
     }
-    const uint32_t tq = (has_t && !wide && qvalid) ? a.rel[o_b + qrow] : 0u;
-    const int64_t tq64 = (wide && qvalid) ? a.ts[o_b + qrow] : 0;
+    const uint32_t tq = (TM == 1 && qvalid) ? a.rel[o_b + qrow] : 0u;
+    const int64_t tq64 = (TM == 2 && qvalid) ? a.ts[o_b + qrow] : 0;
+    uint32_t tqmin = qvalid ? tq : 0xFFFFFFFFu, tqmax = qvalid ? tq : 0u;
+    if constexpr (TM == 1) {
+        for (int o = 32; o >= 1; o >>= 1) {
+            tqmin = min(tqmin, (uint32_t)__shfl_xor((int)tqmin, o, 64));
+            tqmax = max(tqmax, (uint32_t)__shfl_xor((int)tqmax, o, 64));
+        }
+    }
 
     floatx16 oacc[4];
 #pragma unroll
@@ -100,7 +141,7 @@ __global__ void __launch_bounds__(NT) attn_fwd_bf16_kernel(AttnFwdArgs a)
     const int lc = tid >> 4, le = tid & 15;
     u32x4 kreg[4], vreg[4];
     float wreg = 0.f;
-    uint32_t treg = 0;
+    uint32_t treg = 0, tmn = 0xFFFFFFFFu, tmx = 0u;
     auto gload = [&](int kt) {
         const int kb0 = kt * BN;
 #pragma unroll
@@ -111,14 +152,25 @@ __global__ void __launch_bounds__(NT) attn_fwd_bf16_kernel(AttnFwdArgs a)
             kreg[i] = ok ? *(const u32x4 *)(K + row * a.ldk + h * D + le * 8) : u32x4{0, 0, 0, 0};
             vreg[i] = ok ? *(const u32x4 *)(V + row * a.ldv + h * D + le * 8) : u32x4{0, 0, 0, 0};
         }
-        if (tid < WIN) {
-            int dl = kb0 - q0 - (BM - 1) + tid; // key - query of window slot tid
-            dl = dl < -a.N ? -a.N : (dl > a.N ? a.N : dl);
-            wreg = has_p ? a.rab_p[h * a.rp_hs + dl + a.N] : 0.f;
+        if constexpr (HP) {
+            if (tid < WIN) {
+                int dl = kb0 - q0 - (BM - 1) + tid; // key - query of window slot tid
+                dl = dl < -a.N ? -a.N : (dl > a.N ? a.N : dl);
+                wreg = NLOG2E * a.rab_p[h * a.rp_hs + dl + a.N];
+            }
         }
-        if (tid < BN) {
-            const int key = kb0 + tid;
-            treg = (has_t && !wide && key < kend) ? a.rel[o_b + key] : 0u;
+        if constexpr (TM == 1) {
+            if (tid < BN) { // wave 0: key times and the range of each 32-key half
+                const int key = kb0 + tid;
+                const bool ok = key < kend;
+                treg = ok ? a.rel[o_b + key] : 0u;
+                tmn = ok ? treg : 0xFFFFFFFFu;
+                tmx = ok ? treg : 0u;
+                for (int o = 16; o >= 1; o >>= 1) {
+                    tmn = min(tmn, (uint32_t)__shfl_xor((int)tmn, o, 64));
+                    tmx = max(tmx, (uint32_t)__shfl_xor((int)tmx, o, 64));
+                }
+            }
         }
     };
     auto sstore = [&](int buf) {
@@ -128,8 +180,15 @@ __global__ void __launch_bounds__(NT) attn_fwd_bf16_kernel(AttnFwdArgs a)
             *(u32x4 *)&S.k[(lc * 4 + i) * RS + le * 8] = kreg[i];
             *(u32x4 *)&S.v[(lc * 4 + i) * RS + le * 8] = vreg[i];
         }
-        if (tid < WIN) S.win[tid] = wreg;
-        if (tid < BN) S.kt[tid] = treg;
+        if constexpr (HP)
+            if (tid < WIN) S.win[tid] = wreg;
+        if constexpr (TM == 1) {
+            if (tid < BN) S.kt[tid] = treg;
+            if ((tid & 31) == 0 && tid < BN) {
+                S.kmin[tid >> 5] = tmn;
+                S.kmax[tid >> 5] = tmx;
+            }
+        }
     };
 
     gload(0);
@@ -138,8 +197,9 @@ __global__ void __launch_bounds__(NT) attn_fwd_bf16_kernel(AttnFwdArgs a)
 
     const int qstart = q0 + w * 32; // first query of this wave
     // transposing-read lane constants for the V operand
-    const int tj = l & 15, ts_ = tj >> 2;
+    const int tj = l & 15, tsl = tj >> 2;
     const int cpart = ((l >> 4) & 1) * 16 + 4 * (tj & 3);
+    const int64_t *tsk = TM == 2 ? a.ts + o_b : nullptr;
 
     for (int kt = 0; kt < nkt; kt++) {
         if (kt + 1 < nkt) gload(kt + 1);
@@ -157,40 +217,38 @@ __global__ void __launch_bounds__(NT) attn_fwd_bf16_kernel(AttnFwdArgs a)
                 const bf16x8 ka = *(const bf16x8 *)&S.k[(kb * 32 + lq) * RS + s * 16 + g * 8];
                 sacc = mfma32(ka, qreg[s], sacc);
             }
-            // register r <-> key kstart + 8(r/4) + 4g + r%4, query qstart + lq
-            const int xb = kb * 32 + 4 * g - w * 32 - lq + (BM - 1);
-            uint32_t pk[8];
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                float p2[2];
-#pragma unroll
-                for (int u = 0; u < 2; u++) {
-                    const int rr = r + u;
-                    const int koff = 8 * (rr >> 2) + (rr & 3);
-                    float x = sacc[rr];
-                    if (has_p) x += S.win[xb + koff];
-                    if (has_t) {
-                        if (!wide) {
-                            const uint32_t tk = S.kt[kb * 32 + 4 * g + koff];
-                            const uint32_t dd = (tq > tk ? tq - tk : tk - tq) + 1u; // |tq - tk| + 1
-                            x += sm.rabt_rev[__builtin_clz(dd)];
-                        } else {
-                            int key = kstart + 4 * g + koff;
-                            key = key < L ? key : L - 1;
-                            x += sm.rabt[time_bucket64(tq64 - a.ts[o_b + key])];
-                        }
-                    }
-                    float p = silu_f(x);
-                    if (diag && (kstart + 4 * g + koff > qstart + lq)) p = 0.f;
-                    p2[u] = p;
+            const float *win_lane = &S.win[kb * 32 + 4 * g - w * 32 - lq + (BM - 1)];
+            const uint32_t *kt_lane = &S.kt[kb * 32 + 4 * g];
+            const int kbase = kstart + 4 * g;
+            bool uni = false;
+            float ubias = 0.f;
+            if constexpr (TM == 1) {
+                const uint32_t kmn = S.kmin[kb], kmx = S.kmax[kb];
+                if (kmn <= kmx && tqmin <= tqmax) {
+                    const int64_t a1 = (int64_t)tqmin - (int64_t)kmx, a2 = (int64_t)tqmax - (int64_t)kmn;
+                    const int64_t lo = a1 > 0 ? a1 : (a2 < 0 ? -a2 : 0);
+                    const int64_t m1 = a1 < 0 ? -a1 : a1, m2 = a2 < 0 ? -a2 : a2;
+                    const int64_t hi = m1 > m2 ? m1 : m2;
+                    const int blo = floor_log2_u32((uint32_t)lo + 1u), bhi = floor_log2_u32((uint32_t)hi + 1u);
+                    uni = __builtin_amdgcn_readfirstlane(blo == bhi ? 1 : 0) != 0;
+                    ubias = sm.rabt[blo];
                 }
-                pk[r >> 1] = pack2_bf16(p2[0], p2[1]);
             }
+            uint32_t pk[8];
+            if (diag)
+                pointwise<HP, TM, true, false>(sacc, pk, win_lane, kt_lane, sm.rabt_rev, sm.rabt, tq, tq64, tsk, kbase,
+                                               L - 1, ubias, lq - 4 * g);
+            else if (TM == 1 && uni)
+                pointwise<HP, TM, false, true>(sacc, pk, win_lane, kt_lane, sm.rabt_rev, sm.rabt, tq, tq64, tsk, kbase,
+                                               L - 1, ubias, 0);
+            else
+                pointwise<HP, TM, false, false>(sacc, pk, win_lane, kt_lane, sm.rabt_rev, sm.rabt, tq, tq64, tsk,
+                                                kbase, L - 1, ubias, 0);
 #pragma unroll
             for (int m = 0; m < 2; m++) {
                 const bf16x8 pb = as_bf16x8(u32x4{pk[4 * m], pk[4 * m + 1], pk[4 * m + 2], pk[4 * m + 3]});
                 // keys for element e of this lane's operand: 16m + 8(e/4) + 4g + e%4
-                const int key1 = kb * 32 + 16 * m + 4 * g + ts_;
+                const int key1 = kb * 32 + 16 * m + 4 * g + tsl;
 #pragma unroll
                 for (int db = 0; db < 4; db++) {
                     const u32x2 r1 = lds_read_tr(&S.v[key1 * RS + db * 32 + cpart]);
@@ -205,15 +263,17 @@ __global__ void __launch_bounds__(NT) attn_fwd_bf16_kernel(AttnFwdArgs a)
     }
 
     if (!qvalid) return;
-    // O^T accumulator: lane holds query qrow, d = 32 db + 8(r/4) + 4g + r%4.
+    // O^T accumulator: lane holds query qrow, d = 32 db + 8(r/4) + 4g + r%4;
+    // O = (-ln 2 / N) * sum P' V.
+    const float sc = NLN2 * a.inv_n;
     const int64_t row = (int64_t)(o_b + qrow);
 #pragma unroll
     for (int db = 0; db < 4; db++) {
 #pragma unroll
         for (int gr = 0; gr < 4; gr++) {
             const int d0 = db * 32 + 8 * gr + 4 * g;
-            floatx4 o4 = {oacc[db][4 * gr] * a.inv_n, oacc[db][4 * gr + 1] * a.inv_n, oacc[db][4 * gr + 2] * a.inv_n,
-                          oacc[db][4 * gr + 3] * a.inv_n};
+            floatx4 o4 = {oacc[db][4 * gr] * sc, oacc[db][4 * gr + 1] * sc, oacc[db][4 * gr + 2] * sc,
+                          oacc[db][4 * gr + 3] * sc};
             if (a.o32) *(floatx4 *)(a.o32 + row * a.ld_o32 + h * D + d0) = o4;
             if (a.o16) {
                 u32x2 pk2 = {pack2_bf16(o4[0], o4[1]), pack2_bf16(o4[2], o4[3])};
@@ -221,6 +281,29 @@ __global__ void __launch_bounds__(NT) attn_fwd_bf16_kernel(AttnFwdArgs a)
             }
         }
     }
+}
+
+} // namespace
+
+template <bool HP>
+__global__ void __launch_bounds__(NT) attn_fwd_bf16_kernel(AttnFwdArgs a)
+{
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    Smem &sm = *reinterpret_cast<Smem *>(smem_raw);
+    const int item = blockIdx.x;
+    if (item >= *a.n_items) return;
+    const int2 it = a.items[item];
+    const int b = it.x, qt = it.y >> 8, h = it.y & 255;
+    const int o_b = a.offsets[b];
+    const int L = a.offsets[b + 1] - o_b;
+    const bool has_t = a.ts != nullptr && a.rab_t != nullptr;
+    const int tid = threadIdx.x;
+    if (tid < 128) sm.rabt[tid] = has_t ? NLOG2E * a.rab_t[h * a.rt_hs + tid] : 0.f;
+    if (tid < 32) sm.rabt_rev[tid] = has_t ? NLOG2E * a.rab_t[h * a.rt_hs + 31 - tid] : 0.f;
+    // (the first barrier inside fwd_body orders these table writes before use)
+    if (!has_t) fwd_body<HP, 0>(a, sm, o_b, L, qt * BM, h);
+    else if (a.wide[b] != 0) fwd_body<HP, 2>(a, sm, o_b, L, qt * BM, h);
+    else fwd_body<HP, 1>(a, sm, o_b, L, qt * BM, h);
 }
 
 // ---------------------------------------------------------------------------
@@ -299,13 +382,17 @@ hipError_t launch_attn_fwd_bf16(const AttnFwdArgs &a, int max_items, hipStream_t
     static bool init = false;
     const size_t smem = sizeof(Smem);
     if (!init) {
-        hipError_t e = hipFuncSetAttribute((const void *)attn_fwd_bf16_kernel,
+        hipError_t e = hipFuncSetAttribute((const void *)attn_fwd_bf16_kernel<true>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        if (e != hipSuccess) return e;
+        e = hipFuncSetAttribute((const void *)attn_fwd_bf16_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)smem);
         if (e != hipSuccess) return e;
         init = true;
     }
     if (max_items <= 0) return hipSuccess;
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3(max_items), dim3(NT), smem, st, a);
+    if (a.rab_p) hipLaunchKernelGGL(attn_fwd_bf16_kernel<true>, dim3(max_items), dim3(NT), smem, st, a);
+    else hipLaunchKernelGGL(attn_fwd_bf16_kernel<false>, dim3(max_items), dim3(NT), smem, st, a);
     return hipGetLastError();
 }
 

@@ -182,6 +182,22 @@ hstu_status mfalcon_score(const hstu_jagged *hist, const hstu_dims *dims, int32_
                           const int32_t *cand_offsets, int32_t total_cand, const int64_t *cand_ts, hstu_cmat x_cand,
                           int32_t b_m, float *y_cand, void *ws, size_t ws_bytes, void *stream);
 
+/* Kernel timing for benchmarks.  While enabled, every entry point brackets
+ * each kernel (or small group of kernels) it launches with a pair of HIP
+ * events recorded on the launch stream; this adds no device work and does not
+ * change kernel durations.  hstu_profile_collect() waits for the recorded
+ * events and returns, per kernel name, the launch count and summed duration
+ * since the previous collect (at most `cap` entries; returns the number
+ * written).  Off by default.  Not thread-safe against concurrent entry-point
+ * calls on other threads while collecting. */
+typedef struct {
+    char name[48];
+    int32_t launches;
+    double total_ms;
+} hstu_kernel_time;
+void hstu_profile_enable(int32_t on);
+int32_t hstu_profile_collect(hstu_kernel_time *out, int32_t cap);
+
 /* Message of the last non-OK status on this thread ("" if none). */
 const char *hstu_last_error(void);
 
