@@ -8,7 +8,8 @@
 //   dK_j += sum_i dS_ij q_i           dQ_i += sum_j dS_ij k_j
 //   drab_p[clip(j-i)] += dS_ij        drab_t[bucket] += dS_ij
 // x is recomputed from Q, K and the tables (pointwise attention keeps no
-// softmax statistics, so nothing else is needed).
+// softmax statistics, so nothing else is needed).  dO' arrives as two bf16
+// planes (hi + lo) so dP keeps ~16 significant bits.
 //
 // A workgroup of 4 waves owns 128 keys of one (sequence, head); wave w owns
 // keys 32w..32w+31 with their K and V rows in registers and their dK^T, dV^T
@@ -17,14 +18,17 @@
 // (lane = key, registers = queries), the element-wise step, dV^T += dO'^T P
 // and dK^T += Q^T dS (transposing LDS reads for dO'^T and Q^T), and writes dS
 // to LDS; then wave w computes dQ for d-block w over all 128 keys and adds it
-// to an fp32 accumulator with global atomics.  drab_p: each wave also writes
-// its fp32 dS into an LDS tile skewed by j - i ([query][key - query]), one
-// thread per diagonal sums it into an LDS ring indexed by j - i, and an entry
-// is flushed with one global atomic once no later block can touch it.
-// drab_t: when every pair of a 32x32 block falls in one time bucket (checked
-// per block from the min/max times of its queries and keys) the bucket's bias
-// is a scalar and the block's dS is summed by a wave reduction; otherwise
-// per-element adds go to per-wave LDS tables.
+// to an fp32 accumulator with global atomics.
+//
+// drab_p: each wave also writes its fp32 dS into an LDS tile skewed by
+// j - i ([query][key - query]); one thread per diagonal sums it into an LDS
+// ring indexed by j - i, and an entry is flushed with one global atomic once
+// no later block can reach it.  drab_t: when every pair of a 32x32 block falls
+// in one time bucket (decided per block from the min/max times of its queries
+// and keys) the bias is a scalar and the block's dS is summed by a wave
+// reduction; otherwise per-element adds go to per-wave LDS tables.  Bias
+// presence, time mode, diagonal masking and uniform blocks are compile-time
+// instantiations, so the element-wise code has no branches.
 #include "kernels.h"
 
 namespace {
@@ -40,6 +44,7 @@ constexpr int RING = 256;  // drab_p ring (power of two >= WIN + BQ)
 constexpr int DK = 160;    // columns of the skewed dS tile: key - query + BQ - 1
 constexpr int TB = 64;     // time buckets that int64 differences can reach
 constexpr int TCOPY = 4;   // copies of each wave's drab_t table
+constexpr float NLOG2E = -1.4426950408889634f;
 
 struct Stage {
     bf16 q[BQ * RS];
@@ -70,32 +75,81 @@ DEV u32x2 lds_read_tr(const bf16 *p)
     return __builtin_bit_cast(u32x2, r);
 }
 
-} // namespace
+struct BwdLane {
+    const float *win;     // S.win + (32w + lq + BQ - 1) - 4g  (index with -cr)
+    const uint32_t *qt;   // S.qt + 4g   (index with cr)
+    const int64_t *qt64;  // S.qt64 + 4g
+    float *dsk;           // skewed-tile cell of (cr = 0) for this lane
+    float *dtab;          // this wave's drab_t table copy for this lane
+    uint32_t tk;
+    int64_t tk64;
+    int dmask;            // masked (key > query) iff cr < dmask  (diagonal blocks)
+};
 
-__global__ void __launch_bounds__(NT) attn_bwd_bf16_kernel(AttnBwdArgs a)
+// Element-wise step of one 32x32 block.  Register r <-> query ql = 4g + cr(r),
+// cr = 8(r/4) + r%4; this lane's key.  Writes packed bf16 P and dS, the fp32
+// dS into the skewed tile, and the drab_t contributions.
+template <bool HP, int TM, bool DT, bool DIAG, bool UNI>
+DEV void bwd_pointwise(const floatx16 &sacc, const floatx16 &pacc, uint32_t (&ppk)[8], uint32_t (&dpk)[8],
+                       const BwdLane &ln, const float *rabt_rev, const float *rabt, float ubias, float &tsum)
 {
-    extern __shared__ __align__(16) unsigned char smem_raw[];
-    Smem &sm = *reinterpret_cast<Smem *>(smem_raw);
-    const int item = blockIdx.x;
-    if (item >= *a.n_items) return;
-    const int2 it = a.items[item];
-    const int b = it.x, tsched = it.y >> 8, h = it.y & 255;
-    const int o_b = a.offsets[b];
-    const int L = a.offsets[b + 1] - o_b;
-    const int nkt = (L + BN - 1) / BN;
-    const int kt = nkt - 1 - tsched; // most expensive key tile (kt = 0) first
-    const int k0 = kt * BN;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+        float pp[2], dd[2];
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+            const int rr = r + u;
+            const int cr = 8 * (rr >> 2) + (rr & 3);
+            float x = sacc[rr];
+            if constexpr (HP) x += ln.win[-cr];
+            int bucket = 0;
+            if constexpr (TM == 1) {
+                if constexpr (UNI) {
+                    x += ubias;
+                } else {
+                    const uint32_t tq = ln.qt[cr];
+                    const uint32_t dd1 = (tq > ln.tk ? tq - ln.tk : ln.tk - tq) + 1u;
+                    const int cz = __builtin_clz(dd1);
+                    x += rabt_rev[cz];
+                    bucket = 31 - cz;
+                }
+            } else if constexpr (TM == 2) {
+                bucket = time_bucket64(ln.qt64[cr] - ln.tk64);
+                x += rabt[bucket];
+            }
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * NLOG2E));
+            float p = x * sg;
+            float ds = pacc[rr] * sg * __builtin_fmaf(x, 1.0f - sg, 1.0f);
+            if constexpr (DIAG) {
+                if (cr < ln.dmask) {
+                    p = 0.f;
+                    ds = 0.f;
+                }
+            }
+            pp[u] = p;
+            dd[u] = ds;
+            ln.dsk[cr * (DK - 1)] = ds;
+            if constexpr (DT && TM != 0) {
+                if constexpr (UNI) tsum += ds;
+                else atomicAdd(&ln.dtab[bucket], ds);
+            }
+        }
+        ppk[r >> 1] = pack2_bf16(pp[0], pp[1]);
+        dpk[r >> 1] = pack2_bf16(dd[0], dd[1]);
+    }
+}
+
+template <bool HP, int TM, bool DT>
+DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
+{
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, lq = l & 31;
-    const bool has_t = a.ts != nullptr && a.rab_t != nullptr;
-    const bool wide = has_t && a.wide[b] != 0;
-    const bool has_p = a.rab_p != nullptr;
     const bf16 *Q = a.q, *K = a.k, *V = a.v, *dO = a.dO;
     const int64_t ld_do = (int64_t)a.H * D;
+    const bf16 *dOlo = dO + (int64_t)a.T * ld_do;
 
     // ---- prologue: tables, K tile in LDS, own K/V rows in registers
-    if (tid < 128) sm.rabt[tid] = has_t ? a.rab_t[h * a.rt_hs + tid] : 0.f;
-    if (tid < 32) sm.rabt_rev[tid] = has_t ? a.rab_t[h * a.rt_hs + 31 - tid] : 0.f;
     for (int i = tid; i < RING; i += NT) sm.ring[i] = 0.f;
+    for (int i = tid; i < BQ * DK; i += NT) sm.dsk[i] = 0.f;
     for (int i = tid; i < 4 * TCOPY * TB; i += NT) (&sm.dtab[0][0][0])[i] = 0.f;
     {
         const int lc = tid >> 4, le = tid & 15; // 16 keys x 16 d-groups per pass
@@ -119,13 +173,17 @@ __global__ void __launch_bounds__(NT) attn_bwd_bf16_kernel(AttnBwdArgs a)
             vreg[s] = as_bf16x8(kvalid ? *(const u32x4 *)(vp + s * 16) : u32x4{0, 0, 0, 0});
         }
     }
-    const uint32_t tk = (has_t && !wide && kvalid) ? a.rel[o_b + mykey] : 0u;
-    const int64_t tk64 = (wide && kvalid) ? a.ts[o_b + mykey] : 0;
+    BwdLane ln;
+    ln.tk = (TM == 1 && kvalid) ? a.rel[o_b + mykey] : 0u;
+    ln.tk64 = (TM == 2 && kvalid) ? a.ts[o_b + mykey] : 0;
+    ln.dtab = &sm.dtab[w][lq & (TCOPY - 1)][0];
     // time range of this wave's valid keys (for the uniform-bucket test)
-    uint32_t tkmin = kvalid ? tk : 0xFFFFFFFFu, tkmax = kvalid ? tk : 0u;
-    for (int o = 32; o >= 1; o >>= 1) {
-        tkmin = min(tkmin, (uint32_t)__shfl_xor((int)tkmin, o, 64));
-        tkmax = max(tkmax, (uint32_t)__shfl_xor((int)tkmax, o, 64));
+    uint32_t tkmin = kvalid ? ln.tk : 0xFFFFFFFFu, tkmax = kvalid ? ln.tk : 0u;
+    if constexpr (TM == 1) {
+        for (int o = 32; o >= 1; o >>= 1) {
+            tkmin = min(tkmin, (uint32_t)__shfl_xor((int)tkmin, o, 64));
+            tkmax = max(tkmax, (uint32_t)__shfl_xor((int)tkmax, o, 64));
+        }
     }
 
     floatx16 dv_acc[4], dk_acc[4];
@@ -140,7 +198,6 @@ __global__ void __launch_bounds__(NT) attn_bwd_bf16_kernel(AttnBwdArgs a)
     // ---- query-block stage loader: thread -> (query lcq, 16 d-groups)
     const int lcq = tid >> 3, leq = tid & 7; // 32 queries x 8 threads x 16 elements
     u32x4 qreg2[2], dreg2[2], lreg2[2];
-    const bf16 *dOlo = dO + (int64_t)a.T * ld_do;
     float wreg = 0.f;
     uint32_t treg = 0, tmn = 0xFFFFFFFFu, tmx = 0u;
     int64_t treg64 = 0;
@@ -154,21 +211,27 @@ __global__ void __launch_bounds__(NT) attn_bwd_bf16_kernel(AttnBwdArgs a)
             dreg2[c] = ok ? *(const u32x4 *)(dO + row * ld_do + h * D + leq * 16 + c * 8) : u32x4{0, 0, 0, 0};
             lreg2[c] = ok ? *(const u32x4 *)(dOlo + row * ld_do + h * D + leq * 16 + c * 8) : u32x4{0, 0, 0, 0};
         }
-        if (tid < WIN) {
-            int dl = k0 - q0 - (BQ - 1) + tid; // key - query of window slot tid
-            dl = dl < -a.N ? -a.N : (dl > a.N ? a.N : dl);
-            wreg = has_p ? a.rab_p[h * a.rp_hs + dl + a.N] : 0.f;
+        if constexpr (HP) {
+            if (tid < WIN) {
+                int dl = k0 - q0 - (BQ - 1) + tid; // key - query of window slot tid
+                dl = dl < -a.N ? -a.N : (dl > a.N ? a.N : dl);
+                wreg = a.rab_p[h * a.rp_hs + dl + a.N];
+            }
         }
-        if (tid < 64) { // wave 0: query times and their range
-            const int q = q0 + tid;
-            const bool okq = tid < BQ && q < L;
-            treg = (has_t && !wide && okq) ? a.rel[o_b + q] : 0u;
-            treg64 = (wide && okq) ? a.ts[o_b + q] : 0;
-            tmn = okq ? treg : 0xFFFFFFFFu;
-            tmx = okq ? treg : 0u;
-            for (int o = 32; o >= 1; o >>= 1) {
-                tmn = min(tmn, (uint32_t)__shfl_xor((int)tmn, o, 64));
-                tmx = max(tmx, (uint32_t)__shfl_xor((int)tmx, o, 64));
+        if constexpr (TM != 0) {
+            if (tid < 64) { // wave 0: query times and their range
+                const int q = q0 + tid;
+                const bool okq = tid < BQ && q < L;
+                treg = (TM == 1 && okq) ? a.rel[o_b + q] : 0u;
+                treg64 = (TM == 2 && okq) ? a.ts[o_b + q] : 0;
+                tmn = okq ? treg : 0xFFFFFFFFu;
+                tmx = okq ? treg : 0u;
+                if constexpr (TM == 1) {
+                    for (int o = 32; o >= 1; o >>= 1) {
+                        tmn = min(tmn, (uint32_t)__shfl_xor((int)tmn, o, 64));
+                        tmx = max(tmx, (uint32_t)__shfl_xor((int)tmx, o, 64));
+                    }
+                }
             }
         }
     };
@@ -180,14 +243,17 @@ __global__ void __launch_bounds__(NT) attn_bwd_bf16_kernel(AttnBwdArgs a)
             *(u32x4 *)&S.dO[lcq * RS + leq * 16 + c * 8] = dreg2[c];
             *(u32x4 *)&S.dOl[lcq * RS + leq * 16 + c * 8] = lreg2[c];
         }
-        if (tid < WIN) S.win[tid] = wreg;
-        if (tid < BQ) {
-            S.qt[tid] = treg;
-            S.qt64[tid] = treg64;
-        }
-        if (tid == 0) {
-            S.qtmin = tmn;
-            S.qtmax = tmx;
+        if constexpr (HP)
+            if (tid < WIN) S.win[tid] = wreg;
+        if constexpr (TM != 0) {
+            if (tid < BQ) {
+                S.qt[tid] = treg;
+                S.qt64[tid] = treg64;
+            }
+            if (tid == 0) {
+                S.qtmin = tmn;
+                S.qtmax = tmx;
+            }
         }
     };
 
@@ -198,10 +264,11 @@ __global__ void __launch_bounds__(NT) attn_bwd_bf16_kernel(AttnBwdArgs a)
     }
     __syncthreads();
 
-    const int tj = l & 15, ts_ = tj >> 2;
+    const int tj = l & 15, tsl = tj >> 2;
     const int cpart = ((l >> 4) & 1) * 16 + 4 * (tj & 3);
     const int p_hs = a.rp_hs > 0 ? (int)a.rp_hs : 2 * a.N + 1;
     const int t_hs = a.rt_hs > 0 ? (int)a.rt_hs : 128;
+    ln.dsk = &sm.dsk[4 * g * (DK - 1) + 32 * w + lq + (BQ - 1)];
 
     for (int n = 0; n < nqb; n++) {
         const int q0 = k0 + n * BQ;
@@ -226,69 +293,34 @@ __global__ void __launch_bounds__(NT) attn_bwd_bf16_kernel(AttnBwdArgs a)
                 pacc = mfma32(da, vreg[s], pacc);
                 pacc = mfma32(dl, vreg[s], pacc);
             }
-            // register r <-> query q0 + ql(r), ql = 8(r/4) + 4g + r%4; key = mykey
-            // Uniform time bucket over the block: |t_q - t_k| spans [lo, hi].
+            ln.win = &S.win[32 * w + lq + (BQ - 1) - 4 * g];
+            ln.qt = &S.qt[4 * g];
+            ln.qt64 = &S.qt64[4 * g];
+            ln.dmask = kw0 + lq - q0 - 4 * g; // key > query  <=>  cr < dmask
             bool uni = false;
             int ubk = 0;
-            if (has_t && !wide && S.qtmin <= S.qtmax && tkmin <= tkmax) {
-                const int64_t a1 = (int64_t)S.qtmin - (int64_t)tkmax, a2 = (int64_t)S.qtmax - (int64_t)tkmin;
-                const int64_t lo = a1 > 0 ? a1 : (a2 < 0 ? -a2 : 0);
-                const int64_t hi = (a1 < 0 ? -a1 : a1) > (a2 < 0 ? -a2 : a2) ? (a1 < 0 ? -a1 : a1) : (a2 < 0 ? -a2 : a2);
-                const int blo = floor_log2_u32((uint32_t)lo + 1u), bhi = floor_log2_u32((uint32_t)hi + 1u);
-                uni = blo == bhi;
-                ubk = blo;
+            if constexpr (TM == 1) {
+                const uint32_t qmn = S.qtmin, qmx = S.qtmax;
+                if (qmn <= qmx && tkmin <= tkmax) {
+                    const int64_t a1 = (int64_t)qmn - (int64_t)tkmax, a2 = (int64_t)qmx - (int64_t)tkmin;
+                    const int64_t lo = a1 > 0 ? a1 : (a2 < 0 ? -a2 : 0);
+                    const int64_t m1 = a1 < 0 ? -a1 : a1, m2 = a2 < 0 ? -a2 : a2;
+                    const int64_t hi = m1 > m2 ? m1 : m2;
+                    const int blo = floor_log2_u32((uint32_t)lo + 1u), bhi = floor_log2_u32((uint32_t)hi + 1u);
+                    uni = __builtin_amdgcn_readfirstlane(blo == bhi ? 1 : 0) != 0;
+                    ubk = __builtin_amdgcn_readfirstlane(blo);
+                }
             }
-            const float ubias = uni ? sm.rabt[ubk] : 0.f;
+            const float ubias = sm.rabt[ubk];
             float tsum = 0.f;
             uint32_t ppk[8], dpk[8];
-            const int wb = 32 * w + lq + (BQ - 1); // window index = wb - ql
-            float *dskl = &sm.dsk[4 * g * DK + 32 * w + lq + (BQ - 1) - 4 * g];
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                float pp[2], dd[2];
-#pragma unroll
-                for (int u = 0; u < 2; u++) {
-                    const int rr = r + u;
-                    const int cr = 8 * (rr >> 2) + (rr & 3); // ql - 4g
-                    const int ql = cr + 4 * g;
-                    float x = sacc[rr];
-                    if (has_p) x += S.win[wb - ql];
-                    int bucket = 0;
-                    if (has_t) {
-                        if (uni) {
-                            x += ubias;
-                        } else if (!wide) {
-                            const uint32_t tq = S.qt[ql];
-                            const uint32_t dd1 = (tq > tk ? tq - tk : tk - tq) + 1u;
-                            const int cz = __builtin_clz(dd1);
-                            x += sm.rabt_rev[cz];
-                            bucket = 31 - cz;
-                        } else {
-                            bucket = time_bucket64(S.qt64[ql] - tk64);
-                            x += sm.rabt[bucket];
-                        }
-                    }
-                    const float e = __builtin_amdgcn_exp2f(x * -1.4426950408889634f);
-                    const float sg = __builtin_amdgcn_rcpf(1.0f + e);
-                    float p = x * sg;
-                    float ds = pacc[rr] * sg * (1.0f + x * (1.0f - sg));
-                    if (diag && mykey > q0 + ql) {
-                        p = 0.f;
-                        ds = 0.f;
-                    }
-                    pp[u] = p;
-                    dd[u] = ds;
-                    // skewed tile: row ql, column key_local - ql + BQ - 1
-                    dskl[cr * (DK - 1)] = ds;
-                    if (a.drab_t && has_t) {
-                        if (uni) tsum += ds;
-                        else if (ds != 0.f) atomicAdd(&sm.dtab[w][lq & (TCOPY - 1)][bucket], ds);
-                    }
-                }
-                ppk[r >> 1] = pack2_bf16(pp[0], pp[1]);
-                dpk[r >> 1] = pack2_bf16(dd[0], dd[1]);
-            }
-            if (a.drab_t && uni) {
+            if (diag)
+                bwd_pointwise<HP, TM, DT, true, false>(sacc, pacc, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, tsum);
+            else if (TM == 1 && uni)
+                bwd_pointwise<HP, TM, DT, false, true>(sacc, pacc, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, tsum);
+            else
+                bwd_pointwise<HP, TM, DT, false, false>(sacc, pacc, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, tsum);
+            if (DT && TM == 1 && uni && !diag) {
                 tsum = wave_sum(tsum);
                 if (l == 0) sm.dtab[w][0][ubk] += tsum;
             }
@@ -297,7 +329,7 @@ __global__ void __launch_bounds__(NT) attn_bwd_bf16_kernel(AttnBwdArgs a)
             for (int m = 0; m < 2; m++) {
                 const bf16x8 pb = as_bf16x8(u32x4{ppk[4 * m], ppk[4 * m + 1], ppk[4 * m + 2], ppk[4 * m + 3]});
                 const bf16x8 sb = as_bf16x8(u32x4{dpk[4 * m], dpk[4 * m + 1], dpk[4 * m + 2], dpk[4 * m + 3]});
-                const int qr1 = 16 * m + 4 * g + ts_; // query row of the transposing read
+                const int qr1 = 16 * m + 4 * g + tsl; // query row of the transposing read
 #pragma unroll
                 for (int db = 0; db < 4; db++) {
                     const u32x2 d1 = lds_read_tr(&S.dO[qr1 * RS + db * 32 + cpart]);
@@ -319,9 +351,8 @@ __global__ void __launch_bounds__(NT) attn_bwd_bf16_kernel(AttnBwdArgs a)
             const int krow = 32 * w + lq;
 #pragma unroll
             for (int gr = 0; gr < 4; gr++) *(u32x2 *)&sm.ds[krow * SS + 8 * gr + 4 * g] = u32x2{0u, 0u};
-            float *dskl = &sm.dsk[4 * g * DK + 32 * w + lq + (BQ - 1) - 4 * g];
 #pragma unroll
-            for (int rr = 0; rr < 16; rr++) dskl[(8 * (rr >> 2) + (rr & 3)) * (DK - 1)] = 0.f;
+            for (int rr = 0; rr < 16; rr++) ln.dsk[(8 * (rr >> 2) + (rr & 3)) * (DK - 1)] = 0.f;
         }
         __syncthreads();
         // dQ[32 queries][d-block w] = sum over the 128 keys of dS[q][key] K[key][d]
@@ -331,8 +362,8 @@ __global__ void __launch_bounds__(NT) attn_bwd_bf16_kernel(AttnBwdArgs a)
             for (int r = 0; r < 16; r++) qacc[r] = 0.f;
 #pragma unroll
             for (int t = 0; t < BN / 16; t++) {
-                // A: dS[q = lq][keys 16t + 8g..], from ds[key][q]; B: K[keys][d = 32w + lq]
-                const int kr1 = 16 * t + 8 * g + ts_; // keys 16t + 8g + e, e = 0..7 (natural order)
+                // A: dS[q = lq][keys 16t + 8g + e], from ds[key][q]; B: K[keys][d = 32w + lq]
+                const int kr1 = 16 * t + 8 * g + tsl;
                 const u32x2 s1 = lds_read_tr(&sm.ds[kr1 * SS + cpart]);
                 const u32x2 s2 = lds_read_tr(&sm.ds[(kr1 + 4) * SS + cpart]);
                 const u32x2 k1 = lds_read_tr(&sm.k[kr1 * RS + 32 * w + cpart]);
@@ -341,22 +372,24 @@ __global__ void __launch_bounds__(NT) attn_bwd_bf16_kernel(AttnBwdArgs a)
                               as_bf16x8(u32x4{k1[0], k1[1], k2[0], k2[1]}), qacc);
             }
             // C layout: lane holds d = 32w + lq, queries 8(r/4) + 4g + r%4
+            float *dqp = a.dq_acc + (int64_t)(o_b + q0 + 4 * g) * ld_do + h * D + 32 * w + lq;
+            const int qlim = L - q0 - 4 * g;
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const int qi = q0 + 8 * (r >> 2) + 4 * g + (r & 3);
-                if (qi < L) atomicAdd(&a.dq_acc[(int64_t)(o_b + qi) * ld_do + h * D + 32 * w + lq], qacc[r]);
+                const int qq = 8 * (r >> 2) + (r & 3);
+                if (qq < qlim) atomicAdd(dqp + (int64_t)qq * ld_do, qacc[r]);
             }
         }
         // drab_p: thread c sums diagonal c of the skewed tile (key - query =
-        // k0 - q0 + c - (BQ - 1)) over the rows that hold a key of this tile,
-        // adds it into the ring, and flushes the entry once no later block can
-        // reach it (key - query > k0 + BN - 1 - (q0 + BQ)  <=>  c > BN - 2).
+        // k0 - q0 + c - (BQ - 1)); cells outside the tile's keys are never
+        // written and stay 0.  The ring entry is flushed once no later block
+        // can reach it (key - query > k0 + BN - 1 - (q0 + BQ)  <=>  c > BN - 2).
         if (a.drab_p && tid < DK - 1) {
             const int c = tid;
-            const int rlo = c < BQ - 1 ? BQ - 1 - c : 0;
-            const int rhi = c > BN - 1 ? BN + BQ - 2 - c : BQ - 1;
-            float sum = 0.f;
-            for (int rq = rlo; rq <= rhi; rq++) sum += sm.dsk[rq * DK + c];
+            float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int rq = 0; rq < BQ; rq++) part[rq & 3] += sm.dsk[rq * DK + c];
+            const float sum = (part[0] + part[1]) + (part[2] + part[3]);
             const int dl = k0 - q0 + c - (BQ - 1);
             const int slot = dl & (RING - 1);
             const float tot = sm.ring[slot] + sum;
@@ -381,16 +414,18 @@ __global__ void __launch_bounds__(NT) attn_bwd_bf16_kernel(AttnBwdArgs a)
         for (int dl = lo + tid; dl <= hi; dl += NT) {
             const float v = sm.ring[dl & (RING - 1)];
             if (v != 0.f) {
-                int c = dl < -a.N ? -a.N : (dl > a.N ? a.N : dl);
-                atomicAdd(&a.drab_p[h * p_hs + c + a.N], v);
+                const int cl = dl < -a.N ? -a.N : (dl > a.N ? a.N : dl);
+                atomicAdd(&a.drab_p[h * p_hs + cl + a.N], v);
             }
         }
     }
-    if (a.drab_t && has_t && tid < TB) {
-        float s = 0.f;
-        for (int ww = 0; ww < 4; ww++)
-            for (int c = 0; c < TCOPY; c++) s += sm.dtab[ww][c][tid];
-        if (s != 0.f) atomicAdd(&a.drab_t[h * t_hs + tid], s);
+    if constexpr (DT && TM != 0) {
+        if (tid < TB) {
+            float s = 0.f;
+            for (int ww = 0; ww < 4; ww++)
+                for (int c = 0; c < TCOPY; c++) s += sm.dtab[ww][c][tid];
+            if (s != 0.f) atomicAdd(&a.drab_t[h * t_hs + tid], s);
+        }
     }
     // dK^T, dV^T: lane holds key mykey, d = 32 db + 8(r/4) + 4g + r%4
     if (kvalid) {
@@ -410,17 +445,52 @@ __global__ void __launch_bounds__(NT) attn_bwd_bf16_kernel(AttnBwdArgs a)
     }
 }
 
+} // namespace
+
+template <bool HP>
+__global__ void __launch_bounds__(NT) attn_bwd_bf16_kernel(AttnBwdArgs a)
+{
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    Smem &sm = *reinterpret_cast<Smem *>(smem_raw);
+    const int item = blockIdx.x;
+    if (item >= *a.n_items) return;
+    const int2 it = a.items[item];
+    const int b = it.x, tsched = it.y >> 8, h = it.y & 255;
+    const int o_b = a.offsets[b];
+    const int L = a.offsets[b + 1] - o_b;
+    const int nkt = (L + BN - 1) / BN;
+    const int k0 = (nkt - 1 - tsched) * BN; // most expensive key tile (k0 = 0) first
+    const bool has_t = a.ts != nullptr && a.rab_t != nullptr;
+    const int tid = threadIdx.x;
+    if (tid < 128) sm.rabt[tid] = has_t ? a.rab_t[h * a.rt_hs + tid] : 0.f;
+    if (tid < 32) sm.rabt_rev[tid] = has_t ? a.rab_t[h * a.rt_hs + 31 - tid] : 0.f;
+    // (the first barrier inside bwd_body orders these writes before use)
+    const bool dt = a.drab_t != nullptr;
+    if (!has_t) bwd_body<HP, 0, false>(a, sm, o_b, L, k0, h);
+    else if (a.wide[b] != 0) {
+        if (dt) bwd_body<HP, 2, true>(a, sm, o_b, L, k0, h);
+        else bwd_body<HP, 2, false>(a, sm, o_b, L, k0, h);
+    } else {
+        if (dt) bwd_body<HP, 1, true>(a, sm, o_b, L, k0, h);
+        else bwd_body<HP, 1, false>(a, sm, o_b, L, k0, h);
+    }
+}
+
 hipError_t launch_attn_bwd_bf16(const AttnBwdArgs &a, int max_items, hipStream_t st)
 {
     static bool init = false;
     const size_t smem = sizeof(Smem);
     if (!init) {
-        hipError_t e = hipFuncSetAttribute((const void *)attn_bwd_bf16_kernel,
+        hipError_t e = hipFuncSetAttribute((const void *)attn_bwd_bf16_kernel<true>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        if (e != hipSuccess) return e;
+        e = hipFuncSetAttribute((const void *)attn_bwd_bf16_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)smem);
         if (e != hipSuccess) return e;
         init = true;
     }
     if (max_items <= 0) return hipSuccess;
-    hipLaunchKernelGGL(attn_bwd_bf16_kernel, dim3(max_items), dim3(NT), smem, st, a);
+    if (a.rab_p) hipLaunchKernelGGL(attn_bwd_bf16_kernel<true>, dim3(max_items), dim3(NT), smem, st, a);
+    else hipLaunchKernelGGL(attn_bwd_bf16_kernel<false>, dim3(max_items), dim3(NT), smem, st, a);
     return hipGetLastError();
 }
