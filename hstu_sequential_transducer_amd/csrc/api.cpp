@@ -168,48 +168,14 @@ hstu_status debug_check(void *ws, hipStream_t st)
         if (_s != HSTU_OK) return _s;                                                                              \
     } while (0)
 
-} // namespace
-
-extern "C" {
-
-int32_t hstu_abi_version(void) { return HSTU_ABI_VERSION; }
-
-const char *hstu_last_error(void) { return g_err.c_str(); }
-
-size_t hstu_workspace_size(hstu_op op, const hstu_jagged *j, const hstu_dims *dims, int32_t d_model,
-                           int32_t total_cand)
+// Enqueue the forward (launcher, attention kernel, optional LayerNorm gate)
+// on validated arguments; `wb` is the workspace carved as `w`.
+hstu_status attn_fwd_launch(const hstu_jagged *j, const hstu_dims *dm, const hstu_bias *bias, hstu_cmat q, hstu_cmat k,
+                            hstu_cmat v, hstu_cmat u, hstu_mat out, float *o_save, float *ln_stats, char *wb,
+                            const AttnWs &w, hipStream_t st)
 {
-    if (check_jagged(j) != HSTU_OK || check_dims(dims) != HSTU_OK) return 0;
-    switch (op) {
-    case HSTU_OP_ATTN_FWD: return attn_ws(j, dims, fwd_tile(dims)).total;
-    case HSTU_OP_ATTN_BWD: return attn_ws(j, dims, BWD_BN).total;
-    default: break;
-    }
-    (void)d_model;
-    (void)total_cand;
-    fail(HSTU_ERR_ARG, "unknown op %d", (int)op);
-    return 0;
-}
-
-hstu_status hstu_attn_fwd(const hstu_jagged *j, const hstu_dims *dm, const hstu_bias *bias, hstu_cmat q, hstu_cmat k,
-                          hstu_cmat v, hstu_cmat u, hstu_mat out, float *o_save, float *ln_stats, void *ws,
-                          size_t ws_bytes, void *stream)
-{
-    TRY(check_jagged(j));
-    TRY(check_dims(dm));
-    TRY(check_bias(bias, j));
     const int H = dm->heads, d = dm->d_qk, F = H * dm->d_v;
-    TRY(check_view(q.ptr, q.ld, (int64_t)H * d, "q"));
-    TRY(check_view(k.ptr, k.ld, (int64_t)H * d, "k"));
-    TRY(check_view(v.ptr, v.ld, (int64_t)F, "v"));
-    TRY(check_view(u.ptr, u.ld, (int64_t)F, "u", false));
-    TRY(check_view(out.ptr, out.ld, (int64_t)F, "out"));
-    if (ln_stats && !u.ptr) return fail(HSTU_ERR_ARG, "ln_stats requires u (the epilogue)");
     const int tile = fwd_tile(dm);
-    const AttnWs w = attn_ws(j, dm, tile);
-    TRY(check_ws(ws, ws_bytes, w.total));
-    hipStream_t st = (hipStream_t)stream;
-    char *wb = (char *)ws;
     int *status = (int *)(wb + w.header), *n_items = status + 1;
     int2 *items = (int2 *)(wb + w.items);
     uint32_t *rel = (uint32_t *)(wb + w.rel);
@@ -265,10 +231,165 @@ hstu_status hstu_attn_fwd(const hstu_jagged *j, const hstu_dims *dm, const hstu_
         {
             ProfScope ps("ln_gate_fwd_kernel", st);
             e = launch_ln_gate_fwd(obuf, F, 1, 0, u.ptr, u.ld, dm->dtype == HSTU_BF16, out.ptr, out.ld, ln_stats, nullptr,
-                                   0, T, F, dm->ln_eps, status, st);
+                                   0, T, F, dm->ln_eps, nullptr, st);
         }
         TRY(launched(e, "LayerNorm gate kernel"));
     }
+    return HSTU_OK;
+}
+
+// Workspace of hstu_layer_fwd: the attention's, then f1's output Z [T][4Hd]
+// and the gate G [T][Hd] (storage dtype).
+struct LayerWs {
+    AttnWs attn;
+    size_t z, g, total;
+};
+
+LayerWs layer_ws(const hstu_jagged *j, const hstu_dims *dm)
+{
+    LayerWs w{};
+    w.attn = attn_ws(j, dm, fwd_tile(dm));
+    Carver c;
+    c.cur = w.attn.total;
+    const size_t es = elem_size(dm->dtype), T = (size_t)j->total, HD = (size_t)dm->heads * dm->d_qk;
+    w.z = c.take(T * 4 * HD * es);
+    w.g = c.take(T * HD * es);
+    w.total = c.cur;
+    return w;
+}
+
+hstu_status check_gemm_operand(const void *p, int64_t ld, hstu_dtype dt, const char *name)
+{
+    if (dt == HSTU_BF16 && ((((uintptr_t)p) & 15) != 0 || (ld % 8) != 0))
+        return fail(HSTU_ERR_ARG, "%s must be 16-byte aligned with ld a multiple of 8 (bf16)", name);
+    return HSTU_OK;
+}
+
+hstu_status check_layer(const hstu_layer *lay, const hstu_jagged *j, const hstu_dims *dm, int32_t D, int idx)
+{
+    if (!lay) return fail(HSTU_ERR_ARG, "layer %d is NULL", idx);
+    if (!lay->w1 || !lay->w2) return fail(HSTU_ERR_ARG, "layer %d: w1 and w2 are required", idx);
+    if (lay->phi1 != HSTU_ACT_SILU && lay->phi1 != HSTU_ACT_RELU) return fail(HSTU_ERR_ARG, "layer %d: bad phi1", idx);
+    TRY(check_bias(&lay->rab, j));
+    TRY(check_gemm_operand(lay->w1, D, dm->dtype, "w1"));
+    TRY(check_gemm_operand(lay->w2, (int64_t)dm->heads * dm->d_qk, dm->dtype, "w2"));
+    return HSTU_OK;
+}
+
+GemmArgs gemm_args(const void *A, int64_t lda, const void *W, const float *bias, void *C, int64_t ldc, bool c_f32,
+                   int M, int N, int K, int epi)
+{
+    GemmArgs g{};
+    g.A = A;
+    g.lda = lda;
+    g.W = W;
+    g.bias = bias;
+    g.C = C;
+    g.ldc = ldc;
+    g.c_f32 = c_f32;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.epi = epi;
+    return g;
+}
+
+hstu_status run_gemm(const GemmArgs &g, hstu_dtype dt, const char *name, hipStream_t st)
+{
+    ProfScope ps(name, st);
+    return launched(dt == HSTU_BF16 ? launch_gemm_bf16(g, st) : launch_gemm_f32(g, st), "GEMM kernel");
+}
+
+// M-FALCON plan: key splits so a small number of candidate tiles still fills
+// the chip; at most 16 splits.  Depends only on sizes known on the host.
+struct MfPlan {
+    int nsplit, kchunk, max_items;
+};
+
+MfPlan mf_plan(const hstu_jagged *hist, const hstu_dims *dm, int32_t M)
+{
+    MfPlan p{};
+    const int H = dm->heads, U = hist->batch;
+    const int tiles_est = (M + MF_TC - 1) / MF_TC;
+    int ns = (2048 + tiles_est * H - 1) / (tiles_est * H > 0 ? tiles_est * H : 1);
+    ns = ns < 1 ? 1 : (ns > 16 ? 16 : ns);
+    const int64_t span = hist->total > 0 ? hist->total : 1; // no user has more history than all users together
+    int64_t ch = (span + ns - 1) / ns;
+    ch = (ch + 63) / 64 * 64;
+    p.nsplit = ns;
+    p.kchunk = (int)(ch > 0 ? ch : 64);
+    // tiles <= M (one candidate per microbatch at worst) + U
+    p.max_items = (int)(((int64_t)M + U) * H * ns);
+    return p;
+}
+
+struct MfWs {
+    size_t header, items, z, part, g, x32, x16, total;
+};
+
+MfWs mf_ws(const hstu_jagged *hist, const hstu_dims *dm, int32_t D, int32_t M)
+{
+    MfWs w{};
+    const MfPlan p = mf_plan(hist, dm, M);
+    const size_t es = elem_size(dm->dtype), HD = (size_t)dm->heads * dm->d_qk;
+    Carver c;
+    w.header = c.take(256);
+    w.items = c.take((size_t)p.max_items * sizeof(int4));
+    w.z = c.take((size_t)M * 4 * HD * es);
+    w.part = c.take((size_t)p.nsplit * M * HD * 4);
+    w.g = c.take((size_t)M * HD * es);
+    w.x32 = c.take((size_t)M * D * 4);
+    w.x16 = c.take((size_t)M * D * es);
+    w.total = c.cur;
+    return w;
+}
+
+} // namespace
+
+extern "C" {
+
+int32_t hstu_abi_version(void) { return HSTU_ABI_VERSION; }
+
+const char *hstu_last_error(void) { return g_err.c_str(); }
+
+size_t hstu_workspace_size(hstu_op op, const hstu_jagged *j, const hstu_dims *dims, int32_t d_model,
+                           int32_t total_cand)
+{
+    if (check_jagged(j) != HSTU_OK || check_dims(dims) != HSTU_OK) return 0;
+    switch (op) {
+    case HSTU_OP_ATTN_FWD: return attn_ws(j, dims, fwd_tile(dims)).total;
+    case HSTU_OP_ATTN_BWD: return attn_ws(j, dims, BWD_BN).total;
+    case HSTU_OP_LAYER_FWD: return layer_ws(j, dims).total;
+    case HSTU_OP_MFALCON:
+        if (d_model < 1 || total_cand < 0) {
+            fail(HSTU_ERR_ARG, "d_model must be >= 1 and total_cand >= 0");
+            return 0;
+        }
+        return mf_ws(j, dims, d_model, total_cand).total;
+    default: break;
+    }
+    fail(HSTU_ERR_ARG, "unknown op %d", (int)op);
+    return 0;
+}
+
+hstu_status hstu_attn_fwd(const hstu_jagged *j, const hstu_dims *dm, const hstu_bias *bias, hstu_cmat q, hstu_cmat k,
+                          hstu_cmat v, hstu_cmat u, hstu_mat out, float *o_save, float *ln_stats, void *ws,
+                          size_t ws_bytes, void *stream)
+{
+    TRY(check_jagged(j));
+    TRY(check_dims(dm));
+    TRY(check_bias(bias, j));
+    const int H = dm->heads, d = dm->d_qk, F = H * dm->d_v;
+    TRY(check_view(q.ptr, q.ld, (int64_t)H * d, "q"));
+    TRY(check_view(k.ptr, k.ld, (int64_t)H * d, "k"));
+    TRY(check_view(v.ptr, v.ld, (int64_t)F, "v"));
+    TRY(check_view(u.ptr, u.ld, (int64_t)F, "u", false));
+    TRY(check_view(out.ptr, out.ld, (int64_t)F, "out"));
+    if (ln_stats && !u.ptr) return fail(HSTU_ERR_ARG, "ln_stats requires u (the epilogue)");
+    const AttnWs w = attn_ws(j, dm, fwd_tile(dm));
+    TRY(check_ws(ws, ws_bytes, w.total));
+    hipStream_t st = (hipStream_t)stream;
+    TRY(attn_fwd_launch(j, dm, bias, q, k, v, u, out, o_save, ln_stats, (char *)ws, w, st));
     TRY(debug_check(ws, st));
     return ok();
 }
@@ -381,9 +502,48 @@ hstu_status hstu_layer_fwd(const hstu_jagged *j, const hstu_dims *dm, int32_t d_
                            hstu_cmat x, hstu_mat y, hstu_mat k_cache, hstu_mat v_cache, void *ws, size_t ws_bytes,
                            void *stream)
 {
-    (void)j; (void)dm; (void)d_model; (void)layer; (void)x; (void)y; (void)k_cache; (void)v_cache; (void)ws;
-    (void)ws_bytes; (void)stream;
-    return fail(HSTU_ERR_UNSUPPORTED, "hstu_layer_fwd: not built yet");
+    TRY(check_jagged(j));
+    TRY(check_dims(dm));
+    if (d_model < 1) return fail(HSTU_ERR_ARG, "d_model must be >= 1");
+    TRY(check_layer(layer, j, dm, d_model, 0));
+    const int H = dm->heads, d = dm->d_qk, HD = H * d, D = d_model;
+    TRY(check_view(x.ptr, x.ld, D, "x"));
+    TRY(check_view(y.ptr, y.ld, D, "y"));
+    TRY(check_gemm_operand(x.ptr, x.ld, dm->dtype, "x"));
+    TRY(check_view(k_cache.ptr, k_cache.ld, HD, "k_cache", false));
+    TRY(check_view(v_cache.ptr, v_cache.ld, HD, "v_cache", false));
+    if (x.ptr == y.ptr) return fail(HSTU_ERR_ARG, "y may not alias x");
+    const LayerWs w = layer_ws(j, dm);
+    TRY(check_ws(ws, ws_bytes, w.total));
+    hipStream_t st = (hipStream_t)stream;
+    char *wb = (char *)ws;
+    const int T = j->total;
+    const hstu_dtype dt = dm->dtype;
+    const size_t es = elem_size(dt);
+    char *Z = wb + w.z, *G = wb + w.g;
+    // f1 + phi1 -> Z = U | V | Q | K, and this layer's K, V into the cache
+    GemmArgs g1 = gemm_args(x.ptr, x.ld, layer->w1, layer->b1, Z, 4 * HD, dt == HSTU_F32, T, 4 * HD, D,
+                            layer->phi1 == HSTU_ACT_RELU ? EPI_RELU : EPI_SILU);
+    g1.Ck = k_cache.ptr;
+    g1.ldck = k_cache.ld;
+    g1.k_lo = 3 * HD;
+    g1.Cv = v_cache.ptr;
+    g1.ldcv = v_cache.ld;
+    g1.v_lo = HD;
+    g1.kv_w = HD;
+    TRY(run_gemm(g1, dt, "gemm_f1", st));
+    // attention + LayerNorm(O) (.) U on views of Z
+    hstu_cmat zu{Z, 4 * HD}, zv{Z + (size_t)HD * es, 4 * HD}, zq{Z + (size_t)2 * HD * es, 4 * HD},
+        zk{Z + (size_t)3 * HD * es, 4 * HD};
+    hstu_mat gm{G, HD};
+    TRY(attn_fwd_launch(j, dm, &layer->rab, zq, zk, zv, zu, gm, nullptr, nullptr, wb, w.attn, st));
+    // y = x + G W2^T + b2
+    GemmArgs g2 = gemm_args(G, HD, layer->w2, layer->b2, y.ptr, y.ld, dt == HSTU_F32, T, D, HD, EPI_NONE);
+    g2.R16 = x.ptr;
+    g2.ldr = x.ld;
+    TRY(run_gemm(g2, dt, "gemm_f2", st));
+    TRY(debug_check(ws, st));
+    return ok();
 }
 
 hstu_status mfalcon_score(const hstu_jagged *hist, const hstu_dims *dm, int32_t d_model, int32_t n_layers,
@@ -391,10 +551,104 @@ hstu_status mfalcon_score(const hstu_jagged *hist, const hstu_dims *dm, int32_t 
                           const int32_t *cand_offsets, int32_t total_cand, const int64_t *cand_ts, hstu_cmat x_cand,
                           int32_t b_m, float *y_cand, void *ws, size_t ws_bytes, void *stream)
 {
-    (void)hist; (void)dm; (void)d_model; (void)n_layers; (void)layers; (void)k_cache; (void)v_cache;
-    (void)cand_offsets; (void)total_cand; (void)cand_ts; (void)x_cand; (void)b_m; (void)y_cand; (void)ws;
-    (void)ws_bytes; (void)stream;
-    return fail(HSTU_ERR_UNSUPPORTED, "mfalcon_score: not built yet");
+    TRY(check_jagged(hist));
+    TRY(check_dims(dm));
+    if (d_model < 1) return fail(HSTU_ERR_ARG, "d_model must be >= 1");
+    if (n_layers < 1) return fail(HSTU_ERR_ARG, "n_layers must be >= 1");
+    if (!layers || !k_cache || !v_cache) return fail(HSTU_ERR_ARG, "layers, k_cache and v_cache arrays are required");
+    if (!cand_offsets) return fail(HSTU_ERR_ARG, "cand_offsets is NULL");
+    if (total_cand < 0) return fail(HSTU_ERR_ARG, "total_cand must be >= 0");
+    if (b_m < 1) return fail(HSTU_ERR_ARG, "b_m must be >= 1 (got %d)", b_m);
+    if (!y_cand) return fail(HSTU_ERR_ARG, "y_cand is NULL");
+    if ((hist->ts == nullptr) != (cand_ts == nullptr))
+        return fail(HSTU_ERR_ARG, "history ts and cand_ts must both be given or both be NULL");
+    if (dm->heads > 32) return fail(HSTU_ERR_UNSUPPORTED, "M-FALCON supports at most 32 heads");
+    const int H = dm->heads, d = dm->d_qk, HD = H * d, D = d_model, M = total_cand;
+    TRY(check_view(x_cand.ptr, x_cand.ld, D, "x_cand"));
+    TRY(check_gemm_operand(x_cand.ptr, x_cand.ld, dm->dtype, "x_cand"));
+    for (int l = 0; l < n_layers; l++) {
+        TRY(check_layer(&layers[l], hist, dm, D, l));
+        TRY(check_view(k_cache[l].ptr, k_cache[l].ld, HD, "k_cache[l]"));
+        TRY(check_view(v_cache[l].ptr, v_cache[l].ld, HD, "v_cache[l]"));
+    }
+    const MfWs w = mf_ws(hist, dm, D, M);
+    const MfPlan p = mf_plan(hist, dm, M);
+    TRY(check_ws(ws, ws_bytes, w.total));
+    hipStream_t st = (hipStream_t)stream;
+    char *wb = (char *)ws;
+    int *status = (int *)(wb + w.header), *n_items = status + 1;
+    int4 *items = (int4 *)(wb + w.items);
+    const hstu_dtype dt = dm->dtype;
+    const size_t es = elem_size(dt);
+    char *Z = wb + w.z, *G = wb + w.g, *x16 = wb + w.x16;
+    float *part = (float *)(wb + w.part), *x32 = (float *)(wb + w.x32);
+    {
+        ProfScope ps("mfalcon_sched_kernel", st);
+        TRY(launched(launch_mfalcon_sched(hist->offsets, cand_offsets, hist->batch, M, H, b_m, p.nsplit, items,
+                                          n_items, status, p.max_items, st),
+                     "M-FALCON schedule kernel"));
+    }
+    for (int l = 0; l < n_layers; l++) {
+        const hstu_layer &lay = layers[l];
+        const bool last = l == n_layers - 1;
+        // candidate f1 + phi1 -> Z = U | V | Q | K
+        GemmArgs g1 = gemm_args(l == 0 ? x_cand.ptr : (const void *)x16, l == 0 ? x_cand.ld : D, lay.w1, lay.b1, Z,
+                                4 * HD, dt == HSTU_F32, M, 4 * HD, D,
+                                lay.phi1 == HSTU_ACT_RELU ? EPI_RELU : EPI_SILU);
+        TRY(run_gemm(g1, dt, "gemm_f1", st));
+        // history part of the attention, one partial sum per key split
+        MfalconArgs a{};
+        a.q = Z + (size_t)2 * HD * es;
+        a.ldz = 4 * HD;
+        a.kc = k_cache[l].ptr;
+        a.vc = v_cache[l].ptr;
+        a.ldkc = k_cache[l].ld;
+        a.ldvc = v_cache[l].ld;
+        a.hoff = hist->offsets;
+        a.hts = (lay.rab.rab_t && hist->ts) ? hist->ts : nullptr;
+        a.cts = (lay.rab.rab_t && hist->ts) ? cand_ts : nullptr;
+        a.rab_p = lay.rab.rab_p;
+        a.rp_hs = lay.rab.rab_p_hstride;
+        a.rab_t = lay.rab.rab_t;
+        a.rt_hs = lay.rab.rab_t_hstride;
+        a.H = H;
+        a.N = hist->n_max;
+        a.M = M;
+        a.d = d;
+        a.kchunk = p.kchunk;
+        a.items = items;
+        a.n_items = n_items;
+        a.part = part;
+        {
+            ProfScope ps("mfalcon_attn_kernel", st);
+            TRY(launched(launch_mfalcon_attn(a, p.max_items, dt == HSTU_BF16, st), "M-FALCON attention kernel"));
+        }
+        {
+            ProfScope ps("mfalcon_epilogue_kernel", st);
+            TRY(launched(launch_mfalcon_epilogue(part, p.nsplit, Z, 4 * HD, lay.rab.rab_p, lay.rab.rab_p_hstride,
+                                                 lay.rab.rab_t, lay.rab.rab_t_hstride,
+                                                 lay.rab.rab_t != nullptr && hist->ts != nullptr, hist->n_max,
+                                                 dm->ln_eps, G, HD, M, H, d, dt == HSTU_BF16, st),
+                         "M-FALCON epilogue kernel"));
+        }
+        // x = x + G W2^T + b2 in fp32; a storage-dtype copy feeds the next layer
+        GemmArgs g2 = gemm_args(G, HD, lay.w2, lay.b2, last ? (void *)y_cand : (void *)x32, D, true, M, D, HD,
+                                EPI_NONE);
+        if (l == 0) {
+            g2.R16 = x_cand.ptr;
+            g2.ldr = x_cand.ld;
+        } else {
+            g2.R32 = x32;
+            g2.ldr = D;
+        }
+        if (!last) {
+            g2.C16 = x16;
+            g2.ldc16 = D;
+        }
+        TRY(run_gemm(g2, dt, "gemm_f2", st));
+    }
+    TRY(debug_check(ws, st));
+    return ok();
 }
 
 } // extern "C"

@@ -79,59 +79,58 @@ hipError_t launch_scale_bf16(const bf16 *src, int64_t lds, bf16 *dst, int64_t ld
                              hipStream_t st);
 
 // ---- GEMM with fused epilogues (gemm.hip)
-// C[M][N] = epi(A[M][K] . W[N][K]^T + bias) (+ R), A/W/C storage dtype or fp32.
+// C[M][N] = act(A[M][K] . W[N][K]^T + bias) + R, A/W in the storage dtype.
 enum GemmEpi { EPI_NONE = 0, EPI_SILU = 1, EPI_RELU = 2 };
 struct GemmArgs {
     const void *A;
     int64_t lda;
-    const void *W;              // [N][K] ([out][in])
+    const void *W;              // [N][K] ([out][in]), ld = K
     const float *bias;          // [N] or NULL
-    const void *R;              // residual [M][N] or NULL (added after the activation)
+    const float *R32;           // fp32 residual [M][N] (ld ldr) or NULL
+    const void *R16;            // storage-dtype residual (ld ldr) or NULL
     int64_t ldr;
-    bool r_f32;                 // residual is fp32 (else storage dtype)
     void *C;
     int64_t ldc;
-    bool c_f32;                 // output fp32 (else storage dtype)
+    bool c_f32;                 // C is fp32 (else storage dtype)
+    void *C16;                  // optional storage-dtype copy of C
+    int64_t ldc16;
     int M, N, K;
     int epi;
-    // optional second output: columns [split_lo, split_hi) also copied to C2
-    // (used to write this layer's K and V into the M-FALCON cache)
-    void *C2a;
-    int64_t ldc2a;
-    int c2a_lo;
-    void *C2b;
-    int64_t ldc2b;
-    int c2b_lo;
-    int c2_width;
+    // optional copies of columns [k_lo, k_lo + kv_w) and [v_lo, v_lo + kv_w)
+    void *Ck;
+    int64_t ldck;
+    int k_lo;
+    void *Cv;
+    int64_t ldcv;
+    int v_lo;
+    int kv_w;
 };
 hipError_t launch_gemm_bf16(const GemmArgs &g, hipStream_t st);
 hipError_t launch_gemm_f32(const GemmArgs &g, hipStream_t st);
 
 // ---- M-FALCON (mfalcon.hip)
+constexpr int MF_TC = 128; // candidates per attention tile
 struct MfalconArgs {
-    const void *q;              // candidate Q [M][H*d] view (ld)
-    const void *k;              // candidate K
-    const void *v;              // candidate V
+    const void *q;              // candidate Q view of the f1 output [M][4*H*d] (ld ldz)
     int64_t ldz;
-    const void *kc, *vc;        // cached history K, V [T_hist][H][d]
+    const void *kc, *vc;        // this layer's cached history K, V [T_hist][H][d]
     int64_t ldkc, ldvc;
     const int32_t *hoff;        // [U+1]
-    const int32_t *coff;        // [U+1]
     const int64_t *hts;         // [T_hist] or NULL
     const int64_t *cts;         // [U] or NULL
     const float *rab_p;
     int64_t rp_hs;
     const float *rab_t;
     int64_t rt_hs;
-    int H, N, U, M;
-    float inv_n;
-    int ctile;                  // candidates per workgroup tile
+    int H, N, M, d;
     int kchunk;                 // history keys per split
-    int nsplit;                 // key splits
-    const int4 *items;          // (user, cand tile start, head, split)
+    const int4 *items;          // (user, first row, rows, head << 16 | split)
     const int *n_items;
     float *part;                // [nsplit][M][H*d] fp32 partial sums
 };
-hipError_t launch_mfalcon_sched(const int32_t *hoff, const int32_t *coff, int U, int M, int H, int ctile, int kchunk,
-                                int nsplit, int4 *items, int *n_items, int *status, int max_items, hipStream_t st);
+hipError_t launch_mfalcon_sched(const int32_t *hoff, const int32_t *coff, int U, int M, int H, int b_m, int nsplit,
+                                int4 *items, int *n_items, int *status, int max_items, hipStream_t st);
 hipError_t launch_mfalcon_attn(const MfalconArgs &a, int max_items, bool bf16io, hipStream_t st);
+hipError_t launch_mfalcon_epilogue(const float *part, int nsplit, const void *Z, int64_t ldz, const float *rab_p,
+                                   int64_t rp_hs, const float *rab_t, int64_t rt_hs, bool use_t, int N, float eps,
+                                   void *G, int64_t ldg, int M, int H, int d, bool bf16io, hipStream_t st);

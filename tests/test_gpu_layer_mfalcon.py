@@ -1,0 +1,204 @@
+"""GPU parity of hstu_layer_fwd and mfalcon_score (through the C ABI) against
+the fp64 oracle: the layer (f1 + phi1, attention, LayerNorm gate, f2 +
+residual), its K/V cache, and per-candidate M-FALCON scoring."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import BF16_TOL, F32_TOL, bf16_bound, host, rel_err, t_act, t_f32, t_i32, t_i64
+
+pytestmark = pytest.mark.gpu
+
+hs = pytest.importorskip("hstu_sequential_transducer_amd")
+
+
+def dev_layer(lay, dtype):
+    return dict(w1=t_act(lay.w1, dtype), b1=t_f32(lay.b1), w2=t_act(lay.w2, dtype), b2=t_f32(lay.b2),
+                rab_p=t_f32(lay.rab_p), rab_t=t_f32(lay.rab_t), phi1=0)
+
+
+def branch_err(y_gpu, y_ref, x):
+    """max |(y - x) - (y_ref - x)| / RMS(y_ref - x): the layer's branch,
+    which the residual would otherwise swamp."""
+    b_ref = np.asarray(y_ref, np.float64) - x
+    return rel_err(np.asarray(y_gpu, np.float64) - x, b_ref)
+
+
+def branch_bound_bf16(y_ref, x):
+    """2e-2 plus the bf16 storage rounding of y (2^-8 of |y|) measured against
+    the branch's RMS."""
+    b = np.asarray(y_ref, np.float64) - x
+    return BF16_TOL + 2.0 ** -8 * np.abs(y_ref).max() / np.sqrt(np.mean(b ** 2))
+
+
+def branch_bound_act_bf16(y_ref, x):
+    """For an fp32 output computed through bf16-stored activations (f1's
+    U, V, Q, K, the gate G, hidden states between layers): 2e-2 plus 2^-8 of
+    the branch's peak -- each stored activation carries a rounding of up to
+    2^-8 of its own magnitude, so the error tracks the largest elements."""
+    b = np.asarray(y_ref, np.float64) - x
+    return BF16_TOL + 2.0 ** -8 * np.abs(b).max() / np.sqrt(np.mean(b ** 2))
+
+
+def branch_bound_f32(y_ref, x):
+    """fp32 output: 1e-4 plus the fp32 rounding of y itself (2^-24 of |y|)
+    measured against the branch's RMS."""
+    b = np.asarray(y_ref, np.float64) - x
+    return F32_TOL + 2.0 ** -24 * np.abs(y_ref).max() / np.sqrt(np.mean(b ** 2))
+
+
+def run_layer(w, lay, x, kv=False):
+    T = w.total
+    off, ts = t_i32(w.offsets), t_i64(w.ts)
+    xd = t_act(x, w.dtype)
+    td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    kc = torch.empty((T, w.heads * w.d), dtype=td, device=xd.device) if kv else None
+    vc = torch.empty((T, w.heads * w.d), dtype=td, device=xd.device) if kv else None
+    y = hs.layer_fwd(off, T, ts, xd, dev_layer(lay, w.dtype), w.heads, w.d, w.n_max, k_cache=kc, v_cache=vc)
+    torch.cuda.synchronize()
+    return y, kc, vc
+
+
+def test_layer_tiny_fp32():
+    """fp32 layer: B=4, lengths {17, 64, 33, 5}, N_max=64, D=64, H=2, d=32."""
+    w = synth.tiny_layer_f32()
+    lay = w.layers[0]
+    y, kc, vc = run_layer(w, lay, w.x, kv=True)
+    ref, K, V = oracle.layer_fwd(w.offsets, w.ts, w.x, lay, w.heads, w.d, w.n_max, return_kv=True)
+    e = branch_err(host(y), ref, w.x)
+    print("tiny fp32 branch err", e, "bound", branch_bound_f32(ref, w.x), "y err", rel_err(host(y), ref))
+    assert e <= branch_bound_f32(ref, w.x)
+    assert rel_err(host(y), ref) <= F32_TOL
+    assert rel_err(host(kc), K.reshape(w.total, -1)) <= F32_TOL
+    assert rel_err(host(vc), V.reshape(w.total, -1)) <= F32_TOL
+
+
+@pytest.mark.parametrize("strong", [False, True])
+def test_layer_bf16_ragged(strong):
+    """bf16 layer, D=512, H=4, d=128, ragged lengths; strong=True uses weights
+    of std 1/sqrt(fan_in) so the branch is not tiny next to the residual."""
+    L = np.array([100, 300, 1, 64, 129])
+    w = synth.layer_workload("layer", 31, L, d_model=512, heads=4, d=128, n_max=512, dtype="bf16")
+    lay = w.layers[0]
+    if strong:
+        rng = np.random.default_rng(5)
+        lay.w1 = synth.round_bf16(rng.standard_normal(lay.w1.shape).astype(np.float32) / math.sqrt(512))
+        lay.w2 = synth.round_bf16(rng.standard_normal(lay.w2.shape).astype(np.float32) / math.sqrt(512))
+    y, kc, vc = run_layer(w, lay, w.x, kv=True)
+    ref, K, V = oracle.layer_fwd(w.offsets, w.ts, w.x, lay, w.heads, w.d, w.n_max, return_kv=True)
+    e = branch_err(host(y), ref, w.x)
+    print("bf16 layer branch err", e, "bound", branch_bound_bf16(ref, w.x), "y err", rel_err(host(y), ref))
+    assert rel_err(host(y), ref) <= bf16_bound(ref)
+    assert e <= branch_bound_bf16(ref, w.x)
+    Kr, Vr = K.reshape(w.total, -1), V.reshape(w.total, -1)
+    assert rel_err(host(kc), Kr) <= bf16_bound(Kr)
+    assert rel_err(host(vc), Vr) <= bf16_bound(Vr)
+
+
+# ------------------------------------------------------------------ M-FALCON
+
+def gpu_mfalcon(w, b_m=None, x_cand=None, cand_subset=None):
+    """Build the per-layer K/V cache with hstu_layer_fwd on the histories, then
+    score the candidates with mfalcon_score.  Returns y [M][D] (host fp64)."""
+    T = w.total
+    off, ts = t_i32(w.offsets), t_i64(w.ts)
+    td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    layers = [dev_layer(l, w.dtype) for l in w.layers]
+    h = t_act(w.x, w.dtype)
+    kcs, vcs = [], []
+    for lay in layers:
+        kc = torch.empty((T, w.heads * w.d), dtype=td, device=h.device)
+        vc = torch.empty_like(kc)
+        h = hs.layer_fwd(off, T, ts, h, lay, w.heads, w.d, w.n_max, k_cache=kc, v_cache=vc)
+        kcs.append(kc)
+        vcs.append(vc)
+    xc = t_act(w.x_cand if x_cand is None else x_cand, w.dtype)
+    M = xc.shape[0]
+    y = hs.mfalcon_score(off, T, ts, layers, kcs, vcs, t_i32(w.cand_offsets), M, t_i64(w.cand_ts), xc,
+                         b_m or w.b_m, w.heads, w.d, w.n_max)
+    torch.cuda.synchronize()
+    return y
+
+
+def oracle_mfalcon(w, cand_rows=None):
+    kv = oracle.history_cache(w.offsets, w.ts, w.x, w.layers, w.heads, w.d, w.n_max)
+    if cand_rows is None:
+        return oracle.mfalcon(w.offsets, w.ts, w.cand_offsets, w.cand_ts, w.layers, kv, w.x_cand, w.heads, w.d,
+                              w.n_max)
+    # score only the listed candidate rows (each keeps its own user)
+    users = np.searchsorted(w.cand_offsets, cand_rows, side="right") - 1
+    order = np.argsort(users, kind="stable")
+    rows, us = np.asarray(cand_rows)[order], users[order]
+    counts = np.bincount(us, minlength=len(w.lengths))
+    y = oracle.mfalcon(w.offsets, w.ts, synth.offsets_of(counts), w.cand_ts, w.layers, kv, w.x_cand[rows], w.heads,
+                       w.d, w.n_max)
+    out = np.zeros_like(y)
+    out[order] = y
+    return out
+
+
+def small_mfalcon(seed=41, hist=(100, 300, 0), cands=(37, 130, 5), layers=2):
+    w = synth.mfalcon_workload("mf-small", seed, np.array(hist), cands_per_user=1, n_max=512, n_layers=layers)
+    # varying candidate counts per user
+    rng = np.random.default_rng(seed + 1)
+    counts = np.array(cands)
+    w.cand_offsets = synth.offsets_of(counts)
+    w.x_cand = synth.round_bf16(rng.standard_normal((int(counts.sum()), w.d_model)).astype(np.float32))
+    return w
+
+
+def test_mfalcon_small_matches_per_candidate_oracle():
+    w = small_mfalcon()
+    y = host(gpu_mfalcon(w))
+    ref = oracle_mfalcon(w)
+    e = branch_err(y, ref, w.x_cand)
+    print("mfalcon branch err", e, "bound", branch_bound_act_bf16(ref, w.x_cand), "y err", rel_err(y, ref))
+    assert rel_err(y, ref) <= BF16_TOL
+    assert e <= branch_bound_act_bf16(ref, w.x_cand)
+
+
+def test_mfalcon_microbatch_size_invariant_bitwise():
+    w = small_mfalcon(seed=42)
+    ys = [gpu_mfalcon(w, b_m=bm) for bm in (1, 7, 128, 256, 1024)]
+    for y in ys[1:]:
+        assert torch.equal(y, ys[0])
+
+
+def test_mfalcon_candidates_independent_and_permutation_equivariant():
+    w = small_mfalcon(seed=43, hist=(200,), cands=(50,), layers=1)
+    y0 = gpu_mfalcon(w)
+    xc = w.x_cand.copy()
+    perm = np.random.default_rng(1).permutation(50)
+    yp = gpu_mfalcon(w, x_cand=xc[perm])
+    assert torch.equal(yp, y0[torch.from_numpy(perm).to(y0.device)])
+    xc2 = xc.copy()
+    xc2[1:] = synth.round_bf16((np.random.default_rng(2).standard_normal(xc2[1:].shape) * 3).astype(np.float32))
+    y2 = gpu_mfalcon(w, x_cand=xc2)
+    assert torch.equal(y2[0], y0[0])
+
+
+def test_mfalcon_fp32_tiny():
+    w = synth.mfalcon_workload("mf-f32", 44, np.array([17, 40]), cands_per_user=6, d_model=64, heads=2, d=32,
+                               n_max=64, n_layers=2, b_m=4, dtype="f32")
+    y = host(gpu_mfalcon(w))
+    ref = oracle_mfalcon(w)
+    e = branch_err(y, ref, w.x_cand)
+    assert rel_err(y, ref) <= F32_TOL
+    assert e <= branch_bound_f32(ref, w.x_cand), e
+
+
+def test_mfalcon_one_user_4096_full_launch_sampled():
+    """One user, history 4096, m = 1024 candidates, 2 layers, b_m = 256: the
+    full launch; the oracle scores 48 sampled candidates."""
+    w = synth.mfalcon_1user()
+    y = host(gpu_mfalcon(w))
+    rows = np.sort(np.random.default_rng(7).choice(w.x_cand.shape[0], size=48, replace=False))
+    ref = oracle_mfalcon(w, rows)
+    e = branch_err(y[rows], ref, w.x_cand[rows])
+    print("mfalcon 4096 branch err", e, "y err", rel_err(y[rows], ref))
+    assert rel_err(y[rows], ref) <= BF16_TOL
+    assert e <= branch_bound_act_bf16(ref, w.x_cand[rows])
