@@ -37,7 +37,11 @@ constexpr int D = 128;
 constexpr int BN = BWD_BN; // 128 keys per workgroup
 constexpr int BQ = 32;     // queries per block
 constexpr int NT = 256;
-constexpr int RS = 136;    // LDS row stride (bf16) of Q, dO and K tiles
+// LDS row strides (bf16 elements), from measured gfx950 LDS throughput: Q and
+// dO are read both as 16-byte operands (fast at 8 mod 16 elements) and
+// transposed (fast at 160, fair at 168); K is only read transposed.
+constexpr int RS = 168;    // Q, dO tiles
+constexpr int KS = 160;    // K tile
 constexpr int SS = 40;     // LDS row stride (bf16) of the dS tile [key][query]
 constexpr int WIN = 160;   // rab_p window per block (BQ + BN - 1 used)
 constexpr int RING = 256;  // drab_p ring (power of two >= WIN + BQ)
@@ -45,21 +49,24 @@ constexpr int DK = 160;    // columns of the skewed dS tile: key - query + BQ - 
 constexpr int TB = 64;     // time buckets that int64 differences can reach
 constexpr int TCOPY = 4;   // copies of each wave's drab_t table
 constexpr float NLOG2E = -1.4426950408889634f;
+constexpr float NLN2 = -0.69314718055994531f;
 
-struct Stage {
-    bf16 q[BQ * RS];
-    bf16 dO[BQ * RS];
-    bf16 dOl[BQ * RS]; // low part of dO' (dO' = dO + dOl to ~16 bits)
+// Every LDS array is 16-byte aligned so operand reads compile to ds_read_b128
+// (8-byte alignment turns them into ds_read2_b64, several times slower).
+struct alignas(16) Stage {
+    alignas(16) bf16 q[BQ * RS];
+    alignas(16) bf16 dO[BQ * RS];
+    alignas(16) bf16 dOl[BQ * RS]; // low part of dO' (dO' = dO + dOl to ~16 bits)
     float win[WIN];
     uint32_t qt[BQ];
     int64_t qt64[BQ];
     uint32_t qtmin, qtmax; // over the block's valid queries
 };
-struct Smem {
-    bf16 k[BN * RS];
+struct alignas(16) Smem {
+    alignas(16) bf16 k[BN * KS];
     Stage st[2];
-    bf16 ds[BN * SS];
-    float dsk[BQ * DK]; // fp32 dS skewed: [query][key - query + BQ - 1]
+    alignas(16) bf16 ds[BN * SS];
+    alignas(16) float dsk[BQ * DK]; // fp32 dS skewed: [query][key - query + BQ - 1]
     float ring[RING];
     float dtab[4][TCOPY][TB];
     float rabt_rev[32];
@@ -100,26 +107,31 @@ DEV void bwd_pointwise(const floatx16 &sacc, const floatx16 &pacc, uint32_t (&pp
         for (int u = 0; u < 2; u++) {
             const int rr = r + u;
             const int cr = 8 * (rr >> 2) + (rr & 3);
-            float x = sacc[rr];
-            if constexpr (HP) x += ln.win[-cr];
+            // x' = -log2(e) * x (tables staged pre-scaled), sg = sigmoid(x),
+            // p' = x' sg = -log2(e) SiLU(x) (the -ln 2 goes into dV's final scale),
+            // dS = dP sg (1 + x (1 - sg)) = dP (sg - ln2 (p' - p' sg)).
+            float b = 0.f;
+            if constexpr (HP) b = ln.win[-cr];
             int bucket = 0;
             if constexpr (TM == 1) {
                 if constexpr (UNI) {
-                    x += ubias;
+                    b += ubias;
                 } else {
                     const uint32_t tq = ln.qt[cr];
                     const uint32_t dd1 = (tq > ln.tk ? tq - ln.tk : ln.tk - tq) + 1u;
                     const int cz = __builtin_clz(dd1);
-                    x += rabt_rev[cz];
+                    b += rabt_rev[cz];
                     bucket = 31 - cz;
                 }
             } else if constexpr (TM == 2) {
                 bucket = time_bucket64(ln.qt64[cr] - ln.tk64);
-                x += rabt[bucket];
+                b += rabt[bucket];
             }
-            const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * NLOG2E));
+            const float x = __builtin_fmaf(sacc[rr], NLOG2E, b);
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x));
             float p = x * sg;
-            float ds = pacc[rr] * sg * __builtin_fmaf(x, 1.0f - sg, 1.0f);
+            const float t = __builtin_fmaf(-p, sg, p);
+            float ds = pacc[rr] * __builtin_fmaf(t, NLN2, sg);
             if constexpr (DIAG) {
                 if (cr < ln.dmask) {
                     p = 0.f;
@@ -158,7 +170,7 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
             const int key = k0 + pass * 16 + lc;
             const bool ok = key < L;
             u32x4 x = ok ? *(const u32x4 *)(K + (int64_t)(o_b + key) * a.ldk + h * D + le * 8) : u32x4{0, 0, 0, 0};
-            *(u32x4 *)&sm.k[(pass * 16 + lc) * RS + le * 8] = x;
+            *(u32x4 *)&sm.k[(pass * 16 + lc) * KS + le * 8] = x;
         }
     }
     const int mykey = k0 + 32 * w + lq;
@@ -215,7 +227,7 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
             if (tid < WIN) {
                 int dl = k0 - q0 - (BQ - 1) + tid; // key - query of window slot tid
                 dl = dl < -a.N ? -a.N : (dl > a.N ? a.N : dl);
-                wreg = a.rab_p[h * a.rp_hs + dl + a.N];
+                wreg = NLOG2E * a.rab_p[h * a.rp_hs + dl + a.N];
             }
         }
         if constexpr (TM != 0) {
@@ -366,8 +378,8 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
                 const int kr1 = 16 * t + 8 * g + tsl;
                 const u32x2 s1 = lds_read_tr(&sm.ds[kr1 * SS + cpart]);
                 const u32x2 s2 = lds_read_tr(&sm.ds[(kr1 + 4) * SS + cpart]);
-                const u32x2 k1 = lds_read_tr(&sm.k[kr1 * RS + 32 * w + cpart]);
-                const u32x2 k2 = lds_read_tr(&sm.k[(kr1 + 4) * RS + 32 * w + cpart]);
+                const u32x2 k1 = lds_read_tr(&sm.k[kr1 * KS + 32 * w + cpart]);
+                const u32x2 k2 = lds_read_tr(&sm.k[(kr1 + 4) * KS + 32 * w + cpart]);
                 qacc = mfma32(as_bf16x8(u32x4{s1[0], s1[1], s2[0], s2[1]}),
                               as_bf16x8(u32x4{k1[0], k1[1], k2[0], k2[1]}), qacc);
             }
@@ -437,8 +449,8 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
                 const int d0 = db * 32 + 8 * gr + 4 * g;
                 const u32x2 kk = {pack2_bf16(dk_acc[db][4 * gr], dk_acc[db][4 * gr + 1]),
                                   pack2_bf16(dk_acc[db][4 * gr + 2], dk_acc[db][4 * gr + 3])};
-                const u32x2 vv = {pack2_bf16(dv_acc[db][4 * gr], dv_acc[db][4 * gr + 1]),
-                                  pack2_bf16(dv_acc[db][4 * gr + 2], dv_acc[db][4 * gr + 3])};
+                const u32x2 vv = {pack2_bf16(NLN2 * dv_acc[db][4 * gr], NLN2 * dv_acc[db][4 * gr + 1]),
+                                  pack2_bf16(NLN2 * dv_acc[db][4 * gr + 2], NLN2 * dv_acc[db][4 * gr + 3])};
                 *(u32x2 *)(a.dk + row * a.lddk + h * D + d0) = kk;
                 *(u32x2 *)(a.dv + row * a.lddv + h * D + d0) = vv;
             }
@@ -462,8 +474,8 @@ __global__ void __launch_bounds__(NT) attn_bwd_bf16_kernel(AttnBwdArgs a)
     const int k0 = (nkt - 1 - tsched) * BN; // most expensive key tile (k0 = 0) first
     const bool has_t = a.ts != nullptr && a.rab_t != nullptr;
     const int tid = threadIdx.x;
-    if (tid < 128) sm.rabt[tid] = has_t ? a.rab_t[h * a.rt_hs + tid] : 0.f;
-    if (tid < 32) sm.rabt_rev[tid] = has_t ? a.rab_t[h * a.rt_hs + 31 - tid] : 0.f;
+    if (tid < 128) sm.rabt[tid] = has_t ? NLOG2E * a.rab_t[h * a.rt_hs + tid] : 0.f;
+    if (tid < 32) sm.rabt_rev[tid] = has_t ? NLOG2E * a.rab_t[h * a.rt_hs + 31 - tid] : 0.f;
     // (the first barrier inside bwd_body orders these writes before use)
     const bool dt = a.drab_t != nullptr;
     if (!has_t) bwd_body<HP, 0, false>(a, sm, o_b, L, k0, h);

@@ -33,19 +33,23 @@ constexpr int D = 128;
 constexpr int BM = FWD_BM; // 128 query rows
 constexpr int BN = 64;     // keys per LDS tile
 constexpr int NT = 256;
-constexpr int RS = 136;    // LDS row stride (bf16 elements) of K and V tiles
+// LDS row strides (bf16 elements), from measured gfx950 LDS throughput: the
+// 16-byte K-operand reads are conflict-free when the stride is 8 mod 16
+// elements; the transposing V reads are fastest at a stride of 160.
+constexpr int RS = 136;    // K tile
+constexpr int VS = 160;    // V tile
 constexpr int WIN = 192;   // rab_p window entries per tile (BM + BN - 1 used)
 constexpr float NLOG2E = -1.4426950408889634f;
 constexpr float NLN2 = -0.69314718055994531f;
 
-struct Stage {
-    bf16 k[BN * RS];
-    bf16 v[BN * RS];
+struct alignas(16) Stage {
+    alignas(16) bf16 k[BN * RS];
+    alignas(16) bf16 v[BN * VS];
     float win[WIN];        // -log2(e) * rab_p[clip(key - query)]
     uint32_t kt[BN];       // sequence-relative key times
     uint32_t kmin[2], kmax[2]; // per 32-key half, over valid keys
 };
-struct Smem {
+struct alignas(16) Smem {
     Stage st[2];
     float rabt_rev[32]; // -log2(e) * rab_t[31 - c], indexed by clz(|dt| + 1)
     float rabt[128];    // -log2(e) * rab_t
@@ -178,7 +182,7 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h)
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             *(u32x4 *)&S.k[(lc * 4 + i) * RS + le * 8] = kreg[i];
-            *(u32x4 *)&S.v[(lc * 4 + i) * RS + le * 8] = vreg[i];
+            *(u32x4 *)&S.v[(lc * 4 + i) * VS + le * 8] = vreg[i];
         }
         if constexpr (HP)
             if (tid < WIN) S.win[tid] = wreg;
@@ -204,19 +208,38 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h)
     for (int kt = 0; kt < nkt; kt++) {
         if (kt + 1 < nkt) gload(kt + 1);
         const Stage &S = sm.st[kt & 1];
+        // Both 32-key blocks' S^T first (two independent MFMA chains, interleaved),
+        // so the matrix core works on block 1 while the VALU runs block 0's
+        // element-wise step, and on block 0's PV while block 1's runs.
+        bool need[2];
+        floatx16 sacc[2];
 #pragma unroll
         for (int kb = 0; kb < 2; kb++) {
             const int kstart = kt * BN + kb * 32;
-            if (kstart > qstart + 31 || qstart >= L) continue; // wave-uniform
-            const bool diag = kstart + 31 > qstart;
-            floatx16 sacc;
+            need[kb] = !(kstart > qstart + 31 || qstart >= L); // wave-uniform
 #pragma unroll
-            for (int r = 0; r < 16; r++) sacc[r] = 0.f;
+            for (int r = 0; r < 16; r++) sacc[kb][r] = 0.f;
+        }
+        if (need[0] && need[1]) {
 #pragma unroll
             for (int s = 0; s < 8; s++) {
-                const bf16x8 ka = *(const bf16x8 *)&S.k[(kb * 32 + lq) * RS + s * 16 + g * 8];
-                sacc = mfma32(ka, qreg[s], sacc);
+                const bf16x8 ka0 = *(const bf16x8 *)&S.k[lq * RS + s * 16 + g * 8];
+                const bf16x8 ka1 = *(const bf16x8 *)&S.k[(32 + lq) * RS + s * 16 + g * 8];
+                sacc[0] = mfma32(ka0, qreg[s], sacc[0]);
+                sacc[1] = mfma32(ka1, qreg[s], sacc[1]);
             }
+        } else if (need[0]) {
+#pragma unroll
+            for (int s = 0; s < 8; s++) {
+                const bf16x8 ka0 = *(const bf16x8 *)&S.k[lq * RS + s * 16 + g * 8];
+                sacc[0] = mfma32(ka0, qreg[s], sacc[0]);
+            }
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++) {
+            const int kstart = kt * BN + kb * 32;
+            if (!need[kb]) continue;
+            const bool diag = kstart + 31 > qstart;
             const float *win_lane = &S.win[kb * 32 + 4 * g - w * 32 - lq + (BM - 1)];
             const uint32_t *kt_lane = &S.kt[kb * 32 + 4 * g];
             const int kbase = kstart + 4 * g;
@@ -236,13 +259,13 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h)
             }
             uint32_t pk[8];
             if (diag)
-                pointwise<HP, TM, true, false>(sacc, pk, win_lane, kt_lane, sm.rabt_rev, sm.rabt, tq, tq64, tsk, kbase,
-                                               L - 1, ubias, lq - 4 * g);
+                pointwise<HP, TM, true, false>(sacc[kb], pk, win_lane, kt_lane, sm.rabt_rev, sm.rabt, tq, tq64, tsk,
+                                               kbase, L - 1, ubias, lq - 4 * g);
             else if (TM == 1 && uni)
-                pointwise<HP, TM, false, true>(sacc, pk, win_lane, kt_lane, sm.rabt_rev, sm.rabt, tq, tq64, tsk, kbase,
-                                               L - 1, ubias, 0);
+                pointwise<HP, TM, false, true>(sacc[kb], pk, win_lane, kt_lane, sm.rabt_rev, sm.rabt, tq, tq64, tsk,
+                                               kbase, L - 1, ubias, 0);
             else
-                pointwise<HP, TM, false, false>(sacc, pk, win_lane, kt_lane, sm.rabt_rev, sm.rabt, tq, tq64, tsk,
+                pointwise<HP, TM, false, false>(sacc[kb], pk, win_lane, kt_lane, sm.rabt_rev, sm.rabt, tq, tq64, tsk,
                                                 kbase, L - 1, ubias, 0);
 #pragma unroll
             for (int m = 0; m < 2; m++) {
@@ -251,8 +274,8 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h)
                 const int key1 = kb * 32 + 16 * m + 4 * g + tsl;
 #pragma unroll
                 for (int db = 0; db < 4; db++) {
-                    const u32x2 r1 = lds_read_tr(&S.v[key1 * RS + db * 32 + cpart]);
-                    const u32x2 r2 = lds_read_tr(&S.v[(key1 + 8) * RS + db * 32 + cpart]);
+                    const u32x2 r1 = lds_read_tr(&S.v[key1 * VS + db * 32 + cpart]);
+                    const u32x2 r2 = lds_read_tr(&S.v[(key1 + 8) * VS + db * 32 + cpart]);
                     const bf16x8 va = as_bf16x8(u32x4{r1[0], r1[1], r2[0], r2[1]});
                     oacc[db] = mfma32(va, pb, oacc[db]);
                 }
@@ -286,7 +309,7 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h)
 } // namespace
 
 template <bool HP>
-__global__ void __launch_bounds__(NT) attn_fwd_bf16_kernel(AttnFwdArgs a)
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_fwd_bf16_kernel(AttnFwdArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     Smem &sm = *reinterpret_cast<Smem *>(smem_raw);

@@ -17,12 +17,14 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 DEV bf16 to_bf16(float x) { return (bf16)x; }
 DEV float from_bf16(bf16 x) { return (float)x; }
 
-// Two fp32 -> one dword of two bf16 (lo in bits 0..15).
+// Two fp32 -> one dword of two bf16 (lo in bits 0..15), round to nearest even:
+// a single v_cvt_pk_bf16_f32.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 DEV uint32_t pack2_bf16(float lo, float hi)
 {
-    bf16 a = (bf16)lo, b = (bf16)hi;
-    uint16_t ua = __builtin_bit_cast(uint16_t, a), ub = __builtin_bit_cast(uint16_t, b);
-    return (uint32_t)ua | ((uint32_t)ub << 16);
+    const bf16x2 r = __builtin_convertvector((f32x2){lo, hi}, bf16x2);
+    return __builtin_bit_cast(uint32_t, r);
 }
 
 DEV float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }

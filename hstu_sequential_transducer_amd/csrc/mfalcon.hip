@@ -25,7 +25,8 @@ constexpr int D = 128;
 constexpr int TC = MF_TC;  // candidates per tile (4 waves x 32)
 constexpr int BN = 64;     // keys per LDS tile
 constexpr int NT = 256;
-constexpr int RS = 136;
+constexpr int RS = 136; // K tile row stride (16-byte reads: 8 mod 16 elements)
+constexpr int VS = 160; // V tile row stride (transposing reads)
 constexpr float NLOG2E = -1.4426950408889634f;
 constexpr float NLN2 = -0.69314718055994531f;
 
@@ -38,9 +39,9 @@ DEV u32x2 lds_read_tr(const bf16 *p)
     return __builtin_bit_cast(u32x2, r);
 }
 
-struct Stage {
-    bf16 k[BN * RS];
-    bf16 v[BN * RS];
+struct alignas(16) Stage {
+    alignas(16) bf16 k[BN * RS];
+    alignas(16) bf16 v[BN * VS];
     float beta[BN]; // -log2(e) * beta_j
 };
 
@@ -184,7 +185,7 @@ __global__ void __launch_bounds__(NT) mfalcon_attn_kernel(MfalconArgs a)
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             *(u32x4 *)&S.k[(lc * 4 + i) * RS + le * 8] = kreg[i];
-            *(u32x4 *)&S.v[(lc * 4 + i) * RS + le * 8] = vreg[i];
+            *(u32x4 *)&S.v[(lc * 4 + i) * VS + le * 8] = vreg[i];
         }
         if (tid < BN) S.beta[tid] = breg;
     };
@@ -229,8 +230,8 @@ __global__ void __launch_bounds__(NT) mfalcon_attn_kernel(MfalconArgs a)
                     const int key1 = kb * 32 + 16 * m + 4 * g + tsl;
 #pragma unroll
                     for (int db = 0; db < 4; db++) {
-                        const u32x2 r1 = lds_read_tr(&S.v[key1 * RS + db * 32 + cpart]);
-                        const u32x2 r2 = lds_read_tr(&S.v[(key1 + 8) * RS + db * 32 + cpart]);
+                        const u32x2 r1 = lds_read_tr(&S.v[key1 * VS + db * 32 + cpart]);
+                        const u32x2 r2 = lds_read_tr(&S.v[(key1 + 8) * VS + db * 32 + cpart]);
                         oacc[db] = mfma32(as_bf16x8(u32x4{r1[0], r1[1], r2[0], r2[1]}), pb, oacc[db]);
                     }
                 }

@@ -8,6 +8,25 @@
 // expensive items first so the tail of the launch is short.
 #include "kernels.h"
 
+// Exclusive suffix sum over the 1024 threads of the block: returns
+// sum_{j > tid} v_j.  `tmp` is a 1024-entry LDS array.
+__device__ int block_suffix_excl(int v, int *tmp)
+{
+    const int tid = threadIdx.x;
+    __syncthreads();
+    tmp[tid] = v;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {
+        const int add = tid + o < 1024 ? tmp[tid + o] : 0;
+        __syncthreads();
+        tmp[tid] += add;
+        __syncthreads();
+    }
+    const int incl = tmp[tid];
+    __syncthreads();
+    return incl - v;
+}
+
 // One workgroup of 1024 threads.  An item is (sequence b, tile t, head h);
 // a tile t of sequence b costs t + 1 units (causal), so items are ordered by
 // t descending.  With pi = the sequences sorted by tile count descending,
@@ -18,7 +37,8 @@
 // of every kernel are independent of the order.
 __global__ void __launch_bounds__(1024) sched_kernel(const int32_t *__restrict__ offsets, int B, int T, int tile, int H,
                                                       int *__restrict__ status, int *__restrict__ n_items,
-                                                      int2 *__restrict__ items, int max_items)
+                                                      int2 *__restrict__ items, int max_items,
+                                                      int32_t *__restrict__ wide)
 {
     __shared__ int hist[SCHED_BINS];
     __shared__ int fill[SCHED_BINS];
@@ -33,6 +53,7 @@ __global__ void __launch_bounds__(1024) sched_kernel(const int32_t *__restrict__
     if (tid == 0) bad = (offsets[0] != 0 || offsets[B] != T) ? HSTU_DEV_BAD_OFFSETS : 0;
     __syncthreads();
     for (int b = tid; b < B; b += 1024) {
+        wide[b] = 0;
         int L = offsets[b + 1] - offsets[b];
         if (L < 0) atomicOr(&bad, HSTU_DEV_BAD_OFFSETS);
         int n = L > 0 ? (L + tile - 1) / tile : 0;
@@ -47,29 +68,17 @@ __global__ void __launch_bounds__(1024) sched_kernel(const int32_t *__restrict__
         }
         return;
     }
-    // cnt_gt[t] = #{b : n_b > t} = sum_{v > t} hist[v]  (suffix sum, in place
-    // into fill[]), then S[t] = sum_{t' > t} cnt_gt[t'].  Each thread owns a
-    // contiguous chunk of bins; chunk totals are combined serially by thread 0.
+    // cnt_gt[t] = #{b : n_b > t} = sum_{v > t} hist[v]  (suffix sum, into
+    // fill[]), then S[t] = sum_{t' > t} cnt_gt[t'].  Each thread owns a
+    // contiguous chunk of bins; chunk totals go through a block-wide scan.
     const int per = SCHED_BINS / 1024;
     {
         int s = 0;
         for (int i = per - 1; i >= 0; i--) s += hist[tid * per + i];
-        chunk_tot[tid] = s;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        int run = 0;
-        for (int c = 1023; c >= 0; c--) {
-            int v = chunk_tot[c];
-            chunk_tot[c] = run; // exclusive suffix: sum of the chunks above c
-            run += v;
-        }
-    }
-    __syncthreads();
-    {
-        int run = chunk_tot[tid];
+        const int above = block_suffix_excl(s, chunk_tot); // sum of the chunks above tid
+        int run = above;
         for (int i = per - 1; i >= 0; i--) {
-            int t = tid * per + i;
+            const int t = tid * per + i;
             fill[t] = run; // = #{b : n_b > t}
             run += hist[t];
         }
@@ -78,24 +87,14 @@ __global__ void __launch_bounds__(1024) sched_kernel(const int32_t *__restrict__
     {
         int s = 0;
         for (int i = per - 1; i >= 0; i--) s += fill[tid * per + i];
-        chunk_tot[tid] = s;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        int run = 0;
-        for (int c = 1023; c >= 0; c--) {
-            int v = chunk_tot[c];
-            chunk_tot[c] = run;
-            run += v;
+        const int above = block_suffix_excl(s, chunk_tot);
+        if (tid == 0) {
+            *n_items = (above + s) * H; // sum_t cnt_gt[t] = sum_b n_b
+            *status = 0;
         }
-        *n_items = run * H; // sum_t cnt_gt[t] = sum_b n_b
-        *status = 0;
-    }
-    __syncthreads();
-    {
-        int run = chunk_tot[tid];
+        int run = above;
         for (int i = per - 1; i >= 0; i--) {
-            int t = tid * per + i;
+            const int t = tid * per + i;
             S[t] = run;
             run += fill[t];
         }
@@ -120,47 +119,35 @@ __global__ void __launch_bounds__(1024) sched_kernel(const int32_t *__restrict__
     }
 }
 
-// One workgroup per sequence: rel[r] = ts[r] - min(ts of the sequence) as a
-// 32-bit value when the sequence's time span fits (span <= 2^32 - 2, so
-// |t_i - t_j| + 1 fits in 32 bits); otherwise wide[b] = 1 and the kernels use
-// exact 64-bit arithmetic for that sequence.
+// One thread per token: rel[r] = ts[r] - ts[first token of its sequence] +
+// 2^31 as a 32-bit value.  Differences of two such values are exact as long
+// as every time of the sequence lies within 2^31 - 1 of its first time (then
+// |t_i - t_j| + 1 < 2^32); otherwise wide[b] is set and the kernels use exact
+// 64-bit arithmetic for that sequence.  wide[] was zeroed by sched_kernel.
 __global__ void __launch_bounds__(256) reltime_kernel(const int32_t *__restrict__ offsets, const int64_t *__restrict__ ts,
                                                        uint32_t *__restrict__ rel, int32_t *__restrict__ wide, int B,
-                                                       const int *__restrict__ status)
+                                                       int T, const int *__restrict__ status)
 {
     if (*status) return; // offsets failed validation: touch nothing
-    const int b = blockIdx.x;
-    const int o = offsets[b], e = offsets[b + 1];
-    int64_t mn = INT64_MAX, mx = INT64_MIN;
-    for (int r = o + threadIdx.x; r < e; r += 256) {
-        int64_t t = ts[r];
-        mn = t < mn ? t : mn;
-        mx = t > mx ? t : mx;
+    const int r = blockIdx.x * 256 + threadIdx.x;
+    if (r >= T) return;
+    int lo = 0, hi = B - 1; // last b with offsets[b] <= r
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (offsets[mid] <= r) lo = mid;
+        else hi = mid - 1;
     }
-    __shared__ int64_t smn[256], smx[256];
-    smn[threadIdx.x] = mn;
-    smx[threadIdx.x] = mx;
-    __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-        if (threadIdx.x < s) {
-            smn[threadIdx.x] = smn[threadIdx.x + s] < smn[threadIdx.x] ? smn[threadIdx.x + s] : smn[threadIdx.x];
-            smx[threadIdx.x] = smx[threadIdx.x + s] > smx[threadIdx.x] ? smx[threadIdx.x + s] : smx[threadIdx.x];
-        }
-        __syncthreads();
-    }
-    mn = smn[0];
-    mx = smx[0];
-    // span as unsigned: mx - mn may exceed INT64_MAX only for absurd inputs.
-    const bool w = e > o && (uint64_t)mx - (uint64_t)mn > 0xFFFFFFFEull;
-    if (threadIdx.x == 0) wide[b] = w ? 1 : 0;
-    if (!w)
-        for (int r = o + threadIdx.x; r < e; r += 256) rel[r] = (uint32_t)((uint64_t)ts[r] - (uint64_t)mn);
+    while (lo < B - 1 && offsets[lo + 1] <= r) lo++; // skip empty sequences
+    const int64_t d = ts[r] - ts[offsets[lo]];
+    if (d < -(int64_t)0x7FFFFFFF || d > (int64_t)0x7FFFFFFF) atomicOr(&wide[lo], 1);
+    rel[r] = (uint32_t)(d + ((int64_t)1 << 31));
 }
 
 void launch_sched(const int32_t *offsets, const int64_t *ts, int B, int T, int tile, int H, int *status, int *n_items,
                   int2 *items, int max_items, uint32_t *rel, int32_t *wide, hipStream_t st)
 {
     hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(1024), 0, st, offsets, B, T, tile, H, status, n_items, items,
-                       max_items);
-    if (ts) hipLaunchKernelGGL(reltime_kernel, dim3(B), dim3(256), 0, st, offsets, ts, rel, wide, B, status);
+                       max_items, wide);
+    if (ts && T > 0)
+        hipLaunchKernelGGL(reltime_kernel, dim3((T + 255) / 256), dim3(256), 0, st, offsets, ts, rel, wide, B, T, status);
 }
