@@ -13,12 +13,19 @@ Throughput is algorithmic causal TFLOP/s: forward 4*d flops per causal
 recorded on the launch stream around each kernel (libhstu's profiling
 hooks), over the same timed steps.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Besides the headline step, the same run times (unless --no-extras) one
+HSTU layer forward (f1 + SiLU, attention, LayerNorm gate, f2 + residual) on
+B = 16 Stochastic-Length sequences at N_max = 4096, D = 512, and M-FALCON
+scoring of m = 1024 candidates against a 4096-action history (2 layers,
+b_m = 256).  These are reported under "extras"; they are not part of "value".
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
 Prints one JSON line.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -32,20 +39,78 @@ if ROOT not in sys.path:
 
 MFMA_BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
 HBM_PEAK_GBS = 8000.0
+CSRC = os.path.join(ROOT, "hstu_sequential_transducer_amd", "csrc")
+
+# HBM bytes per launch of a kernel on the headline workload, from rocprofv3
+# FETCH_SIZE / WRITE_SIZE counter runs scaled by the factor the same counters
+# read for a plain device copy of known size.  Valid only for the kernel
+# source they were measured on (sha256 over the files listed); otherwise the
+# traffic is reported as null.
+MEASURED_TRAFFIC = {
+    "attn_bwd_bf16_kernel": {"src": "8f0c9f0e5ebb1807", "bytes": 2581547073},   # read 1075754145 + write 1505792928
+}
+
+
+def src_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "attn_bwd_bf16_kernel": ("attn_bwd.hip", "common.h", "kernels.h"),
+    "attn_fwd_bf16_kernel": ("attn_fwd.hip", "common.h", "kernels.h"),
+}
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=80)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=2048,
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--extras-only", action="store_true",
+                    help="time only the layer and M-FALCON extras (for a profiler run); prints their JSON")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=3072,
                     help="prefix length per sequence for the oracle's timed sample")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (a known-size kernel that "
                          "calibrates HBM byte counters in a profiler run)")
     return ap.parse_args()
+
+
+def timed(fn, warmup, steps):
+    """Run fn warmup times, then time `steps` calls: total ms per call from
+    one event pair around all of them, per-call ms from events between calls,
+    and per-kernel durations from libhstu's launch-stream events."""
+    import torch
+    import hstu_sequential_transducer_amd as hs
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    hs.profile_collect()
+    hs.profile_enable(True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(steps):
+        r = fn()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    hs.profile_enable(False)
+    kt = hs.profile_collect()
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+    total = ev[0].elapsed_time(ev[steps]) / steps
+    kernels = {n: {"launches": c, "avg_ms": t / max(c, 1), "total_ms": t} for n, (c, t) in kt.items()}
+    return r, total, per, kernels
+
+
+def pct(per):
+    return {"median": round(float(np.median(per)), 4), "p10": round(float(np.percentile(per, 10)), 4),
+            "p90": round(float(np.percentile(per, 90)), 4)}
 
 
 def causal_pairs_sum(lengths):
@@ -74,6 +139,96 @@ def cpu_baseline(w, prefix):
             "seconds": dt}
 
 
+def _dev_layer(lay, dev):
+    import torch
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev).to(torch.bfloat16)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+    return dict(w1=bf(lay.w1), b1=f32(lay.b1), w2=bf(lay.w2), b2=f32(lay.b2), rab_p=f32(lay.rab_p),
+                rab_t=f32(lay.rab_t), phi1=0)
+
+
+def bench_layer(args):
+    """One HSTU layer forward on B=16 SL(4096, 1.6) sequences, D=512, H=4,
+    d=128, bf16."""
+    import torch
+    import synth
+    import hstu_sequential_transducer_amd as hs
+    dev = torch.device("cuda:0")
+    w = synth.layer_train_4k()
+    T, D, H, d = w.total, w.d_model, w.heads, w.d
+    lay = _dev_layer(w.layers[0], dev)
+    x = torch.from_numpy(w.x).to(dev).to(torch.bfloat16)
+    off = torch.from_numpy(w.offsets.astype(np.int32)).to(dev)
+    ts = torch.from_numpy(w.ts.astype(np.int64)).to(dev)
+    y = torch.empty_like(x)
+    nws = hs.binding.workspace_size(hs.binding.OP_LAYER_FWD, hs.binding._jagged(off, ts, w.n_max, T),
+                                    hs.binding.Dims(1, H, d, d, w.ln_eps), D, 0)
+    wsb = torch.empty(nws, dtype=torch.uint8, device=dev)
+
+    def step():
+        return hs.layer_fwd(off, T, ts, x, lay, H, d, w.n_max, eps=w.ln_eps, out=y, workspace=wsb)
+
+    steps = max(10, args.steps // 4)
+    _, ms, per, kern = timed(step, args.warmup, steps)
+    f_attn = 2.0 * H * d * causal_pairs_sum(w.lengths)
+    f_gemm = 2.0 * T * D * 4 * H * d + 2.0 * T * H * d * D
+    f1 = 2.0 * T * D * 4 * H * d
+    g1, g2 = kern.get("gemm_f1"), kern.get("gemm_f2")
+    a = kern.get("attn_fwd_bf16_kernel")
+    return {"workload": "layer-fwd B16 SL(4096,1.6) D512 H4 d128 bf16", "tokens": T, "ms": round(ms, 4),
+            "step_ms": pct(per), "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "f1_tflops": round(f1 / (g1["avg_ms"] * 1e-3) / 1e12, 2) if g1 else None,
+            "f2_tflops": round((f_gemm - f1) / (g2["avg_ms"] * 1e-3) / 1e12, 2) if g2 else None,
+            "attn_fwd_tflops": round(f_attn / (a["avg_ms"] * 1e-3) / 1e12, 2) if a else None,
+            "total_tflops": round((f_gemm + f_attn) / (ms * 1e-3) / 1e12, 2),
+            "kernels": {n: {"launches": v["launches"] // steps, "avg_ms": round(v["avg_ms"], 5)} for n, v in kern.items()}}
+
+
+def bench_mfalcon(args):
+    """M-FALCON: one user, 4096-action history cached for 2 layers, m = 1024
+    candidates in microbatches of b_m = 256."""
+    import torch
+    import synth
+    import hstu_sequential_transducer_amd as hs
+    dev = torch.device("cuda:0")
+    w = synth.mfalcon_1user()
+    T, D, H, d = w.total, w.d_model, w.heads, w.d
+    off = torch.from_numpy(w.offsets.astype(np.int32)).to(dev)
+    ts = torch.from_numpy(w.ts.astype(np.int64)).to(dev)
+    layers = [_dev_layer(l, dev) for l in w.layers]
+    h = torch.from_numpy(w.x).to(dev).to(torch.bfloat16)
+    kcs, vcs = [], []
+    for lay in layers:
+        kc = torch.empty((T, H * d), dtype=torch.bfloat16, device=dev)
+        vc = torch.empty_like(kc)
+        h = hs.layer_fwd(off, T, ts, h, lay, H, d, w.n_max, eps=w.ln_eps, k_cache=kc, v_cache=vc)
+        kcs.append(kc)
+        vcs.append(vc)
+    xc = torch.from_numpy(w.x_cand).to(dev).to(torch.bfloat16)
+    M = xc.shape[0]
+    co = torch.from_numpy(w.cand_offsets.astype(np.int32)).to(dev)
+    cts = torch.from_numpy(w.cand_ts.astype(np.int64)).to(dev)
+    nws = hs.binding.workspace_size(hs.binding.OP_MFALCON, hs.binding._jagged(off, ts, w.n_max, T),
+                                    hs.binding.Dims(1, H, d, d, w.ln_eps), D, M)
+    wsb = torch.empty(nws, dtype=torch.uint8, device=dev)
+
+    def step():
+        return hs.mfalcon_score(off, T, ts, layers, kcs, vcs, co, M, cts, xc, w.b_m, H, d, w.n_max,
+                                eps=w.ln_eps, workspace=wsb)
+
+    steps = max(10, args.steps // 4)
+    _, ms, per, kern = timed(step, args.warmup, steps)
+    nl = len(layers)
+    f_attn = nl * 4.0 * M * T * d * H
+    f_gemm = nl * (2.0 * M * D * 4 * H * d + 2.0 * M * H * d * D)
+    a = kern.get("mfalcon_attn_kernel")
+    return {"workload": "mfalcon 1 user, history 4096, m=1024, b_m=256, 2 layers, D512 H4 d128 bf16",
+            "ms": round(ms, 4), "step_ms": pct(per), "candidates_per_s": round(M / (ms * 1e-3), 1),
+            "attn_tflops": round(f_attn / (a["total_ms"] / steps * 1e-3) / 1e12, 2) if a else None,
+            "total_tflops": round((f_attn + f_gemm) / (ms * 1e-3) / 1e12, 2),
+            "kernels": {n: {"launches": v["launches"] // steps, "avg_ms": round(v["avg_ms"], 5)} for n, v in kern.items()}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -83,6 +238,9 @@ def main():
     import synth
     import hstu_sequential_transducer_amd as hs
 
+    if args.extras_only:
+        print(json.dumps({"extras": {"layer_fwd": bench_layer(args), "mfalcon": bench_mfalcon(args)}}), flush=True)
+        return
     dev = torch.device("cuda:0")
     w = synth.attn_8k(with_grad=True)
     T, H, d, F = w.total, w.heads, w.d, w.heads * w.d
@@ -104,22 +262,7 @@ def main():
         hs.attn_fwd(off, T, ts, q, k, v, rp, rt, w.n_max, u=u, eps=w.ln_eps, out=out, o_save=osv, ln_stats=lst)
         return hs.attn_bwd(off, T, ts, q, k, v, rp, rt, w.n_max, dg, u=u, o_save=osv, ln_stats=lst, eps=w.ln_eps)
 
-    for _ in range(args.warmup):
-        g = step()
-    torch.cuda.synchronize()
-    hs.profile_collect()           # drop anything recorded so far
-    hs.profile_enable(True)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(args.steps):
-        g = step()
-    e1.record()
-    torch.cuda.synchronize()
-    hs.profile_enable(False)
-    kt = hs.profile_collect()
-    ms = e0.elapsed_time(e1) / args.steps
+    g, ms, per, per_kernel = timed(step, args.warmup, args.steps)
     if not all(bool(torch.isfinite(g[n]).all()) for n in ("dq", "dk", "dv", "du", "drab_p", "drab_t")):
         print("bench.py: non-finite gradients", file=sys.stderr)
         sys.exit(1)
@@ -128,17 +271,21 @@ def main():
     f_fwd = 2.0 * H * d * S2
     f_bwd = 2.0 * f_fwd
     tflops = (f_fwd + f_bwd) / (ms * 1e-3) / 1e12
-    per_kernel = {n: {"launches": c, "avg_ms": t / max(c, 1)} for n, (c, t) in kt.items()}
     # dominant kernel: the largest share of the timed region
-    dom = max(kt.items(), key=lambda kv: kv[1][1])[0]
+    dom = max(per_kernel.items(), key=lambda kv: kv[1]["total_ms"])[0]
     dom_flops = {"attn_bwd_bf16_kernel": f_bwd, "attn_fwd_bf16_kernel": f_fwd}.get(dom)
     avg = per_kernel[dom]["avg_ms"]
     roof = None
     if dom_flops is not None:
         ach = dom_flops / (avg * 1e-3) / 1e12
+        traffic = None
+        mt = MEASURED_TRAFFIC.get(dom)
+        if mt and mt["src"] == src_digest(KERNEL_SOURCES[dom]):
+            traffic = mt["bytes"]
         roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                "avg_ms": round(avg, 4), "algorithmic_flops_per_launch": dom_flops}
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                "traffic_unit": "bytes per launch (HBM read + write)", "avg_ms": round(avg, 4),
+                "algorithmic_flops_per_launch": dom_flops, "kernel_src": src_digest(KERNEL_SOURCES[dom])}
     fwd_ms = per_kernel.get("attn_fwd_bf16_kernel", {}).get("avg_ms")
     bwd_ms = per_kernel.get("attn_bwd_bf16_kernel", {}).get("avg_ms")
     res = {
@@ -159,8 +306,9 @@ def main():
                    "n_max": w.n_max, "heads": H, "d": d, "tokens": T, "lengths": [int(x) for x in w.lengths],
                    "fwd_gflop": round(f_fwd / 1e9, 2), "bwd_gflop": round(f_bwd / 1e9, 2), "seed": 2},
         "tokens_per_s": round(T / (ms * 1e-3), 1),
+        "step_ms": pct(per),
         "roofline": roof,
-        "kernels": per_kernel,
+        "kernels": {n: {"launches": v2["launches"], "avg_ms": round(v2["avg_ms"], 5)} for n, v2 in per_kernel.items()},
         "attn_fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2) if fwd_ms else None,
         "attn_bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2) if bwd_ms else None,
     }
@@ -172,6 +320,8 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         res["copy_probe_bytes_each_way"] = n * 4
+    if not args.no_extras:
+        res["extras"] = {"layer_fwd": bench_layer(args), "mfalcon": bench_mfalcon(args)}
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, args.cpu_sample_tokens)
         res["cpu_baseline"] = {k2: (round(v2, 6) if isinstance(v2, float) else v2) for k2, v2 in cb.items()}

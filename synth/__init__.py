@@ -2,11 +2,11 @@
 
 This module is shared by the CPU oracle (``oracle/``), the tests and the
 benchmark.  It holds no arithmetic of the method itself: it only draws random
-numbers, rounds them to the storage dtype and lays them out.  Every workload
-follows the shapes and distributions of the five HSTU workloads described in
-the design doc (input recipe), which in turn follow the pages on HSTU / Generative
-Recommenders ("Actions Speak Louder than Words", p1 section 3, core formulas
-and Stochastic Length).
+numbers, rounds them to the storage dtype and lays them out.  The workloads
+take their shapes and distributions from the pages on HSTU / Generative
+Recommenders (review of "Actions Speak Louder than Words", section 3: core
+formulas and Stochastic Length): jagged sequences up to N_max = 8192, H = 4
+heads of d = 128, integer timestamps, small N(0, 0.02) tables and weights.
 
 Draw order inside one workload is fixed (a change of it changes every input):
 lengths -> timestamp gaps (per sequence) -> weights and tables in layer order
