@@ -14,21 +14,26 @@
 // A workgroup of 4 waves owns 128 keys of one (sequence, head); wave w owns
 // keys 32w..32w+31 with their K and V rows in registers and their dK^T, dV^T
 // accumulators in registers.  Query blocks of 32 stream through LDS (double
-// buffered).  Per block a wave computes S and dP with 32x32x16 bf16 MFMA
-// (lane = key, registers = queries), the element-wise step, dV^T += dO'^T P
-// and dK^T += Q^T dS (transposing LDS reads for dO'^T and Q^T), and writes dS
-// to LDS; then wave w computes dQ for d-block w over all 128 keys and adds it
-// to an fp32 accumulator with global atomics.
+// buffered).  Per block a wave computes X = Q K^T + rab_p (the rab_p window
+// is loaded into the accumulator) and dP with 32x32x16 bf16 MFMA (lane = key,
+// registers = queries), the element-wise step, dV^T += dO'^T P and
+// dK^T += Q^T dS (transposing LDS reads for dO'^T and Q^T), and writes dS to
+// an LDS tile.  dQ for d-block w over all 128 keys needs every wave's dS, so
+// it runs one block late: in the next iteration, next to that block's
+// QK^T / dP MFMAs, with K for d-block w held in registers as the MFMA
+// operand; the partial dQ goes to an fp32 accumulator with global atomics.
+// One barrier per query block.
 //
-// drab_p: each wave also writes its fp32 dS into an LDS tile skewed by
-// j - i ([query][key - query]); one thread per diagonal sums it into an LDS
-// ring indexed by j - i, and an entry is flushed with one global atomic once
-// no later block can reach it.  drab_t: when every pair of a 32x32 block falls
-// in one time bucket (decided per block from the min/max times of its queries
-// and keys) the bias is a scalar and the block's dS is summed by a wave
-// reduction; otherwise per-element adds go to per-wave LDS tables.  Bias
-// presence, time mode, diagonal masking and uniform blocks are compile-time
-// instantiations, so the element-wise code has no branches.
+// drab_p: each wave writes its fp32 dS into an LDS tile skewed by j - i
+// ([query][key - query]); one block later, one thread per diagonal sums it
+// into an LDS ring indexed by j - i, and an entry is flushed with one global
+// atomic once no later block can reach it.  drab_t: when every pair of a
+// 32x32 block falls in one time bucket (decided per block in scalar code from
+// the min/max times of its queries and keys) the bias is a scalar and the
+// block's dS is summed by a wave reduction; otherwise per-element adds go to
+// per-wave LDS tables.  Bias presence, time mode, diagonal masking and uniform
+// blocks are compile-time instantiations, so the element-wise code has no
+// branches.
 #include "kernels.h"
 
 namespace {
@@ -39,10 +44,10 @@ constexpr int BQ = 32;     // queries per block
 constexpr int NT = 256;
 // LDS row strides (bf16 elements), from measured gfx950 LDS throughput: Q and
 // dO are read both as 16-byte operands (fast at 8 mod 16 elements) and
-// transposed (fast at 160, fair at 168); K is only read transposed.
+// transposed (fast at 160, fair at 168).
 constexpr int RS = 168;    // Q, dO tiles
-constexpr int KS = 160;    // K tile
-constexpr int SS = 40;     // LDS row stride (bf16) of the dS tile [key][query]
+constexpr int KS = 160;    // K tile (prologue only)
+constexpr int SS = 40;     // dS tile [key][query]
 constexpr int WIN = 160;   // rab_p window per block (BQ + BN - 1 used)
 constexpr int RING = 256;  // drab_p ring (power of two >= WIN + BQ)
 constexpr int DK = 160;    // columns of the skewed dS tile: key - query + BQ - 1
@@ -57,25 +62,31 @@ struct alignas(16) Stage {
     alignas(16) bf16 q[BQ * RS];
     alignas(16) bf16 dO[BQ * RS];
     alignas(16) bf16 dOl[BQ * RS]; // low part of dO' (dO' = dO + dOl to ~16 bits)
-    float win[WIN];
+    float win[WIN];                // rab_p[clip(key - query)], slot = key - query + BQ - 1 - (k0 - q0)
     uint32_t qt[BQ];
     int64_t qt64[BQ];
-    uint32_t qtmin, qtmax; // over the block's valid queries
+    uint32_t qtmin, qtmax;         // over the block's valid queries
 };
 struct alignas(16) Smem {
-    alignas(16) bf16 k[BN * KS];
     Stage st[2];
-    alignas(16) bf16 ds[BN * SS];
-    alignas(16) float dsk[BQ * DK]; // fp32 dS skewed: [query][key - query + BQ - 1]
+    alignas(16) bf16 ds[2][BN * SS];
+    union {
+        alignas(16) float dsk[2][BQ * DK]; // fp32 dS skewed: [query][key - query + BQ - 1]
+        alignas(16) bf16 k[BN * KS];       // K tile, prologue only
+    };
     float ring[RING];
     float dtab[4][TCOPY][TB];
     float rabt_rev[32];
     float rabt[128];
 };
+static_assert(sizeof(float) * 2 * BQ * DK >= sizeof(bf16) * BN * KS, "K tile must fit the skewed tiles");
 
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4v lds_short4v;
 
+// Transposing LDS read (ds_read_b64_tr_b16).  Inside each group of 16 lanes,
+// lane i receives element i%4 of the 4-element chunks addressed by lanes
+// i/4, i/4+4, i/4+8, i/4+12 (in that order).
 DEV u32x2 lds_read_tr(const bf16 *p)
 {
     short4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(p));
@@ -83,7 +94,6 @@ DEV u32x2 lds_read_tr(const bf16 *p)
 }
 
 struct BwdLane {
-    const float *win;     // S.win + (32w + lq + BQ - 1) - 4g  (index with -cr)
     const uint32_t *qt;   // S.qt + 4g   (index with cr)
     const int64_t *qt64;  // S.qt64 + 4g
     float *dsk;           // skewed-tile cell of (cr = 0) for this lane
@@ -94,10 +104,11 @@ struct BwdLane {
 };
 
 // Element-wise step of one 32x32 block.  Register r <-> query ql = 4g + cr(r),
-// cr = 8(r/4) + r%4; this lane's key.  Writes packed bf16 P and dS, the fp32
-// dS into the skewed tile, and the drab_t contributions.
-template <bool HP, int TM, bool DT, bool DIAG, bool UNI>
-DEV void bwd_pointwise(const floatx16 &sacc, const floatx16 &pacc, uint32_t (&ppk)[8], uint32_t (&dpk)[8],
+// cr = 8(r/4) + r%4; this lane's key.  xacc holds x - rab_t (the rab_p term is
+// already in).  Writes packed bf16 P and dS, the fp32 dS into the skewed tile,
+// and the drab_t contributions.
+template <int TM, bool DT, bool DIAG, bool UNI>
+DEV void bwd_pointwise(const floatx16 &xacc, const floatx16 &pacc, uint32_t (&ppk)[8], uint32_t (&dpk)[8],
                        const BwdLane &ln, const float *rabt_rev, const float *rabt, float ubias, float &tsum)
 {
 #pragma unroll
@@ -107,27 +118,26 @@ DEV void bwd_pointwise(const floatx16 &sacc, const floatx16 &pacc, uint32_t (&pp
         for (int u = 0; u < 2; u++) {
             const int rr = r + u;
             const int cr = 8 * (rr >> 2) + (rr & 3);
-            // x' = -log2(e) * x (tables staged pre-scaled), sg = sigmoid(x),
+            // x' = -log2(e) x (time tables staged pre-scaled), sg = sigmoid(x),
             // p' = x' sg = -log2(e) SiLU(x) (the -ln 2 goes into dV's final scale),
             // dS = dP sg (1 + x (1 - sg)) = dP (sg - ln2 (p' - p' sg)).
-            float b = 0.f;
-            if constexpr (HP) b = ln.win[-cr];
+            float tb = 0.f;
             int bucket = 0;
             if constexpr (TM == 1) {
                 if constexpr (UNI) {
-                    b += ubias;
+                    tb = ubias;
                 } else {
                     const uint32_t tq = ln.qt[cr];
                     const uint32_t dd1 = (tq > ln.tk ? tq - ln.tk : ln.tk - tq) + 1u;
                     const int cz = __builtin_clz(dd1);
-                    b += rabt_rev[cz];
+                    tb = rabt_rev[cz];
                     bucket = 31 - cz;
                 }
             } else if constexpr (TM == 2) {
                 bucket = time_bucket64(ln.qt64[cr] - ln.tk64);
-                b += rabt[bucket];
+                tb = rabt[bucket];
             }
-            const float x = __builtin_fmaf(sacc[rr], NLOG2E, b);
+            const float x = __builtin_fmaf(xacc[rr], NLOG2E, tb);
             const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x));
             float p = x * sg;
             const float t = __builtin_fmaf(-p, sg, p);
@@ -158,11 +168,11 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
     const bf16 *Q = a.q, *K = a.k, *V = a.v, *dO = a.dO;
     const int64_t ld_do = (int64_t)a.H * D;
     const bf16 *dOlo = dO + (int64_t)a.T * ld_do;
+    // transposing-read lane constants
+    const int tj = l & 15, tsl = tj >> 2;
+    const int cpart = ((l >> 4) & 1) * 16 + 4 * (tj & 3);
 
-    // ---- prologue: tables, K tile in LDS, own K/V rows in registers
-    for (int i = tid; i < RING; i += NT) sm.ring[i] = 0.f;
-    for (int i = tid; i < BQ * DK; i += NT) sm.dsk[i] = 0.f;
-    for (int i = tid; i < 4 * TCOPY * TB; i += NT) (&sm.dtab[0][0][0])[i] = 0.f;
+    // ---- prologue: K tile in LDS (aliasing the skewed tiles), own K/V rows in registers
     {
         const int lc = tid >> 4, le = tid & 15; // 16 keys x 16 d-groups per pass
 #pragma unroll
@@ -185,17 +195,35 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
             vreg[s] = as_bf16x8(kvalid ? *(const u32x4 *)(vp + s * 16) : u32x4{0, 0, 0, 0});
         }
     }
+    __syncthreads();
+    // K as the B operand of dQ = dS K for d-block w: keys 16t + 8g + e of the
+    // workgroup, d = 32w + lq.
+    bf16x8 kq[8];
+#pragma unroll
+    for (int t = 0; t < BN / 16; t++) {
+        const int kr1 = 16 * t + 8 * g + tsl;
+        const u32x2 k1 = lds_read_tr(&sm.k[kr1 * KS + 32 * w + cpart]);
+        const u32x2 k2 = lds_read_tr(&sm.k[(kr1 + 4) * KS + 32 * w + cpart]);
+        kq[t] = as_bf16x8(u32x4{k1[0], k1[1], k2[0], k2[1]});
+    }
+    __syncthreads(); // K tile consumed: its space becomes the skewed tiles
+    for (int i = tid; i < RING; i += NT) sm.ring[i] = 0.f;
+    for (int i = tid; i < 2 * BQ * DK; i += NT) (&sm.dsk[0][0])[i] = 0.f;
+    for (int i = tid; i < 4 * TCOPY * TB; i += NT) (&sm.dtab[0][0][0])[i] = 0.f;
+
     BwdLane ln;
     ln.tk = (TM == 1 && kvalid) ? a.rel[o_b + mykey] : 0u;
     ln.tk64 = (TM == 2 && kvalid) ? a.ts[o_b + mykey] : 0;
     ln.dtab = &sm.dtab[w][lq & (TCOPY - 1)][0];
-    // time range of this wave's valid keys (for the uniform-bucket test)
+    // time range of this wave's valid keys (for the uniform-bucket test), as scalars
     uint32_t tkmin = kvalid ? ln.tk : 0xFFFFFFFFu, tkmax = kvalid ? ln.tk : 0u;
     if constexpr (TM == 1) {
         for (int o = 32; o >= 1; o >>= 1) {
             tkmin = min(tkmin, (uint32_t)__shfl_xor((int)tkmin, o, 64));
             tkmax = max(tkmax, (uint32_t)__shfl_xor((int)tkmax, o, 64));
         }
+        tkmin = __builtin_amdgcn_readfirstlane(tkmin);
+        tkmax = __builtin_amdgcn_readfirstlane(tkmax);
     }
 
     floatx16 dv_acc[4], dk_acc[4];
@@ -215,19 +243,31 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
     int64_t treg64 = 0;
     auto gload = [&](int q0) {
         const int qi = q0 + lcq;
-        const bool ok = qi < L;
-        const int64_t row = (int64_t)(o_b + (ok ? qi : 0));
+        if (q0 + BQ <= L) { // full block: no row checks
+            const int64_t row = (int64_t)(o_b + qi);
 #pragma unroll
-        for (int c = 0; c < 2; c++) {
-            qreg2[c] = ok ? *(const u32x4 *)(Q + row * a.ldq + h * D + leq * 16 + c * 8) : u32x4{0, 0, 0, 0};
-            dreg2[c] = ok ? *(const u32x4 *)(dO + row * ld_do + h * D + leq * 16 + c * 8) : u32x4{0, 0, 0, 0};
-            lreg2[c] = ok ? *(const u32x4 *)(dOlo + row * ld_do + h * D + leq * 16 + c * 8) : u32x4{0, 0, 0, 0};
+            for (int c = 0; c < 2; c++) {
+                qreg2[c] = *(const u32x4 *)(Q + row * a.ldq + h * D + leq * 16 + c * 8);
+                dreg2[c] = *(const u32x4 *)(dO + row * ld_do + h * D + leq * 16 + c * 8);
+                lreg2[c] = *(const u32x4 *)(dOlo + row * ld_do + h * D + leq * 16 + c * 8);
+            }
+        } else {
+            // rows past the sequence: Q from the last row (finite), dO = 0 so
+            // they contribute nothing
+            const bool ok = qi < L;
+            const int64_t row = (int64_t)(o_b + (ok ? qi : L - 1));
+#pragma unroll
+            for (int c = 0; c < 2; c++) {
+                qreg2[c] = *(const u32x4 *)(Q + row * a.ldq + h * D + leq * 16 + c * 8);
+                dreg2[c] = ok ? *(const u32x4 *)(dO + row * ld_do + h * D + leq * 16 + c * 8) : u32x4{0, 0, 0, 0};
+                lreg2[c] = ok ? *(const u32x4 *)(dOlo + row * ld_do + h * D + leq * 16 + c * 8) : u32x4{0, 0, 0, 0};
+            }
         }
         if constexpr (HP) {
             if (tid < WIN) {
                 int dl = k0 - q0 - (BQ - 1) + tid; // key - query of window slot tid
                 dl = dl < -a.N ? -a.N : (dl > a.N ? a.N : dl);
-                wreg = NLOG2E * a.rab_p[h * a.rp_hs + dl + a.N];
+                wreg = a.rab_p[h * a.rp_hs + dl + a.N];
             }
         }
         if constexpr (TM != 0) {
@@ -269,31 +309,82 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
         }
     };
 
-    const int nqb = (L - k0 + BQ - 1) / BQ; // query blocks [k0, L)
-    if (nqb > 0) {
-        gload(k0);
-        sstore(0);
-    }
-    __syncthreads();
-
-    const int tj = l & 15, tsl = tj >> 2;
-    const int cpart = ((l >> 4) & 1) * 16 + 4 * (tj & 3);
     const int p_hs = a.rp_hs > 0 ? (int)a.rp_hs : 2 * a.N + 1;
     const int t_hs = a.rt_hs > 0 ? (int)a.rt_hs : 128;
-    ln.dsk = &sm.dsk[4 * g * (DK - 1) + 32 * w + lq + (BQ - 1)];
 
+    // dQ of the block at q0m from the dS tile `dst` (all 4 waves' keys):
+    // dQ[32 queries][d-block w] = sum over 128 keys of dS[q][key] K[key][d]
+    auto dq_block = [&](const bf16 *dst, int q0m) {
+        floatx16 qacc;
+#pragma unroll
+        for (int r = 0; r < 16; r++) qacc[r] = 0.f;
+#pragma unroll
+        for (int t = 0; t < BN / 16; t++) {
+            const int kr1 = 16 * t + 8 * g + tsl;
+            const u32x2 s1 = lds_read_tr(&dst[kr1 * SS + cpart]);
+            const u32x2 s2 = lds_read_tr(&dst[(kr1 + 4) * SS + cpart]);
+            qacc = mfma32(as_bf16x8(u32x4{s1[0], s1[1], s2[0], s2[1]}), kq[t], qacc);
+        }
+        // C layout: lane holds d = 32w + lq, queries 8(r/4) + 4g + r%4
+        float *dqp = a.dq_acc + (int64_t)(o_b + q0m + 4 * g) * ld_do + h * D + 32 * w + lq;
+        if (q0m + BQ <= L) {
+#pragma unroll
+            for (int r = 0; r < 16; r++) atomicAdd(dqp + (int64_t)(8 * (r >> 2) + (r & 3)) * ld_do, qacc[r]);
+        } else {
+            const int qlim = L - q0m - 4 * g;
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int qq = 8 * (r >> 2) + (r & 3);
+                if (qq < qlim) atomicAdd(dqp + (int64_t)qq * ld_do, qacc[r]);
+            }
+        }
+    };
+    // drab_p of the block at q0m from its skewed tile: thread c sums diagonal
+    // c (key - query = k0 - q0m + c - (BQ - 1)); cells outside the tile's keys
+    // are never written and stay 0.  The ring entry is flushed once no later
+    // block can reach it (key - query > k0 + BN - 1 - (q0m + BQ)  <=>  c > BN - 2).
+    auto drabp_block = [&](const float *dsk, int q0m) {
+        if (a.drab_p && tid < DK - 1) {
+            const int c = tid;
+            float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int rq = 0; rq < BQ; rq++) part[rq & 3] += dsk[rq * DK + c];
+            const float sum = (part[0] + part[1]) + (part[2] + part[3]);
+            const int dl = k0 - q0m + c - (BQ - 1);
+            const int slot = dl & (RING - 1);
+            const float tot = sm.ring[slot] + sum;
+            if (c > BN - 2) {
+                if (tot != 0.f) {
+                    const int cl = dl < -a.N ? -a.N : (dl > a.N ? a.N : dl);
+                    atomicAdd(&a.drab_p[h * p_hs + cl + a.N], tot);
+                }
+                sm.ring[slot] = 0.f;
+            } else {
+                sm.ring[slot] = tot;
+            }
+        }
+    };
+
+    const int nqb = (L - k0 + BQ - 1) / BQ; // query blocks [k0, L); >= 1
+    gload(k0);
+    sstore(0);
+    __syncthreads();
+
+    const int kw0 = k0 + 32 * w; // this wave's first key
     for (int n = 0; n < nqb; n++) {
         const int q0 = k0 + n * BQ;
         if (n + 1 < nqb) gload(q0 + BQ);
         const Stage &S = sm.st[n & 1];
-        const int kw0 = k0 + 32 * w; // this wave's first key
+        float *dskn = sm.dsk[n & 1];
+        bf16 *dsn = sm.ds[n & 1];
         const bool skip = kw0 > q0 + BQ - 1 || kw0 >= L;
-        const bool diag = kw0 + 31 > q0;
+        floatx16 xacc, pacc;
         if (!skip) {
-            floatx16 sacc, pacc;
+            // X = Q K^T + rab_p window, dP = dO' V^T (hi and lo planes)
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                sacc[r] = 0.f;
+                const int cr = 8 * (r >> 2) + (r & 3);
+                xacc[r] = HP ? S.win[32 * w + lq + (BQ - 1) - 4 * g - cr] : 0.f;
                 pacc[r] = 0.f;
             }
 #pragma unroll
@@ -301,40 +392,57 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
                 const bf16x8 qa = *(const bf16x8 *)&S.q[lq * RS + s * 16 + g * 8];
                 const bf16x8 da = *(const bf16x8 *)&S.dO[lq * RS + s * 16 + g * 8];
                 const bf16x8 dl = *(const bf16x8 *)&S.dOl[lq * RS + s * 16 + g * 8];
-                sacc = mfma32(qa, kreg[s], sacc);
+                xacc = mfma32(qa, kreg[s], xacc);
                 pacc = mfma32(da, vreg[s], pacc);
                 pacc = mfma32(dl, vreg[s], pacc);
             }
-            ln.win = &S.win[32 * w + lq + (BQ - 1) - 4 * g];
+        }
+        // the previous block's dQ and drab_p (its dS tiles are complete)
+        if (n > 0) {
+            dq_block(sm.ds[(n - 1) & 1], q0 - BQ);
+            drabp_block(sm.dsk[(n - 1) & 1], q0 - BQ);
+        }
+        ln.dsk = dskn + 4 * g * (DK - 1) + 32 * w + lq + (BQ - 1);
+        const int krow = 32 * w + lq;
+        if (!skip) {
             ln.qt = &S.qt[4 * g];
             ln.qt64 = &S.qt64[4 * g];
             ln.dmask = kw0 + lq - q0 - 4 * g; // key > query  <=>  cr < dmask
+            const bool diag = kw0 + 31 > q0;
             bool uni = false;
             int ubk = 0;
             if constexpr (TM == 1) {
-                const uint32_t qmn = S.qtmin, qmx = S.qtmax;
-                if (qmn <= qmx && tkmin <= tkmax) {
-                    const int64_t a1 = (int64_t)qmn - (int64_t)tkmax, a2 = (int64_t)qmx - (int64_t)tkmin;
-                    const int64_t lo = a1 > 0 ? a1 : (a2 < 0 ? -a2 : 0);
-                    const int64_t m1 = a1 < 0 ? -a1 : a1, m2 = a2 < 0 ? -a2 : a2;
-                    const int64_t hi = m1 > m2 ? m1 : m2;
-                    const int blo = floor_log2_u32((uint32_t)lo + 1u), bhi = floor_log2_u32((uint32_t)hi + 1u);
-                    uni = __builtin_amdgcn_readfirstlane(blo == bhi ? 1 : 0) != 0;
-                    ubk = __builtin_amdgcn_readfirstlane(blo);
+                // all pairs in one bucket iff floor(log2(min|dt| + 1)) == floor(log2(max|dt| + 1));
+                // relative times of one non-wide sequence differ by less than 2^32 - 1
+                const uint32_t qa = __builtin_amdgcn_readfirstlane(S.qtmin);
+                const uint32_t qb = __builtin_amdgcn_readfirstlane(S.qtmax);
+                if (qa <= qb && tkmin <= tkmax) {
+                    const uint32_t lo = tkmin > qb ? tkmin - qb : (qa > tkmax ? qa - tkmax : 0u);
+                    const uint32_t h1 = qb > tkmin ? qb - tkmin : 0u, h2 = tkmax > qa ? tkmax - qa : 0u;
+                    const uint32_t hi = h1 > h2 ? h1 : h2;
+                    const int blo = floor_log2_u32(lo + 1u), bhi = floor_log2_u32(hi + 1u);
+                    uni = blo == bhi;
+                    ubk = blo;
                 }
             }
             const float ubias = sm.rabt[ubk];
             float tsum = 0.f;
             uint32_t ppk[8], dpk[8];
             if (diag)
-                bwd_pointwise<HP, TM, DT, true, false>(sacc, pacc, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, tsum);
+                bwd_pointwise<TM, DT, true, false>(xacc, pacc, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, tsum);
             else if (TM == 1 && uni)
-                bwd_pointwise<HP, TM, DT, false, true>(sacc, pacc, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, tsum);
+                bwd_pointwise<TM, DT, false, true>(xacc, pacc, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, tsum);
             else
-                bwd_pointwise<HP, TM, DT, false, false>(sacc, pacc, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, tsum);
+                bwd_pointwise<TM, DT, false, false>(xacc, pacc, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, tsum);
             if (DT && TM == 1 && uni && !diag) {
                 tsum = wave_sum(tsum);
                 if (l == 0) sm.dtab[w][0][ubk] += tsum;
+            }
+            // dS -> LDS as [key][query]: lane writes 4 queries (r%4) per r/4 group
+#pragma unroll
+            for (int gr = 0; gr < 4; gr++) {
+                const u32x2 v2 = {dpk[2 * gr], dpk[2 * gr + 1]};
+                *(u32x2 *)&dsn[krow * SS + 8 * gr + 4 * g] = v2;
             }
             // dV^T += dO'^T P and dK^T += Q^T dS  (contraction over the 32 queries)
 #pragma unroll
@@ -352,82 +460,30 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
                     dk_acc[db] = mfma32(as_bf16x8(u32x4{q1[0], q1[1], q2[0], q2[1]}), sb, dk_acc[db]);
                 }
             }
-            // dS -> LDS as [key][query]: lane writes 4 queries (r%4) per r/4 group
-            const int krow = 32 * w + lq;
-#pragma unroll
-            for (int gr = 0; gr < 4; gr++) {
-                const u32x2 v2 = {dpk[2 * gr], dpk[2 * gr + 1]};
-                *(u32x2 *)&sm.ds[krow * SS + 8 * gr + 4 * g] = v2;
-            }
         } else {
-            const int krow = 32 * w + lq;
 #pragma unroll
-            for (int gr = 0; gr < 4; gr++) *(u32x2 *)&sm.ds[krow * SS + 8 * gr + 4 * g] = u32x2{0u, 0u};
+            for (int gr = 0; gr < 4; gr++) *(u32x2 *)&dsn[krow * SS + 8 * gr + 4 * g] = u32x2{0u, 0u};
 #pragma unroll
             for (int rr = 0; rr < 16; rr++) ln.dsk[(8 * (rr >> 2) + (rr & 3)) * (DK - 1)] = 0.f;
-        }
-        __syncthreads();
-        // dQ[32 queries][d-block w] = sum over the 128 keys of dS[q][key] K[key][d]
-        {
-            floatx16 qacc;
-#pragma unroll
-            for (int r = 0; r < 16; r++) qacc[r] = 0.f;
-#pragma unroll
-            for (int t = 0; t < BN / 16; t++) {
-                // A: dS[q = lq][keys 16t + 8g + e], from ds[key][q]; B: K[keys][d = 32w + lq]
-                const int kr1 = 16 * t + 8 * g + tsl;
-                const u32x2 s1 = lds_read_tr(&sm.ds[kr1 * SS + cpart]);
-                const u32x2 s2 = lds_read_tr(&sm.ds[(kr1 + 4) * SS + cpart]);
-                const u32x2 k1 = lds_read_tr(&sm.k[kr1 * KS + 32 * w + cpart]);
-                const u32x2 k2 = lds_read_tr(&sm.k[(kr1 + 4) * KS + 32 * w + cpart]);
-                qacc = mfma32(as_bf16x8(u32x4{s1[0], s1[1], s2[0], s2[1]}),
-                              as_bf16x8(u32x4{k1[0], k1[1], k2[0], k2[1]}), qacc);
-            }
-            // C layout: lane holds d = 32w + lq, queries 8(r/4) + 4g + r%4
-            float *dqp = a.dq_acc + (int64_t)(o_b + q0 + 4 * g) * ld_do + h * D + 32 * w + lq;
-            const int qlim = L - q0 - 4 * g;
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int qq = 8 * (r >> 2) + (r & 3);
-                if (qq < qlim) atomicAdd(dqp + (int64_t)qq * ld_do, qacc[r]);
-            }
-        }
-        // drab_p: thread c sums diagonal c of the skewed tile (key - query =
-        // k0 - q0 + c - (BQ - 1)); cells outside the tile's keys are never
-        // written and stay 0.  The ring entry is flushed once no later block
-        // can reach it (key - query > k0 + BN - 1 - (q0 + BQ)  <=>  c > BN - 2).
-        if (a.drab_p && tid < DK - 1) {
-            const int c = tid;
-            float part[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int rq = 0; rq < BQ; rq++) part[rq & 3] += sm.dsk[rq * DK + c];
-            const float sum = (part[0] + part[1]) + (part[2] + part[3]);
-            const int dl = k0 - q0 + c - (BQ - 1);
-            const int slot = dl & (RING - 1);
-            const float tot = sm.ring[slot] + sum;
-            if (c > BN - 2) {
-                if (tot != 0.f) {
-                    const int cl = dl < -a.N ? -a.N : (dl > a.N ? a.N : dl);
-                    atomicAdd(&a.drab_p[h * p_hs + cl + a.N], tot);
-                }
-                sm.ring[slot] = 0.f;
-            } else {
-                sm.ring[slot] = tot;
-            }
         }
         if (n + 1 < nqb) sstore((n + 1) & 1);
         __syncthreads();
     }
-    // flush what is left in the ring and the time tables
-    if (a.drab_p && nqb > 0) {
+    // the last block's dQ and drab_p, then what is left in the ring and the time tables
+    {
         const int qlast = k0 + (nqb - 1) * BQ;
-        // remaining key - query values: [k0 - qlast - (BQ - 1), k0 + BN - 1 - qlast - BQ]
-        const int lo = k0 - qlast - (BQ - 1), hi = k0 + BN - 1 - qlast - BQ;
-        for (int dl = lo + tid; dl <= hi; dl += NT) {
-            const float v = sm.ring[dl & (RING - 1)];
-            if (v != 0.f) {
-                const int cl = dl < -a.N ? -a.N : (dl > a.N ? a.N : dl);
-                atomicAdd(&a.drab_p[h * p_hs + cl + a.N], v);
+        dq_block(sm.ds[(nqb - 1) & 1], qlast);
+        drabp_block(sm.dsk[(nqb - 1) & 1], qlast);
+        __syncthreads();
+        if (a.drab_p) {
+            // remaining key - query values: [k0 - qlast - (BQ - 1), k0 + BN - 1 - qlast - BQ]
+            const int lo = k0 - qlast - (BQ - 1), hi = k0 + BN - 1 - qlast - BQ;
+            for (int dl = lo + tid; dl <= hi; dl += NT) {
+                const float v = sm.ring[dl & (RING - 1)];
+                if (v != 0.f) {
+                    const int cl = dl < -a.N ? -a.N : (dl > a.N ? a.N : dl);
+                    atomicAdd(&a.drab_p[h * p_hs + cl + a.N], v);
+                }
             }
         }
     }
@@ -459,8 +515,11 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
 
 } // namespace
 
-template <bool HP>
-__global__ void __launch_bounds__(NT) attn_bwd_bf16_kernel(AttnBwdArgs a)
+// TMODE: 0 = no time bias; 1 = time bias with drab_t; 2 = time bias without
+// drab_t.  Sequences whose time span does not fit 32 bits take the exact
+// 64-bit body.
+template <bool HP, int TMODE>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) attn_bwd_bf16_kernel(AttnBwdArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     Smem &sm = *reinterpret_cast<Smem *>(smem_raw);
@@ -472,37 +531,49 @@ __global__ void __launch_bounds__(NT) attn_bwd_bf16_kernel(AttnBwdArgs a)
     const int L = a.offsets[b + 1] - o_b;
     const int nkt = (L + BN - 1) / BN;
     const int k0 = (nkt - 1 - tsched) * BN; // most expensive key tile (k0 = 0) first
-    const bool has_t = a.ts != nullptr && a.rab_t != nullptr;
     const int tid = threadIdx.x;
-    if (tid < 128) sm.rabt[tid] = has_t ? NLOG2E * a.rab_t[h * a.rt_hs + tid] : 0.f;
-    if (tid < 32) sm.rabt_rev[tid] = has_t ? NLOG2E * a.rab_t[h * a.rt_hs + 31 - tid] : 0.f;
-    // (the first barrier inside bwd_body orders these writes before use)
-    const bool dt = a.drab_t != nullptr;
-    if (!has_t) bwd_body<HP, 0, false>(a, sm, o_b, L, k0, h);
-    else if (a.wide[b] != 0) {
-        if (dt) bwd_body<HP, 2, true>(a, sm, o_b, L, k0, h);
-        else bwd_body<HP, 2, false>(a, sm, o_b, L, k0, h);
+    if constexpr (TMODE != 0) {
+        if (tid < 128) sm.rabt[tid] = NLOG2E * a.rab_t[h * a.rt_hs + tid];
+        if (tid < 32) sm.rabt_rev[tid] = NLOG2E * a.rab_t[h * a.rt_hs + 31 - tid];
     } else {
-        if (dt) bwd_body<HP, 1, true>(a, sm, o_b, L, k0, h);
-        else bwd_body<HP, 1, false>(a, sm, o_b, L, k0, h);
+        if (tid < 128) sm.rabt[tid] = 0.f;
+        if (tid < 32) sm.rabt_rev[tid] = 0.f;
     }
+    // (the first barrier inside bwd_body orders these writes before use)
+    constexpr bool DT = TMODE == 1;
+    if constexpr (TMODE == 0) bwd_body<HP, 0, false>(a, sm, o_b, L, k0, h);
+    else if (a.wide[b] != 0) bwd_body<HP, 2, DT>(a, sm, o_b, L, k0, h);
+    else bwd_body<HP, 1, DT>(a, sm, o_b, L, k0, h);
 }
 
-hipError_t launch_attn_bwd_bf16(const AttnBwdArgs &a, int max_items, hipStream_t st)
+namespace {
+template <bool HP, int TMODE>
+hipError_t launch_variant(const AttnBwdArgs &a, int max_items, hipStream_t st)
 {
     static bool init = false;
     const size_t smem = sizeof(Smem);
     if (!init) {
-        hipError_t e = hipFuncSetAttribute((const void *)attn_bwd_bf16_kernel<true>,
+        hipError_t e = hipFuncSetAttribute((const void *)attn_bwd_bf16_kernel<HP, TMODE>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        if (e != hipSuccess) return e;
-        e = hipFuncSetAttribute((const void *)attn_bwd_bf16_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)smem);
         if (e != hipSuccess) return e;
         init = true;
     }
-    if (max_items <= 0) return hipSuccess;
-    if (a.rab_p) hipLaunchKernelGGL(attn_bwd_bf16_kernel<true>, dim3(max_items), dim3(NT), smem, st, a);
-    else hipLaunchKernelGGL(attn_bwd_bf16_kernel<false>, dim3(max_items), dim3(NT), smem, st, a);
+    hipLaunchKernelGGL((attn_bwd_bf16_kernel<HP, TMODE>), dim3(max_items), dim3(NT), smem, st, a);
     return hipGetLastError();
+}
+} // namespace
+
+hipError_t launch_attn_bwd_bf16(const AttnBwdArgs &a, int max_items, hipStream_t st)
+{
+    if (max_items <= 0) return hipSuccess;
+    const bool has_t = a.ts != nullptr && a.rab_t != nullptr;
+    const int tmode = !has_t ? 0 : (a.drab_t ? 1 : 2);
+    if (a.rab_p) {
+        if (tmode == 0) return launch_variant<true, 0>(a, max_items, st);
+        if (tmode == 1) return launch_variant<true, 1>(a, max_items, st);
+        return launch_variant<true, 2>(a, max_items, st);
+    }
+    if (tmode == 0) return launch_variant<false, 0>(a, max_items, st);
+    if (tmode == 1) return launch_variant<false, 1>(a, max_items, st);
+    return launch_variant<false, 2>(a, max_items, st);
 }
