@@ -11,17 +11,17 @@
 // softmax statistics, so nothing else is needed).  dO' arrives as two bf16
 // planes (hi + lo) so dP keeps ~16 significant bits.
 //
-// A workgroup of 4 waves owns 128 keys of one (sequence, head); wave w owns
-// keys 32w..32w+31 with their K and V rows in registers and their dK^T, dV^T
+// A workgroup of 4 waves owns 128 keys of one (sequence, head), their K rows
+// in LDS; wave w owns keys 32w..32w+31 with their V rows and their dK^T, dV^T
 // accumulators in registers.  Query blocks of 32 stream through LDS (double
-// buffered).  Per block a wave computes X = Q K^T + rab_p (the rab_p window
+// buffered, copied global -> LDS directly).  Per block a wave computes X = Q K^T + rab_p (the rab_p window
 // is loaded into the accumulator) and dP with 32x32x16 bf16 MFMA (lane = key,
 // registers = queries), the element-wise step, dV^T += dO'^T P and
 // dK^T += Q^T dS (transposing LDS reads for dO'^T and Q^T), and writes dS to
 // an LDS tile.  dQ for d-block w over all 128 keys needs every wave's dS, so
 // it runs one block late: in the next iteration, next to that block's
-// QK^T / dP MFMAs, with K for d-block w held in registers as the MFMA
-// operand; the partial dQ goes to an fp32 accumulator with global atomics.
+// QK^T / dP MFMAs; the partial dQ goes to an fp32 accumulator with global
+// atomics.
 // One barrier per query block.
 //
 // drab_p: each wave writes its fp32 dS into an LDS tile skewed by j - i
@@ -36,21 +36,25 @@
 // branches.
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace {
 
 constexpr int D = 128;
 constexpr int BN = BWD_BN; // 128 keys per workgroup
 constexpr int BQ = 32;     // queries per block
 constexpr int NT = 256;
-// LDS row strides (bf16 elements), from measured gfx950 LDS throughput: Q and
-// dO are read both as 16-byte operands (fast at 8 mod 16 elements) and
-// transposed (fast at 160, fair at 168).
-constexpr int RS = 168;    // Q, dO tiles
-constexpr int KS = 160;    // K tile (prologue only)
+// Q, dO and dO-lo stage tiles are [32][128] bf16 with no padding; the 16-byte
+// chunks of row r are XOR-swizzled by sw(r) = 4(r%4) + (r/4)%4, which keeps
+// both the 16-byte operand reads (16 consecutive rows, one chunk) and the
+// transposing reads (4 consecutive rows, 4 chunks) free of bank conflicts,
+// and lets full blocks be copied global -> LDS directly (4 rows per wave
+// instruction).
 constexpr int SS = 40;     // dS tile [key][query]
 constexpr int WIN = 160;   // rab_p window per block (BQ + BN - 1 used)
 constexpr int RING = 256;  // drab_p ring (power of two >= WIN + BQ)
-constexpr int DK = 160;    // columns of the skewed dS tile: key - query + BQ - 1
+constexpr int DK = 160;    // diagonals of the skewed dS tile: key - query + BQ - 1 (159 used, row 159 stays 0)
+constexpr int DKP = 36;    // row pitch (floats) of the skewed tile: 32 queries + pad, 16-byte rows
 constexpr int TB = 64;     // time buckets that int64 differences can reach
 constexpr int TCOPY = 4;   // copies of each wave's drab_t table
 constexpr float NLOG2E = -1.4426950408889634f;
@@ -59,9 +63,9 @@ constexpr float NLN2 = -0.69314718055994531f;
 // Every LDS array is 16-byte aligned so operand reads compile to ds_read_b128
 // (8-byte alignment turns them into ds_read2_b64, several times slower).
 struct alignas(16) Stage {
-    alignas(16) bf16 q[BQ * RS];
-    alignas(16) bf16 dO[BQ * RS];
-    alignas(16) bf16 dOl[BQ * RS]; // low part of dO' (dO' = dO + dOl to ~16 bits)
+    alignas(16) bf16 q[BQ * D];
+    alignas(16) bf16 dO[BQ * D];
+    alignas(16) bf16 dOl[BQ * D]; // low part of dO' (dO' = dO + dOl to ~16 bits)
     float win[WIN];                // rab_p[clip(key - query)], slot = key - query + BQ - 1 - (k0 - q0)
     uint32_t qt[BQ];
     int64_t qt64[BQ];
@@ -71,16 +75,23 @@ struct alignas(16) Smem {
     Stage st[2];
     alignas(16) bf16 ds[2][BN * SS];
     union {
-        alignas(16) float dsk[2][BQ * DK]; // fp32 dS skewed: [query][key - query + BQ - 1]
-        alignas(16) bf16 k[BN * KS];       // K tile, prologue only
+        alignas(16) float dsk[2][DK * DKP]; // fp32 dS skewed: [key - query + BQ - 1][query]
+        alignas(16) bf16 kt[BN * D];        // the workgroup's K rows (prologue only), swizzled like the stage tiles
     };
     float ring[RING];
     float dtab[4][TCOPY][TB];
     float rabt_rev[32];
     float rabt[128];
 };
-static_assert(sizeof(float) * 2 * BQ * DK >= sizeof(bf16) * BN * KS, "K tile must fit the skewed tiles");
 
+// Element offset of (row, col) in a swizzled [rows][128] stage tile.
+DEV int swz(int row, int col)
+{
+    const int f = ((row & 3) << 2) | ((row >> 2) & 3);
+    return row * D + ((((col >> 3) ^ f)) << 3) + (col & 7);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4v lds_short4v;
 
@@ -93,10 +104,12 @@ DEV u32x2 lds_read_tr(const bf16 *p)
     return __builtin_bit_cast(u32x2, r);
 }
 
+static_assert(sizeof(float) * 2 * DK * DKP >= sizeof(bf16) * BN * D, "K tile must fit the skewed tiles");
+
 struct BwdLane {
     const uint32_t *qt;   // S.qt + 4g   (index with cr)
     const int64_t *qt64;  // S.qt64 + 4g
-    float *dsk;           // skewed-tile cell of (cr = 0) for this lane
+    float *dsk;           // skewed-tile cell of (cr = 0) for this lane; cell of cr at -(DKP - 1) cr
     float *dtab;          // this wave's drab_t table copy for this lane
     uint32_t tk;
     int64_t tk64;
@@ -150,7 +163,7 @@ DEV void bwd_pointwise(const floatx16 &xacc, const floatx16 &pacc, uint32_t (&pp
             }
             pp[u] = p;
             dd[u] = ds;
-            ln.dsk[cr * (DK - 1)] = ds;
+            ln.dsk[-(DKP - 1) * cr] = ds;
             if constexpr (DT && TM != 0) {
                 if constexpr (UNI) tsum += ds;
                 else atomicAdd(&ln.dtab[bucket], ds);
@@ -172,43 +185,41 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
     const int tj = l & 15, tsl = tj >> 2;
     const int cpart = ((l >> 4) & 1) * 16 + 4 * (tj & 3);
 
-    // ---- prologue: K tile in LDS (aliasing the skewed tiles), own K/V rows in registers
-    {
-        const int lc = tid >> 4, le = tid & 15; // 16 keys x 16 d-groups per pass
+    // ---- prologue: the workgroup's K rows into LDS (aliasing the skewed
+    // tiles; rows past the sequence repeat the last row: finite, and every
+    // pair they form is masked or has dS = 0), then into registers: own rows
+    // (B operand of X = Q K^T) and d-block w of all 128 rows (B operand of
+    // dQ = dS K).  Own V rows straight from memory.
 #pragma unroll
-        for (int pass = 0; pass < BN / 16; pass++) {
-            const int key = k0 + pass * 16 + lc;
-            const bool ok = key < L;
-            u32x4 x = ok ? *(const u32x4 *)(K + (int64_t)(o_b + key) * a.ldk + h * D + le * 8) : u32x4{0, 0, 0, 0};
-            *(u32x4 *)&sm.k[(pass * 16 + lc) * KS + le * 8] = x;
-        }
+    for (int i = 0; i < 8; i++) {
+        const int r0 = 4 * (8 * w + i), row = r0 + (l >> 4);
+        const int c = (l & 15) ^ (((row & 3) << 2) | ((row >> 2) & 3));
+        const int key = min(k0 + row, L - 1);
+        __builtin_amdgcn_global_load_lds((const void *)(K + (int64_t)(o_b + key) * a.ldk + h * D + c * 8),
+                                         (lds_void *)(sm.kt + r0 * D), 16, 0, 0);
     }
     const int mykey = k0 + 32 * w + lq;
     const bool kvalid = mykey < L;
-    bf16x8 kreg[8], vreg[8];
+    bf16x8 vreg[8], kreg[8], kq[8];
     {
-        const bf16 *kp = K + (int64_t)(o_b + (kvalid ? mykey : 0)) * a.ldk + h * D + g * 8;
         const bf16 *vp = V + (int64_t)(o_b + (kvalid ? mykey : 0)) * a.ldv + h * D + g * 8;
 #pragma unroll
-        for (int s = 0; s < 8; s++) {
-            kreg[s] = as_bf16x8(kvalid ? *(const u32x4 *)(kp + s * 16) : u32x4{0, 0, 0, 0});
-            vreg[s] = as_bf16x8(kvalid ? *(const u32x4 *)(vp + s * 16) : u32x4{0, 0, 0, 0});
-        }
+        for (int s = 0; s < 8; s++) vreg[s] = as_bf16x8(kvalid ? *(const u32x4 *)(vp + s * 16) : u32x4{0, 0, 0, 0});
     }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    // K as the B operand of dQ = dS K for d-block w: keys 16t + 8g + e of the
-    // workgroup, d = 32w + lq.
-    bf16x8 kq[8];
+#pragma unroll
+    for (int s = 0; s < 8; s++) kreg[s] = *(const bf16x8 *)&sm.kt[swz(32 * w + lq, s * 16 + g * 8)];
 #pragma unroll
     for (int t = 0; t < BN / 16; t++) {
         const int kr1 = 16 * t + 8 * g + tsl;
-        const u32x2 k1 = lds_read_tr(&sm.k[kr1 * KS + 32 * w + cpart]);
-        const u32x2 k2 = lds_read_tr(&sm.k[(kr1 + 4) * KS + 32 * w + cpart]);
+        const u32x2 k1 = lds_read_tr(&sm.kt[swz(kr1, 32 * w + cpart)]);
+        const u32x2 k2 = lds_read_tr(&sm.kt[swz(kr1 + 4, 32 * w + cpart)]);
         kq[t] = as_bf16x8(u32x4{k1[0], k1[1], k2[0], k2[1]});
     }
     __syncthreads(); // K tile consumed: its space becomes the skewed tiles
     for (int i = tid; i < RING; i += NT) sm.ring[i] = 0.f;
-    for (int i = tid; i < 2 * BQ * DK; i += NT) (&sm.dsk[0][0])[i] = 0.f;
+    for (int i = tid; i < 2 * DK * DKP; i += NT) (&sm.dsk[0][0])[i] = 0.f;
     for (int i = tid; i < 4 * TCOPY * TB; i += NT) (&sm.dtab[0][0][0])[i] = 0.f;
 
     BwdLane ln;
@@ -235,34 +246,28 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
             dk_acc[i][r] = 0.f;
         }
 
-    // ---- query-block stage loader: thread -> (query lcq, 16 d-groups)
-    const int lcq = tid >> 3, leq = tid & 7; // 32 queries x 8 threads x 16 elements
-    u32x4 qreg2[2], dreg2[2], lreg2[2];
+    // ---- query-block stage loader.  Full blocks: 24 groups of 4 rows (Q,
+    // dO, dO-lo) copied straight into LDS, 6 per wave; lane l fills physical
+    // chunk l%16 of row 4(G%8) + l/16.  The last, partial block goes through
+    // registers (rows past the sequence: Q from the last row, dO = 0, so they
+    // contribute nothing).
+    const int lcq = tid >> 3, leq = tid & 7; // partial path: 32 queries x 8 threads x 16 elements
     float wreg = 0.f;
     uint32_t treg = 0, tmn = 0xFFFFFFFFu, tmx = 0u;
     int64_t treg64 = 0;
-    auto gload = [&](int q0) {
-        const int qi = q0 + lcq;
-        if (q0 + BQ <= L) { // full block: no row checks
-            const int64_t row = (int64_t)(o_b + qi);
+    auto gload_direct = [&](int q0, Stage &S) {
 #pragma unroll
-            for (int c = 0; c < 2; c++) {
-                qreg2[c] = *(const u32x4 *)(Q + row * a.ldq + h * D + leq * 16 + c * 8);
-                dreg2[c] = *(const u32x4 *)(dO + row * ld_do + h * D + leq * 16 + c * 8);
-                lreg2[c] = *(const u32x4 *)(dOlo + row * ld_do + h * D + leq * 16 + c * 8);
-            }
-        } else {
-            // rows past the sequence: Q from the last row (finite), dO = 0 so
-            // they contribute nothing
-            const bool ok = qi < L;
-            const int64_t row = (int64_t)(o_b + (ok ? qi : L - 1));
-#pragma unroll
-            for (int c = 0; c < 2; c++) {
-                qreg2[c] = *(const u32x4 *)(Q + row * a.ldq + h * D + leq * 16 + c * 8);
-                dreg2[c] = ok ? *(const u32x4 *)(dO + row * ld_do + h * D + leq * 16 + c * 8) : u32x4{0, 0, 0, 0};
-                lreg2[c] = ok ? *(const u32x4 *)(dOlo + row * ld_do + h * D + leq * 16 + c * 8) : u32x4{0, 0, 0, 0};
-            }
+        for (int i = 0; i < 6; i++) {
+            const int G = 6 * w + i, plane = G >> 3, r0 = 4 * (G & 7);
+            const int row = r0 + (l >> 4);
+            const int c = (l & 15) ^ (((row & 3) << 2) | ((row >> 2) & 3));
+            const int64_t grow = (int64_t)(o_b + q0 + row);
+            const bf16 *src = plane == 0 ? Q + grow * a.ldq : (plane == 1 ? dO : dOlo) + grow * ld_do;
+            bf16 *dst = (plane == 0 ? S.q : (plane == 1 ? S.dO : S.dOl)) + r0 * D;
+            __builtin_amdgcn_global_load_lds((const void *)(src + h * D + c * 8), (lds_void *)dst, 16, 0, 0);
         }
+    };
+    auto gload_tables = [&](int q0) {
         if constexpr (HP) {
             if (tid < WIN) {
                 int dl = k0 - q0 - (BQ - 1) + tid; // key - query of window slot tid
@@ -287,14 +292,22 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
             }
         }
     };
-    auto sstore = [&](int buf) {
-        Stage &S = sm.st[buf];
+    auto load_partial = [&](int q0, Stage &S) {
+        const int qi = q0 + lcq;
+        const bool ok = qi < L;
+        const int64_t row = (int64_t)(o_b + (ok ? qi : L - 1));
 #pragma unroll
         for (int c = 0; c < 2; c++) {
-            *(u32x4 *)&S.q[lcq * RS + leq * 16 + c * 8] = qreg2[c];
-            *(u32x4 *)&S.dO[lcq * RS + leq * 16 + c * 8] = dreg2[c];
-            *(u32x4 *)&S.dOl[lcq * RS + leq * 16 + c * 8] = lreg2[c];
+            const int col = leq * 16 + c * 8;
+            const u32x4 qv = *(const u32x4 *)(Q + row * a.ldq + h * D + col);
+            const u32x4 dv = ok ? *(const u32x4 *)(dO + row * ld_do + h * D + col) : u32x4{0, 0, 0, 0};
+            const u32x4 lv = ok ? *(const u32x4 *)(dOlo + row * ld_do + h * D + col) : u32x4{0, 0, 0, 0};
+            *(u32x4 *)&S.q[swz(lcq, col)] = qv;
+            *(u32x4 *)&S.dO[swz(lcq, col)] = dv;
+            *(u32x4 *)&S.dOl[swz(lcq, col)] = lv;
         }
+    };
+    auto sstore_tables = [&](Stage &S) {
         if constexpr (HP)
             if (tid < WIN) S.win[tid] = wreg;
         if constexpr (TM != 0) {
@@ -314,7 +327,7 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
 
     // dQ of the block at q0m from the dS tile `dst` (all 4 waves' keys):
     // dQ[32 queries][d-block w] = sum over 128 keys of dS[q][key] K[key][d]
-    auto dq_block = [&](const bf16 *dst, int q0m) {
+    auto dq_mfma = [&](const bf16 *dst) {
         floatx16 qacc;
 #pragma unroll
         for (int r = 0; r < 16; r++) qacc[r] = 0.f;
@@ -325,9 +338,12 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
             const u32x2 s2 = lds_read_tr(&dst[(kr1 + 4) * SS + cpart]);
             qacc = mfma32(as_bf16x8(u32x4{s1[0], s1[1], s2[0], s2[1]}), kq[t], qacc);
         }
-        // C layout: lane holds d = 32w + lq, queries 8(r/4) + 4g + r%4
+        return qacc;
+    };
+    // C layout: lane holds d = 32w + lq, queries 8(r/4) + 4g + r%4
+    auto dq_atomics = [&](const floatx16 &qacc, int q0m, bool full) {
         float *dqp = a.dq_acc + (int64_t)(o_b + q0m + 4 * g) * ld_do + h * D + 32 * w + lq;
-        if (q0m + BQ <= L) {
+        if (full) {
 #pragma unroll
             for (int r = 0; r < 16; r++) atomicAdd(dqp + (int64_t)(8 * (r >> 2) + (r & 3)) * ld_do, qacc[r]);
         } else {
@@ -339,76 +355,88 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
             }
         }
     };
-    // drab_p of the block at q0m from its skewed tile: thread c sums diagonal
-    // c (key - query = k0 - q0m + c - (BQ - 1)); cells outside the tile's keys
-    // are never written and stay 0.  The ring entry is flushed once no later
-    // block can reach it (key - query > k0 + BN - 1 - (q0m + BQ)  <=>  c > BN - 2).
-    auto drabp_block = [&](const float *dsk, int q0m) {
-        if (a.drab_p && tid < DK - 1) {
-            const int c = tid;
-            float part[4] = {0.f, 0.f, 0.f, 0.f};
+    // drab_p of the block at q0m from its skewed tile (row c = diagonal c,
+    // key - query = k0 - q0m + c - (BQ - 1); cells outside the tile's keys are
+    // never written and stay 0).  Every thread sums one row (threads past the
+    // last diagonal take the all-zero row DK - 1).  The ring entry is flushed
+    // once no later block can reach it (key - query > k0 + BN - 1 - (q0m + BQ)
+    // <=>  c > BN - 2).
+    auto drabp_sum = [&](const float *dsk, int q0m, int &slot, float &tot, int &dl) {
+        const int c = tid < DK - 1 ? tid : DK - 1;
+        const floatx4 *rowp = (const floatx4 *)(dsk + c * DKP);
+        floatx4 acc4 = rowp[0];
 #pragma unroll
-            for (int rq = 0; rq < BQ; rq++) part[rq & 3] += dsk[rq * DK + c];
-            const float sum = (part[0] + part[1]) + (part[2] + part[3]);
-            const int dl = k0 - q0m + c - (BQ - 1);
-            const int slot = dl & (RING - 1);
-            const float tot = sm.ring[slot] + sum;
-            if (c > BN - 2) {
-                if (tot != 0.f) {
-                    const int cl = dl < -a.N ? -a.N : (dl > a.N ? a.N : dl);
-                    atomicAdd(&a.drab_p[h * p_hs + cl + a.N], tot);
-                }
-                sm.ring[slot] = 0.f;
-            } else {
-                sm.ring[slot] = tot;
-            }
+        for (int i = 1; i < BQ / 4; i++) acc4 += rowp[i];
+        const float sum = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
+        dl = k0 - q0m + c - (BQ - 1);
+        slot = dl & (RING - 1);
+        tot = sm.ring[slot] + sum;
+        sm.ring[slot] = c > BN - 2 ? 0.f : tot;
+    };
+    auto drabp_flush = [&](int dl, float tot) {
+        const int c = tid < DK - 1 ? tid : DK - 1;
+        if (c > BN - 2 && tot != 0.f) {
+            const int cl = dl < -a.N ? -a.N : (dl > a.N ? a.N : dl);
+            atomicAdd(&a.drab_p[h * p_hs + cl + a.N], tot);
         }
     };
 
+    // ---- one query block.  MAIN: a block in the middle of the range (every
+    // wave is past its diagonal block, this, the previous and the next block
+    // are full), compiled without the per-block checks so that the MFMA, LDS
+    // and VALU work of the phases can be interleaved.
     const int nqb = (L - k0 + BQ - 1) / BQ; // query blocks [k0, L); >= 1
-    gload(k0);
-    sstore(0);
-    __syncthreads();
-
-    const int kw0 = k0 + 32 * w; // this wave's first key
-    for (int n = 0; n < nqb; n++) {
+    const int kw0 = k0 + 32 * w;            // this wave's first key
+    const int krow = 32 * w + lq;
+    auto iteration = [&](auto main_c, int n) {
+        constexpr bool MAIN = decltype(main_c)::value;
         const int q0 = k0 + n * BQ;
-        if (n + 1 < nqb) gload(q0 + BQ);
+        const bool nfull = q0 + 2 * BQ <= L; // the next block is full
+        if (MAIN) gload_direct(q0 + BQ, sm.st[(n + 1) & 1]);
+        else if (n + 1 < nqb && nfull) gload_direct(q0 + BQ, sm.st[(n + 1) & 1]);
         const Stage &S = sm.st[n & 1];
         float *dskn = sm.dsk[n & 1];
         bf16 *dsn = sm.ds[n & 1];
-        const bool skip = kw0 > q0 + BQ - 1 || kw0 >= L;
+        const bool skip = MAIN ? false : (kw0 > q0 + BQ - 1 || kw0 >= L);
+        // X = Q K^T + rab_p window, dP = dO' V^T (hi and lo planes)
         floatx16 xacc, pacc;
-        if (!skip) {
-            // X = Q K^T + rab_p window, dP = dO' V^T (hi and lo planes)
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int cr = 8 * (r >> 2) + (r & 3);
-                xacc[r] = HP ? S.win[32 * w + lq + (BQ - 1) - 4 * g - cr] : 0.f;
-                pacc[r] = 0.f;
-            }
+        for (int r = 0; r < 16; r++) {
+            const int cr = 8 * (r >> 2) + (r & 3);
+            xacc[r] = HP ? S.win[krow + (BQ - 1) - 4 * g - cr] : 0.f;
+            pacc[r] = 0.f;
+        }
+        if (!skip) {
 #pragma unroll
             for (int s = 0; s < 8; s++) {
-                const bf16x8 qa = *(const bf16x8 *)&S.q[lq * RS + s * 16 + g * 8];
-                const bf16x8 da = *(const bf16x8 *)&S.dO[lq * RS + s * 16 + g * 8];
-                const bf16x8 dl = *(const bf16x8 *)&S.dOl[lq * RS + s * 16 + g * 8];
+                const int o = swz(lq, s * 16 + g * 8);
+                const bf16x8 qa = *(const bf16x8 *)&S.q[o];
+                const bf16x8 da = *(const bf16x8 *)&S.dO[o];
+                const bf16x8 dl = *(const bf16x8 *)&S.dOl[o];
                 xacc = mfma32(qa, kreg[s], xacc);
                 pacc = mfma32(da, vreg[s], pacc);
                 pacc = mfma32(dl, vreg[s], pacc);
             }
         }
         // the previous block's dQ and drab_p (its dS tiles are complete)
-        if (n > 0) {
-            dq_block(sm.ds[(n - 1) & 1], q0 - BQ);
-            drabp_block(sm.dsk[(n - 1) & 1], q0 - BQ);
+        floatx16 qacc;
+        int slot = 0, dlf = 0;
+        float tot = 0.f;
+        if (MAIN || n > 0) {
+            qacc = dq_mfma(sm.ds[(n - 1) & 1]);
+            if (a.drab_p) drabp_sum(sm.dsk[(n - 1) & 1], q0 - BQ, slot, tot, dlf);
+            dq_atomics(qacc, q0 - BQ, MAIN ? true : q0 <= L);
         }
-        ln.dsk = dskn + 4 * g * (DK - 1) + 32 * w + lq + (BQ - 1);
-        const int krow = 32 * w + lq;
+        if (MAIN) gload_tables(q0 + BQ);
+        else if (n + 1 < nqb) gload_tables(q0 + BQ);
+        if ((MAIN || n > 0) && a.drab_p) drabp_flush(dlf, tot);
+
+        ln.dsk = dskn + (krow + (BQ - 1) - 4 * g) * DKP + 4 * g;
         if (!skip) {
             ln.qt = &S.qt[4 * g];
             ln.qt64 = &S.qt64[4 * g];
             ln.dmask = kw0 + lq - q0 - 4 * g; // key > query  <=>  cr < dmask
-            const bool diag = kw0 + 31 > q0;
+            const bool diag = MAIN ? false : kw0 + 31 > q0;
             bool uni = false;
             int ubk = 0;
             if constexpr (TM == 1) {
@@ -452,11 +480,12 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
                 const int qr1 = 16 * m + 4 * g + tsl; // query row of the transposing read
 #pragma unroll
                 for (int db = 0; db < 4; db++) {
-                    const u32x2 d1 = lds_read_tr(&S.dO[qr1 * RS + db * 32 + cpart]);
-                    const u32x2 d2 = lds_read_tr(&S.dO[(qr1 + 8) * RS + db * 32 + cpart]);
+                    const int o1 = swz(qr1, db * 32 + cpart), o2 = swz(qr1 + 8, db * 32 + cpart);
+                    const u32x2 d1 = lds_read_tr(&S.dO[o1]);
+                    const u32x2 d2 = lds_read_tr(&S.dO[o2]);
                     dv_acc[db] = mfma32(as_bf16x8(u32x4{d1[0], d1[1], d2[0], d2[1]}), pb, dv_acc[db]);
-                    const u32x2 q1 = lds_read_tr(&S.q[qr1 * RS + db * 32 + cpart]);
-                    const u32x2 q2 = lds_read_tr(&S.q[(qr1 + 8) * RS + db * 32 + cpart]);
+                    const u32x2 q1 = lds_read_tr(&S.q[o1]);
+                    const u32x2 q2 = lds_read_tr(&S.q[o2]);
                     dk_acc[db] = mfma32(as_bf16x8(u32x4{q1[0], q1[1], q2[0], q2[1]}), sb, dk_acc[db]);
                 }
             }
@@ -464,16 +493,40 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
 #pragma unroll
             for (int gr = 0; gr < 4; gr++) *(u32x2 *)&dsn[krow * SS + 8 * gr + 4 * g] = u32x2{0u, 0u};
 #pragma unroll
-            for (int rr = 0; rr < 16; rr++) ln.dsk[(8 * (rr >> 2) + (rr & 3)) * (DK - 1)] = 0.f;
+            for (int rr = 0; rr < 16; rr++) ln.dsk[-(DKP - 1) * (8 * (rr >> 2) + (rr & 3))] = 0.f;
         }
-        if (n + 1 < nqb) sstore((n + 1) & 1);
+        if (MAIN || n + 1 < nqb) {
+            if (!MAIN && !nfull) load_partial(q0 + BQ, sm.st[(n + 1) & 1]);
+            sstore_tables(sm.st[(n + 1) & 1]);
+        }
+        __builtin_amdgcn_s_waitcnt(0); // direct LDS copies (and everything else) landed
         __syncthreads();
-    }
+    };
+
+    if (k0 + BQ <= L) gload_direct(k0, sm.st[0]);
+    else load_partial(k0, sm.st[0]);
+    gload_tables(k0);
+    sstore_tables(sm.st[0]);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    const std::integral_constant<bool, false> generic{};
+    const std::integral_constant<bool, true> fast{};
+    const int n_main_end = nqb - 2; // main blocks: [4, nqb - 2)
+    int n = 0;
+    for (; n < nqb && (n < 4 || n >= n_main_end); n++) iteration(generic, n);
+    for (; n < n_main_end; n++) iteration(fast, n);
+    for (; n < nqb; n++) iteration(generic, n);
+
     // the last block's dQ and drab_p, then what is left in the ring and the time tables
     {
         const int qlast = k0 + (nqb - 1) * BQ;
-        dq_block(sm.ds[(nqb - 1) & 1], qlast);
-        drabp_block(sm.dsk[(nqb - 1) & 1], qlast);
+        const floatx16 qacc = dq_mfma(sm.ds[(nqb - 1) & 1]);
+        int slot = 0, dlf = 0;
+        float tot = 0.f;
+        if (a.drab_p) drabp_sum(sm.dsk[(nqb - 1) & 1], qlast, slot, tot, dlf);
+        dq_atomics(qacc, qlast, qlast + BQ <= L);
+        if (a.drab_p) drabp_flush(dlf, tot);
         __syncthreads();
         if (a.drab_p) {
             // remaining key - query values: [k0 - qlast - (BQ - 1), k0 + BN - 1 - qlast - BQ]
