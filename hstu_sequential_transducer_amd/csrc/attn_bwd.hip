@@ -418,18 +418,22 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
                 pacc = mfma32(dl, vreg[s], pacc);
             }
         }
-        // the previous block's dQ and drab_p (its dS tiles are complete)
-        floatx16 qacc;
+        // the previous block's drab_p (its skewed tile is complete)
         int slot = 0, dlf = 0;
         float tot = 0.f;
-        if (MAIN || n > 0) {
-            qacc = dq_mfma(sm.ds[(n - 1) & 1]);
-            if (a.drab_p) drabp_sum(sm.dsk[(n - 1) & 1], q0 - BQ, slot, tot, dlf);
-            dq_atomics(qacc, q0 - BQ, MAIN ? true : q0 <= L);
-        }
+        if ((MAIN || n > 0) && a.drab_p) drabp_sum(sm.dsk[(n - 1) & 1], q0 - BQ, slot, tot, dlf);
         if (MAIN) gload_tables(q0 + BQ);
         else if (n + 1 < nqb) gload_tables(q0 + BQ);
         if ((MAIN || n > 0) && a.drab_p) drabp_flush(dlf, tot);
+        // The previous block's dQ and this block's dV/dK come last: they use
+        // transposing LDS reads, before which the compiler waits for the
+        // outstanding direct copies of the next block.
+        auto prev_dq = [&]() {
+            if (MAIN || n > 0) {
+                const floatx16 qacc = dq_mfma(sm.ds[(n - 1) & 1]);
+                dq_atomics(qacc, q0 - BQ, MAIN ? true : q0 <= L);
+            }
+        };
 
         ln.dsk = dskn + (krow + (BQ - 1) - 4 * g) * DKP + 4 * g;
         if (!skip) {
@@ -472,6 +476,7 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
                 const u32x2 v2 = {dpk[2 * gr], dpk[2 * gr + 1]};
                 *(u32x2 *)&dsn[krow * SS + 8 * gr + 4 * g] = v2;
             }
+            prev_dq();
             // dV^T += dO'^T P and dK^T += Q^T dS  (contraction over the 32 queries)
 #pragma unroll
             for (int m = 0; m < 2; m++) {
@@ -494,6 +499,7 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
             for (int gr = 0; gr < 4; gr++) *(u32x2 *)&dsn[krow * SS + 8 * gr + 4 * g] = u32x2{0u, 0u};
 #pragma unroll
             for (int rr = 0; rr < 16; rr++) ln.dsk[-(DKP - 1) * (8 * (rr >> 2) + (rr & 3))] = 0.f;
+            prev_dq();
         }
         if (MAIN || n + 1 < nqb) {
             if (!MAIN && !nfull) load_partial(q0 + BQ, sm.st[(n + 1) & 1]);
