@@ -417,6 +417,16 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
                 pacc = mfma32(da, vreg[s], pacc);
                 pacc = mfma32(dl, vreg[s], pacc);
             }
+            if constexpr (MAIN) {
+                // keep LDS operand reads two steps ahead of the MFMAs
+                __builtin_amdgcn_sched_group_barrier(0x100, 14, 0);
+#pragma unroll
+                for (int i = 0; i < 6; i++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+            }
         }
         // the previous block's drab_p (its skewed tile is complete)
         int slot = 0, dlf = 0;
@@ -520,9 +530,13 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
     const std::integral_constant<bool, true> fast{};
     const int n_main_end = nqb - 2; // main blocks: [4, nqb - 2)
     int n = 0;
-    for (; n < nqb && (n < 4 || n >= n_main_end); n++) iteration(generic, n);
-    for (; n < n_main_end; n++) iteration(fast, n);
-    for (; n < nqb; n++) iteration(generic, n);
+    if constexpr (TM == 2) { // sequences with a time span beyond 32 bits: rare, generic path only
+        for (; n < nqb; n++) iteration(generic, n);
+    } else {
+        for (; n < nqb && (n < 4 || n >= n_main_end); n++) iteration(generic, n);
+        for (; n < n_main_end; n++) iteration(fast, n);
+        for (; n < nqb; n++) iteration(generic, n);
+    }
 
     // the last block's dQ and drab_p, then what is left in the ring and the time tables
     {
