@@ -11,24 +11,24 @@
 // softmax statistics, so nothing else is needed).  dO' arrives as two bf16
 // planes (hi + lo) so dP keeps ~16 significant bits.
 //
-// A workgroup of 4 waves owns 128 keys of one (sequence, head), their K rows
-// in LDS; wave w owns keys 32w..32w+31 with their V rows and their dK^T, dV^T
-// accumulators in registers.  Query blocks of 32 stream through LDS (double
-// buffered, copied global -> LDS directly).  Per block a wave computes X = Q K^T + rab_p (the rab_p window
-// is loaded into the accumulator) and dP with 32x32x16 bf16 MFMA (lane = key,
-// registers = queries), the element-wise step, dV^T += dO'^T P and
+// A workgroup of 8 waves owns 128 keys of one (sequence, head); wave w owns
+// keys 16w..16w+15 with their K and V rows and their dK^T, dV^T accumulators
+// in registers (about 240 registers a wave, so two waves share a SIMD and one
+// wave's element-wise VALU work overlaps the other's MFMAs).  Query blocks of
+// 32 stream through LDS (double buffered, copied global -> LDS directly).  Per
+// block a wave computes X = Q K^T + rab_p (the rab_p window is loaded into the
+// accumulator) and dP on 16x16x32 bf16 MFMA as two 16-query tiles (lane =
+// key, registers = queries), the element-wise step, dV^T += dO'^T P and
 // dK^T += Q^T dS (transposing LDS reads for dO'^T and Q^T), and writes dS to
-// an LDS tile.  dQ for d-block w over all 128 keys needs every wave's dS, so
-// it runs one block late: in the next iteration, next to that block's
-// QK^T / dP MFMAs; the partial dQ goes to an fp32 accumulator with global
-// atomics.
-// One barrier per query block.
+// an LDS tile.  dQ needs every wave's dS, so it runs one block late: wave w
+// computes a 16-query x 32-d slice over all 128 keys and adds it to an fp32
+// accumulator with global atomics.  One barrier per query block.
 //
 // drab_p: each wave writes its fp32 dS into an LDS tile skewed by j - i
-// ([query][key - query]); one block later, one thread per diagonal sums it
+// ([key - query][query]); one block later, one thread per diagonal sums it
 // into an LDS ring indexed by j - i, and an entry is flushed with one global
 // atomic once no later block can reach it.  drab_t: when every pair of a
-// 32x32 block falls in one time bucket (decided per block in scalar code from
+// 16x32 block falls in one time bucket (decided per block in scalar code from
 // the min/max times of its queries and keys) the bias is a scalar and the
 // block's dS is summed by a wave reduction; otherwise per-element adds go to
 // per-wave LDS tables.  Bias presence, time mode, diagonal masking and uniform
@@ -43,14 +43,16 @@ namespace {
 constexpr int D = 128;
 constexpr int BN = BWD_BN; // 128 keys per workgroup
 constexpr int BQ = 32;     // queries per block
-constexpr int NT = 256;
-// Q, dO and dO-lo stage tiles are [32][128] bf16 with no padding; the 16-byte
-// chunks of row r are XOR-swizzled by sw(r) = 4(r%4) + (r/4)%4, which keeps
-// both the 16-byte operand reads (16 consecutive rows, one chunk) and the
-// transposing reads (4 consecutive rows, 4 chunks) free of bank conflicts,
-// and lets full blocks be copied global -> LDS directly (4 rows per wave
-// instruction).
-constexpr int SS = 40;     // dS tile [key][query]
+constexpr int NW = 8;      // waves per workgroup
+constexpr int KW = 16;     // keys per wave
+constexpr int NT = 64 * NW;
+// Q, dO and dO-lo stage tiles (and the prologue's K tile) are [rows][128]
+// bf16 with no padding; the 16-byte chunks of row r are XOR-swizzled by
+// sw(r) = 4(r%4) + bitrev2((r/4)%4), which keeps the 16-byte operand reads
+// (16 consecutive rows, one chunk) and the transposing reads (rows 4g..4g+3
+// of each 16-lane group g, 32 bytes each) free of bank conflicts, and lets
+// full blocks be copied global -> LDS directly (4 rows per wave instruction).
+constexpr int SS = 40;     // dS tile [key][query] row stride (bf16)
 constexpr int WIN = 160;   // rab_p window per block (BQ + BN - 1 used)
 constexpr int RING = 256;  // drab_p ring (power of two >= WIN + BQ)
 constexpr int DK = 160;    // diagonals of the skewed dS tile: key - query + BQ - 1 (159 used, row 159 stays 0)
@@ -60,36 +62,35 @@ constexpr int TCOPY = 4;   // copies of each wave's drab_t table
 constexpr float NLOG2E = -1.4426950408889634f;
 constexpr float NLN2 = -0.69314718055994531f;
 
-// Every LDS array is 16-byte aligned so operand reads compile to ds_read_b128
-// (8-byte alignment turns them into ds_read2_b64, several times slower).
 struct alignas(16) Stage {
     alignas(16) bf16 q[BQ * D];
     alignas(16) bf16 dO[BQ * D];
     alignas(16) bf16 dOl[BQ * D]; // low part of dO' (dO' = dO + dOl to ~16 bits)
-    float win[WIN];                // rab_p[clip(key - query)], slot = key - query + BQ - 1 - (k0 - q0)
+    float win[WIN];               // rab_p[clip(key - query)], slot = key - query + BQ - 1 - (k0 - q0)
     uint32_t qt[BQ];
     int64_t qt64[BQ];
-    uint32_t qtmin, qtmax;         // over the block's valid queries
+    uint32_t qtmin, qtmax;        // over the block's valid queries
 };
 struct alignas(16) Smem {
     Stage st[2];
     alignas(16) bf16 ds[2][BN * SS];
-    union {
-        alignas(16) float dsk[2][DK * DKP]; // fp32 dS skewed: [key - query + BQ - 1][query]
-        alignas(16) bf16 kt[BN * D];        // the workgroup's K rows (prologue only), swizzled like the stage tiles
-    };
+    alignas(16) float dsk[2][DK * DKP]; // fp32 dS skewed: [key - query + BQ - 1][query]
+    alignas(16) bf16 kt[BN * D];        // the workgroup's K rows, swizzled like the stage tiles
     float ring[RING];
-    float dtab[4][TCOPY][TB];
+    float dtab[NW][TCOPY][TB];
     float rabt_rev[32];
     float rabt[128];
 };
+static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget");
 
-// Element offset of (row, col) in a swizzled [rows][128] stage tile.
-DEV int swz(int row, int col)
+// Swizzle of row r: the XOR applied to its 16-byte chunk index.
+DEV int swf(int row)
 {
-    const int f = ((row & 3) << 2) | ((row >> 2) & 3);
-    return row * D + ((((col >> 3) ^ f)) << 3) + (col & 7);
+    const int hi = (row >> 2) & 3;
+    return ((row & 3) << 2) | ((hi & 1) << 1) | (hi >> 1);
 }
+// Element offset of (row, col) in a swizzled [rows][128] tile.
+DEV int swz(int row, int col) { return row * D + (((col >> 3) ^ swf(row)) << 3) + (col & 7); }
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short short4v __attribute__((ext_vector_type(4)));
@@ -97,40 +98,45 @@ typedef __attribute__((address_space(3))) short4v lds_short4v;
 
 // Transposing LDS read (ds_read_b64_tr_b16).  Inside each group of 16 lanes,
 // lane i receives element i%4 of the 4-element chunks addressed by lanes
-// i/4, i/4+4, i/4+8, i/4+12 (in that order).
+// i/4, i/4+4, i/4+8, i/4+12 (in that order).  So if lane L of the group
+// addresses row r0 + L/4, column c0 + 4(L%4), lane i receives rows r0..r0+3
+// of column c0 + i.
 DEV u32x2 lds_read_tr(const bf16 *p)
 {
     short4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(p));
     return __builtin_bit_cast(u32x2, r);
 }
 
-static_assert(sizeof(float) * 2 * DK * DKP >= sizeof(bf16) * BN * D, "K tile must fit the skewed tiles");
+// 16x16x32 bf16 MFMA.  Lane l supplies A[l%16][8*(l/16) .. +8] and
+// B[8*(l/16) .. +8][l%16]; C register r of lane l is C[4*(l/16) + r][l%16].
+DEV floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0); }
 
 struct BwdLane {
-    const uint32_t *qt;   // S.qt + 4g   (index with cr)
+    const uint32_t *qt;   // S.qt + 4g   (index with cq)
     const int64_t *qt64;  // S.qt64 + 4g
-    float *dsk;           // skewed-tile cell of (cr = 0) for this lane; cell of cr at -(DKP - 1) cr
+    float *dsk;           // skewed-tile cell of (cq = 0) for this lane; cell of cq at -(DKP - 1) cq
     float *dtab;          // this wave's drab_t table copy for this lane
     uint32_t tk;
     int64_t tk64;
-    int dmask;            // masked (key > query) iff cr < dmask  (diagonal blocks)
+    int dmask;            // masked (key > query) iff cq < dmask  (diagonal blocks)
 };
 
-// Element-wise step of one 32x32 block.  Register r <-> query ql = 4g + cr(r),
-// cr = 8(r/4) + r%4; this lane's key.  xacc holds x - rab_t (the rab_p term is
-// already in).  Writes packed bf16 P and dS, the fp32 dS into the skewed tile,
-// and the drab_t contributions.
+// Element-wise step of one 16-key x 32-query block.  Element (hh, r) <->
+// query 4g + cq, cq = 16hh + r; this lane's key.  xacc holds x - rab_t (the
+// rab_p term is already in).  Writes packed bf16 P and dS (queries 4g..4g+3
+// then 16+4g..16+4g+3), the fp32 dS into the skewed tile, and the drab_t
+// contributions.
 template <int TM, bool DT, bool DIAG, bool UNI>
-DEV void bwd_pointwise(const floatx16 &xacc, const floatx16 &pacc, uint32_t (&ppk)[8], uint32_t (&dpk)[8],
+DEV void bwd_pointwise(const floatx4 (&xacc)[2], const floatx4 (&pacc)[2], uint32_t (&ppk)[4], uint32_t (&dpk)[4],
                        const BwdLane &ln, const float *rabt_rev, const float *rabt, float ubias, float &tsum)
 {
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
+    for (int e = 0; e < 8; e += 2) {
         float pp[2], dd[2];
 #pragma unroll
         for (int u = 0; u < 2; u++) {
-            const int rr = r + u;
-            const int cr = 8 * (rr >> 2) + (rr & 3);
+            const int hh = (e + u) >> 2, r = (e + u) & 3;
+            const int cq = 16 * hh + r;
             // x' = -log2(e) x (time tables staged pre-scaled), sg = sigmoid(x),
             // p' = x' sg = -log2(e) SiLU(x) (the -ln 2 goes into dV's final scale),
             // dS = dP sg (1 + x (1 - sg)) = dP (sg - ln2 (p' - p' sg)).
@@ -140,96 +146,87 @@ DEV void bwd_pointwise(const floatx16 &xacc, const floatx16 &pacc, uint32_t (&pp
                 if constexpr (UNI) {
                     tb = ubias;
                 } else {
-                    const uint32_t tq = ln.qt[cr];
+                    const uint32_t tq = ln.qt[cq];
                     const uint32_t dd1 = (tq > ln.tk ? tq - ln.tk : ln.tk - tq) + 1u;
                     const int cz = __builtin_clz(dd1);
                     tb = rabt_rev[cz];
                     bucket = 31 - cz;
                 }
             } else if constexpr (TM == 2) {
-                bucket = time_bucket64(ln.qt64[cr] - ln.tk64);
+                bucket = time_bucket64(ln.qt64[cq] - ln.tk64);
                 tb = rabt[bucket];
             }
-            const float x = __builtin_fmaf(xacc[rr], NLOG2E, tb);
+            const float x = __builtin_fmaf(xacc[hh][r], NLOG2E, tb);
             const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x));
             float p = x * sg;
             const float t = __builtin_fmaf(-p, sg, p);
-            float ds = pacc[rr] * __builtin_fmaf(t, NLN2, sg);
+            float ds = pacc[hh][r] * __builtin_fmaf(t, NLN2, sg);
             if constexpr (DIAG) {
-                if (cr < ln.dmask) {
+                if (cq < ln.dmask) {
                     p = 0.f;
                     ds = 0.f;
                 }
             }
             pp[u] = p;
             dd[u] = ds;
-            ln.dsk[-(DKP - 1) * cr] = ds;
+            ln.dsk[-(DKP - 1) * cq] = ds;
             if constexpr (DT && TM != 0) {
                 if constexpr (UNI) tsum += ds;
                 else atomicAdd(&ln.dtab[bucket], ds);
             }
         }
-        ppk[r >> 1] = pack2_bf16(pp[0], pp[1]);
-        dpk[r >> 1] = pack2_bf16(dd[0], dd[1]);
+        ppk[e >> 1] = pack2_bf16(pp[0], pp[1]);
+        dpk[e >> 1] = pack2_bf16(dd[0], dd[1]);
     }
 }
 
 template <bool HP, int TM, bool DT>
 DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
 {
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, lq = l & 31;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, j = l & 15;
     const bf16 *Q = a.q, *K = a.k, *V = a.v, *dO = a.dO;
     const int64_t ld_do = (int64_t)a.H * D;
     const bf16 *dOlo = dO + (int64_t)a.T * ld_do;
-    // transposing-read lane constants
-    const int tj = l & 15, tsl = tj >> 2;
-    const int cpart = ((l >> 4) & 1) * 16 + 4 * (tj & 3);
+    // transposing-read lane constants: row offset j/4, column offset 4(j%4)
+    const int trr = j >> 2, trc = 4 * (j & 3);
 
-    // ---- prologue: the workgroup's K rows into LDS (aliasing the skewed
-    // tiles; rows past the sequence repeat the last row: finite, and every
-    // pair they form is masked or has dS = 0), then into registers: own rows
-    // (B operand of X = Q K^T) and d-block w of all 128 rows (B operand of
-    // dQ = dS K).  Own V rows straight from memory.
+    // ---- prologue: the workgroup's K rows into LDS (rows past the sequence
+    // repeat the last row: finite, and every pair they form is masked or has
+    // dS = 0); it supplies the B operands of X = Q K^T (own rows) and of
+    // dQ = dS K (all rows).  Own V rows into registers.
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-        const int r0 = 4 * (8 * w + i), row = r0 + (l >> 4);
-        const int c = (l & 15) ^ (((row & 3) << 2) | ((row >> 2) & 3));
+    for (int i = 0; i < BN / (4 * NW); i++) {
+        const int r0 = 4 * ((BN / (4 * NW)) * w + i), row = r0 + (l >> 4);
+        const int c = (l & 15) ^ swf(row);
         const int key = min(k0 + row, L - 1);
         __builtin_amdgcn_global_load_lds((const void *)(K + (int64_t)(o_b + key) * a.ldk + h * D + c * 8),
                                          (lds_void *)(sm.kt + r0 * D), 16, 0, 0);
     }
-    const int mykey = k0 + 32 * w + lq;
+    const int kw0 = k0 + KW * w; // this wave's first key
+    const int mykey = kw0 + j;
     const bool kvalid = mykey < L;
-    bf16x8 vreg[8], kreg[8], kq[8];
+    bf16x8 vreg[4];
     {
         const bf16 *vp = V + (int64_t)(o_b + (kvalid ? mykey : 0)) * a.ldv + h * D + g * 8;
 #pragma unroll
-        for (int s = 0; s < 8; s++) vreg[s] = as_bf16x8(kvalid ? *(const u32x4 *)(vp + s * 16) : u32x4{0, 0, 0, 0});
+        for (int s = 0; s < 4; s++) vreg[s] = as_bf16x8(kvalid ? *(const u32x4 *)(vp + s * 32) : u32x4{0, 0, 0, 0});
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-#pragma unroll
-    for (int s = 0; s < 8; s++) kreg[s] = *(const bf16x8 *)&sm.kt[swz(32 * w + lq, s * 16 + g * 8)];
-#pragma unroll
-    for (int t = 0; t < BN / 16; t++) {
-        const int kr1 = 16 * t + 8 * g + tsl;
-        const u32x2 k1 = lds_read_tr(&sm.kt[swz(kr1, 32 * w + cpart)]);
-        const u32x2 k2 = lds_read_tr(&sm.kt[swz(kr1 + 4, 32 * w + cpart)]);
-        kq[t] = as_bf16x8(u32x4{k1[0], k1[1], k2[0], k2[1]});
-    }
-    __syncthreads(); // K tile consumed: its space becomes the skewed tiles
+    const int qt_w = w & 1;           // this wave's query tile of dQ
+    const int dt_w = 2 * (w >> 1);    // its first d-tile of dQ
     for (int i = tid; i < RING; i += NT) sm.ring[i] = 0.f;
     for (int i = tid; i < 2 * DK * DKP; i += NT) (&sm.dsk[0][0])[i] = 0.f;
-    for (int i = tid; i < 4 * TCOPY * TB; i += NT) (&sm.dtab[0][0][0])[i] = 0.f;
+    for (int i = tid; i < NW * TCOPY * TB; i += NT) (&sm.dtab[0][0][0])[i] = 0.f;
 
     BwdLane ln;
     ln.tk = (TM == 1 && kvalid) ? a.rel[o_b + mykey] : 0u;
     ln.tk64 = (TM == 2 && kvalid) ? a.ts[o_b + mykey] : 0;
-    ln.dtab = &sm.dtab[w][lq & (TCOPY - 1)][0];
+    ln.dtab = &sm.dtab[w][j & (TCOPY - 1)][0];
     // time range of this wave's valid keys (for the uniform-bucket test), as scalars
     uint32_t tkmin = kvalid ? ln.tk : 0xFFFFFFFFu, tkmax = kvalid ? ln.tk : 0u;
     if constexpr (TM == 1) {
-        for (int o = 32; o >= 1; o >>= 1) {
+        for (int o = 8; o >= 1; o >>= 1) {
             tkmin = min(tkmin, (uint32_t)__shfl_xor((int)tkmin, o, 64));
             tkmax = max(tkmax, (uint32_t)__shfl_xor((int)tkmax, o, 64));
         }
@@ -237,30 +234,30 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
         tkmax = __builtin_amdgcn_readfirstlane(tkmax);
     }
 
-    floatx16 dv_acc[4], dk_acc[4];
+    floatx4 dv_acc[8], dk_acc[8];
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < 8; i++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
+        for (int r = 0; r < 4; r++) {
             dv_acc[i][r] = 0.f;
             dk_acc[i][r] = 0.f;
         }
 
     // ---- query-block stage loader.  Full blocks: 24 groups of 4 rows (Q,
-    // dO, dO-lo) copied straight into LDS, 6 per wave; lane l fills physical
+    // dO, dO-lo) copied straight into LDS, 3 per wave; lane l fills physical
     // chunk l%16 of row 4(G%8) + l/16.  The last, partial block goes through
     // registers (rows past the sequence: Q from the last row, dO = 0, so they
     // contribute nothing).
-    const int lcq = tid >> 3, leq = tid & 7; // partial path: 32 queries x 8 threads x 16 elements
+    const int lcq = tid >> 4, leq = tid & 15; // partial path: 32 queries x 16 threads x 8 elements
     float wreg = 0.f;
     uint32_t treg = 0, tmn = 0xFFFFFFFFu, tmx = 0u;
     int64_t treg64 = 0;
     auto gload_direct = [&](int q0, Stage &S) {
 #pragma unroll
-        for (int i = 0; i < 6; i++) {
-            const int G = 6 * w + i, plane = G >> 3, r0 = 4 * (G & 7);
+        for (int i = 0; i < 24 / NW; i++) {
+            const int G = (24 / NW) * w + i, plane = G >> 3, r0 = 4 * (G & 7);
             const int row = r0 + (l >> 4);
-            const int c = (l & 15) ^ (((row & 3) << 2) | ((row >> 2) & 3));
+            const int c = (l & 15) ^ swf(row);
             const int64_t grow = (int64_t)(o_b + q0 + row);
             const bf16 *src = plane == 0 ? Q + grow * a.ldq : (plane == 1 ? dO : dOlo) + grow * ld_do;
             bf16 *dst = (plane == 0 ? S.q : (plane == 1 ? S.dO : S.dOl)) + r0 * D;
@@ -296,16 +293,13 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
         const int qi = q0 + lcq;
         const bool ok = qi < L;
         const int64_t row = (int64_t)(o_b + (ok ? qi : L - 1));
-#pragma unroll
-        for (int c = 0; c < 2; c++) {
-            const int col = leq * 16 + c * 8;
-            const u32x4 qv = *(const u32x4 *)(Q + row * a.ldq + h * D + col);
-            const u32x4 dv = ok ? *(const u32x4 *)(dO + row * ld_do + h * D + col) : u32x4{0, 0, 0, 0};
-            const u32x4 lv = ok ? *(const u32x4 *)(dOlo + row * ld_do + h * D + col) : u32x4{0, 0, 0, 0};
-            *(u32x4 *)&S.q[swz(lcq, col)] = qv;
-            *(u32x4 *)&S.dO[swz(lcq, col)] = dv;
-            *(u32x4 *)&S.dOl[swz(lcq, col)] = lv;
-        }
+        const int col = leq * 8;
+        const u32x4 qv = *(const u32x4 *)(Q + row * a.ldq + h * D + col);
+        const u32x4 dv = ok ? *(const u32x4 *)(dO + row * ld_do + h * D + col) : u32x4{0, 0, 0, 0};
+        const u32x4 lv = ok ? *(const u32x4 *)(dOlo + row * ld_do + h * D + col) : u32x4{0, 0, 0, 0};
+        *(u32x4 *)&S.q[swz(lcq, col)] = qv;
+        *(u32x4 *)&S.dO[swz(lcq, col)] = dv;
+        *(u32x4 *)&S.dOl[swz(lcq, col)] = lv;
     };
     auto sstore_tables = [&](Stage &S) {
         if constexpr (HP)
@@ -325,43 +319,52 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
     const int p_hs = a.rp_hs > 0 ? (int)a.rp_hs : 2 * a.N + 1;
     const int t_hs = a.rt_hs > 0 ? (int)a.rt_hs : 128;
 
-    // dQ of the block at q0m from the dS tile `dst` (all 4 waves' keys):
-    // dQ[32 queries][d-block w] = sum over 128 keys of dS[q][key] K[key][d]
-    auto dq_mfma = [&](const bf16 *dst) {
-        floatx16 qacc;
+    // dQ of the block at q0m from the dS tile `dst` (all 8 waves' keys):
+    // wave w's slice dQ[16 queries of tile w%2][d-tiles dt_w, dt_w + 1]
+    // = sum over 128 keys of dS[q][key] K[key][d]
+    auto dq_block = [&](const bf16 *dst, int q0m, bool full) {
+        floatx4 qacc[2];
 #pragma unroll
-        for (int r = 0; r < 16; r++) qacc[r] = 0.f;
+        for (int i = 0; i < 2; i++)
 #pragma unroll
-        for (int t = 0; t < BN / 16; t++) {
-            const int kr1 = 16 * t + 8 * g + tsl;
-            const u32x2 s1 = lds_read_tr(&dst[kr1 * SS + cpart]);
-            const u32x2 s2 = lds_read_tr(&dst[(kr1 + 4) * SS + cpart]);
-            qacc = mfma32(as_bf16x8(u32x4{s1[0], s1[1], s2[0], s2[1]}), kq[t], qacc);
+            for (int r = 0; r < 4; r++) qacc[i][r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+            const int kb = 32 * s + 8 * g, col = 16 * qt_w + trc;
+            const u32x2 s1 = lds_read_tr(&dst[(kb + trr) * SS + col]);
+            const u32x2 s2 = lds_read_tr(&dst[(kb + 4 + trr) * SS + col]);
+            const bf16x8 av = as_bf16x8(u32x4{s1[0], s1[1], s2[0], s2[1]});
+#pragma unroll
+            for (int i = 0; i < 2; i++) {
+                const int kc = 16 * (dt_w + i) + trc;
+                const u32x2 k1 = lds_read_tr(&sm.kt[swz(kb + trr, kc)]);
+                const u32x2 k2 = lds_read_tr(&sm.kt[swz(kb + 4 + trr, kc)]);
+                qacc[i] = mfma16(av, as_bf16x8(u32x4{k1[0], k1[1], k2[0], k2[1]}), qacc[i]);
+            }
         }
-        return qacc;
-    };
-    // C layout: lane holds d = 32w + lq, queries 8(r/4) + 4g + r%4
-    auto dq_atomics = [&](const floatx16 &qacc, int q0m, bool full) {
-        float *dqp = a.dq_acc + (int64_t)(o_b + q0m + 4 * g) * ld_do + h * D + 32 * w + lq;
+        // C layout: lane holds d = 16(dt_w + i) + j, queries 16 qt_w + 4g + r
+        float *dqp = a.dq_acc + (int64_t)(o_b + q0m + 16 * qt_w + 4 * g) * ld_do + h * D + 16 * dt_w + j;
         if (full) {
 #pragma unroll
-            for (int r = 0; r < 16; r++) atomicAdd(dqp + (int64_t)(8 * (r >> 2) + (r & 3)) * ld_do, qacc[r]);
-        } else {
-            const int qlim = L - q0m - 4 * g;
+            for (int i = 0; i < 2; i++)
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int qq = 8 * (r >> 2) + (r & 3);
-                if (qq < qlim) atomicAdd(dqp + (int64_t)qq * ld_do, qacc[r]);
-            }
+                for (int r = 0; r < 4; r++) atomicAdd(dqp + (int64_t)r * ld_do + 16 * i, qacc[i][r]);
+        } else {
+            const int qlim = L - q0m - 16 * qt_w - 4 * g;
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int r = 0; r < 4; r++)
+                    if (r < qlim) atomicAdd(dqp + (int64_t)r * ld_do + 16 * i, qacc[i][r]);
         }
     };
     // drab_p of the block at q0m from its skewed tile (row c = diagonal c,
     // key - query = k0 - q0m + c - (BQ - 1); cells outside the tile's keys are
-    // never written and stay 0).  Every thread sums one row (threads past the
-    // last diagonal take the all-zero row DK - 1).  The ring entry is flushed
-    // once no later block can reach it (key - query > k0 + BN - 1 - (q0m + BQ)
+    // never written and stay 0).  One thread per row; threads past the last
+    // diagonal take the all-zero row DK - 1.  The ring entry is flushed once
+    // no later block can reach it (key - query > k0 + BN - 1 - (q0m + BQ)
     // <=>  c > BN - 2).
-    auto drabp_sum = [&](const float *dsk, int q0m, int &slot, float &tot, int &dl) {
+    auto drabp_sum = [&](const float *dsk, int q0m, float &tot, int &dl) {
         const int c = tid < DK - 1 ? tid : DK - 1;
         const floatx4 *rowp = (const floatx4 *)(dsk + c * DKP);
         floatx4 acc4 = rowp[0];
@@ -369,7 +372,7 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
         for (int i = 1; i < BQ / 4; i++) acc4 += rowp[i];
         const float sum = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
         dl = k0 - q0m + c - (BQ - 1);
-        slot = dl & (RING - 1);
+        const int slot = dl & (RING - 1);
         tot = sm.ring[slot] + sum;
         sm.ring[slot] = c > BN - 2 ? 0.f : tot;
     };
@@ -383,11 +386,9 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
 
     // ---- one query block.  MAIN: a block in the middle of the range (every
     // wave is past its diagonal block, this, the previous and the next block
-    // are full), compiled without the per-block checks so that the MFMA, LDS
-    // and VALU work of the phases can be interleaved.
+    // are full), compiled without the per-block checks.
     const int nqb = (L - k0 + BQ - 1) / BQ; // query blocks [k0, L); >= 1
-    const int kw0 = k0 + 32 * w;            // this wave's first key
-    const int krow = 32 * w + lq;
+    const int krow = KW * w + j;
     auto iteration = [&](auto main_c, int n) {
         constexpr bool MAIN = decltype(main_c)::value;
         const int q0 = k0 + n * BQ;
@@ -398,40 +399,34 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
         float *dskn = sm.dsk[n & 1];
         bf16 *dsn = sm.ds[n & 1];
         const bool skip = MAIN ? false : (kw0 > q0 + BQ - 1 || kw0 >= L);
-        // X = Q K^T + rab_p window, dP = dO' V^T (hi and lo planes)
-        floatx16 xacc, pacc;
+        // X = Q K^T + rab_p window, dP = dO' V^T (hi and lo planes), two 16-query tiles
+        floatx4 xacc[2], pacc[2];
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-            const int cr = 8 * (r >> 2) + (r & 3);
-            xacc[r] = HP ? S.win[krow + (BQ - 1) - 4 * g - cr] : 0.f;
-            pacc[r] = 0.f;
-        }
+        for (int hh = 0; hh < 2; hh++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                xacc[hh][r] = HP ? S.win[krow + (BQ - 1) - 4 * g - 16 * hh - r] : 0.f;
+                pacc[hh][r] = 0.f;
+            }
         if (!skip) {
 #pragma unroll
-            for (int s = 0; s < 8; s++) {
-                const int o = swz(lq, s * 16 + g * 8);
-                const bf16x8 qa = *(const bf16x8 *)&S.q[o];
-                const bf16x8 da = *(const bf16x8 *)&S.dO[o];
-                const bf16x8 dl = *(const bf16x8 *)&S.dOl[o];
-                xacc = mfma32(qa, kreg[s], xacc);
-                pacc = mfma32(da, vreg[s], pacc);
-                pacc = mfma32(dl, vreg[s], pacc);
-            }
-            if constexpr (MAIN) {
-                // keep LDS operand reads two steps ahead of the MFMAs
-                __builtin_amdgcn_sched_group_barrier(0x100, 14, 0);
+            for (int s = 0; s < 4; s++)
 #pragma unroll
-                for (int i = 0; i < 6; i++) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+                for (int hh = 0; hh < 2; hh++) {
+                    const int o = swz(16 * hh + j, 32 * s + 8 * g);
+                    const bf16x8 qa = *(const bf16x8 *)&S.q[o];
+                    const bf16x8 da = *(const bf16x8 *)&S.dO[o];
+                    const bf16x8 dl = *(const bf16x8 *)&S.dOl[o];
+                    const bf16x8 kb = *(const bf16x8 *)&sm.kt[swz(krow, 32 * s + 8 * g)];
+                    xacc[hh] = mfma16(qa, kb, xacc[hh]);
+                    pacc[hh] = mfma16(da, vreg[s], pacc[hh]);
+                    pacc[hh] = mfma16(dl, vreg[s], pacc[hh]);
                 }
-                __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
-            }
         }
         // the previous block's drab_p (its skewed tile is complete)
-        int slot = 0, dlf = 0;
+        int dlf = 0;
         float tot = 0.f;
-        if ((MAIN || n > 0) && a.drab_p) drabp_sum(sm.dsk[(n - 1) & 1], q0 - BQ, slot, tot, dlf);
+        if ((MAIN || n > 0) && a.drab_p) drabp_sum(sm.dsk[(n - 1) & 1], q0 - BQ, tot, dlf);
         if (MAIN) gload_tables(q0 + BQ);
         else if (n + 1 < nqb) gload_tables(q0 + BQ);
         if ((MAIN || n > 0) && a.drab_p) drabp_flush(dlf, tot);
@@ -439,18 +434,15 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
         // transposing LDS reads, before which the compiler waits for the
         // outstanding direct copies of the next block.
         auto prev_dq = [&]() {
-            if (MAIN || n > 0) {
-                const floatx16 qacc = dq_mfma(sm.ds[(n - 1) & 1]);
-                dq_atomics(qacc, q0 - BQ, MAIN ? true : q0 <= L);
-            }
+            if (MAIN || n > 0) dq_block(sm.ds[(n - 1) & 1], q0 - BQ, MAIN ? true : q0 <= L);
         };
 
         ln.dsk = dskn + (krow + (BQ - 1) - 4 * g) * DKP + 4 * g;
         if (!skip) {
             ln.qt = &S.qt[4 * g];
             ln.qt64 = &S.qt64[4 * g];
-            ln.dmask = kw0 + lq - q0 - 4 * g; // key > query  <=>  cr < dmask
-            const bool diag = MAIN ? false : kw0 + 31 > q0;
+            ln.dmask = kw0 + j - q0 - 4 * g; // key > query  <=>  cq < dmask
+            const bool diag = MAIN ? false : kw0 + KW - 1 > q0;
             bool uni = false;
             int ubk = 0;
             if constexpr (TM == 1) {
@@ -469,7 +461,7 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
             }
             const float ubias = sm.rabt[ubk];
             float tsum = 0.f;
-            uint32_t ppk[8], dpk[8];
+            uint32_t ppk[4], dpk[4];
             if (diag)
                 bwd_pointwise<TM, DT, true, false>(xacc, pacc, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, tsum);
             else if (TM == 1 && uni)
@@ -480,35 +472,32 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
                 tsum = wave_sum(tsum);
                 if (l == 0) sm.dtab[w][0][ubk] += tsum;
             }
-            // dS -> LDS as [key][query]: lane writes 4 queries (r%4) per r/4 group
+            // dS -> LDS as [key][query]: lane writes queries 16hh + 4g .. +3
 #pragma unroll
-            for (int gr = 0; gr < 4; gr++) {
-                const u32x2 v2 = {dpk[2 * gr], dpk[2 * gr + 1]};
-                *(u32x2 *)&dsn[krow * SS + 8 * gr + 4 * g] = v2;
+            for (int hh = 0; hh < 2; hh++) {
+                const u32x2 v2 = {dpk[2 * hh], dpk[2 * hh + 1]};
+                *(u32x2 *)&dsn[krow * SS + 16 * hh + 4 * g] = v2;
             }
             prev_dq();
-            // dV^T += dO'^T P and dK^T += Q^T dS  (contraction over the 32 queries)
+            // dV^T += dO'^T P and dK^T += Q^T dS  (contraction over the 32 queries,
+            // in the order 4g..4g+3, 16+4g..16+4g+3 of this lane's group)
+            const bf16x8 pb = as_bf16x8(u32x4{ppk[0], ppk[1], ppk[2], ppk[3]});
+            const bf16x8 sb = as_bf16x8(u32x4{dpk[0], dpk[1], dpk[2], dpk[3]});
 #pragma unroll
-            for (int m = 0; m < 2; m++) {
-                const bf16x8 pb = as_bf16x8(u32x4{ppk[4 * m], ppk[4 * m + 1], ppk[4 * m + 2], ppk[4 * m + 3]});
-                const bf16x8 sb = as_bf16x8(u32x4{dpk[4 * m], dpk[4 * m + 1], dpk[4 * m + 2], dpk[4 * m + 3]});
-                const int qr1 = 16 * m + 4 * g + tsl; // query row of the transposing read
-#pragma unroll
-                for (int db = 0; db < 4; db++) {
-                    const int o1 = swz(qr1, db * 32 + cpart), o2 = swz(qr1 + 8, db * 32 + cpart);
-                    const u32x2 d1 = lds_read_tr(&S.dO[o1]);
-                    const u32x2 d2 = lds_read_tr(&S.dO[o2]);
-                    dv_acc[db] = mfma32(as_bf16x8(u32x4{d1[0], d1[1], d2[0], d2[1]}), pb, dv_acc[db]);
-                    const u32x2 q1 = lds_read_tr(&S.q[o1]);
-                    const u32x2 q2 = lds_read_tr(&S.q[o2]);
-                    dk_acc[db] = mfma32(as_bf16x8(u32x4{q1[0], q1[1], q2[0], q2[1]}), sb, dk_acc[db]);
-                }
+            for (int t = 0; t < D / 16; t++) {
+                const int o1 = swz(4 * g + trr, 16 * t + trc), o2 = swz(16 + 4 * g + trr, 16 * t + trc);
+                const u32x2 d1 = lds_read_tr(&S.dO[o1]);
+                const u32x2 d2 = lds_read_tr(&S.dO[o2]);
+                dv_acc[t] = mfma16(as_bf16x8(u32x4{d1[0], d1[1], d2[0], d2[1]}), pb, dv_acc[t]);
+                const u32x2 q1 = lds_read_tr(&S.q[o1]);
+                const u32x2 q2 = lds_read_tr(&S.q[o2]);
+                dk_acc[t] = mfma16(as_bf16x8(u32x4{q1[0], q1[1], q2[0], q2[1]}), sb, dk_acc[t]);
             }
         } else {
 #pragma unroll
-            for (int gr = 0; gr < 4; gr++) *(u32x2 *)&dsn[krow * SS + 8 * gr + 4 * g] = u32x2{0u, 0u};
+            for (int hh = 0; hh < 2; hh++) *(u32x2 *)&dsn[krow * SS + 16 * hh + 4 * g] = u32x2{0u, 0u};
 #pragma unroll
-            for (int rr = 0; rr < 16; rr++) ln.dsk[-(DKP - 1) * (8 * (rr >> 2) + (rr & 3))] = 0.f;
+            for (int e = 0; e < 8; e++) ln.dsk[-(DKP - 1) * (16 * (e >> 2) + (e & 3))] = 0.f;
             prev_dq();
         }
         if (MAIN || n + 1 < nqb) {
@@ -541,12 +530,13 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
     // the last block's dQ and drab_p, then what is left in the ring and the time tables
     {
         const int qlast = k0 + (nqb - 1) * BQ;
-        const floatx16 qacc = dq_mfma(sm.ds[(nqb - 1) & 1]);
-        int slot = 0, dlf = 0;
+        dq_block(sm.ds[(nqb - 1) & 1], qlast, qlast + BQ <= L);
+        int dlf = 0;
         float tot = 0.f;
-        if (a.drab_p) drabp_sum(sm.dsk[(nqb - 1) & 1], qlast, slot, tot, dlf);
-        dq_atomics(qacc, qlast, qlast + BQ <= L);
-        if (a.drab_p) drabp_flush(dlf, tot);
+        if (a.drab_p) {
+            drabp_sum(sm.dsk[(nqb - 1) & 1], qlast, tot, dlf);
+            drabp_flush(dlf, tot);
+        }
         __syncthreads();
         if (a.drab_p) {
             // remaining key - query values: [k0 - qlast - (BQ - 1), k0 + BN - 1 - qlast - BQ]
@@ -563,26 +553,23 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
     if constexpr (DT && TM != 0) {
         if (tid < TB) {
             float s = 0.f;
-            for (int ww = 0; ww < 4; ww++)
+            for (int ww = 0; ww < NW; ww++)
                 for (int c = 0; c < TCOPY; c++) s += sm.dtab[ww][c][tid];
             if (s != 0.f) atomicAdd(&a.drab_t[h * t_hs + tid], s);
         }
     }
-    // dK^T, dV^T: lane holds key mykey, d = 32 db + 8(r/4) + 4g + r%4
+    // dK^T, dV^T: lane holds key mykey, d = 16t + 4g + r
     if (kvalid) {
         const int64_t row = o_b + mykey;
 #pragma unroll
-        for (int db = 0; db < 4; db++)
-#pragma unroll
-            for (int gr = 0; gr < 4; gr++) {
-                const int d0 = db * 32 + 8 * gr + 4 * g;
-                const u32x2 kk = {pack2_bf16(dk_acc[db][4 * gr], dk_acc[db][4 * gr + 1]),
-                                  pack2_bf16(dk_acc[db][4 * gr + 2], dk_acc[db][4 * gr + 3])};
-                const u32x2 vv = {pack2_bf16(NLN2 * dv_acc[db][4 * gr], NLN2 * dv_acc[db][4 * gr + 1]),
-                                  pack2_bf16(NLN2 * dv_acc[db][4 * gr + 2], NLN2 * dv_acc[db][4 * gr + 3])};
-                *(u32x2 *)(a.dk + row * a.lddk + h * D + d0) = kk;
-                *(u32x2 *)(a.dv + row * a.lddv + h * D + d0) = vv;
-            }
+        for (int t = 0; t < D / 16; t++) {
+            const int d0 = 16 * t + 4 * g;
+            const u32x2 kk = {pack2_bf16(dk_acc[t][0], dk_acc[t][1]), pack2_bf16(dk_acc[t][2], dk_acc[t][3])};
+            const u32x2 vv = {pack2_bf16(NLN2 * dv_acc[t][0], NLN2 * dv_acc[t][1]),
+                              pack2_bf16(NLN2 * dv_acc[t][2], NLN2 * dv_acc[t][3])};
+            *(u32x2 *)(a.dk + row * a.lddk + h * D + d0) = kk;
+            *(u32x2 *)(a.dv + row * a.lddv + h * D + d0) = vv;
+        }
     }
 }
 
@@ -592,7 +579,7 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
 // drab_t.  Sequences whose time span does not fit 32 bits take the exact
 // 64-bit body.
 template <bool HP, int TMODE>
-__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) attn_bwd_bf16_kernel(AttnBwdArgs a)
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_bwd_bf16_kernel(AttnBwdArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     Smem &sm = *reinterpret_cast<Smem *>(smem_raw);
