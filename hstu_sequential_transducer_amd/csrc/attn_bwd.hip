@@ -11,24 +11,27 @@
 // softmax statistics, so nothing else is needed).  dO' arrives as two bf16
 // planes (hi + lo) so dP keeps ~16 significant bits.
 //
-// A workgroup of 8 waves owns 128 keys of one (sequence, head); wave w owns
-// keys 16w..16w+15 with their K and V rows and their dK^T, dV^T accumulators
-// in registers (about 240 registers a wave, so two waves share a SIMD and one
-// wave's element-wise VALU work overlaps the other's MFMAs).  Query blocks of
-// 32 stream through LDS (double buffered, copied global -> LDS directly).  Per
-// block a wave computes X = Q K^T + rab_p (the rab_p window is loaded into the
-// accumulator) and dP on 16x16x32 bf16 MFMA as two 16-query tiles (lane =
-// key, registers = queries), the element-wise step, dV^T += dO'^T P and
-// dK^T += Q^T dS (transposing LDS reads for dO'^T and Q^T), and writes dS to
-// an LDS tile.  dQ needs every wave's dS, so it runs one block late: wave w
-// computes a 16-query x 32-d slice over all 128 keys and adds it to an fp32
+// A workgroup of 8 waves owns 128 keys of one (sequence, head).  Keys come in
+// 4 groups of 32; each group is shared by two waves, which run on the same
+// SIMD and split the work so that each needs only ~220 registers (two waves
+// per SIMD: one's element-wise VALU work overlaps the other's MFMAs):
+//   the V wave (waves 0-3) computes X = Q K^T + rab_p, P = SiLU(X) and
+//     dV^T += dO'^T P for its keys, and, one block late, dQ for d-block w of
+//     all 128 keys (plus the drab_p diagonal sums);
+//   the K wave (waves 4-7) computes X and dP = dO' V^T (hi and lo planes),
+//     dS and dK^T += Q^T dS, and writes dS (bf16 for dQ, fp32 skewed for
+//     drab_p) to LDS.
+// X is computed by both; everything else once.  All products are 32x32x16
+// bf16 MFMA with lane = key, registers = queries.  Query blocks of 32 stream
+// through LDS (double buffered, copied global -> LDS directly); the rab_p
+// window is loaded into the X accumulator.  dQ partial sums go to an fp32
 // accumulator with global atomics.  One barrier per query block.
 //
-// drab_p: each wave writes its fp32 dS into an LDS tile skewed by j - i
+// drab_p: the K wave writes its fp32 dS into an LDS tile skewed by j - i
 // ([key - query][query]); one block later, one thread per diagonal sums it
 // into an LDS ring indexed by j - i, and an entry is flushed with one global
 // atomic once no later block can reach it.  drab_t: when every pair of a
-// 16x32 block falls in one time bucket (decided per block in scalar code from
+// 32x32 block falls in one time bucket (decided per block in scalar code from
 // the min/max times of its queries and keys) the bias is a scalar and the
 // block's dS is summed by a wave reduction; otherwise per-element adds go to
 // per-wave LDS tables.  Bias presence, time mode, diagonal masking and uniform
@@ -44,21 +47,20 @@ constexpr int D = 128;
 constexpr int BN = BWD_BN; // 128 keys per workgroup
 constexpr int BQ = 32;     // queries per block
 constexpr int NW = 8;      // waves per workgroup
-constexpr int KW = 16;     // keys per wave
 constexpr int NT = 64 * NW;
 // Q, dO and dO-lo stage tiles (and the prologue's K tile) are [rows][128]
 // bf16 with no padding; the 16-byte chunks of row r are XOR-swizzled by
 // sw(r) = 4(r%4) + bitrev2((r/4)%4), which keeps the 16-byte operand reads
-// (16 consecutive rows, one chunk) and the transposing reads (rows 4g..4g+3
-// of each 16-lane group g, 32 bytes each) free of bank conflicts, and lets
-// full blocks be copied global -> LDS directly (4 rows per wave instruction).
+// (16 consecutive rows, one chunk) and the transposing reads (4 consecutive
+// rows, 64 bytes each) free of bank conflicts, and lets full blocks be copied
+// global -> LDS directly (4 rows per wave instruction).
 constexpr int SS = 40;     // dS tile [key][query] row stride (bf16)
 constexpr int WIN = 160;   // rab_p window per block (BQ + BN - 1 used)
 constexpr int RING = 256;  // drab_p ring (power of two >= WIN + BQ)
 constexpr int DK = 160;    // diagonals of the skewed dS tile: key - query + BQ - 1 (159 used, row 159 stays 0)
 constexpr int DKP = 36;    // row pitch (floats) of the skewed tile: 32 queries + pad, 16-byte rows
 constexpr int TB = 64;     // time buckets that int64 differences can reach
-constexpr int TCOPY = 4;   // copies of each wave's drab_t table
+constexpr int TCOPY = 4;   // copies of each K wave's drab_t table
 constexpr float NLOG2E = -1.4426950408889634f;
 constexpr float NLN2 = -0.69314718055994531f;
 
@@ -77,7 +79,7 @@ struct alignas(16) Smem {
     alignas(16) float dsk[2][DK * DKP]; // fp32 dS skewed: [key - query + BQ - 1][query]
     alignas(16) bf16 kt[BN * D];        // the workgroup's K rows, swizzled like the stage tiles
     float ring[RING];
-    float dtab[NW][TCOPY][TB];
+    float dtab[4][TCOPY][TB];
     float rabt_rev[32];
     float rabt[128];
 };
@@ -98,102 +100,120 @@ typedef __attribute__((address_space(3))) short4v lds_short4v;
 
 // Transposing LDS read (ds_read_b64_tr_b16).  Inside each group of 16 lanes,
 // lane i receives element i%4 of the 4-element chunks addressed by lanes
-// i/4, i/4+4, i/4+8, i/4+12 (in that order).  So if lane L of the group
-// addresses row r0 + L/4, column c0 + 4(L%4), lane i receives rows r0..r0+3
-// of column c0 + i.
+// i/4, i/4+4, i/4+8, i/4+12 (in that order).
 DEV u32x2 lds_read_tr(const bf16 *p)
 {
     short4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(p));
     return __builtin_bit_cast(u32x2, r);
 }
 
-// 16x16x32 bf16 MFMA.  Lane l supplies A[l%16][8*(l/16) .. +8] and
-// B[8*(l/16) .. +8][l%16]; C register r of lane l is C[4*(l/16) + r][l%16].
-DEV floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0); }
-
 struct BwdLane {
-    const uint32_t *qt;   // S.qt + 4g   (index with cq)
+    const uint32_t *qt;   // S.qt + 4g   (index with cr)
     const int64_t *qt64;  // S.qt64 + 4g
-    float *dsk;           // skewed-tile cell of (cq = 0) for this lane; cell of cq at -(DKP - 1) cq
-    float *dtab;          // this wave's drab_t table copy for this lane
+    float *dsk;           // skewed-tile cell of (cr = 0) for this lane; cell of cr at -(DKP - 1) cr
+    float *dtab;          // this K wave's drab_t table copy for this lane
     uint32_t tk;
     int64_t tk64;
-    int dmask;            // masked (key > query) iff cq < dmask  (diagonal blocks)
+    int dmask;            // masked (key > query) iff cr < dmask  (diagonal blocks)
 };
 
-// Element-wise step of one 16-key x 32-query block.  Element (hh, r) <->
-// query 4g + cq, cq = 16hh + r; this lane's key.  xacc holds x - rab_t (the
-// rab_p term is already in).  Writes packed bf16 P and dS (queries 4g..4g+3
-// then 16+4g..16+4g+3), the fp32 dS into the skewed tile, and the drab_t
-// contributions.
-template <int TM, bool DT, bool DIAG, bool UNI>
-DEV void bwd_pointwise(const floatx4 (&xacc)[2], const floatx4 (&pacc)[2], uint32_t (&ppk)[4], uint32_t (&dpk)[4],
-                       const BwdLane &ln, const float *rabt_rev, const float *rabt, float ubias, float &tsum)
+// x' = -log2(e) x for register r of the X accumulator (which holds x minus
+// the time bias; time tables are staged pre-scaled), and the time bucket.
+template <int TM, bool UNI>
+DEV float xprime(const floatx16 &xacc, int rr, const BwdLane &ln, const float *rabt_rev, const float *rabt,
+                 float ubias, int &bucket)
+{
+    const int cr = 8 * (rr >> 2) + (rr & 3);
+    float tb = 0.f;
+    bucket = 0;
+    if constexpr (TM == 1) {
+        if constexpr (UNI) {
+            tb = ubias;
+        } else {
+            const uint32_t tq = ln.qt[cr];
+            const uint32_t dd1 = (tq > ln.tk ? tq - ln.tk : ln.tk - tq) + 1u;
+            const int cz = __builtin_clz(dd1);
+            tb = rabt_rev[cz];
+            bucket = 31 - cz;
+        }
+    } else if constexpr (TM == 2) {
+        bucket = time_bucket64(ln.qt64[cr] - ln.tk64);
+        tb = rabt[bucket];
+    }
+    return __builtin_fmaf(xacc[rr], NLOG2E, tb);
+}
+
+// V wave: P' = x' sigmoid(x) = -log2(e) SiLU(x) (the -ln 2 goes into dV's
+// final scale), packed to bf16.  Register r <-> query 4g + cr(r),
+// cr = 8(r/4) + r%4; this lane's key.
+template <int TM, bool DIAG, bool UNI>
+DEV void pointwise_v(const floatx16 &xacc, uint32_t (&ppk)[8], const BwdLane &ln, const float *rabt_rev,
+                     const float *rabt, float ubias)
 {
 #pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-        float pp[2], dd[2];
+    for (int r = 0; r < 16; r += 2) {
+        float pp[2];
 #pragma unroll
         for (int u = 0; u < 2; u++) {
-            const int hh = (e + u) >> 2, r = (e + u) & 3;
-            const int cq = 16 * hh + r;
-            // x' = -log2(e) x (time tables staged pre-scaled), sg = sigmoid(x),
-            // p' = x' sg = -log2(e) SiLU(x) (the -ln 2 goes into dV's final scale),
-            // dS = dP sg (1 + x (1 - sg)) = dP (sg - ln2 (p' - p' sg)).
-            float tb = 0.f;
-            int bucket = 0;
-            if constexpr (TM == 1) {
-                if constexpr (UNI) {
-                    tb = ubias;
-                } else {
-                    const uint32_t tq = ln.qt[cq];
-                    const uint32_t dd1 = (tq > ln.tk ? tq - ln.tk : ln.tk - tq) + 1u;
-                    const int cz = __builtin_clz(dd1);
-                    tb = rabt_rev[cz];
-                    bucket = 31 - cz;
-                }
-            } else if constexpr (TM == 2) {
-                bucket = time_bucket64(ln.qt64[cq] - ln.tk64);
-                tb = rabt[bucket];
-            }
-            const float x = __builtin_fmaf(xacc[hh][r], NLOG2E, tb);
-            const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x));
-            float p = x * sg;
-            const float t = __builtin_fmaf(-p, sg, p);
-            float ds = pacc[hh][r] * __builtin_fmaf(t, NLN2, sg);
-            if constexpr (DIAG) {
-                if (cq < ln.dmask) {
-                    p = 0.f;
-                    ds = 0.f;
-                }
-            }
+            const int rr = r + u, cr = 8 * (rr >> 2) + (rr & 3);
+            int bucket;
+            const float x = xprime<TM, UNI>(xacc, rr, ln, rabt_rev, rabt, ubias, bucket);
+            float p = x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x));
+            if constexpr (DIAG) p = cr < ln.dmask ? 0.f : p;
             pp[u] = p;
+        }
+        ppk[r >> 1] = pack2_bf16(pp[0], pp[1]);
+    }
+}
+
+// K wave: dS = dP sg (1 + x (1 - sg)) = dP (sg - ln2 (p' - p' sg)), packed to
+// bf16, written fp32 into the skewed tile, and added to drab_t.
+template <int TM, bool DT, bool DIAG, bool UNI>
+DEV void pointwise_k(const floatx16 &xacc, const floatx16 &pacc, uint32_t (&dpk)[8], const BwdLane &ln,
+                     const float *rabt_rev, const float *rabt, float ubias, float &tsum)
+{
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+        float dd[2];
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+            const int rr = r + u, cr = 8 * (rr >> 2) + (rr & 3);
+            int bucket;
+            const float x = xprime<TM, UNI>(xacc, rr, ln, rabt_rev, rabt, ubias, bucket);
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x));
+            const float p = x * sg;
+            const float t = __builtin_fmaf(-p, sg, p);
+            float ds = pacc[rr] * __builtin_fmaf(t, NLN2, sg);
+            if constexpr (DIAG) ds = cr < ln.dmask ? 0.f : ds;
             dd[u] = ds;
-            ln.dsk[-(DKP - 1) * cq] = ds;
+            ln.dsk[-(DKP - 1) * cr] = ds;
             if constexpr (DT && TM != 0) {
                 if constexpr (UNI) tsum += ds;
                 else atomicAdd(&ln.dtab[bucket], ds);
             }
         }
-        ppk[e >> 1] = pack2_bf16(pp[0], pp[1]);
-        dpk[e >> 1] = pack2_bf16(dd[0], dd[1]);
+        dpk[r >> 1] = pack2_bf16(dd[0], dd[1]);
     }
 }
 
 template <bool HP, int TM, bool DT>
 DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
 {
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, j = l & 15;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, lq = l & 31;
+    const int p = w & 3;          // key group: keys 32p..32p+31 of the tile
+    const bool vwave = w < 4;     // V wave (else K wave); wave-uniform
     const bf16 *Q = a.q, *K = a.k, *V = a.v, *dO = a.dO;
     const int64_t ld_do = (int64_t)a.H * D;
     const bf16 *dOlo = dO + (int64_t)a.T * ld_do;
-    // transposing-read lane constants: row offset j/4, column offset 4(j%4)
-    const int trr = j >> 2, trc = 4 * (j & 3);
+    // transposing-read lane constants
+    const int tj = l & 15, tsl = tj >> 2;
+    const int cpart = ((l >> 4) & 1) * 16 + 4 * (tj & 3);
 
     // ---- prologue: the workgroup's K rows into LDS (rows past the sequence
     // repeat the last row: finite, and every pair they form is masked or has
-    // dS = 0); it supplies the B operands of X = Q K^T (own rows) and of
-    // dQ = dS K (all rows).  Own V rows into registers.
+    // dS = 0); they supply the B operand of X = Q K^T, and a V wave keeps
+    // d-block p of all 128 rows in registers (B operand of dQ = dS K).  A K
+    // wave's own V rows straight from memory.
 #pragma unroll
     for (int i = 0; i < BN / (4 * NW); i++) {
         const int r0 = 4 * ((BN / (4 * NW)) * w + i), row = r0 + (l >> 4);
@@ -202,31 +222,39 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
         __builtin_amdgcn_global_load_lds((const void *)(K + (int64_t)(o_b + key) * a.ldk + h * D + c * 8),
                                          (lds_void *)(sm.kt + r0 * D), 16, 0, 0);
     }
-    const int kw0 = k0 + KW * w; // this wave's first key
-    const int mykey = kw0 + j;
+    const int kw0 = k0 + 32 * p; // this key group's first key
+    const int mykey = kw0 + lq;
     const bool kvalid = mykey < L;
-    bf16x8 vreg[4];
-    {
+    // opnd: V wave -> K d-block p of all rows (dQ operand); K wave -> own V rows
+    bf16x8 opnd[8];
+    if (!vwave) {
         const bf16 *vp = V + (int64_t)(o_b + (kvalid ? mykey : 0)) * a.ldv + h * D + g * 8;
 #pragma unroll
-        for (int s = 0; s < 4; s++) vreg[s] = as_bf16x8(kvalid ? *(const u32x4 *)(vp + s * 32) : u32x4{0, 0, 0, 0});
+        for (int s = 0; s < 8; s++) opnd[s] = as_bf16x8(kvalid ? *(const u32x4 *)(vp + s * 16) : u32x4{0, 0, 0, 0});
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    const int qt_w = w & 1;           // this wave's query tile of dQ
-    const int dt_w = 2 * (w >> 1);    // its first d-tile of dQ
+    if (vwave) {
+#pragma unroll
+        for (int t = 0; t < BN / 16; t++) {
+            const int kr1 = 16 * t + 8 * g + tsl;
+            const u32x2 k1 = lds_read_tr(&sm.kt[swz(kr1, 32 * p + cpart)]);
+            const u32x2 k2 = lds_read_tr(&sm.kt[swz(kr1 + 4, 32 * p + cpart)]);
+            opnd[t] = as_bf16x8(u32x4{k1[0], k1[1], k2[0], k2[1]});
+        }
+    }
     for (int i = tid; i < RING; i += NT) sm.ring[i] = 0.f;
     for (int i = tid; i < 2 * DK * DKP; i += NT) (&sm.dsk[0][0])[i] = 0.f;
-    for (int i = tid; i < NW * TCOPY * TB; i += NT) (&sm.dtab[0][0][0])[i] = 0.f;
+    for (int i = tid; i < 4 * TCOPY * TB; i += NT) (&sm.dtab[0][0][0])[i] = 0.f;
 
     BwdLane ln;
     ln.tk = (TM == 1 && kvalid) ? a.rel[o_b + mykey] : 0u;
     ln.tk64 = (TM == 2 && kvalid) ? a.ts[o_b + mykey] : 0;
-    ln.dtab = &sm.dtab[w][j & (TCOPY - 1)][0];
-    // time range of this wave's valid keys (for the uniform-bucket test), as scalars
+    ln.dtab = &sm.dtab[p][lq & (TCOPY - 1)][0];
+    // time range of this group's valid keys (for the uniform-bucket test), as scalars
     uint32_t tkmin = kvalid ? ln.tk : 0xFFFFFFFFu, tkmax = kvalid ? ln.tk : 0u;
     if constexpr (TM == 1) {
-        for (int o = 8; o >= 1; o >>= 1) {
+        for (int o = 16; o >= 1; o >>= 1) {
             tkmin = min(tkmin, (uint32_t)__shfl_xor((int)tkmin, o, 64));
             tkmax = max(tkmax, (uint32_t)__shfl_xor((int)tkmax, o, 64));
         }
@@ -234,14 +262,12 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
         tkmax = __builtin_amdgcn_readfirstlane(tkmax);
     }
 
-    floatx4 dv_acc[8], dk_acc[8];
+    // acc: V wave -> dV^T, K wave -> dK^T (lane = key, d = 32 db + 8(r/4) + 4g + r%4)
+    floatx16 acc[4];
 #pragma unroll
-    for (int i = 0; i < 8; i++)
+    for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int r = 0; r < 4; r++) {
-            dv_acc[i][r] = 0.f;
-            dk_acc[i][r] = 0.f;
-        }
+        for (int r = 0; r < 16; r++) acc[i][r] = 0.f;
 
     // ---- query-block stage loader.  Full blocks: 24 groups of 4 rows (Q,
     // dO, dO-lo) copied straight into LDS, 3 per wave; lane l fills physical
@@ -319,51 +345,39 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
     const int p_hs = a.rp_hs > 0 ? (int)a.rp_hs : 2 * a.N + 1;
     const int t_hs = a.rt_hs > 0 ? (int)a.rt_hs : 128;
 
-    // dQ of the block at q0m from the dS tile `dst` (all 8 waves' keys):
-    // wave w's slice dQ[16 queries of tile w%2][d-tiles dt_w, dt_w + 1]
-    // = sum over 128 keys of dS[q][key] K[key][d]
+    // V wave: dQ of the block at q0m from the dS tile `dst` (all 128 keys):
+    // dQ[32 queries][d-block p] = sum over the keys of dS[q][key] K[key][d]
     auto dq_block = [&](const bf16 *dst, int q0m, bool full) {
-        floatx4 qacc[2];
+        floatx16 qacc;
 #pragma unroll
-        for (int i = 0; i < 2; i++)
+        for (int r = 0; r < 16; r++) qacc[r] = 0.f;
 #pragma unroll
-            for (int r = 0; r < 4; r++) qacc[i][r] = 0.f;
-#pragma unroll
-        for (int s = 0; s < 4; s++) {
-            const int kb = 32 * s + 8 * g, col = 16 * qt_w + trc;
-            const u32x2 s1 = lds_read_tr(&dst[(kb + trr) * SS + col]);
-            const u32x2 s2 = lds_read_tr(&dst[(kb + 4 + trr) * SS + col]);
-            const bf16x8 av = as_bf16x8(u32x4{s1[0], s1[1], s2[0], s2[1]});
-#pragma unroll
-            for (int i = 0; i < 2; i++) {
-                const int kc = 16 * (dt_w + i) + trc;
-                const u32x2 k1 = lds_read_tr(&sm.kt[swz(kb + trr, kc)]);
-                const u32x2 k2 = lds_read_tr(&sm.kt[swz(kb + 4 + trr, kc)]);
-                qacc[i] = mfma16(av, as_bf16x8(u32x4{k1[0], k1[1], k2[0], k2[1]}), qacc[i]);
-            }
+        for (int t = 0; t < BN / 16; t++) {
+            const int kr1 = 16 * t + 8 * g + tsl;
+            const u32x2 s1 = lds_read_tr(&dst[kr1 * SS + cpart]);
+            const u32x2 s2 = lds_read_tr(&dst[(kr1 + 4) * SS + cpart]);
+            qacc = mfma32(as_bf16x8(u32x4{s1[0], s1[1], s2[0], s2[1]}), opnd[t], qacc);
         }
-        // C layout: lane holds d = 16(dt_w + i) + j, queries 16 qt_w + 4g + r
-        float *dqp = a.dq_acc + (int64_t)(o_b + q0m + 16 * qt_w + 4 * g) * ld_do + h * D + 16 * dt_w + j;
+        // C layout: lane holds d = 32p + lq, queries 8(r/4) + 4g + r%4
+        float *dqp = a.dq_acc + (int64_t)(o_b + q0m + 4 * g) * ld_do + h * D + 32 * p + lq;
         if (full) {
 #pragma unroll
-            for (int i = 0; i < 2; i++)
-#pragma unroll
-                for (int r = 0; r < 4; r++) atomicAdd(dqp + (int64_t)r * ld_do + 16 * i, qacc[i][r]);
+            for (int r = 0; r < 16; r++) atomicAdd(dqp + (int64_t)(8 * (r >> 2) + (r & 3)) * ld_do, qacc[r]);
         } else {
-            const int qlim = L - q0m - 16 * qt_w - 4 * g;
+            const int qlim = L - q0m - 4 * g;
 #pragma unroll
-            for (int i = 0; i < 2; i++)
-#pragma unroll
-                for (int r = 0; r < 4; r++)
-                    if (r < qlim) atomicAdd(dqp + (int64_t)r * ld_do + 16 * i, qacc[i][r]);
+            for (int r = 0; r < 16; r++) {
+                const int qq = 8 * (r >> 2) + (r & 3);
+                if (qq < qlim) atomicAdd(dqp + (int64_t)qq * ld_do, qacc[r]);
+            }
         }
     };
-    // drab_p of the block at q0m from its skewed tile (row c = diagonal c,
-    // key - query = k0 - q0m + c - (BQ - 1); cells outside the tile's keys are
-    // never written and stay 0).  One thread per row; threads past the last
-    // diagonal take the all-zero row DK - 1.  The ring entry is flushed once
-    // no later block can reach it (key - query > k0 + BN - 1 - (q0m + BQ)
-    // <=>  c > BN - 2).
+    // V waves: drab_p of the block at q0m from its skewed tile (row c =
+    // diagonal c, key - query = k0 - q0m + c - (BQ - 1); cells outside the
+    // tile's keys are never written and stay 0).  One thread per row; threads
+    // past the last diagonal take the all-zero row DK - 1.  The ring entry is
+    // flushed once no later block can reach it (key - query > k0 + BN - 1 -
+    // (q0m + BQ)  <=>  c > BN - 2).
     auto drabp_sum = [&](const float *dsk, int q0m, float &tot, int &dl) {
         const int c = tid < DK - 1 ? tid : DK - 1;
         const floatx4 *rowp = (const floatx4 *)(dsk + c * DKP);
@@ -388,7 +402,7 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
     // wave is past its diagonal block, this, the previous and the next block
     // are full), compiled without the per-block checks.
     const int nqb = (L - k0 + BQ - 1) / BQ; // query blocks [k0, L); >= 1
-    const int krow = KW * w + j;
+    const int krow = 32 * p + lq;
     auto iteration = [&](auto main_c, int n) {
         constexpr bool MAIN = decltype(main_c)::value;
         const int q0 = k0 + n * BQ;
@@ -396,53 +410,46 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
         if (MAIN) gload_direct(q0 + BQ, sm.st[(n + 1) & 1]);
         else if (n + 1 < nqb && nfull) gload_direct(q0 + BQ, sm.st[(n + 1) & 1]);
         const Stage &S = sm.st[n & 1];
-        float *dskn = sm.dsk[n & 1];
-        bf16 *dsn = sm.ds[n & 1];
         const bool skip = MAIN ? false : (kw0 > q0 + BQ - 1 || kw0 >= L);
-        // X = Q K^T + rab_p window, dP = dO' V^T (hi and lo planes), two 16-query tiles
-        floatx4 xacc[2], pacc[2];
+        const bool diag = MAIN ? false : kw0 + 31 > q0;
+        // X = Q K^T + rab_p window (both waves); dP = dO' V^T (K wave)
+        floatx16 xacc, pacc;
 #pragma unroll
-        for (int hh = 0; hh < 2; hh++)
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                xacc[hh][r] = HP ? S.win[krow + (BQ - 1) - 4 * g - 16 * hh - r] : 0.f;
-                pacc[hh][r] = 0.f;
-            }
-        if (!skip) {
-#pragma unroll
-            for (int s = 0; s < 4; s++)
-#pragma unroll
-                for (int hh = 0; hh < 2; hh++) {
-                    const int o = swz(16 * hh + j, 32 * s + 8 * g);
-                    const bf16x8 qa = *(const bf16x8 *)&S.q[o];
-                    const bf16x8 da = *(const bf16x8 *)&S.dO[o];
-                    const bf16x8 dl = *(const bf16x8 *)&S.dOl[o];
-                    const bf16x8 kb = *(const bf16x8 *)&sm.kt[swz(krow, 32 * s + 8 * g)];
-                    xacc[hh] = mfma16(qa, kb, xacc[hh]);
-                    pacc[hh] = mfma16(da, vreg[s], pacc[hh]);
-                    pacc[hh] = mfma16(dl, vreg[s], pacc[hh]);
-                }
+        for (int r = 0; r < 16; r++) {
+            const int cr = 8 * (r >> 2) + (r & 3);
+            xacc[r] = HP ? S.win[krow + (BQ - 1) - 4 * g - cr] : 0.f;
+            pacc[r] = 0.f;
         }
-        // the previous block's drab_p (its skewed tile is complete)
+        if (!skip) {
+            if (vwave) {
+#pragma unroll
+                for (int s = 0; s < 8; s++)
+                    xacc = mfma32(*(const bf16x8 *)&S.q[swz(lq, s * 16 + g * 8)],
+                                  *(const bf16x8 *)&sm.kt[swz(krow, s * 16 + g * 8)], xacc);
+            } else {
+#pragma unroll
+                for (int s = 0; s < 8; s++) {
+                    const int o = swz(lq, s * 16 + g * 8);
+                    xacc = mfma32(*(const bf16x8 *)&S.q[o], *(const bf16x8 *)&sm.kt[swz(krow, s * 16 + g * 8)], xacc);
+                    pacc = mfma32(*(const bf16x8 *)&S.dO[o], opnd[s], pacc);
+                    pacc = mfma32(*(const bf16x8 *)&S.dOl[o], opnd[s], pacc);
+                }
+            }
+        }
+        // V waves: the previous block's drab_p (its skewed tile is complete)
         int dlf = 0;
         float tot = 0.f;
-        if ((MAIN || n > 0) && a.drab_p) drabp_sum(sm.dsk[(n - 1) & 1], q0 - BQ, tot, dlf);
+        if (vwave && (MAIN || n > 0) && a.drab_p) drabp_sum(sm.dsk[(n - 1) & 1], q0 - BQ, tot, dlf);
         if (MAIN) gload_tables(q0 + BQ);
         else if (n + 1 < nqb) gload_tables(q0 + BQ);
-        if ((MAIN || n > 0) && a.drab_p) drabp_flush(dlf, tot);
-        // The previous block's dQ and this block's dV/dK come last: they use
-        // transposing LDS reads, before which the compiler waits for the
-        // outstanding direct copies of the next block.
-        auto prev_dq = [&]() {
-            if (MAIN || n > 0) dq_block(sm.ds[(n - 1) & 1], q0 - BQ, MAIN ? true : q0 <= L);
-        };
+        if (vwave && (MAIN || n > 0) && a.drab_p) drabp_flush(dlf, tot);
 
-        ln.dsk = dskn + (krow + (BQ - 1) - 4 * g) * DKP + 4 * g;
+        ln.dsk = sm.dsk[n & 1] + (krow + (BQ - 1) - 4 * g) * DKP + 4 * g;
+        bf16 *dsn = sm.ds[n & 1];
         if (!skip) {
             ln.qt = &S.qt[4 * g];
             ln.qt64 = &S.qt64[4 * g];
-            ln.dmask = kw0 + j - q0 - 4 * g; // key > query  <=>  cq < dmask
-            const bool diag = MAIN ? false : kw0 + KW - 1 > q0;
+            ln.dmask = kw0 + lq - q0 - 4 * g; // key > query  <=>  cr < dmask
             bool uni = false;
             int ubk = 0;
             if constexpr (TM == 1) {
@@ -460,45 +467,65 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
                 }
             }
             const float ubias = sm.rabt[ubk];
-            float tsum = 0.f;
-            uint32_t ppk[4], dpk[4];
-            if (diag)
-                bwd_pointwise<TM, DT, true, false>(xacc, pacc, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, tsum);
-            else if (TM == 1 && uni)
-                bwd_pointwise<TM, DT, false, true>(xacc, pacc, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, tsum);
-            else
-                bwd_pointwise<TM, DT, false, false>(xacc, pacc, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, tsum);
-            if (DT && TM == 1 && uni && !diag) {
-                tsum = wave_sum(tsum);
-                if (l == 0) sm.dtab[w][0][ubk] += tsum;
-            }
-            // dS -> LDS as [key][query]: lane writes queries 16hh + 4g .. +3
+            const int tsl2 = tsl;
+            if (vwave) {
+                uint32_t ppk[8];
+                if (diag) pointwise_v<TM, true, false>(xacc, ppk, ln, sm.rabt_rev, sm.rabt, ubias);
+                else if (TM == 1 && uni) pointwise_v<TM, false, true>(xacc, ppk, ln, sm.rabt_rev, sm.rabt, ubias);
+                else pointwise_v<TM, false, false>(xacc, ppk, ln, sm.rabt_rev, sm.rabt, ubias);
+                // the previous block's dQ (every K wave's dS of it is in its tile)
+                if (MAIN || n > 0) dq_block(sm.ds[(n - 1) & 1], q0 - BQ, MAIN ? true : q0 <= L);
+                // dV^T += dO'^T P  (contraction over the 32 queries)
 #pragma unroll
-            for (int hh = 0; hh < 2; hh++) {
-                const u32x2 v2 = {dpk[2 * hh], dpk[2 * hh + 1]};
-                *(u32x2 *)&dsn[krow * SS + 16 * hh + 4 * g] = v2;
-            }
-            prev_dq();
-            // dV^T += dO'^T P and dK^T += Q^T dS  (contraction over the 32 queries,
-            // in the order 4g..4g+3, 16+4g..16+4g+3 of this lane's group)
-            const bf16x8 pb = as_bf16x8(u32x4{ppk[0], ppk[1], ppk[2], ppk[3]});
-            const bf16x8 sb = as_bf16x8(u32x4{dpk[0], dpk[1], dpk[2], dpk[3]});
+                for (int m = 0; m < 2; m++) {
+                    const bf16x8 pb = as_bf16x8(u32x4{ppk[4 * m], ppk[4 * m + 1], ppk[4 * m + 2], ppk[4 * m + 3]});
+                    const int qr1 = 16 * m + 4 * g + tsl2; // query row of the transposing read
 #pragma unroll
-            for (int t = 0; t < D / 16; t++) {
-                const int o1 = swz(4 * g + trr, 16 * t + trc), o2 = swz(16 + 4 * g + trr, 16 * t + trc);
-                const u32x2 d1 = lds_read_tr(&S.dO[o1]);
-                const u32x2 d2 = lds_read_tr(&S.dO[o2]);
-                dv_acc[t] = mfma16(as_bf16x8(u32x4{d1[0], d1[1], d2[0], d2[1]}), pb, dv_acc[t]);
-                const u32x2 q1 = lds_read_tr(&S.q[o1]);
-                const u32x2 q2 = lds_read_tr(&S.q[o2]);
-                dk_acc[t] = mfma16(as_bf16x8(u32x4{q1[0], q1[1], q2[0], q2[1]}), sb, dk_acc[t]);
+                    for (int db = 0; db < 4; db++) {
+                        const u32x2 d1 = lds_read_tr(&S.dO[swz(qr1, db * 32 + cpart)]);
+                        const u32x2 d2 = lds_read_tr(&S.dO[swz(qr1 + 8, db * 32 + cpart)]);
+                        acc[db] = mfma32(as_bf16x8(u32x4{d1[0], d1[1], d2[0], d2[1]}), pb, acc[db]);
+                    }
+                }
+            } else {
+                float tsum = 0.f;
+                uint32_t dpk[8];
+                if (diag) pointwise_k<TM, DT, true, false>(xacc, pacc, dpk, ln, sm.rabt_rev, sm.rabt, ubias, tsum);
+                else if (TM == 1 && uni)
+                    pointwise_k<TM, DT, false, true>(xacc, pacc, dpk, ln, sm.rabt_rev, sm.rabt, ubias, tsum);
+                else pointwise_k<TM, DT, false, false>(xacc, pacc, dpk, ln, sm.rabt_rev, sm.rabt, ubias, tsum);
+                if (DT && TM == 1 && uni && !diag) {
+                    tsum = wave_sum(tsum);
+                    if (l == 0) sm.dtab[p][0][ubk] += tsum;
+                }
+                // dS -> LDS as [key][query]: lane writes 4 queries (r%4) per r/4 group
+#pragma unroll
+                for (int gr = 0; gr < 4; gr++) {
+                    const u32x2 v2 = {dpk[2 * gr], dpk[2 * gr + 1]};
+                    *(u32x2 *)&dsn[krow * SS + 8 * gr + 4 * g] = v2;
+                }
+                // dK^T += Q^T dS  (contraction over the 32 queries)
+#pragma unroll
+                for (int m = 0; m < 2; m++) {
+                    const bf16x8 sb = as_bf16x8(u32x4{dpk[4 * m], dpk[4 * m + 1], dpk[4 * m + 2], dpk[4 * m + 3]});
+                    const int qr1 = 16 * m + 4 * g + tsl2;
+#pragma unroll
+                    for (int db = 0; db < 4; db++) {
+                        const u32x2 q1 = lds_read_tr(&S.q[swz(qr1, db * 32 + cpart)]);
+                        const u32x2 q2 = lds_read_tr(&S.q[swz(qr1 + 8, db * 32 + cpart)]);
+                        acc[db] = mfma32(as_bf16x8(u32x4{q1[0], q1[1], q2[0], q2[1]}), sb, acc[db]);
+                    }
+                }
             }
         } else {
+            if (vwave) {
+                if (MAIN || n > 0) dq_block(sm.ds[(n - 1) & 1], q0 - BQ, MAIN ? true : q0 <= L);
+            } else {
 #pragma unroll
-            for (int hh = 0; hh < 2; hh++) *(u32x2 *)&dsn[krow * SS + 16 * hh + 4 * g] = u32x2{0u, 0u};
+                for (int gr = 0; gr < 4; gr++) *(u32x2 *)&dsn[krow * SS + 8 * gr + 4 * g] = u32x2{0u, 0u};
 #pragma unroll
-            for (int e = 0; e < 8; e++) ln.dsk[-(DKP - 1) * (16 * (e >> 2) + (e & 3))] = 0.f;
-            prev_dq();
+                for (int rr = 0; rr < 16; rr++) ln.dsk[-(DKP - 1) * (8 * (rr >> 2) + (rr & 3))] = 0.f;
+            }
         }
         if (MAIN || n + 1 < nqb) {
             if (!MAIN && !nfull) load_partial(q0 + BQ, sm.st[(n + 1) & 1]);
@@ -530,12 +557,14 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
     // the last block's dQ and drab_p, then what is left in the ring and the time tables
     {
         const int qlast = k0 + (nqb - 1) * BQ;
-        dq_block(sm.ds[(nqb - 1) & 1], qlast, qlast + BQ <= L);
-        int dlf = 0;
-        float tot = 0.f;
-        if (a.drab_p) {
-            drabp_sum(sm.dsk[(nqb - 1) & 1], qlast, tot, dlf);
-            drabp_flush(dlf, tot);
+        if (vwave) {
+            dq_block(sm.ds[(nqb - 1) & 1], qlast, qlast + BQ <= L);
+            if (a.drab_p) {
+                int dlf = 0;
+                float tot = 0.f;
+                drabp_sum(sm.dsk[(nqb - 1) & 1], qlast, tot, dlf);
+                drabp_flush(dlf, tot);
+            }
         }
         __syncthreads();
         if (a.drab_p) {
@@ -553,23 +582,25 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
     if constexpr (DT && TM != 0) {
         if (tid < TB) {
             float s = 0.f;
-            for (int ww = 0; ww < NW; ww++)
-                for (int c = 0; c < TCOPY; c++) s += sm.dtab[ww][c][tid];
+            for (int pp = 0; pp < 4; pp++)
+                for (int c = 0; c < TCOPY; c++) s += sm.dtab[pp][c][tid];
             if (s != 0.f) atomicAdd(&a.drab_t[h * t_hs + tid], s);
         }
     }
-    // dK^T, dV^T: lane holds key mykey, d = 16t + 4g + r
+    // dK^T (K wave) or dV^T (V wave): lane holds key mykey, d = 32 db + 8(r/4) + 4g + r%4
     if (kvalid) {
         const int64_t row = o_b + mykey;
+        bf16 *outp = vwave ? a.dv + row * a.lddv : a.dk + row * a.lddk;
+        const float sc = vwave ? NLN2 : 1.0f;
 #pragma unroll
-        for (int t = 0; t < D / 16; t++) {
-            const int d0 = 16 * t + 4 * g;
-            const u32x2 kk = {pack2_bf16(dk_acc[t][0], dk_acc[t][1]), pack2_bf16(dk_acc[t][2], dk_acc[t][3])};
-            const u32x2 vv = {pack2_bf16(NLN2 * dv_acc[t][0], NLN2 * dv_acc[t][1]),
-                              pack2_bf16(NLN2 * dv_acc[t][2], NLN2 * dv_acc[t][3])};
-            *(u32x2 *)(a.dk + row * a.lddk + h * D + d0) = kk;
-            *(u32x2 *)(a.dv + row * a.lddv + h * D + d0) = vv;
-        }
+        for (int db = 0; db < 4; db++)
+#pragma unroll
+            for (int gr = 0; gr < 4; gr++) {
+                const int d0 = db * 32 + 8 * gr + 4 * g;
+                const u32x2 vv = {pack2_bf16(sc * acc[db][4 * gr], sc * acc[db][4 * gr + 1]),
+                                  pack2_bf16(sc * acc[db][4 * gr + 2], sc * acc[db][4 * gr + 3])};
+                *(u32x2 *)(outp + h * D + d0) = vv;
+            }
     }
 }
 
