@@ -76,7 +76,7 @@ AttnWs attn_ws(const hstu_jagged *j, const hstu_dims *dm, int tile)
     const int B = j->batch, T = j->total, H = dm->heads;
     w.header = c.take(256);
     w.items = c.take((size_t)max_items_for(B, T, tile, H) * sizeof(int2));
-    w.rel = c.take((size_t)T * 4);
+    w.rel = c.take((size_t)T * 4 * 3); // rel, then rmin and rmax per 32-token block
     w.wide = c.take((size_t)B * 4);
     w.obuf = c.take((size_t)T * H * dm->d_v * 4);
     w.dq = c.take((size_t)T * H * dm->d_qk * 4);
@@ -199,6 +199,8 @@ hstu_status attn_fwd_launch(const hstu_jagged *j, const hstu_dims *dm, const hst
     a.ts = (bias && bias->rab_t) ? j->ts : nullptr;
     a.rel = rel;
     a.wide = wide;
+    a.rmin = rel + T;
+    a.rmax = rel + 2 * (size_t)T;
     a.rab_p = bias ? bias->rab_p : nullptr;
     a.rp_hs = bias ? bias->rab_p_hstride : 0;
     a.rab_t = (bias && j->ts) ? bias->rab_t : nullptr;
@@ -470,6 +472,8 @@ hstu_status hstu_attn_bwd(const hstu_jagged *j, const hstu_dims *dm, const hstu_
     a.ts = has_t ? j->ts : nullptr;
     a.rel = rel;
     a.wide = wide;
+    a.rmin = rel + T;
+    a.rmax = rel + 2 * (size_t)T;
     a.rab_p = has_p ? bias->rab_p : nullptr;
     a.rp_hs = p_hs;
     a.rab_t = has_t ? bias->rab_t : nullptr;

@@ -299,18 +299,14 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
             }
         }
         if constexpr (TM != 0) {
-            if (tid < 64) { // wave 0: query times and their range
+            if (tid < 64) { // wave 0: query times and (precomputed) their range
                 const int q = q0 + tid;
                 const bool okq = tid < BQ && q < L;
                 treg = (TM == 1 && okq) ? a.rel[o_b + q] : 0u;
                 treg64 = (TM == 2 && okq) ? a.ts[o_b + q] : 0;
-                tmn = okq ? treg : 0xFFFFFFFFu;
-                tmx = okq ? treg : 0u;
                 if constexpr (TM == 1) {
-                    for (int o = 32; o >= 1; o >>= 1) {
-                        tmn = min(tmn, (uint32_t)__shfl_xor((int)tmn, o, 64));
-                        tmx = max(tmx, (uint32_t)__shfl_xor((int)tmx, o, 64));
-                    }
+                    tmn = a.rmin[o_b + q0];
+                    tmx = a.rmax[o_b + q0];
                 }
             }
         }

@@ -6,6 +6,9 @@
 constexpr int SCHED_BINS = 4096; // longest sequence: (SCHED_BINS - 1) tiles
 
 // ---- launcher (sched.hip)
+// rel[T] (sequence-relative times) is followed by rmin[T] and rmax[T]: at the
+// first token r of every 32-token block of a sequence (r - start a multiple
+// of 32), the min and max of rel over that block's tokens.
 void launch_sched(const int32_t *offsets, const int64_t *ts, int B, int T, int tile, int H, int *status, int *n_items,
                   int2 *items, int max_items, uint32_t *rel, int32_t *wide, hipStream_t st);
 
@@ -17,6 +20,7 @@ struct AttnFwdArgs {
     const int64_t *ts;          // NULL: no time bias
     const uint32_t *rel;        // sequence-relative 32-bit times
     const int32_t *wide;        // per sequence: 1 = 64-bit time path
+    const uint32_t *rmin, *rmax; // per 32-token block (at its first token): range of rel
     const float *rab_p;         // NULL: no position bias
     int64_t rp_hs;
     const float *rab_t;         // NULL: no time bias
@@ -54,6 +58,7 @@ struct AttnBwdArgs {
     const int64_t *ts;
     const uint32_t *rel;
     const int32_t *wide;
+    const uint32_t *rmin, *rmax; // per 32-token block (at its first token): range of rel
     const float *rab_p;
     int64_t rp_hs;
     const float *rab_t;

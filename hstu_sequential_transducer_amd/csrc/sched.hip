@@ -138,9 +138,21 @@ __global__ void __launch_bounds__(256) reltime_kernel(const int32_t *__restrict_
         else hi = mid - 1;
     }
     while (lo < B - 1 && offsets[lo + 1] <= r) lo++; // skip empty sequences
-    const int64_t d = ts[r] - ts[offsets[lo]];
+    const int64_t t0 = ts[offsets[lo]];
+    const int64_t d = ts[r] - t0;
     if (d < -(int64_t)0x7FFFFFFF || d > (int64_t)0x7FFFFFFF) atomicOr(&wide[lo], 1);
     rel[r] = (uint32_t)(d + ((int64_t)1 << 31));
+    if (((r - offsets[lo]) & 31) == 0) { // first token of a 32-token block: its range of rel
+        const int end = min(r + 32, offsets[lo + 1]);
+        uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+        for (int i = r; i < end; i++) {
+            const uint32_t v = (uint32_t)(ts[i] - t0 + ((int64_t)1 << 31));
+            mn = min(mn, v);
+            mx = max(mx, v);
+        }
+        rel[T + r] = mn;
+        rel[2 * (int64_t)T + r] = mx;
+    }
 }
 
 void launch_sched(const int32_t *offsets, const int64_t *ts, int B, int T, int tile, int H, int *status, int *n_items,
