@@ -27,6 +27,8 @@
 // branches.
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace {
 
 constexpr int D = 128;
@@ -45,9 +47,8 @@ constexpr float NLN2 = -0.69314718055994531f;
 struct alignas(16) Stage {
     alignas(16) bf16 k[BN * RS];
     alignas(16) bf16 v[BN * VS];
-    float win[WIN];        // -log2(e) * rab_p[clip(key - query)]
+    float win[WIN];        // rab_p[clip(key - query)] (unscaled)
     uint32_t kt[BN];       // sequence-relative key times
-    uint32_t kmin[2], kmax[2]; // per 32-key half, over valid keys
 };
 struct alignas(16) Smem {
     Stage st[2];
@@ -69,11 +70,12 @@ DEV u32x2 lds_read_tr(const bf16 *p)
 
 // TM: 0 = no time bias, 1 = 32-bit relative times, 2 = 64-bit times.
 // Register r of the S^T accumulator <-> key kbase + koff(r), koff = 8(r/4) + r%4
-// (kbase = block start + 4g), query = this lane's.
-template <bool HP, int TM, bool DIAG, bool UNI>
-DEV void pointwise(const floatx16 &sacc, uint32_t (&pk)[8], const float *win_lane, const uint32_t *kt_lane,
-                   const float *rabt_rev, const float *rabt, uint32_t tq, int64_t tq64, const int64_t *tsk, int kbase,
-                   int klast, float ubias, int dmask)
+// (kbase = block start + 4g), query = this lane's.  sacc holds s + rab_p (the
+// window is loaded into the accumulator).
+template <int TM, bool DIAG, bool UNI>
+DEV void pointwise(const floatx16 &sacc, uint32_t (&pk)[8], const uint32_t *kt_lane, const float *rabt_rev,
+                   const float *rabt, uint32_t tq, int64_t tq64, const int64_t *tsk, int kbase, int klast, float ubias,
+                   int dmask)
 {
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
@@ -81,21 +83,20 @@ DEV void pointwise(const floatx16 &sacc, uint32_t (&pk)[8], const float *win_lan
 #pragma unroll
         for (int u = 0; u < 2; u++) {
             const int rr = r + u, koff = 8 * (rr >> 2) + (rr & 3);
-            float bsum = 0.f;
-            if constexpr (HP) bsum = win_lane[koff];
+            float tb = 0.f;
             if constexpr (TM == 1) {
                 if constexpr (UNI) {
-                    bsum += ubias;
+                    tb = ubias;
                 } else {
                     const uint32_t tk = kt_lane[koff];
                     const uint32_t dd = (tq > tk ? tq - tk : tk - tq) + 1u; // |dt| + 1
-                    bsum += rabt_rev[__builtin_clz(dd)];
+                    tb = rabt_rev[__builtin_clz(dd)];
                 }
             } else if constexpr (TM == 2) {
                 const int key = min(kbase + koff, klast);
-                bsum += rabt[time_bucket64(tq64 - tsk[key])];
+                tb = rabt[time_bucket64(tq64 - tsk[key])];
             }
-            const float x = __builtin_fmaf(sacc[rr], NLOG2E, bsum);
+            const float x = __builtin_fmaf(sacc[rr], NLOG2E, tb);
             float p = x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x));
             if constexpr (DIAG) p = koff > dmask ? 0.f : p;
             p2[u] = p;
@@ -114,7 +115,8 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h)
 
     // This lane's query and its Q fragment: Q[row][16s + 8g .. +8], s = 0..7
     // (B operand of S^T = K Q^T).
-    const int qrow = q0 + w * 32 + lq;
+    const int qstart = q0 + w * 32; // first query of this wave
+    const int qrow = qstart + lq;
     const bool qvalid = qrow < L;
     bf16x8 qreg[8];
     {
@@ -127,12 +129,11 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h)
     }
     const uint32_t tq = (TM == 1 && qvalid) ? a.rel[o_b + qrow] : 0u;
     const int64_t tq64 = (TM == 2 && qvalid) ? a.ts[o_b + qrow] : 0;
-    uint32_t tqmin = qvalid ? tq : 0xFFFFFFFFu, tqmax = qvalid ? tq : 0u;
-    if constexpr (TM == 1) {
-        for (int o = 32; o >= 1; o >>= 1) {
-            tqmin = min(tqmin, (uint32_t)__shfl_xor((int)tqmin, o, 64));
-            tqmax = max(tqmax, (uint32_t)__shfl_xor((int)tqmax, o, 64));
-        }
+    // time range of this wave's queries (precomputed per 32-token block), as scalars
+    uint32_t tqmin = 0xFFFFFFFFu, tqmax = 0u;
+    if (TM == 1 && qstart < L) {
+        tqmin = a.rmin[o_b + qstart];
+        tqmax = a.rmax[o_b + qstart];
     }
 
     floatx16 oacc[4];
@@ -145,35 +146,35 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h)
     const int lc = tid >> 4, le = tid & 15;
     u32x4 kreg[4], vreg[4];
     float wreg = 0.f;
-    uint32_t treg = 0, tmn = 0xFFFFFFFFu, tmx = 0u;
-    auto gload = [&](int kt) {
+    uint32_t treg = 0;
+    auto gload = [&](int kt, auto full_c) {
+        constexpr bool FULL = decltype(full_c)::value;
         const int kb0 = kt * BN;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int key = kb0 + lc * 4 + i;
-            const bool ok = key < kend;
-            const int64_t row = (int64_t)(o_b + (ok ? key : 0));
-            kreg[i] = ok ? *(const u32x4 *)(K + row * a.ldk + h * D + le * 8) : u32x4{0, 0, 0, 0};
-            vreg[i] = ok ? *(const u32x4 *)(V + row * a.ldv + h * D + le * 8) : u32x4{0, 0, 0, 0};
+            if constexpr (FULL) {
+                const int64_t row = (int64_t)(o_b + key);
+                kreg[i] = *(const u32x4 *)(K + row * a.ldk + h * D + le * 8);
+                vreg[i] = *(const u32x4 *)(V + row * a.ldv + h * D + le * 8);
+            } else {
+                const bool ok = key < kend;
+                const int64_t row = (int64_t)(o_b + (ok ? key : 0));
+                kreg[i] = ok ? *(const u32x4 *)(K + row * a.ldk + h * D + le * 8) : u32x4{0, 0, 0, 0};
+                vreg[i] = ok ? *(const u32x4 *)(V + row * a.ldv + h * D + le * 8) : u32x4{0, 0, 0, 0};
+            }
         }
         if constexpr (HP) {
             if (tid < WIN) {
                 int dl = kb0 - q0 - (BM - 1) + tid; // key - query of window slot tid
                 dl = dl < -a.N ? -a.N : (dl > a.N ? a.N : dl);
-                wreg = NLOG2E * a.rab_p[h * a.rp_hs + dl + a.N];
+                wreg = a.rab_p[h * a.rp_hs + dl + a.N];
             }
         }
         if constexpr (TM == 1) {
-            if (tid < BN) { // wave 0: key times and the range of each 32-key half
+            if (tid < BN) {
                 const int key = kb0 + tid;
-                const bool ok = key < kend;
-                treg = ok ? a.rel[o_b + key] : 0u;
-                tmn = ok ? treg : 0xFFFFFFFFu;
-                tmx = ok ? treg : 0u;
-                for (int o = 16; o >= 1; o >>= 1) {
-                    tmn = min(tmn, (uint32_t)__shfl_xor((int)tmn, o, 64));
-                    tmx = max(tmx, (uint32_t)__shfl_xor((int)tmx, o, 64));
-                }
+                treg = key < kend ? a.rel[o_b + key] : 0u;
             }
         }
     };
@@ -186,39 +187,44 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h)
         }
         if constexpr (HP)
             if (tid < WIN) S.win[tid] = wreg;
-        if constexpr (TM == 1) {
+        if constexpr (TM == 1)
             if (tid < BN) S.kt[tid] = treg;
-            if ((tid & 31) == 0 && tid < BN) {
-                S.kmin[tid >> 5] = tmn;
-                S.kmax[tid >> 5] = tmx;
-            }
-        }
     };
 
-    gload(0);
-    sstore(0);
-    __syncthreads();
-
-    const int qstart = q0 + w * 32; // first query of this wave
+    const std::integral_constant<bool, false> checked{};
+    const std::integral_constant<bool, true> unchecked{};
     // transposing-read lane constants for the V operand
     const int tj = l & 15, tsl = tj >> 2;
     const int cpart = ((l >> 4) & 1) * 16 + 4 * (tj & 3);
     const int64_t *tsk = TM == 2 ? a.ts + o_b : nullptr;
+    // Key tiles strictly below every query of the workgroup need no masking
+    // and are full: the MAIN iterations, compiled without the per-block checks.
+    const int n_main = q0 / BN; // tiles [0, n_main)
 
-    for (int kt = 0; kt < nkt; kt++) {
-        if (kt + 1 < nkt) gload(kt + 1);
+    auto iteration = [&](auto main_c, int kt) {
+        constexpr bool MAIN = decltype(main_c)::value;
+        if (MAIN) {
+            if (kt + 1 < n_main) gload(kt + 1, unchecked);
+            else if (kt + 1 < nkt) gload(kt + 1, checked);
+        } else if (kt + 1 < nkt) {
+            gload(kt + 1, checked);
+        }
         const Stage &S = sm.st[kt & 1];
         // Both 32-key blocks' S^T first (two independent MFMA chains, interleaved),
         // so the matrix core works on block 1 while the VALU runs block 0's
-        // element-wise step, and on block 0's PV while block 1's runs.
+        // element-wise step, and on block 0's PV while block 1's runs.  The
+        // accumulators start from the rab_p window.
         bool need[2];
         floatx16 sacc[2];
 #pragma unroll
         for (int kb = 0; kb < 2; kb++) {
             const int kstart = kt * BN + kb * 32;
-            need[kb] = !(kstart > qstart + 31 || qstart >= L); // wave-uniform
+            need[kb] = MAIN ? true : !(kstart > qstart + 31 || qstart >= L); // wave-uniform
 #pragma unroll
-            for (int r = 0; r < 16; r++) sacc[kb][r] = 0.f;
+            for (int r = 0; r < 16; r++) {
+                const int koff = 8 * (r >> 2) + (r & 3);
+                sacc[kb][r] = HP ? S.win[kb * 32 + 4 * g - w * 32 - lq + (BM - 1) + koff] : 0.f;
+            }
         }
         if (need[0] && need[1]) {
 #pragma unroll
@@ -239,34 +245,34 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h)
         for (int kb = 0; kb < 2; kb++) {
             const int kstart = kt * BN + kb * 32;
             if (!need[kb]) continue;
-            const bool diag = kstart + 31 > qstart;
-            const float *win_lane = &S.win[kb * 32 + 4 * g - w * 32 - lq + (BM - 1)];
+            const bool diag = MAIN ? false : kstart + 31 > qstart;
             const uint32_t *kt_lane = &S.kt[kb * 32 + 4 * g];
             const int kbase = kstart + 4 * g;
             bool uni = false;
             float ubias = 0.f;
             if constexpr (TM == 1) {
-                const uint32_t kmn = S.kmin[kb], kmx = S.kmax[kb];
-                if (kmn <= kmx && tqmin <= tqmax) {
-                    const int64_t a1 = (int64_t)tqmin - (int64_t)kmx, a2 = (int64_t)tqmax - (int64_t)kmn;
-                    const int64_t lo = a1 > 0 ? a1 : (a2 < 0 ? -a2 : 0);
-                    const int64_t m1 = a1 < 0 ? -a1 : a1, m2 = a2 < 0 ? -a2 : a2;
-                    const int64_t hi = m1 > m2 ? m1 : m2;
-                    const int blo = floor_log2_u32((uint32_t)lo + 1u), bhi = floor_log2_u32((uint32_t)hi + 1u);
-                    uni = __builtin_amdgcn_readfirstlane(blo == bhi ? 1 : 0) != 0;
+                // all pairs in one bucket iff floor(log2(min|dt| + 1)) == floor(log2(max|dt| + 1));
+                // relative times of one non-wide sequence differ by less than 2^32 - 1
+                const uint32_t ka = a.rmin[o_b + kstart], kb_ = a.rmax[o_b + kstart];
+                if (tqmin <= tqmax) {
+                    const uint32_t lo = ka > tqmax ? ka - tqmax : (tqmin > kb_ ? tqmin - kb_ : 0u);
+                    const uint32_t h1 = tqmax > ka ? tqmax - ka : 0u, h2 = kb_ > tqmin ? kb_ - tqmin : 0u;
+                    const uint32_t hi = h1 > h2 ? h1 : h2;
+                    const int blo = floor_log2_u32(lo + 1u), bhi = floor_log2_u32(hi + 1u);
+                    uni = blo == bhi;
                     ubias = sm.rabt[blo];
                 }
             }
             uint32_t pk[8];
             if (diag)
-                pointwise<HP, TM, true, false>(sacc[kb], pk, win_lane, kt_lane, sm.rabt_rev, sm.rabt, tq, tq64, tsk,
-                                               kbase, L - 1, ubias, lq - 4 * g);
+                pointwise<TM, true, false>(sacc[kb], pk, kt_lane, sm.rabt_rev, sm.rabt, tq, tq64, tsk, kbase, L - 1,
+                                           ubias, lq - 4 * g);
             else if (TM == 1 && uni)
-                pointwise<HP, TM, false, true>(sacc[kb], pk, win_lane, kt_lane, sm.rabt_rev, sm.rabt, tq, tq64, tsk,
-                                               kbase, L - 1, ubias, 0);
+                pointwise<TM, false, true>(sacc[kb], pk, kt_lane, sm.rabt_rev, sm.rabt, tq, tq64, tsk, kbase, L - 1,
+                                           ubias, 0);
             else
-                pointwise<HP, TM, false, false>(sacc[kb], pk, win_lane, kt_lane, sm.rabt_rev, sm.rabt, tq, tq64, tsk,
-                                                kbase, L - 1, ubias, 0);
+                pointwise<TM, false, false>(sacc[kb], pk, kt_lane, sm.rabt_rev, sm.rabt, tq, tq64, tsk, kbase, L - 1,
+                                            ubias, 0);
 #pragma unroll
             for (int m = 0; m < 2; m++) {
                 const bf16x8 pb = as_bf16x8(u32x4{pk[4 * m], pk[4 * m + 1], pk[4 * m + 2], pk[4 * m + 3]});
@@ -283,7 +289,19 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h)
         }
         if (kt + 1 < nkt) sstore((kt + 1) & 1);
         __syncthreads();
-    }
+    };
+
+    if (n_main > 0) gload(0, unchecked);
+    else gload(0, checked);
+    sstore(0);
+    __syncthreads();
+
+    const std::integral_constant<bool, false> generic{};
+    const std::integral_constant<bool, true> fast{};
+    int kt = 0;
+    if constexpr (TM != 2)
+        for (; kt < n_main; kt++) iteration(fast, kt);
+    for (; kt < nkt; kt++) iteration(generic, kt);
 
     if (!qvalid) return;
     // O^T accumulator: lane holds query qrow, d = 32 db + 8(r/4) + 4g + r%4;
