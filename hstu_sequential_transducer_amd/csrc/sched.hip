@@ -12,19 +12,20 @@
 // sum_{j > tid} v_j.  `tmp` is a 1024-entry LDS array.
 __device__ int block_suffix_excl(int v, int *tmp)
 {
-    const int tid = threadIdx.x;
-    __syncthreads();
-    tmp[tid] = v;
-    __syncthreads();
-    for (int o = 1; o < 1024; o <<= 1) {
-        const int add = tid + o < 1024 ? tmp[tid + o] : 0;
-        __syncthreads();
-        tmp[tid] += add;
-        __syncthreads();
+    // exclusive suffix sum over the 1024 threads: sum of v over threads > tid.
+    // Wave-level inclusive suffix scan with shuffles, then wave totals.
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    int incl = v;
+    for (int o = 1; o < 64; o <<= 1) {
+        const int x = __shfl_down(incl, o, 64);
+        if (lane + o < 64) incl += x;
     }
-    const int incl = tmp[tid];
+    __syncthreads(); // tmp may still be read by a previous call
+    if (lane == 0) tmp[wv] = incl; // wave total
     __syncthreads();
-    return incl - v;
+    int later = 0;
+    for (int k = wv + 1; k < 16; k++) later += tmp[k];
+    return incl - v + later;
 }
 
 // One workgroup of 1024 threads.  An item is (sequence b, tile t, head h);
@@ -104,17 +105,20 @@ __global__ void __launch_bounds__(1024) sched_kernel(const int32_t *__restrict__
     // per-class fill counter.
     for (int i = tid; i < SCHED_BINS; i += 1024) hist[i] = 0;
     __syncthreads();
-    for (int b = tid; b < B; b += 1024) {
-        int L = offsets[b + 1] - offsets[b];
-        int n = L > 0 ? (L + tile - 1) / tile : 0;
+    // one wave per sequence: lane 0 takes the sequence's rank in its length
+    // class, the lanes write its n * H items
+    const int lane = tid & 63, wv = tid >> 6;
+    for (int b = wv; b < B; b += 16) {
+        const int L = offsets[b + 1] - offsets[b];
+        const int n = L > 0 ? (L + tile - 1) / tile : 0;
         if (n == 0) continue;
-        int pos = fill[n] + atomicAdd(&hist[n], 1);
-        for (int t = 0; t < n; t++) {
-            int base = H * (S[t] + pos);
-            for (int h = 0; h < H; h++) {
-                int idx = base + h;
-                if (idx < max_items) items[idx] = make_int2(b, (t << 8) | h);
-            }
+        int pos = 0;
+        if (lane == 0) pos = fill[n] + atomicAdd(&hist[n], 1);
+        pos = __shfl(pos, 0, 64);
+        for (int k = lane; k < n * H; k += 64) {
+            const int t = k / H, h = k - t * H;
+            const int idx = H * (S[t] + pos) + h;
+            if (idx < max_items) items[idx] = make_int2(b, (t << 8) | h);
         }
     }
 }
