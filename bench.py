@@ -47,7 +47,7 @@ CSRC = os.path.join(ROOT, "hstu_sequential_transducer_amd", "csrc")
 # source they were measured on (sha256 over the files listed); otherwise the
 # traffic is reported as null.
 MEASURED_TRAFFIC = {
-    "attn_bwd_bf16_kernel": {"src": "8f0c9f0e5ebb1807", "bytes": 2581547073},   # read 1075754145 + write 1505792928
+    "attn_bwd_bf16_kernel": {"src": "bb8c5d7c9fac2065", "bytes": 2586578174},   # read 1076443720 + write 1510134453
 }
 
 

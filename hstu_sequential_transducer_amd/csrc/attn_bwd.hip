@@ -12,33 +12,37 @@
 // planes (hi + lo) so dP keeps ~16 significant bits.
 //
 // A workgroup of 8 waves owns 128 keys of one (sequence, head).  Keys come in
-// 4 groups of 32; each group is shared by two waves, which run on the same
-// SIMD and split the work so that each needs only ~220 registers (two waves
-// per SIMD: one's element-wise VALU work overlaps the other's MFMAs):
-//   the V wave (waves 0-3) computes X = Q K^T + rab_p, P = SiLU(X) and
-//     dV^T += dO'^T P for its keys, and, one block late, dQ for d-block w of
-//     all 128 keys (plus the drab_p diagonal sums);
-//   the K wave (waves 4-7) computes X and dP = dO' V^T (hi and lo planes),
-//     dS and dK^T += Q^T dS, and writes dS (bf16 for dQ, fp32 skewed for
-//     drab_p) to LDS.
-// X is computed by both; everything else once.  All products are 32x32x16
-// bf16 MFMA with lane = key, registers = queries.  Query blocks of 32 stream
-// through LDS (double buffered, copied global -> LDS directly); the rab_p
-// window is loaded into the X accumulator.  dQ partial sums go to an fp32
-// accumulator with global atomics.  One barrier per query block.
+// 4 groups of 32; each group is served by two waves that run on the same
+// SIMD and split the work by kind, so that one's element-wise VALU work
+// overlaps the other's MFMAs:
+//   the pointwise wave (waves 4-7) keeps its keys' K and V rows in registers
+//     and, for query block n, computes X = Q K^T + rab_p and dP = dO' V^T (hi
+//     and lo planes), then P = SiLU(X) and dS, which it writes to LDS as bf16
+//     [key][query] tiles (and fp32 dS into a tile skewed by j - i for
+//     drab_p), and adds dS to drab_t;
+//   the accumulating wave (waves 0-3) works one block behind: dV^T += dO'^T P
+//     and dK^T += Q^T dS for its keys, dQ for d-block w of all 128 keys
+//     (fp32 global atomics), and the drab_p diagonal sums.
+// X, P and dS are computed once.  All products are 32x32x16 bf16 MFMA with
+// lane = key, registers = queries.  Query blocks of 32 stream through LDS,
+// copied global -> LDS directly: Q and dO' are triple buffered (block n + 1
+// lands while the pointwise waves read block n and the accumulating waves
+// block n - 1), dO'-lo and the per-block tables double buffered.  The rab_p
+// window is loaded into the X accumulator.  One barrier per query block.
 //
-// drab_p: the K wave writes its fp32 dS into an LDS tile skewed by j - i
-// ([key - query][query]); one block later, one thread per diagonal sums it
-// into an LDS ring indexed by j - i, and an entry is flushed with one global
-// atomic once no later block can reach it.  drab_t: when every pair of a
-// 32x32 block falls in one time bucket (decided per block in scalar code from
-// the min/max times of its queries and keys) the bias is a scalar and the
-// block's dS is summed by a wave reduction; otherwise per-element adds go to
-// per-wave LDS tables.  Bias presence, time mode, diagonal masking and uniform
-// blocks are compile-time instantiations, so the element-wise code has no
-// branches.
+// drab_p: the pointwise wave writes its fp32 dS into an LDS tile skewed by
+// j - i ([key - query][query]); one block later, one thread per diagonal sums
+// it into an LDS ring indexed by j - i, and an entry is flushed with one
+// global atomic once no later block can reach it.  drab_t: when every pair of
+// a 32x32 block falls in one time bucket (decided per block in scalar code
+// from the min/max times of its queries and keys) the bias is a scalar and
+// the block's dS is summed by a wave reduction; otherwise per-element adds go
+// to per-wave LDS tables.  Bias presence, time mode, diagonal masking and
+// uniform blocks are compile-time instantiations, so the element-wise code
+// has no branches.
 #include "kernels.h"
 
+#include <cstddef>
 #include <type_traits>
 
 namespace {
@@ -64,9 +68,14 @@ constexpr int TCOPY = 4;   // copies of each K wave's drab_t table
 constexpr float NLOG2E = -1.4426950408889634f;
 constexpr float NLN2 = -0.69314718055994531f;
 
-struct alignas(16) Stage {
+// Stage tiles read by both roles (pointwise waves: block n; accumulating
+// waves: block n - 1): triple buffered.
+struct alignas(16) StageQ {
     alignas(16) bf16 q[BQ * D];
     alignas(16) bf16 dO[BQ * D];
+};
+// Stage data read by the pointwise waves only: double buffered.
+struct alignas(16) StageP {
     alignas(16) bf16 dOl[BQ * D]; // low part of dO' (dO' = dO + dOl to ~16 bits)
     float win[WIN];               // rab_p[clip(key - query)], slot = key - query + BQ - 1 - (k0 - q0)
     uint32_t qt[BQ];
@@ -74,15 +83,19 @@ struct alignas(16) Stage {
     uint32_t qtmin, qtmax;        // over the block's valid queries
 };
 struct alignas(16) Smem {
-    Stage st[2];
-    alignas(16) bf16 ds[2][BN * SS];
+    StageQ sq[3];
+    StageP sp[2];
+    alignas(16) bf16 ds[2][BN * SS];    // dS [key][query] (the prologue's K tile spans ds and pt)
+    alignas(16) bf16 pt[2][BN * SS];    // P' [key][query]
     alignas(16) float dsk[2][DK * DKP]; // fp32 dS skewed: [key - query + BQ - 1][query]
-    alignas(16) bf16 kt[BN * D];        // the workgroup's K rows, swizzled like the stage tiles
     float ring[RING];
     float dtab[4][TCOPY][TB];
     float rabt_rev[32];
     float rabt[128];
 };
+static_assert(offsetof(Smem, pt) == offsetof(Smem, ds) + sizeof(Smem::ds) &&
+                  sizeof(Smem::ds) + sizeof(Smem::pt) >= sizeof(bf16) * BN * D,
+              "the prologue's K tile fits in ds + pt");
 static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget");
 
 // Swizzle of row r: the XOR applied to its 16-byte chunk index.
@@ -143,48 +156,32 @@ DEV float xprime(const floatx16 &xacc, int rr, const BwdLane &ln, const float *r
     return __builtin_fmaf(xacc[rr], NLOG2E, tb);
 }
 
-// V wave: P' = x' sigmoid(x) = -log2(e) SiLU(x) (the -ln 2 goes into dV's
-// final scale), packed to bf16.  Register r <-> query 4g + cr(r),
+// Pointwise wave, one 32x32 block: P' = x' sigmoid(x) = -log2(e) SiLU(x)
+// (the -ln 2 goes into dV's final scale) and dS = dP sg (1 + x (1 - sg)) =
+// dP (sg - ln2 (p' - p' sg)), both packed to bf16; fp32 dS also into the
+// skewed tile and into drab_t.  Register r <-> query 4g + cr(r),
 // cr = 8(r/4) + r%4; this lane's key.
-template <int TM, bool DIAG, bool UNI>
-DEV void pointwise_v(const floatx16 &xacc, uint32_t (&ppk)[8], const BwdLane &ln, const float *rabt_rev,
-                     const float *rabt, float ubias)
-{
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-        float pp[2];
-#pragma unroll
-        for (int u = 0; u < 2; u++) {
-            const int rr = r + u, cr = 8 * (rr >> 2) + (rr & 3);
-            int bucket;
-            const float x = xprime<TM, UNI>(xacc, rr, ln, rabt_rev, rabt, ubias, bucket);
-            float p = x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x));
-            if constexpr (DIAG) p = cr < ln.dmask ? 0.f : p;
-            pp[u] = p;
-        }
-        ppk[r >> 1] = pack2_bf16(pp[0], pp[1]);
-    }
-}
-
-// K wave: dS = dP sg (1 + x (1 - sg)) = dP (sg - ln2 (p' - p' sg)), packed to
-// bf16, written fp32 into the skewed tile, and added to drab_t.
 template <int TM, bool DT, bool DIAG, bool UNI>
-DEV void pointwise_k(const floatx16 &xacc, const floatx16 &pacc, uint32_t (&dpk)[8], const BwdLane &ln,
-                     const float *rabt_rev, const float *rabt, float ubias, float &tsum)
+DEV void pointwise(const floatx16 &xacc, const floatx16 &pacc, uint32_t (&ppk)[8], uint32_t (&dpk)[8],
+                   const BwdLane &ln, const float *rabt_rev, const float *rabt, float ubias, float &tsum)
 {
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-        float dd[2];
+        float pp[2], dd[2];
 #pragma unroll
         for (int u = 0; u < 2; u++) {
             const int rr = r + u, cr = 8 * (rr >> 2) + (rr & 3);
             int bucket;
             const float x = xprime<TM, UNI>(xacc, rr, ln, rabt_rev, rabt, ubias, bucket);
             const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x));
-            const float p = x * sg;
+            float p = x * sg;
             const float t = __builtin_fmaf(-p, sg, p);
             float ds = pacc[rr] * __builtin_fmaf(t, NLN2, sg);
-            if constexpr (DIAG) ds = cr < ln.dmask ? 0.f : ds;
+            if constexpr (DIAG) {
+                p = cr < ln.dmask ? 0.f : p;
+                ds = cr < ln.dmask ? 0.f : ds;
+            }
+            pp[u] = p;
             dd[u] = ds;
             ln.dsk[-(DKP - 1) * cr] = ds;
             if constexpr (DT && TM != 0) {
@@ -192,8 +189,19 @@ DEV void pointwise_k(const floatx16 &xacc, const floatx16 &pacc, uint32_t (&dpk)
                 else atomicAdd(&ln.dtab[bucket], ds);
             }
         }
+        ppk[r >> 1] = pack2_bf16(pp[0], pp[1]);
         dpk[r >> 1] = pack2_bf16(dd[0], dd[1]);
     }
+}
+
+// 16-byte slice o..o+3 of a register block as a bf16x8 MFMA operand.  (Each
+// element is copied to a scalar before the bit cast: clang's bit_cast of a
+// vector-element expression reads element 0.)
+DEV bf16x8 slice8(const floatx16 &f, int o)
+{
+    const float e0 = f[o], e1 = f[o + 1], e2 = f[o + 2], e3 = f[o + 3];
+    return as_bf16x8(u32x4{__builtin_bit_cast(uint32_t, e0), __builtin_bit_cast(uint32_t, e1),
+                           __builtin_bit_cast(uint32_t, e2), __builtin_bit_cast(uint32_t, e3)});
 }
 
 template <bool HP, int TM, bool DT>
@@ -201,46 +209,56 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
 {
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, lq = l & 31;
     const int p = w & 3;          // key group: keys 32p..32p+31 of the tile
-    const bool vwave = w < 4;     // V wave (else K wave); wave-uniform
+    const bool awave = w < 4;     // accumulating wave (else pointwise wave); wave-uniform
     const bf16 *Q = a.q, *K = a.k, *V = a.v, *dO = a.dO;
     const int64_t ld_do = (int64_t)a.H * D;
     const bf16 *dOlo = dO + (int64_t)a.T * ld_do;
     // transposing-read lane constants
     const int tj = l & 15, tsl = tj >> 2;
     const int cpart = ((l >> 4) & 1) * 16 + 4 * (tj & 3);
+    bf16 *kt = &sm.ds[0][0]; // prologue only: the workgroup's K rows, swizzled like the stage tiles
 
     // ---- prologue: the workgroup's K rows into LDS (rows past the sequence
     // repeat the last row: finite, and every pair they form is masked or has
-    // dS = 0); they supply the B operand of X = Q K^T, and a V wave keeps
-    // d-block p of all 128 rows in registers (B operand of dQ = dS K).  A K
-    // wave's own V rows straight from memory.
+    // dS = 0); an accumulating wave keeps d-block p of all 128 rows in
+    // registers (B operand of dQ = dS K).  A pointwise wave's own K and V rows
+    // come straight from memory.
 #pragma unroll
     for (int i = 0; i < BN / (4 * NW); i++) {
         const int r0 = 4 * ((BN / (4 * NW)) * w + i), row = r0 + (l >> 4);
         const int c = (l & 15) ^ swf(row);
         const int key = min(k0 + row, L - 1);
         __builtin_amdgcn_global_load_lds((const void *)(K + (int64_t)(o_b + key) * a.ldk + h * D + c * 8),
-                                         (lds_void *)(sm.kt + r0 * D), 16, 0, 0);
+                                         (lds_void *)(kt + r0 * D), 16, 0, 0);
     }
     const int kw0 = k0 + 32 * p; // this key group's first key
     const int mykey = kw0 + lq;
     const bool kvalid = mykey < L;
-    // opnd: V wave -> K d-block p of all rows (dQ operand); K wave -> own V rows
-    bf16x8 opnd[8];
-    if (!vwave) {
-        const bf16 *vp = V + (int64_t)(o_b + (kvalid ? mykey : 0)) * a.ldv + h * D + g * 8;
+    // acc: accumulating wave -> dV^T.  acc2: accumulating wave -> dK^T;
+    // pointwise wave -> the bits of its K row (chunks 2i, 2i+1 in elements
+    // 0..7 of acc2[i]) and V row (elements 8..15), 16-byte chunk s holding
+    // d = 16s + 8g .. +8 (B operands of X = Q K^T and dP = dO' V^T).
+    // Lane = key, d = 32 db + 8(r/4) + 4g + r%4 for the accumulators.
+    floatx16 acc[4], acc2[4];
 #pragma unroll
-        for (int s = 0; s < 8; s++) opnd[s] = as_bf16x8(kvalid ? *(const u32x4 *)(vp + s * 16) : u32x4{0, 0, 0, 0});
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (vwave) {
+    for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int t = 0; t < BN / 16; t++) {
-            const int kr1 = 16 * t + 8 * g + tsl;
-            const u32x2 k1 = lds_read_tr(&sm.kt[swz(kr1, 32 * p + cpart)]);
-            const u32x2 k2 = lds_read_tr(&sm.kt[swz(kr1 + 4, 32 * p + cpart)]);
-            opnd[t] = as_bf16x8(u32x4{k1[0], k1[1], k2[0], k2[1]});
+        for (int r = 0; r < 16; r++) acc[i][r] = acc2[i][r] = 0.f;
+    if (!awave && kvalid) {
+        const int64_t row = o_b + mykey;
+        const bf16 *kp = K + row * a.ldk + h * D + g * 8, *vp = V + row * a.ldv + h * D + g * 8;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const u32x4 k1 = *(const u32x4 *)(kp + 32 * i), k2 = *(const u32x4 *)(kp + 32 * i + 16);
+            const u32x4 v1 = *(const u32x4 *)(vp + 32 * i), v2 = *(const u32x4 *)(vp + 32 * i + 16);
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const uint32_t ka = k1[e], kb = k2[e], va = v1[e], vb = v2[e];
+                acc2[i][e] = __builtin_bit_cast(float, ka);
+                acc2[i][4 + e] = __builtin_bit_cast(float, kb);
+                acc2[i][8 + e] = __builtin_bit_cast(float, va);
+                acc2[i][12 + e] = __builtin_bit_cast(float, vb);
+            }
         }
     }
     for (int i = tid; i < RING; i += NT) sm.ring[i] = 0.f;
@@ -262,13 +280,6 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
         tkmax = __builtin_amdgcn_readfirstlane(tkmax);
     }
 
-    // acc: V wave -> dV^T, K wave -> dK^T (lane = key, d = 32 db + 8(r/4) + 4g + r%4)
-    floatx16 acc[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int r = 0; r < 16; r++) acc[i][r] = 0.f;
-
     // ---- query-block stage loader.  Full blocks: 24 groups of 4 rows (Q,
     // dO, dO-lo) copied straight into LDS, 3 per wave; lane l fills physical
     // chunk l%16 of row 4(G%8) + l/16.  The last, partial block goes through
@@ -278,7 +289,7 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
     float wreg = 0.f;
     uint32_t treg = 0, tmn = 0xFFFFFFFFu, tmx = 0u;
     int64_t treg64 = 0;
-    auto gload_direct = [&](int q0, Stage &S) {
+    auto gload_direct = [&](int q0, StageQ &SQ, StageP &SP) {
 #pragma unroll
         for (int i = 0; i < 24 / NW; i++) {
             const int G = (24 / NW) * w + i, plane = G >> 3, r0 = 4 * (G & 7);
@@ -286,7 +297,7 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
             const int c = (l & 15) ^ swf(row);
             const int64_t grow = (int64_t)(o_b + q0 + row);
             const bf16 *src = plane == 0 ? Q + grow * a.ldq : (plane == 1 ? dO : dOlo) + grow * ld_do;
-            bf16 *dst = (plane == 0 ? S.q : (plane == 1 ? S.dO : S.dOl)) + r0 * D;
+            bf16 *dst = (plane == 0 ? SQ.q : (plane == 1 ? SQ.dO : SP.dOl)) + r0 * D;
             __builtin_amdgcn_global_load_lds((const void *)(src + h * D + c * 8), (lds_void *)dst, 16, 0, 0);
         }
     };
@@ -311,7 +322,7 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
             }
         }
     };
-    auto load_partial = [&](int q0, Stage &S) {
+    auto load_partial = [&](int q0, StageQ &SQ, StageP &SP) {
         const int qi = q0 + lcq;
         const bool ok = qi < L;
         const int64_t row = (int64_t)(o_b + (ok ? qi : L - 1));
@@ -319,11 +330,11 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
         const u32x4 qv = *(const u32x4 *)(Q + row * a.ldq + h * D + col);
         const u32x4 dv = ok ? *(const u32x4 *)(dO + row * ld_do + h * D + col) : u32x4{0, 0, 0, 0};
         const u32x4 lv = ok ? *(const u32x4 *)(dOlo + row * ld_do + h * D + col) : u32x4{0, 0, 0, 0};
-        *(u32x4 *)&S.q[swz(lcq, col)] = qv;
-        *(u32x4 *)&S.dO[swz(lcq, col)] = dv;
-        *(u32x4 *)&S.dOl[swz(lcq, col)] = lv;
+        *(u32x4 *)&SQ.q[swz(lcq, col)] = qv;
+        *(u32x4 *)&SQ.dO[swz(lcq, col)] = dv;
+        *(u32x4 *)&SP.dOl[swz(lcq, col)] = lv;
     };
-    auto sstore_tables = [&](Stage &S) {
+    auto sstore_tables = [&](StageP &S) {
         if constexpr (HP)
             if (tid < WIN) S.win[tid] = wreg;
         if constexpr (TM != 0) {
@@ -338,11 +349,59 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
         }
     };
 
+    // stage 0, then the K tile's d-block p into the accumulating waves' registers
+    if (k0 + BQ <= L) gload_direct(k0, sm.sq[0], sm.sp[0]);
+    else load_partial(k0, sm.sq[0], sm.sp[0]);
+    gload_tables(k0);
+    sstore_tables(sm.sp[0]);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    bf16x8 opnd[8]; // accumulating wave: K d-block p of all rows (dQ operand)
+    if (awave) {
+#pragma unroll
+        for (int t = 0; t < BN / 16; t++) {
+            const int kr1 = 16 * t + 8 * g + tsl;
+            const u32x2 k1 = lds_read_tr(&kt[swz(kr1, 32 * p + cpart)]);
+            const u32x2 k2 = lds_read_tr(&kt[swz(kr1 + 4, 32 * p + cpart)]);
+            opnd[t] = as_bf16x8(u32x4{k1[0], k1[1], k2[0], k2[1]});
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads(); // the K tile is dead (ds and pt are written from block 0 on)
+
     const int p_hs = a.rp_hs > 0 ? (int)a.rp_hs : 2 * a.N + 1;
     const int t_hs = a.rt_hs > 0 ? (int)a.rt_hs : 128;
 
-    // V wave: dQ of the block at q0m from the dS tile `dst` (all 128 keys):
-    // dQ[32 queries][d-block p] = sum over the keys of dS[q][key] K[key][d]
+    // Accumulating wave, block at q0m (stage SQ, tiles of buffer b), keys of
+    // this group: dV^T += dO'^T P and dK^T += Q^T dS, contractions over the
+    // 32 queries.  The B operands are this lane's key row of the P' and dS
+    // tiles, queries 16m + {4g..4g+3, 8+4g..8+4g+3} (the order of the
+    // transposing reads' k index).
+    auto acc_block = [&](const StageQ &SQ, int b) {
+        const bf16 *ptb = sm.pt[b], *dsb = sm.ds[b];
+        const int krow = 32 * p + lq;
+#pragma unroll
+        for (int m = 0; m < 2; m++) {
+            const u32x2 p1 = *(const u32x2 *)&ptb[krow * SS + 16 * m + 4 * g];
+            const u32x2 p2 = *(const u32x2 *)&ptb[krow * SS + 16 * m + 8 + 4 * g];
+            const u32x2 s1 = *(const u32x2 *)&dsb[krow * SS + 16 * m + 4 * g];
+            const u32x2 s2 = *(const u32x2 *)&dsb[krow * SS + 16 * m + 8 + 4 * g];
+            const bf16x8 pb = as_bf16x8(u32x4{p1[0], p1[1], p2[0], p2[1]});
+            const bf16x8 sb = as_bf16x8(u32x4{s1[0], s1[1], s2[0], s2[1]});
+            const int qr1 = 16 * m + 4 * g + tsl; // query row of the transposing read
+#pragma unroll
+            for (int db = 0; db < 4; db++) {
+                const u32x2 d1 = lds_read_tr(&SQ.dO[swz(qr1, db * 32 + cpart)]);
+                const u32x2 d2 = lds_read_tr(&SQ.dO[swz(qr1 + 8, db * 32 + cpart)]);
+                acc[db] = mfma32(as_bf16x8(u32x4{d1[0], d1[1], d2[0], d2[1]}), pb, acc[db]);
+                const u32x2 q1 = lds_read_tr(&SQ.q[swz(qr1, db * 32 + cpart)]);
+                const u32x2 q2 = lds_read_tr(&SQ.q[swz(qr1 + 8, db * 32 + cpart)]);
+                acc2[db] = mfma32(as_bf16x8(u32x4{q1[0], q1[1], q2[0], q2[1]}), sb, acc2[db]);
+            }
+        }
+    };
+    // Accumulating wave: dQ of the block at q0m from the dS tile `dst` (all
+    // 128 keys): dQ[32 queries][d-block p] = sum over the keys of dS[q][key] K[key][d]
     auto dq_block = [&](const bf16 *dst, int q0m, bool full) {
         floatx16 qacc;
 #pragma unroll
@@ -368,12 +427,12 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
             }
         }
     };
-    // V waves: drab_p of the block at q0m from its skewed tile (row c =
-    // diagonal c, key - query = k0 - q0m + c - (BQ - 1); cells outside the
-    // tile's keys are never written and stay 0).  One thread per row; threads
-    // past the last diagonal take the all-zero row DK - 1.  The ring entry is
-    // flushed once no later block can reach it (key - query > k0 + BN - 1 -
-    // (q0m + BQ)  <=>  c > BN - 2).
+    // Accumulating waves: drab_p of the block at q0m from its skewed tile
+    // (row c = diagonal c, key - query = k0 - q0m + c - (BQ - 1); cells
+    // outside the tile's keys are never written and stay 0).  One thread per
+    // row; threads past the last diagonal take the all-zero row DK - 1.  The
+    // ring entry is flushed once no later block can reach it (key - query >
+    // k0 + BN - 1 - (q0m + BQ)  <=>  c > BN - 2).
     auto drabp_sum = [&](const float *dsk, int q0m, float &tot, int &dl) {
         const int c = tid < DK - 1 ? tid : DK - 1;
         const floatx4 *rowp = (const floatx4 *)(dsk + c * DKP);
@@ -399,60 +458,83 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
     // are full), compiled without the per-block checks.
     const int nqb = (L - k0 + BQ - 1) / BQ; // query blocks [k0, L); >= 1
     const int krow = 32 * p + lq;
-    auto iteration = [&](auto main_c, int n) {
+    // What every wave does at the end of block n: the tables (and, for a
+    // partial next block, the register path) of block n + 1, then the wait
+    // for the direct copies and the barrier.
+    auto finish = [&](auto main_c, int n) {
         constexpr bool MAIN = decltype(main_c)::value;
         const int q0 = k0 + n * BQ;
-        const bool nfull = q0 + 2 * BQ <= L; // the next block is full
-        if (MAIN) gload_direct(q0 + BQ, sm.st[(n + 1) & 1]);
-        else if (n + 1 < nqb && nfull) gload_direct(q0 + BQ, sm.st[(n + 1) & 1]);
-        const Stage &S = sm.st[n & 1];
-        const bool skip = MAIN ? false : (kw0 > q0 + BQ - 1 || kw0 >= L);
-        const bool diag = MAIN ? false : kw0 + 31 > q0;
-        // X = Q K^T + rab_p window (both waves); dP = dO' V^T (K wave)
-        floatx16 xacc, pacc;
-#pragma unroll
-        for (int r = 0; r < 16; r++) {
-            const int cr = 8 * (r >> 2) + (r & 3);
-            xacc[r] = HP ? S.win[krow + (BQ - 1) - 4 * g - cr] : 0.f;
-            pacc[r] = 0.f;
+        if (MAIN || n + 1 < nqb) {
+            const int n3 = n % 3 == 2 ? 0 : n % 3 + 1;
+            if (!MAIN && q0 + 2 * BQ > L) load_partial(q0 + BQ, sm.sq[n3], sm.sp[(n + 1) & 1]);
+            sstore_tables(sm.sp[(n + 1) & 1]);
         }
-        if (!skip) {
-            if (vwave) {
-#pragma unroll
-                for (int s = 0; s < 8; s++)
-                    xacc = mfma32(*(const bf16x8 *)&S.q[swz(lq, s * 16 + g * 8)],
-                                  *(const bf16x8 *)&sm.kt[swz(krow, s * 16 + g * 8)], xacc);
-            } else {
-#pragma unroll
-                for (int s = 0; s < 8; s++) {
-                    const int o = swz(lq, s * 16 + g * 8);
-                    xacc = mfma32(*(const bf16x8 *)&S.q[o], *(const bf16x8 *)&sm.kt[swz(krow, s * 16 + g * 8)], xacc);
-                    pacc = mfma32(*(const bf16x8 *)&S.dO[o], opnd[s], pacc);
-                    pacc = mfma32(*(const bf16x8 *)&S.dOl[o], opnd[s], pacc);
-                }
-            }
-        }
-        // V waves: the previous block's drab_p (its skewed tile is complete)
+        __builtin_amdgcn_s_waitcnt(0); // direct LDS copies (and everything else) landed
+        __syncthreads();
+    };
+    auto start_copy = [&](auto main_c, int n) {
+        constexpr bool MAIN = decltype(main_c)::value;
+        const int q0 = k0 + n * BQ;
+        const int n3 = n % 3 == 2 ? 0 : n % 3 + 1;
+        if (MAIN) gload_direct(q0 + BQ, sm.sq[n3], sm.sp[(n + 1) & 1]);
+        else if (n + 1 < nqb && q0 + 2 * BQ <= L) gload_direct(q0 + BQ, sm.sq[n3], sm.sp[(n + 1) & 1]);
+    };
+    // Accumulating wave, block n: the previous block's dV, dK, dQ and drab_p.
+    auto iter_acc = [&](auto main_c, int n) {
+        constexpr bool MAIN = decltype(main_c)::value;
+        const int q0 = k0 + n * BQ;
+        start_copy(main_c, n);
         int dlf = 0;
         float tot = 0.f;
-        if (vwave && (MAIN || n > 0) && a.drab_p) drabp_sum(sm.dsk[(n - 1) & 1], q0 - BQ, tot, dlf);
+        if (MAIN || n > 0) {
+            const int q0m = q0 - BQ;
+            const bool skipm = MAIN ? false : (kw0 > q0m + BQ - 1 || kw0 >= L);
+            if (!skipm) acc_block(sm.sq[n % 3 == 0 ? 2 : n % 3 - 1], (n - 1) & 1);
+            dq_block(sm.ds[(n - 1) & 1], q0m, MAIN ? true : q0 <= L);
+            if (a.drab_p) drabp_sum(sm.dsk[(n - 1) & 1], q0m, tot, dlf);
+        }
         if (MAIN) gload_tables(q0 + BQ);
         else if (n + 1 < nqb) gload_tables(q0 + BQ);
-        if (vwave && (MAIN || n > 0) && a.drab_p) drabp_flush(dlf, tot);
-
+        if ((MAIN || n > 0) && a.drab_p) drabp_flush(dlf, tot);
+        finish(main_c, n);
+    };
+    // Pointwise wave, block n: X, dP, P', dS.
+    auto iter_pw = [&](auto main_c, int n) {
+        constexpr bool MAIN = decltype(main_c)::value;
+        const int q0 = k0 + n * BQ;
+        start_copy(main_c, n);
+        const StageQ &SQn = sm.sq[n % 3];
+        const StageP &SPn = sm.sp[n & 1];
+        const bool skip = MAIN ? false : (kw0 > q0 + BQ - 1 || kw0 >= L);
+        const bool diag = MAIN ? false : kw0 + 31 > q0;
         ln.dsk = sm.dsk[n & 1] + (krow + (BQ - 1) - 4 * g) * DKP + 4 * g;
-        bf16 *dsn = sm.ds[n & 1];
+        bf16 *dsn = sm.ds[n & 1], *ptn = sm.pt[n & 1];
         if (!skip) {
-            ln.qt = &S.qt[4 * g];
-            ln.qt64 = &S.qt64[4 * g];
+            // X = Q K^T + rab_p window; dP = dO' V^T (hi + lo planes)
+            floatx16 xacc, pacc;
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int cr = 8 * (r >> 2) + (r & 3);
+                xacc[r] = HP ? SPn.win[krow + (BQ - 1) - 4 * g - cr] : 0.f;
+                pacc[r] = 0.f;
+            }
+#pragma unroll
+            for (int s = 0; s < 8; s++) {
+                const int o = swz(lq, s * 16 + g * 8);
+                xacc = mfma32(*(const bf16x8 *)&SQn.q[o], slice8(acc2[s >> 1], 4 * (s & 1)), xacc);
+                pacc = mfma32(*(const bf16x8 *)&SQn.dO[o], slice8(acc2[s >> 1], 8 + 4 * (s & 1)), pacc);
+                pacc = mfma32(*(const bf16x8 *)&SPn.dOl[o], slice8(acc2[s >> 1], 8 + 4 * (s & 1)), pacc);
+            }
+            ln.qt = &SPn.qt[4 * g];
+            ln.qt64 = &SPn.qt64[4 * g];
             ln.dmask = kw0 + lq - q0 - 4 * g; // key > query  <=>  cr < dmask
             bool uni = false;
             int ubk = 0;
             if constexpr (TM == 1) {
                 // all pairs in one bucket iff floor(log2(min|dt| + 1)) == floor(log2(max|dt| + 1));
                 // relative times of one non-wide sequence differ by less than 2^32 - 1
-                const uint32_t qa = __builtin_amdgcn_readfirstlane(S.qtmin);
-                const uint32_t qb = __builtin_amdgcn_readfirstlane(S.qtmax);
+                const uint32_t qa = __builtin_amdgcn_readfirstlane(SPn.qtmin);
+                const uint32_t qb = __builtin_amdgcn_readfirstlane(SPn.qtmax);
                 if (qa <= qb && tkmin <= tkmax) {
                     const uint32_t lo = tkmin > qb ? tkmin - qb : (qa > tkmax ? qa - tkmax : 0u);
                     const uint32_t h1 = qb > tkmin ? qb - tkmin : 0u, h2 = tkmax > qa ? tkmax - qa : 0u;
@@ -463,97 +545,57 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
                 }
             }
             const float ubias = sm.rabt[ubk];
-            const int tsl2 = tsl;
-            if (vwave) {
-                uint32_t ppk[8];
-                if (diag) pointwise_v<TM, true, false>(xacc, ppk, ln, sm.rabt_rev, sm.rabt, ubias);
-                else if (TM == 1 && uni) pointwise_v<TM, false, true>(xacc, ppk, ln, sm.rabt_rev, sm.rabt, ubias);
-                else pointwise_v<TM, false, false>(xacc, ppk, ln, sm.rabt_rev, sm.rabt, ubias);
-                // the previous block's dQ (every K wave's dS of it is in its tile)
-                if (MAIN || n > 0) dq_block(sm.ds[(n - 1) & 1], q0 - BQ, MAIN ? true : q0 <= L);
-                // dV^T += dO'^T P  (contraction over the 32 queries)
+            float tsum = 0.f;
+            uint32_t ppk[8], dpk[8];
+            if (diag) pointwise<TM, DT, true, false>(xacc, pacc, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, tsum);
+            else if (TM == 1 && uni)
+                pointwise<TM, DT, false, true>(xacc, pacc, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, tsum);
+            else pointwise<TM, DT, false, false>(xacc, pacc, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, tsum);
+            // P' and dS -> LDS as [key][query]: lane writes 4 queries (r%4) per r/4 group
 #pragma unroll
-                for (int m = 0; m < 2; m++) {
-                    const bf16x8 pb = as_bf16x8(u32x4{ppk[4 * m], ppk[4 * m + 1], ppk[4 * m + 2], ppk[4 * m + 3]});
-                    const int qr1 = 16 * m + 4 * g + tsl2; // query row of the transposing read
-#pragma unroll
-                    for (int db = 0; db < 4; db++) {
-                        const u32x2 d1 = lds_read_tr(&S.dO[swz(qr1, db * 32 + cpart)]);
-                        const u32x2 d2 = lds_read_tr(&S.dO[swz(qr1 + 8, db * 32 + cpart)]);
-                        acc[db] = mfma32(as_bf16x8(u32x4{d1[0], d1[1], d2[0], d2[1]}), pb, acc[db]);
-                    }
-                }
-            } else {
-                float tsum = 0.f;
-                uint32_t dpk[8];
-                if (diag) pointwise_k<TM, DT, true, false>(xacc, pacc, dpk, ln, sm.rabt_rev, sm.rabt, ubias, tsum);
-                else if (TM == 1 && uni)
-                    pointwise_k<TM, DT, false, true>(xacc, pacc, dpk, ln, sm.rabt_rev, sm.rabt, ubias, tsum);
-                else pointwise_k<TM, DT, false, false>(xacc, pacc, dpk, ln, sm.rabt_rev, sm.rabt, ubias, tsum);
-                if (DT && TM == 1 && uni && !diag) {
-                    tsum = wave_sum(tsum);
-                    if (l == 0) sm.dtab[p][0][ubk] += tsum;
-                }
-                // dS -> LDS as [key][query]: lane writes 4 queries (r%4) per r/4 group
-#pragma unroll
-                for (int gr = 0; gr < 4; gr++) {
-                    const u32x2 v2 = {dpk[2 * gr], dpk[2 * gr + 1]};
-                    *(u32x2 *)&dsn[krow * SS + 8 * gr + 4 * g] = v2;
-                }
-                // dK^T += Q^T dS  (contraction over the 32 queries)
-#pragma unroll
-                for (int m = 0; m < 2; m++) {
-                    const bf16x8 sb = as_bf16x8(u32x4{dpk[4 * m], dpk[4 * m + 1], dpk[4 * m + 2], dpk[4 * m + 3]});
-                    const int qr1 = 16 * m + 4 * g + tsl2;
-#pragma unroll
-                    for (int db = 0; db < 4; db++) {
-                        const u32x2 q1 = lds_read_tr(&S.q[swz(qr1, db * 32 + cpart)]);
-                        const u32x2 q2 = lds_read_tr(&S.q[swz(qr1 + 8, db * 32 + cpart)]);
-                        acc[db] = mfma32(as_bf16x8(u32x4{q1[0], q1[1], q2[0], q2[1]}), sb, acc[db]);
-                    }
-                }
+            for (int gr = 0; gr < 4; gr++) {
+                *(u32x2 *)&ptn[krow * SS + 8 * gr + 4 * g] = u32x2{ppk[2 * gr], ppk[2 * gr + 1]};
+                *(u32x2 *)&dsn[krow * SS + 8 * gr + 4 * g] = u32x2{dpk[2 * gr], dpk[2 * gr + 1]};
+            }
+            if (DT && TM == 1 && uni && !diag) {
+                tsum = wave_sum(tsum);
+                if (l == 0) atomicAdd(&sm.dtab[p][0][ubk], tsum);
             }
         } else {
-            if (vwave) {
-                if (MAIN || n > 0) dq_block(sm.ds[(n - 1) & 1], q0 - BQ, MAIN ? true : q0 <= L);
-            } else {
 #pragma unroll
-                for (int gr = 0; gr < 4; gr++) *(u32x2 *)&dsn[krow * SS + 8 * gr + 4 * g] = u32x2{0u, 0u};
+            for (int gr = 0; gr < 4; gr++) *(u32x2 *)&dsn[krow * SS + 8 * gr + 4 * g] = u32x2{0u, 0u};
 #pragma unroll
-                for (int rr = 0; rr < 16; rr++) ln.dsk[-(DKP - 1) * (8 * (rr >> 2) + (rr & 3))] = 0.f;
-            }
+            for (int rr = 0; rr < 16; rr++) ln.dsk[-(DKP - 1) * (8 * (rr >> 2) + (rr & 3))] = 0.f;
         }
-        if (MAIN || n + 1 < nqb) {
-            if (!MAIN && !nfull) load_partial(q0 + BQ, sm.st[(n + 1) & 1]);
-            sstore_tables(sm.st[(n + 1) & 1]);
-        }
-        __builtin_amdgcn_s_waitcnt(0); // direct LDS copies (and everything else) landed
-        __syncthreads();
+        finish(main_c, n);
     };
 
-    if (k0 + BQ <= L) gload_direct(k0, sm.st[0]);
-    else load_partial(k0, sm.st[0]);
-    gload_tables(k0);
-    sstore_tables(sm.st[0]);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
+    // The two roles run separate loops (so that each keeps only its own
+    // registers live) with the same blocks and barriers: generic blocks at
+    // both ends, main blocks in between.
     const std::integral_constant<bool, false> generic{};
     const std::integral_constant<bool, true> fast{};
     const int n_main_end = nqb - 2; // main blocks: [4, nqb - 2)
-    int n = 0;
-    if constexpr (TM == 2) { // sequences with a time span beyond 32 bits: rare, generic path only
-        for (; n < nqb; n++) iteration(generic, n);
-    } else {
-        for (; n < nqb && (n < 4 || n >= n_main_end); n++) iteration(generic, n);
-        for (; n < n_main_end; n++) iteration(fast, n);
-        for (; n < nqb; n++) iteration(generic, n);
-    }
+    auto run = [&](auto body) {
+        int n = 0;
+        if constexpr (TM == 2) { // sequences with a time span beyond 32 bits: rare, generic path only
+            for (; n < nqb; n++) body(generic, n);
+        } else {
+            for (; n < nqb && (n < 4 || n >= n_main_end); n++) body(generic, n);
+            for (; n < n_main_end; n++) body(fast, n);
+            for (; n < nqb; n++) body(generic, n);
+        }
+    };
+    if (awave) run(iter_acc);
+    else run(iter_pw);
 
-    // the last block's dQ and drab_p, then what is left in the ring and the time tables
+    // the last block's dV, dK, dQ and drab_p, then what is left in the ring
+    // and the time tables
     {
         const int qlast = k0 + (nqb - 1) * BQ;
-        if (vwave) {
+        if (awave) {
+            const bool skipm = kw0 > qlast + BQ - 1 || kw0 >= L;
+            if (!skipm) acc_block(sm.sq[(nqb - 1) % 3], (nqb - 1) & 1);
             dq_block(sm.ds[(nqb - 1) & 1], qlast, qlast + BQ <= L);
             if (a.drab_p) {
                 int dlf = 0;
@@ -583,19 +625,21 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
             if (s != 0.f) atomicAdd(&a.drab_t[h * t_hs + tid], s);
         }
     }
-    // dK^T (K wave) or dV^T (V wave): lane holds key mykey, d = 32 db + 8(r/4) + 4g + r%4
-    if (kvalid) {
+    // dV^T and dK^T (accumulating waves): lane holds key mykey, d = 32 db + 8(r/4) + 4g + r%4
+    if (awave && kvalid) {
         const int64_t row = o_b + mykey;
-        bf16 *outp = vwave ? a.dv + row * a.lddv : a.dk + row * a.lddk;
-        const float sc = vwave ? NLN2 : 1.0f;
+        bf16 *dvp = a.dv + row * a.lddv + h * D, *dkp = a.dk + row * a.lddk + h * D;
 #pragma unroll
         for (int db = 0; db < 4; db++)
 #pragma unroll
             for (int gr = 0; gr < 4; gr++) {
                 const int d0 = db * 32 + 8 * gr + 4 * g;
-                const u32x2 vv = {pack2_bf16(sc * acc[db][4 * gr], sc * acc[db][4 * gr + 1]),
-                                  pack2_bf16(sc * acc[db][4 * gr + 2], sc * acc[db][4 * gr + 3])};
-                *(u32x2 *)(outp + h * D + d0) = vv;
+                const u32x2 vv = {pack2_bf16(NLN2 * acc[db][4 * gr], NLN2 * acc[db][4 * gr + 1]),
+                                  pack2_bf16(NLN2 * acc[db][4 * gr + 2], NLN2 * acc[db][4 * gr + 3])};
+                const u32x2 kk = {pack2_bf16(acc2[db][4 * gr], acc2[db][4 * gr + 1]),
+                                  pack2_bf16(acc2[db][4 * gr + 2], acc2[db][4 * gr + 3])};
+                *(u32x2 *)(dvp + d0) = vv;
+                *(u32x2 *)(dkp + d0) = kk;
             }
     }
 }
