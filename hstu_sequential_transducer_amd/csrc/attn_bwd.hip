@@ -130,24 +130,37 @@ struct BwdLane {
     int dmask;            // masked (key > query) iff cr < dmask  (diagonal blocks)
 };
 
+// Time-bias modes of a 32x32 block (TM == 1): generic (per-element bucket
+// and table lookup), one bucket for every pair (a scalar bias), or two
+// adjacent buckets (per-element choice between two scalars, threshold
+// 2^(blo + 1) on |dt| + 1).
+enum { TB_ANY = 0, TB_ONE = 1, TB_TWO = 2 };
+
 // x' = -log2(e) x for register r of the X accumulator (which holds x minus
-// the time bias; time tables are staged pre-scaled), and the time bucket.
-template <int TM, bool UNI>
+// the time bias; time tables are staged pre-scaled), the time bucket (TB_ANY)
+// or whether the pair is in the upper bucket (TB_TWO).
+template <int TM, int UB>
 DEV float xprime(const floatx16 &xacc, int rr, const BwdLane &ln, const float *rabt_rev, const float *rabt,
-                 float ubias, int &bucket)
+                 float ubias, float ubias2, uint32_t thr, int &bucket, bool &upper)
 {
     const int cr = 8 * (rr >> 2) + (rr & 3);
     float tb = 0.f;
     bucket = 0;
+    upper = false;
     if constexpr (TM == 1) {
-        if constexpr (UNI) {
+        if constexpr (UB == TB_ONE) {
             tb = ubias;
         } else {
             const uint32_t tq = ln.qt[cr];
             const uint32_t dd1 = (tq > ln.tk ? tq - ln.tk : ln.tk - tq) + 1u;
-            const int cz = __builtin_clz(dd1);
-            tb = rabt_rev[cz];
-            bucket = 31 - cz;
+            if constexpr (UB == TB_TWO) {
+                upper = dd1 >= thr;
+                tb = upper ? ubias2 : ubias;
+            } else {
+                const int cz = __builtin_clz(dd1);
+                tb = rabt_rev[cz];
+                bucket = 31 - cz;
+            }
         }
     } else if constexpr (TM == 2) {
         bucket = time_bucket64(ln.qt64[cr] - ln.tk64);
@@ -159,11 +172,14 @@ DEV float xprime(const floatx16 &xacc, int rr, const BwdLane &ln, const float *r
 // Pointwise wave, one 32x32 block: P' = x' sigmoid(x) = -log2(e) SiLU(x)
 // (the -ln 2 goes into dV's final scale) and dS = dP sg (1 + x (1 - sg)) =
 // dP (sg - ln2 (p' - p' sg)), both packed to bf16; fp32 dS also into the
-// skewed tile and into drab_t.  Register r <-> query 4g + cr(r),
+// skewed tile and into drab_t (TB_ONE: the lane's sum in tsum; TB_TWO: the
+// lane's total in tsum and its upper-bucket part in tsum2; TB_ANY: LDS
+// atomics into the wave's tables).  Register r <-> query 4g + cr(r),
 // cr = 8(r/4) + r%4; this lane's key.
-template <int TM, bool DT, bool DIAG, bool UNI>
+template <int TM, bool DT, bool DIAG, int UB>
 DEV void pointwise(const floatx16 &xacc, const floatx16 &pacc, uint32_t (&ppk)[8], uint32_t (&dpk)[8],
-                   const BwdLane &ln, const float *rabt_rev, const float *rabt, float ubias, float &tsum)
+                   const BwdLane &ln, const float *rabt_rev, const float *rabt, float ubias, float ubias2,
+                   uint32_t thr, float &tsum, float &tsum2)
 {
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
@@ -172,7 +188,8 @@ DEV void pointwise(const floatx16 &xacc, const floatx16 &pacc, uint32_t (&ppk)[8
         for (int u = 0; u < 2; u++) {
             const int rr = r + u, cr = 8 * (rr >> 2) + (rr & 3);
             int bucket;
-            const float x = xprime<TM, UNI>(xacc, rr, ln, rabt_rev, rabt, ubias, bucket);
+            bool upper;
+            const float x = xprime<TM, UB>(xacc, rr, ln, rabt_rev, rabt, ubias, ubias2, thr, bucket, upper);
             const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x));
             float p = x * sg;
             const float t = __builtin_fmaf(-p, sg, p);
@@ -185,13 +202,39 @@ DEV void pointwise(const floatx16 &xacc, const floatx16 &pacc, uint32_t (&ppk)[8
             dd[u] = ds;
             ln.dsk[-(DKP - 1) * cr] = ds;
             if constexpr (DT && TM != 0) {
-                if constexpr (UNI) tsum += ds;
-                else atomicAdd(&ln.dtab[bucket], ds);
+                if constexpr (UB == TB_ONE) {
+                    tsum += ds;
+                } else if constexpr (UB == TB_TWO) {
+                    tsum += ds;
+                    tsum2 += upper ? ds : 0.f;
+                } else {
+                    atomicAdd(&ln.dtab[bucket], ds);
+                }
             }
         }
         ppk[r >> 1] = pack2_bf16(pp[0], pp[1]);
         dpk[r >> 1] = pack2_bf16(dd[0], dd[1]);
     }
+}
+
+// Sum over the 64 lanes with DPP moves inside each row of 16 lanes and four
+// lane reads (no LDS traffic); the result is wave-uniform.
+template <int CTRL>
+DEV float dpp_mov(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+DEV float wave_sum_dpp(float v)
+{
+    v += dpp_mov<0xB1>(v);  // quad_perm [1,0,3,2]
+    v += dpp_mov<0x4E>(v);  // quad_perm [2,3,0,1]
+    v += dpp_mov<0x141>(v); // row_half_mirror
+    v += dpp_mov<0x140>(v); // row_mirror: every lane holds its row's sum
+    const int b = __builtin_bit_cast(int, v);
+    return (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0)) +
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16))) +
+           (__builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32)) +
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48)));
 }
 
 // 16-byte slice o..o+3 of a register block as a bf16x8 MFMA operand.  (Each
@@ -289,10 +332,12 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
     float wreg = 0.f;
     uint32_t treg = 0, tmn = 0xFFFFFFFFu, tmx = 0u;
     int64_t treg64 = 0;
-    auto gload_direct = [&](int q0, StageQ &SQ, StageP &SP) {
+    // nw waves share the 24 copies; wi = this wave's index among them.
+    auto gload_direct = [&](auto nw_c, int wi, int q0, StageQ &SQ, StageP &SP) {
+        constexpr int NWC = decltype(nw_c)::value;
 #pragma unroll
-        for (int i = 0; i < 24 / NW; i++) {
-            const int G = (24 / NW) * w + i, plane = G >> 3, r0 = 4 * (G & 7);
+        for (int i = 0; i < 24 / NWC; i++) {
+            const int G = (24 / NWC) * wi + i, plane = G >> 3, r0 = 4 * (G & 7);
             const int row = r0 + (l >> 4);
             const int c = (l & 15) ^ swf(row);
             const int64_t grow = (int64_t)(o_b + q0 + row);
@@ -350,7 +395,9 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
     };
 
     // stage 0, then the K tile's d-block p into the accumulating waves' registers
-    if (k0 + BQ <= L) gload_direct(k0, sm.sq[0], sm.sp[0]);
+    const std::integral_constant<int, NW> all_waves{};
+    const std::integral_constant<int, NW / 2> half_waves{};
+    if (k0 + BQ <= L) gload_direct(all_waves, w, k0, sm.sq[0], sm.sp[0]);
     else load_partial(k0, sm.sq[0], sm.sp[0]);
     gload_tables(k0);
     sstore_tables(sm.sp[0]);
@@ -380,25 +427,45 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
     auto acc_block = [&](const StageQ &SQ, int b) {
         const bf16 *ptb = sm.pt[b], *dsb = sm.ds[b];
         const int krow = 32 * p + lq;
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 pb[2], sb[2];
 #pragma unroll
         for (int m = 0; m < 2; m++) {
             const u32x2 p1 = *(const u32x2 *)&ptb[krow * SS + 16 * m + 4 * g];
             const u32x2 p2 = *(const u32x2 *)&ptb[krow * SS + 16 * m + 8 + 4 * g];
             const u32x2 s1 = *(const u32x2 *)&dsb[krow * SS + 16 * m + 4 * g];
             const u32x2 s2 = *(const u32x2 *)&dsb[krow * SS + 16 * m + 8 + 4 * g];
-            const bf16x8 pb = as_bf16x8(u32x4{p1[0], p1[1], p2[0], p2[1]});
-            const bf16x8 sb = as_bf16x8(u32x4{s1[0], s1[1], s2[0], s2[1]});
-            const int qr1 = 16 * m + 4 * g + tsl; // query row of the transposing read
-#pragma unroll
-            for (int db = 0; db < 4; db++) {
-                const u32x2 d1 = lds_read_tr(&SQ.dO[swz(qr1, db * 32 + cpart)]);
-                const u32x2 d2 = lds_read_tr(&SQ.dO[swz(qr1 + 8, db * 32 + cpart)]);
-                acc[db] = mfma32(as_bf16x8(u32x4{d1[0], d1[1], d2[0], d2[1]}), pb, acc[db]);
-                const u32x2 q1 = lds_read_tr(&SQ.q[swz(qr1, db * 32 + cpart)]);
-                const u32x2 q2 = lds_read_tr(&SQ.q[swz(qr1 + 8, db * 32 + cpart)]);
-                acc2[db] = mfma32(as_bf16x8(u32x4{q1[0], q1[1], q2[0], q2[1]}), sb, acc2[db]);
-            }
+            pb[m] = as_bf16x8(u32x4{p1[0], p1[1], p2[0], p2[1]});
+            sb[m] = as_bf16x8(u32x4{s1[0], s1[1], s2[0], s2[1]});
         }
+        // 16 steps j: m = j / 8, db = (j / 2) % 4; even j: dO'^T slice -> dV, odd j:
+        // Q^T slice -> dK.  Transposing reads run three steps ahead.
+        bf16x8 fa[4];
+        auto fetch = [&](int j) {
+            const int m = j >> 3, db = (j >> 1) & 3;
+            const int qr1 = 16 * m + 4 * g + tsl; // query row of the transposing read
+            const bf16 *t = (j & 1) ? SQ.q : SQ.dO;
+            const u32x2 a1 = lds_read_tr(&t[swz(qr1, db * 32 + cpart)]);
+            const u32x2 a2 = lds_read_tr(&t[swz(qr1 + 8, db * 32 + cpart)]);
+            fa[j & 3] = as_bf16x8(u32x4{a1[0], a1[1], a2[0], a2[1]});
+        };
+        fetch(0);
+        fetch(1);
+        fetch(2);
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+            if (j + 3 < 16) fetch(j + 3);
+            const int m = j >> 3, db = (j >> 1) & 3;
+            if (j & 1) acc2[db] = mfma32(fa[j & 3], sb[m], acc2[db]);
+            else acc[db] = mfma32(fa[j & 3], pb[m], acc[db]);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 14, 0); // B operands and the first three steps
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+            if (j + 3 < 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
     };
     // Accumulating wave: dQ of the block at q0m from the dS tile `dst` (all
     // 128 keys): dQ[32 queries][d-block p] = sum over the keys of dS[q][key] K[key][d]
@@ -406,13 +473,29 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
         floatx16 qacc;
 #pragma unroll
         for (int r = 0; r < 16; r++) qacc[r] = 0.f;
-#pragma unroll
-        for (int t = 0; t < BN / 16; t++) {
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 fs[4];
+        auto fetch = [&](int t) {
             const int kr1 = 16 * t + 8 * g + tsl;
             const u32x2 s1 = lds_read_tr(&dst[kr1 * SS + cpart]);
             const u32x2 s2 = lds_read_tr(&dst[(kr1 + 4) * SS + cpart]);
-            qacc = mfma32(as_bf16x8(u32x4{s1[0], s1[1], s2[0], s2[1]}), opnd[t], qacc);
+            fs[t & 3] = as_bf16x8(u32x4{s1[0], s1[1], s2[0], s2[1]});
+        };
+        fetch(0);
+        fetch(1);
+        fetch(2);
+#pragma unroll
+        for (int t = 0; t < BN / 16; t++) {
+            if (t + 3 < BN / 16) fetch(t + 3);
+            qacc = mfma32(fs[t & 3], opnd[t], qacc);
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+        for (int t = 0; t < BN / 16; t++) {
+            if (t + 3 < BN / 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
         // C layout: lane holds d = 32p + lq, queries 8(r/4) + 4g + r%4
         float *dqp = a.dq_acc + (int64_t)(o_b + q0m + 4 * g) * ld_do + h * D + 32 * p + lq;
         if (full) {
@@ -458,45 +541,53 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
     // are full), compiled without the per-block checks.
     const int nqb = (L - k0 + BQ - 1) / BQ; // query blocks [k0, L); >= 1
     const int krow = 32 * p + lq;
-    // What every wave does at the end of block n: the tables (and, for a
-    // partial next block, the register path) of block n + 1, then the wait
-    // for the direct copies and the barrier.
-    auto finish = [&](auto main_c, int n) {
+    // What every wave does at the end of block n: for a partial next block,
+    // the register path of its stage; then the wait and the barrier.  The
+    // pointwise waves wait for their direct copies; the accumulating waves
+    // only for their LDS traffic (their dQ atomics stay in flight).
+    auto finish = [&](auto main_c, int n, bool copies) {
         constexpr bool MAIN = decltype(main_c)::value;
         const int q0 = k0 + n * BQ;
-        if (MAIN || n + 1 < nqb) {
+        if (!MAIN && n + 1 < nqb && q0 + 2 * BQ > L) {
             const int n3 = n % 3 == 2 ? 0 : n % 3 + 1;
-            if (!MAIN && q0 + 2 * BQ > L) load_partial(q0 + BQ, sm.sq[n3], sm.sp[(n + 1) & 1]);
-            sstore_tables(sm.sp[(n + 1) & 1]);
+            load_partial(q0 + BQ, sm.sq[n3], sm.sp[(n + 1) & 1]);
         }
-        __builtin_amdgcn_s_waitcnt(0); // direct LDS copies (and everything else) landed
+        if (copies || (!MAIN && n + 1 < nqb && q0 + 2 * BQ > L)) __builtin_amdgcn_s_waitcnt(0);
+        else __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0)
         __syncthreads();
     };
+    // The next block's direct copies, issued by the pointwise waves (the
+    // accumulating waves' transposing LDS reads would otherwise wait for them).
     auto start_copy = [&](auto main_c, int n) {
         constexpr bool MAIN = decltype(main_c)::value;
         const int q0 = k0 + n * BQ;
         const int n3 = n % 3 == 2 ? 0 : n % 3 + 1;
-        if (MAIN) gload_direct(q0 + BQ, sm.sq[n3], sm.sp[(n + 1) & 1]);
-        else if (n + 1 < nqb && q0 + 2 * BQ <= L) gload_direct(q0 + BQ, sm.sq[n3], sm.sp[(n + 1) & 1]);
+        if (MAIN) gload_direct(half_waves, w - NW / 2, q0 + BQ, sm.sq[n3], sm.sp[(n + 1) & 1]);
+        else if (n + 1 < nqb && q0 + 2 * BQ <= L)
+            gload_direct(half_waves, w - NW / 2, q0 + BQ, sm.sq[n3], sm.sp[(n + 1) & 1]);
     };
     // Accumulating wave, block n: the previous block's dV, dK, dQ and drab_p.
     auto iter_acc = [&](auto main_c, int n) {
         constexpr bool MAIN = decltype(main_c)::value;
         const int q0 = k0 + n * BQ;
-        start_copy(main_c, n);
+        if (MAIN) gload_tables(q0 + BQ);
+        else if (n + 1 < nqb) gload_tables(q0 + BQ);
         int dlf = 0;
         float tot = 0.f;
+        const int q0m = q0 - BQ;
         if (MAIN || n > 0) {
-            const int q0m = q0 - BQ;
             const bool skipm = MAIN ? false : (kw0 > q0m + BQ - 1 || kw0 >= L);
             if (!skipm) acc_block(sm.sq[n % 3 == 0 ? 2 : n % 3 - 1], (n - 1) & 1);
+        }
+        // the next block's tables go to LDS before this block's dQ atomics
+        // are issued (a wait for the table loads then covers no atomics)
+        if (MAIN || n + 1 < nqb) sstore_tables(sm.sp[(n + 1) & 1]);
+        if (MAIN || n > 0) {
             dq_block(sm.ds[(n - 1) & 1], q0m, MAIN ? true : q0 <= L);
             if (a.drab_p) drabp_sum(sm.dsk[(n - 1) & 1], q0m, tot, dlf);
         }
-        if (MAIN) gload_tables(q0 + BQ);
-        else if (n + 1 < nqb) gload_tables(q0 + BQ);
         if ((MAIN || n > 0) && a.drab_p) drabp_flush(dlf, tot);
-        finish(main_c, n);
+        finish(main_c, n, false);
     };
     // Pointwise wave, block n: X, dP, P', dS.
     auto iter_pw = [&](auto main_c, int n) {
@@ -510,29 +601,51 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
         ln.dsk = sm.dsk[n & 1] + (krow + (BQ - 1) - 4 * g) * DKP + 4 * g;
         bf16 *dsn = sm.ds[n & 1], *ptn = sm.pt[n & 1];
         if (!skip) {
-            // X = Q K^T + rab_p window; dP = dO' V^T (hi + lo planes)
-            floatx16 xacc, pacc;
+            // X = Q K^T + rab_p window; dP = dO' V^T (hi + lo planes).  The
+            // operand reads run two steps ahead of the MFMAs (pinned with
+            // scheduling groups); the window is added after the products.
+            floatx16 xacc, pacc, wacc;
 #pragma unroll
             for (int r = 0; r < 16; r++) {
                 const int cr = 8 * (r >> 2) + (r & 3);
-                xacc[r] = HP ? SPn.win[krow + (BQ - 1) - 4 * g - cr] : 0.f;
-                pacc[r] = 0.f;
+                wacc[r] = HP ? SPn.win[krow + (BQ - 1) - 4 * g - cr] : 0.f;
+                xacc[r] = pacc[r] = 0.f;
             }
+            __builtin_amdgcn_sched_barrier(0);
+            {
+                bf16x8 fq[3], fd[3], fl[3];
+                auto fetch = [&](int s) {
+                    const int o = swz(lq, s * 16 + g * 8);
+                    fq[s % 3] = *(const bf16x8 *)&SQn.q[o];
+                    fd[s % 3] = *(const bf16x8 *)&SQn.dO[o];
+                    fl[s % 3] = *(const bf16x8 *)&SPn.dOl[o];
+                };
+                fetch(0);
+                fetch(1);
 #pragma unroll
-            for (int s = 0; s < 8; s++) {
-                const int o = swz(lq, s * 16 + g * 8);
-                xacc = mfma32(*(const bf16x8 *)&SQn.q[o], slice8(acc2[s >> 1], 4 * (s & 1)), xacc);
-                pacc = mfma32(*(const bf16x8 *)&SQn.dO[o], slice8(acc2[s >> 1], 8 + 4 * (s & 1)), pacc);
-                pacc = mfma32(*(const bf16x8 *)&SPn.dOl[o], slice8(acc2[s >> 1], 8 + 4 * (s & 1)), pacc);
+                for (int s = 0; s < 8; s++) {
+                    if (s + 2 < 8) fetch(s + 2);
+                    xacc = mfma32(fq[s % 3], slice8(acc2[s >> 1], 4 * (s & 1)), xacc);
+                    pacc = mfma32(fd[s % 3], slice8(acc2[s >> 1], 8 + 4 * (s & 1)), pacc);
+                    pacc = mfma32(fl[s % 3], slice8(acc2[s >> 1], 8 + 4 * (s & 1)), pacc);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x100, 6, 0); // DS reads of steps 0, 1
+#pragma unroll
+                for (int s = 0; s < 8; s++) {
+                    if (s + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0); // reads of step s + 2
+                    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);                 // MFMAs of step s
+                }
             }
+            __builtin_amdgcn_sched_barrier(0);
+            xacc += wacc;
             ln.qt = &SPn.qt[4 * g];
             ln.qt64 = &SPn.qt64[4 * g];
             ln.dmask = kw0 + lq - q0 - 4 * g; // key > query  <=>  cr < dmask
-            bool uni = false;
-            int ubk = 0;
+            int ubk = 0, nbk = 0; // the block's lowest time bucket; its number of buckets - 1
             if constexpr (TM == 1) {
-                // all pairs in one bucket iff floor(log2(min|dt| + 1)) == floor(log2(max|dt| + 1));
+                // bucket range from floor(log2(min|dt| + 1)) and floor(log2(max|dt| + 1));
                 // relative times of one non-wide sequence differ by less than 2^32 - 1
+                nbk = 2;
                 const uint32_t qa = __builtin_amdgcn_readfirstlane(SPn.qtmin);
                 const uint32_t qb = __builtin_amdgcn_readfirstlane(SPn.qtmax);
                 if (qa <= qb && tkmin <= tkmax) {
@@ -540,26 +653,37 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
                     const uint32_t h1 = qb > tkmin ? qb - tkmin : 0u, h2 = tkmax > qa ? tkmax - qa : 0u;
                     const uint32_t hi = h1 > h2 ? h1 : h2;
                     const int blo = floor_log2_u32(lo + 1u), bhi = floor_log2_u32(hi + 1u);
-                    uni = blo == bhi;
                     ubk = blo;
+                    nbk = bhi - blo;
                 }
             }
-            const float ubias = sm.rabt[ubk];
-            float tsum = 0.f;
+            const float ubias = sm.rabt[ubk], ubias2 = sm.rabt[ubk + 1]; // ubk <= 31
+            const uint32_t thr = ubk < 31 ? 2u << ubk : 0xFFFFFFFFu;      // 2^(ubk + 1)
+            float tsum = 0.f, tsum2 = 0.f;
             uint32_t ppk[8], dpk[8];
-            if (diag) pointwise<TM, DT, true, false>(xacc, pacc, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, tsum);
-            else if (TM == 1 && uni)
-                pointwise<TM, DT, false, true>(xacc, pacc, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, tsum);
-            else pointwise<TM, DT, false, false>(xacc, pacc, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, tsum);
+            if (diag)
+                pointwise<TM, DT, true, TB_ANY>(xacc, pacc, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, ubias2, thr, tsum, tsum2);
+            else if (TM == 1 && nbk == 0)
+                pointwise<TM, DT, false, TB_ONE>(xacc, pacc, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, ubias2, thr, tsum, tsum2);
+            else if (TM == 1 && nbk == 1)
+                pointwise<TM, DT, false, TB_TWO>(xacc, pacc, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, ubias2, thr, tsum, tsum2);
+            else
+                pointwise<TM, DT, false, TB_ANY>(xacc, pacc, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, ubias2, thr, tsum, tsum2);
             // P' and dS -> LDS as [key][query]: lane writes 4 queries (r%4) per r/4 group
 #pragma unroll
             for (int gr = 0; gr < 4; gr++) {
                 *(u32x2 *)&ptn[krow * SS + 8 * gr + 4 * g] = u32x2{ppk[2 * gr], ppk[2 * gr + 1]};
                 *(u32x2 *)&dsn[krow * SS + 8 * gr + 4 * g] = u32x2{dpk[2 * gr], dpk[2 * gr + 1]};
             }
-            if (DT && TM == 1 && uni && !diag) {
-                tsum = wave_sum(tsum);
-                if (l == 0) atomicAdd(&sm.dtab[p][0][ubk], tsum);
+            // the block's drab_t sums: plain read-modify-write by lane 0 of this wave's
+            // own table (an LDS atomic would wait for the block copies in flight)
+            if (DT && TM == 1 && nbk <= 1 && !diag) {
+                const float s_all = wave_sum_dpp(tsum);
+                const float s_up = nbk == 1 ? wave_sum_dpp(tsum2) : 0.f;
+                if (l == 0) {
+                    sm.dtab[p][0][ubk] += s_all - s_up;
+                    if (nbk == 1) sm.dtab[p][0][ubk + 1] += s_up;
+                }
             }
         } else {
 #pragma unroll
@@ -567,7 +691,7 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
 #pragma unroll
             for (int rr = 0; rr < 16; rr++) ln.dsk[-(DKP - 1) * (8 * (rr >> 2) + (rr & 3))] = 0.f;
         }
-        finish(main_c, n);
+        finish(main_c, n, true);
     };
 
     // The two roles run separate loops (so that each keeps only its own
@@ -586,34 +710,51 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
             for (; n < nqb; n++) body(generic, n);
         }
     };
-    if (awave) run(iter_acc);
-    else run(iter_pw);
-
-    // the last block's dV, dK, dQ and drab_p, then what is left in the ring
-    // and the time tables
-    {
-        const int qlast = k0 + (nqb - 1) * BQ;
-        if (awave) {
-            const bool skipm = kw0 > qlast + BQ - 1 || kw0 >= L;
-            if (!skipm) acc_block(sm.sq[(nqb - 1) % 3], (nqb - 1) & 1);
-            dq_block(sm.ds[(nqb - 1) & 1], qlast, qlast + BQ <= L);
-            if (a.drab_p) {
-                int dlf = 0;
-                float tot = 0.f;
-                drabp_sum(sm.dsk[(nqb - 1) & 1], qlast, tot, dlf);
-                drabp_flush(dlf, tot);
-            }
-        }
-        __syncthreads();
+    const int qlast = k0 + (nqb - 1) * BQ;
+    if (awave) {
+        run(iter_acc);
+        // the last block's dV, dK, dQ and drab_p, then dV^T and dK^T: lane
+        // holds key mykey, d = 32 db + 8(r/4) + 4g + r%4 (stored here so that
+        // the accumulators are dead on the pointwise waves' path)
+        const bool skipm = kw0 > qlast + BQ - 1 || kw0 >= L;
+        if (!skipm) acc_block(sm.sq[(nqb - 1) % 3], (nqb - 1) & 1);
+        dq_block(sm.ds[(nqb - 1) & 1], qlast, qlast + BQ <= L);
         if (a.drab_p) {
-            // remaining key - query values: [k0 - qlast - (BQ - 1), k0 + BN - 1 - qlast - BQ]
-            const int lo = k0 - qlast - (BQ - 1), hi = k0 + BN - 1 - qlast - BQ;
-            for (int dl = lo + tid; dl <= hi; dl += NT) {
-                const float v = sm.ring[dl & (RING - 1)];
-                if (v != 0.f) {
-                    const int cl = dl < -a.N ? -a.N : (dl > a.N ? a.N : dl);
-                    atomicAdd(&a.drab_p[h * p_hs + cl + a.N], v);
+            int dlf = 0;
+            float tot = 0.f;
+            drabp_sum(sm.dsk[(nqb - 1) & 1], qlast, tot, dlf);
+            drabp_flush(dlf, tot);
+        }
+        if (kvalid) {
+            const int64_t row = o_b + mykey;
+            bf16 *dvp = a.dv + row * a.lddv + h * D, *dkp = a.dk + row * a.lddk + h * D;
+#pragma unroll
+            for (int db = 0; db < 4; db++)
+#pragma unroll
+                for (int gr = 0; gr < 4; gr++) {
+                    const int d0 = db * 32 + 8 * gr + 4 * g;
+                    const u32x2 vv = {pack2_bf16(NLN2 * acc[db][4 * gr], NLN2 * acc[db][4 * gr + 1]),
+                                      pack2_bf16(NLN2 * acc[db][4 * gr + 2], NLN2 * acc[db][4 * gr + 3])};
+                    const u32x2 kk = {pack2_bf16(acc2[db][4 * gr], acc2[db][4 * gr + 1]),
+                                      pack2_bf16(acc2[db][4 * gr + 2], acc2[db][4 * gr + 3])};
+                    *(u32x2 *)(dvp + d0) = vv;
+                    *(u32x2 *)(dkp + d0) = kk;
                 }
+        }
+    } else {
+        run(iter_pw);
+    }
+
+    // what is left in the ring and the time tables
+    __syncthreads();
+    if (a.drab_p) {
+        // remaining key - query values: [k0 - qlast - (BQ - 1), k0 + BN - 1 - qlast - BQ]
+        const int lo = k0 - qlast - (BQ - 1), hi = k0 + BN - 1 - qlast - BQ;
+        for (int dl = lo + tid; dl <= hi; dl += NT) {
+            const float v = sm.ring[dl & (RING - 1)];
+            if (v != 0.f) {
+                const int cl = dl < -a.N ? -a.N : (dl > a.N ? a.N : dl);
+                atomicAdd(&a.drab_p[h * p_hs + cl + a.N], v);
             }
         }
     }
@@ -624,23 +765,6 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
                 for (int c = 0; c < TCOPY; c++) s += sm.dtab[pp][c][tid];
             if (s != 0.f) atomicAdd(&a.drab_t[h * t_hs + tid], s);
         }
-    }
-    // dV^T and dK^T (accumulating waves): lane holds key mykey, d = 32 db + 8(r/4) + 4g + r%4
-    if (awave && kvalid) {
-        const int64_t row = o_b + mykey;
-        bf16 *dvp = a.dv + row * a.lddv + h * D, *dkp = a.dk + row * a.lddk + h * D;
-#pragma unroll
-        for (int db = 0; db < 4; db++)
-#pragma unroll
-            for (int gr = 0; gr < 4; gr++) {
-                const int d0 = db * 32 + 8 * gr + 4 * g;
-                const u32x2 vv = {pack2_bf16(NLN2 * acc[db][4 * gr], NLN2 * acc[db][4 * gr + 1]),
-                                  pack2_bf16(NLN2 * acc[db][4 * gr + 2], NLN2 * acc[db][4 * gr + 3])};
-                const u32x2 kk = {pack2_bf16(acc2[db][4 * gr], acc2[db][4 * gr + 1]),
-                                  pack2_bf16(acc2[db][4 * gr + 2], acc2[db][4 * gr + 3])};
-                *(u32x2 *)(dvp + d0) = vv;
-                *(u32x2 *)(dkp + d0) = kk;
-            }
     }
 }
 
