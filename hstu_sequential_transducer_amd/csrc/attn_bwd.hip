@@ -79,8 +79,9 @@ struct alignas(16) StageP {
     alignas(16) bf16 dOl[BQ * D]; // low part of dO' (dO' = dO + dOl to ~16 bits)
     float win[WIN];               // rab_p[clip(key - query)], slot = key - query + BQ - 1 - (k0 - q0)
     uint32_t qt[BQ];
+    uint32_t qtmin, qtmax;        // over the block's valid queries (right after qt: one copy fills both)
+    uint32_t pad_[2];
     int64_t qt64[BQ];
-    uint32_t qtmin, qtmax;        // over the block's valid queries
 };
 struct alignas(16) Smem {
     StageQ sq[3];
@@ -176,43 +177,76 @@ DEV float xprime(const floatx16 &xacc, int rr, const BwdLane &ln, const float *r
 // lane's total in tsum and its upper-bucket part in tsum2; TB_ANY: LDS
 // atomics into the wave's tables).  Register r <-> query 4g + cr(r),
 // cr = 8(r/4) + r%4; this lane's key.
-template <int TM, bool DT, bool DIAG, int UB>
-DEV void pointwise(const floatx16 &xacc, const floatx16 &pacc, uint32_t (&ppk)[8], uint32_t (&dpk)[8],
+//
+// The part that needs only X (P' and the factor multiplying dP, which
+// replaces x in xacc) runs first, two elements per step, while dp_step(s)
+// issues step s of the dP = dO' V^T products (pacc, updated through the
+// functor); then dS = dP * factor.
+template <int TM, bool DT, bool DIAG, int UB, typename DpStep>
+DEV void pointwise(floatx16 &xacc, const floatx16 &pacc, DpStep &&dp_step, uint32_t (&ppk)[8], uint32_t (&dpk)[8],
                    const BwdLane &ln, const float *rabt_rev, const float *rabt, float ubias, float ubias2,
                    uint32_t thr, float &tsum, float &tsum2)
 {
+    floatx16 &fac = xacc; // each element's factor replaces its x
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-        float pp[2], dd[2];
+    for (int s = 0; s < 8; s++) {
+        dp_step(s);
+        float pp[2];
 #pragma unroll
         for (int u = 0; u < 2; u++) {
-            const int rr = r + u, cr = 8 * (rr >> 2) + (rr & 3);
+            const int rr = 2 * s + u, cr = 8 * (rr >> 2) + (rr & 3);
             int bucket;
             bool upper;
             const float x = xprime<TM, UB>(xacc, rr, ln, rabt_rev, rabt, ubias, ubias2, thr, bucket, upper);
             const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x));
             float p = x * sg;
-            const float t = __builtin_fmaf(-p, sg, p);
-            float ds = pacc[rr] * __builtin_fmaf(t, NLN2, sg);
+            float f = __builtin_fmaf(__builtin_fmaf(-p, sg, p), NLN2, sg);
             if constexpr (DIAG) {
                 p = cr < ln.dmask ? 0.f : p;
-                ds = cr < ln.dmask ? 0.f : ds;
+                f = cr < ln.dmask ? 0.f : f;
             }
             pp[u] = p;
+            fac[rr] = f;
+        }
+        ppk[s] = pack2_bf16(pp[0], pp[1]);
+    }
+    if constexpr (UB == TB_ONE && !DIAG) {
+        // per step: the MFMAs of step s among the VALU work of its two elements
+#pragma unroll
+        for (int s = 0; s < 8; s++) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+            if (s + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+        float dd[2];
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+            const int rr = r + u, cr = 8 * (rr >> 2) + (rr & 3);
+            const float ds = pacc[rr] * fac[rr];
             dd[u] = ds;
             ln.dsk[-(DKP - 1) * cr] = ds;
             if constexpr (DT && TM != 0) {
                 if constexpr (UB == TB_ONE) {
                     tsum += ds;
-                } else if constexpr (UB == TB_TWO) {
-                    tsum += ds;
-                    tsum2 += upper ? ds : 0.f;
                 } else {
-                    atomicAdd(&ln.dtab[bucket], ds);
+                    int bucket;
+                    bool upper;
+                    (void)xprime<TM, UB>(xacc, rr, ln, rabt_rev, rabt, ubias, ubias2, thr, bucket, upper);
+                    if constexpr (UB == TB_TWO) {
+                        tsum += ds;
+                        tsum2 += upper ? ds : 0.f;
+                    } else {
+                        atomicAdd(&ln.dtab[bucket], ds);
+                    }
                 }
             }
         }
-        ppk[r >> 1] = pack2_bf16(pp[0], pp[1]);
         dpk[r >> 1] = pack2_bf16(dd[0], dd[1]);
     }
 }
@@ -346,18 +380,19 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
             __builtin_amdgcn_global_load_lds((const void *)(src + h * D + c * 8), (lds_void *)dst, 16, 0, 0);
         }
     };
-    auto gload_tables = [&](int q0) {
+    // Per-block tables, loaded and stored by the threads tt = 0.. of one role.
+    auto gload_tables = [&](int q0, int tt) {
         if constexpr (HP) {
-            if (tid < WIN) {
-                int dl = k0 - q0 - (BQ - 1) + tid; // key - query of window slot tid
+            if (tt >= 0 && tt < WIN) {
+                int dl = k0 - q0 - (BQ - 1) + tt; // key - query of window slot tt
                 dl = dl < -a.N ? -a.N : (dl > a.N ? a.N : dl);
                 wreg = a.rab_p[h * a.rp_hs + dl + a.N];
             }
         }
         if constexpr (TM != 0) {
-            if (tid < 64) { // wave 0: query times and (precomputed) their range
-                const int q = q0 + tid;
-                const bool okq = tid < BQ && q < L;
+            if (tt >= 0 && tt < 64) { // one wave: query times and (precomputed) their range
+                const int q = q0 + tt;
+                const bool okq = tt < BQ && q < L;
                 treg = (TM == 1 && okq) ? a.rel[o_b + q] : 0u;
                 treg64 = (TM == 2 && okq) ? a.ts[o_b + q] : 0;
                 if constexpr (TM == 1) {
@@ -379,17 +414,39 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
         *(u32x4 *)&SQ.dO[swz(lcq, col)] = dv;
         *(u32x4 *)&SP.dOl[swz(lcq, col)] = lv;
     };
-    auto sstore_tables = [&](StageP &S) {
+    auto sstore_tables = [&](StageP &S, int tt) {
         if constexpr (HP)
-            if (tid < WIN) S.win[tid] = wreg;
+            if (tt >= 0 && tt < WIN) S.win[tt] = wreg;
         if constexpr (TM != 0) {
-            if (tid < BQ) {
-                S.qt[tid] = treg;
-                S.qt64[tid] = treg64;
+            if (tt >= 0 && tt < BQ) {
+                S.qt[tt] = treg;
+                S.qt64[tt] = treg64;
             }
-            if (tid == 0) {
+            if (tt == 0) {
                 S.qtmin = tmn;
                 S.qtmax = tmx;
+            }
+        }
+    };
+
+    // A full block's tables copied straight into LDS by the pointwise waves
+    // (4-byte copies, lane i -> 4i bytes past the wave's LDS base): the
+    // window by waves 0-2 of the role (slots 64 pw + lane), the query times
+    // and their range by wave 3 (lanes 0-31, then 32, 33).
+    auto gload_tables_direct = [&](int q0, StageP &SP) {
+        const int pw = w - NW / 2;
+        if constexpr (HP) {
+            if (pw < 3 && 64 * pw + l < WIN) {
+                int dl = k0 - q0 - (BQ - 1) + 64 * pw + l;
+                dl = dl < -a.N ? -a.N : (dl > a.N ? a.N : dl);
+                __builtin_amdgcn_global_load_lds((const void *)(a.rab_p + h * a.rp_hs + dl + a.N),
+                                                 (lds_void *)(SP.win + 64 * pw), 4, 0, 0);
+            }
+        }
+        if constexpr (TM == 1) {
+            if (pw == 3 && l < BQ + 2) {
+                const uint32_t *src = l < BQ ? a.rel + o_b + q0 + l : (l == BQ ? a.rmin : a.rmax) + o_b + q0;
+                __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)SP.qt, 4, 0, 0);
             }
         }
     };
@@ -399,8 +456,8 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
     const std::integral_constant<int, NW / 2> half_waves{};
     if (k0 + BQ <= L) gload_direct(all_waves, w, k0, sm.sq[0], sm.sp[0]);
     else load_partial(k0, sm.sq[0], sm.sp[0]);
-    gload_tables(k0);
-    sstore_tables(sm.sp[0]);
+    gload_tables(k0, tid);
+    sstore_tables(sm.sp[0], tid);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     bf16x8 opnd[8]; // accumulating wave: K d-block p of all rows (dQ operand)
@@ -542,17 +599,25 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
     const int nqb = (L - k0 + BQ - 1) / BQ; // query blocks [k0, L); >= 1
     const int krow = 32 * p + lq;
     // What every wave does at the end of block n: for a partial next block,
-    // the register path of its stage; then the wait and the barrier.  The
-    // pointwise waves wait for their direct copies; the accumulating waves
-    // only for their LDS traffic (their dQ atomics stay in flight).
+    // the register path of its stage and tables (64-bit times: the pointwise
+    // waves store the next block's tables); then the wait and the barrier.  The pointwise waves wait
+    // for their direct copies; the accumulating waves only for their LDS
+    // traffic (their dQ atomics stay in flight).
     auto finish = [&](auto main_c, int n, bool copies) {
         constexpr bool MAIN = decltype(main_c)::value;
         const int q0 = k0 + n * BQ;
-        if (!MAIN && n + 1 < nqb && q0 + 2 * BQ > L) {
+        const bool part = !MAIN && n + 1 < nqb && q0 + 2 * BQ > L; // the next block is partial
+        if (part) {
             const int n3 = n % 3 == 2 ? 0 : n % 3 + 1;
             load_partial(q0 + BQ, sm.sq[n3], sm.sp[(n + 1) & 1]);
+            if constexpr (TM != 2) {
+                gload_tables(q0 + BQ, tid);
+                sstore_tables(sm.sp[(n + 1) & 1], tid);
+            }
         }
-        if (copies || (!MAIN && n + 1 < nqb && q0 + 2 * BQ > L)) __builtin_amdgcn_s_waitcnt(0);
+        if constexpr (TM == 2)
+            if (copies && (MAIN || n + 1 < nqb)) sstore_tables(sm.sp[(n + 1) & 1], tid - NT / 2);
+        if (copies || part) __builtin_amdgcn_s_waitcnt(0);
         else __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0)
         __syncthreads();
     };
@@ -562,16 +627,15 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
         constexpr bool MAIN = decltype(main_c)::value;
         const int q0 = k0 + n * BQ;
         const int n3 = n % 3 == 2 ? 0 : n % 3 + 1;
-        if (MAIN) gload_direct(half_waves, w - NW / 2, q0 + BQ, sm.sq[n3], sm.sp[(n + 1) & 1]);
-        else if (n + 1 < nqb && q0 + 2 * BQ <= L)
+        if (MAIN || (n + 1 < nqb && q0 + 2 * BQ <= L)) {
             gload_direct(half_waves, w - NW / 2, q0 + BQ, sm.sq[n3], sm.sp[(n + 1) & 1]);
+            if constexpr (TM != 2) gload_tables_direct(q0 + BQ, sm.sp[(n + 1) & 1]);
+        }
     };
     // Accumulating wave, block n: the previous block's dV, dK, dQ and drab_p.
     auto iter_acc = [&](auto main_c, int n) {
         constexpr bool MAIN = decltype(main_c)::value;
         const int q0 = k0 + n * BQ;
-        if (MAIN) gload_tables(q0 + BQ);
-        else if (n + 1 < nqb) gload_tables(q0 + BQ);
         int dlf = 0;
         float tot = 0.f;
         const int q0m = q0 - BQ;
@@ -579,9 +643,6 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
             const bool skipm = MAIN ? false : (kw0 > q0m + BQ - 1 || kw0 >= L);
             if (!skipm) acc_block(sm.sq[n % 3 == 0 ? 2 : n % 3 - 1], (n - 1) & 1);
         }
-        // the next block's tables go to LDS before this block's dQ atomics
-        // are issued (a wait for the table loads then covers no atomics)
-        if (MAIN || n + 1 < nqb) sstore_tables(sm.sp[(n + 1) & 1]);
         if (MAIN || n > 0) {
             dq_block(sm.ds[(n - 1) & 1], q0m, MAIN ? true : q0 <= L);
             if (a.drab_p) drabp_sum(sm.dsk[(n - 1) & 1], q0m, tot, dlf);
@@ -590,10 +651,14 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
         finish(main_c, n, false);
     };
     // Pointwise wave, block n: X, dP, P', dS.
+    int rb = 0;              // running drab_t sums of buckets rb, rb + 1 (wave-uniform)
+    float rs0 = 0.f, rs1 = 0.f;
     auto iter_pw = [&](auto main_c, int n) {
         constexpr bool MAIN = decltype(main_c)::value;
         const int q0 = k0 + n * BQ;
         start_copy(main_c, n);
+        if constexpr (TM == 2)
+            if (n + 1 < nqb) gload_tables(q0 + BQ, tid - NT / 2);
         const StageQ &SQn = sm.sq[n % 3];
         const StageP &SPn = sm.sp[n & 1];
         const bool skip = MAIN ? false : (kw0 > q0 + BQ - 1 || kw0 >= L);
@@ -601,9 +666,10 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
         ln.dsk = sm.dsk[n & 1] + (krow + (BQ - 1) - 4 * g) * DKP + 4 * g;
         bf16 *dsn = sm.ds[n & 1], *ptn = sm.pt[n & 1];
         if (!skip) {
-            // X = Q K^T + rab_p window; dP = dO' V^T (hi + lo planes).  The
-            // operand reads run two steps ahead of the MFMAs (pinned with
-            // scheduling groups); the window is added after the products.
+            // X = Q K^T + rab_p window (operand reads two steps ahead of the
+            // MFMAs, pinned with scheduling groups; the window is added after
+            // the products).  dP = dO' V^T (hi + lo planes) is issued inside
+            // the element-wise step, whose X-only part overlaps it.
             floatx16 xacc, pacc, wacc;
 #pragma unroll
             for (int r = 0; r < 16; r++) {
@@ -611,33 +677,40 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
                 wacc[r] = HP ? SPn.win[krow + (BQ - 1) - 4 * g - cr] : 0.f;
                 xacc[r] = pacc[r] = 0.f;
             }
+            bf16x8 fd[2], fl[2];
+            auto fetch_dp = [&](int s) {
+                const int o = swz(lq, s * 16 + g * 8);
+                fd[s & 1] = *(const bf16x8 *)&SQn.dO[o];
+                fl[s & 1] = *(const bf16x8 *)&SPn.dOl[o];
+            };
             __builtin_amdgcn_sched_barrier(0);
             {
-                bf16x8 fq[3], fd[3], fl[3];
-                auto fetch = [&](int s) {
-                    const int o = swz(lq, s * 16 + g * 8);
-                    fq[s % 3] = *(const bf16x8 *)&SQn.q[o];
-                    fd[s % 3] = *(const bf16x8 *)&SQn.dO[o];
-                    fl[s % 3] = *(const bf16x8 *)&SPn.dOl[o];
-                };
+                bf16x8 fq[3];
+                auto fetch = [&](int s) { fq[s % 3] = *(const bf16x8 *)&SQn.q[swz(lq, s * 16 + g * 8)]; };
                 fetch(0);
                 fetch(1);
 #pragma unroll
                 for (int s = 0; s < 8; s++) {
                     if (s + 2 < 8) fetch(s + 2);
                     xacc = mfma32(fq[s % 3], slice8(acc2[s >> 1], 4 * (s & 1)), xacc);
-                    pacc = mfma32(fd[s % 3], slice8(acc2[s >> 1], 8 + 4 * (s & 1)), pacc);
-                    pacc = mfma32(fl[s % 3], slice8(acc2[s >> 1], 8 + 4 * (s & 1)), pacc);
                 }
-                __builtin_amdgcn_sched_group_barrier(0x100, 6, 0); // DS reads of steps 0, 1
+                fetch_dp(0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0); // Q reads of steps 0, 1
 #pragma unroll
                 for (int s = 0; s < 8; s++) {
-                    if (s + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0); // reads of step s + 2
-                    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);                 // MFMAs of step s
+                    if (s + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // read of step s + 2
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // MFMA of step s
                 }
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0); // dP operands of step 0
             }
             __builtin_amdgcn_sched_barrier(0);
             xacc += wacc;
+            auto dp_step = [&](int s) {
+                const bf16x8 d0 = fd[s & 1], d1 = fl[s & 1];
+                if (s + 1 < 8) fetch_dp(s + 1);
+                pacc = mfma32(d0, slice8(acc2[s >> 1], 8 + 4 * (s & 1)), pacc);
+                pacc = mfma32(d1, slice8(acc2[s >> 1], 8 + 4 * (s & 1)), pacc);
+            };
             ln.qt = &SPn.qt[4 * g];
             ln.qt64 = &SPn.qt64[4 * g];
             ln.dmask = kw0 + lq - q0 - 4 * g; // key > query  <=>  cr < dmask
@@ -662,27 +735,43 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
             float tsum = 0.f, tsum2 = 0.f;
             uint32_t ppk[8], dpk[8];
             if (diag)
-                pointwise<TM, DT, true, TB_ANY>(xacc, pacc, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, ubias2, thr, tsum, tsum2);
+                pointwise<TM, DT, true, TB_ANY>(xacc, pacc, dp_step, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, ubias2, thr, tsum, tsum2);
             else if (TM == 1 && nbk == 0)
-                pointwise<TM, DT, false, TB_ONE>(xacc, pacc, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, ubias2, thr, tsum, tsum2);
+                pointwise<TM, DT, false, TB_ONE>(xacc, pacc, dp_step, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, ubias2, thr, tsum, tsum2);
             else if (TM == 1 && nbk == 1)
-                pointwise<TM, DT, false, TB_TWO>(xacc, pacc, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, ubias2, thr, tsum, tsum2);
+                pointwise<TM, DT, false, TB_TWO>(xacc, pacc, dp_step, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, ubias2, thr, tsum, tsum2);
             else
-                pointwise<TM, DT, false, TB_ANY>(xacc, pacc, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, ubias2, thr, tsum, tsum2);
+                pointwise<TM, DT, false, TB_ANY>(xacc, pacc, dp_step, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, ubias2, thr, tsum, tsum2);
             // P' and dS -> LDS as [key][query]: lane writes 4 queries (r%4) per r/4 group
 #pragma unroll
             for (int gr = 0; gr < 4; gr++) {
                 *(u32x2 *)&ptn[krow * SS + 8 * gr + 4 * g] = u32x2{ppk[2 * gr], ppk[2 * gr + 1]};
                 *(u32x2 *)&dsn[krow * SS + 8 * gr + 4 * g] = u32x2{dpk[2 * gr], dpk[2 * gr + 1]};
             }
-            // the block's drab_t sums: plain read-modify-write by lane 0 of this wave's
-            // own table (an LDS atomic would wait for the block copies in flight)
+            // the block's drab_t sums (buckets ubk, ubk + 1) join the wave's
+            // running sums rs0, rs1 of buckets rb, rb + 1; a running sum goes
+            // to the wave's LDS table (lane 0, plain read-modify-write) when
+            // the buckets move on
             if (DT && TM == 1 && nbk <= 1 && !diag) {
                 const float s_all = wave_sum_dpp(tsum);
                 const float s_up = nbk == 1 ? wave_sum_dpp(tsum2) : 0.f;
-                if (l == 0) {
-                    sm.dtab[p][0][ubk] += s_all - s_up;
-                    if (nbk == 1) sm.dtab[p][0][ubk + 1] += s_up;
+                const float s_lo = s_all - s_up;
+                if (ubk == rb) {
+                    rs0 += s_lo;
+                    rs1 += s_up;
+                } else if (ubk == rb + 1) {
+                    if (l == 0) sm.dtab[p][0][rb] += rs0;
+                    rb = ubk;
+                    rs0 = rs1 + s_lo;
+                    rs1 = s_up;
+                } else {
+                    if (l == 0) {
+                        sm.dtab[p][0][rb] += rs0;
+                        sm.dtab[p][0][rb + 1] += rs1;
+                    }
+                    rb = ubk;
+                    rs0 = s_lo;
+                    rs1 = s_up;
                 }
             }
         } else {
@@ -743,6 +832,10 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
         }
     } else {
         run(iter_pw);
+        if (DT && TM == 1 && l == 0) {
+            sm.dtab[p][0][rb] += rs0;
+            sm.dtab[p][0][rb + 1] += rs1;
+        }
     }
 
     // what is left in the ring and the time tables
