@@ -35,18 +35,19 @@ constexpr int D = 128;
 constexpr int BM = FWD_BM; // 128 query rows
 constexpr int BN = 64;     // keys per LDS tile
 constexpr int NT = 256;
-// LDS row strides (bf16 elements), from measured gfx950 LDS throughput: the
-// 16-byte K-operand reads are conflict-free when the stride is 8 mod 16
-// elements; the transposing V reads are fastest at a stride of 160.
-constexpr int RS = 136;    // K tile
-constexpr int VS = 160;    // V tile
+// K and V tiles are [64 keys][128] bf16 with no padding; the 16-byte chunks
+// of row r are XOR-swizzled by sw(r) = 4(r%4) + bitrev2((r/4)%4), which keeps
+// the 16-byte K-operand reads (16 consecutive rows, one chunk) and the
+// transposing V reads (4 consecutive rows, 64 bytes each) free of bank
+// conflicts and lets the tiles be copied global -> LDS directly (4 rows per
+// wave instruction).
 constexpr int WIN = 192;   // rab_p window entries per tile (BM + BN - 1 used)
 constexpr float NLOG2E = -1.4426950408889634f;
 constexpr float NLN2 = -0.69314718055994531f;
 
 struct alignas(16) Stage {
-    alignas(16) bf16 k[BN * RS];
-    alignas(16) bf16 v[BN * VS];
+    alignas(16) bf16 k[BN * D];
+    alignas(16) bf16 v[BN * D];
     float win[WIN];        // rab_p[clip(key - query)] (unscaled)
     uint32_t kt[BN];       // sequence-relative key times
 };
@@ -56,6 +57,16 @@ struct alignas(16) Smem {
     float rabt[128];    // -log2(e) * rab_t
 };
 
+// Swizzle of row r: the XOR applied to its 16-byte chunk index.
+DEV int swf(int row)
+{
+    const int hi = (row >> 2) & 3;
+    return ((row & 3) << 2) | ((hi & 1) << 1) | (hi >> 1);
+}
+// Element offset of (row, col) in a swizzled [rows][128] tile.
+DEV int swz(int row, int col) { return row * D + (((col >> 3) ^ swf(row)) << 3) + (col & 7); }
+
+typedef __attribute__((address_space(3))) void lds_void;
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4v lds_short4v;
 
@@ -142,57 +153,39 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h)
 #pragma unroll
         for (int r = 0; r < 16; r++) oacc[i][r] = 0.f;
 
-    // Loader mapping: thread -> (key quad lc, 8-wide d group le).
-    const int lc = tid >> 4, le = tid & 15;
-    u32x4 kreg[4], vreg[4];
-    float wreg = 0.f;
-    uint32_t treg = 0;
-    auto gload = [&](int kt, auto full_c) {
-        constexpr bool FULL = decltype(full_c)::value;
+    // ---- tile loader: every copy goes global -> LDS directly.  K and V:
+    // 32 groups of 4 rows, 8 per wave; lane l fills physical chunk l%16 of
+    // row 4(G%16) + l/16 (rows past the needed keys repeat the last one:
+    // finite, and every pair they form is masked).  The rab_p window (waves
+    // 0-2, slot 64w + lane) and the key times (wave 3) as 4-byte copies.
+    auto gload = [&](int kt, Stage &S) {
         const int kb0 = kt * BN;
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int key = kb0 + lc * 4 + i;
-            if constexpr (FULL) {
-                const int64_t row = (int64_t)(o_b + key);
-                kreg[i] = *(const u32x4 *)(K + row * a.ldk + h * D + le * 8);
-                vreg[i] = *(const u32x4 *)(V + row * a.ldv + h * D + le * 8);
-            } else {
-                const bool ok = key < kend;
-                const int64_t row = (int64_t)(o_b + (ok ? key : 0));
-                kreg[i] = ok ? *(const u32x4 *)(K + row * a.ldk + h * D + le * 8) : u32x4{0, 0, 0, 0};
-                vreg[i] = ok ? *(const u32x4 *)(V + row * a.ldv + h * D + le * 8) : u32x4{0, 0, 0, 0};
-            }
+        for (int i = 0; i < 8; i++) {
+            const int G = 8 * w + i, plane = G >> 4, r0 = 4 * (G & 15);
+            const int row = r0 + (l >> 4);
+            const int c = (l & 15) ^ swf(row);
+            const int key = min(kb0 + row, kend - 1);
+            const bf16 *src = (plane == 0 ? K + (int64_t)(o_b + key) * a.ldk : V + (int64_t)(o_b + key) * a.ldv);
+            __builtin_amdgcn_global_load_lds((const void *)(src + h * D + c * 8),
+                                             (lds_void *)((plane == 0 ? S.k : S.v) + r0 * D), 16, 0, 0);
         }
         if constexpr (HP) {
-            if (tid < WIN) {
-                int dl = kb0 - q0 - (BM - 1) + tid; // key - query of window slot tid
+            if (w < 3) {
+                int dl = kb0 - q0 - (BM - 1) + 64 * w + l; // key - query of window slot 64w + l
                 dl = dl < -a.N ? -a.N : (dl > a.N ? a.N : dl);
-                wreg = a.rab_p[h * a.rp_hs + dl + a.N];
+                __builtin_amdgcn_global_load_lds((const void *)(a.rab_p + h * a.rp_hs + dl + a.N),
+                                                 (lds_void *)(S.win + 64 * w), 4, 0, 0);
             }
         }
         if constexpr (TM == 1) {
-            if (tid < BN) {
-                const int key = kb0 + tid;
-                treg = key < kend ? a.rel[o_b + key] : 0u;
+            if (w == 3) {
+                const int key = min(kb0 + l, kend - 1);
+                __builtin_amdgcn_global_load_lds((const void *)(a.rel + o_b + key), (lds_void *)S.kt, 4, 0, 0);
             }
         }
     };
-    auto sstore = [&](int buf) {
-        Stage &S = sm.st[buf];
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            *(u32x4 *)&S.k[(lc * 4 + i) * RS + le * 8] = kreg[i];
-            *(u32x4 *)&S.v[(lc * 4 + i) * VS + le * 8] = vreg[i];
-        }
-        if constexpr (HP)
-            if (tid < WIN) S.win[tid] = wreg;
-        if constexpr (TM == 1)
-            if (tid < BN) S.kt[tid] = treg;
-    };
 
-    const std::integral_constant<bool, false> checked{};
-    const std::integral_constant<bool, true> unchecked{};
     // transposing-read lane constants for the V operand
     const int tj = l & 15, tsl = tj >> 2;
     const int cpart = ((l >> 4) & 1) * 16 + 4 * (tj & 3);
@@ -201,99 +194,130 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h)
     // and are full: the MAIN iterations, compiled without the per-block checks.
     const int n_main = q0 / BN; // tiles [0, n_main)
 
+    // S^T of 32-key block kb (keys kb0 + 32 kb ..): 8 MFMAs, K-operand reads
+    // two steps ahead (pinned with scheduling groups); the window is added
+    // afterwards.
+    auto s_block = [&](const Stage &S, int kb, floatx16 &sacc) {
+#pragma unroll
+        for (int r = 0; r < 16; r++) sacc[r] = 0.f;
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 fk[3];
+        auto fetch = [&](int s) { fk[s % 3] = *(const bf16x8 *)&S.k[swz(kb * 32 + lq, s * 16 + g * 8)]; };
+        fetch(0);
+        fetch(1);
+#pragma unroll
+        for (int s = 0; s < 8; s++) {
+            if (s + 2 < 8) fetch(s + 2);
+            sacc = mfma32(fk[s % 3], qreg[s], sacc);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int s = 0; s < 8; s++) {
+            if (s + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (HP) {
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int koff = 8 * (r >> 2) + (r & 3);
+                sacc[r] += S.win[kb * 32 + 4 * g - w * 32 - lq + (BM - 1) + koff];
+            }
+        }
+    };
+    // O^T += V^T P^T for block kb: 8 MFMAs, transposing V reads three steps
+    // ahead.  Step j: m = j / 4 (keys 16m..16m+15 of the block), db = j % 4.
+    auto o_block = [&](const Stage &S, int kb, const uint32_t (&pk)[8]) {
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 fv[4];
+        auto fetch = [&](int j) {
+            const int m = j >> 2, db = j & 3;
+            // keys for element e of this lane's operand: 16m + 8(e/4) + 4g + e%4
+            const int key1 = kb * 32 + 16 * m + 4 * g + tsl;
+            const u32x2 r1 = lds_read_tr(&S.v[swz(key1, db * 32 + cpart)]);
+            const u32x2 r2 = lds_read_tr(&S.v[swz(key1 + 8, db * 32 + cpart)]);
+            fv[j & 3] = as_bf16x8(u32x4{r1[0], r1[1], r2[0], r2[1]});
+        };
+        fetch(0);
+        fetch(1);
+        fetch(2);
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            if (j + 3 < 8) fetch(j + 3);
+            const int m = j >> 2, db = j & 3;
+            const bf16x8 pb = as_bf16x8(u32x4{pk[4 * m], pk[4 * m + 1], pk[4 * m + 2], pk[4 * m + 3]});
+            oacc[db] = mfma32(fv[j & 3], pb, oacc[db]);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            if (j + 3 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // The element-wise step of block kb (sacc holds s + rab_p): time-bias
+    // mode from the block's key-time range, then P' packed to bf16.
+    auto pw_block = [&](const Stage &S, int kt, int kb, const floatx16 &sacc, uint32_t (&pk)[8], bool diag) {
+        const int kstart = kt * BN + kb * 32;
+        const uint32_t *kt_lane = &S.kt[kb * 32 + 4 * g];
+        const int kbase = kstart + 4 * g;
+        bool uni = false;
+        float ubias = 0.f;
+        if constexpr (TM == 1) {
+            // all pairs in one bucket iff floor(log2(min|dt| + 1)) == floor(log2(max|dt| + 1));
+            // relative times of one non-wide sequence differ by less than 2^32 - 1
+            const uint32_t ka = a.rmin[o_b + kstart], kb_ = a.rmax[o_b + kstart];
+            if (tqmin <= tqmax) {
+                const uint32_t lo = ka > tqmax ? ka - tqmax : (tqmin > kb_ ? tqmin - kb_ : 0u);
+                const uint32_t h1 = tqmax > ka ? tqmax - ka : 0u, h2 = kb_ > tqmin ? kb_ - tqmin : 0u;
+                const uint32_t hi = h1 > h2 ? h1 : h2;
+                const int blo = floor_log2_u32(lo + 1u), bhi = floor_log2_u32(hi + 1u);
+                uni = blo == bhi;
+                ubias = sm.rabt[blo];
+            }
+        }
+        if (diag)
+            pointwise<TM, true, false>(sacc, pk, kt_lane, sm.rabt_rev, sm.rabt, tq, tq64, tsk, kbase, L - 1, ubias,
+                                       lq - 4 * g);
+        else if (TM == 1 && uni)
+            pointwise<TM, false, true>(sacc, pk, kt_lane, sm.rabt_rev, sm.rabt, tq, tq64, tsk, kbase, L - 1, ubias, 0);
+        else
+            pointwise<TM, false, false>(sacc, pk, kt_lane, sm.rabt_rev, sm.rabt, tq, tq64, tsk, kbase, L - 1, ubias, 0);
+    };
+
+    // One 64-key tile: the next tile's copies are issued first; the
+    // transposing V reads (which wait for copies in flight) come last, after
+    // both blocks' S^T and element-wise steps.
     auto iteration = [&](auto main_c, int kt) {
         constexpr bool MAIN = decltype(main_c)::value;
-        if (MAIN) {
-            if (kt + 1 < n_main) gload(kt + 1, unchecked);
-            else if (kt + 1 < nkt) gload(kt + 1, checked);
-        } else if (kt + 1 < nkt) {
-            gload(kt + 1, checked);
-        }
+        if (kt + 1 < nkt) gload(kt + 1, sm.st[(kt + 1) & 1]);
         const Stage &S = sm.st[kt & 1];
-        // Both 32-key blocks' S^T first (two independent MFMA chains, interleaved),
-        // so the matrix core works on block 1 while the VALU runs block 0's
-        // element-wise step, and on block 0's PV while block 1's runs.  The
-        // accumulators start from the rab_p window.
-        bool need[2];
-        floatx16 sacc[2];
+        bool need[2], diag[2];
 #pragma unroll
         for (int kb = 0; kb < 2; kb++) {
             const int kstart = kt * BN + kb * 32;
             need[kb] = MAIN ? true : !(kstart > qstart + 31 || qstart >= L); // wave-uniform
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int koff = 8 * (r >> 2) + (r & 3);
-                sacc[kb][r] = HP ? S.win[kb * 32 + 4 * g - w * 32 - lq + (BM - 1) + koff] : 0.f;
-            }
+            diag[kb] = MAIN ? false : kstart + 31 > qstart;
         }
-        if (need[0] && need[1]) {
-#pragma unroll
-            for (int s = 0; s < 8; s++) {
-                const bf16x8 ka0 = *(const bf16x8 *)&S.k[lq * RS + s * 16 + g * 8];
-                const bf16x8 ka1 = *(const bf16x8 *)&S.k[(32 + lq) * RS + s * 16 + g * 8];
-                sacc[0] = mfma32(ka0, qreg[s], sacc[0]);
-                sacc[1] = mfma32(ka1, qreg[s], sacc[1]);
-            }
-        } else if (need[0]) {
-#pragma unroll
-            for (int s = 0; s < 8; s++) {
-                const bf16x8 ka0 = *(const bf16x8 *)&S.k[lq * RS + s * 16 + g * 8];
-                sacc[0] = mfma32(ka0, qreg[s], sacc[0]);
-            }
+        floatx16 sacc0, sacc1;
+        uint32_t pk0[8], pk1[8];
+        if (need[0]) {
+            s_block(S, 0, sacc0);
+            pw_block(S, kt, 0, sacc0, pk0, diag[0]);
         }
-#pragma unroll
-        for (int kb = 0; kb < 2; kb++) {
-            const int kstart = kt * BN + kb * 32;
-            if (!need[kb]) continue;
-            const bool diag = MAIN ? false : kstart + 31 > qstart;
-            const uint32_t *kt_lane = &S.kt[kb * 32 + 4 * g];
-            const int kbase = kstart + 4 * g;
-            bool uni = false;
-            float ubias = 0.f;
-            if constexpr (TM == 1) {
-                // all pairs in one bucket iff floor(log2(min|dt| + 1)) == floor(log2(max|dt| + 1));
-                // relative times of one non-wide sequence differ by less than 2^32 - 1
-                const uint32_t ka = a.rmin[o_b + kstart], kb_ = a.rmax[o_b + kstart];
-                if (tqmin <= tqmax) {
-                    const uint32_t lo = ka > tqmax ? ka - tqmax : (tqmin > kb_ ? tqmin - kb_ : 0u);
-                    const uint32_t h1 = tqmax > ka ? tqmax - ka : 0u, h2 = kb_ > tqmin ? kb_ - tqmin : 0u;
-                    const uint32_t hi = h1 > h2 ? h1 : h2;
-                    const int blo = floor_log2_u32(lo + 1u), bhi = floor_log2_u32(hi + 1u);
-                    uni = blo == bhi;
-                    ubias = sm.rabt[blo];
-                }
-            }
-            uint32_t pk[8];
-            if (diag)
-                pointwise<TM, true, false>(sacc[kb], pk, kt_lane, sm.rabt_rev, sm.rabt, tq, tq64, tsk, kbase, L - 1,
-                                           ubias, lq - 4 * g);
-            else if (TM == 1 && uni)
-                pointwise<TM, false, true>(sacc[kb], pk, kt_lane, sm.rabt_rev, sm.rabt, tq, tq64, tsk, kbase, L - 1,
-                                           ubias, 0);
-            else
-                pointwise<TM, false, false>(sacc[kb], pk, kt_lane, sm.rabt_rev, sm.rabt, tq, tq64, tsk, kbase, L - 1,
-                                            ubias, 0);
-#pragma unroll
-            for (int m = 0; m < 2; m++) {
-                const bf16x8 pb = as_bf16x8(u32x4{pk[4 * m], pk[4 * m + 1], pk[4 * m + 2], pk[4 * m + 3]});
-                // keys for element e of this lane's operand: 16m + 8(e/4) + 4g + e%4
-                const int key1 = kb * 32 + 16 * m + 4 * g + tsl;
-#pragma unroll
-                for (int db = 0; db < 4; db++) {
-                    const u32x2 r1 = lds_read_tr(&S.v[key1 * VS + db * 32 + cpart]);
-                    const u32x2 r2 = lds_read_tr(&S.v[(key1 + 8) * VS + db * 32 + cpart]);
-                    const bf16x8 va = as_bf16x8(u32x4{r1[0], r1[1], r2[0], r2[1]});
-                    oacc[db] = mfma32(va, pb, oacc[db]);
-                }
-            }
+        if (need[1]) {
+            s_block(S, 1, sacc1);
+            pw_block(S, kt, 1, sacc1, pk1, diag[1]);
         }
-        if (kt + 1 < nkt) sstore((kt + 1) & 1);
+        if (need[0]) o_block(S, 0, pk0);
+        if (need[1]) o_block(S, 1, pk1);
+        __builtin_amdgcn_s_waitcnt(0); // the next tile's copies landed
         __syncthreads();
     };
 
-    if (n_main > 0) gload(0, unchecked);
-    else gload(0, checked);
-    sstore(0);
+    gload(0, sm.st[0]);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     const std::integral_constant<bool, false> generic{};
