@@ -75,7 +75,7 @@ AttnWs attn_ws(const hstu_jagged *j, const hstu_dims *dm, int tile)
     Carver c;
     const int B = j->batch, T = j->total, H = dm->heads;
     w.header = c.take(256);
-    w.items = c.take((size_t)max_items_for(B, T, tile, H) * sizeof(int2));
+    w.items = c.take((size_t)2 * max_items_for(B, T, tile, H) * sizeof(int2)); // split items: up to 2 per tile
     w.rel = c.take((size_t)T * 4 * 3); // rel, then rmin and rmax per 32-token block
     w.wide = c.take((size_t)B * 4);
     w.obuf = c.take((size_t)T * H * dm->d_v * 4);
@@ -86,6 +86,21 @@ AttnWs attn_ws(const hstu_jagged *j, const hstu_dims *dm, int tile)
 }
 
 int fwd_tile(const hstu_dims *dm) { return dm->dtype == HSTU_BF16 ? FWD_BM : F32_BM; }
+
+// Forward workgroups that run at once on the current device (two per
+// compute unit: the kernel's LDS allows two).
+int concurrent_slots()
+{
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
+    if (cached[dev] == 0) {
+        int cu = 0;
+        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0) cu = 256;
+        cached[dev] = 2 * cu;
+    }
+    return cached[dev];
+}
 
 hstu_status check_jagged(const hstu_jagged *j)
 {
@@ -181,12 +196,23 @@ hstu_status attn_fwd_launch(const hstu_jagged *j, const hstu_dims *dm, const hst
     uint32_t *rel = (uint32_t *)(wb + w.rel);
     int32_t *wide = (int32_t *)(wb + w.wide);
     const int T = j->total, B = j->batch;
-    const int max_items = max_items_for(B, T, tile, H);
+    // Long query tiles are split over two workgroups (halves of the key
+    // range) when the output accumulates in fp32 (the LayerNorm-gate path):
+    // the halves add into zeroed rows.
+    const bool split = dm->dtype == HSTU_BF16 && u.ptr != nullptr;
+    const int max_items = (split ? 2 : 1) * max_items_for(B, T, tile, H);
+    int *t_split = status + 2;
+    float *obuf = u.ptr ? (o_save ? o_save : (float *)(wb + w.obuf)) : nullptr;
     {
         ProfScope ps("sched_kernel", st);
-        launch_sched(j->offsets, j->ts, B, T, tile, H, status, n_items, items, max_items, rel, wide, st);
+        launch_sched(j->offsets, j->ts, B, T, tile, H, status, n_items, items, max_items, rel, wide,
+                     split ? concurrent_slots() : 0, t_split, st);
     }
     TRY(launched(hipGetLastError(), "schedule kernel"));
+    if (split) {
+        ProfScope ps("zero_split_rows_kernel", st);
+        TRY(launched(launch_zero_split_rows(j->offsets, B, tile, t_split, obuf, F, F, status, st), "zero split rows"));
+    }
 
     AttnFwdArgs a{};
     a.q = q.ptr;
@@ -211,9 +237,7 @@ hstu_status attn_fwd_launch(const hstu_jagged *j, const hstu_dims *dm, const hst
     a.inv_n = 1.0f / (float)j->n_max;
     a.items = items;
     a.n_items = n_items;
-    float *obuf = nullptr;
     if (u.ptr) {
-        obuf = o_save ? o_save : (float *)(wb + w.obuf);
         a.o32 = obuf;
         a.ld_o32 = F;
         a.o16 = nullptr;
@@ -440,7 +464,7 @@ hstu_status hstu_attn_bwd(const hstu_jagged *j, const hstu_dims *dm, const hstu_
     const int64_t t_hs = (bias && bias->rab_t) ? bias->rab_t_hstride : 128;
     {
         ProfScope ps("sched_kernel", st);
-        launch_sched(j->offsets, j->ts, B, T, BWD_BN, H, status, n_items, items, max_items, rel, wide, st);
+        launch_sched(j->offsets, j->ts, B, T, BWD_BN, H, status, n_items, items, max_items, rel, wide, 0, nullptr, st);
     }
     TRY(launched(hipGetLastError(), "schedule kernel"));
     {

@@ -874,7 +874,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int item = blockIdx.x;
     if (item >= *a.n_items) return;
     const int2 it = a.items[item];
-    const int b = it.x, tsched = it.y >> 8, h = it.y & 255;
+    const int b = it.x, tsched = it.y >> ITEM_T_SHIFT, h = it.y & 255; // never split
     const int o_b = a.offsets[b];
     const int L = a.offsets[b + 1] - o_b;
     const int nkt = (L + BN - 1) / BN;

@@ -52,10 +52,11 @@ struct alignas(16) Stage {
     uint32_t kt[BN];       // sequence-relative key times
 };
 struct alignas(16) Smem {
-    Stage st[2];
+    Stage st[2];        // (after the last tile: a split item's output transpose, 4 x 32 x 132 floats)
     float rabt_rev[32]; // -log2(e) * rab_t[31 - c], indexed by clz(|dt| + 1)
     float rabt[128];    // -log2(e) * rab_t
 };
+static_assert(sizeof(Stage) * 2 >= 4 * 32 * 132 * sizeof(float), "split-output transpose fits in the stages");
 
 // Swizzle of row r: the XOR applied to its 16-byte chunk index.
 DEV int swf(int row)
@@ -117,10 +118,13 @@ DEV void pointwise(const floatx16 &sacc, uint32_t (&pk)[8], const uint32_t *kt_l
 }
 
 template <bool HP, int TM>
-DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h)
+DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h, int split, int part)
 {
     const int kend = min(q0 + BM, L); // keys [0, kend) are needed
     const int nkt = (kend + BN - 1) / BN;
+    // a split item covers half of the key tiles: part 0 [0, nkt / 2), part 1 the rest
+    const int kt_begin = split ? (part ? nkt / 2 : 0) : 0;
+    const int kt_end = split ? (part ? nkt : nkt / 2) : nkt;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, lq = l & 31;
     const bf16 *Q = (const bf16 *)a.q, *K = (const bf16 *)a.k, *V = (const bf16 *)a.v;
 
@@ -158,29 +162,55 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h)
     // row 4(G%16) + l/16 (rows past the needed keys repeat the last one:
     // finite, and every pair they form is masked).  The rab_p window (waves
     // 0-2, slot 64w + lane) and the key times (wave 3) as 4-byte copies.
-    auto gload = [&](int kt, Stage &S) {
-        const int kb0 = kt * BN;
+    // Full tiles (every key < kend): wave w copies plane w / 2 (K, then V),
+    // row groups 8(w % 2) + i; the row base is wave-uniform and each lane
+    // adds one of four 32-bit byte offsets (row l/16 of the group, swizzled
+    // chunk), so the copies need no per-lane 64-bit address arithmetic.
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    const bool kplane = wu < 2;
+    const bf16 *pbase = kplane ? K : V;
+    const int64_t pld = kplane ? a.ldk : a.ldv;
+    uint32_t loff[4];
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const int G = 8 * w + i, plane = G >> 4, r0 = 4 * (G & 15);
-            const int row = r0 + (l >> 4);
-            const int c = (l & 15) ^ swf(row);
-            const int key = min(kb0 + row, kend - 1);
-            const bf16 *src = (plane == 0 ? K + (int64_t)(o_b + key) * a.ldk : V + (int64_t)(o_b + key) * a.ldv);
-            __builtin_amdgcn_global_load_lds((const void *)(src + h * D + c * 8),
-                                             (lds_void *)((plane == 0 ? S.k : S.v) + r0 * D), 16, 0, 0);
+    for (int j = 0; j < 4; j++) {
+        const int sw = ((l >> 4) << 2) | ((j & 1) << 1) | (j >> 1); // swf(row), row % 4 = l/16, (row/4) % 4 = j
+        loff[j] = (uint32_t)(((int64_t)(l >> 4) * pld + (((l & 15) ^ sw) << 3)) * 2);
+    }
+    auto gload = [&](int kt, Stage &S, auto full_c) {
+        constexpr bool FULL = decltype(full_c)::value;
+        const int kb0 = kt * BN;
+        if constexpr (FULL) {
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int r0 = 4 * ((8 * wu + i) & 15);
+                const char *rowp = (const char *)(pbase + (int64_t)(o_b + kb0 + r0) * pld + h * D);
+                __builtin_amdgcn_global_load_lds((const void *)(rowp + loff[i & 3]),
+                                                 (lds_void *)((kplane ? S.k : S.v) + r0 * D), 16, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int G = 8 * w + i, plane = G >> 4, r0 = 4 * (G & 15);
+                const int row = r0 + (l >> 4);
+                const int c = (l & 15) ^ swf(row);
+                const int key = min(kb0 + row, kend - 1);
+                const bf16 *src =
+                    (plane == 0 ? K + (int64_t)(o_b + key) * a.ldk : V + (int64_t)(o_b + key) * a.ldv);
+                __builtin_amdgcn_global_load_lds((const void *)(src + h * D + c * 8),
+                                                 (lds_void *)((plane == 0 ? S.k : S.v) + r0 * D), 16, 0, 0);
+            }
         }
         if constexpr (HP) {
-            if (w < 3) {
-                int dl = kb0 - q0 - (BM - 1) + 64 * w + l; // key - query of window slot 64w + l
+            if (wu < 3) {
+                int dl = kb0 - q0 - (BM - 1) + 64 * wu + l; // key - query of window slot 64w + l
                 dl = dl < -a.N ? -a.N : (dl > a.N ? a.N : dl);
                 __builtin_amdgcn_global_load_lds((const void *)(a.rab_p + h * a.rp_hs + dl + a.N),
-                                                 (lds_void *)(S.win + 64 * w), 4, 0, 0);
+                                                 (lds_void *)(S.win + 64 * wu), 4, 0, 0);
             }
         }
         if constexpr (TM == 1) {
-            if (w == 3) {
-                const int key = min(kb0 + l, kend - 1);
+            if (wu == 3) {
+                const int key = FULL ? kb0 + l : min(kb0 + l, kend - 1);
                 __builtin_amdgcn_global_load_lds((const void *)(a.rel + o_b + key), (lds_void *)S.kt, 4, 0, 0);
             }
         }
@@ -257,8 +287,9 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h)
         __builtin_amdgcn_sched_barrier(0);
     };
     // The element-wise step of block kb (sacc holds s + rab_p): time-bias
-    // mode from the block's key-time range, then P' packed to bf16.
-    auto pw_block = [&](const Stage &S, int kt, int kb, const floatx16 &sacc, uint32_t (&pk)[8], bool diag) {
+    // mode from the block's key-time range [ka, kb_], then P' packed to bf16.
+    auto pw_block = [&](const Stage &S, int kt, int kb, const floatx16 &sacc, uint32_t (&pk)[8], bool diag,
+                        uint32_t ka, uint32_t kb_) {
         const int kstart = kt * BN + kb * 32;
         const uint32_t *kt_lane = &S.kt[kb * 32 + 4 * g];
         const int kbase = kstart + 4 * g;
@@ -267,7 +298,6 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h)
         if constexpr (TM == 1) {
             // all pairs in one bucket iff floor(log2(min|dt| + 1)) == floor(log2(max|dt| + 1));
             // relative times of one non-wide sequence differ by less than 2^32 - 1
-            const uint32_t ka = a.rmin[o_b + kstart], kb_ = a.rmax[o_b + kstart];
             if (tqmin <= tqmax) {
                 const uint32_t lo = ka > tqmax ? ka - tqmax : (tqmin > kb_ ? tqmin - kb_ : 0u);
                 const uint32_t h1 = tqmax > ka ? tqmax - ka : 0u, h2 = kb_ > tqmin ? kb_ - tqmin : 0u;
@@ -291,7 +321,21 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h)
     // both blocks' S^T and element-wise steps.
     auto iteration = [&](auto main_c, int kt) {
         constexpr bool MAIN = decltype(main_c)::value;
-        if (kt + 1 < nkt) gload(kt + 1, sm.st[(kt + 1) & 1]);
+        if (kt + 1 < kt_end) {
+            if ((kt + 2) * BN <= kend) gload(kt + 1, sm.st[(kt + 1) & 1], std::true_type{});
+            else gload(kt + 1, sm.st[(kt + 1) & 1], std::false_type{});
+        }
+        // the key-time ranges of both blocks (scalar loads, issued early; a
+        // block past the sequence reads its last block's entry, unused)
+        uint32_t kmn[2] = {0u, 0u}, kmx[2] = {0u, 0u};
+        if constexpr (TM == 1) {
+#pragma unroll
+            for (int kb = 0; kb < 2; kb++) {
+                const int ks = min(kt * BN + kb * 32, L - 1) & ~31;
+                kmn[kb] = a.rmin[o_b + ks];
+                kmx[kb] = a.rmax[o_b + ks];
+            }
+        }
         const Stage &S = sm.st[kt & 1];
         bool need[2], diag[2];
 #pragma unroll
@@ -304,11 +348,11 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h)
         uint32_t pk0[8], pk1[8];
         if (need[0]) {
             s_block(S, 0, sacc0);
-            pw_block(S, kt, 0, sacc0, pk0, diag[0]);
+            pw_block(S, kt, 0, sacc0, pk0, diag[0], kmn[0], kmx[0]);
         }
         if (need[1]) {
             s_block(S, 1, sacc1);
-            pw_block(S, kt, 1, sacc1, pk1, diag[1]);
+            pw_block(S, kt, 1, sacc1, pk1, diag[1], kmn[1], kmx[1]);
         }
         if (need[0]) o_block(S, 0, pk0);
         if (need[1]) o_block(S, 1, pk1);
@@ -316,21 +360,43 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h)
         __syncthreads();
     };
 
-    gload(0, sm.st[0]);
+    gload(kt_begin, sm.st[kt_begin & 1], std::false_type{});
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     const std::integral_constant<bool, false> generic{};
     const std::integral_constant<bool, true> fast{};
-    int kt = 0;
+    int kt = kt_begin;
     if constexpr (TM != 2)
-        for (; kt < n_main; kt++) iteration(fast, kt);
-    for (; kt < nkt; kt++) iteration(generic, kt);
+        for (; kt < min(n_main, kt_end); kt++) iteration(fast, kt);
+    for (; kt < kt_end; kt++) iteration(generic, kt);
 
-    if (!qvalid) return;
     // O^T accumulator: lane holds query qrow, d = 32 db + 8(r/4) + 4g + r%4;
     // O = (-ln 2 / N) * sum P' V.
     const float sc = NLN2 * a.inv_n;
+    if (split) {
+        // The two halves of a split item add their partial sums into the
+        // (zeroed) fp32 output.  Through LDS (the stage tiles are free after
+        // the last barrier) so that each atomic instruction covers 64
+        // consecutive floats of one row: wave w's rows [32][132].
+        float *ot = reinterpret_cast<float *>(&sm.st[0]) + w * 32 * 132;
+#pragma unroll
+        for (int db = 0; db < 4; db++)
+#pragma unroll
+            for (int gr = 0; gr < 4; gr++) {
+                const int d0 = db * 32 + 8 * gr + 4 * g;
+                *(floatx4 *)&ot[lq * 132 + d0] = floatx4{oacc[db][4 * gr] * sc, oacc[db][4 * gr + 1] * sc,
+                                                         oacc[db][4 * gr + 2] * sc, oacc[db][4 * gr + 3] * sc};
+            }
+        __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0): this wave's rows are in LDS
+        for (int r = 0; r < 32 && qstart + r < L; r++) {
+            float *op = a.o32 + (int64_t)(o_b + qstart + r) * a.ld_o32 + h * D;
+            atomicAdd(op + l, ot[r * 132 + l]);
+            atomicAdd(op + 64 + l, ot[r * 132 + 64 + l]);
+        }
+        return;
+    }
+    if (!qvalid) return;
     const int64_t row = (int64_t)(o_b + qrow);
 #pragma unroll
     for (int db = 0; db < 4; db++) {
@@ -358,7 +424,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int item = blockIdx.x;
     if (item >= *a.n_items) return;
     const int2 it = a.items[item];
-    const int b = it.x, qt = it.y >> 8, h = it.y & 255;
+    const int b = it.x, qt = it.y >> ITEM_T_SHIFT, split = (it.y >> 9) & 1, part = (it.y >> 8) & 1, h = it.y & 255;
     const int o_b = a.offsets[b];
     const int L = a.offsets[b + 1] - o_b;
     const bool has_t = a.ts != nullptr && a.rab_t != nullptr;
@@ -366,9 +432,9 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
     if (tid < 128) sm.rabt[tid] = has_t ? NLOG2E * a.rab_t[h * a.rt_hs + tid] : 0.f;
     if (tid < 32) sm.rabt_rev[tid] = has_t ? NLOG2E * a.rab_t[h * a.rt_hs + 31 - tid] : 0.f;
     // (the first barrier inside fwd_body orders these table writes before use)
-    if (!has_t) fwd_body<HP, 0>(a, sm, o_b, L, qt * BM, h);
-    else if (a.wide[b] != 0) fwd_body<HP, 2>(a, sm, o_b, L, qt * BM, h);
-    else fwd_body<HP, 1>(a, sm, o_b, L, qt * BM, h);
+    if (!has_t) fwd_body<HP, 0>(a, sm, o_b, L, qt * BM, h, split, part);
+    else if (a.wide[b] != 0) fwd_body<HP, 2>(a, sm, o_b, L, qt * BM, h, split, part);
+    else fwd_body<HP, 1>(a, sm, o_b, L, qt * BM, h, split, part);
 }
 
 // ---------------------------------------------------------------------------
@@ -385,7 +451,7 @@ __global__ void __launch_bounds__(F32_BM) attn_fwd_f32_kernel(AttnFwdArgs a)
     const int item = blockIdx.x;
     if (item >= *a.n_items) return;
     const int2 it = a.items[item];
-    const int b = it.x, qt = it.y >> 8, h = it.y & 255;
+    const int b = it.x, qt = it.y >> ITEM_T_SHIFT, h = it.y & 255; // never split
     const int o_b = a.offsets[b];
     const int L = a.offsets[b + 1] - o_b;
     const int q0 = qt * F32_BM;

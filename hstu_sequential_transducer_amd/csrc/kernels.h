@@ -9,8 +9,21 @@ constexpr int SCHED_BINS = 4096; // longest sequence: (SCHED_BINS - 1) tiles
 // rel[T] (sequence-relative times) is followed by rmin[T] and rmax[T]: at the
 // first token r of every 32-token block of a sequence (r - start a multiple
 // of 32), the min and max of rel over that block's tokens.
+//
+// Items are int2 {b, (t << 10) | (split << 9) | (part << 8) | h}: sequence b,
+// tile t, head h.  With split_slots > 0 (the number of workgroups that run at
+// once), tiles t >= t_split become two items (part 0 and 1, each half of the
+// tile's key range) where t_split is chosen from the total work so that no
+// item is much longer than the average per slot; *t_split is written (a
+// large value when nothing is split).
+constexpr int ITEM_T_SHIFT = 10;
 void launch_sched(const int32_t *offsets, const int64_t *ts, int B, int T, int tile, int H, int *status, int *n_items,
-                  int2 *items, int max_items, uint32_t *rel, int32_t *wide, hipStream_t st);
+                  int2 *items, int max_items, uint32_t *rel, int32_t *wide, int split_slots, int *t_split,
+                  hipStream_t st);
+// Zeroes the fp32 rows [offsets[b] + tile * t_split, offsets[b + 1]) of
+// every sequence (the rows that split items accumulate into).
+hipError_t launch_zero_split_rows(const int32_t *offsets, int B, int tile, const int *t_split, float *o32, int64_t ld,
+                                  int F, const int *status, hipStream_t st);
 
 // ---- attention forward (attn_fwd.hip)
 struct AttnFwdArgs {

@@ -36,22 +36,34 @@ __device__ int block_suffix_excl(int v, int *tmp)
 //   S[t] = #items with a larger tile index / H = sum_{t' > t} #{b : n_b > t'}.
 // Ties inside a length class are broken by an atomic counter; the results
 // of every kernel are independent of the order.
+//
+// Split items (split_slots > 0): a tile t costs about 2(t + 1) key tiles of
+// half its width, the whole launch about sum_b n_b (n_b + 1) H of them; tiles
+// t >= t_split = max(4, avg / 3), avg = that total over the split_slots
+// concurrent workgroups, become two items of half the cost each.  Both
+// halves of a tile count as a multiplicity m(t) = 2 in the index arithmetic
+// below: index(b, t, h, part) = H * (S[t] + m(t) pos_pi(b) + part) + h.
 __global__ void __launch_bounds__(1024) sched_kernel(const int32_t *__restrict__ offsets, int B, int T, int tile, int H,
                                                       int *__restrict__ status, int *__restrict__ n_items,
                                                       int2 *__restrict__ items, int max_items,
-                                                      int32_t *__restrict__ wide)
+                                                      int32_t *__restrict__ wide, int split_slots,
+                                                      int *__restrict__ t_split_out)
 {
     __shared__ int hist[SCHED_BINS];
     __shared__ int fill[SCHED_BINS];
     __shared__ int S[SCHED_BINS];
     __shared__ int bad;
+    __shared__ unsigned long long work;
     __shared__ int chunk_tot[1024];
     const int tid = threadIdx.x;
     for (int i = tid; i < SCHED_BINS; i += 1024) {
         hist[i] = 0;
         fill[i] = 0;
     }
-    if (tid == 0) bad = (offsets[0] != 0 || offsets[B] != T) ? HSTU_DEV_BAD_OFFSETS : 0;
+    if (tid == 0) {
+        bad = (offsets[0] != 0 || offsets[B] != T) ? HSTU_DEV_BAD_OFFSETS : 0;
+        work = 0;
+    }
     __syncthreads();
     for (int b = tid; b < B; b += 1024) {
         wide[b] = 0;
@@ -59,16 +71,28 @@ __global__ void __launch_bounds__(1024) sched_kernel(const int32_t *__restrict__
         if (L < 0) atomicOr(&bad, HSTU_DEV_BAD_OFFSETS);
         int n = L > 0 ? (L + tile - 1) / tile : 0;
         if (n >= SCHED_BINS) atomicOr(&bad, HSTU_DEV_TOO_LONG);
-        else atomicAdd(&hist[n], 1);
+        else {
+            atomicAdd(&hist[n], 1);
+            atomicAdd(&work, (unsigned long long)n * (unsigned long long)(n + 1));
+        }
     }
     __syncthreads();
     if (bad) {
         if (tid == 0) {
             *status = bad;
             *n_items = 0;
+            if (t_split_out) *t_split_out = SCHED_BINS;
         }
         return;
     }
+    int t_split = SCHED_BINS; // no split
+    if (split_slots > 0) {
+        const unsigned long long avg = work * (unsigned long long)H / (unsigned long long)split_slots;
+        const unsigned long long t3 = avg / 3;
+        t_split = t3 < 4 ? 4 : (t3 > SCHED_BINS ? SCHED_BINS : (int)t3);
+    }
+    if (tid == 0 && t_split_out) *t_split_out = t_split;
+    auto mult = [&](int t) { return t >= t_split ? 2 : 1; };
     // cnt_gt[t] = #{b : n_b > t} = sum_{v > t} hist[v]  (suffix sum, into
     // fill[]), then S[t] = sum_{t' > t} cnt_gt[t'].  Each thread owns a
     // contiguous chunk of bins; chunk totals go through a block-wide scan.
@@ -87,17 +111,17 @@ __global__ void __launch_bounds__(1024) sched_kernel(const int32_t *__restrict__
     __syncthreads();
     {
         int s = 0;
-        for (int i = per - 1; i >= 0; i--) s += fill[tid * per + i];
+        for (int i = per - 1; i >= 0; i--) s += fill[tid * per + i] * mult(tid * per + i);
         const int above = block_suffix_excl(s, chunk_tot);
         if (tid == 0) {
-            *n_items = (above + s) * H; // sum_t cnt_gt[t] = sum_b n_b
+            *n_items = (above + s) * H; // sum_t m(t) cnt_gt[t]
             *status = 0;
         }
         int run = above;
         for (int i = per - 1; i >= 0; i--) {
             const int t = tid * per + i;
             S[t] = run;
-            run += fill[t];
+            run += fill[t] * mult(t);
         }
     }
     __syncthreads();
@@ -117,8 +141,11 @@ __global__ void __launch_bounds__(1024) sched_kernel(const int32_t *__restrict__
         pos = __shfl(pos, 0, 64);
         for (int k = lane; k < n * H; k += 64) {
             const int t = k / H, h = k - t * H;
-            const int idx = H * (S[t] + pos) + h;
-            if (idx < max_items) items[idx] = make_int2(b, (t << 8) | h);
+            const int m = mult(t);
+            for (int part = 0; part < m; part++) {
+                const int idx = H * (S[t] + m * pos + part) + h;
+                if (idx < max_items) items[idx] = make_int2(b, (t << ITEM_T_SHIFT) | ((m - 1) << 9) | (part << 8) | h);
+            }
         }
     }
 }
@@ -159,11 +186,34 @@ __global__ void __launch_bounds__(256) reltime_kernel(const int32_t *__restrict_
     }
 }
 
+// Rows of split items: grid (B, 32), each workgroup every 32nd of one
+// sequence's rows from tile * t_split on.
+__global__ void __launch_bounds__(256) zero_split_rows_kernel(const int32_t *__restrict__ offsets, int tile,
+                                                               const int *__restrict__ t_split, float *__restrict__ o32,
+                                                               int64_t ld, int F, const int *__restrict__ status)
+{
+    if (*status) return;
+    const int b = blockIdx.x;
+    const int o_b = offsets[b], L = offsets[b + 1] - o_b;
+    for (int64_t r = (int64_t)tile * *t_split + blockIdx.y; r < L; r += gridDim.y)
+        for (int c = threadIdx.x; c < F; c += 256) o32[(o_b + r) * ld + c] = 0.f;
+}
+
+hipError_t launch_zero_split_rows(const int32_t *offsets, int B, int tile, const int *t_split, float *o32, int64_t ld,
+                                  int F, const int *status, hipStream_t st)
+{
+    if (B <= 0) return hipSuccess;
+    hipLaunchKernelGGL(zero_split_rows_kernel, dim3(B, 32), dim3(256), 0, st, offsets, tile, t_split, o32, ld, F,
+                       status);
+    return hipGetLastError();
+}
+
 void launch_sched(const int32_t *offsets, const int64_t *ts, int B, int T, int tile, int H, int *status, int *n_items,
-                  int2 *items, int max_items, uint32_t *rel, int32_t *wide, hipStream_t st)
+                  int2 *items, int max_items, uint32_t *rel, int32_t *wide, int split_slots, int *t_split,
+                  hipStream_t st)
 {
     hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(1024), 0, st, offsets, B, T, tile, H, status, n_items, items,
-                       max_items, wide);
+                       max_items, wide, split_slots, t_split);
     if (ts && T > 0)
         hipLaunchKernelGGL(reltime_kernel, dim3((T + 255) / 256), dim3(256), 0, st, offsets, ts, rel, wide, B, T, status);
 }
