@@ -469,7 +469,8 @@ hstu_status hstu_attn_bwd(const hstu_jagged *j, const hstu_dims *dm, const hstu_
     TRY(launched(hipGetLastError(), "schedule kernel"));
     {
         ProfScope ps("fill_zero_kernel", st);
-        TRY(launched(launch_fill_zero(dq_acc, (size_t)T * H * d * 4, st), "zero fill"));
+        // (with the gate, the LayerNorm backward below zeroes dq_acc's rows)
+        if (!u.ptr) TRY(launched(launch_fill_zero(dq_acc, (size_t)T * H * d * 4, st), "zero fill"));
         if (drab_p) TRY(launched(launch_fill_zero(drab_p, (size_t)H * p_hs * 4, st), "zero fill"));
         if (drab_t) TRY(launched(launch_fill_zero(drab_t, (size_t)H * t_hs * 4, st), "zero fill"));
     }
@@ -477,7 +478,7 @@ hstu_status hstu_attn_bwd(const hstu_jagged *j, const hstu_dims *dm, const hstu_
     if (u.ptr) {
         ProfScope ps("ln_gate_bwd_kernel", st);
         TRY(launched(launch_ln_gate_bwd(dout.ptr, dout.ld, u.ptr, u.ld, o_save, F, ln_stats, true, du.ptr, du.ld, dO,
-                                        inv_n, T, F, status, st),
+                                        inv_n, T, F, dq_acc, H * d, status, st),
                      "LayerNorm gate backward kernel"));
     } else {
         ProfScope ps("scale_bf16_kernel", st);

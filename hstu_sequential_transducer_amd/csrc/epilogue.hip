@@ -149,11 +149,13 @@ __global__ void __launch_bounds__(256) ln_gate_bwd_kernel(const void *__restrict
                                                           int64_t ldu, const float *__restrict__ O, int64_t ldo,
                                                           const float *__restrict__ stats, void *__restrict__ dU,
                                                           int64_t lddu, bf16 *__restrict__ dO, float scale, int T, int F,
-                                                          bool vec)
+                                                          bool vec, float *__restrict__ zrows, int zF)
 {
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= T) return;
+    if (zrows)
+        for (int c = 4 * lane; c < zF; c += 256) *(floatx4 *)(zrows + (int64_t)row * zF + c) = floatx4{0.f, 0.f, 0.f, 0.f};
     const float mean = stats[2 * (int64_t)row], rstd = stats[2 * (int64_t)row + 1];
     const int c0 = lane * VPL;
     float xh[VPL], dxh[VPL];
@@ -247,9 +249,10 @@ hipError_t launch_ln_gate_fwd(const float *O, int64_t ldo, int nparts, int64_t p
 
 hipError_t launch_ln_gate_bwd(const void *dG, int64_t ldg, const void *U, int64_t ldu, const float *O, int64_t ldo,
                               const float *stats, bool bf16io, void *dU, int64_t lddu, bf16 *dO, float scale, int T,
-                              int F, const int *status, hipStream_t st)
+                              int F, float *zrows, int zF, const int *status, hipStream_t st)
 {
     (void)status;
+    if (zrows && ((((uintptr_t)zrows) & 15) != 0 || zF % 4 != 0)) return hipErrorInvalidValue;
     if (T <= 0) return hipSuccess;
     dim3 grid((T + 3) / 4);
     const int64_t es = bf16io ? 2 : 4;
@@ -258,9 +261,9 @@ hipError_t launch_ln_gate_bwd(const void *dG, int64_t ldg, const void *U, int64_
                          (lddu * es) % 16 == 0 && ((int64_t)T * F * 2) % 16 == 0;
     if (bf16io)
         VPL_SWITCH(F, hipLaunchKernelGGL((ln_gate_bwd_kernel<V, true>), grid, dim3(256), 0, st, dG, ldg, U, ldu, O,
-                                         ldo, stats, dU, lddu, dO, scale, T, F, aligned && F == 64 * V && V % 8 == 0));
+                                         ldo, stats, dU, lddu, dO, scale, T, F, aligned && F == 64 * V && V % 8 == 0, zrows, zF));
     else
         VPL_SWITCH(F, hipLaunchKernelGGL((ln_gate_bwd_kernel<V, false>), grid, dim3(256), 0, st, dG, ldg, U, ldu, O,
-                                         ldo, stats, dU, lddu, dO, scale, T, F, aligned && F == 64 * V && V % 8 == 0));
+                                         ldo, stats, dU, lddu, dO, scale, T, F, aligned && F == 64 * V && V % 8 == 0, zrows, zF));
     return hipGetLastError();
 }

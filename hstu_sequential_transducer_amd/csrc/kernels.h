@@ -57,9 +57,11 @@ hipError_t launch_attn_fwd_f32(const AttnFwdArgs &a, int max_items, hipStream_t 
 hipError_t launch_ln_gate_fwd(const float *O, int64_t ldo, int nparts, int64_t part_stride, const void *U, int64_t ldu,
                               bool bf16io, void *G, int64_t ldg, float *stats, float *o_copy, int64_t ld_oc, int T,
                               int F, float eps, const int *status, hipStream_t st);
+// zrows (optional, 16-byte aligned, zF a multiple of 4): rows [T][zF] of an
+// fp32 buffer zeroed on the way (the dQ accumulator).
 hipError_t launch_ln_gate_bwd(const void *dG, int64_t ldg, const void *U, int64_t ldu, const float *O, int64_t ldo,
                               const float *stats, bool bf16io, void *dU, int64_t lddu, bf16 *dO, float scale, int T,
-                              int F, const int *status, hipStream_t st);
+                              int F, float *zrows, int zF, const int *status, hipStream_t st);
 
 // ---- attention backward (attn_bwd.hip)
 struct AttnBwdArgs {

@@ -186,8 +186,8 @@ __global__ void __launch_bounds__(256) reltime_kernel(const int32_t *__restrict_
     }
 }
 
-// Rows of split items: grid (B, 32), each workgroup every 32nd of one
-// sequence's rows from tile * t_split on.
+// Rows of split items: grid (B, 128), workgroup y takes every 128th row of
+// sequence b from tile * t_split on; 16-byte stores when the rows allow them.
 __global__ void __launch_bounds__(256) zero_split_rows_kernel(const int32_t *__restrict__ offsets, int tile,
                                                                const int *__restrict__ t_split, float *__restrict__ o32,
                                                                int64_t ld, int F, const int *__restrict__ status)
@@ -195,15 +195,25 @@ __global__ void __launch_bounds__(256) zero_split_rows_kernel(const int32_t *__r
     if (*status) return;
     const int b = blockIdx.x;
     const int o_b = offsets[b], L = offsets[b + 1] - o_b;
-    for (int64_t r = (int64_t)tile * *t_split + blockIdx.y; r < L; r += gridDim.y)
-        for (int c = threadIdx.x; c < F; c += 256) o32[(o_b + r) * ld + c] = 0.f;
+    const int64_t r0 = (int64_t)tile * *t_split;
+    if (r0 >= L) return;
+    const bool vec = ((((uintptr_t)o32) | (uintptr_t)(ld * 4) | (uintptr_t)(F * 4)) & 15) == 0;
+    if (vec) {
+        const int f4 = F / 4;
+        for (int64_t r = r0 + blockIdx.y; r < L; r += gridDim.y)
+            for (int c = threadIdx.x; c < f4; c += 256)
+                *(floatx4 *)(o32 + (o_b + r) * ld + 4 * c) = floatx4{0.f, 0.f, 0.f, 0.f};
+    } else {
+        for (int64_t r = r0 + blockIdx.y; r < L; r += gridDim.y)
+            for (int c = threadIdx.x; c < F; c += 256) o32[(o_b + r) * ld + c] = 0.f;
+    }
 }
 
 hipError_t launch_zero_split_rows(const int32_t *offsets, int B, int tile, const int *t_split, float *o32, int64_t ld,
                                   int F, const int *status, hipStream_t st)
 {
     if (B <= 0) return hipSuccess;
-    hipLaunchKernelGGL(zero_split_rows_kernel, dim3(B, 32), dim3(256), 0, st, offsets, tile, t_split, o32, ld, F,
+    hipLaunchKernelGGL(zero_split_rows_kernel, dim3(B, 128), dim3(256), 0, st, offsets, tile, t_split, o32, ld, F,
                        status);
     return hipGetLastError();
 }
