@@ -66,10 +66,15 @@ int max_items_for(int B, int T, int tile, int H)
 
 // Workspace of the attention entry points.
 struct AttnWs {
-    size_t header, items, rel, wide, obuf, dq, dO, total;
+    size_t header, items, rel, wide, obuf, dO, ds_base, ds, dq, total;
+    int64_t ds_cap; // elements of the dS buffer
 };
 
-AttnWs attn_ws(const hstu_jagged *j, const hstu_dims *dm, int tile)
+// The backward (bwd = true) also carves the dS buffer: H planes of P x P
+// bf16 per sequence, P = L rounded up to DS_PAD.  sum_b P_b^2 <= (n_max +
+// DS_PAD - 1) (T + (DS_PAD - 1) B) for sequences no longer than n_max; a
+// sequence beyond what is left takes the fp32-atomic dQ path instead.
+AttnWs attn_ws(const hstu_jagged *j, const hstu_dims *dm, int tile, bool bwd)
 {
     AttnWs w{};
     Carver c;
@@ -79,8 +84,13 @@ AttnWs attn_ws(const hstu_jagged *j, const hstu_dims *dm, int tile)
     w.rel = c.take((size_t)T * 4 * 3); // rel, then rmin and rmax per 32-token block
     w.wide = c.take((size_t)B * 4);
     w.obuf = c.take((size_t)T * H * dm->d_v * 4);
-    w.dq = c.take((size_t)T * H * dm->d_qk * 4);
-    w.dO = c.take((size_t)T * H * dm->d_v * 2 * 2); // hi and lo bf16 planes
+    if (bwd) {
+        w.dO = c.take((size_t)T * H * dm->d_v * 2 * 2); // hi and lo bf16 planes
+        w.ds_base = c.take((size_t)B * 8);
+        w.ds_cap = ((int64_t)j->n_max + DS_PAD - 1) * ((int64_t)T + (int64_t)(DS_PAD - 1) * B) * H;
+        w.ds = c.take((size_t)w.ds_cap * 2);
+        w.dq = c.take((size_t)T * H * dm->d_qk * 4); // dQ accumulator of sequences beyond the dS buffer
+    }
     w.total = c.cur;
     return w;
 }
@@ -206,7 +216,7 @@ hstu_status attn_fwd_launch(const hstu_jagged *j, const hstu_dims *dm, const hst
     {
         ProfScope ps("sched_kernel", st);
         launch_sched(j->offsets, j->ts, B, T, tile, H, status, n_items, items, max_items, rel, wide,
-                     split ? concurrent_slots() : 0, t_split, st);
+                     split ? concurrent_slots() : 0, t_split, nullptr, 0, st);
     }
     TRY(launched(hipGetLastError(), "schedule kernel"));
     if (split) {
@@ -274,7 +284,7 @@ struct LayerWs {
 LayerWs layer_ws(const hstu_jagged *j, const hstu_dims *dm)
 {
     LayerWs w{};
-    w.attn = attn_ws(j, dm, fwd_tile(dm));
+    w.attn = attn_ws(j, dm, fwd_tile(dm), false);
     Carver c;
     c.cur = w.attn.total;
     const size_t es = elem_size(dm->dtype), T = (size_t)j->total, HD = (size_t)dm->heads * dm->d_qk;
@@ -383,8 +393,8 @@ size_t hstu_workspace_size(hstu_op op, const hstu_jagged *j, const hstu_dims *di
 {
     if (check_jagged(j) != HSTU_OK || check_dims(dims) != HSTU_OK) return 0;
     switch (op) {
-    case HSTU_OP_ATTN_FWD: return attn_ws(j, dims, fwd_tile(dims)).total;
-    case HSTU_OP_ATTN_BWD: return attn_ws(j, dims, BWD_BN).total;
+    case HSTU_OP_ATTN_FWD: return attn_ws(j, dims, fwd_tile(dims), false).total;
+    case HSTU_OP_ATTN_BWD: return attn_ws(j, dims, BWD_BN, true).total;
     case HSTU_OP_LAYER_FWD: return layer_ws(j, dims).total;
     case HSTU_OP_MFALCON:
         if (d_model < 1 || total_cand < 0) {
@@ -412,7 +422,7 @@ hstu_status hstu_attn_fwd(const hstu_jagged *j, const hstu_dims *dm, const hstu_
     TRY(check_view(u.ptr, u.ld, (int64_t)F, "u", false));
     TRY(check_view(out.ptr, out.ld, (int64_t)F, "out"));
     if (ln_stats && !u.ptr) return fail(HSTU_ERR_ARG, "ln_stats requires u (the epilogue)");
-    const AttnWs w = attn_ws(j, dm, fwd_tile(dm));
+    const AttnWs w = attn_ws(j, dm, fwd_tile(dm), false);
     TRY(check_ws(ws, ws_bytes, w.total));
     hipStream_t st = (hipStream_t)stream;
     TRY(attn_fwd_launch(j, dm, bias, q, k, v, u, out, o_save, ln_stats, (char *)ws, w, st));
@@ -448,7 +458,7 @@ hstu_status hstu_attn_bwd(const hstu_jagged *j, const hstu_dims *dm, const hstu_
         return fail(HSTU_ERR_ARG, "drab_p needs a per-head rab_p (hstride != 0)");
     if (drab_t && has_t && bias->rab_t_hstride == 0)
         return fail(HSTU_ERR_ARG, "drab_t needs a per-head rab_t (hstride != 0)");
-    const AttnWs w = attn_ws(j, dm, BWD_BN);
+    const AttnWs w = attn_ws(j, dm, BWD_BN, true);
     TRY(check_ws(ws, ws_bytes, w.total));
     hipStream_t st = (hipStream_t)stream;
     char *wb = (char *)ws;
@@ -456,21 +466,23 @@ hstu_status hstu_attn_bwd(const hstu_jagged *j, const hstu_dims *dm, const hstu_
     int2 *items = (int2 *)(wb + w.items);
     uint32_t *rel = (uint32_t *)(wb + w.rel);
     int32_t *wide = (int32_t *)(wb + w.wide);
-    float *dq_acc = (float *)(wb + w.dq);
     bf16 *dO = (bf16 *)(wb + w.dO);
+    int64_t *ds_base = (int64_t *)(wb + w.ds_base);
+    bf16 *ds = (bf16 *)(wb + w.ds);
+    float *dq_acc = (float *)(wb + w.dq);
     const int T = j->total, B = j->batch, N = j->n_max;
     const int max_items = max_items_for(B, T, BWD_BN, H);
     const int64_t p_hs = has_p ? bias->rab_p_hstride : 2 * (int64_t)N + 1;
     const int64_t t_hs = (bias && bias->rab_t) ? bias->rab_t_hstride : 128;
     {
         ProfScope ps("sched_kernel", st);
-        launch_sched(j->offsets, j->ts, B, T, BWD_BN, H, status, n_items, items, max_items, rel, wide, 0, nullptr, st);
+        launch_sched(j->offsets, j->ts, B, T, BWD_BN, H, status, n_items, items, max_items, rel, wide, 0, nullptr,
+                     ds_base, w.ds_cap, st);
     }
     TRY(launched(hipGetLastError(), "schedule kernel"));
     {
         ProfScope ps("fill_zero_kernel", st);
-        // (with the gate, the LayerNorm backward below zeroes dq_acc's rows)
-        if (!u.ptr) TRY(launched(launch_fill_zero(dq_acc, (size_t)T * H * d * 4, st), "zero fill"));
+        TRY(launched(launch_zero_dqa_rows(j->offsets, B, ds_base, dq_acc, H * d, status, st), "zero fill"));
         if (drab_p) TRY(launched(launch_fill_zero(drab_p, (size_t)H * p_hs * 4, st), "zero fill"));
         if (drab_t) TRY(launched(launch_fill_zero(drab_t, (size_t)H * t_hs * 4, st), "zero fill"));
     }
@@ -478,7 +490,7 @@ hstu_status hstu_attn_bwd(const hstu_jagged *j, const hstu_dims *dm, const hstu_
     if (u.ptr) {
         ProfScope ps("ln_gate_bwd_kernel", st);
         TRY(launched(launch_ln_gate_bwd(dout.ptr, dout.ld, u.ptr, u.ld, o_save, F, ln_stats, true, du.ptr, du.ld, dO,
-                                        inv_n, T, F, dq_acc, H * d, status, st),
+                                        inv_n, T, F, nullptr, 0, status, st),
                      "LayerNorm gate backward kernel"));
     } else {
         ProfScope ps("scale_bf16_kernel", st);
@@ -507,6 +519,8 @@ hstu_status hstu_attn_bwd(const hstu_jagged *j, const hstu_dims *dm, const hstu_
     a.N = N;
     a.items = items;
     a.n_items = n_items;
+    a.ds = ds;
+    a.ds_base = ds_base;
     a.dq_acc = dq_acc;
     a.dk = (bf16 *)dk.ptr;
     a.dv = (bf16 *)dv.ptr;
@@ -519,9 +533,20 @@ hstu_status hstu_attn_bwd(const hstu_jagged *j, const hstu_dims *dm, const hstu_
         TRY(launched(launch_attn_bwd_bf16(a, max_items, st), "attention backward kernel"));
     }
     {
-        ProfScope ps("cast_kernel", st);
-        TRY(launched(launch_cast_f32_to_bf16(dq_acc, (int64_t)H * d, (bf16 *)dq.ptr, dq.ld, T, H * d, status, st),
-                     "cast kernel"));
+        DqArgs qa{};
+        qa.ds = ds;
+        qa.ds_base = ds_base;
+        qa.dq_acc = dq_acc;
+        qa.ldacc = (int64_t)H * d;
+        qa.k = (const bf16 *)k.ptr;
+        qa.ldk = k.ld;
+        qa.offsets = j->offsets;
+        qa.items = items;
+        qa.n_items = n_items;
+        qa.dq = (bf16 *)dq.ptr;
+        qa.lddq = dq.ld;
+        ProfScope ps("dq_gemm_kernel", st);
+        TRY(launched(launch_dq_gemm(qa, max_items, st), "dQ kernel"));
     }
     TRY(debug_check(ws, st));
     return ok();

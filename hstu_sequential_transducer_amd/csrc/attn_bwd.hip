@@ -281,8 +281,8 @@ DEV bf16x8 slice8(const floatx16 &f, int o)
                            __builtin_bit_cast(uint32_t, e2), __builtin_bit_cast(uint32_t, e3)});
 }
 
-template <bool HP, int TM, bool DT>
-DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
+template <bool HP, int TM, bool DT, bool DQA>
+DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int k0, int h)
 {
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, lq = l & 31;
     const int p = w & 3;          // key group: keys 32p..32p+31 of the tile
@@ -293,20 +293,23 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
     // transposing-read lane constants
     const int tj = l & 15, tsl = tj >> 2;
     const int cpart = ((l >> 4) & 1) * 16 + 4 * (tj & 3);
-    bf16 *kt = &sm.ds[0][0]; // prologue only: the workgroup's K rows, swizzled like the stage tiles
 
-    // ---- prologue: the workgroup's K rows into LDS (rows past the sequence
-    // repeat the last row: finite, and every pair they form is masked or has
-    // dS = 0); an accumulating wave keeps d-block p of all 128 rows in
-    // registers (B operand of dQ = dS K).  A pointwise wave's own K and V rows
-    // come straight from memory.
+    // ---- prologue: a pointwise wave's own K and V rows come straight from
+    // memory into registers.  DQA (dQ by atomics, for a sequence whose dS
+    // planes do not fit the dS buffer): the workgroup's K rows also go to LDS
+    // (rows past the sequence repeat the last row: finite, and every pair
+    // they form is masked or has dS = 0), from where an accumulating wave
+    // keeps d-block p of all 128 rows in registers (B operand of dQ = dS K).
+    bf16 *kt = &sm.ds[0][0]; // prologue only
+    if constexpr (DQA) {
 #pragma unroll
-    for (int i = 0; i < BN / (4 * NW); i++) {
-        const int r0 = 4 * ((BN / (4 * NW)) * w + i), row = r0 + (l >> 4);
-        const int c = (l & 15) ^ swf(row);
-        const int key = min(k0 + row, L - 1);
-        __builtin_amdgcn_global_load_lds((const void *)(K + (int64_t)(o_b + key) * a.ldk + h * D + c * 8),
-                                         (lds_void *)(kt + r0 * D), 16, 0, 0);
+        for (int i = 0; i < BN / (4 * NW); i++) {
+            const int r0 = 4 * ((BN / (4 * NW)) * w + i), row = r0 + (l >> 4);
+            const int c = (l & 15) ^ swf(row);
+            const int key = min(k0 + row, L - 1);
+            __builtin_amdgcn_global_load_lds((const void *)(K + (int64_t)(o_b + key) * a.ldk + h * D + c * 8),
+                                             (lds_void *)(kt + r0 * D), 16, 0, 0);
+        }
     }
     const int kw0 = k0 + 32 * p; // this key group's first key
     const int mykey = kw0 + lq;
@@ -451,7 +454,7 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
         }
     };
 
-    // stage 0, then the K tile's d-block p into the accumulating waves' registers
+    // stage 0
     const std::integral_constant<int, NW> all_waves{};
     const std::integral_constant<int, NW / 2> half_waves{};
     if (k0 + BQ <= L) gload_direct(all_waves, w, k0, sm.sq[0], sm.sp[0]);
@@ -460,18 +463,20 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
     sstore_tables(sm.sp[0], tid);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    bf16x8 opnd[8]; // accumulating wave: K d-block p of all rows (dQ operand)
-    if (awave) {
+    bf16x8 opnd[DQA ? 8 : 1]; // DQA, accumulating wave: K d-block p of all rows (dQ operand)
+    if constexpr (DQA) {
+        if (awave) {
 #pragma unroll
-        for (int t = 0; t < BN / 16; t++) {
-            const int kr1 = 16 * t + 8 * g + tsl;
-            const u32x2 k1 = lds_read_tr(&kt[swz(kr1, 32 * p + cpart)]);
-            const u32x2 k2 = lds_read_tr(&kt[swz(kr1 + 4, 32 * p + cpart)]);
-            opnd[t] = as_bf16x8(u32x4{k1[0], k1[1], k2[0], k2[1]});
+            for (int t = 0; t < BN / 16; t++) {
+                const int kr1 = 16 * t + 8 * g + tsl;
+                const u32x2 k1 = lds_read_tr(&kt[swz(kr1, 32 * p + cpart)]);
+                const u32x2 k2 = lds_read_tr(&kt[swz(kr1 + 4, 32 * p + cpart)]);
+                opnd[t] = as_bf16x8(u32x4{k1[0], k1[1], k2[0], k2[1]});
+            }
         }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads(); // the K tile is dead (ds and pt are written from block 0 on)
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads(); // the K tile is dead (ds and pt are written from block 0 on)
 
     const int p_hs = a.rp_hs > 0 ? (int)a.rp_hs : 2 * a.N + 1;
     const int t_hs = a.rt_hs > 0 ? (int)a.rt_hs : 128;
@@ -524,47 +529,44 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
         }
         __builtin_amdgcn_sched_barrier(0);
     };
-    // Accumulating wave: dQ of the block at q0m from the dS tile `dst` (all
-    // 128 keys): dQ[32 queries][d-block p] = sum over the keys of dS[q][key] K[key][d]
+    // Accumulating wave p: keys 32p..32p+31 of the block's dS tile `dst`
+    // ([key][query] in LDS) go to the dS buffer ([query][key] rows of P
+    // elements; dQ = dS K is a separate product).  The transposing reads give
+    // each lane 8 consecutive keys of its query (lq): one 16-byte store per
+    // 16-key step.
+    const int64_t P_ds = ((int64_t)L + DS_PAD - 1) / DS_PAD * DS_PAD;
+    bf16 *ds_plane = DQA ? nullptr : a.ds + a.ds_base[b_seq] + (int64_t)h * P_ds * P_ds;
+    auto ds_store = [&](const bf16 *dst, int q0m) {
+#pragma unroll
+        for (int tt = 0; tt < 2; tt++) {
+            const int t = 2 * p + tt;
+            const int kr1 = 16 * t + 8 * g + tsl;
+            const u32x2 s1 = lds_read_tr(&dst[kr1 * SS + cpart]);
+            const u32x2 s2 = lds_read_tr(&dst[(kr1 + 4) * SS + cpart]);
+            *(u32x4 *)(ds_plane + (int64_t)(q0m + lq) * P_ds + k0 + 16 * t + 8 * g) = u32x4{s1[0], s1[1], s2[0], s2[1]};
+        }
+    };
+    // DQA, accumulating wave: dQ of the block at q0m from the dS tile `dst`
+    // (all 128 keys): dQ[32 queries][d-block p] = sum over the keys of
+    // dS[q][key] K[key][d], added to the fp32 accumulator with atomics.
     auto dq_block = [&](const bf16 *dst, int q0m, bool full) {
         floatx16 qacc;
 #pragma unroll
         for (int r = 0; r < 16; r++) qacc[r] = 0.f;
-        __builtin_amdgcn_sched_barrier(0);
-        bf16x8 fs[4];
-        auto fetch = [&](int t) {
+#pragma unroll
+        for (int t = 0; t < BN / 16; t++) {
             const int kr1 = 16 * t + 8 * g + tsl;
             const u32x2 s1 = lds_read_tr(&dst[kr1 * SS + cpart]);
             const u32x2 s2 = lds_read_tr(&dst[(kr1 + 4) * SS + cpart]);
-            fs[t & 3] = as_bf16x8(u32x4{s1[0], s1[1], s2[0], s2[1]});
-        };
-        fetch(0);
-        fetch(1);
-        fetch(2);
-#pragma unroll
-        for (int t = 0; t < BN / 16; t++) {
-            if (t + 3 < BN / 16) fetch(t + 3);
-            qacc = mfma32(fs[t & 3], opnd[t], qacc);
+            qacc = mfma32(as_bf16x8(u32x4{s1[0], s1[1], s2[0], s2[1]}), opnd[DQA ? t : 0], qacc);
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-        for (int t = 0; t < BN / 16; t++) {
-            if (t + 3 < BN / 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
         // C layout: lane holds d = 32p + lq, queries 8(r/4) + 4g + r%4
         float *dqp = a.dq_acc + (int64_t)(o_b + q0m + 4 * g) * ld_do + h * D + 32 * p + lq;
-        if (full) {
+        const int qlim = full ? BQ : L - q0m - 4 * g;
 #pragma unroll
-            for (int r = 0; r < 16; r++) atomicAdd(dqp + (int64_t)(8 * (r >> 2) + (r & 3)) * ld_do, qacc[r]);
-        } else {
-            const int qlim = L - q0m - 4 * g;
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int qq = 8 * (r >> 2) + (r & 3);
-                if (qq < qlim) atomicAdd(dqp + (int64_t)qq * ld_do, qacc[r]);
-            }
+        for (int r = 0; r < 16; r++) {
+            const int qq = 8 * (r >> 2) + (r & 3);
+            if (qq < qlim) atomicAdd(dqp + (int64_t)qq * ld_do, qacc[r]);
         }
     };
     // Accumulating waves: drab_p of the block at q0m from its skewed tile
@@ -644,7 +646,8 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
             if (!skipm) acc_block(sm.sq[n % 3 == 0 ? 2 : n % 3 - 1], (n - 1) & 1);
         }
         if (MAIN || n > 0) {
-            dq_block(sm.ds[(n - 1) & 1], q0m, MAIN ? true : q0 <= L);
+            if constexpr (DQA) dq_block(sm.ds[(n - 1) & 1], q0m, MAIN ? true : q0 <= L);
+            else ds_store(sm.ds[(n - 1) & 1], q0m);
             if (a.drab_p) drabp_sum(sm.dsk[(n - 1) & 1], q0m, tot, dlf);
         }
         if ((MAIN || n > 0) && a.drab_p) drabp_flush(dlf, tot);
@@ -807,7 +810,8 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int o_b, int L, int k0, int h)
         // the accumulators are dead on the pointwise waves' path)
         const bool skipm = kw0 > qlast + BQ - 1 || kw0 >= L;
         if (!skipm) acc_block(sm.sq[(nqb - 1) % 3], (nqb - 1) & 1);
-        dq_block(sm.ds[(nqb - 1) & 1], qlast, qlast + BQ <= L);
+        if constexpr (DQA) dq_block(sm.ds[(nqb - 1) & 1], qlast, qlast + BQ <= L);
+        else ds_store(sm.ds[(nqb - 1) & 1], qlast);
         if (a.drab_p) {
             int dlf = 0;
             float tot = 0.f;
@@ -889,9 +893,17 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
     // (the first barrier inside bwd_body orders these writes before use)
     constexpr bool DT = TMODE == 1;
-    if constexpr (TMODE == 0) bwd_body<HP, 0, false>(a, sm, o_b, L, k0, h);
-    else if (a.wide[b] != 0) bwd_body<HP, 2, DT>(a, sm, o_b, L, k0, h);
-    else bwd_body<HP, 1, DT>(a, sm, o_b, L, k0, h);
+    const bool dqa = a.ds_base[b] < 0; // this sequence's dS planes did not fit: dQ by atomics
+    if constexpr (TMODE == 0) {
+        if (dqa) bwd_body<HP, 0, false, true>(a, sm, b, o_b, L, k0, h);
+        else bwd_body<HP, 0, false, false>(a, sm, b, o_b, L, k0, h);
+    } else if (a.wide[b] != 0) {
+        if (dqa) bwd_body<HP, 2, DT, true>(a, sm, b, o_b, L, k0, h);
+        else bwd_body<HP, 2, DT, false>(a, sm, b, o_b, L, k0, h);
+    } else {
+        if (dqa) bwd_body<HP, 1, DT, true>(a, sm, b, o_b, L, k0, h);
+        else bwd_body<HP, 1, DT, false>(a, sm, b, o_b, L, k0, h);
+    }
 }
 
 namespace {

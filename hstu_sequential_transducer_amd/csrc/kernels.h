@@ -16,10 +16,17 @@ constexpr int SCHED_BINS = 4096; // longest sequence: (SCHED_BINS - 1) tiles
 // tile's key range) where t_split is chosen from the total work so that no
 // item is much longer than the average per slot; *t_split is written (a
 // large value when nothing is split).
+//
+// ds_base (optional): per sequence, the element offset of its dS blocks in
+// the backward's dS buffer (H planes of P x P bf16, P = L rounded up to 128):
+// the exclusive prefix sum of the plane sizes, or -1 where that prefix plus
+// the sequence's own planes exceeds ds_cap elements (its dQ then goes
+// through fp32 atomics).
 constexpr int ITEM_T_SHIFT = 10;
+constexpr int DS_PAD = 128;
 void launch_sched(const int32_t *offsets, const int64_t *ts, int B, int T, int tile, int H, int *status, int *n_items,
                   int2 *items, int max_items, uint32_t *rel, int32_t *wide, int split_slots, int *t_split,
-                  hipStream_t st);
+                  int64_t *ds_base, int64_t ds_cap, hipStream_t st);
 // Zeroes the fp32 rows [offsets[b] + tile * t_split, offsets[b + 1]) of
 // every sequence (the rows that split items accumulate into).
 hipError_t launch_zero_split_rows(const int32_t *offsets, int B, int tile, const int *t_split, float *o32, int64_t ld,
@@ -81,7 +88,9 @@ struct AttnBwdArgs {
     int H, N;
     const int2 *items;
     const int *n_items;
-    float *dq_acc;              // fp32 [T][H*d] accumulator, zeroed
+    bf16 *ds;                   // dS buffer (see launch_sched's ds_base), written for dQ = dS K
+    const int64_t *ds_base;     // per sequence: offset of its H planes of P x P in ds, -1: did not fit
+    float *dq_acc;              // fp32 [T][H*d] accumulator of the sequences that did not fit (rows zeroed)
     bf16 *dk, *dv;
     int64_t lddk, lddv;
     float *drab_p;              // fp32 [H][2N+1] accumulator (zeroed) or NULL
@@ -89,6 +98,26 @@ struct AttnBwdArgs {
 };
 constexpr int BWD_BN = 128; // keys per workgroup
 hipError_t launch_attn_bwd_bf16(const AttnBwdArgs &a, int max_items, hipStream_t st);
+
+// ---- dQ = dS K (dq.hip): one workgroup per backward item read as
+// (sequence b, query tile t of 128, head h); bf16 dQ out (d = 128).
+struct DqArgs {
+    const bf16 *ds;             // the backward's dS buffer
+    const int64_t *ds_base;     // -1: the sequence's dQ is in dq_acc (converted here)
+    const float *dq_acc;
+    int64_t ldacc;
+    const bf16 *k;
+    int64_t ldk;
+    const int32_t *offsets;
+    const int2 *items;
+    const int *n_items;
+    bf16 *dq;
+    int64_t lddq;
+};
+hipError_t launch_dq_gemm(const DqArgs &a, int max_items, hipStream_t st);
+// Zeroes the dq_acc rows ([T][F] fp32) of the sequences with ds_base < 0.
+hipError_t launch_zero_dqa_rows(const int32_t *offsets, int B, const int64_t *ds_base, float *dq_acc, int F,
+                                const int *status, hipStream_t st);
 
 // ---- small helpers (misc.hip)
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st);

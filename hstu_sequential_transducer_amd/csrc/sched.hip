@@ -28,6 +28,24 @@ __device__ int block_suffix_excl(int v, int *tmp)
     return incl - v + later;
 }
 
+// Exclusive prefix sum over the 1024 threads of the block (64-bit); `tmp` is
+// a 16-entry LDS array.
+__device__ long long block_prefix_excl64(long long v, long long *tmp)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    long long incl = v;
+    for (int o = 1; o < 64; o <<= 1) {
+        const long long x = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += x;
+    }
+    __syncthreads();
+    if (lane == 63) tmp[wv] = incl;
+    __syncthreads();
+    long long before = 0;
+    for (int k = 0; k < wv; k++) before += tmp[k];
+    return before + incl - v;
+}
+
 // One workgroup of 1024 threads.  An item is (sequence b, tile t, head h);
 // a tile t of sequence b costs t + 1 units (causal), so items are ordered by
 // t descending.  With pi = the sequences sorted by tile count descending,
@@ -47,9 +65,11 @@ __global__ void __launch_bounds__(1024) sched_kernel(const int32_t *__restrict__
                                                       int *__restrict__ status, int *__restrict__ n_items,
                                                       int2 *__restrict__ items, int max_items,
                                                       int32_t *__restrict__ wide, int split_slots,
-                                                      int *__restrict__ t_split_out)
+                                                      int *__restrict__ t_split_out, int64_t *__restrict__ ds_base,
+                                                      int64_t ds_cap)
 {
     __shared__ int hist[SCHED_BINS];
+    __shared__ long long ptmp[16];
     __shared__ int fill[SCHED_BINS];
     __shared__ int S[SCHED_BINS];
     __shared__ int bad;
@@ -77,6 +97,21 @@ __global__ void __launch_bounds__(1024) sched_kernel(const int32_t *__restrict__
         }
     }
     __syncthreads();
+    if (ds_base && !bad) {
+        // dS block offsets: thread tid owns sequences [tid * per, (tid + 1) * per)
+        const int per = (B + 1023) / 1024, b0 = tid * per, b1 = min(B, b0 + per);
+        long long own = 0;
+        for (int b = b0; b < b1; b++) {
+            const long long P = ((long long)(offsets[b + 1] - offsets[b]) + DS_PAD - 1) / DS_PAD * DS_PAD;
+            own += P * P * H;
+        }
+        long long run = block_prefix_excl64(own, ptmp);
+        for (int b = b0; b < b1; b++) {
+            const long long P = ((long long)(offsets[b + 1] - offsets[b]) + DS_PAD - 1) / DS_PAD * DS_PAD;
+            ds_base[b] = run + P * P * H <= ds_cap ? run : -1;
+            run += P * P * H;
+        }
+    }
     if (bad) {
         if (tid == 0) {
             *status = bad;
@@ -218,12 +253,34 @@ hipError_t launch_zero_split_rows(const int32_t *offsets, int B, int tile, const
     return hipGetLastError();
 }
 
+// dq_acc rows of the sequences whose dS planes did not fit: grid (B, 32).
+__global__ void __launch_bounds__(256) zero_dqa_rows_kernel(const int32_t *__restrict__ offsets,
+                                                             const int64_t *__restrict__ ds_base,
+                                                             float *__restrict__ dq_acc, int F,
+                                                             const int *__restrict__ status)
+{
+    if (*status) return;
+    const int b = blockIdx.x;
+    if (ds_base[b] >= 0) return;
+    const int o_b = offsets[b], L = offsets[b + 1] - o_b;
+    for (int64_t r = blockIdx.y; r < L; r += gridDim.y)
+        for (int c = threadIdx.x; c < F; c += 256) dq_acc[(o_b + r) * (int64_t)F + c] = 0.f;
+}
+
+hipError_t launch_zero_dqa_rows(const int32_t *offsets, int B, const int64_t *ds_base, float *dq_acc, int F,
+                                const int *status, hipStream_t st)
+{
+    if (B <= 0) return hipSuccess;
+    hipLaunchKernelGGL(zero_dqa_rows_kernel, dim3(B, 32), dim3(256), 0, st, offsets, ds_base, dq_acc, F, status);
+    return hipGetLastError();
+}
+
 void launch_sched(const int32_t *offsets, const int64_t *ts, int B, int T, int tile, int H, int *status, int *n_items,
                   int2 *items, int max_items, uint32_t *rel, int32_t *wide, int split_slots, int *t_split,
-                  hipStream_t st)
+                  int64_t *ds_base, int64_t ds_cap, hipStream_t st)
 {
     hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(1024), 0, st, offsets, B, T, tile, H, status, n_items, items,
-                       max_items, wide, split_slots, t_split);
+                       max_items, wide, split_slots, t_split, ds_base, ds_cap);
     if (ts && T > 0)
         hipLaunchKernelGGL(reltime_kernel, dim3((T + 255) / 256), dim3(256), 0, st, offsets, ts, rel, wide, B, T, status);
 }

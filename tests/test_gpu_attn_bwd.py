@@ -75,8 +75,12 @@ def test_bwd_without_bias_terms_and_wide_times():
     check_all(g, ref)
 
 
-def test_bwd_clip_beyond_n_max():
-    w = with_grad(23, [300, 41], n_max=100, act_std=0.5)
+@pytest.mark.parametrize("lengths", [[300, 41], [41, 300]])
+def test_bwd_clip_beyond_n_max(lengths):
+    """Sequences longer than n_max: rab_p clips, and the dS buffer (sized
+    from n_max) overflows, so dQ of the sequences that do not fit takes the
+    fp32-atomic path ([41, 300]: the first fits, the second does not)."""
+    w = with_grad(23, lengths, n_max=100, act_std=0.5)
     g = gpu_fwd_bwd(w)
     ref = oracle.attn_bwd(w.offsets, w.ts, w.q, w.k, w.v, w.rab_p, w.rab_t, w.n_max, w.u, w.ln_eps, w.dg)
     check_all(g, ref)
