@@ -62,6 +62,7 @@ def src_digest(files):
 KERNEL_SOURCES = {
     "attn_bwd_bf16_kernel": ("attn_bwd.hip", "common.h", "kernels.h"),
     "attn_fwd_bf16_kernel": ("attn_fwd.hip", "common.h", "kernels.h"),
+    "dq_gemm_kernel": ("dq.hip", "common.h", "kernels.h"),
 }
 
 
@@ -271,9 +272,12 @@ def main():
     f_fwd = 2.0 * H * d * S2
     f_bwd = 2.0 * f_fwd
     tflops = (f_fwd + f_bwd) / (ms * 1e-3) / 1e12
-    # dominant kernel: the largest share of the timed region
+    # dominant kernel: the largest share of the timed region.  The backward's
+    # four products per pair: dV, dP, dK in attn_bwd, dQ = dS K in dq_gemm.
     dom = max(per_kernel.items(), key=lambda kv: kv[1]["total_ms"])[0]
-    dom_flops = {"attn_bwd_bf16_kernel": f_bwd, "attn_fwd_bf16_kernel": f_fwd}.get(dom)
+    kernel_flops = {"attn_bwd_bf16_kernel": 0.75 * f_bwd, "dq_gemm_kernel": 0.25 * f_bwd,
+                    "attn_fwd_bf16_kernel": f_fwd}
+    dom_flops = kernel_flops.get(dom)
     avg = per_kernel[dom]["avg_ms"]
     roof = None
     if dom_flops is not None:
@@ -288,6 +292,9 @@ def main():
                 "algorithmic_flops_per_launch": dom_flops, "kernel_src": src_digest(KERNEL_SOURCES[dom])}
     fwd_ms = per_kernel.get("attn_fwd_bf16_kernel", {}).get("avg_ms")
     bwd_ms = per_kernel.get("attn_bwd_bf16_kernel", {}).get("avg_ms")
+    dq_ms = per_kernel.get("dq_gemm_kernel", {}).get("avg_ms")
+    if bwd_ms and dq_ms:
+        bwd_ms += dq_ms
     res = {
         "metric": "HSTU attention fwd+bwd TFLOP/s & % MFMA peak, jagged N_max=8192",
         "value": round(tflops, 3),
@@ -310,7 +317,9 @@ def main():
         "roofline": roof,
         "kernels": {n: {"launches": v2["launches"], "avg_ms": round(v2["avg_ms"], 5)} for n, v2 in per_kernel.items()},
         "attn_fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2) if fwd_ms else None,
-        "attn_bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2) if bwd_ms else None,
+        "attn_bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2) if bwd_ms else None,  # attn_bwd + dq_gemm
+        "kernel_tflops": {n: round(f / (per_kernel[n]["avg_ms"] * 1e-3) / 1e12, 2)
+                          for n, f in kernel_flops.items() if n in per_kernel},
     }
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 4

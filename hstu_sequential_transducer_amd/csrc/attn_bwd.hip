@@ -432,12 +432,12 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
         }
     };
 
-    // A full block's tables copied straight into LDS by the pointwise waves
-    // (4-byte copies, lane i -> 4i bytes past the wave's LDS base): the
-    // window by waves 0-2 of the role (slots 64 pw + lane), the query times
-    // and their range by wave 3 (lanes 0-31, then 32, 33).
+    // A full block's tables copied straight into LDS by the accumulating
+    // waves (4-byte copies, lane i -> 4i bytes past the wave's LDS base): the
+    // window by waves 0-2 (slots 64 w + lane), the query times and their
+    // range by wave 3 (lanes 0-31, then 32, 33).
     auto gload_tables_direct = [&](int q0, StageP &SP) {
-        const int pw = w - NW / 2;
+        const int pw = w;
         if constexpr (HP) {
             if (pw < 3 && 64 * pw + l < WIN) {
                 int dl = k0 - q0 - (BQ - 1) + 64 * pw + l;
@@ -602,9 +602,9 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
     const int krow = 32 * p + lq;
     // What every wave does at the end of block n: for a partial next block,
     // the register path of its stage and tables (64-bit times: the pointwise
-    // waves store the next block's tables); then the wait and the barrier.  The pointwise waves wait
-    // for their direct copies; the accumulating waves only for their LDS
-    // traffic (their dQ atomics stay in flight).
+    // waves store the next block's tables); then the wait and the barrier.
+    // The accumulating waves (copies) wait for their direct copies, the
+    // pointwise waves only for their LDS traffic.
     auto finish = [&](auto main_c, int n, bool copies) {
         constexpr bool MAIN = decltype(main_c)::value;
         const int q0 = k0 + n * BQ;
@@ -618,19 +618,20 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
             }
         }
         if constexpr (TM == 2)
-            if (copies && (MAIN || n + 1 < nqb)) sstore_tables(sm.sp[(n + 1) & 1], tid - NT / 2);
+            if (!copies && (MAIN || n + 1 < nqb)) sstore_tables(sm.sp[(n + 1) & 1], tid - NT / 2);
         if (copies || part) __builtin_amdgcn_s_waitcnt(0);
         else __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0)
         __syncthreads();
     };
-    // The next block's direct copies, issued by the pointwise waves (the
-    // accumulating waves' transposing LDS reads would otherwise wait for them).
+    // The next block's direct copies, issued by the accumulating waves after
+    // their last transposing LDS read of the block (such a read waits for
+    // every copy in flight).
     auto start_copy = [&](auto main_c, int n) {
         constexpr bool MAIN = decltype(main_c)::value;
         const int q0 = k0 + n * BQ;
         const int n3 = n % 3 == 2 ? 0 : n % 3 + 1;
         if (MAIN || (n + 1 < nqb && q0 + 2 * BQ <= L)) {
-            gload_direct(half_waves, w - NW / 2, q0 + BQ, sm.sq[n3], sm.sp[(n + 1) & 1]);
+            gload_direct(half_waves, w, q0 + BQ, sm.sq[n3], sm.sp[(n + 1) & 1]);
             if constexpr (TM != 2) gload_tables_direct(q0 + BQ, sm.sp[(n + 1) & 1]);
         }
     };
@@ -648,10 +649,12 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
         if (MAIN || n > 0) {
             if constexpr (DQA) dq_block(sm.ds[(n - 1) & 1], q0m, MAIN ? true : q0 <= L);
             else ds_store(sm.ds[(n - 1) & 1], q0m);
-            if (a.drab_p) drabp_sum(sm.dsk[(n - 1) & 1], q0m, tot, dlf);
         }
+        start_copy(main_c, n);
+        if (MAIN || n > 0)
+            if (a.drab_p) drabp_sum(sm.dsk[(n - 1) & 1], q0m, tot, dlf);
         if ((MAIN || n > 0) && a.drab_p) drabp_flush(dlf, tot);
-        finish(main_c, n, false);
+        finish(main_c, n, true);
     };
     // Pointwise wave, block n: X, dP, P', dS.
     int rb = 0;              // running drab_t sums of buckets rb, rb + 1 (wave-uniform)
@@ -659,7 +662,6 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
     auto iter_pw = [&](auto main_c, int n) {
         constexpr bool MAIN = decltype(main_c)::value;
         const int q0 = k0 + n * BQ;
-        start_copy(main_c, n);
         if constexpr (TM == 2)
             if (n + 1 < nqb) gload_tables(q0 + BQ, tid - NT / 2);
         const StageQ &SQn = sm.sq[n % 3];
@@ -783,7 +785,7 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
 #pragma unroll
             for (int rr = 0; rr < 16; rr++) ln.dsk[-(DKP - 1) * (8 * (rr >> 2) + (rr & 3))] = 0.f;
         }
-        finish(main_c, n, true);
+        finish(main_c, n, false);
     };
 
     // The two roles run separate loops (so that each keeps only its own
