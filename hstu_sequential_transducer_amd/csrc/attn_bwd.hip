@@ -21,14 +21,21 @@
 //     [key][query] tiles (and fp32 dS into a tile skewed by j - i for
 //     drab_p), and adds dS to drab_t;
 //   the accumulating wave (waves 0-3) works one block behind: dV^T += dO'^T P
-//     and dK^T += Q^T dS for its keys, dQ for d-block w of all 128 keys
-//     (fp32 global atomics), and the drab_p diagonal sums.
+//     and dK^T += Q^T dS for its keys, stores its 32 keys of the block's dS
+//     tile to a bf16 [query][key] plane in global memory (dQ = dS K is a
+//     separate GEMM, dq.hip), and sums the drab_p diagonals.  A sequence
+//     whose plane does not fit the dS buffer takes the other instantiation,
+//     where the accumulating wave adds dQ for d-block w of all 128 keys into
+//     an fp32 buffer with global atomics instead.
 // X, P and dS are computed once.  All products are 32x32x16 bf16 MFMA with
 // lane = key, registers = queries.  Query blocks of 32 stream through LDS,
-// copied global -> LDS directly: Q and dO' are triple buffered (block n + 1
-// lands while the pointwise waves read block n and the accumulating waves
-// block n - 1), dO'-lo and the per-block tables double buffered.  The rab_p
-// window is loaded into the X accumulator.  One barrier per query block.
+// copied global -> LDS directly by the accumulating waves right after their
+// last transposing reads of the block (so the pointwise waves, which carry
+// the longer chain, issue no copies): Q and dO' are triple buffered (block
+// n + 1 lands while the pointwise waves read block n and the accumulating
+// waves block n - 1), dO'-lo and the per-block tables double buffered.  The
+// rab_p window is loaded into the X accumulator.  One barrier per query
+// block.
 //
 // drab_p: the pointwise wave writes its fp32 dS into an LDS tile skewed by
 // j - i ([key - query][query]); one block later, one thread per diagonal sums

@@ -9,9 +9,23 @@
 // storage-dtype copy of C (the M-FALCON hidden state feeding the next layer)
 // and copies of two column ranges (this layer's K and V, the M-FALCON cache).
 //
-// bf16 kernel: 128x128 output tile per workgroup of 4 waves (64x64 each =
-// 2x2 blocks of 32x32x16 bf16 MFMA), K in steps of 32 staged through LDS
-// (double buffered).  Both operands are K-contiguous, so no transposes.
+// bf16, main kernel: 256x128 output tile per workgroup of 4 waves, each wave
+// 64 rows x 128 columns (2x4 blocks of 32x32x16 bf16 MFMA computing C^T, so
+// a lane owns a row and 4 consecutive columns per register group); two
+// workgroups per CU.  K advances in steps of 32 through three LDS stages
+// filled by direct global -> LDS copies two steps ahead, with a plain
+// barrier per step (no wait for the copies still in flight); 64-byte stage
+// rows have their 16-byte chunks XOR-swizzled by (row / 4) % 4, which keeps
+// the operand reads (16 rows at one chunk) free of bank conflicts.  The
+// epilogue (bias from LDS, activation, residual, stores and the K/V copies)
+// runs from registers with 8- or 16-byte accesses.  Workgroup i takes tile
+// (i % 8) * ceil(tiles / 8) + i / 8: consecutive workgroups go to different
+// XCDs, so this keeps the column tiles of one row block (which share A rows)
+// on one XCD and its L2.  Both operands are K-contiguous, so no transposes.
+// (Measured alternatives: a 256x256 tile with one wave per SIMD, and 64-deep
+// K steps with the tile staged through LDS for the epilogue, were slower.)
+// bf16, general kernel (shapes or alignments the main kernel does not take):
+// 128x128 tiles of 4 waves, K in steps of 32, register-staged loads.
 // fp32 kernel: plain VALU tiles for fp32 storage (small layers).
 #include "kernels.h"
 
@@ -34,7 +48,185 @@ DEV void store_out(void *p, int64_t i, float x)
     else ((float *)p)[i] = x;
 }
 
+// main kernel geometry
+// (NW waves: 4 -> 256 x 128 tiles, 8 -> 256 x 256)
+constexpr int TBM = 256, TBK = 32, TSTAGES = 3;
+template <int TBN>
+struct alignas(16) TStage {
+    alignas(16) bf16 a[TBM * TBK]; // [row][k], 64-byte rows, swizzled
+    alignas(16) bf16 w[TBN * TBK];
+};
+// 64-byte rows: 16-byte chunk c of row r sits at chunk c ^ ((r / 4) % 4), so
+// 16 consecutive rows read at one chunk cover all 16 16-byte bank groups
+DEV int tsw(int row) { return (row >> 2) & 3; }
+DEV int tswz(int row, int col) { return row * TBK + (((col >> 3) ^ tsw(row)) << 3) + (col & 7); }
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 4 consecutive outputs: one 16-byte fp32 store or one 8-byte bf16 store
+DEV void store4(void *p, int64_t i, const floatx4 &x, bool f32)
+{
+    if (f32) *(floatx4 *)((float *)p + i) = x;
+    else *(u32x2 *)((bf16 *)p + i) = u32x2{pack2_bf16(x[0], x[1]), pack2_bf16(x[2], x[3])};
+}
+
 } // namespace
+
+// EPI: activation; RES: residual none (0), bf16 (1), fp32 (2).  Waves form a
+// WGM x WGN grid; each wave owns 32 TI rows x 128 columns (TI x 4 MFMA
+// blocks); TBM = 32 TI WGM must be 256.  TI = 2 runs two waves per SIMD
+// (two workgroups per CU), TI = 4 one (its 256 accumulators use the whole
+// register file).
+template <int EPI, int RES, int TI, int WGM, int WGN>
+__global__ void __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(TI == 2 ? 2 : 1, TI == 2 ? 2 : 1)))
+gemm_bf16_tiled_kernel(GemmArgs g, int tiles_n, int n_tiles, int per_xcd)
+{
+    constexpr int NW = WGM * WGN, TBN = 128 * WGN, TNT = 64 * NW;
+    static_assert(32 * TI * WGM == TBM, "tile rows");
+    constexpr int CA = TBM / 16 / NW, CW = TBN / 16 / NW; // direct copies per wave per stage (16 rows each)
+    __shared__ TStage<TBN> st[TSTAGES];
+    __shared__ __align__(16) float bias_s[TBN];
+    const int t = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    if (t >= n_tiles) return;
+    const int mt = t / tiles_n, nt = t - mt * tiles_n;
+    const int m0 = mt * TBM, n0 = nt * TBN;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, gq = l >> 5, lq = l & 31;
+    const int wm = w % WGM, wn = w / WGM; // rows 32 TI wm, columns 128 wn of the tile
+    const bf16 *A = (const bf16 *)g.A, *W = (const bf16 *)g.W;
+    const int nk = g.K / TBK;
+    // the tile's bias (N is a multiple of 8, so a 4-column group is all in or
+    // all out); visible after the first barrier of the K loop
+    if (tid < TBN / 4) {
+        const int n = n0 + 4 * tid;
+        *(floatx4 *)&bias_s[4 * tid] = (g.bias && n < g.N) ? *(const floatx4 *)(g.bias + n) : floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // copies of step kt into stage S: 16 rows per wave instruction, A rows
+    // [16 CA w, 16 CA (w + 1)) and W rows [32w, 32w + 32); rows past M or N
+    // re-read the last row
+    auto gload = [&](int kt, TStage<TBN> &S) {
+        const int k0 = kt * TBK;
+#pragma unroll
+        for (int i = 0; i < CA; i++) {
+            const int r0 = 16 * CA * w + 16 * i, row = r0 + (l >> 2);
+            const int c = (l & 3) ^ tsw(row);
+            const int m = min(m0 + row, g.M - 1);
+            __builtin_amdgcn_global_load_lds((const void *)(A + (int64_t)m * g.lda + k0 + c * 8),
+                                             (lds_void *)(S.a + r0 * TBK), 16, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < CW; i++) {
+            const int r0 = 16 * CW * w + 16 * i, row = r0 + (l >> 2);
+            const int c = (l & 3) ^ tsw(row);
+            const int n = min(n0 + row, g.N - 1);
+            __builtin_amdgcn_global_load_lds((const void *)(W + (int64_t)n * g.K + k0 + c * 8),
+                                             (lds_void *)(S.w + r0 * TBK), 16, 0, 0);
+        }
+    };
+    static_assert(CA + CW <= 15, "wait count field");
+
+    // C^T blocks: acc[i][j] holds rows m = 32 TI wm + 32i + lane%32 (one per
+    // lane) and columns n = 128 wn + 32j + 8(r/4) + 4(lane/32) + r%4
+    // (registers)
+    floatx16 acc[TI][4];
+#pragma unroll
+    for (int i = 0; i < TI; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+
+    // one K step: 2 sub-steps of 16; operands of sub-step 1 are read while
+    // the MFMAs of sub-step 0 run
+    auto compute = [&](const TStage<TBN> &S) {
+        bf16x8 a[2][TI], b[2][4];
+        auto fetch = [&](int ks) {
+            const int col = 16 * ks + 8 * gq;
+#pragma unroll
+            for (int i = 0; i < TI; i++) a[ks][i] = *(const bf16x8 *)&S.a[tswz(32 * TI * wm + 32 * i + lq, col)];
+#pragma unroll
+            for (int j = 0; j < 4; j++) b[ks][j] = *(const bf16x8 *)&S.w[tswz(128 * wn + 32 * j + lq, col)];
+        };
+        fetch(0);
+        fetch(1);
+#pragma unroll
+        for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+#pragma unroll
+                for (int i = 0; i < TI; i++) acc[i][j] = mfma32(b[ks][j], a[ks][i], acc[i][j]);
+    };
+
+    gload(0, st[0]);
+    if (nk > 1) gload(1, st[1]);
+    for (int kt = 0; kt < nk; kt++) {
+        // this wave's copies of this step are done (the next step's may still
+        // fly), then a plain barrier: every wave's copies of this step are in
+        // LDS, and every wave has finished reading the stage that the copies
+        // below overwrite (its reads fed the MFMAs of the last step).
+        // (__syncthreads() would also wait for the next step's copies.)
+        if (kt + 1 < nk) __builtin_amdgcn_s_waitcnt(0x0F70 | (CA + CW)); // vmcnt(CA + CW)
+        else __builtin_amdgcn_s_waitcnt(0x0F70);                      // vmcnt(0)
+        asm volatile("s_barrier" ::: "memory");
+        if (kt + 2 < nk) gload(kt + 2, st[(kt + 2) % TSTAGES]);
+        compute(st[kt % TSTAGES]);
+    }
+
+    // epilogue from registers: each lane owns 4 consecutive columns per
+    // (j, r/4) of its TI rows.  A bf16 residual (32 TI bytes per lane) is
+    // loaded in full before the first store: vector memory operations
+    // complete in issue order, so a load issued after a store would also wait
+    // for the store.  An fp32 residual is loaded per column block.  The bias
+    // comes from LDS.
+    u32x2 rh[RES == 1 ? TI : 1][4][4]; // bf16 residual by i, j, q
+    if constexpr (RES == 1) {
+#pragma unroll
+        for (int i = 0; i < TI; i++) {
+            const int m = min(m0 + 32 * TI * wm + 32 * i + lq, g.M - 1);
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    const int n = min(n0 + 128 * wn + 32 * j + 8 * q + 4 * gq, g.N - 4);
+                    rh[i][j][q] = *(const u32x2 *)((const bf16 *)g.R16 + (int64_t)m * g.ldr + n);
+                }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+#pragma unroll
+        for (int i = 0; i < TI; i++) {
+            const int m = m0 + 32 * TI * wm + 32 * i + lq;
+            floatx4 rf[4];
+            if constexpr (RES == 2) {
+                const int mc = min(m, g.M - 1);
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    const int n = min(n0 + 128 * wn + 32 * j + 8 * q + 4 * gq, g.N - 4);
+                    rf[q] = *(const floatx4 *)(g.R32 + (int64_t)mc * g.ldr + n);
+                }
+            }
+            if (m >= g.M) continue;
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int n = n0 + 128 * wn + 32 * j + 8 * q + 4 * gq;
+                if (n >= g.N) continue;
+                const floatx4 b4 = *(const floatx4 *)&bias_s[128 * wn + 32 * j + 8 * q + 4 * gq];
+                floatx4 x;
+#pragma unroll
+                for (int e = 0; e < 4; e++) x[e] = apply_act(acc[i][j][4 * q + e] + b4[e], EPI);
+                if constexpr (RES == 2) x += rf[q];
+                if constexpr (RES == 1) {
+                    const u32x2 rv = rh[i][j][q];
+                    x += floatx4{bf16_lo(rv[0]), bf16_hi(rv[0]), bf16_lo(rv[1]), bf16_hi(rv[1])};
+                }
+                store4(g.C, (int64_t)m * g.ldc + n, x, g.c_f32);
+                if (g.C16) store4(g.C16, (int64_t)m * g.ldc16 + n, x, false);
+                if (g.Ck && n >= g.k_lo && n < g.k_lo + g.kv_w) store4(g.Ck, (int64_t)m * g.ldck + (n - g.k_lo), x, false);
+                if (g.Cv && n >= g.v_lo && n < g.v_lo + g.kv_w) store4(g.Cv, (int64_t)m * g.ldcv + (n - g.v_lo), x, false);
+            }
+        }
+    }
+}
 
 __global__ void __launch_bounds__(GNT) gemm_bf16_kernel(GemmArgs g)
 {
@@ -169,9 +361,49 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(GemmArgs g)
     }
 }
 
+namespace {
+bool al(const void *p, unsigned bytes) { return ((uintptr_t)p & (bytes - 1)) == 0; }
+// shapes and alignments the main bf16 kernel takes: K a multiple of 64, N
+// and every column offset a multiple of 8, and every row start of every
+// operand, output and residual 16-byte aligned
+bool tiled_ok(const GemmArgs &g)
+{
+    if (g.K % TBK != 0 || g.N % 8 != 0 || g.lda % 8 != 0 || !al(g.A, 16) || !al(g.W, 16)) return false;
+    if (g.ldc % (g.c_f32 ? 4 : 8) != 0 || !al(g.C, 16)) return false;
+    if (g.C16 && (g.ldc16 % 8 != 0 || !al(g.C16, 16))) return false;
+    if (g.R32 && (g.ldr % 4 != 0 || !al(g.R32, 16))) return false;
+    if (g.R16 && (g.ldr % 8 != 0 || !al(g.R16, 16))) return false;
+    if ((g.Ck || g.Cv) && (g.kv_w % 8 != 0 || g.k_lo % 8 != 0 || g.v_lo % 8 != 0)) return false;
+    if (g.Ck && (g.ldck % 8 != 0 || !al(g.Ck, 16))) return false;
+    if (g.Cv && (g.ldcv % 8 != 0 || !al(g.Cv, 16))) return false;
+    return true;
+}
+} // namespace
+
 hipError_t launch_gemm_bf16(const GemmArgs &g, hipStream_t st)
 {
     if (g.M <= 0 || g.N <= 0) return hipSuccess;
+    if (tiled_ok(g)) {
+        const int tiles_n = (g.N + 127) / 128;
+        const int64_t n_tiles = (int64_t)tiles_n * ((g.M + TBM - 1) / TBM);
+        const int per_xcd = (int)((n_tiles + 7) / 8);
+        const dim3 grid(8 * per_xcd), block(256);
+        const int res = g.R32 ? 2 : (g.R16 ? 1 : 0);
+#define HSTU_GEMM_LAUNCH(E, R)                                                                                         \
+    hipLaunchKernelGGL((gemm_bf16_tiled_kernel<E, R, 2, 4, 1>), grid, block, 0, st, g, tiles_n, (int)n_tiles, per_xcd)
+#define HSTU_GEMM_RES(E)                                                                                               \
+    do {                                                                                                               \
+        if (res == 2) HSTU_GEMM_LAUNCH(E, 2);                                                                          \
+        else if (res == 1) HSTU_GEMM_LAUNCH(E, 1);                                                                     \
+        else HSTU_GEMM_LAUNCH(E, 0);                                                                                   \
+    } while (0)
+        if (g.epi == EPI_SILU) HSTU_GEMM_RES(EPI_SILU);
+        else if (g.epi == EPI_RELU) HSTU_GEMM_RES(EPI_RELU);
+        else HSTU_GEMM_RES(EPI_NONE);
+#undef HSTU_GEMM_RES
+#undef HSTU_GEMM_LAUNCH
+        return hipGetLastError();
+    }
     dim3 grid((g.N + GBN - 1) / GBN, (g.M + GBM - 1) / GBM);
     hipLaunchKernelGGL(gemm_bf16_kernel, grid, dim3(GNT), 0, st, g);
     return hipGetLastError();

@@ -99,6 +99,25 @@ def test_layer_bf16_ragged(strong):
     assert rel_err(host(vc), Vr) <= bf16_bound(Vr)
 
 
+def test_layer_bf16_narrow_model():
+    """bf16 layer with D=72, H=1, d=128: f1 (K = 72, not a multiple of the
+    main GEMM kernel's K step) takes the general GEMM kernel; f2 (N = 72)
+    takes the main kernel with a partial column tile; 267 tokens leave a
+    partial row tile."""
+    L = np.array([70, 130, 3, 64])
+    w = synth.layer_workload("layer-narrow", 37, L, d_model=72, heads=1, d=128, n_max=256, dtype="bf16")
+    lay = w.layers[0]
+    y, kc, vc = run_layer(w, lay, w.x, kv=True)
+    ref, K, V = oracle.layer_fwd(w.offsets, w.ts, w.x, lay, w.heads, w.d, w.n_max, return_kv=True)
+    e = branch_err(host(y), ref, w.x)
+    print("bf16 narrow layer branch err", e, "bound", branch_bound_bf16(ref, w.x), "y err", rel_err(host(y), ref))
+    assert rel_err(host(y), ref) <= bf16_bound(ref)
+    assert e <= branch_bound_bf16(ref, w.x)
+    Kr, Vr = K.reshape(w.total, -1), V.reshape(w.total, -1)
+    assert rel_err(host(kc), Kr) <= bf16_bound(Kr)
+    assert rel_err(host(vc), Vr) <= bf16_bound(Vr)
+
+
 # ------------------------------------------------------------------ M-FALCON
 
 def gpu_mfalcon(w, b_m=None, x_cand=None, cand_subset=None):
