@@ -38,7 +38,8 @@
 // block.
 //
 // drab_p: the pointwise wave writes its fp32 dS into an LDS tile skewed by
-// j - i ([key - query][query]); one block later, one thread per diagonal sums
+// j - i ([key - query][key mod 32]: a diagonal crosses a 32-query block at
+// 32 consecutive keys, one per residue); one block later, one thread per diagonal sums
 // it into an LDS ring indexed by j - i, and an entry is flushed with one
 // global atomic once no later block can reach it.  drab_t: when every pair of
 // a 32x32 block falls in one time bucket (decided per block in scalar code
@@ -69,9 +70,12 @@ constexpr int SS = 40;     // dS tile [key][query] row stride (bf16)
 constexpr int WIN = 160;   // rab_p window per block (BQ + BN - 1 used)
 constexpr int RING = 256;  // drab_p ring (power of two >= WIN + BQ)
 constexpr int DK = 160;    // diagonals of the skewed dS tile: key - query + BQ - 1 (159 used, row 159 stays 0)
-constexpr int DKP = 36;    // row pitch (floats) of the skewed tile: 32 queries + pad, 16-byte rows
+// Row pitch (floats) of the skewed tile, whose columns are keys mod 32: 16-byte
+// rows, and 40 = 8 (mod 16) makes each column write (64 lanes: 32 keys x 2
+// query halves 4 rows apart) hit 64 different banks.
+constexpr int DKP = 40;
 constexpr int TB = 64;     // time buckets that int64 differences can reach
-constexpr int TCOPY = 4;   // copies of each K wave's drab_t table
+constexpr int TCOPY = 2;   // copies of each K wave's drab_t table
 constexpr float NLOG2E = -1.4426950408889634f;
 constexpr float NLN2 = -0.69314718055994531f;
 
@@ -95,7 +99,7 @@ struct alignas(16) Smem {
     StageP sp[2];
     alignas(16) bf16 ds[2][BN * SS];    // dS [key][query] (the prologue's K tile spans ds and pt)
     alignas(16) bf16 pt[2][BN * SS];    // P' [key][query]
-    alignas(16) float dsk[2][DK * DKP]; // fp32 dS skewed: [key - query + BQ - 1][query]
+    alignas(16) float dsk[2][DK * DKP]; // fp32 dS skewed: [key - query + BQ - 1][key % 32]
     float ring[RING];
     float dtab[4][TCOPY][TB];
     float rabt_rev[32];
@@ -131,7 +135,7 @@ DEV u32x2 lds_read_tr(const bf16 *p)
 struct BwdLane {
     const uint32_t *qt;   // S.qt + 4g   (index with cr)
     const int64_t *qt64;  // S.qt64 + 4g
-    float *dsk;           // skewed-tile cell of (cr = 0) for this lane; cell of cr at -(DKP - 1) cr
+    float *dsk;           // skewed-tile cell of (cr = 0) for this lane; cell of cr at -DKP cr
     float *dtab;          // this K wave's drab_t table copy for this lane
     uint32_t tk;
     int64_t tk64;
@@ -225,7 +229,7 @@ DEV void pointwise(floatx16 &xacc, const floatx16 &pacc, DpStep &&dp_step, uint3
             __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
-            if (s + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            if (s + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -237,7 +241,7 @@ DEV void pointwise(floatx16 &xacc, const floatx16 &pacc, DpStep &&dp_step, uint3
             const int rr = r + u, cr = 8 * (rr >> 2) + (rr & 3);
             const float ds = pacc[rr] * fac[rr];
             dd[u] = ds;
-            ln.dsk[-(DKP - 1) * cr] = ds;
+            ln.dsk[-DKP * cr] = ds;
             if constexpr (DT && TM != 0) {
                 if constexpr (UB == TB_ONE) {
                     tsum += ds;
@@ -675,7 +679,7 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
         const StageP &SPn = sm.sp[n & 1];
         const bool skip = MAIN ? false : (kw0 > q0 + BQ - 1 || kw0 >= L);
         const bool diag = MAIN ? false : kw0 + 31 > q0;
-        ln.dsk = sm.dsk[n & 1] + (krow + (BQ - 1) - 4 * g) * DKP + 4 * g;
+        ln.dsk = sm.dsk[n & 1] + (krow + (BQ - 1) - 4 * g) * DKP + lq;
         bf16 *dsn = sm.ds[n & 1], *ptn = sm.pt[n & 1];
         if (!skip) {
             // X = Q K^T + rab_p window (operand reads two steps ahead of the
@@ -689,11 +693,11 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
                 wacc[r] = HP ? SPn.win[krow + (BQ - 1) - 4 * g - cr] : 0.f;
                 xacc[r] = pacc[r] = 0.f;
             }
-            bf16x8 fd[2], fl[2];
+            bf16x8 fd[3], fl[3]; // dP operands, read two steps ahead
             auto fetch_dp = [&](int s) {
                 const int o = swz(lq, s * 16 + g * 8);
-                fd[s & 1] = *(const bf16x8 *)&SQn.dO[o];
-                fl[s & 1] = *(const bf16x8 *)&SPn.dOl[o];
+                fd[s % 3] = *(const bf16x8 *)&SQn.dO[o];
+                fl[s % 3] = *(const bf16x8 *)&SPn.dOl[o];
             };
             __builtin_amdgcn_sched_barrier(0);
             {
@@ -707,19 +711,20 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
                     xacc = mfma32(fq[s % 3], slice8(acc2[s >> 1], 4 * (s & 1)), xacc);
                 }
                 fetch_dp(0);
+                fetch_dp(1);
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0); // Q reads of steps 0, 1
 #pragma unroll
                 for (int s = 0; s < 8; s++) {
                     if (s + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // read of step s + 2
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // MFMA of step s
                 }
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0); // dP operands of step 0
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0); // dP operands of steps 0, 1
             }
             __builtin_amdgcn_sched_barrier(0);
             xacc += wacc;
             auto dp_step = [&](int s) {
-                const bf16x8 d0 = fd[s & 1], d1 = fl[s & 1];
-                if (s + 1 < 8) fetch_dp(s + 1);
+                const bf16x8 d0 = fd[s % 3], d1 = fl[s % 3];
+                if (s + 2 < 8) fetch_dp(s + 2);
                 pacc = mfma32(d0, slice8(acc2[s >> 1], 8 + 4 * (s & 1)), pacc);
                 pacc = mfma32(d1, slice8(acc2[s >> 1], 8 + 4 * (s & 1)), pacc);
             };
@@ -790,7 +795,7 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
 #pragma unroll
             for (int gr = 0; gr < 4; gr++) *(u32x2 *)&dsn[krow * SS + 8 * gr + 4 * g] = u32x2{0u, 0u};
 #pragma unroll
-            for (int rr = 0; rr < 16; rr++) ln.dsk[-(DKP - 1) * (8 * (rr >> 2) + (rr & 3))] = 0.f;
+            for (int rr = 0; rr < 16; rr++) ln.dsk[-DKP * (8 * (rr >> 2) + (rr & 3))] = 0.f;
         }
         finish(main_c, n, false);
     };
