@@ -154,6 +154,9 @@ hstu_status check_view(const void *p, int64_t ld, int64_t width, const char *nam
 {
     if (!p) return required ? fail(HSTU_ERR_ARG, "%s is NULL", name) : HSTU_OK;
     if (ld < width) return fail(HSTU_ERR_ARG, "%s: ld (%lld) < row width (%lld)", name, (long long)ld, (long long)width);
+    // kernels form in-row offsets from 24-bit products
+    if (ld >= ((int64_t)1 << 24))
+        return fail(HSTU_ERR_UNSUPPORTED, "%s: ld (%lld) must be below 2^24 elements", name, (long long)ld);
     if (((uintptr_t)p & 3) != 0) return fail(HSTU_ERR_ARG, "%s must be 4-byte aligned", name);
     return HSTU_OK;
 }

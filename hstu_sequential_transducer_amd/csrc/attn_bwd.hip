@@ -381,17 +381,22 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
     uint32_t treg = 0, tmn = 0xFFFFFFFFu, tmx = 0u;
     int64_t treg64 = 0;
     // nw waves share the 24 copies; wi = this wave's index among them.
+    // Row bases are wave-uniform 64-bit pointers; the lane part of each
+    // address is a 32-bit offset (24-bit products).
     auto gload_direct = [&](auto nw_c, int wi, int q0, StageQ &SQ, StageP &SP) {
         constexpr int NWC = decltype(nw_c)::value;
+        const int64_t rq = (int64_t)(o_b + q0);
+        const bf16 *bq = Q + rq * a.ldq + h * D, *bo = dO + rq * ld_do + h * D, *bl = dOlo + rq * ld_do + h * D;
 #pragma unroll
         for (int i = 0; i < 24 / NWC; i++) {
             const int G = (24 / NWC) * wi + i, plane = G >> 3, r0 = 4 * (G & 7);
             const int row = r0 + (l >> 4);
             const int c = (l & 15) ^ swf(row);
-            const int64_t grow = (int64_t)(o_b + q0 + row);
-            const bf16 *src = plane == 0 ? Q + grow * a.ldq : (plane == 1 ? dO : dOlo) + grow * ld_do;
+            const uint32_t ld = plane == 0 ? (uint32_t)a.ldq : (uint32_t)ld_do;
+            const uint32_t off = __umul24((uint32_t)row, ld) + 8u * (uint32_t)c;
+            const bf16 *src = (plane == 0 ? bq : (plane == 1 ? bo : bl)) + off;
             bf16 *dst = (plane == 0 ? SQ.q : (plane == 1 ? SQ.dO : SP.dOl)) + r0 * D;
-            __builtin_amdgcn_global_load_lds((const void *)(src + h * D + c * 8), (lds_void *)dst, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)dst, 16, 0, 0);
         }
     };
     // Per-block tables, loaded and stored by the threads tt = 0.. of one role.
@@ -668,8 +673,8 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
         finish(main_c, n, true);
     };
     // Pointwise wave, block n: X, dP, P', dS.
-    int rb = 0;              // running drab_t sums of buckets rb, rb + 1 (wave-uniform)
-    float rs0 = 0.f, rs1 = 0.f;
+    int rb = 0;              // running drab_t sums of buckets rb, rb + 1 (rb wave-uniform;
+    float rs0 = 0.f, rs1 = 0.f; // the sums per lane, reduced over the wave when flushed)
     auto iter_pw = [&](auto main_c, int n) {
         constexpr bool MAIN = decltype(main_c)::value;
         const int q0 = k0 + n * BQ;
@@ -765,30 +770,31 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
                 *(u32x2 *)&ptn[krow * SS + 8 * gr + 4 * g] = u32x2{ppk[2 * gr], ppk[2 * gr + 1]};
                 *(u32x2 *)&dsn[krow * SS + 8 * gr + 4 * g] = u32x2{dpk[2 * gr], dpk[2 * gr + 1]};
             }
-            // the block's drab_t sums (buckets ubk, ubk + 1) join the wave's
-            // running sums rs0, rs1 of buckets rb, rb + 1; a running sum goes
-            // to the wave's LDS table (lane 0, plain read-modify-write) when
-            // the buckets move on
+            // the lane's drab_t sums of this block (buckets ubk, ubk + 1) join
+            // its running sums rs0, rs1 of buckets rb, rb + 1; when the
+            // buckets move on, a running sum is reduced over the wave and
+            // goes to the wave's LDS table (lane 0, plain read-modify-write)
             if (DT && TM == 1 && nbk <= 1 && !diag) {
-                const float s_all = wave_sum_dpp(tsum);
-                const float s_up = nbk == 1 ? wave_sum_dpp(tsum2) : 0.f;
-                const float s_lo = s_all - s_up;
+                const float v_up = nbk == 1 ? tsum2 : 0.f;
+                const float v_lo = tsum - v_up;
                 if (ubk == rb) {
-                    rs0 += s_lo;
-                    rs1 += s_up;
+                    rs0 += v_lo;
+                    rs1 += v_up;
                 } else if (ubk == rb + 1) {
-                    if (l == 0) sm.dtab[p][0][rb] += rs0;
+                    const float f0 = wave_sum_dpp(rs0);
+                    if (l == 0) sm.dtab[p][0][rb] += f0;
                     rb = ubk;
-                    rs0 = rs1 + s_lo;
-                    rs1 = s_up;
+                    rs0 = rs1 + v_lo;
+                    rs1 = v_up;
                 } else {
+                    const float f0 = wave_sum_dpp(rs0), f1 = wave_sum_dpp(rs1);
                     if (l == 0) {
-                        sm.dtab[p][0][rb] += rs0;
-                        sm.dtab[p][0][rb + 1] += rs1;
+                        sm.dtab[p][0][rb] += f0;
+                        sm.dtab[p][0][rb + 1] += f1;
                     }
                     rb = ubk;
-                    rs0 = s_lo;
-                    rs1 = s_up;
+                    rs0 = v_lo;
+                    rs1 = v_up;
                 }
             }
         } else {
@@ -850,9 +856,12 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
         }
     } else {
         run(iter_pw);
-        if (DT && TM == 1 && l == 0) {
-            sm.dtab[p][0][rb] += rs0;
-            sm.dtab[p][0][rb + 1] += rs1;
+        if (DT && TM == 1) {
+            const float f0 = wave_sum_dpp(rs0), f1 = wave_sum_dpp(rs1);
+            if (l == 0) {
+                sm.dtab[p][0][rb] += f0;
+                sm.dtab[p][0][rb + 1] += f1;
+            }
         }
     }
 

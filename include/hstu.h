@@ -31,7 +31,9 @@
  *   - Jagged batches have no padding: sequence b owns tokens
  *     [offsets[b], offsets[b+1]) of every [T][...] array.
  *   - Matrices are row-major with a token stride `ld` in elements, so Q/K/V/U
- *     may be views into one f1 output buffer [T][4*H*d] (ld = 4*H*d).
+ *     may be views into one f1 output buffer [T][4*H*d] (ld = 4*H*d).  A
+ *     stride must be at least the row width and below 2^24 elements
+ *     (HSTU_ERR_UNSUPPORTED otherwise).
  *     Per-head tensors are [T][H][d] inside a row: head h at column h*d.
  *   - Everything is enqueued on `stream` (a hipStream_t, NULL = default
  *     stream); nothing synchronises the host and nothing is copied device to

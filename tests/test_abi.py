@@ -63,6 +63,8 @@ def test_validation_errors_are_reported():
     assert _call_fwd(_jag(), _dims(), q=None) == bd.HSTU_ERR_ARG
     assert _call_fwd(_jag(), _dims(), ldq=100) == bd.HSTU_ERR_ARG
     assert "ld" in hs.last_error()
+    assert _call_fwd(_jag(), _dims(), ldq=1 << 24) == bd.HSTU_ERR_UNSUPPORTED
+    assert "2^24" in hs.last_error()
     assert _call_fwd(_jag(), _dims(), ws=None) == bd.HSTU_ERR_WORKSPACE
     assert _call_fwd(_jag(), _dims(), ws=256 * 3 + 4, ws_bytes=1 << 30) == bd.HSTU_ERR_WORKSPACE
     assert _call_fwd(_jag(), _dims(), ws=256 * 4, ws_bytes=16) == bd.HSTU_ERR_WORKSPACE
