@@ -651,24 +651,27 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
             if constexpr (TM != 2) gload_tables_direct(q0 + BQ, sm.sp[(n + 1) & 1]);
         }
     };
-    // Accumulating wave, block n: the previous block's dV, dK, dQ and drab_p.
+    // Accumulating wave, block n: the previous block's dS store (or dQ),
+    // drab_p, dV and dK, then the next block's copies.
     auto iter_acc = [&](auto main_c, int n) {
         constexpr bool MAIN = decltype(main_c)::value;
         const int q0 = k0 + n * BQ;
         int dlf = 0;
         float tot = 0.f;
         const int q0m = q0 - BQ;
-        if (MAIN || n > 0) {
-            const bool skipm = MAIN ? false : (kw0 > q0m + BQ - 1 || kw0 >= L);
-            if (!skipm) acc_block(sm.sq[n % 3 == 0 ? 2 : n % 3 - 1], (n - 1) & 1);
-        }
+        // the LDS/VALU work first and the MFMAs last, so that the pointwise
+        // wave's X products meet an idle MFMA pipe after the barrier
         if (MAIN || n > 0) {
             if constexpr (DQA) dq_block(sm.ds[(n - 1) & 1], q0m, MAIN ? true : q0 <= L);
             else ds_store(sm.ds[(n - 1) & 1], q0m);
         }
-        start_copy(main_c, n);
         if (MAIN || n > 0)
             if (a.drab_p) drabp_sum(sm.dsk[(n - 1) & 1], q0m, tot, dlf);
+        if (MAIN || n > 0) {
+            const bool skipm = MAIN ? false : (kw0 > q0m + BQ - 1 || kw0 >= L);
+            if (!skipm) acc_block(sm.sq[n % 3 == 0 ? 2 : n % 3 - 1], (n - 1) & 1);
+        }
+        start_copy(main_c, n);
         if ((MAIN || n > 0) && a.drab_p) drabp_flush(dlf, tot);
         finish(main_c, n, true);
     };
