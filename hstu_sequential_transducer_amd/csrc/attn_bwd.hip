@@ -690,16 +690,17 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
         ln.dsk = sm.dsk[n & 1] + (krow + (BQ - 1) - 4 * g) * DKP + lq;
         bf16 *dsn = sm.ds[n & 1], *ptn = sm.pt[n & 1];
         if (!skip) {
-            // X = Q K^T + rab_p window (operand reads two steps ahead of the
-            // MFMAs, pinned with scheduling groups; the window is added after
-            // the products).  dP = dO' V^T (hi + lo planes) is issued inside
-            // the element-wise step, whose X-only part overlaps it.
-            floatx16 xacc, pacc, wacc;
+            // X = rab_p window + Q K^T (the window is the products' initial
+            // accumulator; operand reads two steps ahead of the MFMAs, pinned
+            // with scheduling groups).  dP = dO' V^T (hi + lo planes) is
+            // issued inside the element-wise step, whose X-only part overlaps
+            // it.
+            floatx16 xacc, pacc;
 #pragma unroll
             for (int r = 0; r < 16; r++) {
                 const int cr = 8 * (r >> 2) + (r & 3);
-                wacc[r] = HP ? SPn.win[krow + (BQ - 1) - 4 * g - cr] : 0.f;
-                xacc[r] = pacc[r] = 0.f;
+                xacc[r] = HP ? SPn.win[krow + (BQ - 1) - 4 * g - cr] : 0.f;
+                pacc[r] = 0.f;
             }
             bf16x8 fd[3], fl[3]; // dP operands, read two steps ahead
             auto fetch_dp = [&](int s) {
@@ -729,7 +730,6 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
                 __builtin_amdgcn_sched_group_barrier(0x100, 4, 0); // dP operands of steps 0, 1
             }
             __builtin_amdgcn_sched_barrier(0);
-            xacc += wacc;
             auto dp_step = [&](int s) {
                 const bf16x8 d0 = fd[s % 3], d1 = fl[s % 3];
                 if (s + 2 < 8) fetch_dp(s + 2);
