@@ -219,7 +219,7 @@ hstu_status attn_fwd_launch(const hstu_jagged *j, const hstu_dims *dm, const hst
     {
         ProfScope ps("sched_kernel", st);
         launch_sched(j->offsets, j->ts, B, T, tile, H, status, n_items, items, max_items, rel, wide,
-                     split ? concurrent_slots() : 0, t_split, nullptr, 0, st);
+                     split ? concurrent_slots() : 0, t_split, nullptr, 0, nullptr, 0, nullptr, 0, st);
     }
     TRY(launched(hipGetLastError(), "schedule kernel"));
     if (split) {
@@ -479,15 +479,14 @@ hstu_status hstu_attn_bwd(const hstu_jagged *j, const hstu_dims *dm, const hstu_
     const int64_t t_hs = (bias && bias->rab_t) ? bias->rab_t_hstride : 128;
     {
         ProfScope ps("sched_kernel", st);
+        // (the scheduler also zeroes drab_p and drab_t)
         launch_sched(j->offsets, j->ts, B, T, BWD_BN, H, status, n_items, items, max_items, rel, wide, 0, nullptr,
-                     ds_base, w.ds_cap, st);
+                     ds_base, w.ds_cap, drab_p, (int64_t)H * p_hs, drab_t, (int64_t)H * t_hs, st);
     }
     TRY(launched(hipGetLastError(), "schedule kernel"));
     {
-        ProfScope ps("fill_zero_kernel", st);
+        ProfScope ps("zero_dqa_rows_kernel", st);
         TRY(launched(launch_zero_dqa_rows(j->offsets, B, ds_base, dq_acc, H * d, status, st), "zero fill"));
-        if (drab_p) TRY(launched(launch_fill_zero(drab_p, (size_t)H * p_hs * 4, st), "zero fill"));
-        if (drab_t) TRY(launched(launch_fill_zero(drab_t, (size_t)H * t_hs * 4, st), "zero fill"));
     }
     const float inv_n = 1.0f / (float)N;
     if (u.ptr) {

@@ -21,12 +21,14 @@ constexpr int SCHED_BINS = 4096; // longest sequence: (SCHED_BINS - 1) tiles
 // the backward's dS buffer (H planes of P x P bf16, P = L rounded up to 128):
 // the exclusive prefix sum of the plane sizes, or -1 where that prefix plus
 // the sequence's own planes exceeds ds_cap elements (its dQ then goes
-// through fp32 atomics).
+// through fp32 atomics).  zero0[0, n0) and zero1[0, n1) (optional) are
+// zeroed on the way.
 constexpr int ITEM_T_SHIFT = 10;
 constexpr int DS_PAD = 128;
 void launch_sched(const int32_t *offsets, const int64_t *ts, int B, int T, int tile, int H, int *status, int *n_items,
                   int2 *items, int max_items, uint32_t *rel, int32_t *wide, int split_slots, int *t_split,
-                  int64_t *ds_base, int64_t ds_cap, hipStream_t st);
+                  int64_t *ds_base, int64_t ds_cap, float *zero0, int64_t n0, float *zero1, int64_t n1,
+                  hipStream_t st);
 // Zeroes the fp32 rows [offsets[b] + tile * t_split, offsets[b + 1]) of
 // every sequence (the rows that split items accumulate into).
 hipError_t launch_zero_split_rows(const int32_t *offsets, int B, int tile, const int *t_split, float *o32, int64_t ld,

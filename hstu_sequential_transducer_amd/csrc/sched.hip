@@ -66,10 +66,14 @@ __global__ void __launch_bounds__(1024) sched_kernel(const int32_t *__restrict__
                                                       int2 *__restrict__ items, int max_items,
                                                       int32_t *__restrict__ wide, int split_slots,
                                                       int *__restrict__ t_split_out, int64_t *__restrict__ ds_base,
-                                                      int64_t ds_cap)
+                                                      int64_t ds_cap, float *__restrict__ zero0, int64_t n0,
+                                                      float *__restrict__ zero1, int64_t n1)
 {
     __shared__ int hist[SCHED_BINS];
     __shared__ long long ptmp[16];
+    // buffers the caller wants zeroed (the backward's bias gradients)
+    for (int64_t i = threadIdx.x; i < n0; i += 1024) zero0[i] = 0.f;
+    for (int64_t i = threadIdx.x; i < n1; i += 1024) zero1[i] = 0.f;
     __shared__ int fill[SCHED_BINS];
     __shared__ int S[SCHED_BINS];
     __shared__ int bad;
@@ -277,10 +281,12 @@ hipError_t launch_zero_dqa_rows(const int32_t *offsets, int B, const int64_t *ds
 
 void launch_sched(const int32_t *offsets, const int64_t *ts, int B, int T, int tile, int H, int *status, int *n_items,
                   int2 *items, int max_items, uint32_t *rel, int32_t *wide, int split_slots, int *t_split,
-                  int64_t *ds_base, int64_t ds_cap, hipStream_t st)
+                  int64_t *ds_base, int64_t ds_cap, float *zero0, int64_t n0, float *zero1, int64_t n1,
+                  hipStream_t st)
 {
     hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(1024), 0, st, offsets, B, T, tile, H, status, n_items, items,
-                       max_items, wide, split_slots, t_split, ds_base, ds_cap);
+                       max_items, wide, split_slots, t_split, ds_base, ds_cap, zero0, zero0 ? n0 : 0, zero1,
+                       zero1 ? n1 : 0);
     if (ts && T > 0)
         hipLaunchKernelGGL(reltime_kernel, dim3((T + 255) / 256), dim3(256), 0, st, offsets, ts, rel, wide, B, T, status);
 }
