@@ -196,7 +196,7 @@ DEV float xprime(const floatx16 &xacc, int rr, const BwdLane &ln, const float *r
 template <int TM, bool DT, bool DIAG, int UB, typename DpStep>
 DEV void pointwise(floatx16 &xacc, const floatx16 &pacc, DpStep &&dp_step, uint32_t (&ppk)[8], uint32_t (&dpk)[8],
                    const BwdLane &ln, const float *rabt_rev, const float *rabt, float ubias, float ubias2,
-                   uint32_t thr, float &tsum, float &tsum2)
+                   uint32_t thr, float &tsum, float &tsum2, bf16 *pt_row)
 {
     floatx16 &fac = xacc; // each element's factor replaces its x
 #pragma unroll
@@ -233,6 +233,10 @@ DEV void pointwise(floatx16 &xacc, const floatx16 &pacc, DpStep &&dp_step, uint3
         }
     }
     __builtin_amdgcn_sched_barrier(0);
+    // P' -> LDS as [key][query] (lane row, 4 queries per r/4 group) while the
+    // last dP products finish
+#pragma unroll
+    for (int gr = 0; gr < 4; gr++) *(u32x2 *)&pt_row[8 * gr] = u32x2{ppk[2 * gr], ppk[2 * gr + 1]};
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
         float dd[2];
@@ -760,19 +764,16 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
             float tsum = 0.f, tsum2 = 0.f;
             uint32_t ppk[8], dpk[8];
             if (diag)
-                pointwise<TM, DT, true, TB_ANY>(xacc, pacc, dp_step, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, ubias2, thr, tsum, tsum2);
+                pointwise<TM, DT, true, TB_ANY>(xacc, pacc, dp_step, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, ubias2, thr, tsum, tsum2, ptn + krow * SS + 4 * g);
             else if (TM == 1 && nbk == 0)
-                pointwise<TM, DT, false, TB_ONE>(xacc, pacc, dp_step, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, ubias2, thr, tsum, tsum2);
+                pointwise<TM, DT, false, TB_ONE>(xacc, pacc, dp_step, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, ubias2, thr, tsum, tsum2, ptn + krow * SS + 4 * g);
             else if (TM == 1 && nbk == 1)
-                pointwise<TM, DT, false, TB_TWO>(xacc, pacc, dp_step, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, ubias2, thr, tsum, tsum2);
+                pointwise<TM, DT, false, TB_TWO>(xacc, pacc, dp_step, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, ubias2, thr, tsum, tsum2, ptn + krow * SS + 4 * g);
             else
-                pointwise<TM, DT, false, TB_ANY>(xacc, pacc, dp_step, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, ubias2, thr, tsum, tsum2);
-            // P' and dS -> LDS as [key][query]: lane writes 4 queries (r%4) per r/4 group
+                pointwise<TM, DT, false, TB_ANY>(xacc, pacc, dp_step, ppk, dpk, ln, sm.rabt_rev, sm.rabt, ubias, ubias2, thr, tsum, tsum2, ptn + krow * SS + 4 * g);
+            // dS -> LDS as [key][query]: lane writes 4 queries (r%4) per r/4 group
 #pragma unroll
-            for (int gr = 0; gr < 4; gr++) {
-                *(u32x2 *)&ptn[krow * SS + 8 * gr + 4 * g] = u32x2{ppk[2 * gr], ppk[2 * gr + 1]};
-                *(u32x2 *)&dsn[krow * SS + 8 * gr + 4 * g] = u32x2{dpk[2 * gr], dpk[2 * gr + 1]};
-            }
+            for (int gr = 0; gr < 4; gr++) *(u32x2 *)&dsn[krow * SS + 8 * gr + 4 * g] = u32x2{dpk[2 * gr], dpk[2 * gr + 1]};
             // the lane's drab_t sums of this block (buckets ubk, ubk + 1) join
             // its running sums rs0, rs1 of buckets rb, rb + 1; when the
             // buckets move on, a running sum is reduced over the wave and
