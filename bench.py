@@ -47,7 +47,9 @@ CSRC = os.path.join(ROOT, "hstu_sequential_transducer_amd", "csrc")
 # source they were measured on (sha256 over the files listed); otherwise the
 # traffic is reported as null.
 MEASURED_TRAFFIC = {
-    "attn_bwd_bf16_kernel": {"src": "bb8c5d7c9fac2065", "bytes": 2586578174},   # read 1076443720 + write 1510134453
+    "attn_bwd_bf16_kernel": {"src": "c648b6ba46988a51", "bytes": 2209285734},  # read 1396754512 + write 812531222
+    "attn_fwd_bf16_kernel": {"src": "9877372e46318e42", "bytes": 419866016},  # read 333402448 + write 86463568
+    "dq_gemm_kernel": {"src": "240ca39b4c769bad", "bytes": 929320006},        # read 893906550 + write 35413456
 }
 
 
