@@ -185,6 +185,29 @@ def layer_fwd(offsets, ts, x, layer, heads: int, d: int, n_max: int, phi1: int =
     return (Y, kv[0], kv[1]) if return_kv else Y
 
 
+def layer_bwd(offsets, ts, x, layer, dy, heads: int, d: int, n_max: int, phi1: int = 0, eps: float = 1e-5):
+    """Gradients of one HSTU layer (Eq. 1-3 + residual) for the upstream
+    gradient ``dy`` at Y, the forward recomputed from ``x``.  Returns dict dx,
+    dw1, db1, dw2, db2, drab_p, drab_t (the table gradients None when the
+    table is None)."""
+    lib = _load()
+    off = _i32(offsets)
+    B = len(off) - 1
+    X, dY = _d(x), _d(dy)
+    T, D = X.shape
+    HD = heads * d
+    rp, rt = _d(layer.rab_p), _d(layer.rab_t)
+    res = dict(dx=np.zeros_like(X), dw1=np.zeros((4 * HD, D)), db1=np.zeros(4 * HD), dw2=np.zeros((D, HD)),
+               db2=np.zeros(D), drab_p=np.zeros_like(rp) if rp is not None else None,
+               drab_t=np.zeros_like(rt) if rt is not None else None)
+    lib.oracle_layer_bwd(ctypes.c_int(B), _p(off), _p(_i64(ts)), ctypes.c_int(heads), ctypes.c_int(d),
+                         ctypes.c_int64(n_max), ctypes.c_int(D), _p(_d(layer.w1)), _p(_d(layer.b1)),
+                         _p(_d(layer.w2)), _p(rp), _p(rt), ctypes.c_int(phi1), ctypes.c_double(eps), _p(X), _p(dY),
+                         _p(res["dx"]), _p(res["dw1"]), _p(res["db1"]), _p(res["dw2"]), _p(res["db2"]),
+                         _p(res["drab_p"]), _p(res["drab_t"]))
+    return res
+
+
 def history_cache(offsets, ts, x, layers, heads: int, d: int, n_max: int, phi1: int = 0, eps: float = 1e-5):
     """Run the layer stack over the user histories and keep every layer's K, V
     (the cacheable computations of M-FALCON).  Returns kv [L][2][T][H][d]."""

@@ -387,6 +387,133 @@ void oracle_layer_fwd(int B, const int32_t *off, const int64_t *ts, int H, int d
     free(G);
 }
 
+/* d phi1 / dz: SiLU' as above; ReLU' read as 1 for z > 0, else 0. */
+static double act_grad(int phi1, double z) { return phi1 == 1 ? (z > 0.0 ? 1.0 : 0.0) : silu_grad(z); }
+
+/*
+ * Backward of oracle_layer_fwd by the chain rule, one step at a time, for the
+ * upstream gradient dY at Y.  The forward is recomputed in fp64 first.
+ *   f2 and the residual:  dX = dY (residual) ; dG = dY W2 ; dW2 = dY^T G ;
+ *                         db2 = column sums of dY
+ *   Eq. 3 and Eq. 2:      oracle_attn_bwd with upstream gradient dG gives
+ *                         dU, dV, dQ, dK and the rab table gradients
+ *   phi1 and f1:          dZ = [dU | dV | dQ | dK] (.) phi1'(Z) ;
+ *                         dX += dZ W1 ; dW1 = dZ^T X ; db1 = column sums of dZ
+ * Outputs are overwritten: dX [T][D], dW1 [4Hd][D], db1 [4Hd], dW2 [D][Hd],
+ * db2 [D], drab_p [H][2N+1], drab_t [H][128] (the last two when the tables
+ * are given).
+ */
+void oracle_layer_bwd(int B, const int32_t *off, const int64_t *ts, int H, int d, int64_t N, int D,
+                      const double *W1, const double *b1, const double *W2, const double *rab_p,
+                      const double *rab_t, int phi1, double eps, const double *X, const double *dY, double *dX,
+                      double *dW1, double *db1, double *dW2, double *db2, double *drab_p, double *drab_t)
+{
+    int64_t T = off[B];
+    int HD = H * d, Z4 = 4 * HD;
+    size_t Tn = (size_t)(T > 0 ? T : 1);
+    double *Z = (double *)malloc(sizeof(double) * Tn * Z4);
+    double *Qm = (double *)malloc(sizeof(double) * Tn * HD);
+    double *Km = (double *)malloc(sizeof(double) * Tn * HD);
+    double *Vm = (double *)malloc(sizeof(double) * Tn * HD);
+    double *Um = (double *)malloc(sizeof(double) * Tn * HD);
+    double *O = (double *)malloc(sizeof(double) * Tn * HD);
+    double *G = (double *)malloc(sizeof(double) * Tn * HD);
+    double *dG = (double *)malloc(sizeof(double) * Tn * HD);
+    double *dA = (double *)malloc(sizeof(double) * Tn * Z4);
+    /* forward: Z = X W1^T + b1 (kept before phi1), U | V | Q | K = phi1(Z) */
+#pragma omp parallel for
+    for (int64_t r = 0; r < T; r++) {
+        for (int n = 0; n < Z4; n++) {
+            double z = b1 ? b1[n] : 0.0;
+            for (int c = 0; c < D; c++) z += X[r * D + c] * W1[(int64_t)n * D + c];
+            Z[r * Z4 + n] = z;
+        }
+        for (int c = 0; c < HD; c++) {
+            Um[r * HD + c] = act(phi1, Z[r * Z4 + c]);
+            Vm[r * HD + c] = act(phi1, Z[r * Z4 + HD + c]);
+            Qm[r * HD + c] = act(phi1, Z[r * Z4 + 2 * HD + c]);
+            Km[r * HD + c] = act(phi1, Z[r * Z4 + 3 * HD + c]);
+        }
+    }
+    oracle_attn_fwd(B, off, ts, H, d, d, N, rab_p, rab_t, Qm, Km, Vm, O, 0, NULL);
+    oracle_ln_gate(T, HD, O, Um, eps, G, NULL);
+    /* f2: dG[r][c] = sum_n dY[r][n] W2[n][c] */
+#pragma omp parallel for
+    for (int64_t r = 0; r < T; r++)
+        for (int c = 0; c < HD; c++) {
+            double s = 0.0;
+            for (int n = 0; n < D; n++) s += dY[r * D + n] * W2[(int64_t)n * HD + c];
+            dG[r * HD + c] = s;
+        }
+    /* dW2[n][c] = sum_r dY[r][n] G[r][c] ; db2[n] = sum_r dY[r][n] */
+#pragma omp parallel for
+    for (int n = 0; n < D; n++) {
+        for (int c = 0; c < HD; c++) {
+            double s = 0.0;
+            for (int64_t r = 0; r < T; r++) s += dY[r * D + n] * G[r * HD + c];
+            dW2[(int64_t)n * HD + c] = s;
+        }
+        if (db2) {
+            double s = 0.0;
+            for (int64_t r = 0; r < T; r++) s += dY[r * D + n];
+            db2[n] = s;
+        }
+    }
+    /* attention and its gate: gradients at U, V, Q, K */
+    {
+        double *dq = (double *)malloc(sizeof(double) * Tn * HD);
+        double *dk = (double *)malloc(sizeof(double) * Tn * HD);
+        double *dv = (double *)malloc(sizeof(double) * Tn * HD);
+        double *du = (double *)malloc(sizeof(double) * Tn * HD);
+        oracle_attn_bwd(B, off, ts, H, d, d, N, rab_p, rab_t, Qm, Km, Vm, Um, eps, dG, dq, dk, dv, du, drab_p,
+                        drab_t);
+        for (int64_t r = 0; r < T; r++)
+            for (int c = 0; c < HD; c++) {
+                dA[r * Z4 + c] = du[r * HD + c];
+                dA[r * Z4 + HD + c] = dv[r * HD + c];
+                dA[r * Z4 + 2 * HD + c] = dq[r * HD + c];
+                dA[r * Z4 + 3 * HD + c] = dk[r * HD + c];
+            }
+        free(dq);
+        free(dk);
+        free(dv);
+        free(du);
+    }
+    /* phi1: dZ = dA (.) phi1'(Z), in dA */
+    for (int64_t e = 0; e < (int64_t)T * Z4; e++) dA[e] *= act_grad(phi1, Z[e]);
+    /* f1 and the residual: dX[r][c] = dY[r][c] + sum_n dZ[r][n] W1[n][c] */
+#pragma omp parallel for
+    for (int64_t r = 0; r < T; r++)
+        for (int c = 0; c < D; c++) {
+            double s = dY[r * D + c];
+            for (int n = 0; n < Z4; n++) s += dA[r * Z4 + n] * W1[(int64_t)n * D + c];
+            dX[r * D + c] = s;
+        }
+    /* dW1[n][c] = sum_r dZ[r][n] X[r][c] ; db1[n] = sum_r dZ[r][n] */
+#pragma omp parallel for
+    for (int n = 0; n < Z4; n++) {
+        for (int c = 0; c < D; c++) {
+            double s = 0.0;
+            for (int64_t r = 0; r < T; r++) s += dA[r * Z4 + n] * X[r * D + c];
+            dW1[(int64_t)n * D + c] = s;
+        }
+        if (db1) {
+            double s = 0.0;
+            for (int64_t r = 0; r < T; r++) s += dA[r * Z4 + n];
+            db1[n] = s;
+        }
+    }
+    free(Z);
+    free(Qm);
+    free(Km);
+    free(Vm);
+    free(Um);
+    free(O);
+    free(G);
+    free(dG);
+    free(dA);
+}
+
 /*
  * M-FALCON scoring of one candidate at a time ([GR review] §3, M-FALCON: the
  * m candidates are split into microbatches whose attention operations are

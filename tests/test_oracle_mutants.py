@@ -44,6 +44,12 @@ MUTANTS = [
     ("mfalcon-no-self", "acc[e] = (acc[e] + p * vv[h * d + e]) / (double)N;", "acc[e] = acc[e] / (double)N;"),
     ("mfalcon-self-time", "rp, rt, 0, 0,\n", "rp, rt, 0, 1,\n"),
     ("drab-t-sign", "oracle_time_bucket(ts[r] - ts[rk])] += ds;", "oracle_time_bucket(ts[r] - ts[rk])] -= ds;"),
+    ("layer-bwd-no-residual", "double s = dY[r * D + c];", "double s = 0.0;"),
+    ("layer-bwd-sigmoid-for-silu-grad", "(z > 0.0 ? 1.0 : 0.0) : silu_grad(z); }", "(z > 0.0 ? 1.0 : 0.0) : 1.0 / (1.0 + exp(-z)); }"),
+    ("layer-bwd-dw1-wrong-operand", "s += dA[r * Z4 + n] * X[r * D + c];", "s += dA[r * Z4 + n] * dY[r * D + c];"),
+    ("layer-bwd-dw2-ungated", "s += dY[r * D + n] * G[r * HD + c];", "s += dY[r * D + n] * Um[r * HD + c];"),
+    ("layer-bwd-dg-transposed-w2", "s += dY[r * D + n] * W2[(int64_t)n * HD + c];", "s += dY[r * D + n] * W2[(int64_t)c * D + n];"),
+    ("layer-bwd-dq-dk-swapped", "dA[r * Z4 + 2 * HD + c] = dq[r * HD + c];", "dA[r * Z4 + 2 * HD + c] = dk[r * HD + c];"),
 ]
 
 PINS = [
@@ -60,6 +66,8 @@ PINS = [
     (pins.test_bwd_finite_differences, dict(with_u=True)),
     (pins.test_bwd_identities, {}),
     (pins.test_mfalcon_equals_last_row_of_full_forward, {}),
+    (pins.test_layer_bwd_residual_and_bias_identities, {}),
+    (pins.test_layer_bwd_finite_differences, dict(phi1=0)),
 ]
 
 

@@ -355,6 +355,74 @@ def test_bwd_identities():
         assert abs(x - y) <= 1e-10 * max(1.0, abs(x))
 
 
+def _layer_case(rng, phi1):
+    H, d, D, N = 2, 3, 5, 6
+    lengths = np.array([4, 3])
+    off = synth.offsets_of(lengths)
+    ts = synth.timestamps(rng, lengths)
+    lay = dict(w1=rng.standard_normal((4 * H * d, D)), b1=rng.standard_normal(4 * H * d) * .5,
+               w2=rng.standard_normal((D, H * d)), b2=rng.standard_normal(D),
+               rab_p=rng.standard_normal((H, 2 * N + 1)), rab_t=rng.standard_normal((H, 128)) * .5)
+    x = rng.standard_normal((int(off[-1]), D))
+    dy = rng.standard_normal(x.shape)
+    return H, d, D, N, off, ts, lay, x, dy
+
+
+@pytest.mark.parametrize("phi1", [0, 1])
+def test_layer_bwd_finite_differences(phi1):
+    """Central differences of the fp64 layer forward (step 1e-6) of the loss
+    sum(dY * Y) against every analytic gradient of the layer backward: dx,
+    dw1, db1, dw2, db2, drab_p, drab_t."""
+    rng = np.random.default_rng(40 + phi1)
+    H, d, D, N, off, ts, lay, x, dy = _layer_case(rng, phi1)
+    eps = 1e-3
+    g = oracle.layer_bwd(off, ts, x, synth.Layer(**lay), dy, H, d, N, phi1=phi1, eps=eps)
+
+    def loss(xx, params):
+        return float((oracle.layer_fwd(off, ts, xx, synth.Layer(**params), H, d, N, phi1=phi1, eps=eps) * dy).sum())
+
+    h = 1e-6
+    grads = dict(x="dx", w1="dw1", b1="db1", w2="dw2", b2="db2", rab_p="drab_p", rab_t="drab_t")
+    for name, gname in grads.items():
+        base = x if name == "x" else lay[name]
+        num = np.zeros_like(base)
+        it = np.nditer(base, flags=["multi_index"])
+        for _ in it:
+            ix = it.multi_index
+            vals = []
+            for sgn in (1, -1):
+                pert = base.copy()
+                pert[ix] += sgn * h
+                if name == "x":
+                    vals.append(loss(pert, lay))
+                else:
+                    vals.append(loss(x, dict(lay, **{name: pert})))
+            num[ix] = (vals[0] - vals[1]) / (2 * h)
+        ana = g[gname]
+        err = np.abs(num - ana).max() / max(1e-12, np.abs(ana).max())
+        assert err < 1e-6, (name, err)
+
+
+def test_layer_bwd_residual_and_bias_identities():
+    """With W2 = 0 the layer is Y = X + b2: dX = dY exactly, every other
+    weight gradient but dW2 and db2 vanishes, db2 = column sums of dY.  And
+    db1 is dW1 of a constant-one input column: appending a unit column to X
+    (a zero column to W1, a zero row to W2, a zero entry to b2 and dY) makes
+    that column of dW1 equal db1."""
+    rng = np.random.default_rng(44)
+    H, d, D, N, off, ts, lay, x, dy = _layer_case(rng, 0)
+    g = oracle.layer_bwd(off, ts, x, synth.Layer(**dict(lay, w2=np.zeros_like(lay["w2"]))), dy, H, d, N)
+    assert np.array_equal(g["dx"], dy)
+    assert not g["dw1"].any() and not g["db1"].any() and not g["drab_p"].any() and not g["drab_t"].any()
+    assert np.allclose(g["db2"], dy.sum(axis=0), rtol=1e-13, atol=1e-13)
+    x1 = np.concatenate([x, np.ones((x.shape[0], 1))], axis=1)
+    w1 = np.concatenate([lay["w1"], np.zeros((lay["w1"].shape[0], 1))], axis=1)
+    lay2 = dict(lay, w1=w1, w2=np.concatenate([lay["w2"], np.zeros((1, H * d))], axis=0), b2=np.append(lay["b2"], 0.))
+    dy1 = np.concatenate([dy, np.zeros((x.shape[0], 1))], axis=1)
+    g2 = oracle.layer_bwd(off, ts, x1, synth.Layer(**lay2), dy1, H, d, N)
+    assert np.allclose(g2["dw1"][:, D], g2["db1"], rtol=1e-12, atol=1e-12)
+
+
 # ---------------------------------------------------------------- M-FALCON
 
 def test_mfalcon_equals_last_row_of_full_forward():
