@@ -6,8 +6,8 @@ The method is the HSTU layer of Generative Recommenders (paper review
 "Actions Speak Louder than Words", arXiv 2402.17152, section 3).
 """
 from .binding import (HSTU_ACT_RELU, HSTU_ACT_SILU, HSTU_BF16, HSTU_F32, HstuError, LIB_PATH, abi_version,
-                      attn_bwd, attn_fwd, last_error, layer_fwd, load_library, mfalcon_score,
+                      attn_bwd, attn_fwd, last_error, layer_bwd, layer_fwd, load_library, mfalcon_score,
                       profile_collect, profile_enable)
 
-__all__ = ["attn_fwd", "attn_bwd", "layer_fwd", "mfalcon_score", "abi_version", "last_error", "load_library",
+__all__ = ["attn_fwd", "attn_bwd", "layer_fwd", "layer_bwd", "mfalcon_score", "abi_version", "last_error", "load_library",
            "HstuError", "LIB_PATH", "profile_enable", "profile_collect", "HSTU_BF16", "HSTU_F32", "HSTU_ACT_SILU", "HSTU_ACT_RELU"]

@@ -19,9 +19,10 @@ LIB_PATH = os.path.join(_HERE, "libhstu.so")
 HSTU_OK, HSTU_ERR_ARG, HSTU_ERR_UNSUPPORTED, HSTU_ERR_WORKSPACE, HSTU_ERR_DEVICE = range(5)
 HSTU_F32, HSTU_BF16 = 0, 1
 HSTU_ACT_SILU, HSTU_ACT_RELU = 0, 1
-OP_ATTN_FWD, OP_ATTN_BWD, OP_LAYER_FWD, OP_MFALCON = range(4)
+OP_ATTN_FWD, OP_ATTN_BWD, OP_LAYER_FWD, OP_MFALCON, OP_LAYER_BWD = range(5)
 
-EXPORTED = ["hstu_attn_fwd", "hstu_attn_bwd", "hstu_layer_fwd", "mfalcon_score", "hstu_workspace_size",
+EXPORTED = ["hstu_attn_fwd", "hstu_attn_bwd", "hstu_layer_fwd", "hstu_layer_bwd", "mfalcon_score",
+            "hstu_workspace_size",
             "hstu_profile_enable", "hstu_profile_collect", "hstu_last_error", "hstu_abi_version"]
 
 
@@ -89,6 +90,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hstu_layer_fwd.restype = ctypes.c_int
     lib.hstu_layer_fwd.argtypes = [P(Jagged), P(Dims), ctypes.c_int32, P(Layer), CMat, Mat, Mat, Mat,
                                    ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.hstu_layer_bwd.restype = ctypes.c_int
+    lib.hstu_layer_bwd.argtypes = [P(Jagged), P(Dims), ctypes.c_int32, P(Layer), CMat, CMat, Mat] + \
+        [ctypes.c_void_p] * 6 + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.mfalcon_score.restype = ctypes.c_int
     lib.mfalcon_score.argtypes = [P(Jagged), P(Dims), ctypes.c_int32, ctypes.c_int32, P(Layer), P(CMat), P(CMat),
                                   ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, CMat, ctypes.c_int32,
@@ -273,6 +277,36 @@ def layer_fwd(offsets: torch.Tensor, total: int, ts: Optional[torch.Tensor], x: 
                             ws.data_ptr(), ws.numel(), _stream(x.device))
     _check(st)
     return y
+
+
+def layer_bwd(offsets: torch.Tensor, total: int, ts: Optional[torch.Tensor], x: torch.Tensor, layer: dict,
+              dy: torch.Tensor, heads: int, d: int, n_max: int, eps: float = 1e-5, want_bias_grads: bool = True,
+              want_drab: bool = True, workspace: Optional[torch.Tensor] = None) -> dict:
+    """hstu_layer_bwd (the forward recomputed from x).  Returns dict dx
+    [T][D] (x's dtype), dw1 [4Hd][D], db1, dw2 [D][Hd], db2, drab_p, drab_t
+    (fp32; the optional ones None when not requested)."""
+    lib = load_library()
+    T, D = x.shape
+    HD = heads * d
+    jag = _jagged(offsets, ts, n_max, total)
+    dims = Dims(_dtype_code(x), heads, d, d, eps)
+    f32 = dict(dtype=torch.float32, device=x.device)
+    dx = torch.empty_like(x)
+    dw1 = torch.empty((4 * HD, D), **f32)
+    dw2 = torch.empty((D, HD), **f32)
+    db1 = torch.empty(4 * HD, **f32) if want_bias_grads else None
+    db2 = torch.empty(D, **f32) if want_bias_grads else None
+    rp, rt = layer.get("rab_p"), layer.get("rab_t")
+    drp = torch.empty_like(rp) if (want_drab and rp is not None) else None
+    drt = torch.empty_like(rt) if (want_drab and rt is not None and ts is not None) else None
+    nws = workspace_size(OP_LAYER_BWD, jag, dims, D, 0)
+    ws = workspace if workspace is not None else _workspace(nws, x.device)
+    L = _layer_struct(layer)
+    st = lib.hstu_layer_bwd(ctypes.byref(jag), ctypes.byref(dims), D, ctypes.byref(L), _rowmat(x, D), _rowmat(dy, D),
+                            _rowmat(dx, D, Mat), _ptr(dw1), _ptr(db1), _ptr(dw2), _ptr(db2), _ptr(drp), _ptr(drt),
+                            ws.data_ptr(), ws.numel(), _stream(x.device))
+    _check(st)
+    return dict(dx=dx, dw1=dw1, db1=db1, dw2=dw2, db2=db2, drab_p=drp, drab_t=drt)
 
 
 def mfalcon_score(hist_offsets: torch.Tensor, hist_total: int, hist_ts: Optional[torch.Tensor], layers: Sequence[dict],

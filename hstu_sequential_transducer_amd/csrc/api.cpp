@@ -277,6 +277,104 @@ hstu_status attn_fwd_launch(const hstu_jagged *j, const hstu_dims *dm, const hst
     return HSTU_OK;
 }
 
+// Enqueue the backward (launcher, gate backward or scaling, attention
+// backward, dQ) on validated arguments; `wb` is the workspace carved as `w`.
+hstu_status attn_bwd_launch(const hstu_jagged *j, const hstu_dims *dm, const hstu_bias *bias, hstu_cmat q,
+                            hstu_cmat k, hstu_cmat v, hstu_cmat u, const float *o_save, const float *ln_stats,
+                            hstu_cmat dout, hstu_mat dq, hstu_mat dk, hstu_mat dv, hstu_mat du, float *drab_p,
+                            float *drab_t, char *wb, const AttnWs &w, hipStream_t st)
+{
+    const int H = dm->heads, d = dm->d_qk, F = H * dm->d_v;
+    const bool has_p = bias && bias->rab_p;
+    const bool has_t = bias && bias->rab_t && j->ts;
+    int *status = (int *)(wb + w.header), *n_items = status + 1;
+    int2 *items = (int2 *)(wb + w.items);
+    uint32_t *rel = (uint32_t *)(wb + w.rel);
+    int32_t *wide = (int32_t *)(wb + w.wide);
+    bf16 *dO = (bf16 *)(wb + w.dO);
+    int64_t *ds_base = (int64_t *)(wb + w.ds_base);
+    bf16 *ds = (bf16 *)(wb + w.ds);
+    float *dq_acc = (float *)(wb + w.dq);
+    const int T = j->total, B = j->batch, N = j->n_max;
+    const int max_items = max_items_for(B, T, BWD_BN, H);
+    const int64_t p_hs = has_p ? bias->rab_p_hstride : 2 * (int64_t)N + 1;
+    const int64_t t_hs = (bias && bias->rab_t) ? bias->rab_t_hstride : 128;
+    {
+        ProfScope ps("sched_kernel", st);
+        // (the scheduler also zeroes drab_p and drab_t)
+        launch_sched(j->offsets, j->ts, B, T, BWD_BN, H, status, n_items, items, max_items, rel, wide, 0, nullptr,
+                     ds_base, w.ds_cap, drab_p, (int64_t)H * p_hs, drab_t, (int64_t)H * t_hs, st);
+    }
+    TRY(launched(hipGetLastError(), "schedule kernel"));
+    {
+        ProfScope ps("zero_dqa_rows_kernel", st);
+        TRY(launched(launch_zero_dqa_rows(j->offsets, B, ds_base, dq_acc, H * d, status, st), "zero fill"));
+    }
+    const float inv_n = 1.0f / (float)N;
+    if (u.ptr) {
+        ProfScope ps("ln_gate_bwd_kernel", st);
+        TRY(launched(launch_ln_gate_bwd(dout.ptr, dout.ld, u.ptr, u.ld, o_save, F, ln_stats, true, du.ptr, du.ld, dO,
+                                        inv_n, T, F, nullptr, 0, status, st),
+                     "LayerNorm gate backward kernel"));
+    } else {
+        ProfScope ps("scale_bf16_kernel", st);
+        TRY(launched(launch_scale_bf16((const bf16 *)dout.ptr, dout.ld, dO, F, T, F, inv_n, st), "scale kernel"));
+    }
+    AttnBwdArgs a{};
+    a.q = (const bf16 *)q.ptr;
+    a.k = (const bf16 *)k.ptr;
+    a.v = (const bf16 *)v.ptr;
+    a.ldq = q.ld;
+    a.ldk = k.ld;
+    a.ldv = v.ld;
+    a.dO = dO;
+    a.T = T;
+    a.offsets = j->offsets;
+    a.ts = has_t ? j->ts : nullptr;
+    a.rel = rel;
+    a.wide = wide;
+    a.rmin = rel + T;
+    a.rmax = rel + 2 * (size_t)T;
+    a.rab_p = has_p ? bias->rab_p : nullptr;
+    a.rp_hs = p_hs;
+    a.rab_t = has_t ? bias->rab_t : nullptr;
+    a.rt_hs = t_hs;
+    a.H = H;
+    a.N = N;
+    a.items = items;
+    a.n_items = n_items;
+    a.ds = ds;
+    a.ds_base = ds_base;
+    a.dq_acc = dq_acc;
+    a.dk = (bf16 *)dk.ptr;
+    a.dv = (bf16 *)dv.ptr;
+    a.lddk = dk.ld;
+    a.lddv = dv.ld;
+    a.drab_p = drab_p;
+    a.drab_t = has_t ? drab_t : nullptr;
+    {
+        ProfScope ps("attn_bwd_bf16_kernel", st);
+        TRY(launched(launch_attn_bwd_bf16(a, max_items, st), "attention backward kernel"));
+    }
+    {
+        DqArgs qa{};
+        qa.ds = ds;
+        qa.ds_base = ds_base;
+        qa.dq_acc = dq_acc;
+        qa.ldacc = (int64_t)H * d;
+        qa.k = (const bf16 *)k.ptr;
+        qa.ldk = k.ld;
+        qa.offsets = j->offsets;
+        qa.items = items;
+        qa.n_items = n_items;
+        qa.dq = (bf16 *)dq.ptr;
+        qa.lddq = dq.ld;
+        ProfScope ps("dq_gemm_kernel", st);
+        TRY(launched(launch_dq_gemm(qa, max_items, st), "dQ kernel"));
+    }
+    return HSTU_OK;
+}
+
 // Workspace of hstu_layer_fwd: the attention's, then f1's output Z [T][4Hd]
 // and the gate G [T][Hd] (storage dtype).
 struct LayerWs {
@@ -293,6 +391,46 @@ LayerWs layer_ws(const hstu_jagged *j, const hstu_dims *dm)
     const size_t es = elem_size(dm->dtype), T = (size_t)j->total, HD = (size_t)dm->heads * dm->d_qk;
     w.z = c.take(T * 4 * HD * es);
     w.g = c.take(T * HD * es);
+    w.total = c.cur;
+    return w;
+}
+
+// Workspace of hstu_layer_bwd: the attention's (the forward and the backward
+// share it, one after the other), then f1's pre-activation Z and output
+// phi1(Z) [T][4Hd], O (fp32 [T][Hd]) and the LayerNorm stats, G and dG
+// [T][Hd], the gradient at f1's output [T][4Hd] (dU | dV | dQ | dK, then dZ
+// in place), W1^T [D][4Hd], W2^T [Hd][D], and the fp32 partial sums of the
+// weight gradients and of the column sums.
+struct LayerBwdWs {
+    AttnWs af, ab;
+    WgradPlan p1, p2;
+    size_t zpre, zact, osave, stats, g, dg, da, w1t, w2t, part, total;
+};
+
+LayerBwdWs layer_bwd_ws(const hstu_jagged *j, const hstu_dims *dm, int32_t D)
+{
+    LayerBwdWs w{};
+    w.af = attn_ws(j, dm, fwd_tile(dm), false);
+    w.ab = attn_ws(j, dm, BWD_BN, true);
+    Carver c;
+    c.cur = align256(w.af.total > w.ab.total ? w.af.total : w.ab.total);
+    const size_t T = (size_t)j->total, HD = (size_t)dm->heads * dm->d_qk, Z4 = 4 * HD, Dz = (size_t)D;
+    w.zpre = c.take(T * Z4 * 2);
+    w.zact = c.take(T * Z4 * 2);
+    w.osave = c.take(T * HD * 4);
+    w.stats = c.take(T * 2 * 4);
+    w.g = c.take(T * HD * 2);
+    w.dg = c.take(T * HD * 2);
+    w.da = c.take(T * Z4 * 2);
+    w.w1t = c.take(Dz * Z4 * 2);
+    w.w2t = c.take(HD * Dz * 2);
+    w.p1 = wgrad_plan((int)Z4, D, j->total);
+    w.p2 = wgrad_plan(D, (int)HD, j->total);
+    size_t pe = (size_t)w.p1.splits * Z4 * Dz;
+    if ((size_t)w.p2.splits * Dz * HD > pe) pe = (size_t)w.p2.splits * Dz * HD;
+    const size_t pc = (size_t)colsum_blocks(j->total) * (Z4 > Dz ? Z4 : Dz);
+    if (pc > pe) pe = pc;
+    w.part = c.take(pe * 4);
     w.total = c.cur;
     return w;
 }
@@ -399,6 +537,12 @@ size_t hstu_workspace_size(hstu_op op, const hstu_jagged *j, const hstu_dims *di
     case HSTU_OP_ATTN_FWD: return attn_ws(j, dims, fwd_tile(dims), false).total;
     case HSTU_OP_ATTN_BWD: return attn_ws(j, dims, BWD_BN, true).total;
     case HSTU_OP_LAYER_FWD: return layer_ws(j, dims).total;
+    case HSTU_OP_LAYER_BWD:
+        if (d_model < 1) {
+            fail(HSTU_ERR_ARG, "d_model must be >= 1");
+            return 0;
+        }
+        return layer_bwd_ws(j, dims, d_model).total;
     case HSTU_OP_MFALCON:
         if (d_model < 1 || total_cand < 0) {
             fail(HSTU_ERR_ARG, "d_model must be >= 1 and total_cand >= 0");
@@ -465,91 +609,7 @@ hstu_status hstu_attn_bwd(const hstu_jagged *j, const hstu_dims *dm, const hstu_
     TRY(check_ws(ws, ws_bytes, w.total));
     hipStream_t st = (hipStream_t)stream;
     char *wb = (char *)ws;
-    int *status = (int *)(wb + w.header), *n_items = status + 1;
-    int2 *items = (int2 *)(wb + w.items);
-    uint32_t *rel = (uint32_t *)(wb + w.rel);
-    int32_t *wide = (int32_t *)(wb + w.wide);
-    bf16 *dO = (bf16 *)(wb + w.dO);
-    int64_t *ds_base = (int64_t *)(wb + w.ds_base);
-    bf16 *ds = (bf16 *)(wb + w.ds);
-    float *dq_acc = (float *)(wb + w.dq);
-    const int T = j->total, B = j->batch, N = j->n_max;
-    const int max_items = max_items_for(B, T, BWD_BN, H);
-    const int64_t p_hs = has_p ? bias->rab_p_hstride : 2 * (int64_t)N + 1;
-    const int64_t t_hs = (bias && bias->rab_t) ? bias->rab_t_hstride : 128;
-    {
-        ProfScope ps("sched_kernel", st);
-        // (the scheduler also zeroes drab_p and drab_t)
-        launch_sched(j->offsets, j->ts, B, T, BWD_BN, H, status, n_items, items, max_items, rel, wide, 0, nullptr,
-                     ds_base, w.ds_cap, drab_p, (int64_t)H * p_hs, drab_t, (int64_t)H * t_hs, st);
-    }
-    TRY(launched(hipGetLastError(), "schedule kernel"));
-    {
-        ProfScope ps("zero_dqa_rows_kernel", st);
-        TRY(launched(launch_zero_dqa_rows(j->offsets, B, ds_base, dq_acc, H * d, status, st), "zero fill"));
-    }
-    const float inv_n = 1.0f / (float)N;
-    if (u.ptr) {
-        ProfScope ps("ln_gate_bwd_kernel", st);
-        TRY(launched(launch_ln_gate_bwd(dout.ptr, dout.ld, u.ptr, u.ld, o_save, F, ln_stats, true, du.ptr, du.ld, dO,
-                                        inv_n, T, F, nullptr, 0, status, st),
-                     "LayerNorm gate backward kernel"));
-    } else {
-        ProfScope ps("scale_bf16_kernel", st);
-        TRY(launched(launch_scale_bf16((const bf16 *)dout.ptr, dout.ld, dO, F, T, F, inv_n, st), "scale kernel"));
-    }
-    AttnBwdArgs a{};
-    a.q = (const bf16 *)q.ptr;
-    a.k = (const bf16 *)k.ptr;
-    a.v = (const bf16 *)v.ptr;
-    a.ldq = q.ld;
-    a.ldk = k.ld;
-    a.ldv = v.ld;
-    a.dO = dO;
-    a.T = T;
-    a.offsets = j->offsets;
-    a.ts = has_t ? j->ts : nullptr;
-    a.rel = rel;
-    a.wide = wide;
-    a.rmin = rel + T;
-    a.rmax = rel + 2 * (size_t)T;
-    a.rab_p = has_p ? bias->rab_p : nullptr;
-    a.rp_hs = p_hs;
-    a.rab_t = has_t ? bias->rab_t : nullptr;
-    a.rt_hs = t_hs;
-    a.H = H;
-    a.N = N;
-    a.items = items;
-    a.n_items = n_items;
-    a.ds = ds;
-    a.ds_base = ds_base;
-    a.dq_acc = dq_acc;
-    a.dk = (bf16 *)dk.ptr;
-    a.dv = (bf16 *)dv.ptr;
-    a.lddk = dk.ld;
-    a.lddv = dv.ld;
-    a.drab_p = drab_p;
-    a.drab_t = has_t ? drab_t : nullptr;
-    {
-        ProfScope ps("attn_bwd_bf16_kernel", st);
-        TRY(launched(launch_attn_bwd_bf16(a, max_items, st), "attention backward kernel"));
-    }
-    {
-        DqArgs qa{};
-        qa.ds = ds;
-        qa.ds_base = ds_base;
-        qa.dq_acc = dq_acc;
-        qa.ldacc = (int64_t)H * d;
-        qa.k = (const bf16 *)k.ptr;
-        qa.ldk = k.ld;
-        qa.offsets = j->offsets;
-        qa.items = items;
-        qa.n_items = n_items;
-        qa.dq = (bf16 *)dq.ptr;
-        qa.lddq = dq.ld;
-        ProfScope ps("dq_gemm_kernel", st);
-        TRY(launched(launch_dq_gemm(qa, max_items, st), "dQ kernel"));
-    }
+    TRY(attn_bwd_launch(j, dm, bias, q, k, v, u, o_save, ln_stats, dout, dq, dk, dv, du, drab_p, drab_t, wb, w, st));
     TRY(debug_check(ws, st));
     return ok();
 }
@@ -598,6 +658,109 @@ hstu_status hstu_layer_fwd(const hstu_jagged *j, const hstu_dims *dm, int32_t d_
     g2.R16 = x.ptr;
     g2.ldr = x.ld;
     TRY(run_gemm(g2, dt, "gemm_f2", st));
+    TRY(debug_check(ws, st));
+    return ok();
+}
+
+hstu_status hstu_layer_bwd(const hstu_jagged *j, const hstu_dims *dm, int32_t d_model, const hstu_layer *layer,
+                           hstu_cmat x, hstu_cmat dy, hstu_mat dx, float *dw1, float *db1, float *dw2, float *db2,
+                           float *drab_p, float *drab_t, void *ws, size_t ws_bytes, void *stream)
+{
+    TRY(check_jagged(j));
+    TRY(check_dims(dm));
+    if (dm->dtype != HSTU_BF16) return fail(HSTU_ERR_UNSUPPORTED, "hstu_layer_bwd supports bf16 storage only");
+    if (d_model < 8 || d_model % 8 != 0)
+        return fail(HSTU_ERR_UNSUPPORTED, "hstu_layer_bwd needs d_model a multiple of 8 (got %d)", d_model);
+    TRY(check_layer(layer, j, dm, d_model, 0));
+    const int H = dm->heads, d = dm->d_qk, HD = H * d, Z4 = 4 * HD, D = d_model;
+    TRY(check_view(x.ptr, x.ld, D, "x"));
+    TRY(check_view(dy.ptr, dy.ld, D, "dy"));
+    TRY(check_view(dx.ptr, dx.ld, D, "dx"));
+    TRY(check_gemm_operand(x.ptr, x.ld, dm->dtype, "x"));
+    TRY(check_gemm_operand(dy.ptr, dy.ld, dm->dtype, "dy"));
+    if (dx.ptr == x.ptr || dx.ptr == dy.ptr) return fail(HSTU_ERR_ARG, "dx may not alias x or dy");
+    if (!dw1 || !dw2) return fail(HSTU_ERR_ARG, "dw1 and dw2 are required");
+    const float *f32out[4] = {dw1, dw2, db1, db2};
+    for (const float *p : f32out)
+        if (p && ((uintptr_t)p & 15) != 0) return fail(HSTU_ERR_ARG, "dw1, dw2, db1, db2 must be 16-byte aligned");
+    const hstu_bias *bias = &layer->rab;
+    if (drab_p && bias->rab_p && bias->rab_p_hstride == 0)
+        return fail(HSTU_ERR_ARG, "drab_p needs a per-head rab_p (hstride != 0)");
+    if (drab_t && bias->rab_t && j->ts && bias->rab_t_hstride == 0)
+        return fail(HSTU_ERR_ARG, "drab_t needs a per-head rab_t (hstride != 0)");
+    const LayerBwdWs w = layer_bwd_ws(j, dm, D);
+    TRY(check_ws(ws, ws_bytes, w.total));
+    hipStream_t st = (hipStream_t)stream;
+    char *wb = (char *)ws;
+    const int T = j->total;
+    bf16 *Zpre = (bf16 *)(wb + w.zpre), *Zact = (bf16 *)(wb + w.zact), *G = (bf16 *)(wb + w.g);
+    bf16 *dG = (bf16 *)(wb + w.dg), *dA = (bf16 *)(wb + w.da), *W1t = (bf16 *)(wb + w.w1t);
+    bf16 *W2t = (bf16 *)(wb + w.w2t);
+    float *osave = (float *)(wb + w.osave), *stats = (float *)(wb + w.stats), *part = (float *)(wb + w.part);
+    const int act = layer->phi1 == HSTU_ACT_RELU ? 2 : 1;
+
+    // forward again: Z and phi1(Z) = U | V | Q | K, then G = Norm(O) (.) U
+    // with O and the LayerNorm statistics kept
+    GemmArgs g1 = gemm_args(x.ptr, x.ld, layer->w1, layer->b1, Zact, Z4, false, T, Z4, D,
+                            act == 2 ? EPI_RELU : EPI_SILU);
+    g1.Cpre = Zpre;
+    g1.ldcpre = Z4;
+    TRY(run_gemm(g1, dm->dtype, "gemm_f1", st));
+    hstu_cmat zu{Zact, Z4}, zv{Zact + HD, Z4}, zq{Zact + 2 * HD, Z4}, zk{Zact + 3 * HD, Z4};
+    TRY(attn_fwd_launch(j, dm, bias, zq, zk, zv, zu, hstu_mat{G, HD}, osave, stats, wb, w.af, st));
+    {
+        ProfScope ps("transpose_bf16_kernel", st);
+        TRY(launched(launch_transpose_bf16((const bf16 *)layer->w2, HD, D, HD, W2t, D, st), "transpose kernel"));
+        TRY(launched(launch_transpose_bf16((const bf16 *)layer->w1, D, Z4, D, W1t, Z4, st), "transpose kernel"));
+    }
+    // f2: dG = dY W2, dW2 = dY^T G, db2 = column sums of dY
+    TRY(run_gemm(gemm_args(dy.ptr, dy.ld, W2t, nullptr, dG, HD, false, T, HD, D, EPI_NONE), dm->dtype, "gemm_dg", st));
+    {
+        WgradArgs a{dy.ptr, dy.ld, G, HD, part, D, HD, T, w.p2.chunk, w.p2.splits};
+        {
+            ProfScope ps("gemm_wgrad_kernel", st);
+            TRY(launched(launch_gemm_wgrad(a, st), "weight-gradient kernel"));
+        }
+        ProfScope ps("sum_splits_kernel", st);
+        TRY(launched(launch_sum_splits(part, w.p2.splits, (int64_t)D * HD, dw2, st), "split-sum kernel"));
+    }
+    if (db2) {
+        {
+            ProfScope ps("colsum_act_kernel", st);
+            TRY(launched(launch_colsum_act((bf16 *)dy.ptr, dy.ld, nullptr, 0, 0, T, D, part, st), "column-sum kernel"));
+        }
+        ProfScope ps("sum_splits_kernel", st);
+        TRY(launched(launch_sum_splits(part, colsum_blocks(T), D, db2, st), "split-sum kernel"));
+    }
+    // gate and attention: dU | dV | dQ | dK into dA, and the table gradients
+    TRY(attn_bwd_launch(j, dm, bias, zq, zk, zv, zu, osave, stats, hstu_cmat{dG, HD}, hstu_mat{dA + 2 * HD, Z4},
+                        hstu_mat{dA + 3 * HD, Z4}, hstu_mat{dA + HD, Z4}, hstu_mat{dA, Z4}, drab_p, drab_t, wb, w.ab,
+                        st));
+    // phi1: dZ = dA (.) phi1'(Z) in place, db1 = its column sums
+    {
+        ProfScope ps("colsum_act_kernel", st);
+        TRY(launched(launch_colsum_act(dA, Z4, Zpre, Z4, act, T, Z4, part, st), "phi1 backward kernel"));
+    }
+    if (db1) {
+        ProfScope ps("sum_splits_kernel", st);
+        TRY(launched(launch_sum_splits(part, colsum_blocks(T), Z4, db1, st), "split-sum kernel"));
+    }
+    // f1 and the residual: dX = dY + dZ W1, dW1 = dZ^T X
+    {
+        GemmArgs gx = gemm_args(dA, Z4, W1t, nullptr, dx.ptr, dx.ld, false, T, D, Z4, EPI_NONE);
+        gx.R16 = dy.ptr;
+        gx.ldr = dy.ld;
+        TRY(run_gemm(gx, dm->dtype, "gemm_dx", st));
+    }
+    {
+        WgradArgs a{dA, Z4, x.ptr, x.ld, part, Z4, D, T, w.p1.chunk, w.p1.splits};
+        {
+            ProfScope ps("gemm_wgrad_kernel", st);
+            TRY(launched(launch_gemm_wgrad(a, st), "weight-gradient kernel"));
+        }
+        ProfScope ps("sum_splits_kernel", st);
+        TRY(launched(launch_sum_splits(part, w.p1.splits, (int64_t)Z4 * D, dw1, st), "split-sum kernel"));
+    }
     TRY(debug_check(ws, st));
     return ok();
 }

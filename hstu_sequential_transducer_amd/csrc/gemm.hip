@@ -6,8 +6,9 @@
 //   C[m][n] = act(sum_k A[m][k] W[n][k] + bias[n]) + R[m][n]
 //
 // W is stored [out][in] (y = x W^T + b).  Optional extra outputs: a
-// storage-dtype copy of C (the M-FALCON hidden state feeding the next layer)
-// and copies of two column ranges (this layer's K and V, the M-FALCON cache).
+// storage-dtype copy of C (the M-FALCON hidden state feeding the next layer),
+// copies of two column ranges (this layer's K and V, the M-FALCON cache) and
+// a storage-dtype copy of the pre-activation (for phi1' in the backward).
 //
 // bf16, main kernel: 256x128 output tile per workgroup of 4 waves, each wave
 // 64 rows x 128 columns (2x4 blocks of 32x32x16 bf16 MFMA computing C^T, so
@@ -211,9 +212,13 @@ gemm_bf16_tiled_kernel(GemmArgs g, int tiles_n, int n_tiles, int per_xcd)
                 const int n = n0 + 128 * wn + 32 * j + 8 * q + 4 * gq;
                 if (n >= g.N) continue;
                 const floatx4 b4 = *(const floatx4 *)&bias_s[128 * wn + 32 * j + 8 * q + 4 * gq];
-                floatx4 x;
+                floatx4 x, pre;
 #pragma unroll
-                for (int e = 0; e < 4; e++) x[e] = apply_act(acc[i][j][4 * q + e] + b4[e], EPI);
+                for (int e = 0; e < 4; e++) {
+                    pre[e] = acc[i][j][4 * q + e] + b4[e];
+                    x[e] = apply_act(pre[e], EPI);
+                }
+                if (g.Cpre) store4(g.Cpre, (int64_t)m * g.ldcpre + n, pre, false);
                 if constexpr (RES == 2) x += rf[q];
                 if constexpr (RES == 1) {
                     const u32x2 rv = rh[i][j][q];
@@ -305,7 +310,9 @@ __global__ void __launch_bounds__(GNT) gemm_bf16_kernel(GemmArgs g)
             for (int r = 0; r < 16; r++) {
                 const int m = m0 + 64 * wm + 32 * i + 8 * (r >> 2) + 4 * gq + (r & 3);
                 if (m >= g.M) continue;
-                float x = apply_act(acc[i][j][r] + bn, g.epi);
+                const float pre = acc[i][j][r] + bn;
+                float x = apply_act(pre, g.epi);
+                if (g.Cpre) store_out<bf16>(g.Cpre, (int64_t)m * g.ldcpre + n, pre);
                 if (g.R32) x += g.R32[(int64_t)m * g.ldr + n];
                 else if (g.R16) x += from_bf16(((const bf16 *)g.R16)[(int64_t)m * g.ldr + n]);
                 if (g.c_f32) store_out<float>(g.C, (int64_t)m * g.ldc + n, x);
@@ -349,6 +356,7 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(GemmArgs g)
             const int n = n0 + tn + j;
             if (n >= g.N) continue;
             float x = acc[i][j] + (g.bias ? g.bias[n] : 0.f);
+            if (g.Cpre) ((float *)g.Cpre)[(int64_t)m * g.ldcpre + n] = x;
             if (g.epi == EPI_SILU) x = x / (1.0f + expf(-x));
             else if (g.epi == EPI_RELU) x = x > 0.f ? x : 0.f;
             if (g.R32) x += g.R32[(int64_t)m * g.ldr + n];
@@ -371,6 +379,7 @@ bool tiled_ok(const GemmArgs &g)
     if (g.K % TBK != 0 || g.N % 8 != 0 || g.lda % 8 != 0 || !al(g.A, 16) || !al(g.W, 16)) return false;
     if (g.ldc % (g.c_f32 ? 4 : 8) != 0 || !al(g.C, 16)) return false;
     if (g.C16 && (g.ldc16 % 8 != 0 || !al(g.C16, 16))) return false;
+    if (g.Cpre && (g.ldcpre % 8 != 0 || !al(g.Cpre, 16))) return false;
     if (g.R32 && (g.ldr % 4 != 0 || !al(g.R32, 16))) return false;
     if (g.R16 && (g.ldr % 8 != 0 || !al(g.R16, 16))) return false;
     if ((g.Ck || g.Cv) && (g.kv_w % 8 != 0 || g.k_lo % 8 != 0 || g.v_lo % 8 != 0)) return false;

@@ -145,6 +145,8 @@ struct GemmArgs {
     bool c_f32;                 // C is fp32 (else storage dtype)
     void *C16;                  // optional storage-dtype copy of C
     int64_t ldc16;
+    void *Cpre;                 // optional storage-dtype copy of acc + bias (before act)
+    int64_t ldcpre;
     int M, N, K;
     int epi;
     // optional copies of columns [k_lo, k_lo + kv_w) and [v_lo, v_lo + kv_w)
@@ -158,6 +160,36 @@ struct GemmArgs {
 };
 hipError_t launch_gemm_bf16(const GemmArgs &g, hipStream_t st);
 hipError_t launch_gemm_f32(const GemmArgs &g, hipStream_t st);
+
+// ---- layer backward outside the attention (layer_bwd.hip)
+// Weight gradient dW[m][n] = sum_t A[t][m] B[t][n] (A [K][M], B [K][N], bf16,
+// token-major), as fp32 partial sums part[splits][M][N] over token ranges
+// [s chunk, (s + 1) chunk).  M, N multiples of 8; lda, ldb multiples of 8;
+// A, B 16-byte aligned.
+struct WgradArgs {
+    const void *A;
+    int64_t lda;
+    const void *B;
+    int64_t ldb;
+    float *part;
+    int M, N, K;
+    int chunk, splits;
+};
+struct WgradPlan {
+    int chunk, splits;
+};
+WgradPlan wgrad_plan(int M, int N, int K);
+hipError_t launch_gemm_wgrad(const WgradArgs &g, hipStream_t st);
+// out[e] = sum over s < S of part[s][e], e < E (E a multiple of 4)
+hipError_t launch_sum_splits(const float *part, int S, int64_t E, float *out, hipStream_t st);
+// act 1 (SiLU') / 2 (ReLU'): a[r][c] *= phi1'(z[r][c]) in place; act 0: no
+// change.  Column sums of the (new) a per block of COLSUM_ROWS rows go to
+// part[colsum_blocks(M)][N].  N a multiple of 8, rows 16-byte aligned.
+constexpr int COLSUM_ROWS = 64;
+int colsum_blocks(int M);
+hipError_t launch_colsum_act(bf16 *a, int64_t lda, const bf16 *z, int64_t ldz, int act, int M, int N, float *part,
+                             hipStream_t st);
+hipError_t launch_transpose_bf16(const bf16 *in, int64_t ldi, int R, int C, bf16 *out, int64_t ldo, hipStream_t st);
 
 // ---- M-FALCON (mfalcon.hip)
 constexpr int MF_TC = 128; // candidates per attention tile

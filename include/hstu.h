@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define HSTU_ABI_VERSION 1
+#define HSTU_ABI_VERSION 2
 
 typedef enum {
     HSTU_OK = 0,
@@ -75,7 +75,8 @@ typedef enum {
     HSTU_OP_ATTN_FWD = 0,
     HSTU_OP_ATTN_BWD = 1,
     HSTU_OP_LAYER_FWD = 2,
-    HSTU_OP_MFALCON = 3
+    HSTU_OP_MFALCON = 3,
+    HSTU_OP_LAYER_BWD = 4
 } hstu_op;
 
 /* A jagged batch.  batch, total and n_max are host values; offsets and ts
@@ -123,7 +124,8 @@ typedef struct {
 } hstu_layer;
 
 /* Bytes of workspace an entry point needs for these sizes.  d_model and
- * total_cand are used by HSTU_OP_LAYER_FWD / HSTU_OP_MFALCON only (pass 0
+ * total_cand are used by HSTU_OP_LAYER_FWD / HSTU_OP_LAYER_BWD / HSTU_OP_MFALCON
+ * (d_model) and HSTU_OP_MFALCON (total_cand) only (pass 0
  * otherwise); for HSTU_OP_MFALCON `j` describes the histories (batch = users).
  * Returns 0 and sets hstu_last_error() on invalid sizes. */
 size_t hstu_workspace_size(hstu_op op, const hstu_jagged *j, const hstu_dims *dims, int32_t d_model,
@@ -167,6 +169,27 @@ hstu_status hstu_attn_bwd(const hstu_jagged *j, const hstu_dims *dims, const hst
 hstu_status hstu_layer_fwd(const hstu_jagged *j, const hstu_dims *dims, int32_t d_model, const hstu_layer *layer,
                            hstu_cmat x, hstu_mat y, hstu_mat k_cache, hstu_mat v_cache, void *ws, size_t ws_bytes,
                            void *stream);
+
+/*
+ * Backward of hstu_layer_fwd: the chain rule through f2 and the residual,
+ * Eq. 3's Norm (.) U, Eq. 2, phi1 and f1 ([GR review] §3 Eq. 1-3).  The
+ * forward is recomputed from x inside the call (nothing is kept between
+ * calls).  bf16 storage only; d_model a multiple of 8.
+ *   dy [T][D] (storage dtype): upstream gradient at y.
+ *   dx [T][D] (storage dtype): gradient at x (the residual's dy plus the
+ *   f1 branch); may not alias x or dy.
+ *   dw1 [4*H*d][D], dw2 [D][H*d] (fp32, required), db1 [4*H*d] and
+ *   db2 [D] (fp32, NULL to skip), drab_p [H][2*N_max+1] and drab_t [H][128]
+ *   (fp32, NULL to skip; as in hstu_attn_bwd, which needs a per-head table
+ *   for each requested gradient).  Every fp32 output is overwritten (not
+ *   accumulated) and 16-byte aligned.
+ *   Weight gradients are sums over all T tokens in fp32 (split over token
+ *   ranges, the partial sums added in a fixed order: the result does not
+ *   depend on the launch or the run).
+ */
+hstu_status hstu_layer_bwd(const hstu_jagged *j, const hstu_dims *dims, int32_t d_model, const hstu_layer *layer,
+                           hstu_cmat x, hstu_cmat dy, hstu_mat dx, float *dw1, float *db1, float *dw2, float *db2,
+                           float *drab_p, float *drab_t, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * M-FALCON candidate scoring ([GR review] §3, M-FALCON).  User u has a history

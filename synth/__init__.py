@@ -94,6 +94,7 @@ class Workload:
     v: Optional[np.ndarray] = None
     u: Optional[np.ndarray] = None   # [T][H*d]
     dg: Optional[np.ndarray] = None  # [T][H*d] upstream gradient at G
+    dy: Optional[np.ndarray] = None  # [T][D] upstream gradient at the layer output Y
     epilogue: bool = True
     ln_eps: float = 1e-5
     # M-FALCON
@@ -169,9 +170,10 @@ def layer_workload(name: str, seed: int, lengths: Optional[np.ndarray], *, d_mod
     T = int(lengths.sum())
     x = _normal(rng, (T, d_model), 1.0, dtype)
     dg = _normal(rng, (T, heads * d), 1.0, dtype) if with_grad else None
+    dy = _normal(rng, (T, d_model), 1.0, dtype) if with_grad else None
     return Workload(name=name, dtype=dtype, heads=heads, d=d, n_max=n_max, lengths=lengths,
                     offsets=offsets_of(lengths), ts=ts, rab_p=layers[0].rab_p, rab_t=layers[0].rab_t,
-                    d_model=d_model, layers=layers, x=x, dg=dg)
+                    d_model=d_model, layers=layers, x=x, dg=dg, dy=dy)
 
 
 def mfalcon_workload(name: str, seed: int, hist_lengths: Optional[np.ndarray], *, cands_per_user: int,
@@ -230,7 +232,7 @@ def attn_8k(seed: int = 2, with_grad: bool = True) -> Workload:
 
 def layer_train_4k(seed: int = 3) -> Workload:
     """bf16 layer train step: B=16, SL(alpha 1.6, n=4096), N_max=4096, D=512,
-    H=4, d=128, upstream dG ~ N(0,1) at G."""
+    H=4, d=128, upstream gradients ~ N(0,1) at G (dg) and at Y (dy)."""
     return layer_workload("layer-train-B16-N4096", seed, None, d_model=512, heads=4, d=128, n_max=4096,
                           dtype="bf16", with_grad=True, sl=(4096, 1.6), batch=16)
 
