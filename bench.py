@@ -16,7 +16,8 @@ hooks), which give the per-kernel durations (roofline, kernels) and
 "profiled_ms_per_step" (the events add small gaps between launches).
 
 Besides the headline step, the same run times (unless --no-extras) one
-HSTU layer forward (f1 + SiLU, attention, LayerNorm gate, f2 + residual) on
+HSTU layer forward (f1 + SiLU, attention, LayerNorm gate, f2 + residual) and
+one layer backward (with its forward recomputed) on
 B = 16 Stochastic-Length sequences at N_max = 4096, D = 512, and M-FALCON
 scoring of m = 1024 candidates against a 4096-action history (2 layers,
 b_m = 256).  These are reported under "extras"; they are not part of "value".
@@ -197,6 +198,43 @@ def bench_layer(args):
             "kernels": {n: {"launches": v["launches"] // steps, "avg_ms": round(v["avg_ms"], 5)} for n, v in kern.items()}}
 
 
+def bench_layer_bwd(args):
+    """One HSTU layer backward (forward recomputed from x inside the call) on
+    the same workload as bench_layer, upstream gradient dy ~ N(0, 1)."""
+    import torch
+    import synth
+    import hstu_sequential_transducer_amd as hs
+    dev = torch.device("cuda:0")
+    w = synth.layer_train_4k()
+    T, D, H, d = w.total, w.d_model, w.heads, w.d
+    lay = _dev_layer(w.layers[0], dev)
+    x = torch.from_numpy(w.x).to(dev).to(torch.bfloat16)
+    dy = torch.from_numpy(w.dy).to(dev).to(torch.bfloat16)
+    off = torch.from_numpy(w.offsets.astype(np.int32)).to(dev)
+    ts = torch.from_numpy(w.ts.astype(np.int64)).to(dev)
+    nws = hs.binding.workspace_size(hs.binding.OP_LAYER_BWD, hs.binding._jagged(off, ts, w.n_max, T),
+                                    hs.binding.Dims(1, H, d, d, w.ln_eps), D, 0)
+    wsb = torch.empty(nws, dtype=torch.uint8, device=dev)
+
+    def step():
+        return hs.layer_bwd(off, T, ts, x, lay, dy, H, d, w.n_max, eps=w.ln_eps, workspace=wsb)
+
+    steps = max(10, args.steps // 4)
+    _, ms, per, kern, _ = timed(step, args.warmup, steps)
+    pairs2 = causal_pairs_sum(w.lengths)            # 2 x causal pairs per head
+    f_attn = 2.0 * H * d * pairs2 * 3               # forward again (4d per pair) + backward (8d per pair)
+    f1 = 2.0 * T * D * 4 * H * d                    # f1, dX, dW1: one each
+    f2 = 2.0 * T * H * d * D                        # dG, dW2
+    total = 3 * f1 + 2 * f2 + f_attn
+    w1, w2 = kern.get("gemm_wgrad_w1"), kern.get("gemm_wgrad_w2")
+    return {"workload": "layer-bwd B16 SL(4096,1.6) D512 H4 d128 bf16 (forward recomputed)", "tokens": T,
+            "ms": round(ms, 4), "step_ms": pct(per), "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "total_tflops": round(total / (ms * 1e-3) / 1e12, 2),
+            "wgrad_w1_tflops": round(f1 / (w1["avg_ms"] * 1e-3) / 1e12, 2) if w1 else None,
+            "wgrad_w2_tflops": round(f2 / (w2["avg_ms"] * 1e-3) / 1e12, 2) if w2 else None,
+            "kernels": {n: {"launches": v["launches"] // steps, "avg_ms": round(v["avg_ms"], 5)} for n, v in kern.items()}}
+
+
 def bench_mfalcon(args):
     """M-FALCON: one user, 4096-action history cached for 2 layers, m = 1024
     candidates in microbatches of b_m = 256."""
@@ -252,7 +290,8 @@ def main():
     import hstu_sequential_transducer_amd as hs
 
     if args.extras_only:
-        print(json.dumps({"extras": {"layer_fwd": bench_layer(args), "mfalcon": bench_mfalcon(args)}}), flush=True)
+        print(json.dumps({"extras": {"layer_fwd": bench_layer(args), "layer_bwd": bench_layer_bwd(args),
+                                     "mfalcon": bench_mfalcon(args)}}), flush=True)
         return
     dev = torch.device("cuda:0")
     w = synth.attn_8k(with_grad=True)
@@ -343,7 +382,8 @@ def main():
         torch.cuda.synchronize()
         res["copy_probe_bytes_each_way"] = n * 4
     if not args.no_extras:
-        res["extras"] = {"layer_fwd": bench_layer(args), "mfalcon": bench_mfalcon(args)}
+        res["extras"] = {"layer_fwd": bench_layer(args), "layer_bwd": bench_layer_bwd(args),
+                         "mfalcon": bench_mfalcon(args)}
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, args.cpu_sample_tokens)
         res["cpu_baseline"] = {k2: (round(v2, 6) if isinstance(v2, float) else v2) for k2, v2 in cb.items()}

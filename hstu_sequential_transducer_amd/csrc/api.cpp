@@ -718,7 +718,7 @@ hstu_status hstu_layer_bwd(const hstu_jagged *j, const hstu_dims *dm, int32_t d_
     {
         WgradArgs a{dy.ptr, dy.ld, G, HD, part, D, HD, T, w.p2.chunk, w.p2.splits};
         {
-            ProfScope ps("gemm_wgrad_kernel", st);
+            ProfScope ps("gemm_wgrad_w2", st);
             TRY(launched(launch_gemm_wgrad(a, st), "weight-gradient kernel"));
         }
         ProfScope ps("sum_splits_kernel", st);
@@ -755,7 +755,7 @@ hstu_status hstu_layer_bwd(const hstu_jagged *j, const hstu_dims *dm, int32_t d_
     {
         WgradArgs a{dA, Z4, x.ptr, x.ld, part, Z4, D, T, w.p1.chunk, w.p1.splits};
         {
-            ProfScope ps("gemm_wgrad_kernel", st);
+            ProfScope ps("gemm_wgrad_w1", st);
             TRY(launched(launch_gemm_wgrad(a, st), "weight-gradient kernel"));
         }
         ProfScope ps("sum_splits_kernel", st);
