@@ -50,9 +50,9 @@ CSRC = os.path.join(ROOT, "hstu_sequential_transducer_amd", "csrc")
 # source they were measured on (sha256 over the files listed); otherwise the
 # traffic is reported as null.
 MEASURED_TRAFFIC = {
-    "attn_bwd_bf16_kernel": {"src": "c648b6ba46988a51", "bytes": 2209285734},  # read 1396754512 + write 812531222
-    "attn_fwd_bf16_kernel": {"src": "9877372e46318e42", "bytes": 419866016},  # read 333402448 + write 86463568
-    "dq_gemm_kernel": {"src": "240ca39b4c769bad", "bytes": 929320006},        # read 893906550 + write 35413456
+    "attn_bwd_bf16_kernel": {"src": "55f0686d34d10927", "bytes": 2196106864},  # read 1383592498 + write 812514365
+    "attn_fwd_bf16_kernel": {"src": "08393dad39682fac", "bytes": 430929197},   # read 344467082 + write 86462115
+    "dq_gemm_kernel": {"src": "526aeabacfc88ccb", "bytes": 929056380},         # read 893660735 + write 35395645
 }
 
 
