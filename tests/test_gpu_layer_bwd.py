@@ -123,8 +123,9 @@ def test_layer_bwd_multihead():
 
 
 def test_layer_bwd_no_timestamps_no_bias_grads():
-    """No timestamps (no rab_t term, no drab_t) and db1, db2 not requested."""
-    L = np.array([33, 97, 128])
+    """No timestamps (no rab_t term, no drab_t), db1 and db2 not requested,
+    and an empty sequence inside the batch."""
+    L = np.array([33, 0, 97, 128])
     w = synth.layer_workload("layer-bwd-nots", 55, L, d_model=128, heads=2, d=128, n_max=128, dtype="bf16",
                              with_grad=True)
     lay = strong(w, 65)
