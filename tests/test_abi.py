@@ -79,3 +79,35 @@ def test_workspace_size_grows_with_tokens():
     assert 0 < small < big
     assert big % 256 == 0
     assert lib.hstu_workspace_size(bd.OP_ATTN_FWD, ctypes.byref(_jag(B=0)), ctypes.byref(d), 0, 0) == 0
+
+
+def _call_layer_bwd(dims, D=512, x=256, dy=512, dx=768, dw1=1024, dw2=1280, db1=None, w1=1536, ws=None, ws_bytes=0):
+    lib = hs.load_library()
+    lay = bd.Layer(w1, None, 1792, None, bd.Bias(None, 0, None, 0), bd.HSTU_ACT_SILU)
+    return lib.hstu_layer_bwd(ctypes.byref(_jag()), ctypes.byref(dims), D, ctypes.byref(lay), bd.CMat(x, D),
+                              bd.CMat(dy, D), bd.Mat(dx, D), dw1, db1, dw2, None, None, None, ws, ws_bytes, None)
+
+
+def test_layer_bwd_validation():
+    """hstu_layer_bwd rejects what it does not take before enqueuing
+    anything (the pointers here are never dereferenced)."""
+    assert _call_layer_bwd(_dims(dtype=bd.HSTU_F32, d=32)) == bd.HSTU_ERR_UNSUPPORTED
+    assert _call_layer_bwd(_dims(), D=70) == bd.HSTU_ERR_UNSUPPORTED
+    assert "multiple of 8" in hs.last_error()
+    assert _call_layer_bwd(_dims(), dx=256) == bd.HSTU_ERR_ARG
+    assert "alias" in hs.last_error()
+    assert _call_layer_bwd(_dims(), dw1=None) == bd.HSTU_ERR_ARG
+    assert _call_layer_bwd(_dims(), db1=1024 + 4) == bd.HSTU_ERR_ARG
+    assert "16-byte" in hs.last_error()
+    assert _call_layer_bwd(_dims(), w1=None) == bd.HSTU_ERR_ARG
+    assert _call_layer_bwd(_dims()) == bd.HSTU_ERR_WORKSPACE
+
+
+def test_layer_bwd_workspace_size():
+    lib = hs.load_library()
+    d = _dims()
+    small = lib.hstu_workspace_size(bd.OP_LAYER_BWD, ctypes.byref(_jag(T=100)), ctypes.byref(d), 512, 0)
+    big = lib.hstu_workspace_size(bd.OP_LAYER_BWD, ctypes.byref(_jag(T=100000)), ctypes.byref(d), 512, 0)
+    attn = lib.hstu_workspace_size(bd.OP_ATTN_BWD, ctypes.byref(_jag(T=100000)), ctypes.byref(d), 0, 0)
+    assert 0 < small < big and big > attn and big % 256 == 0
+    assert lib.hstu_workspace_size(bd.OP_LAYER_BWD, ctypes.byref(_jag(T=100)), ctypes.byref(d), 0, 0) == 0
