@@ -13,7 +13,9 @@
 // bf16, main kernel: 256x128 output tile per workgroup of 4 waves, each wave
 // 64 rows x 128 columns (2x4 blocks of 32x32x16 bf16 MFMA computing C^T, so
 // a lane owns a row and 4 consecutive columns per register group); two
-// workgroups per CU.  K advances in steps of 32 through three LDS stages
+// workgroups per CU.  Products with fewer than two rounds of such tiles
+// (M-FALCON's candidates, narrow outputs) take 128x128 tiles, each wave
+// 32 rows, which doubles their workgroups.  K advances in steps of 32 through three LDS stages
 // filled by direct global -> LDS copies two steps ahead, with a plain
 // barrier per step (no wait for the copies still in flight); 64-byte stage
 // rows have their 16-byte chunks XOR-swizzled by (row / 4) % 4, which keeps
@@ -51,8 +53,8 @@ DEV void store_out(void *p, int64_t i, float x)
 
 // main kernel geometry
 // (NW waves: 4 -> 256 x 128 tiles, 8 -> 256 x 256)
-constexpr int TBM = 256, TBK = 32, TSTAGES = 3;
-template <int TBN>
+constexpr int TBK = 32, TSTAGES = 3;
+template <int TBM, int TBN>
 struct alignas(16) TStage {
     alignas(16) bf16 a[TBM * TBK]; // [row][k], 64-byte rows, swizzled
     alignas(16) bf16 w[TBN * TBK];
@@ -74,17 +76,17 @@ DEV void store4(void *p, int64_t i, const floatx4 &x, bool f32)
 
 // EPI: activation; RES: residual none (0), bf16 (1), fp32 (2).  Waves form a
 // WGM x WGN grid; each wave owns 32 TI rows x 128 columns (TI x 4 MFMA
-// blocks); TBM = 32 TI WGM must be 256.  TI = 2 runs two waves per SIMD
+// blocks); the tile has TBM = 32 TI WGM rows.  TI = 2 runs two waves per SIMD
 // (two workgroups per CU), TI = 4 one (its 256 accumulators use the whole
 // register file).
 template <int EPI, int RES, int TI, int WGM, int WGN>
-__global__ void __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(TI == 2 ? 2 : 1, TI == 2 ? 2 : 1)))
+__global__ void __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(TI == 4 ? 1 : 2, TI == 4 ? 1 : 2)))
 gemm_bf16_tiled_kernel(GemmArgs g, int tiles_n, int n_tiles, int per_xcd)
 {
     constexpr int NW = WGM * WGN, TBN = 128 * WGN, TNT = 64 * NW;
-    static_assert(32 * TI * WGM == TBM, "tile rows");
+    constexpr int TBM = 32 * TI * WGM;
     constexpr int CA = TBM / 16 / NW, CW = TBN / 16 / NW; // direct copies per wave per stage (16 rows each)
-    __shared__ TStage<TBN> st[TSTAGES];
+    __shared__ TStage<TBM, TBN> st[TSTAGES];
     __shared__ __align__(16) float bias_s[TBN];
     const int t = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
     if (t >= n_tiles) return;
@@ -104,7 +106,7 @@ gemm_bf16_tiled_kernel(GemmArgs g, int tiles_n, int n_tiles, int per_xcd)
     // copies of step kt into stage S: 16 rows per wave instruction, A rows
     // [16 CA w, 16 CA (w + 1)) and W rows [32w, 32w + 32); rows past M or N
     // re-read the last row
-    auto gload = [&](int kt, TStage<TBN> &S) {
+    auto gload = [&](int kt, TStage<TBM, TBN> &S) {
         const int k0 = kt * TBK;
 #pragma unroll
         for (int i = 0; i < CA; i++) {
@@ -138,7 +140,7 @@ gemm_bf16_tiled_kernel(GemmArgs g, int tiles_n, int n_tiles, int per_xcd)
 
     // one K step: 2 sub-steps of 16; operands of sub-step 1 are read while
     // the MFMAs of sub-step 0 run
-    auto compute = [&](const TStage<TBN> &S) {
+    auto compute = [&](const TStage<TBM, TBN> &S) {
         bf16x8 a[2][TI], b[2][4];
         auto fetch = [&](int ks) {
             const int col = 16 * ks + 8 * gq;
@@ -393,13 +395,25 @@ hipError_t launch_gemm_bf16(const GemmArgs &g, hipStream_t st)
 {
     if (g.M <= 0 || g.N <= 0) return hipSuccess;
     if (tiled_ok(g)) {
+        // 256-row tiles when they make at least two rounds of workgroups
+        // (two per CU), else 128-row tiles: twice the workgroups for small
+        // products (M-FALCON's 1024 candidates, narrow outputs)
         const int tiles_n = (g.N + 127) / 128;
-        const int64_t n_tiles = (int64_t)tiles_n * ((g.M + TBM - 1) / TBM);
+        const bool tall = (int64_t)tiles_n * ((g.M + 255) / 256) >= 1024;
+        const int tbm = tall ? 256 : 128;
+        const int64_t n_tiles = (int64_t)tiles_n * ((g.M + tbm - 1) / tbm);
         const int per_xcd = (int)((n_tiles + 7) / 8);
         const dim3 grid(8 * per_xcd), block(256);
         const int res = g.R32 ? 2 : (g.R16 ? 1 : 0);
 #define HSTU_GEMM_LAUNCH(E, R)                                                                                         \
-    hipLaunchKernelGGL((gemm_bf16_tiled_kernel<E, R, 2, 4, 1>), grid, block, 0, st, g, tiles_n, (int)n_tiles, per_xcd)
+    do {                                                                                                               \
+        if (tall)                                                                                                      \
+            hipLaunchKernelGGL((gemm_bf16_tiled_kernel<E, R, 2, 4, 1>), grid, block, 0, st, g, tiles_n, (int)n_tiles,  \
+                               per_xcd);                                                                               \
+        else                                                                                                           \
+            hipLaunchKernelGGL((gemm_bf16_tiled_kernel<E, R, 1, 4, 1>), grid, block, 0, st, g, tiles_n, (int)n_tiles,  \
+                               per_xcd);                                                                               \
+    } while (0)
 #define HSTU_GEMM_RES(E)                                                                                               \
     do {                                                                                                               \
         if (res == 2) HSTU_GEMM_LAUNCH(E, 2);                                                                          \
