@@ -48,7 +48,9 @@ struct alignas(16) Stage {
 } // namespace
 
 // One workgroup: items in order (user u, microbatch, 128-candidate tile, head,
-// split).  The item list is built serially per user by a single workgroup.
+// split).  Per chunk of 1024 users: each thread counts its user's tiles, a
+// scan gives every user's first tile, then all threads write the chunk's
+// items (one per thread and pass).
 __global__ void __launch_bounds__(1024) mfalcon_sched_kernel(const int32_t *__restrict__ hoff,
                                                               const int32_t *__restrict__ coff, int U, int M, int H,
                                                               int b_m, int nsplit, int4 *__restrict__ items,
@@ -93,21 +95,30 @@ __global__ void __launch_bounds__(1024) mfalcon_sched_kernel(const int32_t *__re
             cnt[tid] += v;
             __syncthreads();
         }
-        const int first = base_s + cnt[tid] - tiles; // first tile index of user u
-        if (u < U && tiles > 0) {
-            const int m = coff[u + 1] - coff[u];
-            int t = first;
-            for (int s = 0; s < m; s += b_m) {
-                const int e = min(m, s + b_m);
-                for (int r = s; r < e; r += TC, t++) {
-                    const int rows = min(TC, e - r);
-                    for (int h = 0; h < H; h++)
-                        for (int sp = 0; sp < nsplit; sp++) {
-                            const int idx = (t * H + h) * nsplit + sp;
-                            if (idx < max_items) items[idx] = make_int4(u, coff[u] + r, rows, (h << 16) | sp);
-                        }
-                }
+        // the chunk's items, all threads together: item i -> tile lt of the
+        // chunk (its user found by binary search over the inclusive scan),
+        // then that user's microbatch and candidate rows
+        const int chunk_tiles = cnt[1023];
+        const int per_tile = H * nsplit;
+        const int n_chunk = min(U - c0, 1024);
+        for (int i = tid; i < chunk_tiles * per_tile; i += 1024) {
+            const int lt = i / per_tile, hs = i - lt * per_tile;
+            int lo = 0, hi = n_chunk - 1; // first user v of the chunk with cnt[v] > lt
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (cnt[mid] > lt) hi = mid;
+                else lo = mid + 1;
             }
+            const int v = c0 + lo;
+            const int ut = lt - (lo > 0 ? cnt[lo - 1] : 0); // tile of user v
+            const int m = coff[v + 1] - coff[v];
+            const int tpm = (b_m + TC - 1) / TC; // tiles of a full microbatch
+            const int mb = ut / tpm, s0 = mb * b_m, e = min(m, s0 + b_m);
+            const int r = s0 + (ut - mb * tpm) * TC;
+            const int rows = min(TC, e - r);
+            const int t = base_s + lt;
+            const int idx = t * per_tile + hs;
+            if (idx < max_items) items[idx] = make_int4(v, coff[v] + r, rows, ((hs / nsplit) << 16) | (hs % nsplit));
         }
         __syncthreads();
         if (tid == 1023) base_s += cnt[1023];
