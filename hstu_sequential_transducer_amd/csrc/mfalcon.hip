@@ -288,15 +288,50 @@ __global__ void __launch_bounds__(256) mfalcon_epilogue_kernel(const float *__re
     const int64_t zr = (int64_t)row * ldz;
     float x[VPL];
     float qk = 0.f;
+    float vv[VPL]; // this lane's V features (the self term)
+    if constexpr (BF && VPL % 4 == 0) {
+        if (F == 64 * VPL) {
+            // a full row per wave: 16- or 32-byte loads, consecutive lanes on
+            // consecutive features (the partial sums in split order)
+            const int c0 = lane * VPL;
 #pragma unroll
-    for (int i = 0; i < VPL; i++) {
-        const int c = lane * VPL + i;
-        float v = 0.f;
-        if (c < F) {
-            for (int s = 0; s < nsplit; s++) v += part[(int64_t)s * M * F + (int64_t)row * F + c];
-            qk += ld(zr + 2 * F + c) * ld(zr + 3 * F + c); // q.k partial of this lane's head
+            for (int i = 0; i < VPL; i++) x[i] = 0.f;
+            const float *pr = part + (int64_t)row * F + c0;
+            for (int sp = 0; sp < nsplit; sp++) {
+#pragma unroll
+                for (int i = 0; i < VPL; i += 4) {
+                    const floatx4 p4 = *(const floatx4 *)(pr + (int64_t)sp * M * F + i);
+#pragma unroll
+                    for (int e = 0; e < 4; e++) x[i + e] += p4[e];
+                }
+            }
+            const bf16 *zb = (const bf16 *)Z + zr + c0;
+#pragma unroll
+            for (int i = 0; i < VPL; i += 4) {
+                const u32x2 q2 = *(const u32x2 *)(zb + 2 * F + i), k2 = *(const u32x2 *)(zb + 3 * F + i),
+                            v2 = *(const u32x2 *)(zb + F + i);
+                qk += bf16_lo(q2[0]) * bf16_lo(k2[0]) + bf16_hi(q2[0]) * bf16_hi(k2[0]) +
+                      bf16_lo(q2[1]) * bf16_lo(k2[1]) + bf16_hi(q2[1]) * bf16_hi(k2[1]);
+                vv[i] = bf16_lo(v2[0]);
+                vv[i + 1] = bf16_hi(v2[0]);
+                vv[i + 2] = bf16_lo(v2[1]);
+                vv[i + 3] = bf16_hi(v2[1]);
+            }
         }
-        x[i] = v;
+    }
+    if (!(BF && VPL % 4 == 0) || F != 64 * VPL) {
+#pragma unroll
+        for (int i = 0; i < VPL; i++) {
+            const int c = lane * VPL + i;
+            float v = 0.f;
+            vv[i] = 0.f;
+            if (c < F) {
+                for (int sp = 0; sp < nsplit; sp++) v += part[(int64_t)sp * M * F + (int64_t)row * F + c];
+                qk += ld(zr + 2 * F + c) * ld(zr + 3 * F + c); // q.k partial of this lane's head
+                vv[i] = ld(zr + F + c);
+            }
+            x[i] = v;
+        }
     }
     // segmented sum of q.k over the lanes of one head (d / VPL lanes)
     const int seg = d / VPL;
@@ -312,7 +347,7 @@ __global__ void __launch_bounds__(256) mfalcon_epilogue_kernel(const float *__re
 #pragma unroll
     for (int i = 0; i < VPL; i++) {
         const int c = lane * VPL + i;
-        if (c < F) x[i] = (x[i] + ps * ld(zr + F + c)) * inv_n;
+        if (c < F) x[i] = (x[i] + ps * vv[i]) * inv_n;
         s += c < F ? x[i] : 0.f;
     }
     const float mean = wave_sum(s) / (float)F;
@@ -325,6 +360,22 @@ __global__ void __launch_bounds__(256) mfalcon_epilogue_kernel(const float *__re
     }
     const float var = wave_sum(q) / (float)F;
     const float rstd = 1.0f / sqrtf(var + eps);
+    if constexpr (BF && VPL % 4 == 0) {
+        if (F == 64 * VPL) {
+            const bf16 *ub = (const bf16 *)Z + zr + lane * VPL; // U block first
+            bf16 *gb = (bf16 *)G + (int64_t)row * ldg + lane * VPL;
+#pragma unroll
+            for (int i = 0; i < VPL; i += 4) {
+                const u32x2 u2 = *(const u32x2 *)(ub + i);
+                const float u4[4] = {bf16_lo(u2[0]), bf16_hi(u2[0]), bf16_lo(u2[1]), bf16_hi(u2[1])};
+                float g4[4];
+#pragma unroll
+                for (int e = 0; e < 4; e++) g4[e] = (x[i + e] - mean) * rstd * u4[e];
+                *(u32x2 *)(gb + i) = u32x2{pack2_bf16(g4[0], g4[1]), pack2_bf16(g4[2], g4[3])};
+            }
+            return;
+        }
+    }
 #pragma unroll
     for (int i = 0; i < VPL; i++) {
         const int c = lane * VPL + i;
