@@ -281,24 +281,29 @@ def layer_fwd(offsets: torch.Tensor, total: int, ts: Optional[torch.Tensor], x: 
 
 def layer_bwd(offsets: torch.Tensor, total: int, ts: Optional[torch.Tensor], x: torch.Tensor, layer: dict,
               dy: torch.Tensor, heads: int, d: int, n_max: int, eps: float = 1e-5, want_bias_grads: bool = True,
-              want_drab: bool = True, workspace: Optional[torch.Tensor] = None) -> dict:
+              want_drab: bool = True, workspace: Optional[torch.Tensor] = None,
+              out: Optional[dict] = None) -> dict:
     """hstu_layer_bwd (the forward recomputed from x).  Returns dict dx
     [T][D] (x's dtype), dw1 [4Hd][D], db1, dw2 [D][Hd], db2, drab_p, drab_t
-    (fp32; the optional ones None when not requested)."""
+    (fp32; the optional ones None when not requested).  `out`, if given, is
+    a dict of that form from an earlier call whose tensors are reused."""
     lib = load_library()
     T, D = x.shape
     HD = heads * d
     jag = _jagged(offsets, ts, n_max, total)
     dims = Dims(_dtype_code(x), heads, d, d, eps)
-    f32 = dict(dtype=torch.float32, device=x.device)
-    dx = torch.empty_like(x)
-    dw1 = torch.empty((4 * HD, D), **f32)
-    dw2 = torch.empty((D, HD), **f32)
-    db1 = torch.empty(4 * HD, **f32) if want_bias_grads else None
-    db2 = torch.empty(D, **f32) if want_bias_grads else None
     rp, rt = layer.get("rab_p"), layer.get("rab_t")
-    drp = torch.empty_like(rp) if (want_drab and rp is not None) else None
-    drt = torch.empty_like(rt) if (want_drab and rt is not None and ts is not None) else None
+    if out is not None:
+        dx, dw1, dw2, db1, db2, drp, drt = (out[k] for k in ("dx", "dw1", "dw2", "db1", "db2", "drab_p", "drab_t"))
+    else:
+        f32 = dict(dtype=torch.float32, device=x.device)
+        dx = torch.empty_like(x)
+        dw1 = torch.empty((4 * HD, D), **f32)
+        dw2 = torch.empty((D, HD), **f32)
+        db1 = torch.empty(4 * HD, **f32) if want_bias_grads else None
+        db2 = torch.empty(D, **f32) if want_bias_grads else None
+        drp = torch.empty_like(rp) if (want_drab and rp is not None) else None
+        drt = torch.empty_like(rt) if (want_drab and rt is not None and ts is not None) else None
     nws = workspace_size(OP_LAYER_BWD, jag, dims, D, 0)
     ws = workspace if workspace is not None else _workspace(nws, x.device)
     L = _layer_struct(layer)
