@@ -15,7 +15,8 @@
 // a lane owns a row and 4 consecutive columns per register group); two
 // workgroups per CU.  Products with fewer than two rounds of such tiles
 // (M-FALCON's candidates, narrow outputs) take 128x128 tiles, each wave
-// 32 rows, which doubles their workgroups.  K advances in steps of 32 through three LDS stages
+// 32 rows, which doubles their workgroups; products that would still leave
+// most CUs idle take 64x128 tiles of 2 waves.  K advances in steps of 32 through three LDS stages
 // filled by direct global -> LDS copies two steps ahead, with a plain
 // barrier per step (no wait for the copies still in flight); 64-byte stage
 // rows have their 16-byte chunks XOR-swizzled by (row / 4) % 4, which keeps
@@ -399,20 +400,24 @@ hipError_t launch_gemm_bf16(const GemmArgs &g, hipStream_t st)
         // (two per CU), else 128-row tiles: twice the workgroups for small
         // products (M-FALCON's 1024 candidates, narrow outputs)
         const int tiles_n = (g.N + 127) / 128;
-        const bool tall = (int64_t)tiles_n * ((g.M + 255) / 256) >= 1024;
-        const int tbm = tall ? 256 : 128;
+        const int64_t t256 = (int64_t)tiles_n * ((g.M + 255) / 256);
+        // 64-row tiles (2 waves) when even 128-row tiles would leave most CUs idle
+        const int tbm = t256 >= 1024 ? 256 : (t256 >= 128 ? 128 : 64);
         const int64_t n_tiles = (int64_t)tiles_n * ((g.M + tbm - 1) / tbm);
         const int per_xcd = (int)((n_tiles + 7) / 8);
-        const dim3 grid(8 * per_xcd), block(256);
+        const dim3 grid(8 * per_xcd);
         const int res = g.R32 ? 2 : (g.R16 ? 1 : 0);
 #define HSTU_GEMM_LAUNCH(E, R)                                                                                         \
     do {                                                                                                               \
-        if (tall)                                                                                                      \
-            hipLaunchKernelGGL((gemm_bf16_tiled_kernel<E, R, 2, 4, 1>), grid, block, 0, st, g, tiles_n, (int)n_tiles,  \
-                               per_xcd);                                                                               \
+        if (tbm == 256)                                                                                                \
+            hipLaunchKernelGGL((gemm_bf16_tiled_kernel<E, R, 2, 4, 1>), grid, dim3(256), 0, st, g, tiles_n,            \
+                               (int)n_tiles, per_xcd);                                                                 \
+        else if (tbm == 128)                                                                                           \
+            hipLaunchKernelGGL((gemm_bf16_tiled_kernel<E, R, 1, 4, 1>), grid, dim3(256), 0, st, g, tiles_n,            \
+                               (int)n_tiles, per_xcd);                                                                 \
         else                                                                                                           \
-            hipLaunchKernelGGL((gemm_bf16_tiled_kernel<E, R, 1, 4, 1>), grid, block, 0, st, g, tiles_n, (int)n_tiles,  \
-                               per_xcd);                                                                               \
+            hipLaunchKernelGGL((gemm_bf16_tiled_kernel<E, R, 1, 2, 1>), grid, dim3(128), 0, st, g, tiles_n,            \
+                               (int)n_tiles, per_xcd);                                                                 \
     } while (0)
 #define HSTU_GEMM_RES(E)                                                                                               \
     do {                                                                                                               \
