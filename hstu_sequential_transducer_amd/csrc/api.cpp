@@ -33,14 +33,11 @@ hstu_status ok()
     return HSTU_OK;
 }
 
+// HSTU_DEBUG=1: read at every call (a process may switch it on and off).
 bool debug_mode()
 {
-    static int v = -1;
-    if (v < 0) {
-        const char *e = getenv("HSTU_DEBUG");
-        v = (e && e[0] == '1') ? 1 : 0;
-    }
-    return v == 1;
+    const char *e = getenv("HSTU_DEBUG");
+    return e && e[0] == '1';
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -66,14 +63,19 @@ int max_items_for(int B, int T, int tile, int H)
 
 // Workspace of the attention entry points.
 struct AttnWs {
-    size_t header, items, rel, wide, obuf, dO, ds_base, ds, dq, total;
+    size_t header, items, rel, wide, rank, obuf, dO, ds_base, ds, dq, pbase, tbase, dpart, tpart, total;
     int64_t ds_cap; // elements of the dS buffer
+    int64_t p_cap;  // floats of the drab_p partial slots
 };
 
 // The backward (bwd = true) also carves the dS buffer: H planes of P x P
 // bf16 per sequence, P = L rounded up to DS_PAD.  sum_b P_b^2 <= (n_max +
 // DS_PAD - 1) (T + (DS_PAD - 1) B) for sequences no longer than n_max; a
-// sequence beyond what is left takes the fp32-atomic dQ path instead.
+// sequence beyond what is left takes the fp32-atomic dQ path instead.  The
+// same bound holds for the drab_p partial slots (H n_b L_b floats per
+// sequence, n_b = ceil(L_b / 128) <= ceil(n_max / 128)): sequences past it
+// add their share of drab_p with atomics.  The drab_t slots (H n_b TB_SLOTS
+// floats) always fit.
 AttnWs attn_ws(const hstu_jagged *j, const hstu_dims *dm, int tile, bool bwd)
 {
     AttnWs w{};
@@ -83,6 +85,7 @@ AttnWs attn_ws(const hstu_jagged *j, const hstu_dims *dm, int tile, bool bwd)
     w.items = c.take((size_t)2 * max_items_for(B, T, tile, H) * sizeof(int2)); // split items: up to 2 per tile
     w.rel = c.take((size_t)T * 4 * 3); // rel, then rmin and rmax per 32-token block
     w.wide = c.take((size_t)B * 4);
+    w.rank = c.take((size_t)B * 4);
     w.obuf = c.take((size_t)T * H * dm->d_v * 4);
     if (bwd) {
         w.dO = c.take((size_t)T * H * dm->d_v * 2 * 2); // hi and lo bf16 planes
@@ -90,6 +93,11 @@ AttnWs attn_ws(const hstu_jagged *j, const hstu_dims *dm, int tile, bool bwd)
         w.ds_cap = ((int64_t)j->n_max + DS_PAD - 1) * ((int64_t)T + (int64_t)(DS_PAD - 1) * B) * H;
         w.ds = c.take((size_t)w.ds_cap * 2);
         w.dq = c.take((size_t)T * H * dm->d_qk * 4); // dQ accumulator of sequences beyond the dS buffer
+        w.pbase = c.take((size_t)B * 8);
+        w.tbase = c.take((size_t)B * 8);
+        w.p_cap = (int64_t)H * (((int64_t)j->n_max + BWD_BN - 1) / BWD_BN) * (int64_t)T;
+        w.dpart = c.take((size_t)w.p_cap * 4);
+        w.tpart = c.take((size_t)max_items_for(B, T, BWD_BN, H) * TB_SLOTS * 4);
     }
     w.total = c.cur;
     return w;
@@ -161,6 +169,19 @@ hstu_status check_view(const void *p, int64_t ld, int64_t width, const char *nam
     return HSTU_OK;
 }
 
+// bf16 activations are moved with 16-byte accesses (global -> LDS copies,
+// vector loads and stores): base 16-byte aligned and ld a multiple of 8.
+// fp32 buffers written with 16-byte stores (o_save) need the same base.
+hstu_status check_vec_view(const void *p, int64_t ld, hstu_dtype dt, const char *name)
+{
+    if (!p) return HSTU_OK;
+    if (dt == HSTU_BF16 && ((((uintptr_t)p) & 15) != 0 || (ld % 8) != 0))
+        return fail(HSTU_ERR_ARG, "%s must be 16-byte aligned with ld a multiple of 8 (bf16)", name);
+    if (dt == HSTU_F32 && (((uintptr_t)p) & 15) != 0)
+        return fail(HSTU_ERR_ARG, "%s must be 16-byte aligned", name);
+    return HSTU_OK;
+}
+
 hstu_status check_ws(void *ws, size_t ws_bytes, size_t need)
 {
     if (need == 0) return HSTU_OK;
@@ -219,7 +240,7 @@ hstu_status attn_fwd_launch(const hstu_jagged *j, const hstu_dims *dm, const hst
     {
         ProfScope ps("sched_kernel", st);
         launch_sched(j->offsets, j->ts, B, T, tile, H, status, n_items, items, max_items, rel, wide,
-                     split ? concurrent_slots() : 0, t_split, nullptr, 0, nullptr, 0, nullptr, 0, st);
+                     (int32_t *)(wb + w.rank), split ? concurrent_slots() : 0, t_split, SchedBwd{}, st);
     }
     TRY(launched(hipGetLastError(), "schedule kernel"));
     if (split) {
@@ -270,7 +291,7 @@ hstu_status attn_fwd_launch(const hstu_jagged *j, const hstu_dims *dm, const hst
         {
             ProfScope ps("ln_gate_fwd_kernel", st);
             e = launch_ln_gate_fwd(obuf, F, 1, 0, u.ptr, u.ld, dm->dtype == HSTU_BF16, out.ptr, out.ld, ln_stats, nullptr,
-                                   0, T, F, dm->ln_eps, nullptr, st);
+                                   0, T, F, dm->ln_eps, status, st);
         }
         TRY(launched(e, "LayerNorm gate kernel"));
     }
@@ -299,11 +320,26 @@ hstu_status attn_bwd_launch(const hstu_jagged *j, const hstu_dims *dm, const hst
     const int max_items = max_items_for(B, T, BWD_BN, H);
     const int64_t p_hs = has_p ? bias->rab_p_hstride : 2 * (int64_t)N + 1;
     const int64_t t_hs = (bias && bias->rab_t) ? bias->rab_t_hstride : 128;
+    int64_t *pbase = (int64_t *)(wb + w.pbase), *tbase = (int64_t *)(wb + w.tbase);
+    float *dpart = (float *)(wb + w.dpart), *tpart = (float *)(wb + w.tpart);
     {
         ProfScope ps("sched_kernel", st);
-        // (the scheduler also zeroes drab_p and drab_t)
-        launch_sched(j->offsets, j->ts, B, T, BWD_BN, H, status, n_items, items, max_items, rel, wide, 0, nullptr,
-                     ds_base, w.ds_cap, drab_p, (int64_t)H * p_hs, drab_t, (int64_t)H * t_hs, st);
+        // (the scheduler also zeroes drab_p, which sequences without partial
+        // slots add into)
+        SchedBwd sb{};
+        sb.ds_base = ds_base;
+        sb.ds_cap = w.ds_cap;
+        sb.pbase = pbase;
+        sb.p_cap = w.p_cap;
+        sb.tbase = tbase;
+        sb.zero0 = drab_p;
+        sb.n0 = (int64_t)H * p_hs;
+        if (!has_t) { // requested without a time term: its gradient is zero
+            sb.zero1 = drab_t;
+            sb.n1 = (int64_t)H * t_hs;
+        }
+        launch_sched(j->offsets, j->ts, B, T, BWD_BN, H, status, n_items, items, max_items, rel, wide,
+                     (int32_t *)(wb + w.rank), 0, nullptr, sb, st);
     }
     TRY(launched(hipGetLastError(), "schedule kernel"));
     {
@@ -352,9 +388,31 @@ hstu_status attn_bwd_launch(const hstu_jagged *j, const hstu_dims *dm, const hst
     a.lddv = dv.ld;
     a.drab_p = drab_p;
     a.drab_t = has_t ? drab_t : nullptr;
+    a.dpart = dpart;
+    a.pbase = pbase;
+    a.tpart = tpart;
+    a.tbase = tbase;
     {
         ProfScope ps("attn_bwd_bf16_kernel", st);
         TRY(launched(launch_attn_bwd_bf16(a, max_items, st), "attention backward kernel"));
+    }
+    if (drab_p || (drab_t && has_t)) {
+        DrabReduceArgs r{};
+        r.offsets = j->offsets;
+        r.B = B;
+        r.H = H;
+        r.N = N;
+        r.status = status;
+        r.dpart = dpart;
+        r.pbase = pbase;
+        r.tpart = tpart;
+        r.tbase = tbase;
+        r.drab_p = drab_p;
+        r.p_hs = p_hs;
+        r.drab_t = has_t ? drab_t : nullptr;
+        r.t_hs = t_hs;
+        ProfScope ps("drab_reduce_kernel", st);
+        TRY(launched(launch_drab_reduce(r, st), "bias-gradient reduction kernel"));
     }
     {
         DqArgs qa{};
@@ -570,6 +628,14 @@ hstu_status hstu_attn_fwd(const hstu_jagged *j, const hstu_dims *dm, const hstu_
     TRY(check_view(u.ptr, u.ld, (int64_t)F, "u", false));
     TRY(check_view(out.ptr, out.ld, (int64_t)F, "out"));
     if (ln_stats && !u.ptr) return fail(HSTU_ERR_ARG, "ln_stats requires u (the epilogue)");
+    if (dm->dtype == HSTU_BF16) {
+        TRY(check_vec_view(q.ptr, q.ld, HSTU_BF16, "q"));
+        TRY(check_vec_view(k.ptr, k.ld, HSTU_BF16, "k"));
+        TRY(check_vec_view(v.ptr, v.ld, HSTU_BF16, "v"));
+        TRY(check_vec_view(u.ptr, u.ld, HSTU_BF16, "u"));
+        TRY(check_vec_view(out.ptr, out.ld, HSTU_BF16, "out"));
+        TRY(check_vec_view(o_save, F, HSTU_F32, "o_save"));
+    }
     const AttnWs w = attn_ws(j, dm, fwd_tile(dm), false);
     TRY(check_ws(ws, ws_bytes, w.total));
     hipStream_t st = (hipStream_t)stream;
@@ -599,6 +665,13 @@ hstu_status hstu_attn_bwd(const hstu_jagged *j, const hstu_dims *dm, const hstu_
         TRY(check_view(u.ptr, u.ld, (int64_t)F, "u"));
         TRY(check_view(du.ptr, du.ld, (int64_t)F, "du"));
         if (!o_save || !ln_stats) return fail(HSTU_ERR_ARG, "with u, o_save and ln_stats from the forward are required");
+    }
+    {
+        const struct { const void *p; int64_t ld; const char *n; } views[] = {
+            {q.ptr, q.ld, "q"}, {k.ptr, k.ld, "k"}, {v.ptr, v.ld, "v"}, {u.ptr, u.ld, "u"}, {dout.ptr, dout.ld, "dout"},
+            {dq.ptr, dq.ld, "dq"}, {dk.ptr, dk.ld, "dk"}, {dv.ptr, dv.ld, "dv"}, {du.ptr, du.ld, "du"}};
+        for (const auto &x : views) TRY(check_vec_view(x.p, x.ld, HSTU_BF16, x.n));
+        TRY(check_vec_view(o_save, F, HSTU_F32, "o_save"));
     }
     const bool has_p = bias && bias->rab_p;
     const bool has_t = bias && bias->rab_t && j->ts;
@@ -790,6 +863,8 @@ hstu_status mfalcon_score(const hstu_jagged *hist, const hstu_dims *dm, int32_t 
         TRY(check_layer(&layers[l], hist, dm, D, l));
         TRY(check_view(k_cache[l].ptr, k_cache[l].ld, HD, "k_cache[l]"));
         TRY(check_view(v_cache[l].ptr, v_cache[l].ld, HD, "v_cache[l]"));
+        TRY(check_vec_view(k_cache[l].ptr, k_cache[l].ld, dm->dtype, "k_cache[l]"));
+        TRY(check_vec_view(v_cache[l].ptr, v_cache[l].ld, dm->dtype, "v_cache[l]"));
     }
     const MfWs w = mf_ws(hist, dm, D, M);
     const MfPlan p = mf_plan(hist, dm, M);
@@ -805,7 +880,7 @@ hstu_status mfalcon_score(const hstu_jagged *hist, const hstu_dims *dm, int32_t 
     {
         ProfScope ps("mfalcon_sched_kernel", st);
         TRY(launched(launch_mfalcon_sched(hist->offsets, cand_offsets, hist->batch, M, H, b_m, p.nsplit, items,
-                                          n_items, status, p.max_items, st),
+                                          n_items, status, p.max_items, hist->total, st),
                      "M-FALCON schedule kernel"));
     }
     for (int l = 0; l < n_layers; l++) {

@@ -74,7 +74,7 @@ constexpr int DK = 160;    // diagonals of the skewed dS tile: key - query + BQ 
 // rows, and 40 = 8 (mod 16) makes each column write (64 lanes: 32 keys x 2
 // query halves 4 rows apart) hit 64 different banks.
 constexpr int DKP = 40;
-constexpr int TB = 64;     // time buckets that int64 differences can reach
+constexpr int TB = TB_SLOTS; // time buckets that int64 differences can reach
 constexpr int TCOPY = 2;   // copies of each K wave's drab_t table
 constexpr float NLOG2E = -1.4426950408889634f;
 constexpr float NLN2 = -0.69314718055994531f;
@@ -499,7 +499,6 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
     }
 
     const int p_hs = a.rp_hs > 0 ? (int)a.rp_hs : 2 * a.N + 1;
-    const int t_hs = a.rt_hs > 0 ? (int)a.rt_hs : 128;
 
     // Accumulating wave, block at q0m (stage SQ, tiles of buffer b), keys of
     // this group: dV^T += dO'^T P and dK^T += Q^T dS, contractions over the
@@ -607,12 +606,24 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
         tot = sm.ring[slot] + sum;
         sm.ring[slot] = c > BN - 2 ? 0.f : tot;
     };
-    auto drabp_flush = [&](int dl, float tot) {
-        const int c = tid < DK - 1 ? tid : DK - 1;
-        if (c > BN - 2 && tot != 0.f) {
+    // A finished sum goes to this item's slot of partial sums (indexed by
+    // key - query in [k0 - (L - 1), 0], the causal values this key tile
+    // meets; drab_reduce_kernel adds the slots in a fixed order), or, for a
+    // sequence whose slots did not fit, into drab_p with an atomic add.
+    const int tk = k0 / BN, ntk = (L + BN - 1) / BN;
+    float *pslot = nullptr;
+    if (a.drab_p && a.pbase[b_seq] >= 0)
+        pslot = a.dpart + a.pbase[b_seq] + ((int64_t)h * ntk + tk) * L + (L - 1);
+    auto put_p = [&](int dl, float v) {
+        if (pslot) {
+            if (dl <= 0 && dl >= k0 - (L - 1)) pslot[dl] = v;
+        } else if (v != 0.f) {
             const int cl = dl < -a.N ? -a.N : (dl > a.N ? a.N : dl);
-            atomicAdd(&a.drab_p[h * p_hs + cl + a.N], tot);
+            atomicAdd(&a.drab_p[h * p_hs + cl + a.N], v);
         }
+    };
+    auto drabp_flush = [&](int dl, float tot) {
+        if (tid < DK - 1 && tid > BN - 2) put_p(dl, tot); // (the zero row DK - 1 is nobody's)
     };
 
     // ---- one query block.  MAIN: a block in the middle of the range (every
@@ -874,20 +885,14 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
     if (a.drab_p) {
         // remaining key - query values: [k0 - qlast - (BQ - 1), k0 + BN - 1 - qlast - BQ]
         const int lo = k0 - qlast - (BQ - 1), hi = k0 + BN - 1 - qlast - BQ;
-        for (int dl = lo + tid; dl <= hi; dl += NT) {
-            const float v = sm.ring[dl & (RING - 1)];
-            if (v != 0.f) {
-                const int cl = dl < -a.N ? -a.N : (dl > a.N ? a.N : dl);
-                atomicAdd(&a.drab_p[h * p_hs + cl + a.N], v);
-            }
-        }
+        for (int dl = lo + tid; dl <= hi; dl += NT) put_p(dl, sm.ring[dl & (RING - 1)]);
     }
     if constexpr (DT && TM != 0) {
-        if (tid < TB) {
+        if (tid < TB) { // this item's slot of drab_t partial sums (added up by drab_reduce_kernel)
             float s = 0.f;
             for (int pp = 0; pp < 4; pp++)
                 for (int c = 0; c < TCOPY; c++) s += sm.dtab[pp][c][tid];
-            if (s != 0.f) atomicAdd(&a.drab_t[h * t_hs + tid], s);
+            a.tpart[a.tbase[b_seq] + ((int64_t)h * ntk + tk) * TB_SLOTS + tid] = s;
         }
     }
 }
@@ -963,4 +968,81 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs &a, int max_items, hipStream_t
     if (tmode == 0) return launch_variant<false, 0>(a, max_items, st);
     if (tmode == 1) return launch_variant<false, 1>(a, max_items, st);
     return launch_variant<false, 2>(a, max_items, st);
+}
+
+// ---------------------------------------------------------------------------
+// The bias gradients from the items' partial sums, added in a fixed order,
+// so that drab_p and drab_t do not depend on the order in which items ran.
+//
+// drab_p[h][idx] += the sum over sequences b (in order), then the key - query
+// values x folded into idx (idx 0 collects every x <= -N), then the key
+// tiles t (in order) whose slot covers x.  drab_p was zeroed by the
+// launcher; items of a sequence without slots added their share with
+// atomics.  Entries idx > N (key after query) are never reached.  One lane
+// per entry; each lane keeps up to 16 loads in flight and adds them in tile
+// order.
+__global__ void __launch_bounds__(64) drab_p_reduce_kernel(DrabReduceArgs r)
+{
+    if (*r.status) return;
+    const int h = blockIdx.y, idx = blockIdx.x * 64 + threadIdx.x;
+    if (idx > r.N) return;
+    const int dl = idx - r.N;
+    float acc = 0.f;
+    for (int b = 0; b < r.B; b++) {
+        const int64_t pb = r.pbase[b];
+        const int L = r.offsets[b + 1] - r.offsets[b];
+        if (pb < 0 || L <= 0 || -dl > L - 1) continue;
+        const int nt = (L + BWD_BN - 1) / BWD_BN;
+        const float *slot = r.dpart + pb + (int64_t)h * nt * L + (L - 1);
+        const int xlo = idx == 0 ? -(L - 1) : dl;
+        for (int x = dl; x >= xlo; x--) {
+            const int tmax = min(nt - 1, (x + L - 1) / BWD_BN);
+            for (int t0 = 0; t0 <= tmax; t0 += 16) {
+                float v[16];
+#pragma unroll
+                for (int i = 0; i < 16; i++) v[i] = t0 + i <= tmax ? slot[(int64_t)(t0 + i) * L + x] : 0.f;
+#pragma unroll
+                for (int i = 0; i < 16; i++) acc += v[i];
+            }
+        }
+    }
+    r.drab_p[h * r.p_hs + idx] += acc;
+}
+
+// drab_t[h][bucket] = the sum over the items' slots: one wave per entry, lane
+// = sequence (64 at a time, each lane adding its sequence's tiles in order),
+// then a butterfly over the lanes (a fixed tree, the same on every lane).
+// Buckets from TB_SLOTS on are never reached and get 0.
+__global__ void __launch_bounds__(64) drab_t_reduce_kernel(DrabReduceArgs r)
+{
+    if (*r.status) return;
+    const int h = blockIdx.x >> 7, bk = blockIdx.x & 127, lane = threadIdx.x;
+    float acc = 0.f;
+    if (bk < TB_SLOTS)
+        for (int b0 = 0; b0 < r.B; b0 += 64) {
+            const int b = b0 + lane;
+            float s = 0.f;
+            if (b < r.B) {
+                const int L = r.offsets[b + 1] - r.offsets[b];
+                const int nt = (L + BWD_BN - 1) / BWD_BN;
+                const float *slot = r.tpart + r.tbase[b] + (int64_t)h * nt * TB_SLOTS + bk;
+                for (int t0 = 0; t0 < nt; t0 += 16) {
+                    float v[16];
+#pragma unroll
+                    for (int i = 0; i < 16; i++) v[i] = t0 + i < nt ? slot[(int64_t)(t0 + i) * TB_SLOTS] : 0.f;
+#pragma unroll
+                    for (int i = 0; i < 16; i++) s += v[i];
+                }
+            }
+            acc += wave_sum(s);
+        }
+    if (lane == 0) r.drab_t[h * r.t_hs + bk] = acc;
+}
+
+hipError_t launch_drab_reduce(const DrabReduceArgs &r, hipStream_t st)
+{
+    if (r.drab_p)
+        hipLaunchKernelGGL(drab_p_reduce_kernel, dim3((r.N + 1 + 63) / 64, r.H), dim3(64), 0, st, r);
+    if (r.drab_t) hipLaunchKernelGGL(drab_t_reduce_kernel, dim3(r.H * 128), dim3(64), 0, st, r);
+    return hipGetLastError();
 }

@@ -76,11 +76,12 @@ __global__ void __launch_bounds__(256) ln_gate_fwd_kernel(const float *__restric
                                                           int64_t part_stride, const void *__restrict__ U, int64_t ldu,
                                                           void *__restrict__ G, int64_t ldg, float *__restrict__ stats,
                                                           float *__restrict__ o_copy, int64_t ld_oc, int T, int F,
-                                                          float eps, bool vec)
+                                                          float eps, bool vec, const int *__restrict__ status)
 {
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= T) return;
+    if (status && *status) return; // the batch failed the launcher's check: write nothing
     float x[VPL];
     float s = 0.f;
     const int c0 = lane * VPL;
@@ -149,11 +150,13 @@ __global__ void __launch_bounds__(256) ln_gate_bwd_kernel(const void *__restrict
                                                           int64_t ldu, const float *__restrict__ O, int64_t ldo,
                                                           const float *__restrict__ stats, void *__restrict__ dU,
                                                           int64_t lddu, bf16 *__restrict__ dO, float scale, int T, int F,
-                                                          bool vec, float *__restrict__ zrows, int zF)
+                                                          bool vec, float *__restrict__ zrows, int zF,
+                                                          const int *__restrict__ status)
 {
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= T) return;
+    if (status && *status) return; // the batch failed the launcher's check: write nothing
     if (zrows)
         for (int c = 4 * lane; c < zF; c += 256) *(floatx4 *)(zrows + (int64_t)row * zF + c) = floatx4{0.f, 0.f, 0.f, 0.f};
     const float mean = stats[2 * (int64_t)row], rstd = stats[2 * (int64_t)row + 1];
@@ -229,7 +232,6 @@ hipError_t launch_ln_gate_fwd(const float *O, int64_t ldo, int nparts, int64_t p
                               bool bf16io, void *G, int64_t ldg, float *stats, float *o_copy, int64_t ld_oc, int T,
                               int F, float eps, const int *status, hipStream_t st)
 {
-    (void)status;
     if (T <= 0) return hipSuccess;
     dim3 grid((T + 3) / 4);
     const int64_t es = bf16io ? 2 : 4;
@@ -239,11 +241,11 @@ hipError_t launch_ln_gate_fwd(const float *O, int64_t ldo, int nparts, int64_t p
     if (bf16io)
         VPL_SWITCH(F, hipLaunchKernelGGL((ln_gate_fwd_kernel<V, true>), grid, dim3(256), 0, st, O, ldo, nparts,
                                          part_stride, U, ldu, G, ldg, stats, o_copy, ld_oc, T, F, eps,
-                                         aligned && F == 64 * V && V % 8 == 0));
+                                         aligned && F == 64 * V && V % 8 == 0, status));
     else
         VPL_SWITCH(F, hipLaunchKernelGGL((ln_gate_fwd_kernel<V, false>), grid, dim3(256), 0, st, O, ldo, nparts,
                                          part_stride, U, ldu, G, ldg, stats, o_copy, ld_oc, T, F, eps,
-                                         aligned && F == 64 * V && V % 8 == 0));
+                                         aligned && F == 64 * V && V % 8 == 0, status));
     return hipGetLastError();
 }
 
@@ -251,7 +253,6 @@ hipError_t launch_ln_gate_bwd(const void *dG, int64_t ldg, const void *U, int64_
                               const float *stats, bool bf16io, void *dU, int64_t lddu, bf16 *dO, float scale, int T,
                               int F, float *zrows, int zF, const int *status, hipStream_t st)
 {
-    (void)status;
     if (zrows && ((((uintptr_t)zrows) & 15) != 0 || zF % 4 != 0)) return hipErrorInvalidValue;
     if (T <= 0) return hipSuccess;
     dim3 grid((T + 3) / 4);
@@ -261,9 +262,9 @@ hipError_t launch_ln_gate_bwd(const void *dG, int64_t ldg, const void *U, int64_
                          (lddu * es) % 16 == 0 && ((int64_t)T * F * 2) % 16 == 0;
     if (bf16io)
         VPL_SWITCH(F, hipLaunchKernelGGL((ln_gate_bwd_kernel<V, true>), grid, dim3(256), 0, st, dG, ldg, U, ldu, O,
-                                         ldo, stats, dU, lddu, dO, scale, T, F, aligned && F == 64 * V && V % 8 == 0, zrows, zF));
+                                         ldo, stats, dU, lddu, dO, scale, T, F, aligned && F == 64 * V && V % 8 == 0, zrows, zF, status));
     else
         VPL_SWITCH(F, hipLaunchKernelGGL((ln_gate_bwd_kernel<V, false>), grid, dim3(256), 0, st, dG, ldg, U, ldu, O,
-                                         ldo, stats, dU, lddu, dO, scale, T, F, aligned && F == 64 * V && V % 8 == 0, zrows, zF));
+                                         ldo, stats, dU, lddu, dO, scale, T, F, aligned && F == 64 * V && V % 8 == 0, zrows, zF, status));
     return hipGetLastError();
 }

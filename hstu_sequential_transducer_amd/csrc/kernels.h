@@ -17,18 +17,39 @@ constexpr int SCHED_BINS = 4096; // longest sequence: (SCHED_BINS - 1) tiles
 // item is much longer than the average per slot; *t_split is written (a
 // large value when nothing is split).
 //
-// ds_base (optional): per sequence, the element offset of its dS blocks in
-// the backward's dS buffer (H planes of P x P bf16, P = L rounded up to 128):
-// the exclusive prefix sum of the plane sizes, or -1 where that prefix plus
-// the sequence's own planes exceeds ds_cap elements (its dQ then goes
-// through fp32 atomics).  zero0[0, n0) and zero1[0, n1) (optional) are
-// zeroed on the way.
+// rank[B] (workspace): each sequence's rank among the sequences with the
+// same tile count, by index (the tie-break of the longest-first order).
+//
+// SchedBwd (the backward; ds_base NULL otherwise), per sequence b with L_b
+// tokens and n_b = ceil(L_b / tile) key tiles:
+//   ds_base: element offset of its H planes of P x P bf16 in the dS buffer
+//     (P = L rounded up to DS_PAD): the exclusive prefix sum of the plane
+//     sizes, or -1 where that prefix plus the sequence's own planes exceeds
+//     ds_cap elements (its dQ then goes through fp32 atomics);
+//   pbase: float offset of its drab_p partial sums, H * n_b slots of L_b
+//     floats, or -1 past p_cap floats (its items then add into drab_p with
+//     atomics);
+//   tbase: float offset of its drab_t partial sums, H * n_b slots of
+//     TB_SLOTS floats (always fits: the caller sizes the buffer for every
+//     tile).
+// zero0[0, n0) and zero1[0, n1) (optional) are zeroed on the way.
 constexpr int ITEM_T_SHIFT = 10;
 constexpr int DS_PAD = 128;
+constexpr int TB_SLOTS = 64; // time buckets an int64 difference can reach
+struct SchedBwd {
+    int64_t *ds_base;
+    int64_t ds_cap;
+    int64_t *pbase;
+    int64_t p_cap;
+    int64_t *tbase;
+    float *zero0;
+    int64_t n0;
+    float *zero1;
+    int64_t n1;
+};
 void launch_sched(const int32_t *offsets, const int64_t *ts, int B, int T, int tile, int H, int *status, int *n_items,
-                  int2 *items, int max_items, uint32_t *rel, int32_t *wide, int split_slots, int *t_split,
-                  int64_t *ds_base, int64_t ds_cap, float *zero0, int64_t n0, float *zero1, int64_t n1,
-                  hipStream_t st);
+                  int2 *items, int max_items, uint32_t *rel, int32_t *wide, int32_t *rank, int split_slots, int *t_split,
+                  const SchedBwd &bw, hipStream_t st);
 // Zeroes the fp32 rows [offsets[b] + tile * t_split, offsets[b + 1]) of
 // every sequence (the rows that split items accumulate into).
 hipError_t launch_zero_split_rows(const int32_t *offsets, int B, int tile, const int *t_split, float *o32, int64_t ld,
@@ -95,11 +116,32 @@ struct AttnBwdArgs {
     float *dq_acc;              // fp32 [T][H*d] accumulator of the sequences that did not fit (rows zeroed)
     bf16 *dk, *dv;
     int64_t lddk, lddv;
-    float *drab_p;              // fp32 [H][2N+1] accumulator (zeroed) or NULL
-    float *drab_t;              // fp32 [H][128] accumulator (zeroed) or NULL
+    float *drab_p;              // fp32 [H][2N+1] (zeroed; sequences without partial slots add here) or NULL
+    float *drab_t;              // NULL: no drab_t (else the partial slots below are written)
+    float *dpart;               // drab_p partial slots (see launch_sched's pbase)
+    const int64_t *pbase;
+    float *tpart;               // drab_t partial slots (see launch_sched's tbase)
+    const int64_t *tbase;
 };
 constexpr int BWD_BN = 128; // keys per workgroup
 hipError_t launch_attn_bwd_bf16(const AttnBwdArgs &a, int max_items, hipStream_t st);
+// drab_p += and drab_t = the items' partial sums, added in a fixed order
+// (sequence, key - query, key tile): the bias gradients do not depend on
+// the order in which the backward's items ran.
+struct DrabReduceArgs {
+    const int32_t *offsets;
+    int B, H, N;
+    const int *status;
+    const float *dpart;
+    const int64_t *pbase;
+    const float *tpart;
+    const int64_t *tbase;
+    float *drab_p;              // or NULL
+    int64_t p_hs;
+    float *drab_t;              // or NULL
+    int64_t t_hs;
+};
+hipError_t launch_drab_reduce(const DrabReduceArgs &r, hipStream_t st);
 
 // ---- dQ = dS K (dq.hip): one workgroup per backward item read as
 // (sequence b, query tile t of 128, head h); bf16 dQ out (d = 128).
@@ -211,8 +253,10 @@ struct MfalconArgs {
     const int *n_items;
     float *part;                // [nsplit][M][H*d] fp32 partial sums
 };
+// Validates hoff (hoff[0] = 0, non-decreasing, hoff[U] = hist_total) and
+// coff (coff[0] = 0, non-decreasing, coff[U] = M) into *status.
 hipError_t launch_mfalcon_sched(const int32_t *hoff, const int32_t *coff, int U, int M, int H, int b_m, int nsplit,
-                                int4 *items, int *n_items, int *status, int max_items, hipStream_t st);
+                                int4 *items, int *n_items, int *status, int max_items, int hist_total, hipStream_t st);
 hipError_t launch_mfalcon_attn(const MfalconArgs &a, int max_items, bool bf16io, hipStream_t st);
 hipError_t launch_mfalcon_epilogue(const float *part, int nsplit, const void *Z, int64_t ldz, const float *rab_p,
                                    int64_t rp_hs, const float *rab_t, int64_t rt_hs, bool use_t, int N, float eps,

@@ -55,7 +55,7 @@ __global__ void __launch_bounds__(1024) mfalcon_sched_kernel(const int32_t *__re
                                                               const int32_t *__restrict__ coff, int U, int M, int H,
                                                               int b_m, int nsplit, int4 *__restrict__ items,
                                                               int *__restrict__ n_items, int *__restrict__ status,
-                                                              int max_items)
+                                                              int max_items, int hist_total)
 {
     __shared__ int cnt[1024];
     __shared__ int base_s;
@@ -63,7 +63,7 @@ __global__ void __launch_bounds__(1024) mfalcon_sched_kernel(const int32_t *__re
     const int tid = threadIdx.x;
     if (tid == 0) {
         base_s = 0;
-        bad = (hoff[0] != 0 || coff[0] != 0 || coff[U] != M) ? HSTU_DEV_BAD_OFFSETS : 0;
+        bad = (hoff[0] != 0 || hoff[U] != hist_total || coff[0] != 0 || coff[U] != M) ? HSTU_DEV_BAD_OFFSETS : 0;
     }
     __syncthreads();
     for (int u = tid; u < U; u += 1024)
@@ -419,10 +419,10 @@ __global__ void __launch_bounds__(64) mfalcon_attn_f32_kernel(MfalconArgs a)
 }
 
 hipError_t launch_mfalcon_sched(const int32_t *hoff, const int32_t *coff, int U, int M, int H, int b_m, int nsplit,
-                                int4 *items, int *n_items, int *status, int max_items, hipStream_t st)
+                                int4 *items, int *n_items, int *status, int max_items, int hist_total, hipStream_t st)
 {
     hipLaunchKernelGGL(mfalcon_sched_kernel, dim3(1), dim3(1024), 0, st, hoff, coff, U, M, H, b_m, nsplit, items,
-                       n_items, status, max_items);
+                       n_items, status, max_items, hist_total);
     return hipGetLastError();
 }
 

@@ -49,11 +49,13 @@ __device__ long long block_prefix_excl64(long long v, long long *tmp)
 // One workgroup of 1024 threads.  An item is (sequence b, tile t, head h);
 // a tile t of sequence b costs t + 1 units (causal), so items are ordered by
 // t descending.  With pi = the sequences sorted by tile count descending,
-// the sequences that have a tile t form a prefix of pi, hence
+// ties by sequence index, the sequences that have a tile t form a prefix of
+// pi, hence
 //   index(b, t, h) = H * (S[t] + pos_pi(b)) + h,
 //   S[t] = #items with a larger tile index / H = sum_{t' > t} #{b : n_b > t'}.
-// Ties inside a length class are broken by an atomic counter; the results
-// of every kernel are independent of the order.
+// pos_pi(b) = #{b' : n_b' > n_b} + rank(b), rank(b) = #{b' < b : n_b' = n_b}:
+// the work list is a pure function of the offsets (the results of every
+// kernel are independent of the order anyway).
 //
 // Split items (split_slots > 0): a tile t costs about 2(t + 1) key tiles of
 // half its width, the whole launch about sum_b n_b (n_b + 1) H of them; tiles
@@ -61,24 +63,23 @@ __device__ long long block_prefix_excl64(long long v, long long *tmp)
 // concurrent workgroups, become two items of half the cost each.  Both
 // halves of a tile count as a multiplicity m(t) = 2 in the index arithmetic
 // below: index(b, t, h, part) = H * (S[t] + m(t) pos_pi(b) + part) + h.
+//
+// A batch that fails validation gets status != 0 and no items, and nothing
+// else is written (not even the buffers the caller asked to be zeroed).
 __global__ void __launch_bounds__(1024) sched_kernel(const int32_t *__restrict__ offsets, int B, int T, int tile, int H,
                                                       int *__restrict__ status, int *__restrict__ n_items,
                                                       int2 *__restrict__ items, int max_items,
-                                                      int32_t *__restrict__ wide, int split_slots,
-                                                      int *__restrict__ t_split_out, int64_t *__restrict__ ds_base,
-                                                      int64_t ds_cap, float *__restrict__ zero0, int64_t n0,
-                                                      float *__restrict__ zero1, int64_t n1)
+                                                      int32_t *__restrict__ wide, int32_t *__restrict__ rank,
+                                                      int split_slots, int *__restrict__ t_split_out, SchedBwd bw)
 {
     __shared__ int hist[SCHED_BINS];
     __shared__ long long ptmp[16];
-    // buffers the caller wants zeroed (the backward's bias gradients)
-    for (int64_t i = threadIdx.x; i < n0; i += 1024) zero0[i] = 0.f;
-    for (int64_t i = threadIdx.x; i < n1; i += 1024) zero1[i] = 0.f;
     __shared__ int fill[SCHED_BINS];
     __shared__ int S[SCHED_BINS];
     __shared__ int bad;
     __shared__ unsigned long long work;
     __shared__ int chunk_tot[1024];
+    __shared__ int rank_s[SCHED_BINS]; // ranks of the first SCHED_BINS sequences (the rest in rank[])
     const int tid = threadIdx.x;
     for (int i = tid; i < SCHED_BINS; i += 1024) {
         hist[i] = 0;
@@ -90,7 +91,6 @@ __global__ void __launch_bounds__(1024) sched_kernel(const int32_t *__restrict__
     }
     __syncthreads();
     for (int b = tid; b < B; b += 1024) {
-        wide[b] = 0;
         int L = offsets[b + 1] - offsets[b];
         if (L < 0) atomicOr(&bad, HSTU_DEV_BAD_OFFSETS);
         int n = L > 0 ? (L + tile - 1) / tile : 0;
@@ -101,21 +101,6 @@ __global__ void __launch_bounds__(1024) sched_kernel(const int32_t *__restrict__
         }
     }
     __syncthreads();
-    if (ds_base && !bad) {
-        // dS block offsets: thread tid owns sequences [tid * per, (tid + 1) * per)
-        const int per = (B + 1023) / 1024, b0 = tid * per, b1 = min(B, b0 + per);
-        long long own = 0;
-        for (int b = b0; b < b1; b++) {
-            const long long P = ((long long)(offsets[b + 1] - offsets[b]) + DS_PAD - 1) / DS_PAD * DS_PAD;
-            own += P * P * H;
-        }
-        long long run = block_prefix_excl64(own, ptmp);
-        for (int b = b0; b < b1; b++) {
-            const long long P = ((long long)(offsets[b + 1] - offsets[b]) + DS_PAD - 1) / DS_PAD * DS_PAD;
-            ds_base[b] = run + P * P * H <= ds_cap ? run : -1;
-            run += P * P * H;
-        }
-    }
     if (bad) {
         if (tid == 0) {
             *status = bad;
@@ -123,6 +108,39 @@ __global__ void __launch_bounds__(1024) sched_kernel(const int32_t *__restrict__
             if (t_split_out) *t_split_out = SCHED_BINS;
         }
         return;
+    }
+    for (int b = tid; b < B; b += 1024) wide[b] = 0;
+    // buffers the caller wants zeroed (the backward's bias gradients)
+    for (int64_t i = tid; i < bw.n0; i += 1024) bw.zero0[i] = 0.f;
+    for (int64_t i = tid; i < bw.n1; i += 1024) bw.zero1[i] = 0.f;
+    if (bw.ds_base) {
+        // Per sequence, exclusive prefix sums over the sequences before it:
+        // dS plane offsets (H planes of P x P, P = L rounded up to DS_PAD),
+        // drab_p partial slots (H * n * L floats) and drab_t partial slots
+        // (H * n * TB_SLOTS floats, n = the sequence's key tiles).  Thread tid
+        // owns sequences [tid * per, (tid + 1) * per).
+        const int per = (B + 1023) / 1024, b0 = tid * per, b1 = min(B, b0 + per);
+        long long own_ds = 0, own_p = 0, own_t = 0;
+        for (int b = b0; b < b1; b++) {
+            const long long L = offsets[b + 1] - offsets[b];
+            const long long P = (L + DS_PAD - 1) / DS_PAD * DS_PAD, n = (L + tile - 1) / tile;
+            own_ds += P * P * H;
+            own_p += n * L * H;
+            own_t += n * TB_SLOTS * H;
+        }
+        long long run_ds = block_prefix_excl64(own_ds, ptmp);
+        long long run_p = block_prefix_excl64(own_p, ptmp);
+        long long run_t = block_prefix_excl64(own_t, ptmp);
+        for (int b = b0; b < b1; b++) {
+            const long long L = offsets[b + 1] - offsets[b];
+            const long long P = (L + DS_PAD - 1) / DS_PAD * DS_PAD, n = (L + tile - 1) / tile;
+            bw.ds_base[b] = run_ds + P * P * H <= bw.ds_cap ? run_ds : -1;
+            bw.pbase[b] = run_p + n * L * H <= bw.p_cap ? run_p : -1;
+            bw.tbase[b] = run_t;
+            run_ds += P * P * H;
+            run_p += n * L * H;
+            run_t += n * TB_SLOTS * H;
+        }
     }
     int t_split = SCHED_BINS; // no split
     if (split_slots > 0) {
@@ -164,20 +182,45 @@ __global__ void __launch_bounds__(1024) sched_kernel(const int32_t *__restrict__
         }
     }
     __syncthreads();
-    // pos_pi(b) = #{b' : n_b' > n_b} + rank among equal n; hist[] becomes the
-    // per-class fill counter.
+    // rank(b) among the sequences of its length class, by index: wave 0
+    // walks the sequences in order, 64 at a time; inside a group of 64 the
+    // lanes of one class are ranked by a ballot, then the class counter
+    // (hist[], reused) moves on.
     for (int i = tid; i < SCHED_BINS; i += 1024) hist[i] = 0;
     __syncthreads();
-    // one wave per sequence: lane 0 takes the sequence's rank in its length
-    // class, the lanes write its n * H items
     const int lane = tid & 63, wv = tid >> 6;
+    if (wv == 0) {
+        const unsigned long long below = (1ull << lane) - 1ull;
+        for (int b0 = 0; b0 < B; b0 += 64) {
+            const int b = b0 + lane;
+            int n = -1;
+            if (b < B) {
+                const int L = offsets[b + 1] - offsets[b];
+                n = L > 0 ? (L + tile - 1) / tile : -1;
+            }
+            unsigned long long todo = __ballot(n >= 0);
+            while (todo) {
+                const int leader = __ffsll((long long)todo) - 1;
+                const int v = __shfl(n, leader, 64);
+                const unsigned long long same = __ballot(n == v) & todo;
+                const int base = hist[v];
+                if (n == v) {
+                    const int rk = base + __popcll(same & below);
+                    if (b < SCHED_BINS) rank_s[b] = rk;
+                    else rank[b] = rk;
+                }
+                if (lane == leader) hist[v] = base + __popcll(same);
+                todo &= ~same;
+            }
+        }
+    }
+    __syncthreads();
+    // one wave per sequence: the lanes write its n * H items
     for (int b = wv; b < B; b += 16) {
         const int L = offsets[b + 1] - offsets[b];
         const int n = L > 0 ? (L + tile - 1) / tile : 0;
         if (n == 0) continue;
-        int pos = 0;
-        if (lane == 0) pos = fill[n] + atomicAdd(&hist[n], 1);
-        pos = __shfl(pos, 0, 64);
+        const int pos = fill[n] + (b < SCHED_BINS ? rank_s[b] : rank[b]);
         for (int k = lane; k < n * H; k += 64) {
             const int t = k / H, h = k - t * H;
             const int m = mult(t);
@@ -193,7 +236,8 @@ __global__ void __launch_bounds__(1024) sched_kernel(const int32_t *__restrict__
 // 2^31 as a 32-bit value.  Differences of two such values are exact as long
 // as every time of the sequence lies within 2^31 - 1 of its first time (then
 // |t_i - t_j| + 1 < 2^32); otherwise wide[b] is set and the kernels use exact
-// 64-bit arithmetic for that sequence.  wide[] was zeroed by sched_kernel.
+// 64-bit arithmetic for that sequence.  wide[] was zeroed by sched_kernel
+// (which also validated the offsets: nothing runs on a batch that failed).
 __global__ void __launch_bounds__(256) reltime_kernel(const int32_t *__restrict__ offsets, const int64_t *__restrict__ ts,
                                                        uint32_t *__restrict__ rel, int32_t *__restrict__ wide, int B,
                                                        int T, const int *__restrict__ status)
@@ -280,13 +324,14 @@ hipError_t launch_zero_dqa_rows(const int32_t *offsets, int B, const int64_t *ds
 }
 
 void launch_sched(const int32_t *offsets, const int64_t *ts, int B, int T, int tile, int H, int *status, int *n_items,
-                  int2 *items, int max_items, uint32_t *rel, int32_t *wide, int split_slots, int *t_split,
-                  int64_t *ds_base, int64_t ds_cap, float *zero0, int64_t n0, float *zero1, int64_t n1,
-                  hipStream_t st)
+                  int2 *items, int max_items, uint32_t *rel, int32_t *wide, int32_t *rank, int split_slots, int *t_split,
+                  const SchedBwd &bw, hipStream_t st)
 {
+    SchedBwd b2 = bw;
+    if (!b2.zero0) b2.n0 = 0;
+    if (!b2.zero1) b2.n1 = 0;
     hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(1024), 0, st, offsets, B, T, tile, H, status, n_items, items,
-                       max_items, wide, split_slots, t_split, ds_base, ds_cap, zero0, zero0 ? n0 : 0, zero1,
-                       zero1 ? n1 : 0);
+                       max_items, wide, rank, split_slots, t_split, b2);
     if (ts && T > 0)
         hipLaunchKernelGGL(reltime_kernel, dim3((T + 255) / 256), dim3(256), 0, st, offsets, ts, rel, wide, B, T, status);
 }

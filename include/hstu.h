@@ -33,7 +33,10 @@
  *   - Matrices are row-major with a token stride `ld` in elements, so Q/K/V/U
  *     may be views into one f1 output buffer [T][4*H*d] (ld = 4*H*d).  A
  *     stride must be at least the row width and below 2^24 elements
- *     (HSTU_ERR_UNSUPPORTED otherwise).
+ *     (HSTU_ERR_UNSUPPORTED otherwise).  bf16 views are moved with 16-byte
+ *     accesses: their base must be 16-byte aligned and ld a multiple of 8
+ *     (HSTU_ERR_ARG otherwise); so must fp32 buffers the attention writes
+ *     with 16-byte stores (o_save).
  *     Per-head tensors are [T][H][d] inside a row: head h at column h*d.
  *   - Everything is enqueued on `stream` (a hipStream_t, NULL = default
  *     stream); nothing synchronises the host and nothing is copied device to
@@ -42,9 +45,12 @@
  *     describes the problem.  Launch failures return HSTU_ERR_DEVICE.
  *     Device-side data checks (offsets[0] == 0, non-decreasing offsets,
  *     offsets[B] == T) write a status word into the workspace; with the
- *     environment variable HSTU_DEBUG=1 each call synchronises the stream and
- *     reports a failed check as HSTU_ERR_ARG.  A batch that fails the check
- *     computes nothing (outputs are left unwritten).
+ *     environment variable HSTU_DEBUG=1 (read at every call) each call
+ *     synchronises the stream and reports a failed check as HSTU_ERR_ARG.
+ *     hstu_attn_fwd and hstu_attn_bwd compute nothing on a batch that fails
+ *     the check: their outputs are left unwritten.  The layer entry points
+ *     and mfalcon_score run their linear maps before the check and leave
+ *     their outputs unspecified on such a batch.
  *   - Entry points are thread-safe for distinct workspaces; calls that share
  *     a workspace must be ordered on one stream.
  */
@@ -153,6 +159,12 @@ hstu_status hstu_attn_fwd(const hstu_jagged *j, const hstu_dims *dims, const hst
  *   (when u is given); fp32 drab_p [H][2*N_max+1] and drab_t [H][128] (each
  *   may be NULL to skip; contiguous, hstride as in `bias`, which must not be
  *   0 when the gradient is requested).
+ *   Every output is the same bit for bit from run to run when every sequence
+ *   is at most N_max long: the bias gradients are per-work-item partial
+ *   sums added in a fixed order (sequence, key - query, key tile).  A batch
+ *   with sequences longer than N_max may exceed the workspace's partial-sum
+ *   and dS buffers (sized from N_max); such sequences fall back to fp32
+ *   atomics for drab_p and dQ, whose rounding then depends on the order.
  */
 hstu_status hstu_attn_bwd(const hstu_jagged *j, const hstu_dims *dims, const hstu_bias *bias, hstu_cmat q,
                           hstu_cmat k, hstu_cmat v, hstu_cmat u, const float *o_save, const float *ln_stats,
@@ -201,6 +213,9 @@ hstu_status hstu_layer_bwd(const hstu_jagged *j, const hstu_dims *dims, int32_t 
  * depend on b_m.  Output: the candidates' final hidden states, fp32 [M][D].
  *   layers, k_cache, v_cache: host arrays of n_layers entries (device data).
  *   cand_offsets: device [U+1]; cand_ts: device [U] (NULL iff hist->ts NULL).
+ *   Device-side checks: hist->offsets[0] = 0, non-decreasing,
+ *   hist->offsets[U] = hist->total; cand_offsets[0] = 0, non-decreasing,
+ *   cand_offsets[U] = total_cand.
  */
 hstu_status mfalcon_score(const hstu_jagged *hist, const hstu_dims *dims, int32_t d_model, int32_t n_layers,
                           const hstu_layer *layers, const hstu_cmat *k_cache, const hstu_cmat *v_cache,

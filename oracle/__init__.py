@@ -208,14 +208,31 @@ def layer_bwd(offsets, ts, x, layer, dy, heads: int, d: int, n_max: int, phi1: i
     return res
 
 
+def layer_kv(x, layer, heads: int, d: int, phi1: int = 0):
+    """K and V of one layer for the tokens x [T][D] (the K and V column blocks
+    of phi1(x W1^T + b1)).  Returns kv [2][T][H][d]."""
+    lib = _load()
+    X = _d(x)
+    T, D = X.shape
+    kv = np.zeros((2, T, heads, d))
+    lib.oracle_layer_kv(ctypes.c_int64(T), ctypes.c_int(heads), ctypes.c_int(d), ctypes.c_int(D),
+                        _p(_d(layer.w1)), _p(_d(layer.b1)), ctypes.c_int(phi1), _p(X), _p(kv))
+    return kv
+
+
 def history_cache(offsets, ts, x, layers, heads: int, d: int, n_max: int, phi1: int = 0, eps: float = 1e-5):
     """Run the layer stack over the user histories and keep every layer's K, V
-    (the cacheable computations of M-FALCON).  Returns kv [L][2][T][H][d]."""
+    (the cacheable computations of M-FALCON).  The last layer's output is not
+    part of the cache, so that layer only computes its K and V.  Returns kv
+    [L][2][T][H][d]."""
     kvs = []
     h = x
-    for layer in layers:
-        h, K, V = layer_fwd(offsets, ts, h, layer, heads, d, n_max, phi1, eps, return_kv=True)
-        kvs.append(np.stack([K, V]))
+    for i, layer in enumerate(layers):
+        if i == len(layers) - 1:
+            kvs.append(layer_kv(h, layer, heads, d, phi1))
+        else:
+            h, K, V = layer_fwd(offsets, ts, h, layer, heads, d, n_max, phi1, eps, return_kv=True)
+            kvs.append(np.stack([K, V]))
     return np.stack(kvs)
 
 
@@ -242,3 +259,27 @@ def mfalcon(hist_offsets, hist_ts, cand_offsets, cand_ts, layers, kv, x_cand, he
                        _p(W2), _p(b2), _p(rp), _p(rt), ctypes.c_int(phi1), ctypes.c_double(eps), _p(kvd), _p(Xc),
                        _p(y))
     return y
+
+
+def layer_append(hist_offsets, hist_ts, add_offsets, add_ts, layer, kv_cache, x_new, heads: int, d: int, n_max: int,
+                 phi1: int = 0, eps: float = 1e-5):
+    """One layer over newly appended actions against a cached history
+    (kv_cache [2][T_hist][H][d], this layer's K, V of the history): new
+    token i of user u sits at position n_u + i and attends to the history
+    and to the new tokens up to itself.  Returns (y_new [T_new][D], the merged
+    cache [2][T_hist + T_new][H][d], user u's rows starting at
+    hist_offsets[u] + add_offsets[u])."""
+    lib = _load()
+    hoff, aoff = _i32(hist_offsets), _i32(add_offsets)
+    U = len(hoff) - 1
+    X = _d(x_new)
+    Tn, D = X.shape
+    Th = int(hoff[-1])
+    y = np.zeros_like(X)
+    kv_out = np.zeros((2, Th + Tn, heads, d))
+    lib.oracle_layer_append(ctypes.c_int(U), _p(hoff), _p(_i64(hist_ts)), _p(aoff), _p(_i64(add_ts)),
+                            ctypes.c_int(heads), ctypes.c_int(d), ctypes.c_int64(n_max), ctypes.c_int(D),
+                            _p(_d(layer.w1)), _p(_d(layer.b1)), _p(_d(layer.w2)), _p(_d(layer.b2)),
+                            _p(_d(layer.rab_p)), _p(_d(layer.rab_t)), ctypes.c_int(phi1), ctypes.c_double(eps),
+                            _p(_d(kv_cache)), _p(X), _p(y), _p(kv_out))
+    return y, kv_out

@@ -387,6 +387,32 @@ void oracle_layer_fwd(int B, const int32_t *off, const int64_t *ts, int H, int d
     free(G);
 }
 
+/*
+ * The part of one layer that M-FALCON caches for a history ([GR review] §3,
+ * M-FALCON: the history's linear computations are cacheable): the layer's
+ * K and V, i.e. the K and V column blocks of phi1(X W1^T + b1) (Eq. 1), for
+ * every token r of X [T][D].  kv_out [2][T][H][d].  (The same values
+ * oracle_layer_fwd returns in kv_out, without the attention and f2 that the
+ * cache does not need.)
+ */
+void oracle_layer_kv(int64_t T, int H, int d, int D, const double *W1, const double *b1, int phi1,
+                     const double *X, double *kv_out)
+{
+    int HD = H * d;
+#pragma omp parallel for
+    for (int64_t r = 0; r < T; r++)
+        for (int c = 0; c < HD; c++) {
+            int nk = 3 * HD + c, nv = HD + c; /* K and V column blocks of U | V | Q | K */
+            double zk = b1 ? b1[nk] : 0.0, zv = b1 ? b1[nv] : 0.0;
+            for (int e = 0; e < D; e++) {
+                zk += X[r * D + e] * W1[(int64_t)nk * D + e];
+                zv += X[r * D + e] * W1[(int64_t)nv * D + e];
+            }
+            kv_out[r * HD + c] = act(phi1, zk);
+            kv_out[(size_t)T * HD + r * HD + c] = act(phi1, zv);
+        }
+}
+
 /* d phi1 / dz: SiLU' as above; ReLU' read as 1 for z > 0, else 0. */
 static double act_grad(int phi1, double z) { return phi1 == 1 ? (z > 0.0 ? 1.0 : 0.0) : silu_grad(z); }
 
@@ -589,6 +615,99 @@ void oracle_mfalcon(int n_users, const int32_t *hist_off, const int64_t *hist_ts
         free(o);
         free(g);
     }
+}
+
+/*
+ * Appending new actions to a user's cached history, one layer ([GR review]
+ * §3: the history's linear and attention computations are cacheable, and
+ * the architecture tree's streaming setting adds actions as they arrive).
+ * User u has a cached history of n_u tokens (this layer's K, V in kv_cache
+ * [2][T_hist][H][d], rows hist_off[u]..) and a_u new tokens x_new (rows
+ * add_off[u]..).  New token i of user u is the token at position n_u + i
+ * of the user's sequence, with time add_ts[r]:
+ *   a = phi1(x W1^T + b1) = u | v | q | k of the new token (Eq. 1)
+ *   o = (1/N) [ sum_{j < n_u} SiLU(q.K_j + rab_p[clip(j - (n_u + i))] + rab_t[b(t - t_j)]) V_j
+ *             + sum_{i' <= i} SiLU(q.k_i' + rab_p[clip(i' - i)] + rab_t[b(t - t_i')]) v_i' ]   (Eq. 2)
+ *   y = x + (Norm(o) (.) u) W2^T + b2                                          (Eq. 3 + residual)
+ * i.e. exactly rows n_u.. of the layer over the user's whole sequence
+ * [history; new], whose causal mask lets a new token see the history and
+ * the new tokens up to itself.  y_new [T_new][D]; kv_out [2][T_hist + T_new]
+ * [H][d] (optional): the merged cache, user u's history rows then its new
+ * rows, starting at row hist_off[u] + add_off[u].
+ */
+void oracle_layer_append(int U, const int32_t *hist_off, const int64_t *hist_ts, const int32_t *add_off,
+                         const int64_t *add_ts, int H, int d, int64_t N, int D, const double *W1, const double *b1,
+                         const double *W2, const double *b2, const double *rab_p, const double *rab_t, int phi1,
+                         double eps, const double *kv_cache, const double *x_new, double *y_new, double *kv_out)
+{
+    int HD = H * d, Z4 = 4 * HD;
+    int64_t Th = hist_off[U], Tn = add_off[U];
+    const double *Kc = kv_cache, *Vc = kv_cache + Th * HD;
+    double *A = (double *)malloc(sizeof(double) * (size_t)(Tn > 0 ? Tn : 1) * Z4);
+    int have_t = hist_ts != NULL && add_ts != NULL;
+    /* f1 + phi1 of every new token */
+#pragma omp parallel for
+    for (int64_t r = 0; r < Tn; r++)
+        for (int n = 0; n < Z4; n++) {
+            double z = b1 ? b1[n] : 0.0;
+            for (int e = 0; e < D; e++) z += x_new[r * D + e] * W1[(int64_t)n * D + e];
+            A[r * Z4 + n] = act(phi1, z);
+        }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < Tn; r++) {
+        int u = seq_of(U, add_off, r);
+        int64_t ho = hist_off[u], nu = hist_off[u + 1] - hist_off[u], ao = add_off[u], i = r - ao;
+        int64_t pos = nu + i;
+        const double *uu = A + r * Z4, *qq = A + r * Z4 + 2 * HD;
+        double *o = (double *)malloc(sizeof(double) * HD);
+        double *g = (double *)malloc(sizeof(double) * HD);
+        for (int h = 0; h < H; h++) {
+            double *acc = o + h * d;
+            for (int e = 0; e < d; e++) acc[e] = 0.0;
+            for (int64_t j = 0; j < nu; j++) { /* the cached history */
+                int64_t rk = ho + j;
+                double s = pair_logit(qq + h * d, Kc + (rk * H + h) * d, d, pos, j, N, h, rab_p, rab_t,
+                                      have_t ? add_ts[r] : 0, have_t ? hist_ts[rk] : 0, have_t);
+                double p = silu(s);
+                for (int e = 0; e < d; e++) acc[e] += p * Vc[(rk * H + h) * d + e];
+            }
+            for (int64_t i2 = 0; i2 <= i; i2++) { /* the new tokens up to this one */
+                int64_t rk = ao + i2;
+                const double *kk = A + rk * Z4 + 3 * HD, *vv = A + rk * Z4 + HD;
+                double s = pair_logit(qq + h * d, kk + h * d, d, pos, nu + i2, N, h, rab_p, rab_t,
+                                      have_t ? add_ts[r] : 0, have_t ? add_ts[rk] : 0, have_t);
+                double p = silu(s);
+                for (int e = 0; e < d; e++) acc[e] += p * vv[h * d + e];
+            }
+            for (int e = 0; e < d; e++) acc[e] /= (double)N;
+        }
+        oracle_ln_gate(1, HD, o, uu, eps, g, NULL);
+        for (int n = 0; n < D; n++) {
+            double yy = b2 ? b2[n] : 0.0;
+            for (int e = 0; e < HD; e++) yy += g[e] * W2[(int64_t)n * HD + e];
+            y_new[r * D + n] = x_new[r * D + n] + yy;
+        }
+        free(o);
+        free(g);
+    }
+    if (kv_out) {
+        int64_t Tm = Th + Tn;
+        for (int u = 0; u < U; u++) {
+            int64_t ho = hist_off[u], nu = hist_off[u + 1] - ho, ao = add_off[u], au = add_off[u + 1] - ao;
+            int64_t mo = ho + ao; /* merged offset of user u */
+            for (int64_t j = 0; j < nu; j++)
+                for (int c = 0; c < HD; c++) {
+                    kv_out[(mo + j) * HD + c] = Kc[(ho + j) * HD + c];
+                    kv_out[Tm * HD + (mo + j) * HD + c] = Vc[(ho + j) * HD + c];
+                }
+            for (int64_t i = 0; i < au; i++)
+                for (int c = 0; c < HD; c++) {
+                    kv_out[(mo + nu + i) * HD + c] = A[(ao + i) * Z4 + 3 * HD + c];
+                    kv_out[Tm * HD + (mo + nu + i) * HD + c] = A[(ao + i) * Z4 + HD + c];
+                }
+        }
+    }
+    free(A);
 }
 
 int oracle_abi_version(void) { return 1; }

@@ -43,13 +43,15 @@ def _jag(B=2, T=10, n=8, off=1, ts=None):
     return bd.Jagged(B, T, n, off, ts)
 
 
-def _call_fwd(jag, dims, ws=None, ws_bytes=0, q=8, ldq=512, out=8):
+def _call_fwd(jag, dims, ws=None, ws_bytes=0, q=256, ldq=512, out=1024, k=512, ldk=512, o_save=None):
+    """hstu_attn_fwd with made-up device addresses (never dereferenced: every
+    case below fails validation before anything is enqueued)."""
     lib = hs.load_library()
     bias = bd.Bias(None, 0, None, 0)
     m = lambda p, ld: bd.CMat(p, ld)
     return lib.hstu_attn_fwd(ctypes.byref(jag) if jag is not None else None, ctypes.byref(dims), ctypes.byref(bias),
-                             m(q, ldq), m(8, 512), m(8, 512), m(None, 0), bd.Mat(out, 512), None, None, ws, ws_bytes,
-                             None)
+                             m(q, ldq), m(k, ldk), m(768, 512), m(None, 0), bd.Mat(out, 512), o_save, None, ws,
+                             ws_bytes, None)
 
 
 def test_validation_errors_are_reported():
@@ -69,6 +71,39 @@ def test_validation_errors_are_reported():
     assert _call_fwd(_jag(), _dims(), ws=256 * 3 + 4, ws_bytes=1 << 30) == bd.HSTU_ERR_WORKSPACE
     assert _call_fwd(_jag(), _dims(), ws=256 * 4, ws_bytes=16) == bd.HSTU_ERR_WORKSPACE
     assert "too small" in hs.last_error()
+
+
+def test_bf16_views_must_be_16_byte_aligned():
+    """bf16 Q/K/V/U/outputs are moved with 16-byte accesses: a base that is
+    not 16-byte aligned, or a token stride that is not a multiple of 8
+    elements, is rejected before any launch; so is an fp32 o_save that is not
+    16-byte aligned."""
+    assert _call_fwd(_jag(), _dims(), q=256 + 4) == bd.HSTU_ERR_ARG
+    assert "16-byte" in hs.last_error() and "q" in hs.last_error()
+    assert _call_fwd(_jag(), _dims(), k=512 + 8) == bd.HSTU_ERR_ARG
+    assert _call_fwd(_jag(), _dims(), ldk=516) == bd.HSTU_ERR_ARG
+    assert "multiple of 8" in hs.last_error()
+    assert _call_fwd(_jag(), _dims(), out=1024 + 2) == bd.HSTU_ERR_ARG
+    assert _call_fwd(_jag(), _dims(), o_save=2048 + 4) == bd.HSTU_ERR_ARG
+    assert "o_save" in hs.last_error()
+    # fp32 views keep 4-byte alignment (the fp32 kernel reads them one by one)
+    assert _call_fwd(_jag(), _dims(dtype=bd.HSTU_F32, d=32), q=256 + 4, ldq=128, ldk=128, k=512) == bd.HSTU_ERR_WORKSPACE
+
+
+def _call_bwd(dq=1280, lddq=512):
+    lib = hs.load_library()
+    bias = bd.Bias(None, 0, None, 0)
+    c = lambda p: bd.CMat(p, 512)
+    return lib.hstu_attn_bwd(ctypes.byref(_jag()), ctypes.byref(_dims()), ctypes.byref(bias), c(256), c(512), c(768),
+                             c(None), None, None, c(1024), bd.Mat(dq, lddq), bd.Mat(1536, 512), bd.Mat(1792, 512),
+                             bd.Mat(None, 0), None, None, None, 0, None)
+
+
+def test_bwd_views_checked_before_launch():
+    assert _call_bwd(dq=1280 + 8) == bd.HSTU_ERR_ARG
+    assert "dq" in hs.last_error()
+    assert _call_bwd(lddq=520 + 4) == bd.HSTU_ERR_ARG
+    assert _call_bwd() == bd.HSTU_ERR_WORKSPACE
 
 
 def test_workspace_size_grows_with_tokens():

@@ -5,7 +5,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import BF16_TOL, bf16_bound, host, rel_err, sample_rows, t_act, t_f32, t_i32, t_i64
+from gpu_util import BF16_TOL, bf16_bound, host, rel_err, round_bf16, t_act, t_f32, t_i32, t_i64
 
 pytestmark = pytest.mark.gpu
 
@@ -38,12 +38,40 @@ def with_grad(seed, lengths, n_max=None, act_std=None):
     return w
 
 
-def check_all(g, ref, names=("dq", "dk", "dv", "du", "drab_p", "drab_t")):
+def check_du(got, ref, dg):
+    """dU = xhat (.) dG, where xhat = Norm(O) carries the forward's error
+    (bf16 P in the AV product: about 1 % of its RMS at the worst element).
+    In max|err|/RMS a product's error is that of xhat scaled by the other
+    factor's local size, so it is checked on the quantity the kernel
+    computes: xhat = dU / dG element by element (dG != 0), within 2e-2 of
+    RMS(xhat) plus what rounding dU to bf16 alone does to that ratio.  dU
+    itself must then sit within the bound that implies:
+    (2e-2 RMS(xhat) max|dG| + max|round(dU) - dU|) / RMS(dU)."""
+    dg = np.asarray(dg, np.float64)
+    nz = dg != 0
+    xh_ref, xh_got = ref[nz] / dg[nz], got[nz] / dg[nz]
+    e_x = rel_err(xh_got, xh_ref)
+    b_x = BF16_TOL + rel_err(round_bf16(ref)[nz] / dg[nz], xh_ref)
+    rms_x = np.sqrt(np.mean(xh_ref ** 2))
+    rms_u = np.sqrt(np.mean(ref ** 2))
+    b_u = (BF16_TOL * rms_x * np.abs(dg).max() + np.abs(round_bf16(ref) - ref).max()) / rms_u
+    e_u = rel_err(got, ref)
+    print("du: xhat err", e_x, "bound", b_x, "| du err", e_u, "bound", b_u, "(2e-2 + RNE would be",
+          bf16_bound(ref), ")")
+    assert e_x <= b_x, ("du/dg", e_x, b_x)
+    assert e_u <= b_u, ("du", e_u, b_u)
+    return e_u
+
+
+def check_all(g, ref, names=("dq", "dk", "dv", "du", "drab_p", "drab_t"), dg=None):
     errs = {}
     for n in names:
         if ref.get(n) is None or g.get(n) is None:
             continue
         got = host(g[n]).reshape(ref[n].shape)
+        if n == "du":
+            errs[n] = check_du(got, ref[n], dg)
+            continue
         e = rel_err(got, ref[n])
         errs[n] = e
         bound = BF16_TOL if n.startswith("drab") else bf16_bound(ref[n])
@@ -58,7 +86,7 @@ def test_bwd_small_ragged(epilogue):
     g = gpu_fwd_bwd(w, epilogue=epilogue)
     ref = oracle.attn_bwd(w.offsets, w.ts, w.q, w.k, w.v, w.rab_p, w.rab_t, w.n_max, w.u if epilogue else None,
                           w.ln_eps, w.dg)
-    check_all(g, ref)
+    check_all(g, ref, dg=w.dg)
 
 
 def test_bwd_without_bias_terms_and_wide_times():
@@ -68,11 +96,11 @@ def test_bwd_without_bias_terms_and_wide_times():
         ref = oracle.attn_bwd(w.offsets, w.ts if use_t else None, w.q, w.k, w.v, w.rab_p if use_p else None,
                               w.rab_t if use_t else None, w.n_max, w.u, w.ln_eps, w.dg)
         names = ("dq", "dk", "dv", "du") + (("drab_p",) if use_p else ()) + (("drab_t",) if use_t else ())
-        check_all(g, ref, names)
+        check_all(g, ref, names, dg=w.dg)
     w.ts = (w.ts - synth.EPOCH) * (1 << 24) + synth.EPOCH
     g = gpu_fwd_bwd(w)
     ref = oracle.attn_bwd(w.offsets, w.ts, w.q, w.k, w.v, w.rab_p, w.rab_t, w.n_max, w.u, w.ln_eps, w.dg)
-    check_all(g, ref)
+    check_all(g, ref, dg=w.dg)
 
 
 @pytest.mark.parametrize("lengths", [[300, 41], [41, 300]])
@@ -83,14 +111,14 @@ def test_bwd_clip_beyond_n_max(lengths):
     w = with_grad(23, lengths, n_max=100, act_std=0.5)
     g = gpu_fwd_bwd(w)
     ref = oracle.attn_bwd(w.offsets, w.ts, w.q, w.k, w.v, w.rab_p, w.rab_t, w.n_max, w.u, w.ln_eps, w.dg)
-    check_all(g, ref)
+    check_all(g, ref, dg=w.dg)
 
 
 def test_bwd_normalising_regime():
     w = with_grad(24, [200, 90], act_std=1.0)
     g = gpu_fwd_bwd(w, eps=1e-12)
     ref = oracle.attn_bwd(w.offsets, w.ts, w.q, w.k, w.v, w.rab_p, w.rab_t, w.n_max, w.u, 1e-12, w.dg)
-    check_all(g, ref)
+    check_all(g, ref, dg=w.dg)
 
 
 def test_bwd_layer_train_shapes_cap_lengths():
@@ -100,27 +128,23 @@ def test_bwd_layer_train_shapes_cap_lengths():
                                  with_grad=True)
     g = gpu_fwd_bwd(w)
     ref = oracle.attn_bwd(w.offsets, w.ts, w.q, w.k, w.v, w.rab_p, w.rab_t, w.n_max, w.u, w.ln_eps, w.dg)
-    check_all(g, ref)
+    check_all(g, ref, dg=w.dg)
 
 
-def test_bwd_full_size_8k_sampled_and_invariants():
-    """B=8 SL lengths at N_max=8192: the full launch.  dq and du on sampled
-    rows against the oracle; identities that hold at any size for the rest:
-    sum(drab_p[h]) = sum(drab_t[h]) = sum of dS, and
-    sum_i dq_i.q_i = sum_j dk_j.k_j (= sum dS_ij q_i.k_j) per head."""
+@pytest.mark.timeout(1200)
+def test_bwd_full_size_8k_every_element():
+    """B=8 SL lengths at N_max=8192: the full launch that the benchmark times.
+    Every element of dq, dk, dv, du, drab_p and drab_t against one full run
+    of the oracle's backward (about 530 GFLOP of fp64 on the host), plus
+    identities that hold at any size: sum(drab_p[h]) = sum(drab_t[h]) = sum
+    of dS, and sum_i dq_i.q_i = sum_j dk_j.k_j (= sum dS_ij q_i.k_j) per
+    head."""
     w = synth.attn_8k(with_grad=True)
+    print("case bwd 8k T", w.total, flush=True)
     g = gpu_fwd_bwd(w)
-    rows = sample_rows(w.offsets, 24, np.random.default_rng(3))
-    dq_ref = oracle.attn_bwd_dq_rows(w.offsets, w.ts, w.q, w.k, w.v, w.rab_p, w.rab_t, w.n_max, w.u, w.ln_eps, w.dg,
-                                     rows)
-    dq = host(g["dq"])[rows]
-    e = rel_err(dq, dq_ref)
-    assert e <= bf16_bound(dq_ref), e
-    O = oracle.attn_fwd(w.offsets, w.ts, w.q, w.k, w.v, w.rab_p, w.rab_t, w.n_max, rows=rows)
-    xh, _ = oracle.ln_gate(O, np.ones_like(O), w.ln_eps)
-    du_ref = xh * w.dg[rows]
-    e2 = rel_err(host(g["du"])[rows], du_ref)
-    assert e2 <= bf16_bound(du_ref), e2
+    ref = oracle.attn_bwd(w.offsets, w.ts, w.q, w.k, w.v, w.rab_p, w.rab_t, w.n_max, w.u, w.ln_eps, w.dg)
+    errs = check_all(g, ref, dg=w.dg)
+    print("8k bwd errors", errs, flush=True)
     drp, drt = host(g["drab_p"]), host(g["drab_t"])
     q, k = w.q.astype(np.float64), w.k.astype(np.float64)
     dqa, dka = host(g["dq"]).reshape(q.shape), host(g["dk"]).reshape(k.shape)
@@ -132,4 +156,34 @@ def test_bwd_full_size_8k_sampled_and_invariants():
         y = (dka[:, h] * k[:, h]).sum()
         sc = np.abs(dqa[:, h] * q[:, h]).sum()
         assert abs(x - y) <= 2e-2 * sc, (h, x, y)
-    print("8k bwd dq err", e, "du err", e2)
+
+
+def test_bwd_deterministic_bitwise():
+    """Two backward calls on the same inputs give bit-identical dq, dk, dv,
+    du, drab_p and drab_t: the bias gradients are summed in a fixed order
+    (per-item partial sums added by sequence, key - query and key tile), not
+    with atomics.  B=16 sequences of 777 tokens plus ragged ones."""
+    L = np.concatenate([np.full(12, 777), [1, 130, 2000, 64]])
+    w = synth.attention_workload("bwd-det", 25, L, heads=4, d=128, n_max=4096, epilogue=True, with_grad=True)
+    g1 = gpu_fwd_bwd(w)
+    g2 = gpu_fwd_bwd(w)
+    for n in ("dq", "dk", "dv", "du", "drab_p", "drab_t"):
+        assert torch.equal(g1[n], g2[n]), n
+
+
+def test_bwd_neighbours_nan():
+    """NaN in the other sequences' Q, K, V, U and upstream gradient: the
+    gradients of sequence 1 are bit-identical to a clean run (drab tables
+    then differ, as they sum over every sequence, so they are not
+    compared)."""
+    L = [260, 190, 70]
+    w = with_grad(26, L, act_std=0.5)
+    base = gpu_fwd_bwd(w)
+    w2 = with_grad(26, L, act_std=0.5)
+    for a in (w2.q, w2.k, w2.v, w2.u, w2.dg):
+        a[:260] = np.nan
+        a[450:] = np.nan
+    g = gpu_fwd_bwd(w2)
+    for n in ("dq", "dk", "dv", "du"):
+        assert torch.equal(g[n][260:450], base[n][260:450]), n
+        assert not torch.isnan(g[n][260:450].float()).any(), n

@@ -50,6 +50,13 @@ MUTANTS = [
     ("layer-bwd-dw2-ungated", "s += dY[r * D + n] * G[r * HD + c];", "s += dY[r * D + n] * Um[r * HD + c];"),
     ("layer-bwd-dg-transposed-w2", "s += dY[r * D + n] * W2[(int64_t)n * HD + c];", "s += dY[r * D + n] * W2[(int64_t)c * D + n];"),
     ("layer-bwd-dq-dk-swapped", "dA[r * Z4 + 2 * HD + c] = dq[r * HD + c];", "dA[r * Z4 + 2 * HD + c] = dk[r * HD + c];"),
+    ("append-position", "int64_t pos = nu + i;", "int64_t pos = nu + i + 1;"),
+    ("append-strict-causal", "for (int64_t i2 = 0; i2 <= i; i2++)", "for (int64_t i2 = 0; i2 < i; i2++)"),
+    ("append-no-history", "for (int64_t j = 0; j < nu; j++) { /* the cached history */",
+     "for (int64_t j = 0; j < nu - 1; j++) { /* the cached history */"),
+    ("append-merged-offset", "int64_t mo = ho + ao;", "int64_t mo = ho;"),
+    ("append-new-time", "have_t ? add_ts[r] : 0, have_t ? add_ts[rk] : 0, have_t);",
+     "have_t ? add_ts[r] : 0, have_t ? add_ts[r] : 0, have_t);"),
 ]
 
 PINS = [
@@ -68,6 +75,7 @@ PINS = [
     (pins.test_mfalcon_equals_last_row_of_full_forward, {}),
     (pins.test_layer_bwd_residual_and_bias_identities, {}),
     (pins.test_layer_bwd_finite_differences, dict(phi1=0)),
+    (pins.test_layer_append_equals_full_forward, {}),
 ]
 
 

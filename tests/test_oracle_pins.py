@@ -455,6 +455,51 @@ def test_mfalcon_equals_last_row_of_full_forward():
             assert np.allclose(y[c], h[-1], rtol=1e-12, atol=1e-12), (u, c)
 
 
+def test_layer_kv_equals_layer_forward_cache():
+    """The cache-only layer (K, V of phi1(x W1^T + b1)) returns exactly the
+    K and V the full layer forward keeps, for SiLU and ReLU."""
+    rng = np.random.default_rng(23)
+    H, d, D, N = 2, 4, 12, 16
+    hist = np.array([5, 9])
+    off = synth.offsets_of(hist)
+    ts = synth.timestamps(rng, hist)
+    lay = synth.Layer(w1=rng.standard_normal((4 * H * d, D)), b1=rng.standard_normal(4 * H * d),
+                      w2=rng.standard_normal((D, H * d)), b2=rng.standard_normal(D),
+                      rab_p=rng.standard_normal((H, 2 * N + 1)), rab_t=rng.standard_normal((H, 128)))
+    x = rng.standard_normal((int(off[-1]), D))
+    for phi1 in (0, 1):
+        _, K, V = oracle.layer_fwd(off, ts, x, lay, H, d, N, phi1=phi1, return_kv=True)
+        kv = oracle.layer_kv(x, lay, H, d, phi1=phi1)
+        assert np.allclose(kv[0], K, rtol=1e-14, atol=1e-14) and np.allclose(kv[1], V, rtol=1e-14, atol=1e-14)
+
+
+def test_layer_append_equals_full_forward():
+    """Appending a_u new actions to a cached history gives exactly rows
+    n_u.. of the layer run over the whole sequence [history; new] (the cache
+    only removes recomputation), and the merged cache equals that run's K,
+    V.  Users with no history, no new actions, one new action and several."""
+    rng = np.random.default_rng(24)
+    H, d, D, N = 2, 4, 12, 16
+    hist = np.array([5, 0, 9, 4, 7])
+    add = np.array([3, 4, 1, 0, 6])
+    hoff, aoff = synth.offsets_of(hist), synth.offsets_of(add)
+    lay = synth.Layer(w1=rng.standard_normal((4 * H * d, D)) / math.sqrt(D), b1=rng.standard_normal(4 * H * d) * .1,
+                      w2=rng.standard_normal((D, H * d)) / math.sqrt(H * d), b2=rng.standard_normal(D) * .1,
+                      rab_p=rng.standard_normal((H, 2 * N + 1)), rab_t=rng.standard_normal((H, 128)))
+    full_len = hist + add
+    ts_full = synth.timestamps(rng, full_len)
+    x_full = rng.standard_normal((int(full_len.sum()), D))
+    foff = synth.offsets_of(full_len)
+    hrows = np.concatenate([np.arange(foff[u], foff[u] + hist[u]) for u in range(len(hist))])
+    arows = np.concatenate([np.arange(foff[u] + hist[u], foff[u + 1]) for u in range(len(hist))])
+    _, Kh, Vh = oracle.layer_fwd(hoff, ts_full[hrows], x_full[hrows], lay, H, d, N, return_kv=True)
+    y_new, kv_out = oracle.layer_append(hoff, ts_full[hrows], aoff, ts_full[arows], lay, np.stack([Kh, Vh]),
+                                        x_full[arows], H, d, N)
+    y_full, Kf, Vf = oracle.layer_fwd(foff, ts_full, x_full, lay, H, d, N, return_kv=True)
+    assert np.allclose(y_new, y_full[arows], rtol=1e-12, atol=1e-12)
+    assert np.allclose(kv_out[0], Kf, rtol=1e-12, atol=1e-12) and np.allclose(kv_out[1], Vf, rtol=1e-12, atol=1e-12)
+
+
 def test_mfalcon_candidates_independent():
     """A candidate's score does not depend on the other candidates."""
     rng = np.random.default_rng(20)
