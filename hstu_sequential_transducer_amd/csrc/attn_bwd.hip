@@ -608,15 +608,13 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
     };
     // A finished sum goes to this item's slot of partial sums (indexed by
     // key - query in [k0 - (L - 1), 0], the causal values this key tile
-    // meets; drab_reduce_kernel adds the slots in a fixed order), or, for a
+    // meets; drab_p_reduce_kernel adds the slots in a fixed order), or, for a
     // sequence whose slots did not fit, into drab_p with an atomic add.
-    const int tk = k0 / BN, ntk = (L + BN - 1) / BN;
-    float *pslot = nullptr;
-    if (a.drab_p && a.pbase[b_seq] >= 0)
-        pslot = a.dpart + a.pbase[b_seq] + ((int64_t)h * ntk + tk) * L + (L - 1);
     auto put_p = [&](int dl, float v) {
-        if (pslot) {
-            if (dl <= 0 && dl >= k0 - (L - 1)) pslot[dl] = v;
+        const int64_t pb = a.pbase[b_seq]; // (reloaded here: nothing stays live across the loop)
+        if (pb >= 0) {
+            const int tk = k0 / BN, ntk = (L + BN - 1) / BN;
+            if (dl <= 0 && dl >= k0 - (L - 1)) a.dpart[pb + ((int64_t)h * ntk + tk) * L + (L - 1) + dl] = v;
         } else if (v != 0.f) {
             const int cl = dl < -a.N ? -a.N : (dl > a.N ? a.N : dl);
             atomicAdd(&a.drab_p[h * p_hs + cl + a.N], v);
@@ -888,10 +886,11 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
         for (int dl = lo + tid; dl <= hi; dl += NT) put_p(dl, sm.ring[dl & (RING - 1)]);
     }
     if constexpr (DT && TM != 0) {
-        if (tid < TB) { // this item's slot of drab_t partial sums (added up by drab_reduce_kernel)
+        if (tid < TB) { // this item's slot of drab_t partial sums (added up by drab_t_reduce_kernel)
             float s = 0.f;
             for (int pp = 0; pp < 4; pp++)
                 for (int c = 0; c < TCOPY; c++) s += sm.dtab[pp][c][tid];
+            const int tk = k0 / BN, ntk = (L + BN - 1) / BN;
             a.tpart[a.tbase[b_seq] + ((int64_t)h * ntk + tk) * TB_SLOTS + tid] = s;
         }
     }
@@ -974,75 +973,89 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs &a, int max_items, hipStream_t
 // The bias gradients from the items' partial sums, added in a fixed order,
 // so that drab_p and drab_t do not depend on the order in which items ran.
 //
-// drab_p[h][idx] += the sum over sequences b (in order), then the key - query
-// values x folded into idx (idx 0 collects every x <= -N), then the key
-// tiles t (in order) whose slot covers x.  drab_p was zeroed by the
-// launcher; items of a sequence without slots added their share with
-// atomics.  Entries idx > N (key after query) are never reached.  One lane
-// per entry; each lane keeps up to 16 loads in flight and adds them in tile
-// order.
-__global__ void __launch_bounds__(64) drab_p_reduce_kernel(DrabReduceArgs r)
+// drab_p[h][idx] += the sum of the slot entries for key - query x = idx - N
+// (idx 0 collects every x <= -N) over the items that cover it.  A workgroup
+// takes 64 entries of one head; its 16 waves split the key tiles by residue
+// (wave g adds tiles t = g, g + 16, ... of every sequence, in order of
+// sequence, x and t), then lane i of wave 0 adds the 16 wave sums in order
+// of g.  drab_p was zeroed by the launcher; items of a sequence without
+// slots added their share with atomics.  Entries idx > N (key after query)
+// are never reached.
+constexpr int RED_G = 16;
+__global__ void __launch_bounds__(64 * RED_G) drab_p_reduce_kernel(DrabReduceArgs r)
 {
+    __shared__ float part[RED_G][64];
     if (*r.status) return;
-    const int h = blockIdx.y, idx = blockIdx.x * 64 + threadIdx.x;
-    if (idx > r.N) return;
+    const int h = blockIdx.y, lane = threadIdx.x & 63, g = threadIdx.x >> 6;
+    const int idx = blockIdx.x * 64 + lane;
+    const bool valid = idx <= r.N;
     const int dl = idx - r.N;
     float acc = 0.f;
-    for (int b = 0; b < r.B; b++) {
-        const int64_t pb = r.pbase[b];
-        const int L = r.offsets[b + 1] - r.offsets[b];
-        if (pb < 0 || L <= 0 || -dl > L - 1) continue;
-        const int nt = (L + BWD_BN - 1) / BWD_BN;
-        const float *slot = r.dpart + pb + (int64_t)h * nt * L + (L - 1);
-        const int xlo = idx == 0 ? -(L - 1) : dl;
-        for (int x = dl; x >= xlo; x--) {
-            const int tmax = min(nt - 1, (x + L - 1) / BWD_BN);
-            for (int t0 = 0; t0 <= tmax; t0 += 16) {
-                float v[16];
+    // per-sequence slot bases and lengths, 64 sequences at a time, one per
+    // lane; the loop reads them back with uniform lane reads, so only the
+    // slot loads themselves wait on memory
+    for (int b0 = 0; b0 < r.B; b0 += 64) {
+        const int bl = b0 + lane;
+        const int64_t pbl = bl < r.B ? r.pbase[bl] : -1;
+        const int Ll = bl < r.B ? r.offsets[bl + 1] - r.offsets[bl] : 0;
+        const int nb = min(64, r.B - b0);
+#pragma unroll 4
+        for (int jb = 0; jb < nb; jb++) {
+            const int64_t pb = ((int64_t)__builtin_amdgcn_readlane((int)(pbl >> 32), jb) << 32) |
+                               (uint32_t)__builtin_amdgcn_readlane((int)pbl, jb);
+            const int L = __builtin_amdgcn_readlane(Ll, jb);
+            if (!valid || pb < 0 || L <= 0 || -dl > L - 1) continue;
+            const int nt = (L + BWD_BN - 1) / BWD_BN;
+            const float *slot = r.dpart + pb + (int64_t)h * nt * L + (L - 1);
+            const int xlo = idx == 0 ? -(L - 1) : dl;
+            for (int x = dl; x >= xlo; x--) {
+                const int tmax = min(nt - 1, (x + L - 1) / BWD_BN);
+                float v[4];
 #pragma unroll
-                for (int i = 0; i < 16; i++) v[i] = t0 + i <= tmax ? slot[(int64_t)(t0 + i) * L + x] : 0.f;
+                for (int i = 0; i < 4; i++) {
+                    const int t = g + RED_G * i;
+                    v[i] = t <= tmax ? slot[(int64_t)t * L + x] : 0.f;
+                }
 #pragma unroll
-                for (int i = 0; i < 16; i++) acc += v[i];
+                for (int i = 0; i < 4; i++) acc += v[i];
+                for (int t = g + 4 * RED_G; t <= tmax; t += RED_G) acc += slot[(int64_t)t * L + x];
             }
         }
     }
-    r.drab_p[h * r.p_hs + idx] += acc;
+    part[g][lane] = acc;
+    __syncthreads();
+    if (g == 0 && valid) {
+        float s = 0.f;
+#pragma unroll
+        for (int k = 0; k < RED_G; k++) s += part[k][lane];
+        r.drab_p[h * r.p_hs + idx] += s;
+    }
 }
 
-// drab_t[h][bucket] = the sum over the items' slots: one wave per entry, lane
-// = sequence (64 at a time, each lane adding its sequence's tiles in order),
-// then a butterfly over the lanes (a fixed tree, the same on every lane).
-// Buckets from TB_SLOTS on are never reached and get 0.
+// drab_t[h][bucket] = the sum over the items' slots: one wave per entry;
+// lane l adds tiles t = l, l + 64, ... of every sequence (in order of
+// sequence and t), then a butterfly over the lanes (a fixed tree, the same
+// on every lane).  Buckets from TB_SLOTS on are never reached and get 0.
 __global__ void __launch_bounds__(64) drab_t_reduce_kernel(DrabReduceArgs r)
 {
     if (*r.status) return;
     const int h = blockIdx.x >> 7, bk = blockIdx.x & 127, lane = threadIdx.x;
-    float acc = 0.f;
+    float s = 0.f;
     if (bk < TB_SLOTS)
-        for (int b0 = 0; b0 < r.B; b0 += 64) {
-            const int b = b0 + lane;
-            float s = 0.f;
-            if (b < r.B) {
-                const int L = r.offsets[b + 1] - r.offsets[b];
-                const int nt = (L + BWD_BN - 1) / BWD_BN;
-                const float *slot = r.tpart + r.tbase[b] + (int64_t)h * nt * TB_SLOTS + bk;
-                for (int t0 = 0; t0 < nt; t0 += 16) {
-                    float v[16];
-#pragma unroll
-                    for (int i = 0; i < 16; i++) v[i] = t0 + i < nt ? slot[(int64_t)(t0 + i) * TB_SLOTS] : 0.f;
-#pragma unroll
-                    for (int i = 0; i < 16; i++) s += v[i];
-                }
-            }
-            acc += wave_sum(s);
+        for (int b = 0; b < r.B; b++) {
+            const int L = r.offsets[b + 1] - r.offsets[b];
+            const int nt = (L + BWD_BN - 1) / BWD_BN;
+            const float *slot = r.tpart + r.tbase[b] + (int64_t)h * nt * TB_SLOTS + bk;
+            for (int t = lane; t < nt; t += 64) s += slot[(int64_t)t * TB_SLOTS];
         }
-    if (lane == 0) r.drab_t[h * r.t_hs + bk] = acc;
+    s = wave_sum(s);
+    if (lane == 0) r.drab_t[h * r.t_hs + bk] = s;
 }
 
 hipError_t launch_drab_reduce(const DrabReduceArgs &r, hipStream_t st)
 {
     if (r.drab_p)
-        hipLaunchKernelGGL(drab_p_reduce_kernel, dim3((r.N + 1 + 63) / 64, r.H), dim3(64), 0, st, r);
+        hipLaunchKernelGGL(drab_p_reduce_kernel, dim3((r.N + 1 + 63) / 64, r.H), dim3(64 * RED_G), 0, st, r);
     if (r.drab_t) hipLaunchKernelGGL(drab_t_reduce_kernel, dim3(r.H * 128), dim3(64), 0, st, r);
     return hipGetLastError();
 }
