@@ -22,7 +22,7 @@ HSTU_ACT_SILU, HSTU_ACT_RELU = 0, 1
 OP_ATTN_FWD, OP_ATTN_BWD, OP_LAYER_FWD, OP_MFALCON, OP_LAYER_BWD = range(5)
 
 EXPORTED = ["hstu_attn_fwd", "hstu_attn_bwd", "hstu_layer_fwd", "hstu_layer_bwd", "mfalcon_score",
-            "hstu_workspace_size",
+            "hstu_workspace_size", "hstu_attn_fwd_noalloc",
             "hstu_profile_enable", "hstu_profile_collect", "hstu_last_error", "hstu_abi_version"]
 
 
@@ -83,6 +83,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hstu_attn_fwd.restype = ctypes.c_int
     lib.hstu_attn_fwd.argtypes = [P(Jagged), P(Dims), P(Bias), CMat, CMat, CMat, CMat, Mat, ctypes.c_void_p,
                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.hstu_attn_fwd_noalloc.restype = ctypes.c_int
+    lib.hstu_attn_fwd_noalloc.argtypes = [P(Jagged), P(Dims), P(Bias), CMat, CMat, CMat, CMat, Mat, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p]
     lib.hstu_attn_bwd.restype = ctypes.c_int
     lib.hstu_attn_bwd.argtypes = [P(Jagged), P(Dims), P(Bias), CMat, CMat, CMat, CMat, ctypes.c_void_p,
                                   ctypes.c_void_p, CMat, Mat, Mat, Mat, Mat, ctypes.c_void_p, ctypes.c_void_p,
@@ -222,6 +225,27 @@ def attn_fwd(offsets: torch.Tensor, total: int, ts: Optional[torch.Tensor], q: t
     st = lib.hstu_attn_fwd(ctypes.byref(jag), ctypes.byref(dims), ctypes.byref(bias), _rowmat(q, H * d),
                            _rowmat(k, H * d), _rowmat(v, H * d), _rowmat(u, H * d), _rowmat(out, H * d, Mat),
                            _ptr(o_save), _ptr(ln_stats), ws.data_ptr(), ws.numel(), _stream(q.device))
+    _check(st)
+    return out
+
+
+def attn_fwd_noalloc(offsets: torch.Tensor, total: int, ts: Optional[torch.Tensor], q: torch.Tensor, k: torch.Tensor,
+                     v: torch.Tensor, rab_p: Optional[torch.Tensor], rab_t: Optional[torch.Tensor], n_max: int,
+                     u: Optional[torch.Tensor] = None, eps: float = 1e-5, out: Optional[torch.Tensor] = None,
+                     o_save: Optional[torch.Tensor] = None, ln_stats: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """hstu_attn_fwd_noalloc: hstu_attn_fwd with the library's static scratch
+    array instead of a workspace.  `out` should be given by callers that must
+    not allocate (otherwise it is allocated here, by torch)."""
+    lib = load_library()
+    T, H, d = q.shape
+    jag = _jagged(offsets, ts, n_max, total)
+    dims = Dims(_dtype_code(q), H, d, v.shape[2], eps)
+    if out is None:
+        out = torch.empty((T, H * d), dtype=q.dtype, device=q.device)
+    bias = _bias(rab_p, rab_t)
+    st = lib.hstu_attn_fwd_noalloc(ctypes.byref(jag), ctypes.byref(dims), ctypes.byref(bias), _rowmat(q, H * d),
+                                   _rowmat(k, H * d), _rowmat(v, H * d), _rowmat(u, H * d), _rowmat(out, H * d, Mat),
+                                   _ptr(o_save), _ptr(ln_stats), _stream(q.device))
     _check(st)
     return out
 

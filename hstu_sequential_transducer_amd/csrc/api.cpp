@@ -76,7 +76,7 @@ struct AttnWs {
 // sequence, n_b = ceil(L_b / 128) <= ceil(n_max / 128)): sequences past it
 // add their share of drab_p with atomics.  The drab_t slots (H n_b TB_SLOTS
 // floats) always fit.
-AttnWs attn_ws(const hstu_jagged *j, const hstu_dims *dm, int tile, bool bwd)
+AttnWs attn_ws(const hstu_jagged *j, const hstu_dims *dm, int tile, bool bwd, bool with_obuf = true)
 {
     AttnWs w{};
     Carver c;
@@ -86,7 +86,7 @@ AttnWs attn_ws(const hstu_jagged *j, const hstu_dims *dm, int tile, bool bwd)
     w.rel = c.take((size_t)T * 4 * 3); // rel, then rmin and rmax per 32-token block
     w.wide = c.take((size_t)B * 4);
     w.rank = c.take((size_t)B * 4);
-    w.obuf = c.take((size_t)T * H * dm->d_v * 4);
+    w.obuf = with_obuf ? c.take((size_t)T * H * dm->d_v * 4) : 0;
     if (bwd) {
         w.dO = c.take((size_t)T * H * dm->d_v * 2 * 2); // hi and lo bf16 planes
         w.ds_base = c.take((size_t)B * 8);
@@ -582,6 +582,48 @@ MfWs mf_ws(const hstu_jagged *hist, const hstu_dims *dm, int32_t D, int32_t M)
 
 } // namespace
 
+namespace hstu_internal {
+
+hstu_status set_error(hstu_status s, const char *msg) { return fail(s, "%s", msg); }
+
+// The forward's validation and launch on the workspace ws of ws_bytes.
+// lean: the fp32 O staging buffer is carved only when the gate needs it
+// (u given and no o_save); with ws == NULL only the validation runs and the
+// bytes needed go to *need.
+hstu_status attn_fwd_entry(const hstu_jagged *j, const hstu_dims *dm, const hstu_bias *bias, hstu_cmat q, hstu_cmat k,
+                           hstu_cmat v, hstu_cmat u, hstu_mat out, float *o_save, float *ln_stats, void *ws,
+                           size_t ws_bytes, void *stream, bool lean, size_t *need)
+{
+    TRY(check_jagged(j));
+    TRY(check_dims(dm));
+    TRY(check_bias(bias, j));
+    const int H = dm->heads, d = dm->d_qk, F = H * dm->d_v;
+    TRY(check_view(q.ptr, q.ld, (int64_t)H * d, "q"));
+    TRY(check_view(k.ptr, k.ld, (int64_t)H * d, "k"));
+    TRY(check_view(v.ptr, v.ld, (int64_t)F, "v"));
+    TRY(check_view(u.ptr, u.ld, (int64_t)F, "u", false));
+    TRY(check_view(out.ptr, out.ld, (int64_t)F, "out"));
+    if (ln_stats && !u.ptr) return fail(HSTU_ERR_ARG, "ln_stats requires u (the epilogue)");
+    if (dm->dtype == HSTU_BF16) {
+        TRY(check_vec_view(q.ptr, q.ld, HSTU_BF16, "q"));
+        TRY(check_vec_view(k.ptr, k.ld, HSTU_BF16, "k"));
+        TRY(check_vec_view(v.ptr, v.ld, HSTU_BF16, "v"));
+        TRY(check_vec_view(u.ptr, u.ld, HSTU_BF16, "u"));
+        TRY(check_vec_view(out.ptr, out.ld, HSTU_BF16, "out"));
+        TRY(check_vec_view(o_save, F, HSTU_F32, "o_save"));
+    }
+    const AttnWs w = attn_ws(j, dm, fwd_tile(dm), false, !lean || (u.ptr && !o_save));
+    if (need) *need = w.total;
+    if (!ws && need) return ok();
+    TRY(check_ws(ws, ws_bytes, w.total));
+    hipStream_t st = (hipStream_t)stream;
+    TRY(attn_fwd_launch(j, dm, bias, q, k, v, u, out, o_save, ln_stats, (char *)ws, w, st));
+    TRY(debug_check(ws, st));
+    return ok();
+}
+
+} // namespace hstu_internal
+
 extern "C" {
 
 int32_t hstu_abi_version(void) { return HSTU_ABI_VERSION; }
@@ -618,30 +660,8 @@ hstu_status hstu_attn_fwd(const hstu_jagged *j, const hstu_dims *dm, const hstu_
                           hstu_cmat v, hstu_cmat u, hstu_mat out, float *o_save, float *ln_stats, void *ws,
                           size_t ws_bytes, void *stream)
 {
-    TRY(check_jagged(j));
-    TRY(check_dims(dm));
-    TRY(check_bias(bias, j));
-    const int H = dm->heads, d = dm->d_qk, F = H * dm->d_v;
-    TRY(check_view(q.ptr, q.ld, (int64_t)H * d, "q"));
-    TRY(check_view(k.ptr, k.ld, (int64_t)H * d, "k"));
-    TRY(check_view(v.ptr, v.ld, (int64_t)F, "v"));
-    TRY(check_view(u.ptr, u.ld, (int64_t)F, "u", false));
-    TRY(check_view(out.ptr, out.ld, (int64_t)F, "out"));
-    if (ln_stats && !u.ptr) return fail(HSTU_ERR_ARG, "ln_stats requires u (the epilogue)");
-    if (dm->dtype == HSTU_BF16) {
-        TRY(check_vec_view(q.ptr, q.ld, HSTU_BF16, "q"));
-        TRY(check_vec_view(k.ptr, k.ld, HSTU_BF16, "k"));
-        TRY(check_vec_view(v.ptr, v.ld, HSTU_BF16, "v"));
-        TRY(check_vec_view(u.ptr, u.ld, HSTU_BF16, "u"));
-        TRY(check_vec_view(out.ptr, out.ld, HSTU_BF16, "out"));
-        TRY(check_vec_view(o_save, F, HSTU_F32, "o_save"));
-    }
-    const AttnWs w = attn_ws(j, dm, fwd_tile(dm), false);
-    TRY(check_ws(ws, ws_bytes, w.total));
-    hipStream_t st = (hipStream_t)stream;
-    TRY(attn_fwd_launch(j, dm, bias, q, k, v, u, out, o_save, ln_stats, (char *)ws, w, st));
-    TRY(debug_check(ws, st));
-    return ok();
+    return hstu_internal::attn_fwd_entry(j, dm, bias, q, k, v, u, out, o_save, ln_stats, ws, ws_bytes, stream, false,
+                                         nullptr);
 }
 
 hstu_status hstu_attn_bwd(const hstu_jagged *j, const hstu_dims *dm, const hstu_bias *bias, hstu_cmat q, hstu_cmat k,

@@ -2,6 +2,15 @@
 // gfx950 kernels.  Internal to libhstu; not part of the public C ABI.
 #pragma once
 #include "common.h"
+#include "../../include/hstu.h"
+
+// ---- entry-point internals shared by the C ABI sources (api.cpp, noalloc.hip)
+namespace hstu_internal {
+hstu_status set_error(hstu_status s, const char *msg);
+hstu_status attn_fwd_entry(const hstu_jagged *j, const hstu_dims *dm, const hstu_bias *bias, hstu_cmat q, hstu_cmat k,
+                           hstu_cmat v, hstu_cmat u, hstu_mat out, float *o_save, float *ln_stats, void *ws,
+                           size_t ws_bytes, void *stream, bool lean, size_t *need);
+} // namespace hstu_internal
 
 constexpr int SCHED_BINS = 4096; // longest sequence: (SCHED_BINS - 1) tiles
 

@@ -222,6 +222,25 @@ hstu_status mfalcon_score(const hstu_jagged *hist, const hstu_dims *dims, int32_
                           const int32_t *cand_offsets, int32_t total_cand, const int64_t *cand_ts, hstu_cmat x_cand,
                           int32_t b_m, float *y_cand, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * hstu_attn_fwd without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, results and errors as hstu_attn_fwd;
+ * its scratch space (launcher work list, relative times, and the fp32 O
+ * staging rows when u is given without o_save) is a static device array of
+ * HSTU_NOALLOC_SCRATCH_BYTES per GPU, held by the library until the process
+ * ends.  A batch needing more returns HSTU_ERR_WORKSPACE before anything is
+ * enqueued (about 12 bytes per token plus 16 per 128-token tile and head,
+ * plus 4*H*d_v bytes per token for the staging rows: pass o_save with u to
+ * avoid them).  The call allocates nothing.  All calls on one GPU share its
+ * array: calls that overlap on one GPU (other streams or threads) race and
+ * must be ordered by the caller.
+ */
+#define HSTU_NOALLOC_SCRATCH_BYTES (16u << 20)
+hstu_status hstu_attn_fwd_noalloc(const hstu_jagged *j, const hstu_dims *dims, const hstu_bias *bias, hstu_cmat q,
+                                  hstu_cmat k, hstu_cmat v, hstu_cmat u, hstu_mat out, float *o_save,
+                                  float *ln_stats, void *stream);
+
 /* Kernel timing for benchmarks.  While enabled, every entry point brackets
  * each kernel (or small group of kernels) it launches with a pair of HIP
  * events recorded on the launch stream; this adds no device work and does not

@@ -146,3 +146,25 @@ def test_layer_bwd_workspace_size():
     attn = lib.hstu_workspace_size(bd.OP_ATTN_BWD, ctypes.byref(_jag(T=100000)), ctypes.byref(d), 0, 0)
     assert 0 < small < big and big > attn and big % 256 == 0
     assert lib.hstu_workspace_size(bd.OP_LAYER_BWD, ctypes.byref(_jag(T=100)), ctypes.byref(d), 0, 0) == 0
+
+
+def test_noalloc_rejects_batches_beyond_its_scratch_limit():
+    """hstu_attn_fwd_noalloc validates like hstu_attn_fwd and refuses a batch
+    whose scratch would exceed HSTU_NOALLOC_SCRATCH_BYTES before touching the
+    device (the pointers are never dereferenced)."""
+    lib = hs.load_library()
+    limit = int(re.search(r"#define HSTU_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+                .group(1)) << 20
+    assert limit == 16 << 20
+    bias = bd.Bias(None, 0, None, 0)
+    m = lambda p, ld=512: bd.CMat(p, ld)
+    call = lambda T, u=None, o_save=None: lib.hstu_attn_fwd_noalloc(
+        ctypes.byref(_jag(T=T)), ctypes.byref(_dims()), ctypes.byref(bias), m(256), m(512), m(768), m(u),
+        bd.Mat(1024, 512), o_save, None, None)
+    assert call(2_000_000) == bd.HSTU_ERR_WORKSPACE      # 12 bytes of relative time per token alone
+    assert "limit" in hs.last_error()
+    assert call(20_000, u=1280) == bd.HSTU_ERR_WORKSPACE  # fp32 O staging rows for the gate
+    assert "o_save" in hs.last_error()
+    assert lib.hstu_attn_fwd_noalloc(ctypes.byref(_jag()), ctypes.byref(_dims(d=64)), ctypes.byref(bias), m(256),
+                                     m(512), m(768), m(None), bd.Mat(1024, 512), None, None,
+                                     None) == bd.HSTU_ERR_UNSUPPORTED
