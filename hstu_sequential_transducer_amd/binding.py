@@ -19,10 +19,10 @@ LIB_PATH = os.path.join(_HERE, "libhstu.so")
 HSTU_OK, HSTU_ERR_ARG, HSTU_ERR_UNSUPPORTED, HSTU_ERR_WORKSPACE, HSTU_ERR_DEVICE = range(5)
 HSTU_F32, HSTU_BF16 = 0, 1
 HSTU_ACT_SILU, HSTU_ACT_RELU = 0, 1
-OP_ATTN_FWD, OP_ATTN_BWD, OP_LAYER_FWD, OP_MFALCON, OP_LAYER_BWD = range(5)
+OP_ATTN_FWD, OP_ATTN_BWD, OP_LAYER_FWD, OP_MFALCON, OP_LAYER_BWD, OP_LAYER_APPEND = range(6)
 
 EXPORTED = ["hstu_attn_fwd", "hstu_attn_bwd", "hstu_layer_fwd", "hstu_layer_bwd", "mfalcon_score",
-            "hstu_workspace_size", "hstu_attn_fwd_noalloc",
+            "hstu_workspace_size", "hstu_attn_fwd_noalloc", "hstu_layer_append",
             "hstu_profile_enable", "hstu_profile_collect", "hstu_last_error", "hstu_abi_version"]
 
 
@@ -96,6 +96,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hstu_layer_bwd.restype = ctypes.c_int
     lib.hstu_layer_bwd.argtypes = [P(Jagged), P(Dims), ctypes.c_int32, P(Layer), CMat, CMat, Mat] + \
         [ctypes.c_void_p] * 6 + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.hstu_layer_append.restype = ctypes.c_int
+    lib.hstu_layer_append.argtypes = [P(Jagged), P(Jagged), P(Dims), ctypes.c_int32, P(Layer), CMat, CMat, CMat, Mat,
+                                      Mat, Mat, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.mfalcon_score.restype = ctypes.c_int
     lib.mfalcon_score.argtypes = [P(Jagged), P(Dims), ctypes.c_int32, ctypes.c_int32, P(Layer), P(CMat), P(CMat),
                                   ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, CMat, ctypes.c_int32,
@@ -336,6 +339,36 @@ def layer_bwd(offsets: torch.Tensor, total: int, ts: Optional[torch.Tensor], x: 
                             ws.data_ptr(), ws.numel(), _stream(x.device))
     _check(st)
     return dict(dx=dx, dw1=dw1, db1=db1, dw2=dw2, db2=db2, drab_p=drp, drab_t=drt)
+
+
+def layer_append(hist_offsets: torch.Tensor, hist_total: int, hist_ts: Optional[torch.Tensor],
+                 add_offsets: torch.Tensor, add_total: int, add_ts: Optional[torch.Tensor], x_new: torch.Tensor,
+                 layer: dict, k_cache: Optional[torch.Tensor], v_cache: Optional[torch.Tensor], heads: int, d: int,
+                 n_max: int, eps: float = 1e-5, out: Optional[torch.Tensor] = None,
+                 k_out: Optional[torch.Tensor] = None, v_out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None):
+    """hstu_layer_append.  Returns (y_new [T_new][D], k_out, v_out
+    [T_hist + T_new][H*d]): the new actions' layer output and the merged
+    caches (user u's rows from hist_offsets[u] + add_offsets[u])."""
+    lib = load_library()
+    Tn, D = x_new.shape
+    HD = heads * d
+    hj = _jagged(hist_offsets, hist_ts, n_max, hist_total)
+    aj = _jagged(add_offsets, add_ts, n_max, add_total)
+    dims = Dims(_dtype_code(x_new), heads, d, d, eps)
+    y = out if out is not None else torch.empty((Tn, D), dtype=x_new.dtype, device=x_new.device)
+    Tm = int(hist_total) + int(add_total)
+    ko = k_out if k_out is not None else torch.empty((Tm, HD), dtype=x_new.dtype, device=x_new.device)
+    vo = v_out if v_out is not None else torch.empty((Tm, HD), dtype=x_new.dtype, device=x_new.device)
+    nws = workspace_size(OP_LAYER_APPEND, hj, dims, D, int(add_total))
+    ws = workspace if workspace is not None else _workspace(nws, x_new.device)
+    L = _layer_struct(layer)
+    st = lib.hstu_layer_append(ctypes.byref(hj), ctypes.byref(aj), ctypes.byref(dims), D, ctypes.byref(L),
+                               _rowmat(k_cache, HD), _rowmat(v_cache, HD), _rowmat(x_new, D), _rowmat(y, D, Mat),
+                               _rowmat(ko, HD, Mat), _rowmat(vo, HD, Mat), ws.data_ptr(), ws.numel(),
+                               _stream(x_new.device))
+    _check(st)
+    return y, ko, vo
 
 
 def mfalcon_score(hist_offsets: torch.Tensor, hist_total: int, hist_ts: Optional[torch.Tensor], layers: Sequence[dict],

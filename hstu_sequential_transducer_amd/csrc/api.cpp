@@ -538,6 +538,35 @@ hstu_status run_gemm(const GemmArgs &g, hstu_dtype dt, const char *name, hipStre
 // M-FALCON plan: key splits so a small number of candidate tiles still fills
 // the chip; at most 8 splits (16 measured 9 % slower for one user, 4 slower
 // still).  Depends only on sizes known on the host.
+// Workspace of hstu_layer_append: header, work list, merged offsets [U+1],
+// merged times int64 [Tm] and relative times (12 B per merged token), wide
+// flags, the new tokens' f1 output Z [Tn][4Hd] (bf16), their fp32 O [Tn][Hd]
+// and gate G [Tn][Hd].
+struct AppendWs {
+    size_t header, items, moff, tsm, rel, wide, z, obuf, g, total;
+    int max_items;
+};
+
+AppendWs append_ws(int U, int Th, int Tn, const hstu_dims *dm)
+{
+    AppendWs w{};
+    Carver c;
+    const size_t H = dm->heads, HD = H * dm->d_qk, Tm = (size_t)Th + Tn;
+    // tiles with new positions: sum_u (ceil((n+a)/BM) - floor(n/BM)) <= Tn / BM + 2 U per head
+    w.max_items = (int)(((int64_t)Tn / FWD_BM + 2 * (int64_t)U) * (int64_t)H);
+    w.header = c.take(256);
+    w.items = c.take((size_t)w.max_items * sizeof(int2));
+    w.moff = c.take((size_t)(U + 1) * 4);
+    w.tsm = c.take(Tm * 8);
+    w.rel = c.take(Tm * 12);
+    w.wide = c.take((size_t)U * 4);
+    w.z = c.take((size_t)Tn * 4 * HD * 2);
+    w.obuf = c.take((size_t)Tn * HD * 4);
+    w.g = c.take((size_t)Tn * HD * 2);
+    w.total = c.cur;
+    return w;
+}
+
 struct MfPlan {
     int nsplit, kchunk, max_items;
 };
@@ -644,6 +673,12 @@ size_t hstu_workspace_size(hstu_op op, const hstu_jagged *j, const hstu_dims *di
             return 0;
         }
         return layer_bwd_ws(j, dims, d_model).total;
+    case HSTU_OP_LAYER_APPEND:
+        if (d_model < 1 || total_cand < 0) {
+            fail(HSTU_ERR_ARG, "d_model must be >= 1 and the new actions' total (total_cand) >= 0");
+            return 0;
+        }
+        return append_ws(j->batch, j->total, total_cand, dims).total;
     case HSTU_OP_MFALCON:
         if (d_model < 1 || total_cand < 0) {
             fail(HSTU_ERR_ARG, "d_model must be >= 1 and total_cand >= 0");
@@ -854,6 +889,144 @@ hstu_status hstu_layer_bwd(const hstu_jagged *j, const hstu_dims *dm, int32_t d_
         }
         ProfScope ps("sum_splits_kernel", st);
         TRY(launched(launch_sum_splits(part, w.p1.splits, (int64_t)Z4 * D, dw1, st), "split-sum kernel"));
+    }
+    TRY(debug_check(ws, st));
+    return ok();
+}
+
+hstu_status hstu_layer_append(const hstu_jagged *hist, const hstu_jagged *add, const hstu_dims *dm, int32_t d_model,
+                              const hstu_layer *layer, hstu_cmat k_cache, hstu_cmat v_cache, hstu_cmat x_new,
+                              hstu_mat y_new, hstu_mat k_out, hstu_mat v_out, void *ws, size_t ws_bytes, void *stream)
+{
+    TRY(check_jagged(hist));
+    if (!add) return fail(HSTU_ERR_ARG, "add (the new actions) is NULL");
+    if (add->batch != hist->batch)
+        return fail(HSTU_ERR_ARG, "add->batch (%d) != hist->batch (%d)", add->batch, hist->batch);
+    if (add->total < 0) return fail(HSTU_ERR_ARG, "add->total must be >= 0");
+    if (!add->offsets) return fail(HSTU_ERR_ARG, "add->offsets is NULL");
+    if ((hist->ts == nullptr) != (add->ts == nullptr))
+        return fail(HSTU_ERR_ARG, "history and new-action timestamps must both be given or both be NULL");
+    if ((int64_t)hist->total + add->total > INT32_MAX / 16)
+        return fail(HSTU_ERR_UNSUPPORTED, "history plus new actions: too many tokens");
+    TRY(check_dims(dm));
+    if (dm->dtype != HSTU_BF16) return fail(HSTU_ERR_UNSUPPORTED, "hstu_layer_append supports bf16 storage only");
+    if (d_model < 1) return fail(HSTU_ERR_ARG, "d_model must be >= 1");
+    TRY(check_layer(layer, hist, dm, d_model, 0));
+    const int H = dm->heads, d = dm->d_qk, HD = H * d, D = d_model, U = hist->batch;
+    const int Th = hist->total, Tn = add->total;
+    TRY(check_view(x_new.ptr, x_new.ld, D, "x_new"));
+    TRY(check_view(y_new.ptr, y_new.ld, D, "y_new"));
+    TRY(check_gemm_operand(x_new.ptr, x_new.ld, dm->dtype, "x_new"));
+    if (x_new.ptr == y_new.ptr) return fail(HSTU_ERR_ARG, "y_new may not alias x_new");
+    const struct { const void *p; int64_t ld; const char *n; } views[] = {
+        {k_cache.ptr, k_cache.ld, "k_cache"}, {v_cache.ptr, v_cache.ld, "v_cache"},
+        {k_out.ptr, k_out.ld, "k_out"}, {v_out.ptr, v_out.ld, "v_out"}};
+    for (const auto &x : views) {
+        TRY(check_view(x.p, x.ld, HD, x.n, !(Th == 0 && (x.p == k_cache.ptr || x.p == v_cache.ptr))));
+        TRY(check_vec_view(x.p, x.ld, HSTU_BF16, x.n));
+    }
+    if (k_out.ptr == k_cache.ptr || k_out.ptr == v_cache.ptr || v_out.ptr == k_cache.ptr ||
+        v_out.ptr == v_cache.ptr || k_out.ptr == v_out.ptr)
+        return fail(HSTU_ERR_ARG, "k_out and v_out may not alias each other or the caches they are built from");
+    const AppendWs w = append_ws(U, Th, Tn, dm);
+    TRY(check_ws(ws, ws_bytes, w.total));
+    hipStream_t st = (hipStream_t)stream;
+    char *wb = (char *)ws;
+    int *status = (int *)(wb + w.header), *n_items = status + 1;
+    int2 *items = (int2 *)(wb + w.items);
+    int32_t *moff = (int32_t *)(wb + w.moff);
+    int64_t *ts_m = (int64_t *)(wb + w.tsm);
+    uint32_t *rel = (uint32_t *)(wb + w.rel);
+    int32_t *wide = (int32_t *)(wb + w.wide);
+    bf16 *Z = (bf16 *)(wb + w.z), *G = (bf16 *)(wb + w.g);
+    float *obuf = (float *)(wb + w.obuf);
+    const int Tm = Th + Tn;
+    const bool use_t = hist->ts != nullptr && layer->rab.rab_t != nullptr;
+    // f1 + phi1 of the new tokens: Z = U | V | Q | K
+    if (Tn > 0) {
+        GemmArgs g1 = gemm_args(x_new.ptr, x_new.ld, layer->w1, layer->b1, Z, 4 * HD, false, Tn, 4 * HD, D,
+                                layer->phi1 == HSTU_ACT_RELU ? EPI_RELU : EPI_SILU);
+        TRY(run_gemm(g1, dm->dtype, "gemm_f1", st));
+    }
+    // validate, merged offsets and work list; the merged caches and times
+    {
+        AppendPlan p{};
+        p.hoff = hist->offsets;
+        p.aoff = add->offsets;
+        p.U = U;
+        p.Th = Th;
+        p.Tn = Tn;
+        p.H = H;
+        p.tile = FWD_BM;
+        p.max_items = w.max_items;
+        p.status = status;
+        p.n_items = n_items;
+        p.items = items;
+        p.moff = moff;
+        p.kc = (const bf16 *)k_cache.ptr;
+        p.vc = (const bf16 *)v_cache.ptr;
+        p.ldkc = k_cache.ld;
+        p.ldvc = v_cache.ld;
+        p.knew = Z + 3 * HD;
+        p.vnew = Z + HD;
+        p.ldnew = 4 * HD;
+        p.kout = (bf16 *)k_out.ptr;
+        p.vout = (bf16 *)v_out.ptr;
+        p.ldko = k_out.ld;
+        p.ldvo = v_out.ld;
+        p.hd = HD;
+        p.ts_h = use_t ? hist->ts : nullptr;
+        p.ts_a = use_t ? add->ts : nullptr;
+        p.ts_m = use_t ? ts_m : nullptr;
+        p.rel = rel;
+        p.wide = wide;
+        ProfScope ps("append_plan_kernel", st);
+        TRY(launched(launch_append_plan(p, st), "append plan kernels"));
+    }
+    // attention of the new positions over [history; new]
+    AttnFwdArgs a{};
+    a.q = Z + 2 * HD;
+    a.ldq = 4 * HD;
+    a.k = k_out.ptr;
+    a.v = v_out.ptr;
+    a.ldk = k_out.ld;
+    a.ldv = v_out.ld;
+    a.offsets = moff;
+    a.ts = use_t ? ts_m : nullptr;
+    a.rel = rel;
+    a.wide = wide;
+    a.rmin = rel + Tm;
+    a.rmax = rel + 2 * (size_t)Tm;
+    a.rab_p = layer->rab.rab_p;
+    a.rp_hs = layer->rab.rab_p_hstride;
+    a.rab_t = use_t ? layer->rab.rab_t : nullptr;
+    a.rt_hs = layer->rab.rab_t_hstride;
+    a.H = H;
+    a.N = hist->n_max;
+    a.d = d;
+    a.inv_n = 1.0f / (float)hist->n_max;
+    a.items = items;
+    a.n_items = n_items;
+    a.o32 = obuf;
+    a.ld_o32 = HD;
+    a.o16 = nullptr;
+    a.hoff = hist->offsets;
+    a.aoff = add->offsets;
+    {
+        ProfScope ps("attn_fwd_bf16_kernel", st);
+        TRY(launched(launch_attn_fwd_bf16(a, w.max_items, st), "attention forward kernel"));
+    }
+    if (Tn > 0) {
+        {
+            ProfScope ps("ln_gate_fwd_kernel", st);
+            TRY(launched(launch_ln_gate_fwd(obuf, HD, 1, 0, Z, 4 * HD, true, G, HD, nullptr, nullptr, 0, Tn, HD,
+                                            dm->ln_eps, status, st),
+                         "LayerNorm gate kernel"));
+        }
+        GemmArgs g2 = gemm_args(G, HD, layer->w2, layer->b2, y_new.ptr, y_new.ld, false, Tn, D, HD, EPI_NONE);
+        g2.R16 = x_new.ptr;
+        g2.ldr = x_new.ld;
+        TRY(run_gemm(g2, dm->dtype, "gemm_f2", st));
     }
     TRY(debug_check(ws, st));
     return ok();

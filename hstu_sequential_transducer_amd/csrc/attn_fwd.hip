@@ -117,8 +117,14 @@ DEV void pointwise(const floatx16 &sacc, uint32_t (&pk)[8], const uint32_t *kt_l
     }
 }
 
+// qs, qmap: the queries are positions [qs, L) of the sequence (qs = 0
+// except when new actions are appended to a cached history: then the
+// sequence is [history; new] and only the new positions are queries), and
+// query position p reads Q and writes O at row qmap + p (o_b for a whole
+// sequence).
 template <bool HP, int TM>
-DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h, int split, int part)
+DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h, int split, int part, int qs,
+                  int64_t qmap)
 {
     const int kend = min(q0 + BM, L); // keys [0, kend) are needed
     const int nkt = (kend + BN - 1) / BN;
@@ -132,10 +138,11 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h,
     // (B operand of S^T = K Q^T).
     const int qstart = q0 + w * 32; // first query of this wave
     const int qrow = qstart + lq;
-    const bool qvalid = qrow < L;
+    const bool qvalid = qrow < L && qrow >= qs;
+    const bool wact = qstart < L && qstart + 31 >= qs; // the wave has queries (wave-uniform)
     bf16x8 qreg[8];
     {
-        const bf16 *qp = Q + (int64_t)(o_b + (qvalid ? qrow : 0)) * a.ldq + h * D + g * 8;
+        const bf16 *qp = Q + (qvalid ? qmap + qrow : 0) * a.ldq + h * D + g * 8;
 #pragma unroll
         for (int s = 0; s < 8; s++) {
             u32x4 x = qvalid ? *(const u32x4 *)(qp + s * 16) : u32x4{0, 0, 0, 0};
@@ -341,7 +348,7 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h,
 #pragma unroll
         for (int kb = 0; kb < 2; kb++) {
             const int kstart = kt * BN + kb * 32;
-            need[kb] = MAIN ? true : !(kstart > qstart + 31 || qstart >= L); // wave-uniform
+            need[kb] = wact && (MAIN ? true : kstart <= qstart + 31); // wave-uniform
             diag[kb] = MAIN ? false : kstart + 31 > qstart;
         }
         floatx16 sacc0, sacc1;
@@ -397,7 +404,7 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h,
         return;
     }
     if (!qvalid) return;
-    const int64_t row = (int64_t)(o_b + qrow);
+    const int64_t row = qmap + qrow;
 #pragma unroll
     for (int db = 0; db < 4; db++) {
 #pragma unroll
@@ -432,9 +439,15 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
     if (tid < 128) sm.rabt[tid] = has_t ? NLOG2E * a.rab_t[h * a.rt_hs + tid] : 0.f;
     if (tid < 32) sm.rabt_rev[tid] = has_t ? NLOG2E * a.rab_t[h * a.rt_hs + 31 - tid] : 0.f;
     // (the first barrier inside fwd_body orders these table writes before use)
-    if (!has_t) fwd_body<HP, 0>(a, sm, o_b, L, qt * BM, h, split, part);
-    else if (a.wide[b] != 0) fwd_body<HP, 2>(a, sm, o_b, L, qt * BM, h, split, part);
-    else fwd_body<HP, 1>(a, sm, o_b, L, qt * BM, h, split, part);
+    int qs = 0;
+    int64_t qmap = o_b;
+    if (a.aoff) { // appended actions: queries are the new positions [n_b, L)
+        qs = a.hoff[b + 1] - a.hoff[b];
+        qmap = (int64_t)a.aoff[b] - qs;
+    }
+    if (!has_t) fwd_body<HP, 0>(a, sm, o_b, L, qt * BM, h, split, part, qs, qmap);
+    else if (a.wide[b] != 0) fwd_body<HP, 2>(a, sm, o_b, L, qt * BM, h, split, part, qs, qmap);
+    else fwd_body<HP, 1>(a, sm, o_b, L, qt * BM, h, split, part, qs, qmap);
 }
 
 // ---------------------------------------------------------------------------

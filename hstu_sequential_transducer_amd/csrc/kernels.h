@@ -59,6 +59,36 @@ struct SchedBwd {
 void launch_sched(const int32_t *offsets, const int64_t *ts, int B, int T, int tile, int H, int *status, int *n_items,
                   int2 *items, int max_items, uint32_t *rel, int32_t *wide, int32_t *rank, int split_slots, int *t_split,
                   const SchedBwd &bw, hipStream_t st);
+// Appending new actions to cached histories: validates hoff / aoff (first 0,
+// non-decreasing, last = Th / Tn) into *status, writes the merged offsets
+// moff[u] = hoff[u] + aoff[u] (user u's sequence [history; new]) and the
+// work list: items (u, tile t, head h) for the query tiles that hold new
+// positions, t from hoff-length / tile on (the format of launch_sched's).
+// Then one wave per merged row copies that row's K and V -- from the cache
+// (k_cache, v_cache) for history rows, from the new tokens' f1 output (knew,
+// vnew, row aoff[u] + i) for new ones -- into kout / vout, and (when ts are
+// given) its time into ts_m; then the relative times of the merged batch as
+// launch_sched computes them.
+struct AppendPlan {
+    const int32_t *hoff, *aoff;
+    int U, Th, Tn, H, tile, max_items;
+    int *status, *n_items;
+    int2 *items;
+    int32_t *moff;
+    const bf16 *kc, *vc;
+    int64_t ldkc, ldvc;
+    const bf16 *knew, *vnew;
+    int64_t ldnew;
+    bf16 *kout, *vout;
+    int64_t ldko, ldvo;
+    int hd;                     // H * d elements per row
+    const int64_t *ts_h, *ts_a;
+    int64_t *ts_m;
+    uint32_t *rel;
+    int32_t *wide;
+};
+hipError_t launch_append_plan(const AppendPlan &p, hipStream_t st);
+
 // Zeroes the fp32 rows [offsets[b] + tile * t_split, offsets[b + 1]) of
 // every sequence (the rows that split items accumulate into).
 hipError_t launch_zero_split_rows(const int32_t *offsets, int B, int tile, const int *t_split, float *o32, int64_t ld,
@@ -85,6 +115,11 @@ struct AttnFwdArgs {
     int64_t ld_o32;
     void *o16;                  // storage-dtype output or NULL
     int64_t ld_o16;
+    // Appended actions (bf16 kernel; NULL otherwise): sequence b is
+    // [history; new] with hoff[b+1] - hoff[b] history tokens; only its new
+    // positions are queries, and new token i reads Q and writes O at row
+    // aoff[b] + i.
+    const int32_t *hoff, *aoff;
 };
 constexpr int FWD_BM = 128; // query rows per workgroup (bf16 MFMA kernel)
 constexpr int F32_BM = 64;  // query rows per workgroup (fp32 kernel)

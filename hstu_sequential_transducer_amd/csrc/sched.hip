@@ -335,3 +335,118 @@ void launch_sched(const int32_t *offsets, const int64_t *ts, int B, int T, int t
     if (ts && T > 0)
         hipLaunchKernelGGL(reltime_kernel, dim3((T + 255) / 256), dim3(256), 0, st, offsets, ts, rel, wide, B, T, status);
 }
+
+// ---------------------------------------------------------------------------
+// Appending new actions to cached histories (the streaming side of M-FALCON's
+// cacheable history work): one workgroup of 1024 threads validates the two
+// offset arrays, writes the merged offsets and the work list.  User u's
+// sequence is [history (n_u); new (a_u)]; its query tiles holding new
+// positions are t in [n_u / tile, ceil((n_u + a_u) / tile)).  Items are
+// written user by user (block-wide scan of the per-user counts, 1024 users
+// at a time), the highest tile first.
+__global__ void __launch_bounds__(1024) append_plan_kernel(AppendPlan p)
+{
+    __shared__ int bad;
+    __shared__ int cnt[1024];
+    __shared__ int base_s;
+    const int tid = threadIdx.x, U = p.U;
+    if (tid == 0) {
+        bad = (p.hoff[0] != 0 || p.aoff[0] != 0 || p.hoff[U] != p.Th || p.aoff[U] != p.Tn) ? HSTU_DEV_BAD_OFFSETS : 0;
+        base_s = 0;
+    }
+    __syncthreads();
+    for (int u = tid; u < U; u += 1024)
+        if (p.hoff[u + 1] < p.hoff[u] || p.aoff[u + 1] < p.aoff[u]) atomicOr(&bad, HSTU_DEV_BAD_OFFSETS);
+    __syncthreads();
+    if (bad) {
+        if (tid == 0) {
+            *p.status = bad;
+            *p.n_items = 0;
+        }
+        return;
+    }
+    for (int u = tid; u <= U; u += 1024) p.moff[u] = p.hoff[u] + p.aoff[u];
+    for (int u = tid; u < U; u += 1024) p.wide[u] = 0;
+    for (int c0 = 0; c0 < U; c0 += 1024) {
+        const int u = c0 + tid;
+        int t0 = 0, t1 = 0;
+        if (u < U) {
+            const int n = p.hoff[u + 1] - p.hoff[u], a = p.aoff[u + 1] - p.aoff[u];
+            if (a > 0) {
+                t0 = n / p.tile;
+                t1 = (n + a + p.tile - 1) / p.tile;
+            }
+        }
+        const int mine = (t1 - t0) * p.H;
+        cnt[tid] = mine;
+        __syncthreads();
+        for (int o = 1; o < 1024; o <<= 1) { // inclusive scan over the chunk
+            const int v = tid >= o ? cnt[tid - o] : 0;
+            __syncthreads();
+            cnt[tid] += v;
+            __syncthreads();
+        }
+        const int first = base_s + cnt[tid] - mine;
+        for (int k = 0; k < mine; k++) {
+            const int t = t1 - 1 - k / p.H, h = k % p.H;
+            if (first + k < p.max_items) p.items[first + k] = make_int2(u, (t << ITEM_T_SHIFT) | h);
+        }
+        __syncthreads();
+        if (tid == 1023) base_s += cnt[1023];
+        __syncthreads();
+    }
+    if (tid == 0) {
+        *p.n_items = base_s;
+        *p.status = 0;
+    }
+}
+
+// One wave per merged row r (user u, position i): K and V rows (hd bf16
+// elements, 16 bytes per lane and step) from the cache or from the new
+// tokens, and the row's time.
+__global__ void __launch_bounds__(256) append_merge_kernel(AppendPlan p)
+{
+    if (*p.status) return;
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int Tm = p.Th + p.Tn;
+    if (r >= Tm) return;
+    int lo = 0, hi = p.U - 1; // last u with moff[u] <= r
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (p.moff[mid] <= r) lo = mid;
+        else hi = mid - 1;
+    }
+    while (lo < p.U - 1 && p.moff[lo + 1] <= r) lo++; // skip users with nothing
+    const int u = lo;
+    const int64_t i = r - p.moff[u];
+    const int n = p.hoff[u + 1] - p.hoff[u];
+    const bf16 *ks, *vs;
+    if (i < n) {
+        ks = p.kc + (p.hoff[u] + i) * p.ldkc;
+        vs = p.vc + (p.hoff[u] + i) * p.ldvc;
+        if (p.ts_m && lane == 0) p.ts_m[r] = p.ts_h[p.hoff[u] + i];
+    } else {
+        const int64_t rn = p.aoff[u] + (i - n);
+        ks = p.knew + rn * p.ldnew;
+        vs = p.vnew + rn * p.ldnew;
+        if (p.ts_m && lane == 0) p.ts_m[r] = p.ts_a[rn];
+    }
+    for (int c = 8 * lane; c < p.hd; c += 512) {
+        *(u32x4 *)(p.kout + r * p.ldko + c) = *(const u32x4 *)(ks + c);
+        *(u32x4 *)(p.vout + r * p.ldvo + c) = *(const u32x4 *)(vs + c);
+    }
+}
+
+hipError_t launch_append_plan(const AppendPlan &p, hipStream_t st)
+{
+    hipLaunchKernelGGL(append_plan_kernel, dim3(1), dim3(1024), 0, st, p);
+    const int Tm = p.Th + p.Tn;
+    if (Tm > 0) {
+        hipLaunchKernelGGL(append_merge_kernel, dim3((Tm + 3) / 4), dim3(256), 0, st, p);
+        if (p.ts_m)
+            hipLaunchKernelGGL(reltime_kernel, dim3((Tm + 255) / 256), dim3(256), 0, st, p.moff, p.ts_m, p.rel, p.wide,
+                               p.U, Tm, p.status);
+    }
+    return hipGetLastError();
+}

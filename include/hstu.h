@@ -82,7 +82,8 @@ typedef enum {
     HSTU_OP_ATTN_BWD = 1,
     HSTU_OP_LAYER_FWD = 2,
     HSTU_OP_MFALCON = 3,
-    HSTU_OP_LAYER_BWD = 4
+    HSTU_OP_LAYER_BWD = 4,
+    HSTU_OP_LAYER_APPEND = 5
 } hstu_op;
 
 /* A jagged batch.  batch, total and n_max are host values; offsets and ts
@@ -130,9 +131,11 @@ typedef struct {
 } hstu_layer;
 
 /* Bytes of workspace an entry point needs for these sizes.  d_model and
- * total_cand are used by HSTU_OP_LAYER_FWD / HSTU_OP_LAYER_BWD / HSTU_OP_MFALCON
- * (d_model) and HSTU_OP_MFALCON (total_cand) only (pass 0
- * otherwise); for HSTU_OP_MFALCON `j` describes the histories (batch = users).
+ * total_cand are used by HSTU_OP_LAYER_FWD / HSTU_OP_LAYER_BWD /
+ * HSTU_OP_MFALCON / HSTU_OP_LAYER_APPEND (d_model) and HSTU_OP_MFALCON /
+ * HSTU_OP_LAYER_APPEND (total_cand: the candidates', or the new actions',
+ * total) only (pass 0 otherwise); for HSTU_OP_MFALCON and
+ * HSTU_OP_LAYER_APPEND `j` describes the histories (batch = users).
  * Returns 0 and sets hstu_last_error() on invalid sizes. */
 size_t hstu_workspace_size(hstu_op op, const hstu_jagged *j, const hstu_dims *dims, int32_t d_model,
                            int32_t total_cand);
@@ -202,6 +205,33 @@ hstu_status hstu_layer_fwd(const hstu_jagged *j, const hstu_dims *dims, int32_t 
 hstu_status hstu_layer_bwd(const hstu_jagged *j, const hstu_dims *dims, int32_t d_model, const hstu_layer *layer,
                            hstu_cmat x, hstu_cmat dy, hstu_mat dx, float *dw1, float *db1, float *dw2, float *db2,
                            float *drab_p, float *drab_t, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * One layer over new actions appended to cached user histories ([GR review]
+ * §3, M-FALCON: the history's linear and attention computations are
+ * cacheable; the architecture tree's streaming training adds actions as they
+ * arrive).  User u has n_u cached history tokens (this layer's K, V in
+ * k_cache / v_cache, rows hist->offsets[u]..) and a_u new tokens x_new (rows
+ * add->offsets[u]..).  New token i is position n_u + i of the user's
+ * sequence [history; new] with time add->ts[row]: it attends causally to
+ * the whole history and to the new tokens up to itself, so y_new equals rows
+ * n_u.. of hstu_layer_fwd run on the whole sequence.
+ *   hist: U users (batch), total = T_hist, n_max (the model's N_max), ts
+ *     [T_hist] or NULL; add: batch = U, total = T_new, offsets [U+1], ts
+ *     [T_new] (NULL iff hist->ts is NULL); add->n_max is not used.
+ *   k_cache, v_cache [T_hist][H][d] (may be NULL when T_hist = 0).
+ *   x_new [T_new][D] in, y_new [T_new][D] out (may not alias).
+ *   k_out, v_out [T_hist + T_new][H][d] out: the merged caches, user u's
+ *   history rows then its new rows from row hist->offsets[u] +
+ *   add->offsets[u] (the next call's caches, with offsets summed).  They may
+ *   not alias the input caches.
+ * bf16 storage only.  Device-side checks as for the other entry points
+ * (both offset arrays start at 0, do not decrease and end at the totals).
+ */
+hstu_status hstu_layer_append(const hstu_jagged *hist, const hstu_jagged *add, const hstu_dims *dims, int32_t d_model,
+                              const hstu_layer *layer, hstu_cmat k_cache, hstu_cmat v_cache, hstu_cmat x_new,
+                              hstu_mat y_new, hstu_mat k_out, hstu_mat v_out, void *ws, size_t ws_bytes,
+                              void *stream);
 
 /*
  * M-FALCON candidate scoring ([GR review] §3, M-FALCON).  User u has a history

@@ -247,3 +247,32 @@ def mfalcon_64users(seed: int = 4) -> Workload:
     # Drawn from its own stream so the 1-user workload is unchanged.
     return mfalcon_workload("mfalcon-64users-SL-m1024", seed * 1000 + 64, None, cands_per_user=1024,
                             sl=(4096, 1.6), users=64)
+
+
+def append_workload(name: str, seed: int, hist_lengths, add_lengths, *, d_model: int = 512, heads: int = 4,
+                    d: int = 128, n_max: int = 4096, n_layers: int = 1, dtype: str = "bf16") -> Workload:
+    """New actions appended to cached user histories: per user a history of
+    hist_lengths[u] actions (x, ts, which build the cache) and add_lengths[u]
+    new actions (x_new, ts_new) whose times continue the user's history
+    (last history time + cumulative Exp(60) gaps).  The new actions are kept
+    in fields of their own: add_offsets, add_ts, x_new."""
+    rng = np.random.default_rng(seed)
+    hl = np.asarray(hist_lengths, np.int64)
+    al = np.asarray(add_lengths, np.int64)
+    ts = timestamps(rng, hl)
+    offs = offsets_of(hl)
+    add_ts = []
+    for u in range(len(hl)):
+        last = ts[offs[u + 1] - 1] if hl[u] > 0 else EPOCH
+        g = rng.exponential(TIME_GAP_MEAN, size=int(al[u]))
+        add_ts.append(last + np.floor(np.cumsum(g)).astype(np.int64))
+    add_ts = np.concatenate(add_ts) if len(add_ts) else np.zeros(0, np.int64)
+    layers = [_layer(rng, d_model, heads, d, n_max, dtype) for _ in range(n_layers)]
+    x = _normal(rng, (int(hl.sum()), d_model), 1.0, dtype)
+    x_new = _normal(rng, (int(al.sum()), d_model), 1.0, dtype)
+    w = Workload(name=name, dtype=dtype, heads=heads, d=d, n_max=n_max, lengths=hl, offsets=offs, ts=ts,
+                 rab_p=layers[0].rab_p, rab_t=layers[0].rab_t, d_model=d_model, layers=layers, x=x)
+    w.add_offsets = offsets_of(al)
+    w.add_ts = add_ts
+    w.x_new = x_new
+    return w
