@@ -22,7 +22,7 @@ HSTU_ACT_SILU, HSTU_ACT_RELU = 0, 1
 OP_ATTN_FWD, OP_ATTN_BWD, OP_LAYER_FWD, OP_MFALCON, OP_LAYER_BWD, OP_LAYER_APPEND = range(6)
 
 EXPORTED = ["hstu_attn_fwd", "hstu_attn_bwd", "hstu_layer_fwd", "hstu_layer_bwd", "mfalcon_score",
-            "hstu_workspace_size", "hstu_attn_fwd_noalloc", "hstu_layer_append",
+            "hstu_workspace_size", "hstu_attn_fwd_noalloc", "hstu_layer_append", "hstu_softmax_attn_fwd",
             "hstu_profile_enable", "hstu_profile_collect", "hstu_last_error", "hstu_abi_version"]
 
 
@@ -96,6 +96,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hstu_layer_bwd.restype = ctypes.c_int
     lib.hstu_layer_bwd.argtypes = [P(Jagged), P(Dims), ctypes.c_int32, P(Layer), CMat, CMat, Mat] + \
         [ctypes.c_void_p] * 6 + [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.hstu_softmax_attn_fwd.restype = ctypes.c_int
+    lib.hstu_softmax_attn_fwd.argtypes = [P(Jagged), P(Dims), CMat, CMat, CMat, Mat, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_size_t, ctypes.c_void_p]
     lib.hstu_layer_append.restype = ctypes.c_int
     lib.hstu_layer_append.argtypes = [P(Jagged), P(Jagged), P(Dims), ctypes.c_int32, P(Layer), CMat, CMat, CMat, Mat,
                                       Mat, Mat, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
@@ -228,6 +231,26 @@ def attn_fwd(offsets: torch.Tensor, total: int, ts: Optional[torch.Tensor], q: t
     st = lib.hstu_attn_fwd(ctypes.byref(jag), ctypes.byref(dims), ctypes.byref(bias), _rowmat(q, H * d),
                            _rowmat(k, H * d), _rowmat(v, H * d), _rowmat(u, H * d), _rowmat(out, H * d, Mat),
                            _ptr(o_save), _ptr(ln_stats), ws.data_ptr(), ws.numel(), _stream(q.device))
+    _check(st)
+    return out
+
+
+def softmax_attn_fwd(offsets: torch.Tensor, total: int, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, n_max: int,
+                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """hstu_softmax_attn_fwd: causal softmax(Q K^T / sqrt(d)) V (the
+    comparator).  Returns out [T][H*d]."""
+    lib = load_library()
+    T, H, d = q.shape
+    jag = _jagged(offsets, None, n_max, total)
+    dims = Dims(_dtype_code(q), H, d, v.shape[2], 1e-5)
+    if out is None:
+        out = torch.empty((T, H * d), dtype=q.dtype, device=q.device)
+    nws = workspace_size(OP_ATTN_FWD, jag, dims)
+    ws = workspace if workspace is not None else _workspace(nws, q.device)
+    st = lib.hstu_softmax_attn_fwd(ctypes.byref(jag), ctypes.byref(dims), _rowmat(q, H * d), _rowmat(k, H * d),
+                                   _rowmat(v, H * d), _rowmat(out, H * d, Mat), _ptr(lse), ws.data_ptr(), ws.numel(),
+                                   _stream(q.device))
     _check(st)
     return out
 

@@ -699,6 +699,59 @@ hstu_status hstu_attn_fwd(const hstu_jagged *j, const hstu_dims *dm, const hstu_
                                          nullptr);
 }
 
+hstu_status hstu_softmax_attn_fwd(const hstu_jagged *j, const hstu_dims *dm, hstu_cmat q, hstu_cmat k, hstu_cmat v,
+                                  hstu_mat out, float *lse, void *ws, size_t ws_bytes, void *stream)
+{
+    TRY(check_jagged(j));
+    TRY(check_dims(dm));
+    if (dm->dtype != HSTU_BF16) return fail(HSTU_ERR_UNSUPPORTED, "hstu_softmax_attn_fwd supports bf16 storage only");
+    const int H = dm->heads, d = dm->d_qk, F = H * dm->d_v;
+    const struct { const void *p; int64_t ld; int64_t w; const char *n; } views[] = {
+        {q.ptr, q.ld, (int64_t)H * d, "q"}, {k.ptr, k.ld, (int64_t)H * d, "k"}, {v.ptr, v.ld, F, "v"},
+        {out.ptr, out.ld, F, "out"}};
+    for (const auto &x : views) {
+        TRY(check_view(x.p, x.ld, x.w, x.n));
+        TRY(check_vec_view(x.p, x.ld, HSTU_BF16, x.n));
+    }
+    const AttnWs w = attn_ws(j, dm, FWD_BM, false, false);
+    TRY(check_ws(ws, ws_bytes, w.total));
+    hipStream_t st = (hipStream_t)stream;
+    char *wb = (char *)ws;
+    int *status = (int *)(wb + w.header), *n_items = status + 1;
+    int2 *items = (int2 *)(wb + w.items);
+    const int T = j->total, B = j->batch;
+    const int max_items = max_items_for(B, T, FWD_BM, H);
+    {
+        ProfScope ps("sched_kernel", st);
+        launch_sched(j->offsets, nullptr, B, T, FWD_BM, H, status, n_items, items, max_items, (uint32_t *)(wb + w.rel),
+                     (int32_t *)(wb + w.wide), (int32_t *)(wb + w.rank), 0, nullptr, SchedBwd{}, st);
+    }
+    TRY(launched(hipGetLastError(), "schedule kernel"));
+    AttnFwdArgs a{};
+    a.q = q.ptr;
+    a.k = k.ptr;
+    a.v = v.ptr;
+    a.ldq = q.ld;
+    a.ldk = k.ld;
+    a.ldv = v.ld;
+    a.offsets = j->offsets;
+    a.wide = (int32_t *)(wb + w.wide);
+    a.H = H;
+    a.N = j->n_max;
+    a.d = d;
+    a.items = items;
+    a.n_items = n_items;
+    a.o16 = out.ptr;
+    a.ld_o16 = out.ld;
+    a.lse = lse;
+    {
+        ProfScope ps("attn_softmax_fwd_kernel", st);
+        TRY(launched(launch_attn_softmax_fwd(a, max_items, st), "softmax attention kernel"));
+    }
+    TRY(debug_check(ws, st));
+    return ok();
+}
+
 hstu_status hstu_attn_bwd(const hstu_jagged *j, const hstu_dims *dm, const hstu_bias *bias, hstu_cmat q, hstu_cmat k,
                           hstu_cmat v, hstu_cmat u, const float *o_save, const float *ln_stats, hstu_cmat dout,
                           hstu_mat dq, hstu_mat dk, hstu_mat dv, hstu_mat du, float *drab_p, float *drab_t, void *ws,

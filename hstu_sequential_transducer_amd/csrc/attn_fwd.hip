@@ -122,7 +122,42 @@ DEV void pointwise(const floatx16 &sacc, uint32_t (&pk)[8], const uint32_t *kt_l
 // sequence is [history; new] and only the new positions are queries), and
 // query position p reads Q and writes O at row qmap + p (o_b for a whole
 // sequence).
-template <bool HP, int TM>
+// Softmax elements of one 32x32 block (the comparator, SM): P' = 2^(s c - m)
+// with the tile's running max m (scaled domain), masked pairs exactly 0;
+// the lane's share of the row sum goes to lsum.
+template <bool DIAG>
+DEV void pointwise_softmax(const floatx16 &sacc, uint32_t (&pk)[8], float c, float m, float &lsum, int dmask)
+{
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+        float p2[2];
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+            const int rr = r + u, koff = 8 * (rr >> 2) + (rr & 3);
+            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[rr], c, -m));
+            if constexpr (DIAG) p = koff > dmask ? 0.f : p;
+            lsum += p;
+            p2[u] = p;
+        }
+        pk[r >> 1] = pack2_bf16(p2[0], p2[1]);
+    }
+}
+
+// The largest scaled score of a block among the lane's unmasked pairs.
+template <bool DIAG>
+DEV float block_max(const floatx16 &sacc, float c, int dmask)
+{
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int rr = 0; rr < 16; rr++) {
+        const int koff = 8 * (rr >> 2) + (rr & 3);
+        const float x = sacc[rr] * c;
+        mx = (DIAG && koff > dmask) ? mx : fmaxf(mx, x);
+    }
+    return mx;
+}
+
+template <bool HP, int TM, bool SM = false>
 DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h, int split, int part, int qs,
                   int64_t qmap)
 {
@@ -163,6 +198,10 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h,
     for (int i = 0; i < 4; i++)
 #pragma unroll
         for (int r = 0; r < 16; r++) oacc[i][r] = 0.f;
+    // softmax comparator: running max (scaled by c = log2(e) / sqrt(d)) and
+    // this lane's share of the row sum
+    const float sm_c = 1.4426950408889634f * __builtin_amdgcn_rsqf((float)D);
+    float sm_m = -__builtin_inff(), sm_l = 0.f;
 
     // ---- tile loader: every copy goes global -> LDS directly.  K and V:
     // 32 groups of 4 rows, 8 per wave; lane l fills physical chunk l%16 of
@@ -353,13 +392,44 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h,
         }
         floatx16 sacc0, sacc1;
         uint32_t pk0[8], pk1[8];
-        if (need[0]) {
-            s_block(S, 0, sacc0);
-            pw_block(S, kt, 0, sacc0, pk0, diag[0], kmn[0], kmx[0]);
-        }
-        if (need[1]) {
-            s_block(S, 1, sacc1);
-            pw_block(S, kt, 1, sacc1, pk1, diag[1], kmn[1], kmx[1]);
+        if constexpr (SM) {
+            // online softmax over the tile: both blocks' scores, the tile's
+            // max (shared by the two lanes of a query), the rescale of the
+            // running sum and of O when the max grew, then P of both blocks
+            if (need[0]) s_block(S, 0, sacc0);
+            if (need[1]) s_block(S, 1, sacc1);
+            float mx = -__builtin_inff();
+            if (need[0]) mx = diag[0] ? block_max<true>(sacc0, sm_c, lq - 4 * g) : block_max<false>(sacc0, sm_c, 0);
+            if (need[1])
+                mx = fmaxf(mx, diag[1] ? block_max<true>(sacc1, sm_c, lq - 4 * g) : block_max<false>(sacc1, sm_c, 0));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float m_new = fmaxf(sm_m, mx);
+            if (__any(m_new > sm_m)) { // wave-uniform: some query's max grew
+                const float alpha = __builtin_amdgcn_exp2f(sm_m - m_new);
+                sm_l *= alpha;
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+#pragma unroll
+                    for (int r = 0; r < 16; r++) oacc[i][r] *= alpha;
+                sm_m = m_new;
+            }
+            if (need[0]) {
+                if (diag[0]) pointwise_softmax<true>(sacc0, pk0, sm_c, sm_m, sm_l, lq - 4 * g);
+                else pointwise_softmax<false>(sacc0, pk0, sm_c, sm_m, sm_l, 0);
+            }
+            if (need[1]) {
+                if (diag[1]) pointwise_softmax<true>(sacc1, pk1, sm_c, sm_m, sm_l, lq - 4 * g);
+                else pointwise_softmax<false>(sacc1, pk1, sm_c, sm_m, sm_l, 0);
+            }
+        } else {
+            if (need[0]) {
+                s_block(S, 0, sacc0);
+                pw_block(S, kt, 0, sacc0, pk0, diag[0], kmn[0], kmx[0]);
+            }
+            if (need[1]) {
+                s_block(S, 1, sacc1);
+                pw_block(S, kt, 1, sacc1, pk1, diag[1], kmn[1], kmx[1]);
+            }
         }
         if (need[0]) o_block(S, 0, pk0);
         if (need[1]) o_block(S, 1, pk1);
@@ -403,6 +473,12 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h,
         }
         return;
     }
+    float osc = sc;
+    if constexpr (SM) {
+        const float lt = sm_l + __shfl_xor(sm_l, 32, 64); // the query's whole row sum
+        osc = 1.0f / lt;
+        if (qvalid && g == 0 && a.lse) a.lse[(qmap + qrow) * a.H + h] = (sm_m + __log2f(lt)) * 0.69314718055994531f;
+    }
     if (!qvalid) return;
     const int64_t row = qmap + qrow;
 #pragma unroll
@@ -410,8 +486,8 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h,
 #pragma unroll
         for (int gr = 0; gr < 4; gr++) {
             const int d0 = db * 32 + 8 * gr + 4 * g;
-            floatx4 o4 = {oacc[db][4 * gr] * sc, oacc[db][4 * gr + 1] * sc, oacc[db][4 * gr + 2] * sc,
-                          oacc[db][4 * gr + 3] * sc};
+            floatx4 o4 = {oacc[db][4 * gr] * osc, oacc[db][4 * gr + 1] * osc, oacc[db][4 * gr + 2] * osc,
+                          oacc[db][4 * gr + 3] * osc};
             if (a.o32) *(floatx4 *)(a.o32 + row * a.ld_o32 + h * D + d0) = o4;
             if (a.o16) {
                 u32x2 pk2 = {pack2_bf16(o4[0], o4[1]), pack2_bf16(o4[2], o4[3])};
@@ -448,6 +524,22 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
     if (!has_t) fwd_body<HP, 0>(a, sm, o_b, L, qt * BM, h, split, part, qs, qmap);
     else if (a.wide[b] != 0) fwd_body<HP, 2>(a, sm, o_b, L, qt * BM, h, split, part, qs, qmap);
     else fwd_body<HP, 1>(a, sm, o_b, L, qt * BM, h, split, part, qs, qmap);
+}
+
+// The comparator: causal softmax attention O = softmax(Q K^T / sqrt(d)) V on
+// the same skeleton (no bias, no gate, never split), for the pages'
+// comparison of pointwise aggregated attention with softmax attention.
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_softmax_fwd_kernel(AttnFwdArgs a)
+{
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    Smem &sm = *reinterpret_cast<Smem *>(smem_raw);
+    const int item = blockIdx.x;
+    if (item >= *a.n_items) return;
+    const int2 it = a.items[item];
+    const int b = it.x, qt = it.y >> ITEM_T_SHIFT, h = it.y & 255;
+    const int o_b = a.offsets[b];
+    const int L = a.offsets[b + 1] - o_b;
+    fwd_body<false, 0, true>(a, sm, o_b, L, qt * BM, h, 0, 0, 0, o_b);
 }
 
 // ---------------------------------------------------------------------------
@@ -537,6 +629,21 @@ hipError_t launch_attn_fwd_bf16(const AttnFwdArgs &a, int max_items, hipStream_t
     if (max_items <= 0) return hipSuccess;
     if (a.rab_p) hipLaunchKernelGGL(attn_fwd_bf16_kernel<true>, dim3(max_items), dim3(NT), smem, st, a);
     else hipLaunchKernelGGL(attn_fwd_bf16_kernel<false>, dim3(max_items), dim3(NT), smem, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_softmax_fwd(const AttnFwdArgs &a, int max_items, hipStream_t st)
+{
+    static bool init = false;
+    const size_t smem = sizeof(Smem);
+    if (!init) {
+        hipError_t e = hipFuncSetAttribute((const void *)attn_softmax_fwd_kernel,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        if (e != hipSuccess) return e;
+        init = true;
+    }
+    if (max_items <= 0) return hipSuccess;
+    hipLaunchKernelGGL(attn_softmax_fwd_kernel, dim3(max_items), dim3(NT), smem, st, a);
     return hipGetLastError();
 }
 

@@ -120,8 +120,13 @@ struct AttnFwdArgs {
     // positions are queries, and new token i reads Q and writes O at row
     // aoff[b] + i.
     const int32_t *hoff, *aoff;
+    float *lse;                 // softmax comparator: per (row, head) log-sum-exp [T][H], or NULL
 };
 constexpr int FWD_BM = 128; // query rows per workgroup (bf16 MFMA kernel)
+// Causal softmax attention softmax(Q K^T / sqrt(d)) V, bf16, d = 128, on the
+// forward's skeleton (the comparator of pointwise aggregated attention):
+// items from launch_sched without splits; o16 (and o32 if given) written.
+hipError_t launch_attn_softmax_fwd(const AttnFwdArgs &a, int max_items, hipStream_t st);
 constexpr int F32_BM = 64;  // query rows per workgroup (fp32 kernel)
 hipError_t launch_attn_fwd_bf16(const AttnFwdArgs &a, int max_items, hipStream_t st);
 hipError_t launch_attn_fwd_f32(const AttnFwdArgs &a, int max_items, hipStream_t st);

@@ -154,6 +154,21 @@ hstu_status hstu_attn_fwd(const hstu_jagged *j, const hstu_dims *dims, const hst
                           void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * The comparator of pointwise aggregated attention: causal softmax attention
+ * O = softmax(Q K^T / sqrt(d)) V per sequence and head, with no relative
+ * bias and no gate -- the "softmax, no rab" row of [GR review] §6's
+ * component ablation and the attention of the Transformer baseline of §5's
+ * efficiency table -- computed on the same kernel skeleton as
+ * hstu_attn_fwd (same tiles, work list and operand path; the element-wise
+ * step is an online softmax), so that the two can be timed side by side.
+ *   q, k, v [T][H][d], out [T][H*d] (bf16 only, d = 128); lse (optional,
+ *   fp32 [T][H]): the natural log of each row's sum of exp(s - max) plus the
+ *   max, for a backward.  Workspace: hstu_workspace_size(HSTU_OP_ATTN_FWD).
+ */
+hstu_status hstu_softmax_attn_fwd(const hstu_jagged *j, const hstu_dims *dims, hstu_cmat q, hstu_cmat k,
+                                  hstu_cmat v, hstu_mat out, float *lse, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * Backward of hstu_attn_fwd (chain rule through Eq. 3's Norm (.) U and
  * Eq. 2).  bf16 only.
  *   dout: upstream gradient at G when u is given (then o_save and ln_stats

@@ -283,3 +283,19 @@ def layer_append(hist_offsets, hist_ts, add_offsets, add_ts, layer, kv_cache, x_
                             _p(_d(layer.rab_p)), _p(_d(layer.rab_t)), ctypes.c_int(phi1), ctypes.c_double(eps),
                             _p(_d(kv_cache)), _p(X), _p(y), _p(kv_out))
     return y, kv_out
+
+
+def softmax_attn_fwd(offsets, q, k, v, want_lse: bool = False):
+    """The comparator: causal softmax(Q K^T / sqrt(d)) V per sequence and
+    head (no bias).  Returns O [T][H*dv] (and lse [T][H] if asked)."""
+    lib = _load()
+    off = _i32(offsets)
+    B = len(off) - 1
+    q, k, v = _d(q), _d(k), _d(v)
+    T, H, dqk = q.shape
+    dv = v.shape[2]
+    out = np.zeros((T, H * dv))
+    lse = np.zeros((T, H)) if want_lse else None
+    lib.oracle_softmax_attn_fwd(ctypes.c_int(B), _p(off), ctypes.c_int(H), ctypes.c_int(dqk), ctypes.c_int(dv), _p(q),
+                                _p(k), _p(v), _p(out), _p(lse))
+    return (out, lse) if want_lse else out

@@ -710,4 +710,47 @@ void oracle_layer_append(int U, const int32_t *hist_off, const int64_t *hist_ts,
     free(A);
 }
 
+/*
+ * The comparator the pages set pointwise aggregated attention against
+ * ([GR review] §5 efficiency table: Transformers built on FlashAttention2;
+ * §6 component ablation: softmax in place of the pointwise normalisation,
+ * without rab): causal softmax attention per sequence b, head h and query
+ * i, with the usual 1/sqrt(d) scale,
+ *   s_ij = q_i . k_j / sqrt(dqk) for j <= i,
+ *   O_i  = sum_j exp(s_ij - max_j s_ij) v_j / sum_j exp(s_ij - max_j s_ij).
+ * lse (optional, [T][H]): max_j s_ij + log(sum_j exp(s_ij - max_j s_ij)).
+ */
+void oracle_softmax_attn_fwd(int B, const int32_t *off, int H, int dqk, int dv, const double *q, const double *k,
+                             const double *v, double *out, double *lse)
+{
+    int64_t T = off[B];
+    double scale = 1.0 / sqrt((double)dqk);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t w = 0; w < T * H; w++) {
+        int64_t r = w / H;
+        int h = (int)(w % H);
+        int b = seq_of(B, off, r);
+        int64_t o_b = off[b], i = r - o_b;
+        double *s = (double *)malloc(sizeof(double) * (size_t)(i + 1));
+        double mx = -INFINITY;
+        for (int64_t j = 0; j <= i; j++) {
+            double x = 0.0;
+            for (int c = 0; c < dqk; c++) x += q[(r * H + h) * dqk + c] * k[((o_b + j) * H + h) * dqk + c];
+            s[j] = x * scale;
+            if (s[j] > mx) mx = s[j];
+        }
+        double den = 0.0;
+        double *acc = out + r * (int64_t)H * dv + (int64_t)h * dv;
+        for (int c = 0; c < dv; c++) acc[c] = 0.0;
+        for (int64_t j = 0; j <= i; j++) {
+            double p = exp(s[j] - mx);
+            den += p;
+            for (int c = 0; c < dv; c++) acc[c] += p * v[((o_b + j) * H + h) * dv + c];
+        }
+        for (int c = 0; c < dv; c++) acc[c] /= den;
+        if (lse) lse[r * H + h] = mx + log(den);
+        free(s);
+    }
+}
+
 int oracle_abi_version(void) { return 1; }

@@ -55,6 +55,10 @@ MUTANTS = [
     ("append-no-history", "for (int64_t j = 0; j < nu; j++) { /* the cached history */",
      "for (int64_t j = 0; j < nu - 1; j++) { /* the cached history */"),
     ("append-merged-offset", "int64_t mo = ho + ao;", "int64_t mo = ho;"),
+    ("softmax-no-scale", "double scale = 1.0 / sqrt((double)dqk);", "double scale = 1.0;"),
+    ("softmax-strict-causal", "for (int64_t j = 0; j <= i; j++) {\n            double x = 0.0;",
+     "for (int64_t j = 0; j < i; j++) {\n            double x = 0.0;"),
+    ("softmax-no-denominator", "for (int c = 0; c < dv; c++) acc[c] /= den;", "for (int c = 0; c < dv; c++) acc[c] /= 1.0;"),
     ("append-new-time", "have_t ? add_ts[r] : 0, have_t ? add_ts[rk] : 0, have_t);",
      "have_t ? add_ts[r] : 0, have_t ? add_ts[r] : 0, have_t);"),
 ]
@@ -76,6 +80,8 @@ PINS = [
     (pins.test_layer_bwd_residual_and_bias_identities, {}),
     (pins.test_layer_bwd_finite_differences, dict(phi1=0)),
     (pins.test_layer_append_equals_full_forward, {}),
+    (pins.test_softmax_comparator_against_library_softmax, {}),
+    (pins.test_softmax_comparator_closed_forms, {}),
 ]
 
 

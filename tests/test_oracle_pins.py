@@ -535,3 +535,52 @@ def test_inputs_deterministic():
     assert np.array_equal(a.q, b.q) and np.array_equal(a.ts, b.ts) and np.array_equal(a.rab_p, b.rab_p)
     w = synth.tiny_layer_f32()
     assert list(w.lengths) == [17, 64, 33, 5] and w.total == 119
+
+
+# ---------------------------------------------------------------- softmax comparator
+
+def test_softmax_comparator_against_library_softmax():
+    """The comparator equals a dense formulation built from scipy's softmax
+    with an explicit causal mask, on random tiny ragged batches."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(30)
+    for trial in range(10):
+        L = rng.integers(0, 9, size=rng.integers(1, 4))
+        H, d = int(rng.integers(1, 3)), int(rng.choice([1, 4, 8]))
+        off = synth.offsets_of(L)
+        T = int(off[-1])
+        q, k, v = (rng.standard_normal((T, H, d)) for _ in range(3))
+        got, lse = oracle.softmax_attn_fwd(off, q, k, v, want_lse=True)
+        for b in range(len(L)):
+            o, n = int(off[b]), int(L[b])
+            for h in range(H):
+                S = q[o:o + n, h] @ k[o:o + n, h].T / math.sqrt(d)
+                S = np.where(np.tril(np.ones((n, n), bool)), S, -np.inf)
+                P = softmax(S, axis=1) if n else S
+                ref = P @ v[o:o + n, h] if n else np.zeros((0, d))
+                assert np.allclose(got[o:o + n, h * d:(h + 1) * d], ref, rtol=1e-12, atol=1e-12)
+                if n:
+                    m = S.max(axis=1)
+                    assert np.allclose(lse[o:o + n, h], m + np.log(np.exp(S - m[:, None]).sum(axis=1)), rtol=1e-12)
+
+
+def test_softmax_comparator_closed_forms():
+    """Q = 0: every key weighs the same, O_i is the mean of V_0..V_i (a
+    prefix mean).  Adding one vector t to every key of a sequence shifts each
+    row's scores by q_i.t and leaves O unchanged.  V = 1 gives O = 1."""
+    rng = np.random.default_rng(31)
+    L = np.array([7, 1, 12])
+    off = synth.offsets_of(L)
+    T, H, d = int(off[-1]), 2, 4
+    q, k, v = (rng.standard_normal((T, H, d)) for _ in range(3))
+    o0 = oracle.softmax_attn_fwd(off, np.zeros_like(q), k, v)
+    for b in range(3):
+        s, n = int(off[b]), int(L[b])
+        pm = np.cumsum(v[s:s + n], axis=0) / np.arange(1, n + 1)[:, None, None]
+        assert np.allclose(o0[s:s + n].reshape(n, H, d), pm, rtol=1e-12, atol=1e-12)
+    base = oracle.softmax_attn_fwd(off, q, k, v)
+    k2 = k.copy()
+    for b in range(3):
+        k2[off[b]:off[b + 1]] += rng.standard_normal((1, H, d)) * 3
+    assert np.allclose(oracle.softmax_attn_fwd(off, q, k2, v), base, rtol=1e-10, atol=1e-10)
+    assert np.allclose(oracle.softmax_attn_fwd(off, q, k, np.ones_like(v)), 1.0, rtol=1e-13, atol=1e-13)
