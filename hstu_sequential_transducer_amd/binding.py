@@ -23,6 +23,7 @@ OP_ATTN_FWD, OP_ATTN_BWD, OP_LAYER_FWD, OP_MFALCON, OP_LAYER_BWD, OP_LAYER_APPEN
 
 EXPORTED = ["hstu_attn_fwd", "hstu_attn_bwd", "hstu_layer_fwd", "hstu_layer_bwd", "mfalcon_score",
             "hstu_workspace_size", "hstu_attn_fwd_noalloc", "hstu_layer_append", "hstu_softmax_attn_fwd",
+            "hstu_sl_sample",
             "hstu_profile_enable", "hstu_profile_collect", "hstu_last_error", "hstu_abi_version"]
 
 
@@ -99,6 +100,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hstu_softmax_attn_fwd.restype = ctypes.c_int
     lib.hstu_softmax_attn_fwd.argtypes = [P(Jagged), P(Dims), CMat, CMat, CMat, Mat, ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_size_t, ctypes.c_void_p]
+    lib.hstu_sl_sample.restype = ctypes.c_int
+    lib.hstu_sl_sample.argtypes = [P(Jagged), ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.hstu_layer_append.restype = ctypes.c_int
     lib.hstu_layer_append.argtypes = [P(Jagged), P(Jagged), P(Dims), ctypes.c_int32, P(Layer), CMat, CMat, CMat, Mat,
                                       Mat, Mat, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
@@ -233,6 +238,33 @@ def attn_fwd(offsets: torch.Tensor, total: int, ts: Optional[torch.Tensor], q: t
                            _ptr(o_save), _ptr(ln_stats), ws.data_ptr(), ws.numel(), _stream(q.device))
     _check(st)
     return out
+
+
+def sl_sample(offsets: torch.Tensor, total: int, ts: Optional[torch.Tensor], alpha: float, u: torch.Tensor,
+              keys: torch.Tensor, x: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """hstu_sl_sample.  u: fp64 [B]; keys: int32 [T] read as uint32.
+    Returns (out_offsets [B+1], out_index [T] (first out_offsets[B] valid),
+    x_out [T][...] or None, ts_out [T] or None)."""
+    lib = load_library()
+    jag = _jagged(offsets, ts, 1, total)
+    if u.dtype != torch.float64 or keys.dtype != torch.int32:
+        raise ValueError("u must be float64 and keys int32 (bits read as uint32)")
+    dev_ = offsets.device
+    T = int(total)
+    B = offsets.numel() - 1
+    out_off = torch.empty(B + 1, dtype=torch.int32, device=dev_)
+    out_idx = torch.empty(max(T, 1), dtype=torch.int32, device=dev_)
+    x_out = torch.empty_like(x) if x is not None else None
+    ts_out = torch.empty(max(T, 1), dtype=torch.int64, device=dev_) if ts is not None else None
+    es = x.element_size() if x is not None else 0
+    ws = workspace if workspace is not None else _workspace(256, dev_)
+    st = lib.hstu_sl_sample(ctypes.byref(jag), float(alpha), u.data_ptr(), keys.data_ptr(), _ptr(x),
+                            x.stride(0) * es if x is not None else 0, x.shape[1] * es if x is not None else 0,
+                            out_off.data_ptr(), out_idx.data_ptr(), _ptr(x_out),
+                            x_out.stride(0) * es if x_out is not None else 0, _ptr(ts_out), ws.data_ptr(), ws.numel(),
+                            _stream(dev_))
+    _check(st)
+    return out_off, out_idx, x_out, ts_out
 
 
 def softmax_attn_fwd(offsets: torch.Tensor, total: int, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, n_max: int,

@@ -699,6 +699,47 @@ hstu_status hstu_attn_fwd(const hstu_jagged *j, const hstu_dims *dm, const hstu_
                                          nullptr);
 }
 
+hstu_status hstu_sl_sample(const hstu_jagged *in, double alpha, const double *u, const uint32_t *keys, const void *x,
+                           int64_t ldx, int32_t row_bytes, int32_t *out_offsets, int32_t *out_index, void *x_out,
+                           int64_t ldx_out, int64_t *ts_out, void *ws, size_t ws_bytes, void *stream)
+{
+    TRY(check_jagged(in));
+    if (!(alpha > 0.0)) return fail(HSTU_ERR_ARG, "alpha must be > 0");
+    if (!u || !keys) return fail(HSTU_ERR_ARG, "u and keys are required");
+    if (!out_offsets || !out_index) return fail(HSTU_ERR_ARG, "out_offsets and out_index are required");
+    if (x) {
+        if (!x_out) return fail(HSTU_ERR_ARG, "x_out is required with x");
+        if (row_bytes < 1) return fail(HSTU_ERR_ARG, "row_bytes must be >= 1");
+        if (ldx < row_bytes || ldx_out < row_bytes) return fail(HSTU_ERR_ARG, "ldx and ldx_out must be >= row_bytes");
+    }
+    if (ts_out && !in->ts) return fail(HSTU_ERR_ARG, "ts_out needs in->ts");
+    TRY(check_ws(ws, ws_bytes, 256));
+    SlArgs a{};
+    a.offsets = in->offsets;
+    a.B = in->batch;
+    a.T = in->total;
+    a.alpha = alpha;
+    a.u = u;
+    a.keys = keys;
+    a.out_off = out_offsets;
+    a.out_idx = out_index;
+    a.x = x;
+    a.ldx_bytes = ldx;
+    a.y = x_out;
+    a.ldy_bytes = ldx_out;
+    a.row_bytes = row_bytes;
+    a.ts = in->ts;
+    a.ts_out = ts_out;
+    a.status = (int *)ws;
+    hipStream_t st = (hipStream_t)stream;
+    {
+        ProfScope ps("sl_sample_kernels", st);
+        TRY(launched(launch_sl_sample(a, st), "Stochastic Length kernels"));
+    }
+    TRY(debug_check(ws, st));
+    return ok();
+}
+
 hstu_status hstu_softmax_attn_fwd(const hstu_jagged *j, const hstu_dims *dm, hstu_cmat q, hstu_cmat k, hstu_cmat v,
                                   hstu_mat out, float *lse, void *ws, size_t ws_bytes, void *stream)
 {

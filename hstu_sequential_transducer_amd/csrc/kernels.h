@@ -310,3 +310,23 @@ hipError_t launch_mfalcon_attn(const MfalconArgs &a, int max_items, bool bf16io,
 hipError_t launch_mfalcon_epilogue(const float *part, int nsplit, const void *Z, int64_t ldz, const float *rab_p,
                                    int64_t rp_hs, const float *rab_t, int64_t rt_hs, bool use_t, int N, float eps,
                                    void *G, int64_t ldg, int M, int H, int d, bool bf16io, hipStream_t st);
+
+// ---- Stochastic Length sampling as a device gather (sl.hip)
+struct SlArgs {
+    const int32_t *offsets;     // input batch [B+1]
+    int B, T;
+    double alpha;
+    const double *u;            // [B] in (0, 1]
+    const uint32_t *keys;       // [T]
+    int32_t *out_off;           // [B+1]
+    int32_t *out_idx;           // [T] capacity (first out_off[B] written)
+    const void *x;              // rows to gather, or NULL
+    int64_t ldx_bytes;
+    void *y;
+    int64_t ldy_bytes;
+    int64_t row_bytes;
+    const int64_t *ts;          // [T] or NULL
+    int64_t *ts_out;            // [T] capacity or NULL
+    int *status;
+};
+hipError_t launch_sl_sample(const SlArgs &a, hipStream_t st);

@@ -154,6 +154,30 @@ hstu_status hstu_attn_fwd(const hstu_jagged *j, const hstu_dims *dims, const hst
                           void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Stochastic Length ([GR review] §3, Stochastic Length): builds the sampled
+ * jagged batch from full user histories.  Sequence b of `in` (n_b actions)
+ * keeps L_b = min(n_b, ceil(n_b u_b^(1/alpha))) of them (at least 1 when
+ * n_b > 0), a random subsequence: the L_b actions with the smallest keys
+ * (ties by position), in their original order -- a uniformly random subset
+ * for uniform keys (the pages give the length law and say the subsequence
+ * is random; this selection rule is the plain reading).  L_b is computed in
+ * fp64.
+ *   u: device fp64 [B] in (0, 1]; keys: device uint32 [T] (the random
+ *   numbers, drawn by the caller).
+ *   out_offsets: device int32 [B+1], the sampled batch's offsets;
+ *   out_index: device int32 [T] capacity, the first out_offsets[B] entries
+ *   are each sampled action's row in `in`.
+ *   x (optional): rows to gather, row_bytes bytes each with a stride of ldx
+ *   bytes, into x_out (stride ldx_out bytes, T rows of capacity); ts_out
+ *   (optional, int64 [T] capacity) gathers in->ts.
+ *   Workspace: 256 bytes (a status word).  The sampled total is known on
+ *   the device only (out_offsets[B]); nothing is copied to the host.
+ */
+hstu_status hstu_sl_sample(const hstu_jagged *in, double alpha, const double *u, const uint32_t *keys, const void *x,
+                           int64_t ldx, int32_t row_bytes, int32_t *out_offsets, int32_t *out_index, void *x_out,
+                           int64_t ldx_out, int64_t *ts_out, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * The comparator of pointwise aggregated attention: causal softmax attention
  * O = softmax(Q K^T / sqrt(d)) V per sequence and head, with no relative
  * bias and no gate -- the "softmax, no rab" row of [GR review] §6's

@@ -299,3 +299,18 @@ def softmax_attn_fwd(offsets, q, k, v, want_lse: bool = False):
     lib.oracle_softmax_attn_fwd(ctypes.c_int(B), _p(off), ctypes.c_int(H), ctypes.c_int(dqk), ctypes.c_int(dv), _p(q),
                                 _p(k), _p(v), _p(out), _p(lse))
     return (out, lse) if want_lse else out
+
+
+def sl_sample(offsets, alpha: float, u, keys):
+    """Stochastic Length sampling: per sequence a length from the SL law and
+    the actions with the L smallest keys, in order.  Returns (out_offsets
+    [B+1] int32, out_index [out_offsets[B]] int32 rows of the input)."""
+    lib = _load()
+    off = _i32(offsets)
+    B = len(off) - 1
+    ua = np.ascontiguousarray(u, dtype=np.float64)
+    ka = np.ascontiguousarray(keys, dtype=np.uint32)
+    out_off = np.zeros(B + 1, np.int32)
+    out_idx = np.zeros(max(1, int(off[-1])), np.int32)
+    lib.oracle_sl_sample(ctypes.c_int(B), _p(off), ctypes.c_double(alpha), _p(ua), _p(ka), _p(out_off), _p(out_idx))
+    return out_off, out_idx[:int(out_off[-1])]

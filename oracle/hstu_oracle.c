@@ -753,4 +753,37 @@ void oracle_softmax_attn_fwd(int B, const int32_t *off, int H, int dqk, int dv, 
     }
 }
 
+/*
+ * Stochastic Length ([GR review] §3 SL: each user's history is cut to a
+ * length drawn from L = min(n, ceil(n u^(1/alpha))), u ~ U(0, 1), and a
+ * random subsequence of that length is kept).  Readings: a length is at least
+ * 1 for a non-empty history; the subsequence is a uniformly random subset of
+ * L of the n actions kept in their original order, drawn as the L actions
+ * with the smallest random keys (ties by position).  The random numbers (u
+ * per sequence, a uint32 key per action) are inputs.  Outputs: out_off [B+1]
+ * (the sampled batch's offsets) and out_idx [out_off[B]] (for each sampled
+ * action, its row in the input batch).  A plain O(n^2) rank count per action.
+ */
+void oracle_sl_sample(int B, const int32_t *off, double alpha, const double *u, const uint32_t *keys,
+                      int32_t *out_off, int32_t *out_idx)
+{
+    out_off[0] = 0;
+    for (int b = 0; b < B; b++) {
+        int64_t o = off[b], n = off[b + 1] - off[b];
+        int64_t L = 0;
+        if (n > 0) {
+            double x = ceil((double)n * pow(u[b], 1.0 / alpha));
+            L = x < 1.0 ? 1 : (x > (double)n ? n : (int64_t)x);
+        }
+        int64_t w = out_off[b];
+        for (int64_t j = 0; j < n; j++) {
+            int64_t rank = 0; /* actions before j in (key, position) order */
+            for (int64_t i = 0; i < n; i++)
+                if (keys[o + i] < keys[o + j] || (keys[o + i] == keys[o + j] && i < j)) rank++;
+            if (rank < L) out_idx[w++] = (int32_t)(o + j);
+        }
+        out_off[b + 1] = (int32_t)w;
+    }
+}
+
 int oracle_abi_version(void) { return 1; }

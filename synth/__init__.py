@@ -276,3 +276,15 @@ def append_workload(name: str, seed: int, hist_lengths, add_lengths, *, d_model:
     w.add_ts = add_ts
     w.x_new = x_new
     return w
+
+
+def sl_draws(seed: int, lengths, distinct_keys: int = 0):
+    """The random numbers of Stochastic Length sampling for sequences of the
+    given full lengths: u ~ U(0, 1) per sequence (fp64) and a uint32 key per
+    action (uniform; or uniform over `distinct_keys` values, to force ties)."""
+    rng = np.random.default_rng(seed)
+    L = np.asarray(lengths, np.int64)
+    u = rng.random(len(L))
+    hi = distinct_keys if distinct_keys > 0 else 2 ** 32
+    keys = rng.integers(0, hi, size=int(L.sum()), dtype=np.uint64).astype(np.uint32)
+    return u, keys

@@ -59,6 +59,10 @@ MUTANTS = [
     ("softmax-strict-causal", "for (int64_t j = 0; j <= i; j++) {\n            double x = 0.0;",
      "for (int64_t j = 0; j < i; j++) {\n            double x = 0.0;"),
     ("softmax-no-denominator", "for (int c = 0; c < dv; c++) acc[c] /= den;", "for (int c = 0; c < dv; c++) acc[c] /= 1.0;"),
+    ("sl-floor-length", "double x = ceil((double)n * pow(u[b], 1.0 / alpha));",
+     "double x = floor((double)n * pow(u[b], 1.0 / alpha));"),
+    ("sl-ties-reversed", "(keys[o + i] == keys[o + j] && i < j)", "(keys[o + i] == keys[o + j] && i > j)"),
+    ("sl-largest-keys", "if (keys[o + i] < keys[o + j] ||", "if (keys[o + i] > keys[o + j] ||"),
     ("append-new-time", "have_t ? add_ts[r] : 0, have_t ? add_ts[rk] : 0, have_t);",
      "have_t ? add_ts[r] : 0, have_t ? add_ts[r] : 0, have_t);"),
 ]
@@ -82,6 +86,7 @@ PINS = [
     (pins.test_layer_append_equals_full_forward, {}),
     (pins.test_softmax_comparator_against_library_softmax, {}),
     (pins.test_softmax_comparator_closed_forms, {}),
+    (pins.test_sl_sample_selection_definition, {}),
 ]
 
 

@@ -584,3 +584,52 @@ def test_softmax_comparator_closed_forms():
         k2[off[b]:off[b + 1]] += rng.standard_normal((1, H, d)) * 3
     assert np.allclose(oracle.softmax_attn_fwd(off, q, k2, v), base, rtol=1e-10, atol=1e-10)
     assert np.allclose(oracle.softmax_attn_fwd(off, q, k, np.ones_like(v)), 1.0, rtol=1e-13, atol=1e-13)
+
+
+# ---------------------------------------------------------------- Stochastic Length sampler
+
+def test_sl_sample_selection_definition():
+    """Against a sort-based statement of the same rule (numpy lexsort by key
+    then position): the kept actions are the L with the smallest keys, in
+    input order, with L = max(1, min(n, ceil(n u^(1/alpha)))); duplicate
+    keys (few distinct values) take the earlier positions first."""
+    rng = np.random.default_rng(40)
+    for trial in range(30):
+        L = rng.integers(0, 40, size=rng.integers(1, 6))
+        off = synth.offsets_of(L)
+        keys = rng.integers(0, 6 if trial % 2 else 2 ** 32, size=int(off[-1]), dtype=np.uint64).astype(np.uint32)
+        u = rng.random(len(L))
+        alpha = float(rng.choice([1.2, 1.6, 2.0]))
+        oo, idx = oracle.sl_sample(off, alpha, u, keys)
+        want = []
+        for b in range(len(L)):
+            n = int(L[b])
+            m = 0 if n == 0 else max(1, min(n, math.ceil(n * u[b] ** (1.0 / alpha))))
+            kk = keys[off[b]:off[b + 1]]
+            order = np.lexsort((np.arange(n), kk))[:m]
+            want += sorted((off[b] + order).tolist())
+            assert oo[b + 1] - oo[b] == m
+        assert idx.tolist() == want
+
+
+def test_sl_sample_law_and_uniformity():
+    """u = 1 keeps everything and a tiny u keeps one action; over many draws
+    the mean kept length is n alpha/(alpha+1) + ~1/2 (the law's closed form),
+    and every position is kept with the same probability (uniform keys)."""
+    n, alpha = 64, 1.6
+    off = np.array([0, n], np.int32)
+    keys = np.arange(n, dtype=np.uint32)
+    oo, _ = oracle.sl_sample(off, alpha, [1.0], keys)
+    assert oo[1] == n
+    oo, _ = oracle.sl_sample(off, alpha, [1e-12], keys)
+    assert oo[1] == 1
+    rng = np.random.default_rng(41)
+    trials = 4000
+    B = trials
+    offs = synth.offsets_of(np.full(B, n))
+    oo, idx = oracle.sl_sample(offs, alpha, rng.random(B), rng.integers(0, 2 ** 32, size=B * n, dtype=np.uint64).astype(np.uint32))
+    lens = np.diff(oo)
+    assert abs(lens.mean() - (n * alpha / (alpha + 1) + 0.5)) < 1.0
+    pos_counts = np.bincount(idx % n, minlength=n)
+    expect = lens.sum() / n
+    assert np.abs(pos_counts - expect).max() < 6 * np.sqrt(expect)
