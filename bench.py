@@ -147,7 +147,17 @@ def cpu_baseline(w, prefix):
     oracle.attn_bwd(off, ts, q, k, v, w.rab_p, w.rab_t, w.n_max, u, w.ln_eps, dg)
     dt = time.perf_counter() - t0
     flops = 3 * 2 * w.heads * w.d * causal_pairs_sum(lens)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(), "cpu_model": cpu_model,
+            "kind": "oracle",
             "sample": "fwd+LN gate+bwd of the same 8 sequences cut to their first %d tokens (T=%d, %.1f GFLOP "
                       "algorithmic, %.1f s)" % (prefix, int(lens.sum()), flops / 1e9, dt),
             "seconds": dt}
@@ -282,6 +292,236 @@ def bench_mfalcon(args):
             "kernels": {n: {"launches": v["launches"] // steps, "avg_ms": round(v["avg_ms"], 5)} for n, v in kern.items()}}
 
 
+def _dev_attn(w, dev):
+    import torch
+    T = w.total
+    act = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev).to(torch.bfloat16)
+    q, k, v = (act(a).reshape(T, w.heads, w.d) for a in (w.q, w.k, w.v))
+    return (torch.from_numpy(w.offsets.astype(np.int32)).to(dev), torch.from_numpy(w.ts).to(dev), q, k, v,
+            act(w.u), torch.from_numpy(w.rab_p).to(dev), torch.from_numpy(w.rab_t).to(dev))
+
+
+def _kern(kern, steps):
+    return {n: {"launches": v["launches"] // steps, "avg_ms": round(v["avg_ms"], 5)} for n, v in kern.items()}
+
+
+def bench_fwd_call_8k(args):
+    """The forward call alone at the headline shapes (launcher, split-row
+    zeroing, attention, LayerNorm gate with O and the statistics saved):
+    the spec forward figure, as a fraction of the bf16 MFMA peak."""
+    import torch
+    import synth
+    import hstu_sequential_transducer_amd as hs
+    dev = torch.device("cuda:0")
+    w = synth.attn_8k(with_grad=False)
+    off, ts, q, k, v, u, rp, rt = _dev_attn(w, dev)
+    T, F = w.total, w.heads * w.d
+    out = torch.empty((T, F), dtype=torch.bfloat16, device=dev)
+    osv = torch.empty((T, F), dtype=torch.float32, device=dev)
+    lst = torch.empty((T, 2), dtype=torch.float32, device=dev)
+
+    def step():
+        return hs.attn_fwd(off, T, ts, q, k, v, rp, rt, w.n_max, u=u, eps=w.ln_eps, out=out, o_save=osv, ln_stats=lst)
+
+    steps = max(20, args.steps)
+    _, ms, per, kern, _ = timed(step, args.warmup, steps)
+    f = 2.0 * w.heads * w.d * causal_pairs_sum(w.lengths)
+    t = f / (ms * 1e-3) / 1e12
+    return {"workload": "attn-8k-B8-SL1.6 forward call with the LayerNorm(AV)*U gate", "ms": round(ms, 4),
+            "step_ms": pct(per), "tflops": round(t, 2), "pct_mfma_peak": round(100 * t / MFMA_BF16_PEAK_TFLOPS, 2),
+            "kernels": _kern(kern, steps)}
+
+
+def bench_fwd_1k(args):
+    """Config 1: bf16 attention forward, B=32, lengths U{64..1024},
+    N_max=1024, no gate (O bf16 out)."""
+    import torch
+    import synth
+    import hstu_sequential_transducer_amd as hs
+    dev = torch.device("cuda:0")
+    w = synth.attn_fwd_1k()
+    off, ts, q, k, v, _, rp, rt = _dev_attn(w, dev)
+    T, F = w.total, w.heads * w.d
+    out = torch.empty((T, F), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        return hs.attn_fwd(off, T, ts, q, k, v, rp, rt, w.n_max, out=out)
+
+    steps = max(20, args.steps)
+    _, ms, per, kern, _ = timed(step, args.warmup, steps)
+    f = 2.0 * w.heads * w.d * causal_pairs_sum(w.lengths)
+    t = f / (ms * 1e-3) / 1e12
+    return {"workload": "attn-fwd-B32-N1024 (lengths U{64..1024}, no gate)", "tokens": T, "gflop": round(f / 1e9, 2),
+            "ms": round(ms, 4), "step_ms": pct(per), "tflops": round(t, 2),
+            "pct_mfma_peak": round(100 * t / MFMA_BF16_PEAK_TFLOPS, 2), "kernels": _kern(kern, steps)}
+
+
+def bench_layer_tiny_f32(args):
+    """Config 0: the tiny fp32 layer forward (B=4, lengths {17, 64, 33, 5},
+    D=64, H=2, d=32): a latency figure."""
+    import torch
+    import synth
+    import hstu_sequential_transducer_amd as hs
+    dev = torch.device("cuda:0")
+    w = synth.tiny_layer_f32()
+    lay = w.layers[0]
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+    dl = dict(w1=f32(lay.w1), b1=f32(lay.b1), w2=f32(lay.w2), b2=f32(lay.b2), rab_p=f32(lay.rab_p),
+              rab_t=f32(lay.rab_t), phi1=0)
+    x = f32(w.x)
+    off = torch.from_numpy(w.offsets.astype(np.int32)).to(dev)
+    ts = torch.from_numpy(w.ts).to(dev)
+    y = torch.empty_like(x)
+
+    def step():
+        return hs.layer_fwd(off, w.total, ts, x, dl, w.heads, w.d, w.n_max, eps=w.ln_eps, out=y)
+
+    steps = max(50, args.steps)
+    _, ms, per, kern, _ = timed(step, args.warmup, steps)
+    return {"workload": "tiny fp32 layer forward B4 {17,64,33,5} D64 H2 d32", "us": round(ms * 1e3, 2),
+            "step_us": {k2: round(v2 * 1e3, 2) for k2, v2 in pct(per).items()}, "kernels": _kern(kern, steps)}
+
+
+def bench_mfalcon_64(args):
+    """Config 4b: M-FALCON over 64 users with SL(4096, 1.6) histories,
+    m = 1024 candidates each, 2 layers, b_m = 256."""
+    import torch
+    import synth
+    import hstu_sequential_transducer_amd as hs
+    dev = torch.device("cuda:0")
+    w = synth.mfalcon_64users()
+    T, D, H, d = w.total, w.d_model, w.heads, w.d
+    off = torch.from_numpy(w.offsets.astype(np.int32)).to(dev)
+    ts = torch.from_numpy(w.ts.astype(np.int64)).to(dev)
+    layers = [_dev_layer(l, dev) for l in w.layers]
+    h = torch.from_numpy(w.x).to(dev).to(torch.bfloat16)
+    kcs, vcs = [], []
+    for lay in layers:
+        kc = torch.empty((T, H * d), dtype=torch.bfloat16, device=dev)
+        vc = torch.empty_like(kc)
+        h = hs.layer_fwd(off, T, ts, h, lay, H, d, w.n_max, eps=w.ln_eps, k_cache=kc, v_cache=vc)
+        kcs.append(kc)
+        vcs.append(vc)
+    xc = torch.from_numpy(w.x_cand).to(dev).to(torch.bfloat16)
+    M = xc.shape[0]
+    co = torch.from_numpy(w.cand_offsets.astype(np.int32)).to(dev)
+    cts = torch.from_numpy(w.cand_ts.astype(np.int64)).to(dev)
+
+    def step():
+        return hs.mfalcon_score(off, T, ts, layers, kcs, vcs, co, M, cts, xc, w.b_m, H, d, w.n_max, eps=w.ln_eps)
+
+    steps = max(5, args.steps // 4)
+    _, ms, per, kern, _ = timed(step, args.warmup, steps)
+    nl = len(layers)
+    f_attn = nl * 4.0 * (M // len(w.lengths)) * float(w.lengths.sum()) * d * H
+    f_gemm = nl * (2.0 * M * D * 4 * H * d + 2.0 * M * H * d * D)
+    a = kern.get("mfalcon_attn_kernel")
+    return {"workload": "mfalcon 64 users, histories SL(4096,1.6) (T_hist=%d), m=1024 each, b_m=256, 2 layers, "
+                        "D512 H4 d128 bf16" % T,
+            "ms": round(ms, 4), "step_ms": pct(per), "candidates_per_s": round(M / (ms * 1e-3), 1),
+            "attn_tflops": round(f_attn / (a["total_ms"] / steps * 1e-3) / 1e12, 2) if a else None,
+            "total_tflops": round((f_attn + f_gemm) / (ms * 1e-3) / 1e12, 2), "kernels": _kern(kern, steps)}
+
+
+def bench_comparator_8k(args):
+    """Pointwise aggregated attention beside its comparator on the same
+    kernel skeleton, at the headline shapes, forward only with O out (no
+    gate): HSTU with both relative biases, HSTU without them, and causal
+    softmax attention (no bias).  Context for the pages' speed-up of HSTU
+    over softmax-attention Transformers; the same causal FLOPs in each."""
+    import torch
+    import synth
+    import hstu_sequential_transducer_amd as hs
+    dev = torch.device("cuda:0")
+    w = synth.attn_8k(with_grad=False)
+    off, ts, q, k, v, _, rp, rt = _dev_attn(w, dev)
+    T, F = w.total, w.heads * w.d
+    out = torch.empty((T, F), dtype=torch.bfloat16, device=dev)
+    f = 2.0 * w.heads * w.d * causal_pairs_sum(w.lengths)
+    steps = max(20, args.steps // 2)
+    res = {"workload": "attn-8k-B8-SL1.6 forward, O out (no gate)", "gflop": round(f / 1e9, 2)}
+    runs = {"hstu_rab": lambda: hs.attn_fwd(off, T, ts, q, k, v, rp, rt, w.n_max, out=out),
+            "hstu_no_rab": lambda: hs.attn_fwd(off, T, None, q, k, v, None, None, w.n_max, out=out),
+            "softmax_no_rab": lambda: hs.softmax_attn_fwd(off, T, q, k, v, w.n_max, out=out)}
+    for name, fn in runs.items():
+        _, ms, per, kern, _ = timed(fn, args.warmup, steps)
+        res[name] = {"ms": round(ms, 4), "tflops": round(f / (ms * 1e-3) / 1e12, 2), "kernels": _kern(kern, steps)}
+    res["softmax_over_hstu_rab_time"] = round(res["softmax_no_rab"]["ms"] / res["hstu_rab"]["ms"], 3)
+    return res
+
+
+def bench_sl_sample(args):
+    """Stochastic Length sampling of 8 full 8192-action histories (alpha
+    1.6) with their 512-wide bf16 rows gathered: the sampled batch's
+    construction, as a latency."""
+    import torch
+    import synth
+    import hstu_sequential_transducer_amd as hs
+    dev = torch.device("cuda:0")
+    L = np.full(8, 8192)
+    off_np = synth.offsets_of(L)
+    T = int(off_np[-1])
+    u, keys = synth.sl_draws(115, L)
+    off = torch.from_numpy(off_np).to(dev)
+    ts = torch.from_numpy(synth.timestamps(np.random.default_rng(116), L)).to(dev)
+    x = torch.randn((T, 512), device=dev).to(torch.bfloat16)
+    ud = torch.from_numpy(u).to(dev)
+    kd = torch.from_numpy(keys.view(np.int32)).to(dev)
+
+    def step():
+        return hs.sl_sample(off, T, ts, 1.6, ud, kd, x)
+
+    steps = max(20, args.steps // 2)
+    r, ms, per, kern, _ = timed(step, args.warmup, steps)
+    kept = int(r[0][-1].item())
+    return {"workload": "SL(alpha 1.6) of 8 x 8192 histories, 512-wide bf16 rows gathered", "kept": kept,
+            "ms": round(ms, 4), "step_ms": pct(per), "kernels": _kern(kern, steps)}
+
+
+def bench_append_64(args):
+    """Appending 16 new actions to each of 64 cached users (SL(4096, 1.6)
+    histories), one layer: f1, merged caches, attention of the new
+    positions, gate, f2."""
+    import torch
+    import synth
+    import hstu_sequential_transducer_amd as hs
+    dev = torch.device("cuda:0")
+    m = synth.mfalcon_64users()
+    w = synth.append_workload("append-64", 96, m.lengths, np.full(64, 16), n_max=4096)
+    lay = _dev_layer(w.layers[0], dev)
+    T, H, d = w.total, w.heads, w.d
+    off = torch.from_numpy(w.offsets.astype(np.int32)).to(dev)
+    ts = torch.from_numpy(w.ts).to(dev)
+    kc = torch.empty((T, H * d), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    hs.layer_fwd(off, T, ts, torch.from_numpy(w.x).to(dev).to(torch.bfloat16), lay, H, d, w.n_max, k_cache=kc,
+                 v_cache=vc)
+    aoff = torch.from_numpy(w.add_offsets.astype(np.int32)).to(dev)
+    ats = torch.from_numpy(w.add_ts).to(dev)
+    xn = torch.from_numpy(w.x_new).to(dev).to(torch.bfloat16)
+    Tn = xn.shape[0]
+    ko = torch.empty((T + Tn, H * d), dtype=torch.bfloat16, device=dev)
+    vo = torch.empty_like(ko)
+    y = torch.empty_like(xn)
+
+    def step():
+        return hs.layer_append(off, T, ts, aoff, Tn, ats, xn, lay, kc, vc, H, d, w.n_max, out=y, k_out=ko, v_out=vo)
+
+    steps = max(20, args.steps // 2)
+    _, ms, per, kern, _ = timed(step, args.warmup, steps)
+    return {"workload": "append 16 actions to each of 64 users (T_hist=%d), one layer D512 H4 d128 bf16" % T,
+            "ms": round(ms, 4), "step_ms": pct(per), "actions_per_s": round(Tn / (ms * 1e-3), 1),
+            "kernels": _kern(kern, steps)}
+
+
+def all_extras(args):
+    return {"fwd_call_8k": bench_fwd_call_8k(args), "fwd_1k": bench_fwd_1k(args),
+            "layer_tiny_f32": bench_layer_tiny_f32(args), "layer_fwd": bench_layer(args),
+            "layer_bwd": bench_layer_bwd(args), "mfalcon": bench_mfalcon(args), "mfalcon_64users": bench_mfalcon_64(args),
+            "comparator_8k": bench_comparator_8k(args), "sl_sample_8k": bench_sl_sample(args),
+            "append_64users": bench_append_64(args)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -292,8 +532,7 @@ def main():
     import hstu_sequential_transducer_amd as hs
 
     if args.extras_only:
-        print(json.dumps({"extras": {"layer_fwd": bench_layer(args), "layer_bwd": bench_layer_bwd(args),
-                                     "mfalcon": bench_mfalcon(args)}}), flush=True)
+        print(json.dumps({"extras": all_extras(args)}), flush=True)
         return
     dev = torch.device("cuda:0")
     w = synth.attn_8k(with_grad=True)
@@ -384,8 +623,7 @@ def main():
         torch.cuda.synchronize()
         res["copy_probe_bytes_each_way"] = n * 4
     if not args.no_extras:
-        res["extras"] = {"layer_fwd": bench_layer(args), "layer_bwd": bench_layer_bwd(args),
-                         "mfalcon": bench_mfalcon(args)}
+        res["extras"] = all_extras(args)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, args.cpu_sample_tokens)
         res["cpu_baseline"] = {k2: (round(v2, 6) if isinstance(v2, float) else v2) for k2, v2 in cb.items()}
