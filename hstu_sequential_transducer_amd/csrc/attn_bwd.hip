@@ -221,17 +221,7 @@ DEV void pointwise(floatx16 &xacc, const floatx16 &pacc, DpStep &&dp_step, uint3
         }
         ppk[s] = pack2_bf16(pp[0], pp[1]);
     }
-    if constexpr (UB == TB_ONE && !DIAG) {
-        // per step: the MFMAs of step s among the VALU work of its two elements
-#pragma unroll
-        for (int s = 0; s < 8; s++) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
-            if (s + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
-    }
+
     __builtin_amdgcn_sched_barrier(0);
     // P' -> LDS as [key][query] (lane row, 4 queries per r/4 group) while the
     // last dP products finish

@@ -84,13 +84,21 @@ DEV u32x2 lds_read_tr(const bf16 *p)
 // Register r of the S^T accumulator <-> key kbase + koff(r), koff = 8(r/4) + r%4
 // (kbase = block start + 4g), query = this lane's.  sacc holds s + rab_p (the
 // window is loaded into the accumulator).
-template <int TM, bool DIAG, bool UNI>
+//
+// step(s), s = 0..7, is called at the start of each two-element step: the
+// caller's next products (the following block's S^T, or the previous
+// block's O^T) issue one MFMA per step, so that the MFMA pipe works while
+// this wave's VALU does the element-wise step.  In the common variant (one
+// time bucket, off the diagonal) the order is pinned: per step its operand
+// reads, its MFMA, then the step's VALU work.
+template <int TM, bool DIAG, bool UNI, typename Step>
 DEV void pointwise(const floatx16 &sacc, uint32_t (&pk)[8], const uint32_t *kt_lane, const float *rabt_rev,
                    const float *rabt, uint32_t tq, int64_t tq64, const int64_t *tsk, int kbase, int klast, float ubias,
-                   int dmask)
+                   int dmask, Step &&step)
 {
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
+        step(r >> 1);
         float p2[2];
 #pragma unroll
         for (int u = 0; u < 2; u++) {
@@ -115,6 +123,15 @@ DEV void pointwise(const floatx16 &sacc, uint32_t (&pk)[8], const uint32_t *kt_l
         }
         pk[r >> 1] = pack2_bf16(p2[0], p2[1]);
     }
+    if constexpr ((TM == 0 || (TM == 1 && UNI)) && !DIAG) {
+#pragma unroll
+        for (int s = 0; s < 8; s++) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0); // the step's operand reads
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // its MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 11, 0); // two elements
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // qs, qmap: the queries are positions [qs, L) of the sequence (qs = 0
@@ -273,61 +290,70 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h,
     // S^T of 32-key block kb (keys kb0 + 32 kb ..): 8 MFMAs, K-operand reads
     // two steps ahead (pinned with scheduling groups); the window is added
     // afterwards.
-    auto s_block = [&](const Stage &S, int kb, floatx16 &sacc) {
+    // S^T of 32-key block kb (keys kb0 + 32 kb ..) in 8 steps of one MFMA:
+    // s_init starts the accumulator at the block's rab_p window (so the
+    // products add the bias for free) and reads the first two K operands;
+    // s_step(s) reads the operand two steps ahead and issues MFMA s.
+    auto s_init = [&](const Stage &S, int kb, floatx16 &sacc, bf16x8 (&fk)[3]) {
 #pragma unroll
-        for (int r = 0; r < 16; r++) sacc[r] = 0.f;
+        for (int r = 0; r < 16; r++) {
+            const int koff = 8 * (r >> 2) + (r & 3);
+            sacc[r] = HP ? S.win[kb * 32 + 4 * g - w * 32 - lq + (BM - 1) + koff] : 0.f;
+        }
+        fk[0] = *(const bf16x8 *)&S.k[swz(kb * 32 + lq, g * 8)];
+        fk[1] = *(const bf16x8 *)&S.k[swz(kb * 32 + lq, 16 + g * 8)];
+    };
+    auto s_step = [&](const Stage &S, int kb, floatx16 &sacc, bf16x8 (&fk)[3], int st) {
+        if (st + 2 < 8) fk[(st + 2) % 3] = *(const bf16x8 *)&S.k[swz(kb * 32 + lq, (st + 2) * 16 + g * 8)];
+        sacc = mfma32(fk[st % 3], qreg[st], sacc);
+    };
+    // The whole S^T of a block, reads two steps ahead of the MFMAs.
+    auto s_block = [&](const Stage &S, int kb, floatx16 &sacc) {
         __builtin_amdgcn_sched_barrier(0);
         bf16x8 fk[3];
-        auto fetch = [&](int s) { fk[s % 3] = *(const bf16x8 *)&S.k[swz(kb * 32 + lq, s * 16 + g * 8)]; };
-        fetch(0);
-        fetch(1);
+        s_init(S, kb, sacc, fk);
 #pragma unroll
-        for (int s = 0; s < 8; s++) {
-            if (s + 2 < 8) fetch(s + 2);
-            sacc = mfma32(fk[s % 3], qreg[s], sacc);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        for (int st = 0; st < 8; st++) s_step(S, kb, sacc, fk, st);
+        __builtin_amdgcn_sched_group_barrier(0x100, 18, 0); // the window and the first K operands
 #pragma unroll
-        for (int s = 0; s < 8; s++) {
-            if (s + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int st = 0; st < 8; st++) {
+            if (st + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (HP) {
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int koff = 8 * (r >> 2) + (r & 3);
-                sacc[r] += S.win[kb * 32 + 4 * g - w * 32 - lq + (BM - 1) + koff];
-            }
-        }
     };
-    // O^T += V^T P^T for block kb: 8 MFMAs, transposing V reads three steps
-    // ahead.  Step j: m = j / 4 (keys 16m..16m+15 of the block), db = j % 4.
+    // O^T += V^T P^T for block kb in 8 steps of one MFMA, transposing V
+    // reads three steps ahead.  Step j: m = j / 4 (keys 16m..16m+15 of the
+    // block), db = j % 4.
+    auto o_fetch = [&](const Stage &S, int kb, bf16x8 (&fv)[4], int jj) {
+        const int m = jj >> 2, db = jj & 3;
+        // keys for element e of this lane's operand: 16m + 8(e/4) + 4g + e%4
+        const int key1 = kb * 32 + 16 * m + 4 * g + tsl;
+        const u32x2 r1 = lds_read_tr(&S.v[swz(key1, db * 32 + cpart)]);
+        const u32x2 r2 = lds_read_tr(&S.v[swz(key1 + 8, db * 32 + cpart)]);
+        fv[jj & 3] = as_bf16x8(u32x4{r1[0], r1[1], r2[0], r2[1]});
+    };
+    auto o_init = [&](const Stage &S, int kb, bf16x8 (&fv)[4]) {
+        o_fetch(S, kb, fv, 0);
+        o_fetch(S, kb, fv, 1);
+        o_fetch(S, kb, fv, 2);
+    };
+    auto o_step = [&](const Stage &S, int kb, const uint32_t (&pk)[8], bf16x8 (&fv)[4], int jj) {
+        if (jj + 3 < 8) o_fetch(S, kb, fv, jj + 3);
+        const int m = jj >> 2, db = jj & 3;
+        const bf16x8 pb = as_bf16x8(u32x4{pk[4 * m], pk[4 * m + 1], pk[4 * m + 2], pk[4 * m + 3]});
+        oacc[db] = mfma32(fv[jj & 3], pb, oacc[db]);
+    };
     auto o_block = [&](const Stage &S, int kb, const uint32_t (&pk)[8]) {
         __builtin_amdgcn_sched_barrier(0);
         bf16x8 fv[4];
-        auto fetch = [&](int j) {
-            const int m = j >> 2, db = j & 3;
-            // keys for element e of this lane's operand: 16m + 8(e/4) + 4g + e%4
-            const int key1 = kb * 32 + 16 * m + 4 * g + tsl;
-            const u32x2 r1 = lds_read_tr(&S.v[swz(key1, db * 32 + cpart)]);
-            const u32x2 r2 = lds_read_tr(&S.v[swz(key1 + 8, db * 32 + cpart)]);
-            fv[j & 3] = as_bf16x8(u32x4{r1[0], r1[1], r2[0], r2[1]});
-        };
-        fetch(0);
-        fetch(1);
-        fetch(2);
+        o_init(S, kb, fv);
 #pragma unroll
-        for (int j = 0; j < 8; j++) {
-            if (j + 3 < 8) fetch(j + 3);
-            const int m = j >> 2, db = j & 3;
-            const bf16x8 pb = as_bf16x8(u32x4{pk[4 * m], pk[4 * m + 1], pk[4 * m + 2], pk[4 * m + 3]});
-            oacc[db] = mfma32(fv[j & 3], pb, oacc[db]);
-        }
+        for (int jj = 0; jj < 8; jj++) o_step(S, kb, pk, fv, jj);
         __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
-        for (int j = 0; j < 8; j++) {
-            if (j + 3 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        for (int jj = 0; jj < 8; jj++) {
+            if (jj + 3 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -335,7 +361,7 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h,
     // The element-wise step of block kb (sacc holds s + rab_p): time-bias
     // mode from the block's key-time range [ka, kb_], then P' packed to bf16.
     auto pw_block = [&](const Stage &S, int kt, int kb, const floatx16 &sacc, uint32_t (&pk)[8], bool diag,
-                        uint32_t ka, uint32_t kb_) {
+                        uint32_t ka, uint32_t kb_, auto &&step) {
         const int kstart = kt * BN + kb * 32;
         const uint32_t *kt_lane = &S.kt[kb * 32 + 4 * g];
         const int kbase = kstart + 4 * g;
@@ -355,11 +381,13 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h,
         }
         if (diag)
             pointwise<TM, true, false>(sacc, pk, kt_lane, sm.rabt_rev, sm.rabt, tq, tq64, tsk, kbase, L - 1, ubias,
-                                       lq - 4 * g);
+                                       lq - 4 * g, step);
         else if (TM == 1 && uni)
-            pointwise<TM, false, true>(sacc, pk, kt_lane, sm.rabt_rev, sm.rabt, tq, tq64, tsk, kbase, L - 1, ubias, 0);
+            pointwise<TM, false, true>(sacc, pk, kt_lane, sm.rabt_rev, sm.rabt, tq, tq64, tsk, kbase, L - 1, ubias, 0,
+                                       step);
         else
-            pointwise<TM, false, false>(sacc, pk, kt_lane, sm.rabt_rev, sm.rabt, tq, tq64, tsk, kbase, L - 1, ubias, 0);
+            pointwise<TM, false, false>(sacc, pk, kt_lane, sm.rabt_rev, sm.rabt, tq, tq64, tsk, kbase, L - 1, ubias, 0,
+                                        step);
     };
 
     // One 64-key tile: the next tile's copies are issued first; the
@@ -421,18 +449,23 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h,
                 if (diag[1]) pointwise_softmax<true>(sacc1, pk1, sm_c, sm_m, sm_l, lq - 4 * g);
                 else pointwise_softmax<false>(sacc1, pk1, sm_c, sm_m, sm_l, 0);
             }
-        } else {
-            if (need[0]) {
-                s_block(S, 0, sacc0);
-                pw_block(S, kt, 0, sacc0, pk0, diag[0], kmn[0], kmx[0]);
-            }
-            if (need[1]) {
-                s_block(S, 1, sacc1);
-                pw_block(S, kt, 1, sacc1, pk1, diag[1], kmn[1], kmx[1]);
-            }
+            if (need[0]) o_block(S, 0, pk0);
+            if (need[1]) o_block(S, 1, pk1);
+        } else if (need[1]) {
+            // both blocks (need[1] implies need[0]): block 1's S^T products
+            // run during block 0's element-wise step, block 0's O^T products
+            // during block 1's, then block 1's O^T
+            s_block(S, 0, sacc0);
+            pw_block(S, kt, 0, sacc0, pk0, diag[0], kmn[0], kmx[0], [](int) {});
+            s_block(S, 1, sacc1);
+            pw_block(S, kt, 1, sacc1, pk1, diag[1], kmn[1], kmx[1], [](int) {});
+            o_block(S, 0, pk0);
+            o_block(S, 1, pk1);
+        } else if (need[0]) {
+            s_block(S, 0, sacc0);
+            pw_block(S, kt, 0, sacc0, pk0, diag[0], kmn[0], kmx[0], [](int) {});
+            o_block(S, 0, pk0);
         }
-        if (need[0]) o_block(S, 0, pk0);
-        if (need[1]) o_block(S, 1, pk1);
         __builtin_amdgcn_s_waitcnt(0); // the next tile's copies landed
         __syncthreads();
     };
