@@ -85,12 +85,13 @@ DEV u32x2 lds_read_tr(const bf16 *p)
 // (kbase = block start + 4g), query = this lane's.  sacc holds s + rab_p (the
 // window is loaded into the accumulator).
 //
-// step(s), s = 0..7, is called at the start of each two-element step: the
-// caller's next products (the following block's S^T, or the previous
-// block's O^T) issue one MFMA per step, so that the MFMA pipe works while
-// this wave's VALU does the element-wise step.  In the common variant (one
-// time bucket, off the diagonal) the order is pinned: per step its operand
-// reads, its MFMA, then the step's VALU work.
+// step(s), s = 0..7, is called at the start of each two-element step, for a
+// caller that interleaves other products with the element-wise work (one
+// MFMA per step; in the common variant -- one time bucket, off the diagonal
+// -- the order is then pinned: per step its operand reads, its MFMA, then
+// the step's VALU work).  The tile loop passes a no-op: issuing the next
+// block's S^T here needs about 35 more registers than the 256 a wave has at
+// two waves per SIMD, and the spills cost more than the overlap gains.
 template <int TM, bool DIAG, bool UNI, typename Step>
 DEV void pointwise(const floatx16 &sacc, uint32_t (&pk)[8], const uint32_t *kt_lane, const float *rabt_rev,
                    const float *rabt, uint32_t tq, int64_t tq64, const int64_t *tsk, int kbase, int klast, float ubias,
@@ -134,11 +135,6 @@ DEV void pointwise(const floatx16 &sacc, uint32_t (&pk)[8], const uint32_t *kt_l
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// qs, qmap: the queries are positions [qs, L) of the sequence (qs = 0
-// except when new actions are appended to a cached history: then the
-// sequence is [history; new] and only the new positions are queries), and
-// query position p reads Q and writes O at row qmap + p (o_b for a whole
-// sequence).
 // Softmax elements of one 32x32 block (the comparator, SM): P' = 2^(s c - m)
 // with the tile's running max m (scaled domain), masked pairs exactly 0;
 // the lane's share of the row sum goes to lsum.
@@ -174,6 +170,11 @@ DEV float block_max(const floatx16 &sacc, float c, int dmask)
     return mx;
 }
 
+// qs, qmap: the queries are positions [qs, L) of the sequence (qs = 0
+// except when new actions are appended to a cached history: then the
+// sequence is [history; new] and only the new positions are queries), and
+// query position p reads Q and writes O at row qmap + p (o_b for a whole
+// sequence).  SM: the softmax comparator (no bias, online softmax).
 template <bool HP, int TM, bool SM = false>
 DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h, int split, int part, int qs,
                   int64_t qmap)
