@@ -14,7 +14,9 @@ from typing import List, Optional, Sequence
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libhstu.so")
+# HSTU_LIB_PATH selects another build of the same library (the host-sanitizer
+# build of the CPU tests); the default is the in-tree libhstu.so.
+LIB_PATH = os.environ.get("HSTU_LIB_PATH") or os.path.join(_HERE, "libhstu.so")
 
 HSTU_OK, HSTU_ERR_ARG, HSTU_ERR_UNSUPPORTED, HSTU_ERR_WORKSPACE, HSTU_ERR_DEVICE = range(5)
 HSTU_F32, HSTU_BF16 = 0, 1

@@ -36,9 +36,10 @@ def round_bf16(a: np.ndarray) -> np.ndarray:
 
 
 def stochastic_lengths(rng: np.random.Generator, batch: int, n: int, alpha: float) -> np.ndarray:
-    """Sequence lengths from the Stochastic Length law printed on p1 (section 3,
-    Stochastic Length): L = min(n, ceil(n * u**(1/alpha))), u ~ U(0, 1).  A draw
-    of u = 0 would give L = 0; it is clamped to 1."""
+    """Sequence lengths from the Stochastic Length law of the paper review
+    "Actions Speak Louder than Words" (section 3, Stochastic Length):
+    L = min(n, ceil(n * u**(1/alpha))), u ~ U(0, 1).  A draw of u = 0 would
+    give L = 0; it is clamped to 1."""
     u = rng.random(batch)
     L = np.minimum(n, np.ceil(n * u ** (1.0 / alpha))).astype(np.int64)
     return np.maximum(L, 1)
