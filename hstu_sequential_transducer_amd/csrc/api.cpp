@@ -133,15 +133,21 @@ hstu_status check_jagged(const hstu_jagged *j)
     return HSTU_OK;
 }
 
-hstu_status check_dims(const hstu_dims *dm)
+// `bf16_heads`: the bf16 head sizes the calling entry point's kernels take
+// (the attention forwards take 32, 64 and 128; everything else 128).
+enum Bf16Heads { BF16_D128, BF16_D32_64_128 };
+
+hstu_status check_dims(const hstu_dims *dm, Bf16Heads bf16_heads = BF16_D128)
 {
     if (!dm) return fail(HSTU_ERR_ARG, "dims descriptor is NULL");
     if (dm->dtype != HSTU_F32 && dm->dtype != HSTU_BF16) return fail(HSTU_ERR_ARG, "unknown dtype %d", (int)dm->dtype);
     if (dm->heads < 1 || dm->heads > 255) return fail(HSTU_ERR_ARG, "heads must be in [1, 255] (got %d)", dm->heads);
     if (dm->d_qk != dm->d_v) return fail(HSTU_ERR_UNSUPPORTED, "d_qk != d_v is not supported");
     if (!(dm->ln_eps > 0.f)) return fail(HSTU_ERR_ARG, "ln_eps must be > 0");
-    if (dm->dtype == HSTU_BF16 && dm->d_qk != 128)
-        return fail(HSTU_ERR_UNSUPPORTED, "bf16 path supports d = 128 (got %d)", dm->d_qk);
+    if (dm->dtype == HSTU_BF16 && bf16_heads == BF16_D128 && dm->d_qk != 128)
+        return fail(HSTU_ERR_UNSUPPORTED, "this bf16 entry point supports d = 128 (got %d)", dm->d_qk);
+    if (dm->dtype == HSTU_BF16 && dm->d_qk != 32 && dm->d_qk != 64 && dm->d_qk != 128)
+        return fail(HSTU_ERR_UNSUPPORTED, "bf16 attention forward supports d in {32, 64, 128} (got %d)", dm->d_qk);
     if (dm->dtype == HSTU_F32 && dm->d_qk != 16 && dm->d_qk != 32 && dm->d_qk != 64 && dm->d_qk != 128)
         return fail(HSTU_ERR_UNSUPPORTED, "fp32 path supports d in {16, 32, 64, 128} (got %d)", dm->d_qk);
     if (dm->heads * dm->d_v > 2048) return fail(HSTU_ERR_UNSUPPORTED, "H*d_v above 2048 is not supported");
@@ -233,7 +239,7 @@ hstu_status attn_fwd_launch(const hstu_jagged *j, const hstu_dims *dm, const hst
     // Long query tiles are split over two workgroups (halves of the key
     // range) when the output accumulates in fp32 (the LayerNorm-gate path):
     // the halves add into zeroed rows.
-    const bool split = dm->dtype == HSTU_BF16 && u.ptr != nullptr;
+    const bool split = dm->dtype == HSTU_BF16 && d == 128 && u.ptr != nullptr;
     const int max_items = (split ? 2 : 1) * max_items_for(B, T, tile, H);
     int *t_split = status + 2;
     float *obuf = u.ptr ? (o_save ? o_save : (float *)(wb + w.obuf)) : nullptr;
@@ -624,7 +630,7 @@ hstu_status attn_fwd_entry(const hstu_jagged *j, const hstu_dims *dm, const hstu
                            size_t ws_bytes, void *stream, bool lean, size_t *need)
 {
     TRY(check_jagged(j));
-    TRY(check_dims(dm));
+    TRY(check_dims(dm, BF16_D32_64_128));
     TRY(check_bias(bias, j));
     const int H = dm->heads, d = dm->d_qk, F = H * dm->d_v;
     TRY(check_view(q.ptr, q.ld, (int64_t)H * d, "q"));
@@ -662,7 +668,8 @@ const char *hstu_last_error(void) { return g_err.c_str(); }
 size_t hstu_workspace_size(hstu_op op, const hstu_jagged *j, const hstu_dims *dims, int32_t d_model,
                            int32_t total_cand)
 {
-    if (check_jagged(j) != HSTU_OK || check_dims(dims) != HSTU_OK) return 0;
+    if (check_jagged(j) != HSTU_OK || check_dims(dims, op == HSTU_OP_ATTN_FWD ? BF16_D32_64_128 : BF16_D128) != HSTU_OK)
+        return 0;
     switch (op) {
     case HSTU_OP_ATTN_FWD: return attn_ws(j, dims, fwd_tile(dims), false).total;
     case HSTU_OP_ATTN_BWD: return attn_ws(j, dims, BWD_BN, true).total;
@@ -744,7 +751,7 @@ hstu_status hstu_softmax_attn_fwd(const hstu_jagged *j, const hstu_dims *dm, hst
                                   hstu_mat out, float *lse, void *ws, size_t ws_bytes, void *stream)
 {
     TRY(check_jagged(j));
-    TRY(check_dims(dm));
+    TRY(check_dims(dm, BF16_D32_64_128));
     if (dm->dtype != HSTU_BF16) return fail(HSTU_ERR_UNSUPPORTED, "hstu_softmax_attn_fwd supports bf16 storage only");
     const int H = dm->heads, d = dm->d_qk, F = H * dm->d_v;
     const struct { const void *p; int64_t ld; int64_t w; const char *n; } views[] = {

@@ -31,41 +31,45 @@
 
 namespace {
 
-constexpr int D = 128;
 constexpr int BM = FWD_BM; // 128 query rows
 constexpr int BN = 64;     // keys per LDS tile
 constexpr int NT = 256;
-// K and V tiles are [64 keys][128] bf16 with no padding; the 16-byte chunks
-// of row r are XOR-swizzled by sw(r) = 4(r%4) + bitrev2((r/4)%4), which keeps
-// the 16-byte K-operand reads (16 consecutive rows, one chunk) and the
-// transposing V reads (4 consecutive rows, 64 bytes each) free of bank
-// conflicts and lets the tiles be copied global -> LDS directly (4 rows per
-// wave instruction).
+// K and V tiles are [64 keys][D] bf16 (D = 128, 64 or 32: the head size)
+// with no padding; the 16-byte chunks of row r are XOR-swizzled by sw(r) =
+// 4(r%4) + bitrev2((r/4)%4), masked to the row's D/8 chunks, which for D =
+// 128 keeps the 16-byte K-operand reads (16 consecutive rows, one chunk) and
+// the transposing V reads (4 consecutive rows, 64 bytes each) free of bank
+// conflicts, and lets the tiles be copied global -> LDS directly (1 KB, i.e.
+// 1024 / (2 D) rows, per wave instruction).
 constexpr int WIN = 192;   // rab_p window entries per tile (BM + BN - 1 used)
 constexpr float NLOG2E = -1.4426950408889634f;
 constexpr float NLN2 = -0.69314718055994531f;
 
+template <int D>
 struct alignas(16) Stage {
     alignas(16) bf16 k[BN * D];
     alignas(16) bf16 v[BN * D];
     float win[WIN];        // rab_p[clip(key - query)] (unscaled)
     uint32_t kt[BN];       // sequence-relative key times
 };
+template <int D>
 struct alignas(16) Smem {
-    Stage st[2];        // (after the last tile: a split item's output transpose, 4 x 32 x 132 floats)
+    Stage<D> st[2];     // (D = 128, after the last tile: a split item's output transpose, 4 x 32 x 132 floats)
     float rabt_rev[32]; // -log2(e) * rab_t[31 - c], indexed by clz(|dt| + 1)
     float rabt[128];    // -log2(e) * rab_t
 };
-static_assert(sizeof(Stage) * 2 >= 4 * 32 * 132 * sizeof(float), "split-output transpose fits in the stages");
+static_assert(sizeof(Stage<128>) * 2 >= 4 * 32 * 132 * sizeof(float), "split-output transpose fits in the stages");
 
-// Swizzle of row r: the XOR applied to its 16-byte chunk index.
+// Swizzle of row r: the XOR applied to its 16-byte chunk index (of D/8).
+template <int D>
 DEV int swf(int row)
 {
     const int hi = (row >> 2) & 3;
-    return ((row & 3) << 2) | ((hi & 1) << 1) | (hi >> 1);
+    return (((row & 3) << 2) | ((hi & 1) << 1) | (hi >> 1)) & (D / 8 - 1);
 }
-// Element offset of (row, col) in a swizzled [rows][128] tile.
-DEV int swz(int row, int col) { return row * D + (((col >> 3) ^ swf(row)) << 3) + (col & 7); }
+// Element offset of (row, col) in a swizzled [rows][D] tile.
+template <int D>
+DEV int swz(int row, int col) { return row * D + (((col >> 3) ^ swf<D>(row)) << 3) + (col & 7); }
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short short4v __attribute__((ext_vector_type(4)));
@@ -175,10 +179,15 @@ DEV float block_max(const floatx16 &sacc, float c, int dmask)
 // sequence is [history; new] and only the new positions are queries), and
 // query position p reads Q and writes O at row qmap + p (o_b for a whole
 // sequence).  SM: the softmax comparator (no bias, online softmax).
-template <bool HP, int TM, bool SM = false>
-DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h, int split, int part, int qs,
+template <int D, bool HP, int TM, bool SM = false>
+DEV void fwd_body(const AttnFwdArgs &a, Smem<D> &sm, int o_b, int L, int q0, int h, int split, int part, int qs,
                   int64_t qmap)
 {
+    constexpr int KS = D / 16;      // K steps of the S^T products (and Q registers)
+    constexpr int DB = D / 32;      // 32-wide d-blocks of O^T
+    constexpr int NCH = D / 8;      // 16-byte chunks per row
+    constexpr int RPI = 64 / NCH;   // rows per wave copy instruction
+    constexpr int NPAT = 16 / RPI;  // distinct swizzle patterns of a wave's copy rows
     const int kend = min(q0 + BM, L); // keys [0, kend) are needed
     const int nkt = (kend + BN - 1) / BN;
     // a split item covers half of the key tiles: part 0 [0, nkt / 2), part 1 the rest
@@ -193,11 +202,11 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h,
     const int qrow = qstart + lq;
     const bool qvalid = qrow < L && qrow >= qs;
     const bool wact = qstart < L && qstart + 31 >= qs; // the wave has queries (wave-uniform)
-    bf16x8 qreg[8];
+    bf16x8 qreg[KS];
     {
         const bf16 *qp = Q + (qvalid ? qmap + qrow : 0) * a.ldq + h * D + g * 8;
 #pragma unroll
-        for (int s = 0; s < 8; s++) {
+        for (int s = 0; s < KS; s++) {
             u32x4 x = qvalid ? *(const u32x4 *)(qp + s * 16) : u32x4{0, 0, 0, 0};
             qreg[s] = as_bf16x8(x);
         }
@@ -211,9 +220,9 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h,
         tqmax = a.rmax[o_b + qstart];
     }
 
-    floatx16 oacc[4];
+    floatx16 oacc[DB];
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < DB; i++)
 #pragma unroll
         for (int r = 0; r < 16; r++) oacc[i][r] = 0.f;
     // softmax comparator: running max (scaled by c = log2(e) / sqrt(d)) and
@@ -222,41 +231,44 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h,
     float sm_m = -__builtin_inff(), sm_l = 0.f;
 
     // ---- tile loader: every copy goes global -> LDS directly.  K and V:
-    // 32 groups of 4 rows, 8 per wave; lane l fills physical chunk l%16 of
-    // row 4(G%16) + l/16 (rows past the needed keys repeat the last one:
-    // finite, and every pair they form is masked).  The rab_p window (waves
-    // 0-2, slot 64w + lane) and the key times (wave 3) as 4-byte copies.
-    // Full tiles (every key < kend): wave w copies plane w / 2 (K, then V),
-    // row groups 8(w % 2) + i; the row base is wave-uniform and each lane
-    // adds one of four 32-bit byte offsets (row l/16 of the group, swizzled
-    // chunk), so the copies need no per-lane 64-bit address arithmetic.
+    // groups of RPI rows (one wave instruction each, 2 * 64 / RPI groups,
+    // IPW per wave); lane l fills physical chunk l % NCH of row
+    // RPI (G % (64 / RPI)) + l / NCH (rows past the needed keys repeat the
+    // last one: finite, and every pair they form is masked).  The rab_p
+    // window (waves 0-2, slot 64w + lane) and the key times (wave 3) as
+    // 4-byte copies.  Full tiles (every key < kend): wave w copies plane w / 2
+    // (K, then V), row groups IPW (w % 2) + i; the row base is wave-uniform
+    // and each lane adds one of NPAT 32-bit byte offsets (its row of the
+    // group, swizzled chunk), so the copies need no per-lane 64-bit address
+    // arithmetic.
+    constexpr int IPP = 64 / RPI, IPW = IPP / 2;
     const int wu = __builtin_amdgcn_readfirstlane(w);
     const bool kplane = wu < 2;
     const bf16 *pbase = kplane ? K : V;
     const int64_t pld = kplane ? a.ldk : a.ldv;
-    uint32_t loff[4];
+    uint32_t loff[NPAT];
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const int sw = ((l >> 4) << 2) | ((j & 1) << 1) | (j >> 1); // swf(row), row % 4 = l/16, (row/4) % 4 = j
-        loff[j] = (uint32_t)(((int64_t)(l >> 4) * pld + (((l & 15) ^ sw) << 3)) * 2);
+    for (int j = 0; j < NPAT; j++) {
+        const int rr = l / NCH, sw = swf<D>(RPI * j + rr);
+        loff[j] = (uint32_t)(((int64_t)rr * pld + (((l % NCH) ^ sw) << 3)) * 2);
     }
-    auto gload = [&](int kt, Stage &S, auto full_c) {
+    auto gload = [&](int kt, Stage<D> &S, auto full_c) {
         constexpr bool FULL = decltype(full_c)::value;
         const int kb0 = kt * BN;
         if constexpr (FULL) {
 #pragma unroll
-            for (int i = 0; i < 8; i++) {
-                const int r0 = 4 * ((8 * wu + i) & 15);
+            for (int i = 0; i < IPW; i++) {
+                const int gi = IPW * (wu & 1) + i, r0 = RPI * gi;
                 const char *rowp = (const char *)(pbase + (int64_t)(o_b + kb0 + r0) * pld + h * D);
-                __builtin_amdgcn_global_load_lds((const void *)(rowp + loff[i & 3]),
+                __builtin_amdgcn_global_load_lds((const void *)(rowp + loff[gi % NPAT]),
                                                  (lds_void *)((kplane ? S.k : S.v) + r0 * D), 16, 0, 0);
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < 8; i++) {
-                const int G = 8 * w + i, plane = G >> 4, r0 = 4 * (G & 15);
-                const int row = r0 + (l >> 4);
-                const int c = (l & 15) ^ swf(row);
+            for (int i = 0; i < IPW; i++) {
+                const int G = IPW * w + i, plane = G / IPP, r0 = RPI * (G % IPP);
+                const int row = r0 + l / NCH;
+                const int c = (l % NCH) ^ swf<D>(row);
                 const int key = min(kb0 + row, kend - 1);
                 const bf16 *src =
                     (plane == 0 ? K + (int64_t)(o_b + key) * a.ldk : V + (int64_t)(o_b + key) * a.ldv);
@@ -288,80 +300,77 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h,
     // and are full: the MAIN iterations, compiled without the per-block checks.
     const int n_main = q0 / BN; // tiles [0, n_main)
 
-    // S^T of 32-key block kb (keys kb0 + 32 kb ..): 8 MFMAs, K-operand reads
-    // two steps ahead (pinned with scheduling groups); the window is added
-    // afterwards.
-    // S^T of 32-key block kb (keys kb0 + 32 kb ..) in 8 steps of one MFMA:
+    // S^T of 32-key block kb (keys kb0 + 32 kb ..) in KS steps of one MFMA:
     // s_init starts the accumulator at the block's rab_p window (so the
     // products add the bias for free) and reads the first two K operands;
     // s_step(s) reads the operand two steps ahead and issues MFMA s.
-    auto s_init = [&](const Stage &S, int kb, floatx16 &sacc, bf16x8 (&fk)[3]) {
+    auto s_init = [&](const Stage<D> &S, int kb, floatx16 &sacc, bf16x8 (&fk)[3]) {
 #pragma unroll
         for (int r = 0; r < 16; r++) {
             const int koff = 8 * (r >> 2) + (r & 3);
             sacc[r] = HP ? S.win[kb * 32 + 4 * g - w * 32 - lq + (BM - 1) + koff] : 0.f;
         }
-        fk[0] = *(const bf16x8 *)&S.k[swz(kb * 32 + lq, g * 8)];
-        fk[1] = *(const bf16x8 *)&S.k[swz(kb * 32 + lq, 16 + g * 8)];
+        fk[0] = *(const bf16x8 *)&S.k[swz<D>(kb * 32 + lq, g * 8)];
+        fk[1] = *(const bf16x8 *)&S.k[swz<D>(kb * 32 + lq, 16 + g * 8)];
     };
-    auto s_step = [&](const Stage &S, int kb, floatx16 &sacc, bf16x8 (&fk)[3], int st) {
-        if (st + 2 < 8) fk[(st + 2) % 3] = *(const bf16x8 *)&S.k[swz(kb * 32 + lq, (st + 2) * 16 + g * 8)];
+    auto s_step = [&](const Stage<D> &S, int kb, floatx16 &sacc, bf16x8 (&fk)[3], int st) {
+        if (st + 2 < KS) fk[(st + 2) % 3] = *(const bf16x8 *)&S.k[swz<D>(kb * 32 + lq, (st + 2) * 16 + g * 8)];
         sacc = mfma32(fk[st % 3], qreg[st], sacc);
     };
     // The whole S^T of a block, reads two steps ahead of the MFMAs.
-    auto s_block = [&](const Stage &S, int kb, floatx16 &sacc) {
+    auto s_block = [&](const Stage<D> &S, int kb, floatx16 &sacc) {
         __builtin_amdgcn_sched_barrier(0);
         bf16x8 fk[3];
         s_init(S, kb, sacc, fk);
 #pragma unroll
-        for (int st = 0; st < 8; st++) s_step(S, kb, sacc, fk, st);
+        for (int st = 0; st < KS; st++) s_step(S, kb, sacc, fk, st);
         __builtin_amdgcn_sched_group_barrier(0x100, 18, 0); // the window and the first K operands
 #pragma unroll
-        for (int st = 0; st < 8; st++) {
-            if (st + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int st = 0; st < KS; st++) {
+            if (st + 2 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
     };
-    // O^T += V^T P^T for block kb in 8 steps of one MFMA, transposing V
-    // reads three steps ahead.  Step j: m = j / 4 (keys 16m..16m+15 of the
-    // block), db = j % 4.
-    auto o_fetch = [&](const Stage &S, int kb, bf16x8 (&fv)[4], int jj) {
-        const int m = jj >> 2, db = jj & 3;
+    // O^T += V^T P^T for block kb in OS = 2 DB steps of one MFMA,
+    // transposing V reads three steps ahead.  Step j: m = j / DB (keys
+    // 16m..16m+15 of the block), db = j % DB.
+    constexpr int OS = 2 * DB;
+    auto o_fetch = [&](const Stage<D> &S, int kb, bf16x8 (&fv)[4], int jj) {
+        const int m = jj / DB, db = jj % DB;
         // keys for element e of this lane's operand: 16m + 8(e/4) + 4g + e%4
         const int key1 = kb * 32 + 16 * m + 4 * g + tsl;
-        const u32x2 r1 = lds_read_tr(&S.v[swz(key1, db * 32 + cpart)]);
-        const u32x2 r2 = lds_read_tr(&S.v[swz(key1 + 8, db * 32 + cpart)]);
+        const u32x2 r1 = lds_read_tr(&S.v[swz<D>(key1, db * 32 + cpart)]);
+        const u32x2 r2 = lds_read_tr(&S.v[swz<D>(key1 + 8, db * 32 + cpart)]);
         fv[jj & 3] = as_bf16x8(u32x4{r1[0], r1[1], r2[0], r2[1]});
     };
-    auto o_init = [&](const Stage &S, int kb, bf16x8 (&fv)[4]) {
-        o_fetch(S, kb, fv, 0);
-        o_fetch(S, kb, fv, 1);
-        o_fetch(S, kb, fv, 2);
+    auto o_init = [&](const Stage<D> &S, int kb, bf16x8 (&fv)[4]) {
+#pragma unroll
+        for (int jj = 0; jj < 3 && jj < OS; jj++) o_fetch(S, kb, fv, jj);
     };
-    auto o_step = [&](const Stage &S, int kb, const uint32_t (&pk)[8], bf16x8 (&fv)[4], int jj) {
-        if (jj + 3 < 8) o_fetch(S, kb, fv, jj + 3);
-        const int m = jj >> 2, db = jj & 3;
+    auto o_step = [&](const Stage<D> &S, int kb, const uint32_t (&pk)[8], bf16x8 (&fv)[4], int jj) {
+        if (jj + 3 < OS) o_fetch(S, kb, fv, jj + 3);
+        const int m = jj / DB, db = jj % DB;
         const bf16x8 pb = as_bf16x8(u32x4{pk[4 * m], pk[4 * m + 1], pk[4 * m + 2], pk[4 * m + 3]});
         oacc[db] = mfma32(fv[jj & 3], pb, oacc[db]);
     };
-    auto o_block = [&](const Stage &S, int kb, const uint32_t (&pk)[8]) {
+    auto o_block = [&](const Stage<D> &S, int kb, const uint32_t (&pk)[8]) {
         __builtin_amdgcn_sched_barrier(0);
         bf16x8 fv[4];
         o_init(S, kb, fv);
 #pragma unroll
-        for (int jj = 0; jj < 8; jj++) o_step(S, kb, pk, fv, jj);
-        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+        for (int jj = 0; jj < OS; jj++) o_step(S, kb, pk, fv, jj);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (OS < 3 ? OS : 3), 0);
 #pragma unroll
-        for (int jj = 0; jj < 8; jj++) {
-            if (jj + 3 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        for (int jj = 0; jj < OS; jj++) {
+            if (jj + 3 < OS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
     };
     // The element-wise step of block kb (sacc holds s + rab_p): time-bias
     // mode from the block's key-time range [ka, kb_], then P' packed to bf16.
-    auto pw_block = [&](const Stage &S, int kt, int kb, const floatx16 &sacc, uint32_t (&pk)[8], bool diag,
+    auto pw_block = [&](const Stage<D> &S, int kt, int kb, const floatx16 &sacc, uint32_t (&pk)[8], bool diag,
                         uint32_t ka, uint32_t kb_, auto &&step) {
         const int kstart = kt * BN + kb * 32;
         const uint32_t *kt_lane = &S.kt[kb * 32 + 4 * g];
@@ -411,7 +420,7 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h,
                 kmx[kb] = a.rmax[o_b + ks];
             }
         }
-        const Stage &S = sm.st[kt & 1];
+        const Stage<D> &S = sm.st[kt & 1];
         bool need[2], diag[2];
 #pragma unroll
         for (int kb = 0; kb < 2; kb++) {
@@ -485,14 +494,14 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h,
     // O^T accumulator: lane holds query qrow, d = 32 db + 8(r/4) + 4g + r%4;
     // O = (-ln 2 / N) * sum P' V.
     const float sc = NLN2 * a.inv_n;
-    if (split) {
+    if (D == 128 && split) { // (items are split for D = 128 only)
         // The two halves of a split item add their partial sums into the
         // (zeroed) fp32 output.  Through LDS (the stage tiles are free after
         // the last barrier) so that each atomic instruction covers 64
         // consecutive floats of one row: wave w's rows [32][132].
         float *ot = reinterpret_cast<float *>(&sm.st[0]) + w * 32 * 132;
 #pragma unroll
-        for (int db = 0; db < 4; db++)
+        for (int db = 0; db < DB; db++)
 #pragma unroll
             for (int gr = 0; gr < 4; gr++) {
                 const int d0 = db * 32 + 8 * gr + 4 * g;
@@ -516,7 +525,7 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h,
     if (!qvalid) return;
     const int64_t row = qmap + qrow;
 #pragma unroll
-    for (int db = 0; db < 4; db++) {
+    for (int db = 0; db < DB; db++) {
 #pragma unroll
         for (int gr = 0; gr < 4; gr++) {
             const int d0 = db * 32 + 8 * gr + 4 * g;
@@ -533,11 +542,11 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem &sm, int o_b, int L, int q0, int h,
 
 } // namespace
 
-template <bool HP>
+template <int D, bool HP>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_fwd_bf16_kernel(AttnFwdArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem_raw[];
-    Smem &sm = *reinterpret_cast<Smem *>(smem_raw);
+    Smem<D> &sm = *reinterpret_cast<Smem<D> *>(smem_raw);
     const int item = blockIdx.x;
     if (item >= *a.n_items) return;
     const int2 it = a.items[item];
@@ -555,25 +564,26 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
         qs = a.hoff[b + 1] - a.hoff[b];
         qmap = (int64_t)a.aoff[b] - qs;
     }
-    if (!has_t) fwd_body<HP, 0>(a, sm, o_b, L, qt * BM, h, split, part, qs, qmap);
-    else if (a.wide[b] != 0) fwd_body<HP, 2>(a, sm, o_b, L, qt * BM, h, split, part, qs, qmap);
-    else fwd_body<HP, 1>(a, sm, o_b, L, qt * BM, h, split, part, qs, qmap);
+    if (!has_t) fwd_body<D, HP, 0>(a, sm, o_b, L, qt * BM, h, split, part, qs, qmap);
+    else if (a.wide[b] != 0) fwd_body<D, HP, 2>(a, sm, o_b, L, qt * BM, h, split, part, qs, qmap);
+    else fwd_body<D, HP, 1>(a, sm, o_b, L, qt * BM, h, split, part, qs, qmap);
 }
 
 // The comparator: causal softmax attention O = softmax(Q K^T / sqrt(d)) V on
 // the same skeleton (no bias, no gate, never split), for the pages'
 // comparison of pointwise aggregated attention with softmax attention.
+template <int D>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_softmax_fwd_kernel(AttnFwdArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem_raw[];
-    Smem &sm = *reinterpret_cast<Smem *>(smem_raw);
+    Smem<D> &sm = *reinterpret_cast<Smem<D> *>(smem_raw);
     const int item = blockIdx.x;
     if (item >= *a.n_items) return;
     const int2 it = a.items[item];
     const int b = it.x, qt = it.y >> ITEM_T_SHIFT, h = it.y & 255;
     const int o_b = a.offsets[b];
     const int L = a.offsets[b + 1] - o_b;
-    fwd_body<false, 0, true>(a, sm, o_b, L, qt * BM, h, 0, 0, 0, o_b);
+    fwd_body<D, false, 0, true>(a, sm, o_b, L, qt * BM, h, 0, 0, 0, o_b);
 }
 
 // ---------------------------------------------------------------------------
@@ -647,38 +657,64 @@ __global__ void __launch_bounds__(F32_BM) attn_fwd_f32_kernel(AttnFwdArgs a)
     }
 }
 
-hipError_t launch_attn_fwd_bf16(const AttnFwdArgs &a, int max_items, hipStream_t st)
+namespace {
+template <typename K>
+hipError_t set_smem(K kernel, size_t smem)
+{
+    return hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+}
+
+template <int D>
+hipError_t launch_fwd_d(const AttnFwdArgs &a, int max_items, hipStream_t st)
 {
     static bool init = false;
-    const size_t smem = sizeof(Smem);
+    const size_t smem = sizeof(Smem<D>);
     if (!init) {
-        hipError_t e = hipFuncSetAttribute((const void *)attn_fwd_bf16_kernel<true>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        if (e != hipSuccess) return e;
-        e = hipFuncSetAttribute((const void *)attn_fwd_bf16_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)smem);
+        hipError_t e = set_smem(attn_fwd_bf16_kernel<D, true>, smem);
+        if (e == hipSuccess) e = set_smem(attn_fwd_bf16_kernel<D, false>, smem);
         if (e != hipSuccess) return e;
         init = true;
     }
     if (max_items <= 0) return hipSuccess;
-    if (a.rab_p) hipLaunchKernelGGL(attn_fwd_bf16_kernel<true>, dim3(max_items), dim3(NT), smem, st, a);
-    else hipLaunchKernelGGL(attn_fwd_bf16_kernel<false>, dim3(max_items), dim3(NT), smem, st, a);
+    if (a.rab_p) hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true>), dim3(max_items), dim3(NT), smem, st, a);
+    else hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false>), dim3(max_items), dim3(NT), smem, st, a);
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_softmax_d(const AttnFwdArgs &a, int max_items, hipStream_t st)
+{
+    static bool init = false;
+    const size_t smem = sizeof(Smem<D>);
+    if (!init) {
+        hipError_t e = set_smem(attn_softmax_fwd_kernel<D>, smem);
+        if (e != hipSuccess) return e;
+        init = true;
+    }
+    if (max_items <= 0) return hipSuccess;
+    hipLaunchKernelGGL((attn_softmax_fwd_kernel<D>), dim3(max_items), dim3(NT), smem, st, a);
+    return hipGetLastError();
+}
+} // namespace
+
+hipError_t launch_attn_fwd_bf16(const AttnFwdArgs &a, int max_items, hipStream_t st)
+{
+    switch (a.d) {
+    case 128: return launch_fwd_d<128>(a, max_items, st);
+    case 64: return launch_fwd_d<64>(a, max_items, st);
+    case 32: return launch_fwd_d<32>(a, max_items, st);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_attn_softmax_fwd(const AttnFwdArgs &a, int max_items, hipStream_t st)
 {
-    static bool init = false;
-    const size_t smem = sizeof(Smem);
-    if (!init) {
-        hipError_t e = hipFuncSetAttribute((const void *)attn_softmax_fwd_kernel,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        if (e != hipSuccess) return e;
-        init = true;
+    switch (a.d) {
+    case 128: return launch_softmax_d<128>(a, max_items, st);
+    case 64: return launch_softmax_d<64>(a, max_items, st);
+    case 32: return launch_softmax_d<32>(a, max_items, st);
+    default: return hipErrorInvalidValue;
     }
-    if (max_items <= 0) return hipSuccess;
-    hipLaunchKernelGGL(attn_softmax_fwd_kernel, dim3(max_items), dim3(NT), smem, st, a);
-    return hipGetLastError();
 }
 
 hipError_t launch_attn_fwd_f32(const AttnFwdArgs &a, int max_items, hipStream_t st)

@@ -99,7 +99,11 @@ typedef struct {
 
 /* Head geometry and storage dtype of activations (Q, K, V, U, outputs). */
 typedef struct {
-    hstu_dtype dtype; /* HSTU_BF16: MFMA path (d_qk = d_v = 128); HSTU_F32: any d <= 128 */
+    hstu_dtype dtype; /* HSTU_BF16: MFMA path, d_qk = d_v in {32, 64, 128} for the
+                       * attention forwards (hstu_attn_fwd, its _noalloc variant,
+                       * hstu_softmax_attn_fwd, and their workspace size), 128 for
+                       * every other entry point; HSTU_F32: d in {16, 32, 64, 128}.
+                       * Other sizes: HSTU_ERR_UNSUPPORTED. */
     int32_t heads;    /* H >= 1 */
     int32_t d_qk;
     int32_t d_v;      /* d_qk must equal d_v */
@@ -185,7 +189,7 @@ hstu_status hstu_sl_sample(const hstu_jagged *in, double alpha, const double *u,
  * efficiency table -- computed on the same kernel skeleton as
  * hstu_attn_fwd (same tiles, work list and operand path; the element-wise
  * step is an online softmax), so that the two can be timed side by side.
- *   q, k, v [T][H][d], out [T][H*d] (bf16 only, d = 128); lse (optional,
+ *   q, k, v [T][H][d], out [T][H*d] (bf16 only, d in {32, 64, 128}); lse (optional,
  *   fp32 [T][H]): the natural log of each row's sum of exp(s - max) plus the
  *   max, for a backward.  Workspace: hstu_workspace_size(HSTU_OP_ATTN_FWD).
  */

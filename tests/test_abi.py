@@ -59,7 +59,9 @@ def test_validation_errors_are_reported():
     assert "NULL" in hs.last_error()
     assert _call_fwd(_jag(B=0), _dims()) == bd.HSTU_ERR_ARG
     assert _call_fwd(_jag(n=0), _dims()) == bd.HSTU_ERR_ARG
-    assert _call_fwd(_jag(), _dims(d=64)) == bd.HSTU_ERR_UNSUPPORTED
+    assert _call_fwd(_jag(), _dims(d=48)) == bd.HSTU_ERR_UNSUPPORTED
+    assert _call_fwd(_jag(), _dims(d=256)) == bd.HSTU_ERR_UNSUPPORTED
+    assert _call_fwd(_jag(), _dims(d=64), ldq=256, ldk=256) == bd.HSTU_ERR_WORKSPACE  # d = 64 passes validation
     assert _call_fwd(_jag(), _dims(dtype=bd.HSTU_F32, d=24)) == bd.HSTU_ERR_UNSUPPORTED
     assert _call_fwd(_jag(), _dims(eps=0.0)) == bd.HSTU_ERR_ARG
     assert _call_fwd(_jag(), _dims(), q=None) == bd.HSTU_ERR_ARG
@@ -100,6 +102,11 @@ def _call_bwd(dq=1280, lddq=512):
 
 
 def test_bwd_views_checked_before_launch():
+    lib = hs.load_library()
+    assert lib.hstu_attn_bwd(ctypes.byref(_jag()), ctypes.byref(_dims(d=64)), None, *(bd.CMat(256, 512),) * 3,
+                             bd.CMat(None, 0), None, None, bd.CMat(1024, 512), *(bd.Mat(1280, 512),) * 3,
+                             bd.Mat(None, 0), None, None, None, 0, None) == bd.HSTU_ERR_UNSUPPORTED
+    assert "d = 128" in hs.last_error()  # the backward keeps one head size
     assert _call_bwd(dq=1280 + 8) == bd.HSTU_ERR_ARG
     assert "dq" in hs.last_error()
     assert _call_bwd(lddq=520 + 4) == bd.HSTU_ERR_ARG
@@ -165,6 +172,6 @@ def test_noalloc_rejects_batches_beyond_its_scratch_limit():
     assert "limit" in hs.last_error()
     assert call(20_000, u=1280) == bd.HSTU_ERR_WORKSPACE  # fp32 O staging rows for the gate
     assert "o_save" in hs.last_error()
-    assert lib.hstu_attn_fwd_noalloc(ctypes.byref(_jag()), ctypes.byref(_dims(d=64)), ctypes.byref(bias), m(256),
+    assert lib.hstu_attn_fwd_noalloc(ctypes.byref(_jag()), ctypes.byref(_dims(d=48)), ctypes.byref(bias), m(256),
                                      m(512), m(768), m(None), bd.Mat(1024, 512), None, None,
                                      None) == bd.HSTU_ERR_UNSUPPORTED
