@@ -135,7 +135,8 @@ DEV u32x2 lds_read_tr(const bf16 *p)
 struct BwdLane {
     const uint32_t *qt;   // S.qt + 4g   (index with cr)
     const int64_t *qt64;  // S.qt64 + 4g
-    float *dsk;           // skewed-tile cell of (cr = 0) for this lane; cell of cr at -DKP cr
+    float *dsk;           // skewed-tile cell of (cr = 27) for this lane; cell of cr at DKP (27 - cr)
+                          // (positive offsets fit the LDS instructions' offset field)
     float *dtab;          // this K wave's drab_t table copy for this lane
     uint32_t tk;
     int64_t tk64;
@@ -235,7 +236,7 @@ DEV void pointwise(floatx16 &xacc, const floatx16 &pacc, DpStep &&dp_step, uint3
             const int rr = r + u, cr = 8 * (rr >> 2) + (rr & 3);
             const float ds = pacc[rr] * fac[rr];
             dd[u] = ds;
-            ln.dsk[-DKP * cr] = ds;
+            ln.dsk[DKP * (27 - cr)] = ds;
             if constexpr (DT && TM != 0) {
                 if constexpr (UB == TB_ONE) {
                     tsum += ds;
@@ -690,7 +691,7 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
         const StageP &SPn = sm.sp[n & 1];
         const bool skip = MAIN ? false : (kw0 > q0 + BQ - 1 || kw0 >= L);
         const bool diag = MAIN ? false : kw0 + 31 > q0;
-        ln.dsk = sm.dsk[n & 1] + (krow + (BQ - 1) - 4 * g) * DKP + lq;
+        ln.dsk = sm.dsk[n & 1] + (krow + (BQ - 1) - 4 * g - 27) * DKP + lq;
         bf16 *dsn = sm.ds[n & 1], *ptn = sm.pt[n & 1];
         if (!skip) {
             // X = rab_p window + Q K^T (the window is the products' initial
@@ -804,7 +805,7 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
 #pragma unroll
             for (int gr = 0; gr < 4; gr++) *(u32x2 *)&dsn[krow * SS + 8 * gr + 4 * g] = u32x2{0u, 0u};
 #pragma unroll
-            for (int rr = 0; rr < 16; rr++) ln.dsk[-DKP * (8 * (rr >> 2) + (rr & 3))] = 0.f;
+            for (int rr = 0; rr < 16; rr++) ln.dsk[DKP * (27 - (8 * (rr >> 2) + (rr & 3)))] = 0.f;
         }
         finish(main_c, n, false);
     };
