@@ -134,7 +134,8 @@ hstu_status check_jagged(const hstu_jagged *j)
 }
 
 // `bf16_heads`: the bf16 head sizes the calling entry point's kernels take
-// (the attention forwards take 32, 64 and 128; everything else 128).
+// (the attention forwards and backward take 32, 64 and 128; everything else
+// 128).
 enum Bf16Heads { BF16_D128, BF16_D32_64_128 };
 
 hstu_status check_dims(const hstu_dims *dm, Bf16Heads bf16_heads = BF16_D128)
@@ -400,7 +401,7 @@ hstu_status attn_bwd_launch(const hstu_jagged *j, const hstu_dims *dm, const hst
     a.tbase = tbase;
     {
         ProfScope ps("attn_bwd_bf16_kernel", st);
-        TRY(launched(launch_attn_bwd_bf16(a, max_items, st), "attention backward kernel"));
+        TRY(launched(launch_attn_bwd_bf16(a, d, max_items, st), "attention backward kernel"));
     }
     if (drab_p || (drab_t && has_t)) {
         DrabReduceArgs r{};
@@ -433,6 +434,7 @@ hstu_status attn_bwd_launch(const hstu_jagged *j, const hstu_dims *dm, const hst
         qa.n_items = n_items;
         qa.dq = (bf16 *)dq.ptr;
         qa.lddq = dq.ld;
+        qa.d = d;
         ProfScope ps("dq_gemm_kernel", st);
         TRY(launched(launch_dq_gemm(qa, max_items, st), "dQ kernel"));
     }
@@ -668,7 +670,8 @@ const char *hstu_last_error(void) { return g_err.c_str(); }
 size_t hstu_workspace_size(hstu_op op, const hstu_jagged *j, const hstu_dims *dims, int32_t d_model,
                            int32_t total_cand)
 {
-    if (check_jagged(j) != HSTU_OK || check_dims(dims, op == HSTU_OP_ATTN_FWD ? BF16_D32_64_128 : BF16_D128) != HSTU_OK)
+    const bool attn_op = op == HSTU_OP_ATTN_FWD || op == HSTU_OP_ATTN_BWD;
+    if (check_jagged(j) != HSTU_OK || check_dims(dims, attn_op ? BF16_D32_64_128 : BF16_D128) != HSTU_OK)
         return 0;
     switch (op) {
     case HSTU_OP_ATTN_FWD: return attn_ws(j, dims, fwd_tile(dims), false).total;
@@ -806,7 +809,7 @@ hstu_status hstu_attn_bwd(const hstu_jagged *j, const hstu_dims *dm, const hstu_
                           size_t ws_bytes, void *stream)
 {
     TRY(check_jagged(j));
-    TRY(check_dims(dm));
+    TRY(check_dims(dm, BF16_D32_64_128));
     TRY(check_bias(bias, j));
     if (dm->dtype != HSTU_BF16) return fail(HSTU_ERR_UNSUPPORTED, "hstu_attn_bwd supports bf16 storage only");
     const int H = dm->heads, d = dm->d_qk, F = H * dm->d_v;

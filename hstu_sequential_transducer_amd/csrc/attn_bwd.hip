@@ -55,17 +55,18 @@
 
 namespace {
 
-constexpr int D = 128;
 constexpr int BN = BWD_BN; // 128 keys per workgroup
 constexpr int BQ = 32;     // queries per block
 constexpr int NW = 8;      // waves per workgroup
 constexpr int NT = 64 * NW;
-// Q, dO and dO-lo stage tiles (and the prologue's K tile) are [rows][128]
-// bf16 with no padding; the 16-byte chunks of row r are XOR-swizzled by
-// sw(r) = 4(r%4) + bitrev2((r/4)%4), which keeps the 16-byte operand reads
-// (16 consecutive rows, one chunk) and the transposing reads (4 consecutive
-// rows, 64 bytes each) free of bank conflicts, and lets full blocks be copied
-// global -> LDS directly (4 rows per wave instruction).
+// The head size D (128, 64 or 32) is a template parameter.  Q, dO and dO-lo
+// stage tiles (and the prologue's K tile) are [rows][D] bf16 with no
+// padding; the 16-byte chunks of row r are XOR-swizzled by sw(r) = 4(r%4) +
+// bitrev2((r/4)%4), masked to the row's D/8 chunks, which for D = 128 keeps
+// the 16-byte operand reads (16 consecutive rows, one chunk) and the
+// transposing reads (4 consecutive rows, 64 bytes each) free of bank
+// conflicts, and lets full blocks be copied global -> LDS directly (1024 /
+// (2 D) rows per wave instruction).
 constexpr int SS = 40;     // dS tile [key][query] row stride (bf16)
 constexpr int WIN = 160;   // rab_p window per block (BQ + BN - 1 used)
 constexpr int RING = 256;  // drab_p ring (power of two >= WIN + BQ)
@@ -81,11 +82,13 @@ constexpr float NLN2 = -0.69314718055994531f;
 
 // Stage tiles read by both roles (pointwise waves: block n; accumulating
 // waves: block n - 1): triple buffered.
+template <int D>
 struct alignas(16) StageQ {
     alignas(16) bf16 q[BQ * D];
     alignas(16) bf16 dO[BQ * D];
 };
 // Stage data read by the pointwise waves only: double buffered.
+template <int D>
 struct alignas(16) StageP {
     alignas(16) bf16 dOl[BQ * D]; // low part of dO' (dO' = dO + dOl to ~16 bits)
     float win[WIN];               // rab_p[clip(key - query)], slot = key - query + BQ - 1 - (k0 - q0)
@@ -94,9 +97,10 @@ struct alignas(16) StageP {
     uint32_t pad_[2];
     int64_t qt64[BQ];
 };
+template <int D>
 struct alignas(16) Smem {
-    StageQ sq[3];
-    StageP sp[2];
+    StageQ<D> sq[3];
+    StageP<D> sp[2];
     alignas(16) bf16 ds[2][BN * SS];    // dS [key][query] (the prologue's K tile spans ds and pt)
     alignas(16) bf16 pt[2][BN * SS];    // P' [key][query]
     alignas(16) float dsk[2][DK * DKP]; // fp32 dS skewed: [key - query + BQ - 1][key % 32]
@@ -105,19 +109,21 @@ struct alignas(16) Smem {
     float rabt_rev[32];
     float rabt[128];
 };
-static_assert(offsetof(Smem, pt) == offsetof(Smem, ds) + sizeof(Smem::ds) &&
-                  sizeof(Smem::ds) + sizeof(Smem::pt) >= sizeof(bf16) * BN * D,
+static_assert(offsetof(Smem<128>, pt) == offsetof(Smem<128>, ds) + sizeof(Smem<128>::ds) &&
+                  sizeof(Smem<128>::ds) + sizeof(Smem<128>::pt) >= sizeof(bf16) * BN * 128,
               "the prologue's K tile fits in ds + pt");
-static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget");
+static_assert(sizeof(Smem<128>) <= 160 * 1024, "LDS budget");
 
-// Swizzle of row r: the XOR applied to its 16-byte chunk index.
+// Swizzle of row r: the XOR applied to its 16-byte chunk index (of D/8).
+template <int D>
 DEV int swf(int row)
 {
     const int hi = (row >> 2) & 3;
-    return ((row & 3) << 2) | ((hi & 1) << 1) | (hi >> 1);
+    return (((row & 3) << 2) | ((hi & 1) << 1) | (hi >> 1)) & (D / 8 - 1);
 }
-// Element offset of (row, col) in a swizzled [rows][128] tile.
-DEV int swz(int row, int col) { return row * D + (((col >> 3) ^ swf(row)) << 3) + (col & 7); }
+// Element offset of (row, col) in a swizzled [rows][D] tile.
+template <int D>
+DEV int swz(int row, int col) { return row * D + (((col >> 3) ^ swf<D>(row)) << 3) + (col & 7); }
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short short4v __attribute__((ext_vector_type(4)));
@@ -287,9 +293,17 @@ DEV bf16x8 slice8(const floatx16 &f, int o)
                            __builtin_bit_cast(uint32_t, e2), __builtin_bit_cast(uint32_t, e3)});
 }
 
-template <bool HP, int TM, bool DT, bool DQA>
-DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int k0, int h)
+template <int D, bool HP, int TM, bool DT, bool DQA>
+DEV void bwd_body(const AttnBwdArgs &a, Smem<D> &sm, int b_seq, int o_b, int L, int k0, int h)
 {
+    constexpr int KS = D / 16;     // K steps of the X and dP products
+    constexpr int DB = D / 32;     // 32-wide d-blocks of dV^T, dK^T (and the K/V registers)
+    constexpr int NCH = D / 8;     // 16-byte chunks per row
+    constexpr int RPI = 64 / NCH;  // rows per wave copy instruction
+    constexpr int GPP = BQ / RPI;  // copy groups per stage plane (8, 4 or 2)
+    static_assert(GPP == 8 || GPP == 4 || GPP == 2, "copy groups per plane");
+    using StageQD = StageQ<D>;
+    using StagePD = StageP<D>;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 5, lq = l & 31;
     const int p = w & 3;          // key group: keys 32p..32p+31 of the tile
     const bool awave = w < 4;     // accumulating wave (else pointwise wave); wave-uniform
@@ -309,9 +323,9 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
     bf16 *kt = &sm.ds[0][0]; // prologue only
     if constexpr (DQA) {
 #pragma unroll
-        for (int i = 0; i < BN / (4 * NW); i++) {
-            const int r0 = 4 * ((BN / (4 * NW)) * w + i), row = r0 + (l >> 4);
-            const int c = (l & 15) ^ swf(row);
+        for (int i = 0; i < BN / (RPI * NW); i++) {
+            const int r0 = RPI * ((BN / (RPI * NW)) * w + i), row = r0 + l / NCH;
+            const int c = (l % NCH) ^ swf<D>(row);
             const int key = min(k0 + row, L - 1);
             __builtin_amdgcn_global_load_lds((const void *)(K + (int64_t)(o_b + key) * a.ldk + h * D + c * 8),
                                              (lds_void *)(kt + r0 * D), 16, 0, 0);
@@ -325,16 +339,16 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
     // 0..7 of acc2[i]) and V row (elements 8..15), 16-byte chunk s holding
     // d = 16s + 8g .. +8 (B operands of X = Q K^T and dP = dO' V^T).
     // Lane = key, d = 32 db + 8(r/4) + 4g + r%4 for the accumulators.
-    floatx16 acc[4], acc2[4];
+    floatx16 acc[DB], acc2[DB];
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < DB; i++)
 #pragma unroll
         for (int r = 0; r < 16; r++) acc[i][r] = acc2[i][r] = 0.f;
     if (!awave && kvalid) {
         const int64_t row = o_b + mykey;
         const bf16 *kp = K + row * a.ldk + h * D + g * 8, *vp = V + row * a.ldv + h * D + g * 8;
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
+        for (int i = 0; i < DB; i++) {
             const u32x4 k1 = *(const u32x4 *)(kp + 32 * i), k2 = *(const u32x4 *)(kp + 32 * i + 16);
             const u32x4 v1 = *(const u32x4 *)(vp + 32 * i), v2 = *(const u32x4 *)(vp + 32 * i + 16);
 #pragma unroll
@@ -366,27 +380,37 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
         tkmax = __builtin_amdgcn_readfirstlane(tkmax);
     }
 
-    // ---- query-block stage loader.  Full blocks: 24 groups of 4 rows (Q,
-    // dO, dO-lo) copied straight into LDS, 3 per wave; lane l fills physical
-    // chunk l%16 of row 4(G%8) + l/16.  The last, partial block goes through
+    // ---- query-block stage loader.  Full blocks: 3 GPP groups of RPI rows
+    // (Q, dO, dO-lo; 24 groups of 4 rows at D = 128) copied straight into
+    // LDS, spread over the copying waves; lane l fills physical chunk l % NCH
+    // of row RPI (G % GPP) + l / NCH.  The last, partial block goes through
     // registers (rows past the sequence: Q from the last row, dO = 0, so they
     // contribute nothing).
-    const int lcq = tid >> 4, leq = tid & 15; // partial path: 32 queries x 16 threads x 8 elements
+    const int lcq = tid / NCH, leq = tid % NCH; // partial path: 32 queries x NCH threads x 8 elements
     float wreg = 0.f;
     uint32_t treg = 0, tmn = 0xFFFFFFFFu, tmx = 0u;
     int64_t treg64 = 0;
-    // nw waves share the 24 copies; wi = this wave's index among them.
+    // nw waves share the copies; wi = this wave's index among them.
     // Row bases are wave-uniform 64-bit pointers; the lane part of each
     // address is a 32-bit offset (24-bit products).
-    auto gload_direct = [&](auto nw_c, int wi, int q0, StageQ &SQ, StageP &SP) {
+    auto gload_direct = [&](auto nw_c, int wi, int q0, StageQD &SQ, StagePD &SP) {
         constexpr int NWC = decltype(nw_c)::value;
+        constexpr int TOT = 3 * GPP; // copy groups of the three planes
         const int64_t rq = (int64_t)(o_b + q0);
         const bf16 *bq = Q + rq * a.ldq + h * D, *bo = dO + rq * ld_do + h * D, *bl = dOlo + rq * ld_do + h * D;
 #pragma unroll
-        for (int i = 0; i < 24 / NWC; i++) {
-            const int G = (24 / NWC) * wi + i, plane = G >> 3, r0 = 4 * (G & 7);
-            const int row = r0 + (l >> 4);
-            const int c = (l & 15) ^ swf(row);
+        for (int i = 0; i < (TOT + NWC - 1) / NWC; i++) {
+            int G;
+            if constexpr (TOT % NWC == 0) {
+                G = (TOT / NWC) * wi + i;
+            } else {
+                G = wi + NWC * i;
+                if (G >= TOT) break; // (wave-uniform)
+            }
+            // (GPP is a power of two: shift and mask, no signed-division fix-up)
+            const int plane = G >> (GPP == 8 ? 3 : (GPP == 4 ? 2 : 1)), r0 = RPI * (G & (GPP - 1));
+            const int row = r0 + l / NCH;
+            const int c = (l % NCH) ^ swf<D>(row);
             const uint32_t ld = plane == 0 ? (uint32_t)a.ldq : (uint32_t)ld_do;
             const uint32_t off = __umul24((uint32_t)row, ld) + 8u * (uint32_t)c;
             const bf16 *src = (plane == 0 ? bq : (plane == 1 ? bo : bl)) + off;
@@ -416,7 +440,9 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
             }
         }
     };
-    auto load_partial = [&](int q0, StageQ &SQ, StageP &SP) {
+    auto load_partial = [&](int q0, StageQD &SQ, StagePD &SP) {
+        if constexpr (BQ * NCH < NT)
+            if (lcq >= BQ) return; // (D < 128: fewer threads than the workgroup's)
         const int qi = q0 + lcq;
         const bool ok = qi < L;
         const int64_t row = (int64_t)(o_b + (ok ? qi : L - 1));
@@ -424,11 +450,11 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
         const u32x4 qv = *(const u32x4 *)(Q + row * a.ldq + h * D + col);
         const u32x4 dv = ok ? *(const u32x4 *)(dO + row * ld_do + h * D + col) : u32x4{0, 0, 0, 0};
         const u32x4 lv = ok ? *(const u32x4 *)(dOlo + row * ld_do + h * D + col) : u32x4{0, 0, 0, 0};
-        *(u32x4 *)&SQ.q[swz(lcq, col)] = qv;
-        *(u32x4 *)&SQ.dO[swz(lcq, col)] = dv;
-        *(u32x4 *)&SP.dOl[swz(lcq, col)] = lv;
+        *(u32x4 *)&SQ.q[swz<D>(lcq, col)] = qv;
+        *(u32x4 *)&SQ.dO[swz<D>(lcq, col)] = dv;
+        *(u32x4 *)&SP.dOl[swz<D>(lcq, col)] = lv;
     };
-    auto sstore_tables = [&](StageP &S, int tt) {
+    auto sstore_tables = [&](StagePD &S, int tt) {
         if constexpr (HP)
             if (tt >= 0 && tt < WIN) S.win[tt] = wreg;
         if constexpr (TM != 0) {
@@ -447,7 +473,7 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
     // waves (4-byte copies, lane i -> 4i bytes past the wave's LDS base): the
     // window by waves 0-2 (slots 64 w + lane), the query times and their
     // range by wave 3 (lanes 0-31, then 32, 33).
-    auto gload_tables_direct = [&](int q0, StageP &SP) {
+    auto gload_tables_direct = [&](int q0, StagePD &SP) {
         const int pw = w;
         if constexpr (HP) {
             if (pw < 3 && 64 * pw + l < WIN) {
@@ -474,14 +500,14 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
     sstore_tables(sm.sp[0], tid);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    bf16x8 opnd[DQA ? 8 : 1]; // DQA, accumulating wave: K d-block p of all rows (dQ operand)
+    bf16x8 opnd[DQA ? 8 : 1]; // DQA, accumulating wave p < DB: K d-block p of all rows (dQ operand)
     if constexpr (DQA) {
-        if (awave) {
+        if (awave && (DB == 4 || p < DB)) {
 #pragma unroll
             for (int t = 0; t < BN / 16; t++) {
                 const int kr1 = 16 * t + 8 * g + tsl;
-                const u32x2 k1 = lds_read_tr(&kt[swz(kr1, 32 * p + cpart)]);
-                const u32x2 k2 = lds_read_tr(&kt[swz(kr1 + 4, 32 * p + cpart)]);
+                const u32x2 k1 = lds_read_tr(&kt[swz<D>(kr1, 32 * p + cpart)]);
+                const u32x2 k2 = lds_read_tr(&kt[swz<D>(kr1 + 4, 32 * p + cpart)]);
                 opnd[t] = as_bf16x8(u32x4{k1[0], k1[1], k2[0], k2[1]});
             }
         }
@@ -496,7 +522,7 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
     // 32 queries.  The B operands are this lane's key row of the P' and dS
     // tiles, queries 16m + {4g..4g+3, 8+4g..8+4g+3} (the order of the
     // transposing reads' k index).
-    auto acc_block = [&](const StageQ &SQ, int b) {
+    auto acc_block = [&](const StageQD &SQ, int b) {
         const bf16 *ptb = sm.pt[b], *dsb = sm.ds[b];
         const int krow = 32 * p + lq;
         __builtin_amdgcn_sched_barrier(0);
@@ -510,31 +536,32 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
             pb[m] = as_bf16x8(u32x4{p1[0], p1[1], p2[0], p2[1]});
             sb[m] = as_bf16x8(u32x4{s1[0], s1[1], s2[0], s2[1]});
         }
-        // 16 steps j: m = j / 8, db = (j / 2) % 4; even j: dO'^T slice -> dV, odd j:
-        // Q^T slice -> dK.  Transposing reads run three steps ahead.
+        // NJ = 4 DB steps j: m = j / (2 DB), db = (j / 2) % DB; even j: dO'^T slice
+        // -> dV, odd j: Q^T slice -> dK.  Transposing reads run three steps ahead.
+        constexpr int NJ = 4 * DB;
         bf16x8 fa[4];
         auto fetch = [&](int j) {
-            const int m = j >> 3, db = (j >> 1) & 3;
+            const int m = j / (2 * DB), db = (j >> 1) % DB;
             const int qr1 = 16 * m + 4 * g + tsl; // query row of the transposing read
             const bf16 *t = (j & 1) ? SQ.q : SQ.dO;
-            const u32x2 a1 = lds_read_tr(&t[swz(qr1, db * 32 + cpart)]);
-            const u32x2 a2 = lds_read_tr(&t[swz(qr1 + 8, db * 32 + cpart)]);
+            const u32x2 a1 = lds_read_tr(&t[swz<D>(qr1, db * 32 + cpart)]);
+            const u32x2 a2 = lds_read_tr(&t[swz<D>(qr1 + 8, db * 32 + cpart)]);
             fa[j & 3] = as_bf16x8(u32x4{a1[0], a1[1], a2[0], a2[1]});
         };
         fetch(0);
         fetch(1);
         fetch(2);
 #pragma unroll
-        for (int j = 0; j < 16; j++) {
-            if (j + 3 < 16) fetch(j + 3);
-            const int m = j >> 3, db = (j >> 1) & 3;
+        for (int j = 0; j < NJ; j++) {
+            if (j + 3 < NJ) fetch(j + 3);
+            const int m = j / (2 * DB), db = (j >> 1) % DB;
             if (j & 1) acc2[db] = mfma32(fa[j & 3], sb[m], acc2[db]);
             else acc[db] = mfma32(fa[j & 3], pb[m], acc[db]);
         }
         __builtin_amdgcn_sched_group_barrier(0x100, 14, 0); // B operands and the first three steps
 #pragma unroll
-        for (int j = 0; j < 16; j++) {
-            if (j + 3 < 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        for (int j = 0; j < NJ; j++) {
+            if (j + 3 < NJ) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -560,6 +587,8 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
     // (all 128 keys): dQ[32 queries][d-block p] = sum over the keys of
     // dS[q][key] K[key][d], added to the fp32 accumulator with atomics.
     auto dq_block = [&](const bf16 *dst, int q0m, bool full) {
+        if constexpr (DB < 4)
+            if (p >= DB) return; // (wave-uniform) d-block p does not exist
         floatx16 qacc;
 #pragma unroll
         for (int r = 0; r < 16; r++) qacc[r] = 0.f;
@@ -687,8 +716,8 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
         const int q0 = k0 + n * BQ;
         if constexpr (TM == 2)
             if (n + 1 < nqb) gload_tables(q0 + BQ, tid - NT / 2);
-        const StageQ &SQn = sm.sq[n % 3];
-        const StageP &SPn = sm.sp[n & 1];
+        const StageQD &SQn = sm.sq[n % 3];
+        const StagePD &SPn = sm.sp[n & 1];
         const bool skip = MAIN ? false : (kw0 > q0 + BQ - 1 || kw0 >= L);
         const bool diag = MAIN ? false : kw0 + 31 > q0;
         ln.dsk = sm.dsk[n & 1] + (krow + (BQ - 1) - 4 * g - 27) * DKP + lq;
@@ -708,35 +737,36 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
             }
             bf16x8 fd[3], fl[3]; // dP operands, read two steps ahead
             auto fetch_dp = [&](int s) {
-                const int o = swz(lq, s * 16 + g * 8);
+                const int o = swz<D>(lq, s * 16 + g * 8);
                 fd[s % 3] = *(const bf16x8 *)&SQn.dO[o];
                 fl[s % 3] = *(const bf16x8 *)&SPn.dOl[o];
             };
             __builtin_amdgcn_sched_barrier(0);
             {
                 bf16x8 fq[3];
-                auto fetch = [&](int s) { fq[s % 3] = *(const bf16x8 *)&SQn.q[swz(lq, s * 16 + g * 8)]; };
+                auto fetch = [&](int s) { fq[s % 3] = *(const bf16x8 *)&SQn.q[swz<D>(lq, s * 16 + g * 8)]; };
                 fetch(0);
                 fetch(1);
 #pragma unroll
-                for (int s = 0; s < 8; s++) {
-                    if (s + 2 < 8) fetch(s + 2);
+                for (int s = 0; s < KS; s++) {
+                    if (s + 2 < KS) fetch(s + 2);
                     xacc = mfma32(fq[s % 3], slice8(acc2[s >> 1], 4 * (s & 1)), xacc);
                 }
                 fetch_dp(0);
                 fetch_dp(1);
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0); // Q reads of steps 0, 1
 #pragma unroll
-                for (int s = 0; s < 8; s++) {
-                    if (s + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // read of step s + 2
+                for (int s = 0; s < KS; s++) {
+                    if (s + 2 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // read of step s + 2
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // MFMA of step s
                 }
                 __builtin_amdgcn_sched_group_barrier(0x100, 4, 0); // dP operands of steps 0, 1
             }
             __builtin_amdgcn_sched_barrier(0);
             auto dp_step = [&](int s) {
+                if (s >= KS) return; // (D < 128: the products fill the first KS steps)
                 const bf16x8 d0 = fd[s % 3], d1 = fl[s % 3];
-                if (s + 2 < 8) fetch_dp(s + 2);
+                if (s + 2 < KS) fetch_dp(s + 2);
                 pacc = mfma32(d0, slice8(acc2[s >> 1], 8 + 4 * (s & 1)), pacc);
                 pacc = mfma32(d1, slice8(acc2[s >> 1], 8 + 4 * (s & 1)), pacc);
             };
@@ -846,7 +876,7 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
             const int64_t row = o_b + mykey;
             bf16 *dvp = a.dv + row * a.lddv + h * D, *dkp = a.dk + row * a.lddk + h * D;
 #pragma unroll
-            for (int db = 0; db < 4; db++)
+            for (int db = 0; db < DB; db++)
 #pragma unroll
                 for (int gr = 0; gr < 4; gr++) {
                     const int d0 = db * 32 + 8 * gr + 4 * g;
@@ -892,11 +922,11 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem &sm, int b_seq, int o_b, int L, int
 // TMODE: 0 = no time bias; 1 = time bias with drab_t; 2 = time bias without
 // drab_t.  Sequences whose time span does not fit 32 bits take the exact
 // 64-bit body.
-template <bool HP, int TMODE>
+template <int D, bool HP, int TMODE>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_bwd_bf16_kernel(AttnBwdArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem_raw[];
-    Smem &sm = *reinterpret_cast<Smem *>(smem_raw);
+    Smem<D> &sm = *reinterpret_cast<Smem<D> *>(smem_raw);
     const int item = blockIdx.x;
     if (item >= *a.n_items) return;
     const int2 it = a.items[item];
@@ -917,47 +947,58 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
     constexpr bool DT = TMODE == 1;
     const bool dqa = a.ds_base[b] < 0; // this sequence's dS planes did not fit: dQ by atomics
     if constexpr (TMODE == 0) {
-        if (dqa) bwd_body<HP, 0, false, true>(a, sm, b, o_b, L, k0, h);
-        else bwd_body<HP, 0, false, false>(a, sm, b, o_b, L, k0, h);
+        if (dqa) bwd_body<D, HP, 0, false, true>(a, sm, b, o_b, L, k0, h);
+        else bwd_body<D, HP, 0, false, false>(a, sm, b, o_b, L, k0, h);
     } else if (a.wide[b] != 0) {
-        if (dqa) bwd_body<HP, 2, DT, true>(a, sm, b, o_b, L, k0, h);
-        else bwd_body<HP, 2, DT, false>(a, sm, b, o_b, L, k0, h);
+        if (dqa) bwd_body<D, HP, 2, DT, true>(a, sm, b, o_b, L, k0, h);
+        else bwd_body<D, HP, 2, DT, false>(a, sm, b, o_b, L, k0, h);
     } else {
-        if (dqa) bwd_body<HP, 1, DT, true>(a, sm, b, o_b, L, k0, h);
-        else bwd_body<HP, 1, DT, false>(a, sm, b, o_b, L, k0, h);
+        if (dqa) bwd_body<D, HP, 1, DT, true>(a, sm, b, o_b, L, k0, h);
+        else bwd_body<D, HP, 1, DT, false>(a, sm, b, o_b, L, k0, h);
     }
 }
 
 namespace {
-template <bool HP, int TMODE>
+template <int D, bool HP, int TMODE>
 hipError_t launch_variant(const AttnBwdArgs &a, int max_items, hipStream_t st)
 {
     static bool init = false;
-    const size_t smem = sizeof(Smem);
+    const size_t smem = sizeof(Smem<D>);
     if (!init) {
-        hipError_t e = hipFuncSetAttribute((const void *)attn_bwd_bf16_kernel<HP, TMODE>,
+        hipError_t e = hipFuncSetAttribute((const void *)attn_bwd_bf16_kernel<D, HP, TMODE>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
         if (e != hipSuccess) return e;
         init = true;
     }
-    hipLaunchKernelGGL((attn_bwd_bf16_kernel<HP, TMODE>), dim3(max_items), dim3(NT), smem, st, a);
+    hipLaunchKernelGGL((attn_bwd_bf16_kernel<D, HP, TMODE>), dim3(max_items), dim3(NT), smem, st, a);
     return hipGetLastError();
 }
-} // namespace
 
-hipError_t launch_attn_bwd_bf16(const AttnBwdArgs &a, int max_items, hipStream_t st)
+template <int D>
+hipError_t launch_d(const AttnBwdArgs &a, int max_items, hipStream_t st)
 {
-    if (max_items <= 0) return hipSuccess;
     const bool has_t = a.ts != nullptr && a.rab_t != nullptr;
     const int tmode = !has_t ? 0 : (a.drab_t ? 1 : 2);
     if (a.rab_p) {
-        if (tmode == 0) return launch_variant<true, 0>(a, max_items, st);
-        if (tmode == 1) return launch_variant<true, 1>(a, max_items, st);
-        return launch_variant<true, 2>(a, max_items, st);
+        if (tmode == 0) return launch_variant<D, true, 0>(a, max_items, st);
+        if (tmode == 1) return launch_variant<D, true, 1>(a, max_items, st);
+        return launch_variant<D, true, 2>(a, max_items, st);
     }
-    if (tmode == 0) return launch_variant<false, 0>(a, max_items, st);
-    if (tmode == 1) return launch_variant<false, 1>(a, max_items, st);
-    return launch_variant<false, 2>(a, max_items, st);
+    if (tmode == 0) return launch_variant<D, false, 0>(a, max_items, st);
+    if (tmode == 1) return launch_variant<D, false, 1>(a, max_items, st);
+    return launch_variant<D, false, 2>(a, max_items, st);
+}
+} // namespace
+
+hipError_t launch_attn_bwd_bf16(const AttnBwdArgs &a, int d, int max_items, hipStream_t st)
+{
+    if (max_items <= 0) return hipSuccess;
+    switch (d) {
+    case 128: return launch_d<128>(a, max_items, st);
+    case 64: return launch_d<64>(a, max_items, st);
+    case 32: return launch_d<32>(a, max_items, st);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 // ---------------------------------------------------------------------------

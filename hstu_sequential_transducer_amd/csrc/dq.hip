@@ -7,7 +7,7 @@
 // L_b rounded up to 128, with zeros wherever j > i; every entry this kernel
 // reads for a valid query was written there.  Workgroup = 128 queries of one
 // (sequence, head), 4 waves of 32.  Keys stream in tiles of 64 through LDS
-// (dS tile [128][64] and K tile [64][128], double buffered, copied global ->
+// (dS tile [128][64] and K tile [64][d], double buffered, copied global ->
 // LDS directly); each wave accumulates dQ^T = K^T dS^T on 32x32x16 bf16 MFMA
 // (K^T by transposing LDS reads) and stores bf16 dQ.  The two stages are
 // separate LDS objects with the tile loop unrolled by two, so the compiler
@@ -19,24 +19,28 @@
 
 namespace {
 
-constexpr int D = 128;
 constexpr int BM = 128; // queries per workgroup
 constexpr int BK = 64;  // keys per tile
 constexpr int NT = 256;
 
+// D: the head size (128, 64 or 32).
+template <int D>
 struct alignas(16) DqStage {
     alignas(16) bf16 s[BM * BK]; // dS tile [query][key], 128-byte rows
-    alignas(16) bf16 k[BK * D];  // K tile [key][d], 256-byte rows
+    alignas(16) bf16 k[BK * D];  // K tile [key][d], 2D-byte rows
 };
 
-// 256-byte rows (K tile): 16-byte chunk c of row r at c ^ sw(r),
-// sw(r) = 4(r%4) + bitrev2((r/4)%4) (conflict-free transposing reads).
+// K tile rows: 16-byte chunk c of row r at c ^ sw(r), sw(r) = 4(r%4) +
+// bitrev2((r/4)%4) masked to the row's D/8 chunks (conflict-free
+// transposing reads at D = 128).
+template <int D>
 DEV int swf(int row)
 {
     const int hi = (row >> 2) & 3;
-    return ((row & 3) << 2) | ((hi & 1) << 1) | (hi >> 1);
+    return (((row & 3) << 2) | ((hi & 1) << 1) | (hi >> 1)) & (D / 8 - 1);
 }
-DEV int swz(int row, int col) { return row * D + (((col >> 3) ^ swf(row)) << 3) + (col & 7); }
+template <int D>
+DEV int swz(int row, int col) { return row * D + (((col >> 3) ^ swf<D>(row)) << 3) + (col & 7); }
 // 128-byte rows (dS tile): chunk c of row r at c ^ ((r/2) % 8), so 16
 // consecutive rows read at one chunk hit 16 different 16-byte bank groups.
 DEV int s8f(int row) { return (row >> 1) & 7; }
@@ -57,9 +61,14 @@ DEV u32x2 lds_read_tr(const bf16 *p)
 
 } // namespace
 
+template <int D>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) dq_gemm_kernel(DqArgs a)
 {
-    __shared__ DqStage st0, st1;
+    constexpr int DB = D / 32;     // 32-wide d-blocks of dQ^T
+    constexpr int NCH = D / 8;     // 16-byte chunks per K row
+    constexpr int RPI = 64 / NCH;  // K rows per wave copy instruction
+    constexpr int KPW = BK / RPI / 4; // K copy instructions per wave
+    __shared__ DqStage<D> st0, st1;
     const int item = blockIdx.x;
     if (item >= *a.n_items) return;
     const int2 it = a.items[item];
@@ -87,8 +96,8 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int tj = l & 15, tsl = tj >> 2;
     const int cpart = ((l >> 4) & 1) * 16 + 4 * (tj & 3);
 
-    // copies: dS 16 groups of 8 rows, K 16 groups of 4 rows; 4 + 4 per wave
-    auto gload = [&](int kt, DqStage &S) {
+    // copies: dS 16 groups of 8 rows, K BK / RPI groups of RPI rows; 4 + KPW per wave
+    auto gload = [&](int kt, DqStage<D> &S) {
         const int kb0 = kt * BK;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
@@ -98,25 +107,25 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
                                              (lds_void *)(S.s + r0 * BK), 16, 0, 0);
         }
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int r0 = 4 * (4 * w + i), row = r0 + (l >> 4);
-            const int c = (l & 15) ^ swf(row);
+        for (int i = 0; i < KPW; i++) {
+            const int r0 = RPI * (KPW * w + i), row = r0 + l / NCH;
+            const int c = (l % NCH) ^ swf<D>(row);
             const int key = min(kb0 + row, L - 1);
             __builtin_amdgcn_global_load_lds((const void *)(a.k + (int64_t)(o_b + key) * a.ldk + h * D + c * 8),
                                              (lds_void *)(S.k + r0 * D), 16, 0, 0);
         }
     };
 
-    floatx16 acc[4];
+    floatx16 acc[DB];
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < DB; i++)
 #pragma unroll
         for (int r = 0; r < 16; r++) acc[i][r] = 0.f;
 
     // One tile: 4 steps of 16 keys.  B = dS^T fragment of this lane's query,
     // keys 16m + {4g..4g+3, 8+4g..8+4g+3} (the order of the transposing
     // reads' k index); A = K^T for d-block db.
-    auto compute = [&](const DqStage &S) {
+    auto compute = [&](const DqStage<D> &S) {
         const int qrow = 32 * w + lq;
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -126,9 +135,9 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
             const bf16x8 sb = as_bf16x8(u32x4{s1[0], s1[1], s2[0], s2[1]});
             const int key1 = 16 * m + 4 * g + tsl;
 #pragma unroll
-            for (int db = 0; db < 4; db++) {
-                const u32x2 r1 = lds_read_tr(&S.k[swz(key1, db * 32 + cpart)]);
-                const u32x2 r2 = lds_read_tr(&S.k[swz(key1 + 8, db * 32 + cpart)]);
+            for (int db = 0; db < DB; db++) {
+                const u32x2 r1 = lds_read_tr(&S.k[swz<D>(key1, db * 32 + cpart)]);
+                const u32x2 r2 = lds_read_tr(&S.k[swz<D>(key1 + 8, db * 32 + cpart)]);
                 acc[db] = mfma32(as_bf16x8(u32x4{r1[0], r1[1], r2[0], r2[1]}), sb, acc[db]);
             }
         }
@@ -155,7 +164,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
     if (qrow >= L) return;
     bf16 *out = a.dq + (int64_t)(o_b + qrow) * a.lddq + h * D;
 #pragma unroll
-    for (int db = 0; db < 4; db++)
+    for (int db = 0; db < DB; db++)
 #pragma unroll
         for (int gr = 0; gr < 4; gr++) {
             const int d0 = db * 32 + 8 * gr + 4 * g;
@@ -167,6 +176,11 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 hipError_t launch_dq_gemm(const DqArgs &a, int max_items, hipStream_t st)
 {
     if (max_items <= 0) return hipSuccess;
-    hipLaunchKernelGGL(dq_gemm_kernel, dim3(max_items), dim3(NT), 0, st, a);
+    switch (a.d) {
+    case 128: hipLaunchKernelGGL(dq_gemm_kernel<128>, dim3(max_items), dim3(NT), 0, st, a); break;
+    case 64: hipLaunchKernelGGL(dq_gemm_kernel<64>, dim3(max_items), dim3(NT), 0, st, a); break;
+    case 32: hipLaunchKernelGGL(dq_gemm_kernel<32>, dim3(max_items), dim3(NT), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }

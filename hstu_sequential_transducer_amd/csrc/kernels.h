@@ -173,7 +173,8 @@ struct AttnBwdArgs {
     const int64_t *tbase;
 };
 constexpr int BWD_BN = 128; // keys per workgroup
-hipError_t launch_attn_bwd_bf16(const AttnBwdArgs &a, int max_items, hipStream_t st);
+// d: the head size (128, 64 or 32), which selects the kernel instantiation
+hipError_t launch_attn_bwd_bf16(const AttnBwdArgs &a, int d, int max_items, hipStream_t st);
 // drab_p += and drab_t = the items' partial sums, added in a fixed order
 // (sequence, key - query, key tile): the bias gradients do not depend on
 // the order in which the backward's items ran.
@@ -206,6 +207,7 @@ struct DqArgs {
     const int *n_items;
     bf16 *dq;
     int64_t lddq;
+    int d;                      // head size: 128, 64 or 32
 };
 hipError_t launch_dq_gemm(const DqArgs &a, int max_items, hipStream_t st);
 // Zeroes the dq_acc rows ([T][F] fp32) of the sequences with ds_base < 0.

@@ -100,10 +100,11 @@ typedef struct {
 /* Head geometry and storage dtype of activations (Q, K, V, U, outputs). */
 typedef struct {
     hstu_dtype dtype; /* HSTU_BF16: MFMA path, d_qk = d_v in {32, 64, 128} for the
-                       * attention forwards (hstu_attn_fwd, its _noalloc variant,
-                       * hstu_softmax_attn_fwd, and their workspace size), 128 for
-                       * every other entry point; HSTU_F32: d in {16, 32, 64, 128}.
-                       * Other sizes: HSTU_ERR_UNSUPPORTED. */
+                       * attention entry points (hstu_attn_fwd, its _noalloc
+                       * variant, hstu_softmax_attn_fwd, hstu_attn_bwd, and their
+                       * workspace sizes), 128 for the layer and M-FALCON entry
+                       * points; HSTU_F32: d in {16, 32, 64, 128}.  Other sizes:
+                       * HSTU_ERR_UNSUPPORTED. */
     int32_t heads;    /* H >= 1 */
     int32_t d_qk;
     int32_t d_v;      /* d_qk must equal d_v */
@@ -198,7 +199,7 @@ hstu_status hstu_softmax_attn_fwd(const hstu_jagged *j, const hstu_dims *dims, h
 
 /*
  * Backward of hstu_attn_fwd (chain rule through Eq. 3's Norm (.) U and
- * Eq. 2).  bf16 only.
+ * Eq. 2).  bf16 only, d in {32, 64, 128}.
  *   dout: upstream gradient at G when u is given (then o_save and ln_stats
  *   from the forward are required), else at O.
  *   Outputs (storage dtype): dq, dk [T][H][d], dv [T][H][d], du [T][H*d]

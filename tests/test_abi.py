@@ -103,10 +103,12 @@ def _call_bwd(dq=1280, lddq=512):
 
 def test_bwd_views_checked_before_launch():
     lib = hs.load_library()
-    assert lib.hstu_attn_bwd(ctypes.byref(_jag()), ctypes.byref(_dims(d=64)), None, *(bd.CMat(256, 512),) * 3,
-                             bd.CMat(None, 0), None, None, bd.CMat(1024, 512), *(bd.Mat(1280, 512),) * 3,
-                             bd.Mat(None, 0), None, None, None, 0, None) == bd.HSTU_ERR_UNSUPPORTED
-    assert "d = 128" in hs.last_error()  # the backward keeps one head size
+    call = lambda d: lib.hstu_attn_bwd(ctypes.byref(_jag()), ctypes.byref(_dims(d=d)), None,
+                                       *(bd.CMat(256, 512),) * 3, bd.CMat(None, 0), None, None, bd.CMat(1024, 512),
+                                       *(bd.Mat(1280, 512),) * 3, bd.Mat(None, 0), None, None, None, 0, None)
+    assert call(48) == bd.HSTU_ERR_UNSUPPORTED
+    assert "{32, 64, 128}" in hs.last_error()
+    assert call(64) == bd.HSTU_ERR_WORKSPACE  # d = 64 passes validation
     assert _call_bwd(dq=1280 + 8) == bd.HSTU_ERR_ARG
     assert "dq" in hs.last_error()
     assert _call_bwd(lddq=520 + 4) == bd.HSTU_ERR_ARG
@@ -134,6 +136,8 @@ def test_layer_bwd_validation():
     """hstu_layer_bwd rejects what it does not take before enqueuing
     anything (the pointers here are never dereferenced)."""
     assert _call_layer_bwd(_dims(dtype=bd.HSTU_F32, d=32)) == bd.HSTU_ERR_UNSUPPORTED
+    assert _call_layer_bwd(_dims(d=64)) == bd.HSTU_ERR_UNSUPPORTED  # the layer keeps d = 128
+    assert "d = 128" in hs.last_error()
     assert _call_layer_bwd(_dims(), D=70) == bd.HSTU_ERR_UNSUPPORTED
     assert "multiple of 8" in hs.last_error()
     assert _call_layer_bwd(_dims(), dx=256) == bd.HSTU_ERR_ARG

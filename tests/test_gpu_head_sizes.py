@@ -1,8 +1,9 @@
-"""GPU parity of the bf16 attention forwards at head sizes d = 64 and d = 32
-(hstu_attn_fwd, hstu_attn_fwd_noalloc, hstu_softmax_attn_fwd through the C
-ABI) against the fp64 oracle.  The kernels are the d = 128 ones instantiated
-for the smaller head: K/V tiles of [64][d], d/16 MFMA steps for S, d/32
-column blocks for O, and no split of long query tiles."""
+"""GPU parity of bf16 attention at head sizes d = 64 and d = 32
+(hstu_attn_fwd, hstu_attn_fwd_noalloc, hstu_softmax_attn_fwd and
+hstu_attn_bwd through the C ABI) against the fp64 oracle.  The kernels are
+the d = 128 ones instantiated for the smaller head: tiles of [rows][d], d/16
+MFMA steps for the d contractions, d/32 column blocks for the d-wide
+accumulators, and no split of long forward query tiles."""
 import numpy as np
 import pytest
 import torch
@@ -116,12 +117,93 @@ def test_softmax_head_size(d):
     assert el <= F32_TOL
 
 
-def test_head_size_128_only_entry_points_refuse_smaller_heads():
-    """The backward keeps d = 128: a d = 64 call returns
-    HSTU_ERR_UNSUPPORTED before any device work."""
-    w = work(90, [40, 9], 64)
-    T = w.total
+# ---------------------------------------------------------------- backward
+
+def bwd_work(seed, lengths, d, n_max=None, act_std=0.5, H=4):
+    L = np.array(lengths)
+    return synth.attention_workload("heads-bwd", seed, L, heads=H, d=d, n_max=n_max or int(max(1, L.max())),
+                                    epilogue=True, with_grad=True, act_std=act_std)
+
+
+def gpu_fwd_bwd(w, epi=True, use_t=True, use_p=True):
+    T, F = w.total, w.heads * w.d
     q, k, v = (t_act(a, "bf16").reshape(T, w.heads, w.d) for a in (w.q, w.k, w.v))
-    dout = torch.zeros((T, w.heads * w.d), dtype=torch.bfloat16, device=q.device)
+    u = t_act(w.u, "bf16") if epi else None
+    dg = t_act(w.dg, "bf16")
+    off, ts = t_i32(w.offsets), t_i64(w.ts) if use_t else None
+    rp = t_f32(w.rab_p) if use_p else None
+    rt = t_f32(w.rab_t) if use_t else None
+    osv = torch.empty((T, F), dtype=torch.float32, device=q.device) if epi else None
+    lst = torch.empty((T, 2), dtype=torch.float32, device=q.device) if epi else None
+    if epi:
+        hs.attn_fwd(off, T, ts, q, k, v, rp, rt, w.n_max, u=u, eps=w.ln_eps, o_save=osv, ln_stats=lst)
+    g = hs.attn_bwd(off, T, ts, q, k, v, rp, rt, w.n_max, dg, u=u, o_save=osv, ln_stats=lst, eps=w.ln_eps)
+    torch.cuda.synchronize()
+    return g
+
+
+def check_bwd(g, ref, w, names=("dq", "dk", "dv", "du", "drab_p", "drab_t")):
+    from test_gpu_attn_bwd import check_all
+    return check_all(g, ref, names, dg=w.dg)
+
+
+@pytest.mark.parametrize("d", HEADS)
+@pytest.mark.parametrize("epi", [True, False], ids=["gate", "plain"])
+def test_bwd_head_size_ragged(d, epi):
+    """Every gradient at d = 64 and d = 32 on a ragged batch: partial query
+    blocks, one-token and empty sequences, several key tiles."""
+    w = bwd_work(100 + d, RAGGED, d)
+    g = gpu_fwd_bwd(w, epi=epi)
+    ref = oracle.attn_bwd(w.offsets, w.ts, w.q, w.k, w.v, w.rab_p, w.rab_t, w.n_max, w.u if epi else None,
+                          w.ln_eps, w.dg)
+    print("bwd d", d, "gate" if epi else "plain", flush=True)
+    check_bwd(g, ref, w)
+
+
+@pytest.mark.parametrize("d", HEADS)
+def test_bwd_head_size_bias_modes_and_wide_times(d):
+    w = bwd_work(110 + d, [260, 77, 5], d)
+    for use_t, use_p in [(False, True), (True, False)]:
+        g = gpu_fwd_bwd(w, use_t=use_t, use_p=use_p)
+        ref = oracle.attn_bwd(w.offsets, w.ts if use_t else None, w.q, w.k, w.v, w.rab_p if use_p else None,
+                              w.rab_t if use_t else None, w.n_max, w.u, w.ln_eps, w.dg)
+        names = ("dq", "dk", "dv", "du") + (("drab_p",) if use_p else ()) + (("drab_t",) if use_t else ())
+        check_bwd(g, ref, w, names)
+    w.ts = (w.ts - synth.EPOCH) * (1 << 24) + synth.EPOCH
+    g = gpu_fwd_bwd(w)
+    ref = oracle.attn_bwd(w.offsets, w.ts, w.q, w.k, w.v, w.rab_p, w.rab_t, w.n_max, w.u, w.ln_eps, w.dg)
+    check_bwd(g, ref, w)
+
+
+@pytest.mark.parametrize("d", HEADS)
+def test_bwd_head_size_beyond_n_max_and_deterministic(d):
+    """Sequences longer than n_max (clipped positions; the second one's dS
+    plane does not fit the buffer sized from n_max, so its dQ goes through
+    the fp32-atomic path), then a longer batch twice: every output
+    bit-identical."""
+    w = bwd_work(120 + d, [41, 300], d, n_max=100)
+    g = gpu_fwd_bwd(w)
+    ref = oracle.attn_bwd(w.offsets, w.ts, w.q, w.k, w.v, w.rab_p, w.rab_t, w.n_max, w.u, w.ln_eps, w.dg)
+    check_bwd(g, ref, w)
+    w = bwd_work(130 + d, [777, 1, 1500, 64, 333], d, n_max=2048, H=8)
+    g1 = gpu_fwd_bwd(w)
+    g2 = gpu_fwd_bwd(w)
+    for n in ("dq", "dk", "dv", "du", "drab_p", "drab_t"):
+        assert torch.equal(g1[n], g2[n]), n
+    ref = oracle.attn_bwd(w.offsets, w.ts, w.q, w.k, w.v, w.rab_p, w.rab_t, w.n_max, w.u, w.ln_eps, w.dg)
+    check_bwd(g1, ref, w)
+
+
+def test_head_size_128_only_entry_points_refuse_smaller_heads():
+    """The layer entry points keep d = 128: a d = 64 layer forward returns
+    HSTU_ERR_UNSUPPORTED before any device work."""
+    H, d, D = 4, 64, 256
+    L = np.array([40, 9])
+    T = int(L.sum())
+    dev_ = torch.device("cuda:0")
+    x = torch.zeros((T, D), dtype=torch.bfloat16, device=dev_)
+    lay = {"w1": torch.zeros((4 * H * d, D), dtype=torch.bfloat16, device=dev_), "b1": None,
+           "w2": torch.zeros((D, H * d), dtype=torch.bfloat16, device=dev_), "b2": None,
+           "rab_p": None, "rab_t": None, "phi1": hs.HSTU_ACT_SILU}
     with pytest.raises(hs.HstuError, match="d = 128"):
-        hs.attn_bwd(t_i32(w.offsets), T, t_i64(w.ts), q, k, v, t_f32(w.rab_p), t_f32(w.rab_t), w.n_max, dout)
+        hs.layer_fwd(t_i32(synth.offsets_of(L)), T, None, x, lay, H, d, 64)
