@@ -522,6 +522,16 @@ def all_extras(args):
             "append_64users": bench_append_64(args)}
 
 
+def hbm_bytes(w, T, H, d):
+    """Algorithmic HBM bytes per launch of the bandwidth-bound kernels of the
+    headline step (bf16 storage, fp32 O and statistics)."""
+    F = H * d
+    n_t = (w.lengths + 127) // 128  # key tiles per sequence
+    return {"ln_gate_fwd_kernel": T * (4 * F + 2 * F + 2 * F + 8),
+            "ln_gate_bwd_kernel": T * (2 * F + 2 * F + 4 * F + 8 + 2 * F + 4 * F),
+            "drab_reduce_kernel": int(4 * H * ((n_t * w.lengths).sum() + 64 * n_t.sum()))}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -613,6 +623,12 @@ def main():
         "attn_bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 2) if bwd_ms else None,  # attn_bwd + dq_gemm
         "kernel_tflops": {n: round(f / (per_kernel[n]["avg_ms"] * 1e-3) / 1e12, 2)
                           for n, f in kernel_flops.items() if n in per_kernel},
+        # the HBM-bound kernels: algorithmic bytes per launch / average
+        # duration (gate forward: O fp32 + U read, G and the stats written;
+        # gate backward: dG, U, O, stats read, dU and the dO' hi/lo planes
+        # written; the drab reduction: the items' partial sums read)
+        "hbm_gbps": {n: round(nb / (per_kernel[n]["avg_ms"] * 1e-3) / 1e9, 1)
+                     for n, nb in hbm_bytes(w, T, H, d).items() if n in per_kernel},
     }
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 4
