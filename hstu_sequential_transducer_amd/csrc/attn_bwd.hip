@@ -805,31 +805,25 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem<D> &sm, int b_seq, int o_b, int L, 
 #pragma unroll
             for (int gr = 0; gr < 4; gr++) *(u32x2 *)&dsn[krow * SS + 8 * gr + 4 * g] = u32x2{dpk[2 * gr], dpk[2 * gr + 1]};
             // the lane's drab_t sums of this block (buckets ubk, ubk + 1) join
-            // its running sums rs0, rs1 of buckets rb, rb + 1; when the
-            // buckets move on, a running sum is reduced over the wave and
-            // goes to the wave's LDS table (lane 0, plain read-modify-write)
+            // its running sums rs0, rs1 of buckets rb, rb + 1; when the block's
+            // buckets differ, both running sums are first reduced over the wave
+            // and go to the wave's LDS table (lane 0, plain read-modify-write).
+            // One rarely taken branch: cheaper than carrying rs1 over when the
+            // buckets move up by one (measured).
             if (DT && TM == 1 && nbk <= 1 && !diag) {
                 const float v_up = nbk == 1 ? tsum2 : 0.f;
-                const float v_lo = tsum - v_up;
-                if (ubk == rb) {
-                    rs0 += v_lo;
-                    rs1 += v_up;
-                } else if (ubk == rb + 1) {
-                    const float f0 = wave_sum_dpp(rs0);
-                    if (l == 0) sm.dtab[p][0][rb] += f0;
-                    rb = ubk;
-                    rs0 = rs1 + v_lo;
-                    rs1 = v_up;
-                } else {
+                if (ubk != rb) { // (rare: the buckets moved on) both running sums to the wave's table
                     const float f0 = wave_sum_dpp(rs0), f1 = wave_sum_dpp(rs1);
                     if (l == 0) {
                         sm.dtab[p][0][rb] += f0;
                         sm.dtab[p][0][rb + 1] += f1;
                     }
                     rb = ubk;
-                    rs0 = v_lo;
-                    rs1 = v_up;
+                    rs0 = 0.f;
+                    rs1 = 0.f;
                 }
+                rs0 += tsum - v_up;
+                rs1 += v_up;
             }
         } else {
 #pragma unroll
