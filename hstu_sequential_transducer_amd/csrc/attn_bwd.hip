@@ -29,13 +29,15 @@
 //     an fp32 buffer with global atomics instead.
 // X, P and dS are computed once.  All products are 32x32x16 bf16 MFMA with
 // lane = key, registers = queries.  Query blocks of 32 stream through LDS,
-// copied global -> LDS directly by the accumulating waves right after their
-// last transposing reads of the block (so the pointwise waves, which carry
-// the longer chain, issue no copies): Q and dO' are triple buffered (block
-// n + 1 lands while the pointwise waves read block n and the accumulating
-// waves block n - 1), dO'-lo and the per-block tables double buffered.  The
-// rab_p window is loaded into the X accumulator.  One barrier per query
-// block.
+// copied global -> LDS directly by the accumulating waves at the start of the
+// preceding block (so the pointwise waves, which carry the longer chain,
+// issue no copies, and the copies have a whole block to land): Q and dO' are triple
+// buffered (block n + 1 lands while the pointwise waves read block n and the
+// accumulating waves block n - 1), dO'-lo and the per-block tables double
+// buffered (only the pointwise waves read them).  The accumulating waves'
+// transposing reads are asm blocks that wait for their own results, so that
+// they do not wait for the copies in flight.  The rab_p window is loaded into
+// the X accumulator.  One barrier per query block.
 //
 // drab_p: the pointwise wave writes its fp32 dS into an LDS tile skewed by
 // j - i ([key - query][key mod 32]: a diagonal crosses a 32-query block at
@@ -136,6 +138,38 @@ DEV u32x2 lds_read_tr(const bf16 *p)
 {
     short4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)(p));
     return __builtin_bit_cast(u32x2, r);
+}
+DEV uint32_t lds_byte(const void *p) { return (uint32_t)(uintptr_t)(lds_void *)p; }
+// The same read, four or eight at a time at LDS byte addresses ad[i], waited
+// for inside one asm block: the accumulating waves issue the next block's
+// direct copies before these reads, and the compiler, not seeing which buffer
+// a builtin transposing read touches, would wait for every copy in flight.
+DEV void lds_tr4(u32x2 (&r)[4], const uint32_t (&ad)[4])
+{
+    asm volatile("ds_read_b64_tr_b16 %0, %4\n\t"
+                 "ds_read_b64_tr_b16 %1, %5\n\t"
+                 "ds_read_b64_tr_b16 %2, %6\n\t"
+                 "ds_read_b64_tr_b16 %3, %7\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+                 : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+                 : "memory");
+}
+DEV void lds_tr8(u32x2 (&r)[8], const uint32_t (&ad)[8])
+{
+    asm volatile("ds_read_b64_tr_b16 %0, %8\n\t"
+                 "ds_read_b64_tr_b16 %1, %9\n\t"
+                 "ds_read_b64_tr_b16 %2, %10\n\t"
+                 "ds_read_b64_tr_b16 %3, %11\n\t"
+                 "ds_read_b64_tr_b16 %4, %12\n\t"
+                 "ds_read_b64_tr_b16 %5, %13\n\t"
+                 "ds_read_b64_tr_b16 %6, %14\n\t"
+                 "ds_read_b64_tr_b16 %7, %15\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+                   "=&v"(r[7])
+                 : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7])
+                 : "memory");
 }
 
 struct BwdLane {
@@ -539,30 +573,27 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem<D> &sm, int b_seq, int o_b, int L, 
         // NJ = 4 DB steps j: m = j / (2 DB), db = (j / 2) % DB; even j: dO'^T slice
         // -> dV, odd j: Q^T slice -> dK.  Transposing reads run three steps ahead.
         constexpr int NJ = 4 * DB;
-        bf16x8 fa[4];
-        auto fetch = [&](int j) {
-            const int m = j / (2 * DB), db = (j >> 1) % DB;
-            const int qr1 = 16 * m + 4 * g + tsl; // query row of the transposing read
-            const bf16 *t = (j & 1) ? SQ.q : SQ.dO;
-            const u32x2 a1 = lds_read_tr(&t[swz<D>(qr1, db * 32 + cpart)]);
-            const u32x2 a2 = lds_read_tr(&t[swz<D>(qr1 + 8, db * 32 + cpart)]);
-            fa[j & 3] = as_bf16x8(u32x4{a1[0], a1[1], a2[0], a2[1]});
-        };
-        fetch(0);
-        fetch(1);
-        fetch(2);
+        // four steps per batch of transposing reads
 #pragma unroll
-        for (int j = 0; j < NJ; j++) {
-            if (j + 3 < NJ) fetch(j + 3);
-            const int m = j / (2 * DB), db = (j >> 1) % DB;
-            if (j & 1) acc2[db] = mfma32(fa[j & 3], sb[m], acc2[db]);
-            else acc[db] = mfma32(fa[j & 3], pb[m], acc[db]);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, 14, 0); // B operands and the first three steps
+        for (int j0 = 0; j0 < NJ; j0 += 4) {
+            uint32_t ad[8];
 #pragma unroll
-        for (int j = 0; j < NJ; j++) {
-            if (j + 3 < NJ) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            for (int jj = 0; jj < 4; jj++) {
+                const int j = j0 + jj, m = j / (2 * DB), db = (j >> 1) % DB;
+                const int qr1 = 16 * m + 4 * g + tsl; // query row of the transposing read
+                const bf16 *t = (j & 1) ? SQ.q : SQ.dO;
+                ad[2 * jj] = lds_byte(&t[swz<D>(qr1, db * 32 + cpart)]);
+                ad[2 * jj + 1] = lds_byte(&t[swz<D>(qr1 + 8, db * 32 + cpart)]);
+            }
+            u32x2 r[8];
+            lds_tr8(r, ad);
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++) {
+                const int j = j0 + jj, m = j / (2 * DB), db = (j >> 1) % DB;
+                const bf16x8 fa = as_bf16x8(u32x4{r[2 * jj][0], r[2 * jj][1], r[2 * jj + 1][0], r[2 * jj + 1][1]});
+                if (j & 1) acc2[db] = mfma32(fa, sb[m], acc2[db]);
+                else acc[db] = mfma32(fa, pb[m], acc[db]);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -574,13 +605,20 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem<D> &sm, int b_seq, int o_b, int L, 
     const int64_t P_ds = ((int64_t)L + DS_PAD - 1) / DS_PAD * DS_PAD;
     bf16 *ds_plane = DQA ? nullptr : a.ds + a.ds_base[b_seq] + (int64_t)h * P_ds * P_ds;
     auto ds_store = [&](const bf16 *dst, int q0m) {
+        uint32_t ad[4];
+#pragma unroll
+        for (int tt = 0; tt < 2; tt++) {
+            const int kr1 = 16 * (2 * p + tt) + 8 * g + tsl;
+            ad[2 * tt] = lds_byte(&dst[kr1 * SS + cpart]);
+            ad[2 * tt + 1] = lds_byte(&dst[(kr1 + 4) * SS + cpart]);
+        }
+        u32x2 r[4];
+        lds_tr4(r, ad);
 #pragma unroll
         for (int tt = 0; tt < 2; tt++) {
             const int t = 2 * p + tt;
-            const int kr1 = 16 * t + 8 * g + tsl;
-            const u32x2 s1 = lds_read_tr(&dst[kr1 * SS + cpart]);
-            const u32x2 s2 = lds_read_tr(&dst[(kr1 + 4) * SS + cpart]);
-            *(u32x4 *)(ds_plane + (int64_t)(q0m + lq) * P_ds + k0 + 16 * t + 8 * g) = u32x4{s1[0], s1[1], s2[0], s2[1]};
+            *(u32x4 *)(ds_plane + (int64_t)(q0m + lq) * P_ds + k0 + 16 * t + 8 * g) =
+                u32x4{r[2 * tt][0], r[2 * tt][1], r[2 * tt + 1][0], r[2 * tt + 1][1]};
         }
     };
     // DQA, accumulating wave: dQ of the block at q0m from the dS tile `dst`
@@ -672,9 +710,8 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem<D> &sm, int b_seq, int o_b, int L, 
         else __builtin_amdgcn_s_waitcnt(0xC07F); // lgkmcnt(0)
         __syncthreads();
     };
-    // The next block's direct copies, issued by the accumulating waves after
-    // their last transposing LDS read of the block (such a read waits for
-    // every copy in flight).
+    // The next block's direct copies, issued by the accumulating waves at the
+    // start of the block (their buffers were last read in the block before).
     auto start_copy = [&](auto main_c, int n) {
         constexpr bool MAIN = decltype(main_c)::value;
         const int q0 = k0 + n * BQ;
@@ -684,14 +721,18 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem<D> &sm, int b_seq, int o_b, int L, 
             if constexpr (TM != 2) gload_tables_direct(q0 + BQ, sm.sp[(n + 1) & 1]);
         }
     };
-    // Accumulating wave, block n: the previous block's dS store (or dQ),
-    // drab_p, dV and dK, then the next block's copies.
+    // Accumulating wave, block n: the next block's copies, the previous
+    // block's dS store (or dQ), drab_p, dV and dK.  (The atomic-dQ variant
+    // issues the copies after its transposing reads: its dQ products read dS
+    // with the builtin.)
     auto iter_acc = [&](auto main_c, int n) {
         constexpr bool MAIN = decltype(main_c)::value;
         const int q0 = k0 + n * BQ;
         int dlf = 0;
         float tot = 0.f;
         const int q0m = q0 - BQ;
+        // the next block's copies first (a whole block to land)
+        if constexpr (!DQA) start_copy(main_c, n);
         // the LDS/VALU work first and the MFMAs last, so that the pointwise
         // wave's X products meet an idle MFMA pipe after the barrier
         if (MAIN || n > 0) {
@@ -704,7 +745,7 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem<D> &sm, int b_seq, int o_b, int L, 
             const bool skipm = MAIN ? false : (kw0 > q0m + BQ - 1 || kw0 >= L);
             if (!skipm) acc_block(sm.sq[n % 3 == 0 ? 2 : n % 3 - 1], (n - 1) & 1);
         }
-        start_copy(main_c, n);
+        if constexpr (DQA) start_copy(main_c, n);
         if ((MAIN || n > 0) && a.drab_p) drabp_flush(dlf, tot);
         finish(main_c, n, true);
     };

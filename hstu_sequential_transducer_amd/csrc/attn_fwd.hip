@@ -400,27 +400,33 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem<D> &sm, int o_b, int L, int q0, int
                                         step);
     };
 
-    // One 64-key tile: the next tile's copies are issued first; the
-    // transposing V reads (which wait for copies in flight) come last, after
-    // both blocks' S^T and element-wise steps.
-    auto iteration = [&](auto main_c, int kt) {
+    // The key-time ranges of the two 32-key blocks of a tile, loaded one
+    // tile ahead: the loads of tile kt + 1 are issued during tile kt, whose
+    // final wait retires them.  (Loaded in the tile itself, after its copies,
+    // they made the element-wise step wait for every copy of the next tile:
+    // loads retire in order.)
+    uint32_t krn[2] = {0u, 0u}, krx[2] = {0u, 0u};
+    auto load_kr = [&](int kt) {
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++) {
+            const int ks = min(kt * BN + kb * 32, L - 1) & ~31; // past the sequence: its last block (unused)
+            krn[kb] = a.rmin[o_b + ks];
+            krx[kb] = a.rmax[o_b + ks];
+        }
+    };
+    // One 64-key tile in stage par: the next tile's copies are issued first;
+    // the transposing V reads (which wait for copies in flight) come last,
+    // after both blocks' S^T and element-wise steps.
+    auto iteration = [&](auto main_c, int kt, auto par) {
         constexpr bool MAIN = decltype(main_c)::value;
         if (kt + 1 < kt_end) {
-            if ((kt + 2) * BN <= kend) gload(kt + 1, sm.st[(kt + 1) & 1], std::true_type{});
-            else gload(kt + 1, sm.st[(kt + 1) & 1], std::false_type{});
+            if ((kt + 2) * BN <= kend) gload(kt + 1, sm.st[1 - par], std::true_type{});
+            else gload(kt + 1, sm.st[1 - par], std::false_type{});
         }
-        // the key-time ranges of both blocks (scalar loads, issued early; a
-        // block past the sequence reads its last block's entry, unused)
-        uint32_t kmn[2] = {0u, 0u}, kmx[2] = {0u, 0u};
-        if constexpr (TM == 1) {
-#pragma unroll
-            for (int kb = 0; kb < 2; kb++) {
-                const int ks = min(kt * BN + kb * 32, L - 1) & ~31;
-                kmn[kb] = a.rmin[o_b + ks];
-                kmx[kb] = a.rmax[o_b + ks];
-            }
-        }
-        const Stage<D> &S = sm.st[kt & 1];
+        const uint32_t kmn[2] = {krn[0], krn[1]}, kmx[2] = {krx[0], krx[1]};
+        if constexpr (TM == 1)
+            if (kt + 1 < kt_end) load_kr(kt + 1);
+        const Stage<D> &S = sm.st[par];
         bool need[2], diag[2];
 #pragma unroll
         for (int kb = 0; kb < 2; kb++) {
@@ -480,7 +486,12 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem<D> &sm, int o_b, int L, int q0, int
         __syncthreads();
     };
 
-    gload(kt_begin, sm.st[kt_begin & 1], std::false_type{});
+    // Tile kt is in stage (kt - kt_begin) & 1.  The full-tile loop takes the
+    // tiles in pairs, so that the stage of each is known at compile time and
+    // its LDS addresses are constant offsets from per-lane bases (about a
+    // fifth fewer VALU instructions per tile).
+    gload(kt_begin, sm.st[0], std::false_type{});
+    if constexpr (TM == 1) load_kr(kt_begin);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
@@ -488,8 +499,11 @@ DEV void fwd_body(const AttnFwdArgs &a, Smem<D> &sm, int o_b, int L, int q0, int
     const std::integral_constant<bool, true> fast{};
     int kt = kt_begin;
     if constexpr (TM != 2)
-        for (; kt < min(n_main, kt_end); kt++) iteration(fast, kt);
-    for (; kt < kt_end; kt++) iteration(generic, kt);
+        for (; kt + 1 < min(n_main, kt_end); kt += 2) {
+            iteration(fast, kt, std::integral_constant<int, 0>{});
+            iteration(fast, kt + 1, std::integral_constant<int, 1>{});
+        }
+    for (; kt < kt_end; kt++) iteration(generic, kt, (kt - kt_begin) & 1);
 
     // O^T accumulator: lane holds query qrow, d = 32 db + 8(r/4) + 4g + r%4;
     // O = (-ln 2 / N) * sum P' V.
