@@ -666,7 +666,7 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem<D> &sm, int b_seq, int o_b, int L, 
     };
     // A finished sum goes to this item's slot of partial sums (indexed by
     // key - query in [k0 - (L - 1), 0], the causal values this key tile
-    // meets; drab_p_reduce_kernel adds the slots in a fixed order), or, for a
+    // meets; drab_reduce_kernel adds the slots in a fixed order), or, for a
     // sequence whose slots did not fit, into drab_p with an atomic add.
     auto put_p = [&](int dl, float v) {
         const int64_t pb = a.pbase[b_seq]; // (reloaded here: nothing stays live across the loop)
@@ -942,7 +942,7 @@ DEV void bwd_body(const AttnBwdArgs &a, Smem<D> &sm, int b_seq, int o_b, int L, 
         for (int dl = lo + tid; dl <= hi; dl += NT) put_p(dl, sm.ring[dl & (RING - 1)]);
     }
     if constexpr (DT && TM != 0) {
-        if (tid < TB) { // this item's slot of drab_t partial sums (added up by drab_t_reduce_kernel)
+        if (tid < TB) { // this item's slot of drab_t partial sums (added up by drab_reduce_kernel)
             float s = 0.f;
             for (int pp = 0; pp < 4; pp++)
                 for (int c = 0; c < TCOPY; c++) s += sm.dtab[pp][c][tid];
@@ -1040,6 +1040,48 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs &a, int d, int max_items, hipS
 // The bias gradients from the items' partial sums, added in a fixed order,
 // so that drab_p and drab_t do not depend on the order in which items ran.
 //
+// drab_t[h][bucket] = the sum over the items' slots: one wave per entry;
+// lane l adds tiles t = l, l + 64, ... of every sequence (in order of
+// sequence and t), then a butterfly over the lanes (a fixed tree, the same
+// on every lane).  Buckets from TB_SLOTS on are never reached and get 0.
+__device__ void drab_t_reduce(const DrabReduceArgs &r, int h, int bk, int lane)
+{
+    float s = 0.f;
+    // per-sequence tile counts and slot bases, 64 sequences at a time (one
+    // per lane, read back with uniform lane reads); the first tile loads of
+    // eight sequences are issued together, then added in order
+    if (bk < TB_SLOTS)
+        for (int b0 = 0; b0 < r.B; b0 += 64) {
+            const int bl = b0 + lane;
+            const int ntl = bl < r.B ? (r.offsets[bl + 1] - r.offsets[bl] + BWD_BN - 1) / BWD_BN : 0;
+            const int64_t tbl = bl < r.B ? r.tbase[bl] : 0;
+            const int nb = min(64, r.B - b0);
+            for (int jb0 = 0; jb0 < nb; jb0 += 8) {
+                float v[8];
+                const float *sl[8];
+                int ntu[8];
+#pragma unroll
+                for (int u = 0; u < 8; u++) {
+                    const int jb = min(jb0 + u, nb - 1);
+                    const int nt = jb0 + u < nb ? __builtin_amdgcn_readlane(ntl, jb) : 0;
+                    const int64_t tb = ((int64_t)__builtin_amdgcn_readlane((int)(tbl >> 32), jb) << 32) |
+                                       (uint32_t)__builtin_amdgcn_readlane((int)tbl, jb);
+                    sl[u] = r.tpart + (nt > 0 ? tb + (int64_t)h * nt * TB_SLOTS + bk : 0);
+                    ntu[u] = nt;
+                    v[u] = lane < nt ? sl[u][(int64_t)lane * TB_SLOTS] : 0.f;
+                }
+#pragma unroll
+                for (int u = 0; u < 8; u++) {
+                    s += v[u];
+                    for (int t = lane + 64; t < ntu[u]; t += 64) s += sl[u][(int64_t)t * TB_SLOTS];
+                }
+            }
+        }
+    s = wave_sum(s);
+    if (lane == 0) r.drab_t[h * r.t_hs + bk] = s;
+}
+
+constexpr int RED_G = 16;
 // drab_p[h][idx] += the sum of the slot entries for key - query x = idx - N
 // (idx 0 collects every x <= -N) over the items that cover it.  A workgroup
 // takes 64 entries of one head; its 16 waves split the key tiles by residue
@@ -1048,46 +1090,73 @@ hipError_t launch_attn_bwd_bf16(const AttnBwdArgs &a, int d, int max_items, hipS
 // of g.  drab_p was zeroed by the launcher; items of a sequence without
 // slots added their share with atomics.  Entries idx > N (key after query)
 // are never reached.
-constexpr int RED_G = 16;
-__global__ void __launch_bounds__(64 * RED_G) drab_p_reduce_kernel(DrabReduceArgs r)
+// One launch for both tables: workgroups x < np (np = 0 without drab_p)
+// reduce drab_p, the rest drab_t (one wave per bucket).
+__global__ void __launch_bounds__(64 * RED_G) drab_reduce_kernel(DrabReduceArgs r, int np)
 {
     __shared__ float part[RED_G][64];
     if (*r.status) return;
     const int h = blockIdx.y, lane = threadIdx.x & 63, g = threadIdx.x >> 6;
+    if ((int)blockIdx.x >= np) { // (workgroup-uniform)
+        drab_t_reduce(r, h, ((int)blockIdx.x - np) * RED_G + g, lane);
+        return;
+    }
     const int idx = blockIdx.x * 64 + lane;
     const bool valid = idx <= r.N;
     const int dl = idx - r.N;
     float acc = 0.f;
     // per-sequence slot bases and lengths, 64 sequences at a time, one per
-    // lane; the loop reads them back with uniform lane reads, so only the
-    // slot loads themselves wait on memory
+    // lane; the loop reads them back with uniform lane reads.  Entries idx > 0
+    // take one x per sequence: the first four tiles' loads of eight sequences
+    // are issued together, then added in order (sequence, tile); idx = 0
+    // (every x <= -N) takes the general loop.
     for (int b0 = 0; b0 < r.B; b0 += 64) {
         const int bl = b0 + lane;
         const int64_t pbl = bl < r.B ? r.pbase[bl] : -1;
         const int Ll = bl < r.B ? r.offsets[bl + 1] - r.offsets[bl] : 0;
         const int nb = min(64, r.B - b0);
-#pragma unroll 4
-        for (int jb = 0; jb < nb; jb++) {
-            const int64_t pb = ((int64_t)__builtin_amdgcn_readlane((int)(pbl >> 32), jb) << 32) |
-                               (uint32_t)__builtin_amdgcn_readlane((int)pbl, jb);
-            const int L = __builtin_amdgcn_readlane(Ll, jb);
-            if (!valid || pb < 0 || L <= 0 || -dl > L - 1) continue;
-            const int nt = (L + BWD_BN - 1) / BWD_BN;
-            const float *slot = r.dpart + pb + (int64_t)h * nt * L + (L - 1);
-            const int xlo = idx == 0 ? -(L - 1) : dl;
-            for (int x = dl; x >= xlo; x--) {
-                const int tmax = min(nt - 1, (x + L - 1) / BWD_BN);
-                float v[4];
+        for (int jb0 = 0; jb0 < nb; jb0 += 8) {
+            float v[8][4];
+            int tmx[8];
+            const float *sl[8];
+#pragma unroll
+            for (int u = 0; u < 8; u++) {
+                const int jb = min(jb0 + u, nb - 1);
+                const int64_t pb = ((int64_t)__builtin_amdgcn_readlane((int)(pbl >> 32), jb) << 32) |
+                                   (uint32_t)__builtin_amdgcn_readlane((int)pbl, jb);
+                const int L = __builtin_amdgcn_readlane(Ll, jb);
+                const bool ok = jb0 + u < nb && valid && idx > 0 && pb >= 0 && L > 0 && -dl <= L - 1;
+                const int nt = (L + BWD_BN - 1) / BWD_BN;
+                sl[u] = r.dpart + (ok ? pb + (int64_t)h * nt * L + (L - 1) + dl : 0);
+                tmx[u] = ok ? min(nt - 1, (dl + L - 1) / BWD_BN) : -1;
+                const int Ls = ok ? L : 0;
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
                     const int t = g + RED_G * i;
-                    v[i] = t <= tmax ? slot[(int64_t)t * L + x] : 0.f;
+                    v[u][i] = t <= tmx[u] ? sl[u][(int64_t)t * Ls] : 0.f;
                 }
+            }
 #pragma unroll
-                for (int i = 0; i < 4; i++) acc += v[i];
-                for (int t = g + 4 * RED_G; t <= tmax; t += RED_G) acc += slot[(int64_t)t * L + x];
+            for (int u = 0; u < 8; u++) {
+                const int L = __builtin_amdgcn_readlane(Ll, min(jb0 + u, nb - 1));
+#pragma unroll
+                for (int i = 0; i < 4; i++) acc += v[u][i];
+                for (int t = g + 4 * RED_G; t <= tmx[u]; t += RED_G) acc += sl[u][(int64_t)t * L];
             }
         }
+        if (idx == 0) // (lane 0 of the first workgroup of each head: x = -N down to -(L - 1))
+            for (int jb = 0; jb < nb; jb++) {
+                const int64_t pb = ((int64_t)__builtin_amdgcn_readlane((int)(pbl >> 32), jb) << 32) |
+                                   (uint32_t)__builtin_amdgcn_readlane((int)pbl, jb);
+                const int L = __builtin_amdgcn_readlane(Ll, jb);
+                if (pb < 0 || L <= 0 || -dl > L - 1) continue;
+                const int nt = (L + BWD_BN - 1) / BWD_BN;
+                const float *slot = r.dpart + pb + (int64_t)h * nt * L + (L - 1);
+                for (int x = dl; x >= -(L - 1); x--) {
+                    const int tmax = min(nt - 1, (x + L - 1) / BWD_BN);
+                    for (int t = g; t <= tmax; t += RED_G) acc += slot[(int64_t)t * L + x];
+                }
+            }
     }
     part[g][lane] = acc;
     __syncthreads();
@@ -1099,30 +1168,9 @@ __global__ void __launch_bounds__(64 * RED_G) drab_p_reduce_kernel(DrabReduceArg
     }
 }
 
-// drab_t[h][bucket] = the sum over the items' slots: one wave per entry;
-// lane l adds tiles t = l, l + 64, ... of every sequence (in order of
-// sequence and t), then a butterfly over the lanes (a fixed tree, the same
-// on every lane).  Buckets from TB_SLOTS on are never reached and get 0.
-__global__ void __launch_bounds__(64) drab_t_reduce_kernel(DrabReduceArgs r)
-{
-    if (*r.status) return;
-    const int h = blockIdx.x >> 7, bk = blockIdx.x & 127, lane = threadIdx.x;
-    float s = 0.f;
-    if (bk < TB_SLOTS)
-        for (int b = 0; b < r.B; b++) {
-            const int L = r.offsets[b + 1] - r.offsets[b];
-            const int nt = (L + BWD_BN - 1) / BWD_BN;
-            const float *slot = r.tpart + r.tbase[b] + (int64_t)h * nt * TB_SLOTS + bk;
-            for (int t = lane; t < nt; t += 64) s += slot[(int64_t)t * TB_SLOTS];
-        }
-    s = wave_sum(s);
-    if (lane == 0) r.drab_t[h * r.t_hs + bk] = s;
-}
-
 hipError_t launch_drab_reduce(const DrabReduceArgs &r, hipStream_t st)
 {
-    if (r.drab_p)
-        hipLaunchKernelGGL(drab_p_reduce_kernel, dim3((r.N + 1 + 63) / 64, r.H), dim3(64 * RED_G), 0, st, r);
-    if (r.drab_t) hipLaunchKernelGGL(drab_t_reduce_kernel, dim3(r.H * 128), dim3(64), 0, st, r);
+    const int np = r.drab_p ? (r.N + 1 + 63) / 64 : 0, nt = r.drab_t ? 128 / RED_G : 0;
+    if (np + nt > 0) hipLaunchKernelGGL(drab_reduce_kernel, dim3(np + nt, r.H), dim3(64 * RED_G), 0, st, r, np);
     return hipGetLastError();
 }
