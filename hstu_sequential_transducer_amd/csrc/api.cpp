@@ -245,15 +245,21 @@ hstu_status attn_fwd_launch(const hstu_jagged *j, const hstu_dims *dm, const hst
     int *t_split = status + 2;
     float *obuf = u.ptr ? (o_save ? o_save : (float *)(wb + w.obuf)) : nullptr;
     {
+        // (the launch after the launcher also zeroes the rows split items add into)
         ProfScope ps("sched_kernel", st);
+        ZeroRows z{};
+        if (split) {
+            z.mode = ZeroRows::SPLIT_ROWS;
+            z.tile = tile;
+            z.t_split = t_split;
+            z.rows = obuf;
+            z.ld = F;
+            z.F = F;
+        }
         launch_sched(j->offsets, j->ts, B, T, tile, H, status, n_items, items, max_items, rel, wide,
-                     (int32_t *)(wb + w.rank), split ? concurrent_slots() : 0, t_split, SchedBwd{}, st);
+                     (int32_t *)(wb + w.rank), split ? concurrent_slots() : 0, t_split, SchedBwd{}, st, z);
     }
     TRY(launched(hipGetLastError(), "schedule kernel"));
-    if (split) {
-        ProfScope ps("zero_split_rows_kernel", st);
-        TRY(launched(launch_zero_split_rows(j->offsets, B, tile, t_split, obuf, F, F, status, st), "zero split rows"));
-    }
 
     AttnFwdArgs a{};
     a.q = q.ptr;
@@ -345,14 +351,17 @@ hstu_status attn_bwd_launch(const hstu_jagged *j, const hstu_dims *dm, const hst
             sb.zero1 = drab_t;
             sb.n1 = (int64_t)H * t_hs;
         }
+        // (and the launch after it zeroes the fp32 dQ rows of the sequences
+        // whose dS planes do not fit the buffer)
+        ZeroRows z{};
+        z.mode = ZeroRows::DQA_ROWS;
+        z.ds_base = ds_base;
+        z.rows = dq_acc;
+        z.F = H * d;
         launch_sched(j->offsets, j->ts, B, T, BWD_BN, H, status, n_items, items, max_items, rel, wide,
-                     (int32_t *)(wb + w.rank), 0, nullptr, sb, st);
+                     (int32_t *)(wb + w.rank), 0, nullptr, sb, st, z);
     }
     TRY(launched(hipGetLastError(), "schedule kernel"));
-    {
-        ProfScope ps("zero_dqa_rows_kernel", st);
-        TRY(launched(launch_zero_dqa_rows(j->offsets, B, ds_base, dq_acc, H * d, status, st), "zero fill"));
-    }
     const float inv_n = 1.0f / (float)N;
     if (u.ptr) {
         ProfScope ps("ln_gate_bwd_kernel", st);

@@ -56,9 +56,23 @@ struct SchedBwd {
     float *zero1;
     int64_t n1;
 };
+// Rows zeroed in the launch that follows the launcher (after validation):
+// SPLIT_ROWS: the fp32 rows [offsets[b] + tile * *t_split, offsets[b + 1])
+// of rows/ld/F (the rows that split forward items accumulate into);
+// DQA_ROWS: the rows of rows ([T][F] fp32) of the sequences with
+// ds_base[b] < 0 (their dQ goes through the fp32 accumulator).
+struct ZeroRows {
+    enum Mode { NONE = 0, SPLIT_ROWS = 1, DQA_ROWS = 2 } mode;
+    int tile;
+    const int *t_split;
+    const int64_t *ds_base;
+    float *rows;
+    int64_t ld;
+    int F;
+};
 void launch_sched(const int32_t *offsets, const int64_t *ts, int B, int T, int tile, int H, int *status, int *n_items,
                   int2 *items, int max_items, uint32_t *rel, int32_t *wide, int32_t *rank, int split_slots, int *t_split,
-                  const SchedBwd &bw, hipStream_t st);
+                  const SchedBwd &bw, hipStream_t st, const ZeroRows &z = ZeroRows{});
 // Appending new actions to cached histories: validates hoff / aoff (first 0,
 // non-decreasing, last = Th / Tn) into *status, writes the merged offsets
 // moff[u] = hoff[u] + aoff[u] (user u's sequence [history; new]) and the
@@ -89,10 +103,6 @@ struct AppendPlan {
 };
 hipError_t launch_append_plan(const AppendPlan &p, hipStream_t st);
 
-// Zeroes the fp32 rows [offsets[b] + tile * t_split, offsets[b + 1]) of
-// every sequence (the rows that split items accumulate into).
-hipError_t launch_zero_split_rows(const int32_t *offsets, int B, int tile, const int *t_split, float *o32, int64_t ld,
-                                  int F, const int *status, hipStream_t st);
 
 // ---- attention forward (attn_fwd.hip)
 struct AttnFwdArgs {
@@ -210,9 +220,6 @@ struct DqArgs {
     int d;                      // head size: 128, 64 or 32
 };
 hipError_t launch_dq_gemm(const DqArgs &a, int max_items, hipStream_t st);
-// Zeroes the dq_acc rows ([T][F] fp32) of the sequences with ds_base < 0.
-hipError_t launch_zero_dqa_rows(const int32_t *offsets, int B, const int64_t *ds_base, float *dq_acc, int F,
-                                const int *status, hipStream_t st);
 
 // ---- small helpers (misc.hip)
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st);

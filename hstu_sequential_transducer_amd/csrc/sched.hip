@@ -238,12 +238,10 @@ __global__ void __launch_bounds__(1024) sched_kernel(const int32_t *__restrict__
 // |t_i - t_j| + 1 < 2^32); otherwise wide[b] is set and the kernels use exact
 // 64-bit arithmetic for that sequence.  wide[] was zeroed by sched_kernel
 // (which also validated the offsets: nothing runs on a batch that failed).
-__global__ void __launch_bounds__(256) reltime_kernel(const int32_t *__restrict__ offsets, const int64_t *__restrict__ ts,
-                                                       uint32_t *__restrict__ rel, int32_t *__restrict__ wide, int B,
-                                                       int T, const int *__restrict__ status)
+__device__ void reltime_rows(const int32_t *__restrict__ offsets, const int64_t *__restrict__ ts,
+                             uint32_t *__restrict__ rel, int32_t *__restrict__ wide, int B, int T, int blk)
 {
-    if (*status) return; // offsets failed validation: touch nothing
-    const int r = blockIdx.x * 256 + threadIdx.x;
+    const int r = blk * 256 + threadIdx.x;
     if (r >= T) return;
     int lo = 0, hi = B - 1; // last b with offsets[b] <= r
     while (lo < hi) {
@@ -269,71 +267,80 @@ __global__ void __launch_bounds__(256) reltime_kernel(const int32_t *__restrict_
     }
 }
 
-// Rows of split items: grid (B, 128), workgroup y takes every 128th row of
-// sequence b from tile * t_split on; 16-byte stores when the rows allow them.
-__global__ void __launch_bounds__(256) zero_split_rows_kernel(const int32_t *__restrict__ offsets, int tile,
-                                                               const int *__restrict__ t_split, float *__restrict__ o32,
-                                                               int64_t ld, int F, const int *__restrict__ status)
+__global__ void __launch_bounds__(256) reltime_kernel(const int32_t *__restrict__ offsets, const int64_t *__restrict__ ts,
+                                                       uint32_t *__restrict__ rel, int32_t *__restrict__ wide, int B,
+                                                       int T, const int *__restrict__ status)
 {
-    if (*status) return;
-    const int b = blockIdx.x;
+    if (*status) return; // offsets failed validation: touch nothing
+    reltime_rows(offsets, ts, rel, wide, B, T, blockIdx.x);
+}
+
+// Rows of split items: workgroup y of sequence b (of ny) takes every ny-th
+// row of the sequence from tile * t_split on; 16-byte stores when the rows
+// allow them.
+__device__ void zero_split_rows(const int32_t *__restrict__ offsets, const ZeroRows &z, int b, int y, int ny)
+{
     const int o_b = offsets[b], L = offsets[b + 1] - o_b;
-    const int64_t r0 = (int64_t)tile * *t_split;
+    const int64_t r0 = (int64_t)z.tile * *z.t_split;
     if (r0 >= L) return;
+    float *o32 = z.rows;
+    const int64_t ld = z.ld;
+    const int F = z.F;
     const bool vec = ((((uintptr_t)o32) | (uintptr_t)(ld * 4) | (uintptr_t)(F * 4)) & 15) == 0;
     if (vec) {
         const int f4 = F / 4;
-        for (int64_t r = r0 + blockIdx.y; r < L; r += gridDim.y)
+        for (int64_t r = r0 + y; r < L; r += ny)
             for (int c = threadIdx.x; c < f4; c += 256)
                 *(floatx4 *)(o32 + (o_b + r) * ld + 4 * c) = floatx4{0.f, 0.f, 0.f, 0.f};
     } else {
-        for (int64_t r = r0 + blockIdx.y; r < L; r += gridDim.y)
+        for (int64_t r = r0 + y; r < L; r += ny)
             for (int c = threadIdx.x; c < F; c += 256) o32[(o_b + r) * ld + c] = 0.f;
     }
 }
 
-hipError_t launch_zero_split_rows(const int32_t *offsets, int B, int tile, const int *t_split, float *o32, int64_t ld,
-                                  int F, const int *status, hipStream_t st)
+// dq_acc rows ([T][F] fp32) of the sequences whose dS planes did not fit
+// (ds_base < 0): workgroup y of sequence b (of ny) takes every ny-th row.
+__device__ void zero_dqa_rows(const int32_t *__restrict__ offsets, const ZeroRows &z, int b, int y, int ny)
 {
-    if (B <= 0) return hipSuccess;
-    hipLaunchKernelGGL(zero_split_rows_kernel, dim3(B, 128), dim3(256), 0, st, offsets, tile, t_split, o32, ld, F,
-                       status);
-    return hipGetLastError();
-}
-
-// dq_acc rows of the sequences whose dS planes did not fit: grid (B, 32).
-__global__ void __launch_bounds__(256) zero_dqa_rows_kernel(const int32_t *__restrict__ offsets,
-                                                             const int64_t *__restrict__ ds_base,
-                                                             float *__restrict__ dq_acc, int F,
-                                                             const int *__restrict__ status)
-{
-    if (*status) return;
-    const int b = blockIdx.x;
-    if (ds_base[b] >= 0) return;
+    if (z.ds_base[b] >= 0) return;
     const int o_b = offsets[b], L = offsets[b + 1] - o_b;
-    for (int64_t r = blockIdx.y; r < L; r += gridDim.y)
-        for (int c = threadIdx.x; c < F; c += 256) dq_acc[(o_b + r) * (int64_t)F + c] = 0.f;
+    for (int64_t r = y; r < L; r += ny)
+        for (int c = threadIdx.x; c < z.F; c += 256) z.rows[(o_b + r) * (int64_t)z.F + c] = 0.f;
 }
 
-hipError_t launch_zero_dqa_rows(const int32_t *offsets, int B, const int64_t *ds_base, float *dq_acc, int F,
-                                const int *status, hipStream_t st)
+// What runs after the launcher, in one launch: workgroups [0, nrel) write
+// the relative times, the next B * ZERO_NY zero rows (z.mode).
+constexpr int ZERO_NY = 64;
+__global__ void __launch_bounds__(256) post_sched_kernel(const int32_t *__restrict__ offsets,
+                                                          const int64_t *__restrict__ ts, uint32_t *__restrict__ rel,
+                                                          int32_t *__restrict__ wide, int B, int T, int nrel, ZeroRows z,
+                                                          const int *__restrict__ status)
 {
-    if (B <= 0) return hipSuccess;
-    hipLaunchKernelGGL(zero_dqa_rows_kernel, dim3(B, 32), dim3(256), 0, st, offsets, ds_base, dq_acc, F, status);
-    return hipGetLastError();
+    if (*status) return; // offsets failed validation: touch nothing
+    const int blk = blockIdx.x;
+    if (blk < nrel) {
+        reltime_rows(offsets, ts, rel, wide, B, T, blk);
+        return;
+    }
+    const int zb = blk - nrel, b = zb / ZERO_NY, y = zb - b * ZERO_NY;
+    if (z.mode == ZeroRows::SPLIT_ROWS) zero_split_rows(offsets, z, b, y, ZERO_NY);
+    else zero_dqa_rows(offsets, z, b, y, ZERO_NY);
 }
 
 void launch_sched(const int32_t *offsets, const int64_t *ts, int B, int T, int tile, int H, int *status, int *n_items,
                   int2 *items, int max_items, uint32_t *rel, int32_t *wide, int32_t *rank, int split_slots, int *t_split,
-                  const SchedBwd &bw, hipStream_t st)
+                  const SchedBwd &bw, hipStream_t st, const ZeroRows &z)
 {
     SchedBwd b2 = bw;
     if (!b2.zero0) b2.n0 = 0;
     if (!b2.zero1) b2.n1 = 0;
     hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(1024), 0, st, offsets, B, T, tile, H, status, n_items, items,
                        max_items, wide, rank, split_slots, t_split, b2);
-    if (ts && T > 0)
-        hipLaunchKernelGGL(reltime_kernel, dim3((T + 255) / 256), dim3(256), 0, st, offsets, ts, rel, wide, B, T, status);
+    const int nrel = ts && T > 0 ? (T + 255) / 256 : 0;
+    const int nz = z.mode != ZeroRows::NONE && B > 0 ? B * ZERO_NY : 0;
+    if (nrel + nz > 0)
+        hipLaunchKernelGGL(post_sched_kernel, dim3(nrel + nz), dim3(256), 0, st, offsets, ts, rel, wide, B, T, nrel, z,
+                           status);
 }
 
 // ---------------------------------------------------------------------------
