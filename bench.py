@@ -50,9 +50,9 @@ CSRC = os.path.join(ROOT, "hstu_sequential_transducer_amd", "csrc")
 # source they were measured on (sha256 over the files listed); otherwise the
 # traffic is reported as null.
 MEASURED_TRAFFIC = {
-    "attn_bwd_bf16_kernel": {"src": "55f0686d34d10927", "bytes": 2196106864},  # read 1383592498 + write 812514365
-    "attn_fwd_bf16_kernel": {"src": "08393dad39682fac", "bytes": 430929197},   # read 344467082 + write 86462115
-    "dq_gemm_kernel": {"src": "526aeabacfc88ccb", "bytes": 929056380},         # read 893660735 + write 35395645
+    "attn_bwd_bf16_kernel": {"src": "63db4237b98653e2", "bytes": 2274891751},  # read 1464424462 + write 810467289
+    "attn_fwd_bf16_kernel": {"src": "a4bec85aa21b7744", "bytes": 450978331},   # read 344233250 + write 106745081
+    "dq_gemm_kernel": {"src": "fdc3097f8d6cf2fa", "bytes": 928029683},         # read 892620090 + write 35409593
 }
 
 
