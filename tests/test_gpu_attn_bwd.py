@@ -187,3 +187,36 @@ def test_bwd_neighbours_nan():
     for n in ("dq", "dk", "dv", "du"):
         assert torch.equal(g[n][260:450], base[n][260:450]), n
         assert not torch.isnan(g[n][260:450].float()).any(), n
+
+
+@pytest.mark.timeout(600)
+def test_fwd_bwd_maximum_length():
+    """The longest sequence the headline configuration allows, L = N_max =
+    8192 (64 key tiles of 128, 128 of 64: the largest split forward items,
+    the largest dS plane and every key - query value in [-(N_max - 1), 0]),
+    batched with a 37-token and a 1-token sequence: every element of G and of
+    the fp32 O, and of dq, dk, dv, du, drab_p and drab_t, against the oracle
+    (about 240 GFLOP of fp64 on the host)."""
+    w = synth.attention_workload("max-len", 27, np.array([8192, 37, 1]), heads=4, d=128, n_max=8192,
+                                 epilogue=True, with_grad=True)
+    print("case max length T", w.total, flush=True)
+    T, F = w.total, w.heads * w.d
+    q, k, v = (t_act(a, "bf16").reshape(T, w.heads, w.d) for a in (w.q, w.k, w.v))
+    u = t_act(w.u, "bf16")
+    off, ts = t_i32(w.offsets), t_i64(w.ts)
+    rp, rt = t_f32(w.rab_p), t_f32(w.rab_t)
+    osv = torch.empty((T, F), dtype=torch.float32, device=q.device)
+    lst = torch.empty((T, 2), dtype=torch.float32, device=q.device)
+    G = hs.attn_fwd(off, T, ts, q, k, v, rp, rt, w.n_max, u=u, eps=w.ln_eps, o_save=osv, ln_stats=lst)
+    g = hs.attn_bwd(off, T, ts, q, k, v, rp, rt, w.n_max, t_act(w.dg, "bf16"), u=u, o_save=osv, ln_stats=lst,
+                    eps=w.ln_eps)
+    torch.cuda.synchronize()
+    O = oracle.attn_fwd(w.offsets, w.ts, w.q, w.k, w.v, w.rab_p, w.rab_t, w.n_max)
+    Gr, _ = oracle.ln_gate(O, w.u, w.ln_eps)
+    eo, eg = rel_err(host(osv), O), rel_err(host(G), Gr)
+    print("max length fwd errors O", eo, "G", eg, "bound", bf16_bound(Gr), flush=True)
+    assert eo <= BF16_TOL
+    assert eg <= bf16_bound(Gr)
+    ref = oracle.attn_bwd(w.offsets, w.ts, w.q, w.k, w.v, w.rab_p, w.rab_t, w.n_max, w.u, w.ln_eps, w.dg)
+    errs = check_all(g, ref, dg=w.dg)
+    print("max length bwd errors", errs, flush=True)
