@@ -644,12 +644,13 @@ hstu_status attn_fwd_entry(const hstu_jagged *j, const hstu_dims *dm, const hstu
     TRY(check_dims(dm, BF16_D32_64_128));
     TRY(check_bias(bias, j));
     const int H = dm->heads, d = dm->d_qk, F = H * dm->d_v;
-    TRY(check_view(q.ptr, q.ld, (int64_t)H * d, "q"));
-    TRY(check_view(k.ptr, k.ld, (int64_t)H * d, "k"));
-    TRY(check_view(v.ptr, v.ld, (int64_t)F, "v"));
+    const bool rows = j->total > 0; // an empty batch has no rows to read or write: its views may be NULL
+    TRY(check_view(q.ptr, q.ld, (int64_t)H * d, "q", rows));
+    TRY(check_view(k.ptr, k.ld, (int64_t)H * d, "k", rows));
+    TRY(check_view(v.ptr, v.ld, (int64_t)F, "v", rows));
     TRY(check_view(u.ptr, u.ld, (int64_t)F, "u", false));
-    TRY(check_view(out.ptr, out.ld, (int64_t)F, "out"));
-    if (ln_stats && !u.ptr) return fail(HSTU_ERR_ARG, "ln_stats requires u (the epilogue)");
+    TRY(check_view(out.ptr, out.ld, (int64_t)F, "out", rows));
+    if (ln_stats && !u.ptr && rows) return fail(HSTU_ERR_ARG, "ln_stats requires u (the epilogue)");
     if (dm->dtype == HSTU_BF16) {
         TRY(check_vec_view(q.ptr, q.ld, HSTU_BF16, "q"));
         TRY(check_vec_view(k.ptr, k.ld, HSTU_BF16, "k"));
@@ -822,17 +823,19 @@ hstu_status hstu_attn_bwd(const hstu_jagged *j, const hstu_dims *dm, const hstu_
     TRY(check_bias(bias, j));
     if (dm->dtype != HSTU_BF16) return fail(HSTU_ERR_UNSUPPORTED, "hstu_attn_bwd supports bf16 storage only");
     const int H = dm->heads, d = dm->d_qk, F = H * dm->d_v;
-    TRY(check_view(q.ptr, q.ld, (int64_t)H * d, "q"));
-    TRY(check_view(k.ptr, k.ld, (int64_t)H * d, "k"));
-    TRY(check_view(v.ptr, v.ld, (int64_t)F, "v"));
-    TRY(check_view(dout.ptr, dout.ld, (int64_t)F, "dout"));
-    TRY(check_view(dq.ptr, dq.ld, (int64_t)H * d, "dq"));
-    TRY(check_view(dk.ptr, dk.ld, (int64_t)H * d, "dk"));
-    TRY(check_view(dv.ptr, dv.ld, (int64_t)F, "dv"));
+    const bool rows = j->total > 0; // an empty batch has no rows to read or write: its views may be NULL
+    TRY(check_view(q.ptr, q.ld, (int64_t)H * d, "q", rows));
+    TRY(check_view(k.ptr, k.ld, (int64_t)H * d, "k", rows));
+    TRY(check_view(v.ptr, v.ld, (int64_t)F, "v", rows));
+    TRY(check_view(dout.ptr, dout.ld, (int64_t)F, "dout", rows));
+    TRY(check_view(dq.ptr, dq.ld, (int64_t)H * d, "dq", rows));
+    TRY(check_view(dk.ptr, dk.ld, (int64_t)H * d, "dk", rows));
+    TRY(check_view(dv.ptr, dv.ld, (int64_t)F, "dv", rows));
     if (u.ptr) {
         TRY(check_view(u.ptr, u.ld, (int64_t)F, "u"));
-        TRY(check_view(du.ptr, du.ld, (int64_t)F, "du"));
-        if (!o_save || !ln_stats) return fail(HSTU_ERR_ARG, "with u, o_save and ln_stats from the forward are required");
+        TRY(check_view(du.ptr, du.ld, (int64_t)F, "du", rows));
+        if (rows && (!o_save || !ln_stats))
+            return fail(HSTU_ERR_ARG, "with u, o_save and ln_stats from the forward are required");
     }
     {
         const struct { const void *p; int64_t ld; const char *n; } views[] = {

@@ -88,7 +88,10 @@ typedef enum {
 
 /* A jagged batch.  batch, total and n_max are host values; offsets and ts
  * are device pointers.  n_max is the N_max of phi2 and of rab^p (a constant
- * of the model, not the realised maximum length). */
+ * of the model, not the realised maximum length).  A batch of empty
+ * sequences (total = 0) is valid: hstu_attn_fwd and hstu_attn_bwd then
+ * accept NULL activation views (there are no rows), and the backward still
+ * writes its bias gradients (zeros). */
 typedef struct {
     int32_t batch;          /* B >= 1 */
     int32_t total;          /* T = offsets[B] (host copy), >= 0 */

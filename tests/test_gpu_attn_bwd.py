@@ -220,3 +220,24 @@ def test_fwd_bwd_maximum_length():
     ref = oracle.attn_bwd(w.offsets, w.ts, w.q, w.k, w.v, w.rab_p, w.rab_t, w.n_max, w.u, w.ln_eps, w.dg)
     errs = check_all(g, ref, dg=w.dg)
     print("max length bwd errors", errs, flush=True)
+
+
+def test_empty_batch():
+    """A batch whose every sequence is empty (B = 3, total = 0): the forward
+    with and without the gate and the backward return OK with NULL (empty)
+    activation views, and the backward's bias gradients, which are
+    overwritten, never accumulated, come back as exact zeros."""
+    w = synth.attention_workload("empty", 28, np.array([0, 0, 0]), heads=4, d=128, n_max=64, epilogue=True,
+                                 with_grad=True)
+    assert w.total == 0
+    dev = torch.device("cuda:0")
+    e = lambda *s: torch.empty(s, dtype=torch.bfloat16, device=dev)
+    q, k, v, u, dg = e(0, 4, 128), e(0, 4, 128), e(0, 4, 128), e(0, 512), e(0, 512)
+    off, ts = t_i32(w.offsets), t_i64(w.ts)
+    rp, rt = t_f32(w.rab_p), t_f32(w.rab_t)
+    G = hs.attn_fwd(off, 0, ts, q, k, v, rp, rt, w.n_max, u=u, eps=w.ln_eps)
+    O = hs.attn_fwd(off, 0, ts, q, k, v, rp, rt, w.n_max)
+    g = hs.attn_bwd(off, 0, ts, q, k, v, rp, rt, w.n_max, dg)
+    torch.cuda.synchronize()
+    assert G.shape == (0, 512) and O.shape == (0, 512) and g["dq"].shape == (0, 4, 128)
+    assert torch.count_nonzero(g["drab_p"]) == 0 and torch.count_nonzero(g["drab_t"]) == 0
