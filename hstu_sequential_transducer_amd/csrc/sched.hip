@@ -408,40 +408,64 @@ __global__ void __launch_bounds__(1024) append_plan_kernel(AppendPlan p)
     }
 }
 
-// One wave per merged row r (user u, position i): K and V rows (hd bf16
-// elements, 16 bytes per lane and step) from the cache or from the new
-// tokens, and the row's time.
+// Each wave copies MERGE_ROWS consecutive merged rows r (user u, position
+// i): K and V rows (hd bf16 elements, 16 bytes per lane and step) from the
+// cache or from the new tokens, and the rows' times.  The user of the first
+// row comes from a binary search over the merged offsets, the following rows
+// walk forward from it; every row's loads are issued before its stores.
+constexpr int MERGE_ROWS = 4;
 __global__ void __launch_bounds__(256) append_merge_kernel(AppendPlan p)
 {
     if (*p.status) return;
-    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t r0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * MERGE_ROWS;
     const int lane = threadIdx.x & 63;
     const int Tm = p.Th + p.Tn;
-    if (r >= Tm) return;
-    int lo = 0, hi = p.U - 1; // last u with moff[u] <= r
+    if (r0 >= Tm) return;
+    int lo = 0, hi = p.U - 1; // last u with moff[u] <= r0
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (p.moff[mid] <= r) lo = mid;
+        if (p.moff[mid] <= r0) lo = mid;
         else hi = mid - 1;
     }
-    while (lo < p.U - 1 && p.moff[lo + 1] <= r) lo++; // skip users with nothing
-    const int u = lo;
-    const int64_t i = r - p.moff[u];
-    const int n = p.hoff[u + 1] - p.hoff[u];
-    const bf16 *ks, *vs;
-    if (i < n) {
-        ks = p.kc + (p.hoff[u] + i) * p.ldkc;
-        vs = p.vc + (p.hoff[u] + i) * p.ldvc;
-        if (p.ts_m && lane == 0) p.ts_m[r] = p.ts_h[p.hoff[u] + i];
-    } else {
-        const int64_t rn = p.aoff[u] + (i - n);
-        ks = p.knew + rn * p.ldnew;
-        vs = p.vnew + rn * p.ldnew;
-        if (p.ts_m && lane == 0) p.ts_m[r] = p.ts_a[rn];
+    const bf16 *ks[MERGE_ROWS], *vs[MERGE_ROWS];
+    int nrow = 0;
+#pragma unroll
+    for (int j = 0; j < MERGE_ROWS; j++) {
+        const int64_t r = r0 + j;
+        ks[j] = vs[j] = nullptr;
+        if (r < Tm) {
+            while (lo < p.U - 1 && p.moff[lo + 1] <= r) lo++; // next user, skipping users with nothing
+            const int64_t i = r - p.moff[lo];
+            const int n = p.hoff[lo + 1] - p.hoff[lo];
+            int64_t tsrc;
+            if (i < n) {
+                ks[j] = p.kc + (p.hoff[lo] + i) * p.ldkc;
+                vs[j] = p.vc + (p.hoff[lo] + i) * p.ldvc;
+                tsrc = p.hoff[lo] + i;
+            } else {
+                const int64_t rn = p.aoff[lo] + (i - n);
+                ks[j] = p.knew + rn * p.ldnew;
+                vs[j] = p.vnew + rn * p.ldnew;
+                tsrc = -1 - rn;
+            }
+            if (p.ts_m && lane == j) p.ts_m[r] = tsrc >= 0 ? p.ts_h[tsrc] : p.ts_a[-1 - tsrc];
+            nrow = j + 1;
+        }
     }
     for (int c = 8 * lane; c < p.hd; c += 512) {
-        *(u32x4 *)(p.kout + r * p.ldko + c) = *(const u32x4 *)(ks + c);
-        *(u32x4 *)(p.vout + r * p.ldvo + c) = *(const u32x4 *)(vs + c);
+        u32x4 kx[MERGE_ROWS], vx[MERGE_ROWS];
+#pragma unroll
+        for (int j = 0; j < MERGE_ROWS; j++)
+            if (j < nrow) {
+                kx[j] = *(const u32x4 *)(ks[j] + c);
+                vx[j] = *(const u32x4 *)(vs[j] + c);
+            }
+#pragma unroll
+        for (int j = 0; j < MERGE_ROWS; j++)
+            if (j < nrow) {
+                *(u32x4 *)(p.kout + (r0 + j) * p.ldko + c) = kx[j];
+                *(u32x4 *)(p.vout + (r0 + j) * p.ldvo + c) = vx[j];
+            }
     }
 }
 
@@ -450,7 +474,7 @@ hipError_t launch_append_plan(const AppendPlan &p, hipStream_t st)
     hipLaunchKernelGGL(append_plan_kernel, dim3(1), dim3(1024), 0, st, p);
     const int Tm = p.Th + p.Tn;
     if (Tm > 0) {
-        hipLaunchKernelGGL(append_merge_kernel, dim3((Tm + 3) / 4), dim3(256), 0, st, p);
+        hipLaunchKernelGGL(append_merge_kernel, dim3((Tm + 4 * MERGE_ROWS - 1) / (4 * MERGE_ROWS)), dim3(256), 0, st, p);
         if (p.ts_m)
             hipLaunchKernelGGL(reltime_kernel, dim3((Tm + 255) / 256), dim3(256), 0, st, p.moff, p.ts_m, p.rel, p.wide,
                                p.U, Tm, p.status);
