@@ -90,7 +90,7 @@ __global__ void __launch_bounds__(NT) sl_select_kernel(const int32_t *__restrict
     __shared__ uint32_t s_prefix;
     __shared__ int s_k;
     if (*status) return;
-    const int b = blockIdx.x, tid = threadIdx.x;
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int o = off[b], n = off[b + 1] - o;
     const int w0 = out_off[b], L = out_off[b + 1] - w0;
     if (L <= 0) return;
@@ -108,11 +108,28 @@ __global__ void __launch_bounds__(NT) sl_select_kernel(const int32_t *__restrict
                 if ((key & hmask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
             }
             __syncthreads();
-            if (tid == 0) {
-                int c = 0, d = 0;
-                while (c + hist[d] < k) c += hist[d++];
-                s_prefix = prefix | ((uint32_t)d << shift);
-                s_k = k - c;
+            // the bin d holding the k-th key: counts before d < k <= counts
+            // up to d (an inclusive scan of the 256 bins by the first four
+            // waves; empty bins never qualify, so exactly one bin does)
+            int v = 0, incl = 0;
+            if (tid < 256) {
+                v = hist[tid];
+                incl = v;
+                for (int sh = 1; sh < 64; sh <<= 1) {
+                    const int x = __shfl_up(incl, sh, 64);
+                    if (lane >= sh) incl += x;
+                }
+                if (lane == 63) tmp[wv] = incl;
+            }
+            __syncthreads();
+            if (tid < 256) {
+                int before = 0;
+                for (int w = 0; w < wv; w++) before += tmp[w];
+                const int cin = before + incl, cex = cin - v;
+                if (cex < k && k <= cin) {
+                    s_prefix = prefix | ((uint32_t)tid << shift);
+                    s_k = k - cex;
+                }
             }
             __syncthreads();
             prefix = s_prefix;
@@ -122,25 +139,24 @@ __global__ void __launch_bounds__(NT) sl_select_kernel(const int32_t *__restrict
         prefix = 0xFFFFFFFFu; // keep every action
         k = n;
     }
-    // kept: key < K, or key == K among the first k such positions
-    int run_eq = 0, run_kept = 0;
+    // kept: key < K, or key == K among the first k such positions.  A kept
+    // position's rank among the kept ones is (#keys < K before it) +
+    // min(#keys == K before it, k): one scan of both counts, packed.
+    int run_lt = 0, run_eq = 0;
     for (int j0 = 0; j0 < n; j0 += NT) {
         const int j = j0 + tid;
-        uint32_t key = 0;
         bool lt = false, eq = false;
         if (j < n) {
-            key = keys[o + j];
+            const uint32_t key = keys[o + j];
             lt = L == n || key < prefix;
             eq = L < n && key == prefix;
         }
-        int eq_tot;
-        const int eq_before = run_eq + block_excl(eq ? 1 : 0, tmp, &eq_tot);
-        const bool keep = lt || (eq && eq_before < k);
-        int kept_tot;
-        const int pos = run_kept + block_excl(keep ? 1 : 0, tmp, &kept_tot);
-        if (keep) out_idx[w0 + pos] = o + j;
-        run_eq += eq_tot;
-        run_kept += kept_tot;
+        int tot;
+        const int ex = block_excl((lt ? 1 : 0) | (eq ? 1 << 16 : 0), tmp, &tot);
+        const int eq_before = run_eq + (ex >> 16);
+        if (lt || (eq && eq_before < k)) out_idx[w0 + run_lt + (ex & 0xFFFF) + min(eq_before, k)] = o + j;
+        run_lt += tot & 0xFFFF;
+        run_eq += tot >> 16;
     }
 }
 
