@@ -255,10 +255,13 @@ __device__ void reltime_rows(const int32_t *__restrict__ offsets, const int64_t 
     if (d < -(int64_t)0x7FFFFFFF || d > (int64_t)0x7FFFFFFF) atomicOr(&wide[lo], 1);
     rel[r] = (uint32_t)(d + ((int64_t)1 << 31));
     if (((r - offsets[lo]) & 31) == 0) { // first token of a 32-token block: its range of rel
-        const int end = min(r + 32, offsets[lo + 1]);
+        // every index clamped to the block's last token (repeats change
+        // neither bound), so the 32 loads go out together
+        const int last = min(r + 32, offsets[lo + 1]) - 1;
         uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-        for (int i = r; i < end; i++) {
-            const uint32_t v = (uint32_t)(ts[i] - t0 + ((int64_t)1 << 31));
+#pragma unroll
+        for (int k = 0; k < 32; k++) {
+            const uint32_t v = (uint32_t)(ts[min(r + k, last)] - t0 + ((int64_t)1 << 31));
             mn = min(mn, v);
             mx = max(mx, v);
         }
