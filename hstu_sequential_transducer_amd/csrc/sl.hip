@@ -19,6 +19,7 @@
 namespace {
 
 constexpr int NT = 1024;
+constexpr int KPT = 8; // keys per thread held in registers (histories up to NT * KPT actions)
 
 // Exclusive prefix sum over the 1024 threads (int); `tmp` holds 16 wave totals.
 __device__ int block_excl(int v, int *tmp, int *total)
@@ -94,6 +95,15 @@ __global__ void __launch_bounds__(NT) sl_select_kernel(const int32_t *__restrict
     const int o = off[b], n = off[b + 1] - o;
     const int w0 = out_off[b], L = out_off[b + 1] - w0;
     if (L <= 0) return;
+    // Histories of at most NT * KPT actions keep their keys in registers,
+    // KPT consecutive positions per thread (all loads issued at once); longer
+    // ones re-read the keys from memory in every pass.
+    const bool reg = n <= NT * KPT;
+    uint32_t kr[KPT];
+    if (reg) {
+#pragma unroll
+        for (int i = 0; i < KPT; i++) kr[i] = keys[o + min(tid * KPT + i, n - 1)];
+    }
     // the threshold: the L-th smallest key K (prefix) and how many keys equal
     // to K are kept (k), by radix passes over the bits from the top
     uint32_t prefix = 0;
@@ -103,9 +113,15 @@ __global__ void __launch_bounds__(NT) sl_select_kernel(const int32_t *__restrict
             for (int i = tid; i < 256; i += NT) hist[i] = 0;
             __syncthreads();
             const uint32_t hmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
-            for (int j = tid; j < n; j += NT) {
-                const uint32_t key = keys[o + j];
-                if ((key & hmask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+            if (reg) {
+#pragma unroll
+                for (int i = 0; i < KPT; i++)
+                    if (tid * KPT + i < n && (kr[i] & hmask) == prefix) atomicAdd(&hist[(kr[i] >> shift) & 255], 1);
+            } else {
+                for (int j = tid; j < n; j += NT) {
+                    const uint32_t key = keys[o + j];
+                    if ((key & hmask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+                }
             }
             __syncthreads();
             // the bin d holding the k-th key: counts before d < k <= counts
@@ -142,6 +158,28 @@ __global__ void __launch_bounds__(NT) sl_select_kernel(const int32_t *__restrict
     // kept: key < K, or key == K among the first k such positions.  A kept
     // position's rank among the kept ones is (#keys < K before it) +
     // min(#keys == K before it, k): one scan of both counts, packed.
+    if (reg) {
+        int cl = 0, ce = 0;
+#pragma unroll
+        for (int i = 0; i < KPT; i++) {
+            const bool valid = tid * KPT + i < n;
+            cl += valid && (L == n || kr[i] < prefix) ? 1 : 0;
+            ce += valid && L < n && kr[i] == prefix ? 1 : 0;
+        }
+        int tot;
+        const int ex = block_excl(cl | (ce << 16), tmp, &tot);
+        int lt_before = ex & 0xFFFF, eq_before = ex >> 16;
+#pragma unroll
+        for (int i = 0; i < KPT; i++) {
+            const int j = tid * KPT + i;
+            const bool valid = j < n;
+            const bool lt = valid && (L == n || kr[i] < prefix), eq = valid && L < n && kr[i] == prefix;
+            if (lt || (eq && eq_before < k)) out_idx[w0 + lt_before + min(eq_before, k)] = o + j;
+            lt_before += lt ? 1 : 0;
+            eq_before += eq ? 1 : 0;
+        }
+        return;
+    }
     int run_lt = 0, run_eq = 0;
     for (int j0 = 0; j0 < n; j0 += NT) {
         const int j = j0 + tid;

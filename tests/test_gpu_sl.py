@@ -59,3 +59,13 @@ def test_sl_headline_histories():
     consumes, alpha = 1.6."""
     run(np.full(8, 8192), 115)
     run(np.full(64, 4096), 116, with_x=False)
+
+
+def test_sl_histories_around_the_register_limit():
+    """Histories of up to 8192 actions keep their keys in registers, longer
+    ones re-read them every pass: lengths on both sides of the limit, with
+    distinct keys and with heavy ties, and with everything kept."""
+    run([8192, 8193, 20000, 1, 8191, 700], 117)
+    run([8193, 8192, 12000, 3], 118, distinct=4)
+    o = run([8192, 9000], 119, u=1.0)
+    assert list(np.diff(o)) == [8192, 9000]
