@@ -357,7 +357,7 @@ void launch_sched(const int32_t *offsets, const int64_t *ts, int B, int T, int t
 __global__ void __launch_bounds__(1024) append_plan_kernel(AppendPlan p)
 {
     __shared__ int bad;
-    __shared__ int cnt[1024];
+    __shared__ long long ptmp[16];
     __shared__ int base_s;
     const int tid = threadIdx.x, U = p.U;
     if (tid == 0) {
@@ -388,21 +388,14 @@ __global__ void __launch_bounds__(1024) append_plan_kernel(AppendPlan p)
             }
         }
         const int mine = (t1 - t0) * p.H;
-        cnt[tid] = mine;
-        __syncthreads();
-        for (int o = 1; o < 1024; o <<= 1) { // inclusive scan over the chunk
-            const int v = tid >= o ? cnt[tid - o] : 0;
-            __syncthreads();
-            cnt[tid] += v;
-            __syncthreads();
-        }
-        const int first = base_s + cnt[tid] - mine;
+        const int ex = (int)block_prefix_excl64(mine, ptmp); // items of the chunk's earlier users
+        const int first = base_s + ex;
         for (int k = 0; k < mine; k++) {
             const int t = t1 - 1 - k / p.H, h = k % p.H;
             if (first + k < p.max_items) p.items[first + k] = make_int2(u, (t << ITEM_T_SHIFT) | h);
         }
-        __syncthreads();
-        if (tid == 1023) base_s += cnt[1023];
+        __syncthreads(); // every thread has read base_s
+        if (tid == 1023) base_s += ex + mine;
         __syncthreads();
     }
     if (tid == 0) {
